@@ -1,0 +1,386 @@
+"""Pins for the CPU oracle: each check compares it with something other than
+itself -- a textbook/library routine, a closed form, an invariant the pages fix,
+brute force on tiny inputs, or a hand-derived worked example (tests/golden)."""
+import itertools
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "worked_examples.json")))
+
+
+def _rand_logits(T, E, seed):
+    return np.random.default_rng(seed).standard_normal((T, E)).astype(np.float32)
+
+
+# ---------------------------------------------------------------- routing
+@pytest.mark.parametrize("E,k", [(8, 2), (16, 4), (160, 6), (32, 2), (5, 5)])
+def test_route_matches_stable_argsort(E, k):
+    for logits in (_rand_logits(300, E, E * 10 + k), synth.tie_logits(300, E)):
+        idx, _ = oracle.route(logits, k)
+        ref = np.argsort(-logits, axis=1, kind="stable")[:, :k]
+        assert np.array_equal(idx, ref)
+
+
+def test_route_bruteforce_subsets():
+    """Exactly one k-subset S satisfies: every e in S beats every e' outside (higher
+    logit, or equal logit and lower index); it must be the oracle's set."""
+    rng = np.random.default_rng(3)
+    for trial in range(200):
+        E = int(rng.integers(2, 7))
+        k = int(rng.integers(1, E + 1))
+        row = (rng.integers(-2, 3, size=E) * 0.5).astype(np.float32)
+        beats = lambda a, b: row[a] > row[b] or (row[a] == row[b] and a < b)
+        winners = [S for S in itertools.combinations(range(E), k)
+                   if all(beats(a, b) for a in S for b in range(E) if b not in S)]
+        assert len(winners) == 1
+        idx, _ = oracle.route(row[None, :], k)
+        assert set(idx[0].tolist()) == set(winners[0])
+        # slot order: descending logit, ties by index
+        assert all(beats(idx[0][i], idx[0][i + 1]) for i in range(k - 1))
+
+
+def test_route_k2_closed_form():
+    logits = _rand_logits(1000, 8, 11)
+    idx, w = oracle.route(logits, 2)
+    l0 = logits[np.arange(1000), idx[:, 0]].astype(np.float64)
+    l1 = logits[np.arange(1000), idx[:, 1]].astype(np.float64)
+    w0 = 1.0 / (1.0 + np.exp(l1 - l0))
+    assert np.all(np.abs(w[:, 0] - w0) <= 2.0 ** -24 * 2)
+    assert np.all(np.abs(w[:, 1] - (1.0 - w0)) <= 2.0 ** -24 * 2)
+
+
+def test_route_k_equals_E_is_full_softmax():
+    logits = _rand_logits(200, 6, 12)
+    idx, w = oracle.route(logits, 6)
+    sm = torch.softmax(torch.from_numpy(logits).double(), dim=1).numpy()
+    ref = np.take_along_axis(sm, idx.astype(np.int64), axis=1)
+    assert np.max(np.abs(w - ref)) <= 2.0 ** -23
+
+
+def test_route_weights_sum_to_one():
+    for E, k in [(8, 2), (160, 6), (16, 4)]:
+        _, w = oracle.route(_rand_logits(500, E, E), k)
+        assert np.max(np.abs(w.astype(np.float64).sum(1) - 1.0)) <= 2.0 ** -22 * k
+
+
+def test_route_golden():
+    for case in GOLD["route"]:
+        idx, w = oracle.route(np.array(case["logits"], np.float32), case["k"])
+        assert idx.tolist() == case["idx"], case["cite"]
+        assert np.array_equal(w, np.array(case["w"], np.float32)), case["cite"]
+
+
+# ------------------------------------------------------------- statistics
+def test_histogram_counts():
+    logits = _rand_logits(777, 16, 5)
+    idx, _ = oracle.route(logits, 4)
+    n = oracle.histogram(idx, 16)
+    assert n.sum() == 777 * 4
+    assert np.array_equal(n, np.bincount(idx.ravel(), minlength=16))
+
+
+def _onehot_counts(idx, E):
+    A = np.zeros((idx.shape[0], E), np.int64)
+    for i in range(idx.shape[1]):
+        np.add.at(A, (np.arange(idx.shape[0]), idx[:, i]), 1)
+    return A
+
+
+@pytest.mark.parametrize("E,k", [(8, 2), (32, 2), (16, 4), (6, 1)])
+def test_cooccurrence_matrix_identities(E, k):
+    rng = np.random.default_rng(E + k)
+    prev, _ = oracle.route(rng.standard_normal((400, E)).astype(np.float32), k)
+    nxt, _ = oracle.route(rng.standard_normal((400, E)).astype(np.float32), k)
+    C = oracle.cooccurrence(prev, nxt, E)
+    # textbook: C = A_prev^T A_next with per-token expert-count rows
+    assert np.array_equal(C, _onehot_counts(prev, E).T @ _onehot_counts(nxt, E))
+    assert np.array_equal(C.sum(1), k * np.bincount(prev.ravel(), minlength=E))
+    assert np.array_equal(C.sum(0), k * np.bincount(nxt.ravel(), minlength=E))
+    assert C.sum() == 400 * k * k
+
+
+def test_cooccurrence_golden():
+    for case in GOLD["cooccurrence"]:
+        E = case["E"]
+        C = oracle.cooccurrence(np.array(case["prev"]), np.array(case["next"]), E)
+        assert C.tolist() == case["C"], case["cite"]
+        P = oracle.conditional(C.astype(np.int64))
+        assert np.array_equal(P, np.array(case["P"], np.float32))
+        ph = oracle.predict_next(np.array(case["p_seq_prev"], np.float32), P)
+        assert np.array_equal(ph, np.array(case["p_hat"], np.float32))
+
+
+def test_popularity_window_identities():
+    """p_seq = Nw/sum(Nw): sums to one; with constant T it equals the mean of the
+    per-iteration fractions exactly (both readings of the window average agree)."""
+    rng = np.random.default_rng(21)
+    E, T, k, s = 8, 64, 2, 10
+    per_iter = []
+    for it in range(s):
+        idx, _ = oracle.route(rng.standard_normal((T, E)).astype(np.float32), k)
+        per_iter.append(oracle.histogram(idx, E))
+    Nw = np.sum(per_iter, axis=0).astype(np.int64)
+    p = oracle.popularity(Nw)
+    assert abs(float(p.astype(np.float64).sum()) - 1.0) <= 1e-6
+    for e in range(E):
+        mean_frac = sum(Fraction(int(n[e]), T * k) for n in per_iter) / s
+        assert p[e] == np.float32(float(mean_frac))
+    assert np.all(oracle.popularity(np.zeros(E, np.int64)) == 0)
+
+
+def test_conditional_rows_normalised():
+    rng = np.random.default_rng(4)
+    Cw = rng.integers(0, 50, size=(12, 12)).astype(np.int64)
+    Cw[3] = 0
+    P = oracle.conditional(Cw)
+    sums = P.astype(np.float64).sum(1)
+    assert np.all(np.abs(np.delete(sums, 3) - 1.0) <= 1e-6)
+    assert np.all(P[3] == 0)
+    assert np.array_equal(P[5], (Cw[5].astype(np.float32) / np.float32(Cw[5].sum())).astype(np.float32))
+
+
+def test_prediction_end_of_window_identity():
+    """Once layer l+1 has recorded the same iterations as layer l, propagating
+    p_seq^l through P_l gives p_seq^{l+1} (the row normaliser k*Nw_l[a] cancels
+    against p_seq^l[a] = Nw_l[a]/(k T_w) and the column sums are k*Nw_{l+1})."""
+    cfg = synth.CONFIGS["tiny"]
+    st = oracle.WindowStats(cfg.L, cfg.E, cfg.window)
+    for it in range(13):
+        prev = None
+        for layer in range(cfg.L):
+            lg = synth.logits(cfg, layer, it, None if prev is None else prev[:, 0])
+            idx, _ = oracle.route(lg, cfg.k)
+            st.record(layer, it, idx, prev)
+            prev = idx
+        p0, P0, _ = st.outputs(0)
+        p1, _, _ = st.outputs(1)
+        ph = oracle.predict_next(p0, P0)
+        assert np.max(np.abs(ph.astype(np.float64) - p1)) <= 1e-6
+
+
+def test_prediction_uses_causal_window():
+    """Right after layer 0 records iteration it, pair (0,1) still holds it-window .. it-1."""
+    E, k, window = 6, 2, 3
+    st = oracle.WindowStats(2, E, window)
+    rng = np.random.default_rng(8)
+    hist = []
+    for it in range(7):
+        i0, _ = oracle.route(rng.standard_normal((50, E)).astype(np.float32), k)
+        i1, _ = oracle.route(rng.standard_normal((50, E)).astype(np.float32), k)
+        st.record(0, it, i0)
+        _, P, _ = st.outputs(0)
+        expect = sum((oracle.cooccurrence(a, b, E).astype(np.int64) for a, b in hist[-window:]),
+                     np.zeros((E, E), np.int64))
+        assert np.array_equal(P, oracle.conditional(expect))
+        st.record(1, it, i1, i0)
+        hist.append((i0, i1))
+
+
+# --------------------------------------------------------------- replicas
+def test_replicas_golden():
+    for case in GOLD["replicas"]:
+        r = oracle.replicas(np.array(case["counts"]), case["T"], case["k"], case["R"])
+        assert r.tolist() == case["r"], case["cite"]
+
+
+def test_replicas_closed_form_when_budget_does_not_bind():
+    """MoE-GPS duplicate_experts with target T*k/E and threshold 1.0:
+    copies = ceil(load/target) - 1 for load > target."""
+    rng = np.random.default_rng(9)
+    for trial in range(300):
+        E = int(rng.integers(2, 12))
+        T, k = int(rng.integers(4, 60)), int(rng.integers(1, min(E, 4) + 1))
+        idx, _ = oracle.route(rng.standard_normal((T, E)).astype(np.float32) +
+                              np.linspace(2, -2, E).astype(np.float32), k)
+        n = oracle.histogram(idx, E)
+        r = oracle.replicas(n, T, k, 10 ** 6)
+        ref = [max(0, math.ceil(Fraction(int(ne) * E, T * k)) - 1) for ne in n]
+        assert r.tolist() == ref
+
+
+def test_replicas_bruteforce_minmax_when_budget_binds():
+    rng = np.random.default_rng(10)
+    for trial in range(150):
+        E = int(rng.integers(2, 6))
+        T, k = int(rng.integers(6, 30)), 1
+        n = rng.multinomial(T * k, rng.dirichlet(np.ones(E) * 0.5)).astype(np.int32)
+        R = int(rng.integers(1, 5))
+        r = oracle.replicas(n, T, k, R)
+        assert r.sum() <= R and np.all(r >= 0)
+        unbound = [max(0, math.ceil(Fraction(int(ne) * E, T * k)) - 1) for ne in n]
+        if sum(unbound) <= R:
+            assert r.tolist() == unbound
+            continue
+        assert r.sum() == R
+        got = max(Fraction(int(n[e]), int(r[e]) + 1) for e in range(E))
+        best = min(max(Fraction(int(n[e]), a[e] + 1) for e in range(E))
+                   for a in itertools.product(range(R + 1), repeat=E) if sum(a) <= R)
+        assert got == best
+
+
+# --------------------------------------------------------------- dispatch
+def test_dispatch_golden():
+    for case in GOLD["dispatch"]:
+        d = oracle.dispatch(np.array(case["idx"]), case["E"], np.array(case["replicas"]))
+        for key in ("expert_off", "perm_src", "inv_pos", "slot_off", "slot_expert"):
+            assert np.asarray(d[key]).tolist() == case[key], (key, case["cite"])
+
+
+@pytest.mark.parametrize("E,k,T", [(8, 2, 256), (160, 6, 300), (16, 4, 97)])
+def test_dispatch_textbook_and_bijection(E, k, T):
+    rng = np.random.default_rng(E * T)
+    idx, _ = oracle.route(rng.standard_normal((T, E)).astype(np.float32) - np.log1p(np.arange(E)).astype(np.float32), k)
+    n = oracle.histogram(idx, E)
+    reps = oracle.replicas(n, T, k, 7)
+    d = oracle.dispatch(idx, E, reps)
+    assert np.array_equal(d["perm_src"], np.argsort(idx.ravel(), kind="stable") // k)
+    assert np.array_equal(d["expert_off"], np.concatenate([[0], np.cumsum(n)]))
+    flat = d["inv_pos"].ravel()
+    assert np.array_equal(np.sort(flat), np.arange(T * k))                  # bijection
+    assert np.array_equal(d["perm_src"][flat], np.repeat(np.arange(T), k))  # inv_pos o perm = id
+    assert np.all(np.repeat(np.arange(E), n)[flat] == idx.ravel())          # row lies in its expert
+    # replica chunks: contiguous, sizes differ by at most one, sum to n_e
+    so, se = d["slot_off"], d["slot_expert"]
+    assert d["n_slots"] == E + reps.sum() and so[-1] == T * k
+    for e in range(E):
+        sizes = np.diff(so)[se == e]
+        assert len(sizes) == reps[e] + 1 and sizes.sum() == n[e] and sizes.max() - sizes.min() <= 1
+
+
+def test_dispatch_empty_experts_and_no_replicas():
+    idx = np.array([[3, 1]] * 5, np.int32)
+    d = oracle.dispatch(idx, 6)
+    assert d["expert_off"].tolist() == [0, 0, 5, 5, 10, 10, 10]
+    assert d["slot_off"].tolist() == [0, 0, 5, 5, 10, 10, 10] and d["n_slots"] == 6
+
+
+def test_permute_rows_bit_identical():
+    x = synth.f32_to_bf16_bits(np.random.default_rng(1).standard_normal((33, 40)).astype(np.float32))
+    perm = np.random.default_rng(2).integers(0, 33, size=70).astype(np.int32)
+    assert np.array_equal(oracle.permute(x, perm), x[perm])
+
+
+# ------------------------------------------------------------- expert FFN
+def _np_ffn(x64, wg, wu, wd, act, rnd):
+    z = x64 @ wg.T
+    if act == "swiglu":
+        a = z / (1.0 + np.exp(-z)) * (x64 @ wu.T)
+    else:
+        a = 0.5 * z * (1.0 + torch.erf(torch.from_numpy(z) / math.sqrt(2.0)).numpy())
+    return rnd(rnd(a) @ wd.T)
+
+
+def test_ffn_fp32_matches_numpy_fp64():
+    rng = np.random.default_rng(5)
+    E, H, I, n = 3, 48, 80, 20
+    x = rng.standard_normal((n, H)).astype(np.float32)
+    wg, wu, wd = (rng.standard_normal(s).astype(np.float32) / 7 for s in [(E, I, H), (E, I, H), (E, H, I)])
+    ex = rng.integers(0, E, size=n).astype(np.int32)
+    for act in ("swiglu", "gelu"):
+        y = oracle.ffn_rows(x, ex, wg, wu if act == "swiglu" else None, wd, act)
+        rnd = lambda v: v.astype(np.float32).astype(np.float64)
+        for j in range(n):
+            e = ex[j]
+            ref = _np_ffn(x[j:j + 1].astype(np.float64), wg[e].astype(np.float64), wu[e].astype(np.float64),
+                          wd[e].astype(np.float64), act, rnd)
+            assert np.max(np.abs(y[j] - ref[0])) <= 1e-6 * max(1.0, np.max(np.abs(ref)))
+
+
+def test_ffn_bf16_matches_numpy_fp64():
+    rng = np.random.default_rng(6)
+    E, H, I, n = 2, 32, 64, 12
+    b = lambda a: synth.f32_to_bf16_bits(a.astype(np.float32))
+    f = synth.bf16_bits_to_f32
+    x = b(rng.standard_normal((n, H)))
+    wg, wu, wd = (b(rng.standard_normal(s) / 5) for s in [(E, I, H), (E, I, H), (E, H, I)])
+    ex = rng.integers(0, E, size=n).astype(np.int32)
+    y = oracle.ffn_rows(x, ex, wg, wu, wd, "swiglu")
+    rnd = lambda v: torch.from_numpy(np.asarray(v, np.float64)).to(torch.bfloat16).double().numpy()
+    for j in range(n):
+        e = ex[j]
+        ref = _np_ffn(f(x[j:j + 1]).astype(np.float64), f(wg[e]).astype(np.float64), f(wu[e]).astype(np.float64),
+                      f(wd[e]).astype(np.float64), "swiglu", rnd)
+        got = f(y[j]).astype(np.float64)
+        # one bf16 ulp of slack per element for a double-vs-single rounding of h
+        assert np.all(np.abs(got - ref[0]) <= 2.0 ** -7 * np.abs(ref[0]) + 1e-30)
+
+
+def test_bf16_rounding_matches_torch_on_fp32_values():
+    rng = np.random.default_rng(7)
+    v = rng.standard_normal(20000).astype(np.float32)
+    v[:4] = np.array([1.00390625, 1.01171875, -1.00390625, 3.0e-39], np.float32)  # ties + subnormal
+    ours = oracle.bf16_round_bits(v.astype(np.float64))
+    ref = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+
+
+def test_single_expert_top1_is_dense_ffn():
+    """E = 1, k = 1: the layer reduces to one dense FFN applied to every token."""
+    rng = np.random.default_rng(13)
+    T, H, I = 40, 32, 48
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    wg, wu, wd = (rng.standard_normal(s).astype(np.float32) / 6 for s in [(1, I, H), (1, I, H), (1, H, I)])
+    res = oracle.moe_layer(x, np.zeros((T, 1), np.float32), 1, (wg, wu, wd), "swiglu")
+    assert np.all(res["w"] == 1.0)
+    dense = oracle.ffn_rows(x, np.zeros(T, np.int32), wg, wu, wd, "swiglu")
+    assert np.array_equal(res["out"], dense)
+
+
+# ---------------------------------------------------------------- combine
+def test_combine_golden():
+    for case in GOLD["combine"]:
+        out = oracle.combine(np.array(case["y_perm"], np.float32), np.array(case["inv_pos"]),
+                             np.array(case["w"], np.float32))
+        assert out.tolist() == case["out"], case["cite"]
+
+
+def test_combine_k1_is_inverse_permutation():
+    rng = np.random.default_rng(14)
+    T, E, H = 64, 8, 16
+    idx, w = oracle.route(rng.standard_normal((T, E)).astype(np.float32), 1)
+    assert np.all(w == 1.0)
+    d = oracle.dispatch(idx, E)
+    y = rng.standard_normal((T, H)).astype(np.float32)
+    out = oracle.combine(y, d["inv_pos"], w)
+    assert np.array_equal(out, y[d["inv_pos"][:, 0]])
+
+
+def test_combine_identity_experts_returns_input():
+    rng = np.random.default_rng(15)
+    T, E, k, H = 100, 8, 2, 24
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    idx, w = oracle.route(rng.standard_normal((T, E)).astype(np.float32), k)
+    d = oracle.dispatch(idx, E)
+    out = oracle.combine(oracle.permute(x, d["perm_src"]), d["inv_pos"], w)
+    assert np.max(np.abs(out - x)) <= 4 * 2.0 ** -24 * np.max(np.abs(x))
+
+
+def test_replication_does_not_change_layer_output():
+    cfg = synth.CONFIGS["tiny"]
+    x = synth.hidden0(cfg, 0)
+    lg = synth.logits(cfg, 0, 0)
+    wts = synth.expert_weights(cfg)
+    a = oracle.moe_layer(x, lg, cfg.k, wts, cfg.act)
+    b = oracle.moe_layer(x, lg, cfg.k, wts, cfg.act, reps_budget=cfg.R)
+    assert b["reps"].sum() == cfg.R
+    assert np.array_equal(a["out"], b["out"])
+
+
+def test_token_forward_matches_full_layer():
+    cfg = synth.CONFIGS["tiny"]
+    x = synth.hidden0(cfg, 1)
+    lg = synth.logits(cfg, 0, 1)
+    wts = synth.expert_weights(cfg)
+    full = oracle.moe_layer(x, lg, cfg.k, wts, cfg.act)
+    sample = np.array([0, 7, 100, 255])
+    _, out = oracle.token_forward(x[sample], full["idx"][sample], full["w"][sample], wts, cfg.act)
+    assert np.array_equal(out, full["out"][sample])
