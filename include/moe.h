@@ -1,0 +1,200 @@
+/*
+ * moe.h -- C ABI of libmoe_mi355x.so: one Mixture-of-Experts layer's forward
+ * pass on one AMD Instinct MI355X (gfx950), as five stream-ordered calls:
+ *
+ *   moe_route -> moe_stats -> moe_dispatch -> moe_expert_ffn -> moe_combine
+ *
+ * Sources (page title, section):
+ *   [PF]   "PopFetcher: Towards Accelerated Mixture-of-Experts Training Via
+ *           Popularity Based Expert-Wise Prefetch (ATC 2025)", wiki summary
+ *   [GPS]  "MoE-GPS框架：动态专家复制的负载均衡优化策略", blog
+ *   [EPS]  "EPS-MoE: Expert Pipeline Scheduler for Cost-Efficient MoE Inference",
+ *           review
+ *   [MPMC] "Fast MoE Inference via Predictive Prefetching and Expert
+ *           Replication", summary
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE pointers unless marked [host].  The caller allocates
+ *     and owns every buffer (outputs, workspaces, the statistics state); the
+ *     library never allocates or frees device memory and keeps no device state
+ *     between calls.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Each
+ *     call checks its host-side arguments, enqueues its kernels on `stream` and
+ *     returns without waiting, except where a call says otherwise.
+ *   - Return value: MOE_OK or a negative moe_status.  Argument errors are
+ *     reported before anything is enqueued; moe_last_error() then holds a
+ *     message for the calling thread.  Nothing throws across the ABI.
+ *   - Arrays are row-major and contiguous.  Expert weights use the [out, in]
+ *     layout per expert, so the reduction dimension is contiguous for both
+ *     operands of every product.
+ *   - Kernels never access memory outside the extents given, whatever the
+ *     values in index arrays; out-of-range indices are skipped (results for
+ *     such inputs are unspecified, but memory-safe).
+ *   - Calls are reentrant.  Two in-flight calls must not share an output,
+ *     workspace or statistics state.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = -1, /* null pointer, negative size, k > E, misalignment ... */
+    MOE_ERR_UNSUPPORTED = -2, /* valid but outside this build's limits (E > 256, H % 64 ...) */
+    MOE_ERR_WORKSPACE = -3,   /* workspace or state smaller than the *_bytes query says */
+    MOE_ERR_HIP = -4          /* a HIP runtime call failed; moe_last_error() has its text */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;       /* activations and weights */
+typedef enum { MOE_SWIGLU = 0, MOE_GELU = 1 } moe_act;
+typedef enum { MOE_GEMM_AUTO = 0, MOE_GEMM_GROUPED = 1, MOE_GEMM_DENSE = 2 } moe_gemm_path;
+
+/* ---------------------------------------------------------------- routing
+ * moe_route -- top-k softmax gate ([PF] observations and trade-offs: the naive
+ * top-k gate; [MPMC] problem statement: softmax routing).
+ *   logits    fp32 [T, E]
+ *   topk_idx  int32 [T, k] out: the k experts of each token, by logit
+ *             descending; equal logits go to the lower expert index; slot 0 is
+ *             the top-1.
+ *   topk_w    fp32 [T, k] out: softmax probabilities of the kept experts,
+ *             renormalised to sum to one (= softmax over the kept logits).
+ * Limits: 1 <= E <= 256, 1 <= k <= min(E, 8), 0 <= T, T*k < 2^31.
+ * Logits are expected finite; NaN is ordered as -inf (indices stay in range).
+ */
+int moe_route(const float* logits, int64_t T, int E, int k, int32_t* topk_idx, float* topk_w,
+              void* stream);
+
+/* ------------------------------------------------------------- statistics
+ * Sliding-window routing statistics of a chain of L MoE layers ([PF] method:
+ * Routing Information Collector, sliding window s, Eq.(1)-(3); [GPS] 2.1:
+ * distribution-only prediction p_i = n_i / N with a sliding-window average).
+ *
+ * The state is a caller-owned device buffer of moe_stats_state_bytes(L, E,
+ * window) bytes holding, per layer, a ring of `window` per-iteration count
+ * vectors, per adjacent layer pair a ring of E x E co-occurrence matrices, and
+ * a small accumulator.  It is plain memory: a checkpoint is a byte copy.
+ * moe_stats_init zeroes it (enqueued on `stream`).
+ *
+ * moe_stats records layer `layer` of iteration `iter` and reports:
+ *   - counts[e]   int32 [E]: tokens routed to e by topk_idx (this iteration);
+ *   - p_seq[e]    fp32 [E]: window popularity of `layer`,
+ *                 Nw[e] / sum(Nw), Nw = the ring's counts summed ([PF] Eq.(1));
+ *   - cond        fp32 [E, E]: Pr(next = b | this = a) for pair (layer,
+ *                 layer+1), the pair's windowed co-occurrence with each row
+ *                 normalised (zero rows stay zero) ([PF] Eq.(2));
+ *   - pred_next   fp32 [E]: predicted popularity of layer+1,
+ *                 sum_a p_seq[a] * cond[a, b] ([PF] Eq.(3));
+ *   - replicas    int32 [E]: extra copies per expert from this iteration's
+ *                 counts: the budget of `replica_budget` copies is handed out
+ *                 one at a time to the expert with the largest per-copy load
+ *                 counts[e]/(r_e+1) among those still above the mean
+ *                 T*k/E per copy (counts[e]*E > T*k*(r_e+1)); ties go to the
+ *                 lower index ([GPS] 2.1 duplicate_experts with threshold 1;
+ *                 [MPMC] contribution 3: capacity-bounded replication).
+ * Recording replaces ring slot iter % window of layer's counts and, when
+ * layer > 0, of pair (layer-1, layer)'s co-occurrence (k*k pairs per token,
+ * from prev_topk_idx = layer-1's routing of the same tokens).  The outputs are
+ * computed after that update, so p_seq covers the last `window` recorded
+ * iterations and cond/pred_next, whose pair has not recorded `iter` yet,
+ * cover the `window` iterations before it: a causal prediction.
+ * Any output pointer may be NULL (not written).  cond and pred_next are not
+ * written when layer == L-1.  topk_idx == NULL records nothing and only
+ * reports (T, k and prev_topk_idx are then ignored; counts and replicas are
+ * not written).
+ * Limits: 1 <= E <= 256, 1 <= L, 1 <= window <= 1024, 0 <= layer < L,
+ * iter >= 0, window * T * k * k < 2^31, 0 <= replica_budget <= 4096.
+ */
+size_t moe_stats_state_bytes(int L, int E, int window); /* [host] */
+int moe_stats_init(void* state, size_t state_bytes, int L, int E, int window, void* stream);
+int moe_stats(void* state, size_t state_bytes, int L, int E, int window, int layer, int64_t iter,
+              const int32_t* topk_idx, const int32_t* prev_topk_idx, int64_t T, int k,
+              int32_t* counts, float* p_seq, float* cond, float* pred_next,
+              int replica_budget, int32_t* replicas, void* stream);
+
+/* --------------------------------------------------------------- dispatch
+ * moe_dispatch -- permute tokens into expert/replica-contiguous rows (the
+ * token dispatch that precedes the expert computation; [EPS] section 3 and
+ * [PF] motivation: the dispatch All-to-All, here a local permute).  With
+ * M = T*k rows:
+ *   expert_off  int32 [E+1]: exclusive prefix sum of the per-expert counts;
+ *               expert e owns rows [expert_off[e], expert_off[e+1]).
+ *   perm_src    int32 [M]: source token of each row.  Inside an expert, rows
+ *               follow ascending token index (a stable permutation).
+ *   inv_pos     int32 [T, k]: the row holding (t, topk_idx[t, i]).
+ *   x_perm      [M, H] in dtype `dt`: x_perm[r] = x[perm_src[r]] (byte copy).
+ *   slot table  replicas[e] extra copies cut expert e's rows into
+ *               replicas[e]+1 contiguous chunks in token order, chunk rho
+ *               covering [floor(rho*n_e/(r_e+1)), floor((rho+1)*n_e/(r_e+1)))
+ *               of the expert's rows ([MPMC] method: replicas of one expert
+ *               serve disjoint token subsets).  Slots are expert-major:
+ *               slot_expert [max_slots], slot_off [max_slots+1] (slot s owns
+ *               rows [slot_off[s], slot_off[s+1])), n_slots [1].  Unused slots
+ *               up to max_slots are empty (slot_off = M).  replicas == NULL
+ *               means one slot per expert.  Copies beyond max_slots - E are
+ *               dropped in expert order (the kernel never writes past
+ *               max_slots); negative counts are taken as 0.
+ *   workspace   at least moe_dispatch_workspace_bytes(T, k, E) bytes.
+ * Limits: 1 <= E <= 256, 1 <= k <= min(E, 8), T*k < 2^31, E <= max_slots,
+ * H*sizeof(dt) % 16 == 0, x and x_perm 16-byte aligned.
+ */
+size_t moe_dispatch_workspace_bytes(int64_t T, int k, int E); /* [host] */
+int moe_dispatch(const void* x, moe_dtype dt, int64_t T, int H, const int32_t* topk_idx, int k, int E,
+                 const int32_t* replicas, int max_slots,
+                 void* x_perm, int32_t* perm_src, int32_t* inv_pos, int32_t* expert_off,
+                 int32_t* slot_off, int32_t* slot_expert, int32_t* n_slots,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------- expert FFN
+ * moe_expert_ffn -- every slot's rows through its expert's FFN ([EPS] section
+ * 3: the gate, up and down GEMMs; GroupGemm runs all experts in one kernel,
+ * DenseGemm runs a uniform padded batch):
+ *   SwiGLU: h = silu(x Wg^T) * (x Wu^T), y = h Wd^T
+ *           w_gate, w_up [E, I, H]; w_down [E, H, I]
+ *   GELU:   h = gelu(x W1^T) (exact erf form), y = h W2^T
+ *           w_gate = W1 [E, I, H]; w_up must be NULL; w_down = W2 [E, H, I]
+ * bf16 inputs are multiplied on bf16 MFMA with fp32 accumulation, fp32 inputs
+ * on fp32 MFMA; h is rounded to dtype (kept in the workspace), then y.  Each
+ * row's result depends only on that row: it is the same whichever slot, tile
+ * or path computes it (fixed reduction order, no split-K), so replicated and
+ * non-replicated dispatches give bit-identical y_perm.
+ *   path  GROUPED: tiles cover each slot's rows exactly (no host sync).
+ *         DENSE:   every slot padded to the largest slot's row count, run as
+ *                  one uniform batch; reads the slot table back to the host
+ *                  (synchronises `stream`).
+ *         AUTO:    reads the slot table back and picks DENSE when the
+ *                  largest slot is small, else GROUPED.
+ *   workspace  at least moe_expert_ffn_workspace_bytes(...) bytes.
+ * Limits: dtype F32 or BF16; H and I multiples of 64; E <= max_slots;
+ * M <= 2^31 - 1; rows referenced by slot_off lie in [0, M).
+ */
+size_t moe_expert_ffn_workspace_bytes(moe_dtype dt, int64_t M, int H, int I, int max_slots); /* [host] */
+int moe_expert_ffn(const void* x_perm, moe_dtype dt, int64_t M, int H, int I, int E,
+                   const int32_t* slot_off, const int32_t* slot_expert, const int32_t* n_slots, int max_slots,
+                   const void* w_gate, const void* w_up, const void* w_down, moe_act act, moe_gemm_path path,
+                   void* y_perm, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------- combine
+ * moe_combine -- weighted combine back to token order ([EPS] section 3: the
+ * LocalReduce that follows the expert computation):
+ *   out[t] = sum_{i<k} topk_w[t, i] * y_perm[inv_pos[t, i]]
+ * accumulated in fp32 in slot order i = 0..k-1, rounded once to dtype.
+ * inv_pos entries outside [0, M) contribute nothing.
+ * Limits: 1 <= k <= 8, H*sizeof(dt) % 16 == 0, y_perm and out 16-byte aligned.
+ */
+int moe_combine(const void* y_perm, moe_dtype dt, int64_t M, const int32_t* inv_pos, const float* topk_w,
+                int64_t T, int k, int H, void* out, void* stream);
+
+/* ---------------------------------------------------------------- errors */
+const char* moe_status_string(int status); /* [host] static text */
+const char* moe_last_error(void);          /* [host] calling thread's last message */
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

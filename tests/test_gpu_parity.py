@@ -1,0 +1,287 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle, on the same
+seeded inputs.  Small shapes are compared element by element (several tiles and
+ragged tails); the full workload shapes are compared bit-exactly on every
+integer output and on sampled tokens for the floating-point outputs."""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_routing_top_amd as moe
+import oracle
+import synth
+from _util import assert_close, f64, from_dev, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _sync():
+    torch.cuda.synchronize()
+
+
+def _logits(T, E, seed, skew=1.0):
+    rng = np.random.default_rng(seed)
+    bias = -skew * np.log1p(rng.permutation(E)).astype(np.float32)
+    return (rng.standard_normal((T, E)).astype(np.float32) + bias).astype(np.float32)
+
+
+# ------------------------------------------------------------------ routing
+@pytest.mark.parametrize("T,E,k", [(256, 8, 2), (1000, 160, 6), (333, 16, 4), (4097, 32, 2), (77, 5, 3),
+                                   (50, 256, 8), (64, 1, 1), (10, 3, 3), (129, 7, 7)])
+def test_route_matches_oracle(T, E, k):
+    for lg in (_logits(T, E, T + E), synth.tie_logits(T, E)):
+        idx, w = moe.moe_route(to_dev(lg), k)
+        _sync()
+        ridx, rw = oracle.route(lg, k)
+        assert np.array_equal(from_dev(idx), ridx)
+        assert_close(from_dev(w), rw, "fp32", "topk_w")
+        assert np.max(np.abs(from_dev(w) - rw)) <= 2e-6
+
+
+@pytest.mark.parametrize("name,T", [("mixtral", 8192), ("dsv2", 16384), ("dbrx", 4096), ("popfetcher", 16384)])
+def test_route_full_size(name, T):
+    cfg = synth.CONFIGS[name].with_T(T)
+    lg = synth.logits(cfg, 0, 0)
+    idx, w = moe.moe_route(to_dev(lg), cfg.k)
+    _sync()
+    ridx, rw = oracle.route(lg, cfg.k)
+    assert np.array_equal(from_dev(idx), ridx)
+    assert_close(from_dev(w), rw, "fp32", "topk_w")
+
+
+def test_route_empty_batch():
+    idx, w = moe.moe_route(torch.empty((0, 8), dtype=torch.float32, device="cuda"), 2)
+    _sync()
+    assert idx.shape == (0, 2)
+
+
+# --------------------------------------------------------------- statistics
+def _run_stats_chain(cfg, iters, check_every=True):
+    """Route + record every layer of every iteration on both sides and compare."""
+    L, E, k, win, R = cfg.L, cfg.E, cfg.k, cfg.window, cfg.R
+    state = torch.empty(moe.moe_stats_state_bytes(L, E, win), dtype=torch.uint8, device="cuda")
+    moe.moe_stats_init(state, L, E, win)
+    ost = oracle.WindowStats(L, E, win)
+    outs = {n: torch.empty(s, dtype=d, device="cuda") for n, s, d in
+            [("counts", E, torch.int32), ("p_seq", E, torch.float32), ("cond", (E, E), torch.float32),
+             ("pred", E, torch.float32), ("reps", E, torch.int32)]}
+    for it in range(iters):
+        prev_o, prev_g = None, None
+        for layer in range(L):
+            lg = synth.logits(cfg, layer, it, None if prev_o is None else prev_o[:, 0])
+            idx_g, _ = moe.moe_route(to_dev(lg), k)
+            last = layer + 1 >= L
+            moe.moe_stats(state, L, E, win, layer, it, idx_g, prev_g, k, outs["counts"], outs["p_seq"],
+                          None if last else outs["cond"], None if last else outs["pred"], R,
+                          outs["reps"] if R > 0 else None)
+            _sync()
+            idx_o, _ = oracle.route(lg, k)
+            assert np.array_equal(from_dev(idx_g), idx_o), (it, layer)
+            cnt = ost.record(layer, it, idx_o, prev_o)
+            if check_every or it == iters - 1:
+                assert np.array_equal(from_dev(outs["counts"]), cnt), (it, layer)
+                p, P, ph = ost.outputs(layer)
+                assert_close(from_dev(outs["p_seq"]), p, "fp32", "p_seq")
+                assert np.max(np.abs(from_dev(outs["p_seq"]) - p)) <= 1e-7
+                if not last:
+                    assert_close(from_dev(outs["cond"]), P, "fp32", "cond")
+                    assert np.max(np.abs(from_dev(outs["cond"]) - P)) <= 1e-7
+                    assert np.max(np.abs(from_dev(outs["pred"]) - ph)) <= 1e-6
+                if R > 0:
+                    assert np.array_equal(from_dev(outs["reps"]), oracle.replicas(cnt, cfg.T, k, R))
+            prev_o, prev_g = idx_o, idx_g
+    return state, ost
+
+
+def test_stats_tiny_chain_window():
+    cfg = synth.CONFIGS["tiny"]
+    state, ost = _run_stats_chain(cfg, 14)   # wraps the 10-slot ring
+    # read-only call after layer 1 recorded the last iteration: the prediction
+    # for layer 1 from layer 0 now equals layer 1's own popularity.
+    E = cfg.E
+    pred = torch.empty(E, dtype=torch.float32, device="cuda")
+    p0 = torch.empty(E, dtype=torch.float32, device="cuda")
+    moe.moe_stats(state, cfg.L, E, cfg.window, 0, 13, None, None, 0, None, p0, None, pred)
+    _sync()
+    p1, _, _ = ost.outputs(1)
+    assert np.max(np.abs(from_dev(pred).astype(np.float64) - p1)) <= 1e-6
+    p0_ref, P0, _ = ost.outputs(0)
+    assert np.max(np.abs(from_dev(pred) - oracle.predict_next(p0_ref, P0))) <= 1e-7
+
+
+def test_stats_popfetcher_shape():
+    cfg = synth.CONFIGS["popfetcher"]
+    _run_stats_chain(cfg, cfg.iters, check_every=False)
+
+
+def test_stats_dsv2_replicas_large_E():
+    cfg = synth.CONFIGS["dsv2"].scaled(R=64, window=3)
+    _run_stats_chain(cfg, 4)
+
+
+# ----------------------------------------------------------------- dispatch
+@pytest.mark.parametrize("T,E,k,H,dt,R", [(256, 8, 2, 64, "f32", 4), (1000, 160, 6, 96, "bf16", 0),
+                                          (513, 16, 4, 64, "bf16", 16), (1, 8, 2, 8, "bf16", 3),
+                                          (300, 32, 2, 40, "f32", 5), (4100, 8, 2, 128, "bf16", 8)])
+def test_dispatch_matches_oracle(T, E, k, H, dt, R):
+    lg = _logits(T, E, 7 * T + E, skew=2.0)
+    idx_o, _ = oracle.route(lg, k)
+    rng = np.random.default_rng(T)
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    x = synth.f32_to_bf16_bits(x) if dt == "bf16" else x
+    reps = oracle.replicas(oracle.histogram(idx_o, E), T, k, R) if R else None
+    max_slots = E + R
+    d = moe.moe_dispatch(to_dev(x), to_dev(idx_o), E, None if reps is None else to_dev(reps), max_slots)
+    _sync()
+    ref = oracle.dispatch(idx_o, E, reps)
+    for key in ("expert_off", "perm_src", "inv_pos"):
+        assert np.array_equal(from_dev(d[key]), ref[key]), key
+    S = ref["n_slots"]
+    assert int(from_dev(d["n_slots"])[0]) == S
+    assert np.array_equal(from_dev(d["slot_off"])[:S + 1], ref["slot_off"])
+    assert np.all(from_dev(d["slot_off"])[S:] == T * k)
+    assert np.array_equal(from_dev(d["slot_expert"])[:S], ref["slot_expert"])
+    assert np.array_equal(from_dev(d["x_perm"]), oracle.permute(x, ref["perm_src"]))
+
+
+def test_dispatch_replicas_beyond_budget_are_dropped():
+    T, E, k = 64, 4, 2
+    idx_o, _ = oracle.route(_logits(T, E, 3), k)
+    reps = np.array([5, 1, 7, 2], np.int32)    # 15 copies requested, room for 6
+    d = moe.moe_dispatch(to_dev(np.zeros((T, 8), np.float32)), to_dev(idx_o), E, to_dev(reps), E + 6)
+    _sync()
+    kept = np.array([5, 1, 0, 0], np.int32)     # expert order: 5 + 1 fill the 6 spare slots
+    ref = oracle.dispatch(idx_o, E, kept)
+    assert int(from_dev(d["n_slots"])[0]) == E + 6
+    assert np.array_equal(from_dev(d["slot_off"]), ref["slot_off"])
+
+
+# ------------------------------------------------------------ whole layer
+MINI = {
+    "tiny": synth.CONFIGS["tiny"],
+    "mixtral-mini": synth.CONFIGS["mixtral"].scaled(T=300, H=256, I=448),
+    "dsv2-mini": synth.CONFIGS["dsv2"].scaled(T=200, H=320, I=192),
+    "dbrx-mini": synth.CONFIGS["dbrx"].scaled(T=257, H=384, I=640),
+    "popf-mini": synth.CONFIGS["popfetcher"].scaled(T=500, H=128, I=256, L=1),
+}
+
+
+def _gpu_layer(cfg, x, lg, wts, R, path="grouped"):
+    wg, wu, wd = (None if w is None else to_dev(w) for w in wts)
+    res = moe.moe_layer_forward(to_dev(x), to_dev(lg), cfg.k, wg, wu, wd, cfg.act, R, path=path)
+    _sync()
+    return res
+
+
+@pytest.mark.parametrize("name", list(MINI))
+@pytest.mark.parametrize("use_reps", [False, True])
+def test_layer_small_elementwise(name, use_reps):
+    cfg = MINI[name]
+    R = (cfg.R or 8) if use_reps else 0
+    x = synth.hidden0(cfg, 0)
+    lg = synth.logits(cfg, 0, 0)
+    wts = synth.expert_weights(cfg)
+    res = _gpu_layer(cfg, x, lg, wts, R)
+    ref = oracle.moe_layer(x, lg, cfg.k, wts, cfg.act, reps_budget=R)
+    assert np.array_equal(from_dev(res["idx"]), ref["idx"])
+    assert np.array_equal(from_dev(res["x_perm"]), ref["x_perm"])
+    kind = "bf16" if cfg.dtype == "bf16" else "fp32_gemm"
+    assert_close(from_dev(res["y_perm"]), ref["y_perm"], kind, "y_perm")
+    assert_close(from_dev(res["out"]), ref["out"], kind, "out")
+
+
+@pytest.mark.parametrize("name", ["mixtral-mini", "dbrx-mini", "popf-mini"])
+def test_replication_is_bit_identical(name):
+    cfg = MINI[name]
+    x = synth.hidden0(cfg, 1)
+    lg = synth.logits(cfg, 0, 1)
+    wts = synth.expert_weights(cfg)
+    a = _gpu_layer(cfg, x, lg, wts, 0)
+    ya, oa = from_dev(a["y_perm"]), from_dev(a["out"])
+    b = _gpu_layer(cfg, x, lg, wts, cfg.R or 8)
+    assert int(from_dev(b["n_slots"])[0]) > cfg.E
+    assert np.array_equal(from_dev(b["y_perm"]), ya)
+    assert np.array_equal(from_dev(b["out"]), oa)
+
+
+def test_single_expert_top1_is_dense_ffn():
+    cfg = synth.CONFIGS["mixtral"].scaled(T=130, H=128, I=192, E=1, k=1)
+    x = synth.hidden0(cfg, 0)
+    wts = synth.expert_weights(cfg)
+    res = _gpu_layer(cfg, x, np.zeros((cfg.T, 1), np.float32), wts, 0)
+    ref = oracle.ffn_rows(x, np.zeros(cfg.T, np.int32), *wts, act="swiglu")
+    assert_close(from_dev(res["out"]), ref, "bf16", "out")
+    assert np.array_equal(from_dev(res["out"]), from_dev(res["y_perm"]))
+
+
+# --------------------------------------------- full workload shapes, sampled
+def _sampled_layer_check(cfg, R, n_sample=12, seed=0):
+    x = synth.hidden0(cfg, 0)
+    lg = synth.logits(cfg, 0, 0)
+    wts = synth.expert_weights(cfg, threads=16)
+    res = _gpu_layer(cfg, x, lg, wts, R)
+    idx_o, w_o = oracle.route(lg, cfg.k)
+    assert np.array_equal(from_dev(res["idx"]), idx_o)
+    reps = oracle.replicas(oracle.histogram(idx_o, cfg.E), cfg.T, cfg.k, R) if R else None
+    d = oracle.dispatch(idx_o, cfg.E, reps)
+    for key in ("expert_off", "perm_src", "inv_pos"):
+        assert np.array_equal(from_dev(res[key]), d[key]), key
+    S = d["n_slots"]
+    assert np.array_equal(from_dev(res["slot_off"])[:S + 1], d["slot_off"])
+    sample = np.random.default_rng(seed).choice(cfg.T, size=n_sample, replace=False)
+    y_ref, out_ref = oracle.token_forward(x[sample], idx_o[sample], w_o[sample], wts, cfg.act)
+    y_gpu = from_dev(res["y_perm"])[d["inv_pos"][sample].ravel()].reshape(y_ref.shape)
+    kind = "bf16" if cfg.dtype == "bf16" else "fp32_gemm"
+    assert_close(y_gpu, y_ref, kind, "sampled y_perm rows")
+    assert_close(from_dev(res["out"])[sample], out_ref, kind, "sampled out rows")
+    x_perm = from_dev(res["x_perm"])
+    rows = np.random.default_rng(seed + 1).choice(cfg.T * cfg.k, size=256, replace=False)
+    assert np.array_equal(x_perm[rows], x[d["perm_src"][rows]])
+    return res
+
+
+@pytest.mark.parametrize("R", [0, 8])
+def test_mixtral_full_size_sampled(R):
+    _sampled_layer_check(synth.CONFIGS["mixtral"], R)
+
+
+@pytest.mark.parametrize("T", synth.DSV2_T_SWEEP)
+def test_dsv2_full_size_sampled(T):
+    _sampled_layer_check(synth.CONFIGS["dsv2"].with_T(T), 0, n_sample=6)
+
+
+def test_dbrx_full_size_replication_equivalence():
+    cfg = synth.CONFIGS["dbrx"]
+    res = _sampled_layer_check(cfg, cfg.R, n_sample=6)
+    y_rep, out_rep = from_dev(res["y_perm"]), from_dev(res["out"])
+    del res
+    x = synth.hidden0(cfg, 0)
+    lg = synth.logits(cfg, 0, 0)
+    wts = synth.expert_weights(cfg, threads=16)
+    plain = _gpu_layer(cfg, x, lg, wts, 0)
+    assert np.array_equal(from_dev(plain["y_perm"]), y_rep)
+    assert np.array_equal(from_dev(plain["out"]), out_rep)
+
+
+def test_popfetcher_full_chain_sampled():
+    """12 chained fp32 GELU layers at T=16384: routing bit-exact at every layer,
+    and the final hidden states of sampled tokens against the oracle's per-token
+    chain (a token's trajectory depends only on its own row)."""
+    cfg = synth.CONFIGS["popfetcher"]
+    sample = np.random.default_rng(5).choice(cfg.T, size=8, replace=False)
+    x = synth.hidden0(cfg, 0)
+    xg = to_dev(x)
+    xs = x[sample]
+    prev = None
+    bufs = {}
+    for layer in range(cfg.L):
+        wts = synth.expert_weights(cfg, layer=layer, threads=16)
+        lg = synth.logits(cfg, layer, 0, None if prev is None else prev[:, 0])
+        wg, _, wd = (None if w is None else to_dev(w) for w in wts)
+        res = moe.moe_layer_forward(xg, to_dev(lg), cfg.k, wg, None, wd, cfg.act, 0, bufs=bufs)
+        _sync()
+        idx_o, w_o = oracle.route(lg, cfg.k)
+        assert np.array_equal(from_dev(res["idx"]), idx_o), layer
+        _, xs = oracle.token_forward(xs, idx_o[sample], w_o[sample], wts, cfg.act)
+        xg = res["out"].clone()
+        prev = idx_o
+    assert_close(from_dev(xg)[sample], xs, "fp32_gemm", "layer-12 hidden states (sampled)")
