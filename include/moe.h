@@ -190,6 +190,17 @@ int moe_expert_ffn(const void* x_perm, moe_dtype dt, int64_t M, int H, int I, in
 int moe_combine(const void* y_perm, moe_dtype dt, int64_t M, const int32_t* inv_pos, const float* topk_w,
                 int64_t T, int k, int H, void* out, void* stream);
 
+/* -------------------------------------------------------------- profiling
+ * moe_ffn_set_timing_events -- measures the GEMM launches inside
+ * moe_expert_ffn.  While set (per calling thread), every moe_expert_ffn call
+ * records `before_gateup` on its stream right before the gate/up (W1) GEMM,
+ * `after_gateup` right after it, and `after_down` right after the down (W2)
+ * GEMM.  The three hipEvent_t handles (passed as void*) are created and owned
+ * by the caller; all three NULL stops the recording.  Either all three are
+ * NULL or none is (MOE_ERR_INVALID_ARG otherwise).
+ */
+int moe_ffn_set_timing_events(void* before_gateup, void* after_gateup, void* after_down);
+
 /* ---------------------------------------------------------------- errors */
 const char* moe_status_string(int status); /* [host] static text */
 const char* moe_last_error(void);          /* [host] calling thread's last message */

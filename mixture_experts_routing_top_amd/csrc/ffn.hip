@@ -7,27 +7,36 @@
 // SwiGLU h = silu(x Wg^T) * (x Wu^T), y = h Wd^T; GELU h = gelu(x W1^T),
 // y = h W2^T.
 //
-// Two launches of one tiled kernel after a tiny tile-table pass:
-//   tiles:   walks the slot table and lists every (slot, 128-row tile) --
-//            tiles cover each slot's rows exactly, no host sync.
-//   phase 1: for each tile x each block of I columns, the gate and up tiles
-//            (or W1) are accumulated side by side so one lane holds g and u of
-//            the same element; the activation runs in the epilogue and h is
-//            rounded to the dtype once.
-//   phase 2: y = h Wd^T over the same tiles, rounded to the dtype.
-// 256 threads = 4 waves in 2 x 2; each wave owns a 64 x 64 block per weight
-// matrix as 2 x 2 MFMA tiles of 32 x 32 (v_mfma_f32_32x32x16_bf16 for bf16,
-// v_mfma_f32_32x32x2f32 for fp32).  A and B tiles are staged through LDS with
-// 16-byte global loads, the next K tile prefetched into registers while the
-// current one is multiplied.  Each output row depends only on its own input
-// row and the fixed K order, so a row's value does not depend on the tile,
-// slot or path that computes it.
+// A tile-table pass, then two launches of one tiled kernel:
+//   tiles:   lists every (slot, 256-row tile); tiles cover each slot's rows
+//            exactly, no host sync.
+//   phase 1: per tile and per 128 columns of I, the gate and up weight tiles
+//            are multiplied side by side so one lane holds g and u of the same
+//            element; the activation runs in the epilogue and h is rounded to
+//            the dtype once (GELU: one 256-column weight tile).
+//   phase 2: y = h Wd^T per tile and 256 columns of H, rounded to the dtype.
+//
+// gfx950 mapping.  A block is 256 threads (4 waves, one per SIMD) computing a
+// 256 x 256 output tile; each wave owns 128 x 128 as 4 x 4 MFMA tiles of
+// 32 x 32 (v_mfma_f32_32x32x16_bf16, or v_mfma_f32_32x32x2f32 for fp32), 256
+// accumulator registers.  K advances 128 bytes per row per step (64 bf16 / 32
+// fp32) through two LDS stages (2 x 144 KB-ish of padded rows, conflict-free
+// 16-byte fragment reads); the next step's tiles travel global -> registers
+// while the current one is multiplied, one barrier per step.  Operands are
+// read with raw buffer loads whose range ends at the slot's (or matrix's)
+// last valid row, so rows past the end read as zero and need no clamping.
+// Blocks are remapped so each of the 8 XCDs works on a contiguous run of
+// tiles, ordered 8 row tiles by N columns, which keeps the A and B tiles that
+// neighbouring blocks share inside that XCD's L2.  Each output row depends
+// only on its own input row and the fixed K order, so a row's value does not
+// depend on the tile, slot or path that computes it.
 #include "common.h"
 
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 enum Epi { kEpiSwiGLU = 0, kEpiGELU = 1, kEpiStore = 2 };
 
@@ -36,10 +45,9 @@ struct Tr;
 template <>
 struct Tr<true> {
   using T = uint16_t;
-  static constexpr int BK = 64;   // K elements per LDS tile (128 bytes per row)
-  static constexpr int MK = 16;   // K per MFMA
-  static constexpr int KV = 8;    // K elements per lane per MFMA
-  static constexpr int PAD = 8;   // row padding (elements) against LDS bank conflicts
+  static constexpr int BK = 64;  // K elements per step (128 bytes per row)
+  static constexpr int MK = 16;  // K per MFMA
+  static constexpr int KV = 8;   // K elements per lane per MFMA
   using Frag = uint4;
 };
 template <>
@@ -48,7 +56,6 @@ struct Tr<false> {
   static constexpr int BK = 32;
   static constexpr int MK = 2;
   static constexpr int KV = 1;
-  static constexpr int PAD = 4;
   using Frag = float;
 };
 
@@ -59,6 +66,12 @@ __device__ __forceinline__ f32x16 mma(const uint4& a, const uint4& b, const f32x
 __device__ __forceinline__ f32x16 mma(float a, float b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
+
+constexpr int kTileM = 256;      // rows per tile
+constexpr int kTileN = 256;      // weight rows per tile (gate/up: 128 + 128)
+constexpr int kRowBytes = 144;   // LDS row pitch: 128 data bytes + 16 pad
+constexpr int kStageBytes = (kTileM + kTileN) * kRowBytes;
+constexpr int kGroupM = 8;       // row tiles per raster group
 
 struct GemmArgs {
   const void* A;   // [M, K]
@@ -75,134 +88,159 @@ struct GemmArgs {
   int n_col_tiles;
 };
 
-template <bool kBf16, int BM, int BN, int NMAT, int EPI>
-__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
+  const int n = bytes > 0x7fffffff ? 0x7fffffff : static_cast<int>(bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), n, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, int off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+template <bool kBf16, int NMAT, int EPI>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_kernel(GemmArgs g) {
   using TR = Tr<kBf16>;
   using T = typename TR::T;
   using Frag = typename TR::Frag;
-  constexpr int BK = TR::BK, LDK = BK + TR::PAD, EPV = 16 / sizeof(T);  // elements per 16 bytes
-  constexpr int TM = BM / 64, TN = BN / 64;
-  constexpr int PA = BM / 32, PB = BN / 32;  // 16-byte load passes per tile (32 rows per pass)
-  __shared__ __align__(16) T As[BM * LDK];
-  __shared__ __align__(16) T Bs[NMAT * BN * LDK];
+  constexpr int S = sizeof(T);
+  constexpr int BK = TR::BK;
+  constexpr int NSUB = kTileN / NMAT;  // output columns per tile
+  __shared__ __align__(16) char lds[2 * kStageBytes];
 
-  const int tile = blockIdx.x / g.n_col_tiles;
-  const int nt = blockIdx.x - tile * g.n_col_tiles;
-  if (tile >= *g.n_tiles) return;
-  const int s = g.tile_slot[tile];
-  const int64_t r0 = g.tile_row0[tile];
+  // ---- which tile: XCD-contiguous runs, grouped raster inside a run --------
+  const int total_m = *g.n_tiles;
+  const int NT = g.n_col_tiles;
+  const int total = total_m * NT;
+  const int b = blockIdx.x;
+  if (b >= total) return;
+  const int xcd = b & 7, q = total >> 3, rem = total & 7;
+  const int l = xcd * q + min(xcd, rem) + (b >> 3);
+  const int grp = l / (kGroupM * NT);
+  const int gsz = min(kGroupM, total_m - grp * kGroupM);
+  const int li = l - grp * kGroupM * NT;
+  const int mt = grp * kGroupM + li % gsz;
+  const int nt = li / gsz;
+
+  const int s = g.tile_slot[mt];
+  const int64_t r0 = g.tile_row0[mt];
   const int64_t rend = min<int64_t>(g.slot_off[s + 1], g.M);
   const int e = g.slot_expert[s];
   if (r0 >= rend || e < 0 || e >= g.E) return;
-  const int n0 = nt * BN;
   const int K = g.K, N = g.N;
+  const int n0 = nt * NSUB;
+  const int m_valid = static_cast<int>(min<int64_t>(kTileM, rend - r0));
+  const int n_valid = min(NSUB, N - n0);
+  const int64_t row_b = static_cast<int64_t>(K) * S;  // bytes per operand row
 
+  const T* A = static_cast<const T*>(g.A) + r0 * K;
+  const __amdgpu_buffer_rsrc_t ra = rsrc(A, m_valid * row_b);
+  const int64_t wofs = (static_cast<int64_t>(e) * N + n0) * K;
+  const __amdgpu_buffer_rsrc_t rb0 = rsrc(static_cast<const T*>(g.B0) + wofs, n_valid * row_b);
+  const __amdgpu_buffer_rsrc_t rb1 =
+      NMAT > 1 ? rsrc(static_cast<const T*>(g.B1) + wofs, n_valid * row_b) : rb0;
+
+  // ---- global -> register staging: 16 x 16 bytes per thread per step ------
   const int tid = threadIdx.x;
   const int lrow = tid >> 3, lchunk = tid & 7;
-  const T* A = static_cast<const T*>(g.A);
-  const T* Bm[2] = {static_cast<const T*>(g.B0) + static_cast<int64_t>(e) * N * K,
-                    NMAT > 1 ? static_cast<const T*>(g.B1) + static_cast<int64_t>(e) * N * K : nullptr};
-  const T* a_src[PA];
-  const T* b_src[NMAT][PB];
+  const int goff = lrow * static_cast<int>(row_b) + lchunk * 16;  // + pass*32 rows + step*128
+  const int pass_b = 32 * static_cast<int>(row_b);
+  const int loff = lrow * kRowBytes + lchunk * 16;
+  uint4 st[16];
+
+  const int nk = K / BK;
+  auto issue = [&](int kt) {
+    const int o = goff + kt * 128;
 #pragma unroll
-  for (int p = 0; p < PA; ++p) {
-    const int64_t r = min<int64_t>(r0 + p * 32 + lrow, rend - 1);
-    a_src[p] = A + r * K + lchunk * EPV;
-  }
+    for (int p = 0; p < 8; ++p) st[p] = bload(ra, o + p * pass_b);
+    if constexpr (NMAT == 2) {
 #pragma unroll
-  for (int m = 0; m < NMAT; ++m)
+      for (int p = 0; p < 4; ++p) st[8 + p] = bload(rb0, o + p * pass_b);
 #pragma unroll
-    for (int p = 0; p < PB; ++p) {
-      const int64_t n = min(n0 + p * 32 + lrow, N - 1);
-      b_src[m][p] = Bm[m] + n * K + lchunk * EPV;
+      for (int p = 0; p < 4; ++p) st[12 + p] = bload(rb1, o + p * pass_b);
+    } else {
+#pragma unroll
+      for (int p = 0; p < 8; ++p) st[8 + p] = bload(rb0, o + p * pass_b);
     }
-
-  uint4 ra[PA], rb[NMAT][PB];
-  auto load = [&](int kt) {
-    const int ko = kt * BK;
-#pragma unroll
-    for (int p = 0; p < PA; ++p) ra[p] = *reinterpret_cast<const uint4*>(a_src[p] + ko);
-#pragma unroll
-    for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-      for (int p = 0; p < PB; ++p) rb[m][p] = *reinterpret_cast<const uint4*>(b_src[m][p] + ko);
   };
-  auto stash = [&]() {
+  auto stash = [&](int stage) {
+    char* base = lds + stage * kStageBytes + loff;
 #pragma unroll
-    for (int p = 0; p < PA; ++p) *reinterpret_cast<uint4*>(&As[(p * 32 + lrow) * LDK + lchunk * EPV]) = ra[p];
-#pragma unroll
-    for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-      for (int p = 0; p < PB; ++p)
-        *reinterpret_cast<uint4*>(&Bs[(m * BN + p * 32 + lrow) * LDK + lchunk * EPV]) = rb[m][p];
+    for (int p = 0; p < 16; ++p) *reinterpret_cast<uint4*>(base + p * 32 * kRowBytes) = st[p];
   };
 
+  // ---- MFMA mapping --------------------------------------------------------
   const int wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
   const int lr = lane & 31, lg = lane >> 5;
-  f32x16 acc[NMAT][TM][TN];
-#pragma unroll
-  for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j) acc[m][i][j] = f32x16{};
+  // B row (within the tile) of N-subtile j for this wave.
+  auto brow = [&](int j) {
+    return NMAT == 2 ? (j >> 1) * 128 + wn * 64 + (j & 1) * 32 : wn * 128 + j * 32;
+  };
+  const int a_rd = (wm * 128 + lr) * kRowBytes + lg * TR::KV * S;
+  const int b_rd0 = (kTileM + brow(0) + lr) * kRowBytes + lg * TR::KV * S;
+  const int b_rd1 = (kTileM + brow(1) + lr) * kRowBytes + lg * TR::KV * S;
+  const int b_rd2 = (kTileM + brow(2) + lr) * kRowBytes + lg * TR::KV * S;
+  const int b_rd3 = (kTileM + brow(3) + lr) * kRowBytes + lg * TR::KV * S;
 
-  const int nk = K / BK;
-  load(0);
-  stash();
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+
+  issue(0);
+  stash(0);
+  if (nk > 1) issue(1);
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) load(kt + 1);
+    const char* sb = lds + (kt & 1) * kStageBytes;
 #pragma unroll
     for (int kk = 0; kk < BK / TR::MK; ++kk) {
-      Frag fa[TM], fb[NMAT][TN];
+      const int ko = kk * TR::MK * S;
+      Frag fa[4], fb[4];
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
-        fa[i] = *reinterpret_cast<const Frag*>(&As[(wm * (BM / 2) + i * 32 + lr) * LDK + kk * TR::MK + lg * TR::KV]);
+      for (int i = 0; i < 4; ++i) fa[i] = *reinterpret_cast<const Frag*>(sb + a_rd + i * 32 * kRowBytes + ko);
+      fb[0] = *reinterpret_cast<const Frag*>(sb + b_rd0 + ko);
+      fb[1] = *reinterpret_cast<const Frag*>(sb + b_rd1 + ko);
+      fb[2] = *reinterpret_cast<const Frag*>(sb + b_rd2 + ko);
+      fb[3] = *reinterpret_cast<const Frag*>(sb + b_rd3 + ko);
 #pragma unroll
-      for (int m = 0; m < NMAT; ++m)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
-          fb[m][j] = *reinterpret_cast<const Frag*>(
-              &Bs[(m * BN + wn * (BN / 2) + j * 32 + lr) * LDK + kk * TR::MK + lg * TR::KV]);
-#pragma unroll
-      for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int j = 0; j < TN; ++j) acc[m][i][j] = mma(fa[i], fb[m][j], acc[m][i][j]);
+        for (int j = 0; j < 4; ++j) acc[i][j] = mma(fa[i], fb[j], acc[i][j]);
     }
+    if (kt + 1 < nk) stash((kt + 1) & 1);
     __syncthreads();
-    if (kt + 1 < nk) {
-      stash();
-      __syncthreads();
-    }
+    if (kt + 2 < nk) issue(kt + 2);
   }
 
-  // Epilogue: lane holds column lr of each 32 x 32 tile, rows 8*(r/4) + 4*lg + r%4.
+  // ---- epilogue: lane holds column lr of each 32 x 32 tile, rows
+  // 8*(r/4) + 4*lg + r%4 --------------------------------------------------
   T* C = static_cast<T*>(g.C);
+  constexpr int JO = NMAT == 2 ? 2 : 4;  // output column subtiles per wave
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int col = n0 + wn * (BN / 2) + j * 32 + lr;
+    for (int j = 0; j < JO; ++j) {
+      const int col = n0 + (NMAT == 2 ? wn * 64 + j * 32 : wn * 128 + j * 32) + lr;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t row = r0 + wm * (BM / 2) + i * 32 + 8 * (r >> 2) + 4 * lg + (r & 3);
-        if (row >= rend || col >= N) continue;
+        const int lrow_out = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * lg + (r & 3);
+        if (lrow_out >= m_valid || col >= N) continue;
         float v;
         if constexpr (EPI == kEpiSwiGLU) {
-          const float gt = acc[0][i][j][r], up = acc[NMAT - 1][i][j][r];
+          const float gt = acc[i][j][r], up = acc[i][j + 2][r];
           v = gt / (1.f + expf(-gt)) * up;
         } else if constexpr (EPI == kEpiGELU) {
-          const float z = acc[0][i][j][r];
+          const float z = acc[i][j][r];
           v = 0.5f * z * (1.f + erff(z * 0.70710678118654752f));
         } else {
-          v = acc[0][i][j][r];
+          v = acc[i][j][r];
         }
-        if constexpr (kBf16) C[row * N + col] = static_cast<uint16_t>(f32_to_bf16_bits(v));
-        else C[row * N + col] = v;
+        const int64_t o = (r0 + lrow_out) * N + col;
+        if constexpr (kBf16) C[o] = static_cast<uint16_t>(f32_to_bf16_bits(v));
+        else C[o] = v;
       }
     }
 }
@@ -250,7 +288,7 @@ __global__ __launch_bounds__(256) void tiles_kernel(const int32_t* __restrict__ 
   if (tid == 0) *n_tiles = min(carry, max_tiles);
 }
 
-constexpr int kBM = 128, kBN = 128;
+constexpr int kBM = kTileM;
 
 struct WsLayout {
   size_t h, tile_slot, tile_row0, n_tiles, bytes;
@@ -270,11 +308,21 @@ WsLayout ws_layout(moe_dtype dt, int64_t M, int I, int max_slots) {
   return w;
 }
 
+// Caller-owned events recorded around the two GEMM launches (profiling only).
+thread_local hipEvent_t g_timing[3] = {nullptr, nullptr, nullptr};
+
+hipError_t mark(int i, hipStream_t s) { return g_timing[i] ? hipEventRecord(g_timing[i], s) : hipSuccess; }
+
 template <bool kBf16>
-void launch_ffn(const GemmArgs& p1, const GemmArgs& p2, bool swiglu, unsigned grid1, unsigned grid2, hipStream_t s) {
-  if (swiglu) gemm_kernel<kBf16, kBM, kBN, 2, kEpiSwiGLU><<<grid1, 256, 0, s>>>(p1);
-  else gemm_kernel<kBf16, kBM, kBN, 1, kEpiGELU><<<grid1, 256, 0, s>>>(p1);
-  gemm_kernel<kBf16, kBM, kBN, 1, kEpiStore><<<grid2, 256, 0, s>>>(p2);
+int launch_ffn(const GemmArgs& p1, const GemmArgs& p2, bool swiglu, unsigned grid1, unsigned grid2, hipStream_t s) {
+  if (int rc = moe::hip_status(mark(0, s), "moe_expert_ffn timing event")) return rc;
+  if (swiglu) gemm_kernel<kBf16, 2, kEpiSwiGLU><<<grid1, 256, 0, s>>>(p1);
+  else gemm_kernel<kBf16, 1, kEpiGELU><<<grid1, 256, 0, s>>>(p1);
+  if (int rc = moe::hip_status(hipGetLastError(), "moe_expert_ffn gate/up launch")) return rc;
+  if (int rc = moe::hip_status(mark(1, s), "moe_expert_ffn timing event")) return rc;
+  gemm_kernel<kBf16, 1, kEpiStore><<<grid2, 256, 0, s>>>(p2);
+  if (int rc = moe::hip_status(hipGetLastError(), "moe_expert_ffn down launch")) return rc;
+  return moe::hip_status(mark(2, s), "moe_expert_ffn timing event");
 }
 
 }  // namespace
@@ -332,7 +380,7 @@ extern "C" int moe_expert_ffn(const void* x_perm, moe_dtype dt, int64_t M, int H
   p1.tile_slot = tile_slot;
   p1.tile_row0 = tile_row0;
   p1.n_tiles = n_tiles;
-  p1.n_col_tiles = static_cast<int>(ceil_div(I, kBN));
+  p1.n_col_tiles = static_cast<int>(ceil_div(I, act == MOE_SWIGLU ? kTileN / 2 : kTileN));
   GemmArgs p2 = p1;
   p2.A = ws + w.h;
   p2.B0 = w_down;
@@ -340,10 +388,19 @@ extern "C" int moe_expert_ffn(const void* x_perm, moe_dtype dt, int64_t M, int H
   p2.C = y_perm;
   p2.K = I;
   p2.N = H;
-  p2.n_col_tiles = static_cast<int>(ceil_div(H, kBN));
+  p2.n_col_tiles = static_cast<int>(ceil_div(H, kTileN));
   const unsigned grid1 = static_cast<unsigned>(w.max_tiles) * p1.n_col_tiles;
   const unsigned grid2 = static_cast<unsigned>(w.max_tiles) * p2.n_col_tiles;
-  if (dt == MOE_BF16) launch_ffn<true>(p1, p2, act == MOE_SWIGLU, grid1, grid2, s);
-  else launch_ffn<false>(p1, p2, act == MOE_SWIGLU, grid1, grid2, s);
-  return hip_status(hipGetLastError(), "moe_expert_ffn launch");
+  if (int rc = hip_status(hipGetLastError(), "moe_expert_ffn tile-table launch")) return rc;
+  return dt == MOE_BF16 ? launch_ffn<true>(p1, p2, act == MOE_SWIGLU, grid1, grid2, s)
+                        : launch_ffn<false>(p1, p2, act == MOE_SWIGLU, grid1, grid2, s);
+}
+
+extern "C" int moe_ffn_set_timing_events(void* before_gateup, void* after_gateup, void* after_down) {
+  const int set = (before_gateup != nullptr) + (after_gateup != nullptr) + (after_down != nullptr);
+  if (set != 0 && set != 3) return moe::fail(MOE_ERR_INVALID_ARG, "moe_ffn_set_timing_events: pass three events or none");
+  g_timing[0] = static_cast<hipEvent_t>(before_gateup);
+  g_timing[1] = static_cast<hipEvent_t>(after_gateup);
+  g_timing[2] = static_cast<hipEvent_t>(after_down);
+  return MOE_OK;
 }
