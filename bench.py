@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--path", default="grouped", choices=["grouped", "dense", "auto"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=96, help="FFN rows the CPU oracle runs (sample)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only copy a 256 MiB buffer 3 times (reference for the HBM byte counters) and exit")
     return ap.parse_args()
 
 
@@ -124,6 +126,16 @@ def main():
     import numpy as np
     import torch
 
+    if a.calibrate_copy:
+        x = torch.empty(64 << 20, dtype=torch.float32, device="cuda")
+        y = torch.empty_like(x)
+        x.fill_(1.0)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "copied 268435456 bytes 3 times"}))
+        return
+
     import mixture_experts_routing_top_amd as moe
     import synth
 
@@ -181,26 +193,29 @@ def main():
     gateup_ms = float(np.mean([ev[i][0].elapsed_time(ev[i][1]) for i in range(a.steps)]))
     down_ms = float(np.mean([ev[i][1].elapsed_time(ev[i][2]) for i in range(a.steps)]))
 
-    # Per-phase split (diagnostic, outside the timed region).
-    phase_ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
-    res = None
-    torch.cuda.synchronize()
-    phase_ev[0].record(stream)
-    idx, w = moe.moe_route(logits, k, bufs["idx"], bufs["w"], stream)
-    phase_ev[1].record(stream)
-    moe.moe_stats(state, L, E, win, 1, 10 ** 6, idx, prev_idx, k, bufs["counts"], bufs["p_seq"], bufs["cond"],
-                  bufs["pred_next"], R, bufs["replicas"], stream)
-    phase_ev[2].record(stream)
-    d = moe.moe_dispatch(x, idx, E, bufs["replicas"], E + R, bufs["disp"], bufs["ws_d"], stream)
-    phase_ev[3].record(stream)
-    y = moe.moe_expert_ffn(d["x_perm"], d["slot_off"], d["slot_expert"], d["n_slots"], wg, wu, wd, "swiglu",
-                           a.path, bufs["y_perm"], bufs["ws_f"], stream)
-    phase_ev[4].record(stream)
-    moe.moe_combine(y, d["inv_pos"], w, bufs["out"], stream)
-    phase_ev[5].record(stream)
-    torch.cuda.synchronize()
+    # Per-phase split (diagnostic, outside the timed region): median of 5 passes.
     names = ["route", "stats", "dispatch", "expert_ffn", "combine"]
-    phase_us = {n: round(phase_ev[j].elapsed_time(phase_ev[j + 1]) * 1e3, 2) for j, n in enumerate(names)}
+    samples = {n: [] for n in names}
+    for rep in range(5):
+        phase_ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        torch.cuda.synchronize()
+        phase_ev[0].record(stream)
+        idx, w = moe.moe_route(logits, k, bufs["idx"], bufs["w"], stream)
+        phase_ev[1].record(stream)
+        moe.moe_stats(state, L, E, win, 1, 10 ** 6 + rep, idx, prev_idx, k, bufs["counts"], bufs["p_seq"],
+                      bufs["cond"], bufs["pred_next"], R, bufs["replicas"], stream)
+        phase_ev[2].record(stream)
+        d = moe.moe_dispatch(x, idx, E, bufs["replicas"], E + R, bufs["disp"], bufs["ws_d"], stream)
+        phase_ev[3].record(stream)
+        y = moe.moe_expert_ffn(d["x_perm"], d["slot_off"], d["slot_expert"], d["n_slots"], wg, wu, wd, "swiglu",
+                               a.path, bufs["y_perm"], bufs["ws_f"], stream)
+        phase_ev[4].record(stream)
+        moe.moe_combine(y, d["inv_pos"], w, bufs["out"], stream)
+        phase_ev[5].record(stream)
+        torch.cuda.synchronize()
+        for j, n in enumerate(names):
+            samples[n].append(phase_ev[j].elapsed_time(phase_ev[j + 1]) * 1e3)
+    phase_us = {n: round(float(np.median(v)), 2) for n, v in samples.items()}
     n_slots = int(d["n_slots"].item())
 
     flops, w_bytes, mem = algorithmic_layer_work(T, H, I, E, k, 3)

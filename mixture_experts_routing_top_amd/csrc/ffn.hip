@@ -189,30 +189,85 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
+  constexpr int KS = BK / TR::MK;  // MFMA sub-steps per K step
+  static_assert(KS == 4 || KS == 16, "unexpected K split");
+  Frag fa[2][4], fb[2][4];
+  auto frags = [&](const char* sb, int kk, int buf) {
+    const int ko = kk * TR::MK * S;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[buf][i] = *reinterpret_cast<const Frag*>(sb + a_rd + i * 32 * kRowBytes + ko);
+    fb[buf][0] = *reinterpret_cast<const Frag*>(sb + b_rd0 + ko);
+    fb[buf][1] = *reinterpret_cast<const Frag*>(sb + b_rd1 + ko);
+    fb[buf][2] = *reinterpret_cast<const Frag*>(sb + b_rd2 + ko);
+    fb[buf][3] = *reinterpret_cast<const Frag*>(sb + b_rd3 + ko);
+  };
+  auto mfmas = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = mma(fa[buf][i], fb[buf][j], acc[i][j]);
+  };
+  // out-of-range offset: the buffer load returns zeros without touching memory
+  auto issue_one = [&](int p, int o) {
+    if constexpr (NMAT == 2) {
+      if (p < 8) st[p] = bload(ra, o + p * pass_b);
+      else if (p < 12) st[p] = bload(rb0, o + (p - 8) * pass_b);
+      else st[p] = bload(rb1, o + (p - 12) * pass_b);
+    } else {
+      st[p] = p < 8 ? bload(ra, o + p * pass_b) : bload(rb0, o + (p - 8) * pass_b);
+    }
+  };
+
   issue(0);
   stash(0);
   if (nk > 1) issue(1);
   __syncthreads();
+  frags(lds, 0, 0);
   for (int kt = 0; kt < nk; ++kt) {
     const char* sb = lds + (kt & 1) * kStageBytes;
+    char* wb = lds + ((kt + 1) & 1) * kStageBytes + loff;
+    const int o2 = (kt + 2 < nk) ? goff + (kt + 2) * 128 : 0x7ffff000;
+    // sub-steps 0 .. KS-2: MFMAs + next fragments + LDS writes of step kt+1 + loads of step kt+2
 #pragma unroll
-    for (int kk = 0; kk < BK / TR::MK; ++kk) {
-      const int ko = kk * TR::MK * S;
-      Frag fa[4], fb[4];
+    for (int kk = 0; kk < KS - 1; ++kk) {
+      constexpr int PER = (16 + KS - 2) / (KS - 1);
+      frags(sb, kk + 1, (kk + 1) & 1);
+      mfmas(kk & 1);
+      int nw = 0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) fa[i] = *reinterpret_cast<const Frag*>(sb + a_rd + i * 32 * kRowBytes + ko);
-      fb[0] = *reinterpret_cast<const Frag*>(sb + b_rd0 + ko);
-      fb[1] = *reinterpret_cast<const Frag*>(sb + b_rd1 + ko);
-      fb[2] = *reinterpret_cast<const Frag*>(sb + b_rd2 + ko);
-      fb[3] = *reinterpret_cast<const Frag*>(sb + b_rd3 + ko);
+      for (int p = kk * PER; p < (kk + 1) * PER && p < 16; ++p) {
+        *reinterpret_cast<uint4*>(wb + p * 32 * kRowBytes) = st[p];
+        issue_one(p, o2);
+        ++nw;
+      }
+      // interleave: 8 x (fragment read, MFMA), nw x (LDS write, global load, MFMA), rest MFMA
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int t = 0; t < 8; ++t) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mma(fa[i], fb[j], acc[i][j]);
+      for (int t = 0; t < 8; ++t) {
+        if (t < nw) {
+          __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (kt + 1 < nk) stash((kt + 1) & 1);
     __syncthreads();
-    if (kt + 2 < nk) issue(kt + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    // last sub-step: its fragments are in registers; fetch the next step's first ones
+    frags(lds + ((kt + 1) & 1) * kStageBytes, 0, KS & 1);
+    mfmas((KS - 1) & 1);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // ---- epilogue: lane holds column lr of each 32 x 32 tile, rows
