@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--path", default="grouped", choices=["grouped", "dense", "auto"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=96, help="FFN rows the CPU oracle runs (sample)")
+    ap.add_argument("--crossover", action="store_true",
+                    help="time the grouped and the dense expert-FFN paths on the DeepSeek-V2 T sweep and on the "
+                         "GEMM shapes profiled by EPS-MoE, print one JSON line per case, and exit")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only copy a 256 MiB buffer 3 times (reference for the HBM byte counters) and exit")
     return ap.parse_args()
@@ -116,6 +119,69 @@ def cpu_baseline(cfg, x, logits, wts, prev_idx_np, rows):
                        f"({per_row:.3f} s/row); measured CPU time {t_mem + t_rows + t_comb:.1f} s")}
 
 
+def crossover(moe, synth, torch, np):
+    """Grouped (256-row tiles) vs dense padded (64-row tiles) expert FFN.  Routing
+    and slot tables come from the seeded generators; weights and activations are
+    random device tensors (values do not change the timing)."""
+    dev = torch.device("cuda:0")
+    torch.manual_seed(0)
+    lib = moe.lib()
+
+    def time_paths(x_perm, slot_off, slot_expert, n_slots, wg, wu, wd, label, extra):
+        M, H = x_perm.shape
+        I = wg.shape[1]
+        ws = torch.empty(moe.moe_expert_ffn_workspace_bytes(x_perm.dtype, M, H, I, slot_expert.numel()),
+                         dtype=torch.uint8, device=dev)
+        y = torch.empty_like(x_perm)
+        res = dict(case=label, **extra)
+        for path in ("grouped", "dense", "auto"):
+            for _ in range(2):
+                moe.moe_expert_ffn(x_perm, slot_off, slot_expert, n_slots, wg, wu, wd, "swiglu", path, y, ws)
+            torch.cuda.synchronize()
+            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(5)]
+            for tr in ev:
+                for e in tr:
+                    e.record()
+            torch.cuda.synchronize()
+            for i in range(5):
+                lib.moe_ffn_set_timing_events(*(ev[i][j].cuda_event for j in range(3)))
+                moe.moe_expert_ffn(x_perm, slot_off, slot_expert, n_slots, wg, wu, wd, "swiglu", path, y, ws)
+            torch.cuda.synchronize()
+            lib.moe_ffn_set_timing_events(None, None, None)
+            g = float(np.median([ev[i][0].elapsed_time(ev[i][1]) for i in range(5)]))
+            d = float(np.median([ev[i][1].elapsed_time(ev[i][2]) for i in range(5)]))
+            res[path] = {"gateup_ms": round(g, 4), "down_ms": round(d, 4), "ffn_ms": round(g + d, 4)}
+        # which path AUTO takes (it reads the slot sizes back): compare its output timing-free
+        res["faster"] = min(("grouped", "dense"), key=lambda p: res[p]["ffn_ms"])
+        print(json.dumps(res), flush=True)
+
+    cfg0 = synth.CONFIGS["dsv2"]
+    E, H, I, k = cfg0.E, cfg0.H, cfg0.I, cfg0.k
+    wg = (torch.randn(E, I, H, device=dev) * H ** -0.5).to(torch.bfloat16)
+    wu = (torch.randn(E, I, H, device=dev) * H ** -0.5).to(torch.bfloat16)
+    wd = (torch.randn(E, H, I, device=dev) * I ** -0.5).to(torch.bfloat16)
+    for T in synth.DSV2_T_SWEEP:
+        cfg = cfg0.with_T(T)
+        idx, _ = moe.moe_route(torch.from_numpy(synth.logits(cfg, 0, 0)).to(dev), k)
+        x = torch.randn(T, H, device=dev).to(torch.bfloat16)
+        d = moe.moe_dispatch(x, idx, E, None, E)
+        counts = np.diff(d["expert_off"].cpu().numpy())
+        time_paths(d["x_perm"], d["slot_off"], d["slot_expert"], d["n_slots"], wg, wu, wd, f"dsv2_T{T}",
+                   {"E": E, "k": k, "H": H, "I": I, "rows": int(T * k), "max_rows": int(counts.max()),
+                    "mean_rows": round(float(counts.mean()), 1), "empty_experts": int((counts == 0).sum())})
+    del wg, wu, wd
+    # single-expert GEMM shapes M x K x N printed by EPS-MoE (K = H; N = I of one projection)
+    for M, K_, N_ in ((512, 5120, 1536), (2048, 5120, 1536), (512, 5120, 14336)):
+        x = torch.randn(M, K_, device=dev).to(torch.bfloat16)
+        g1 = (torch.randn(1, N_, K_, device=dev) * K_ ** -0.5).to(torch.bfloat16)
+        u1 = (torch.randn(1, N_, K_, device=dev) * K_ ** -0.5).to(torch.bfloat16)
+        d1 = (torch.randn(1, K_, N_, device=dev) * N_ ** -0.5).to(torch.bfloat16)
+        so = torch.tensor([0, M], dtype=torch.int32, device=dev)
+        se = torch.zeros(1, dtype=torch.int32, device=dev)
+        ns = torch.ones(1, dtype=torch.int32, device=dev)
+        time_paths(x, so, se, ns, g1, u1, d1, f"gemm_{M}x{K_}x{N_}", {"M": M, "K": K_, "N": N_})
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -138,6 +204,10 @@ def main():
 
     import mixture_experts_routing_top_amd as moe
     import synth
+
+    if a.crossover:
+        crossover(moe, synth, torch, np)
+        return
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

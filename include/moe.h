@@ -163,12 +163,17 @@ int moe_dispatch(const void* x, moe_dtype dt, int64_t T, int H, const int32_t* t
  * row's result depends only on that row: it is the same whichever slot, tile
  * or path computes it (fixed reduction order, no split-K), so replicated and
  * non-replicated dispatches give bit-identical y_perm.
- *   path  GROUPED: tiles cover each slot's rows exactly (no host sync).
- *         DENSE:   every slot padded to the largest slot's row count, run as
- *                  one uniform batch; reads the slot table back to the host
- *                  (synchronises `stream`).
- *         AUTO:    reads the slot table back and picks DENSE when the
- *                  largest slot is small, else GROUPED.
+ *   path  GROUPED: 256-row tiles cover each slot's rows exactly (no host
+ *                  sync): the large-batch form.
+ *         DENSE:   every slot with rows is padded to the largest slot's row
+ *                  count (rounded up to 64) and the uniform batch runs in
+ *                  64-row tiles; tiles wholly in the padding exit at once.
+ *                  Reads the slot table back (synchronises `stream`).
+ *         AUTO:    reads the slot table back and picks per GEMM: DENSE when
+ *                  the grouped grid would leave over a quarter of the 256 CUs
+ *                  idle and at most half of the padded batch is padding,
+ *                  else GROUPED.
+ *         All paths give bit-identical y_perm.
  *   workspace  at least moe_expert_ffn_workspace_bytes(...) bytes.
  * Limits: dtype F32 or BF16; H and I multiples of 64; E <= max_slots;
  * M <= 2^31 - 1; rows referenced by slot_off lie in [0, M).

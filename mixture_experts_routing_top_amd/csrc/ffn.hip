@@ -30,6 +30,9 @@
 // neighbouring blocks share inside that XCD's L2.  Each output row depends
 // only on its own input row and the fixed K order, so a row's value does not
 // depend on the tile, slot or path that computes it.
+#include <algorithm>
+#include <vector>
+
 #include "common.h"
 
 namespace {
@@ -67,10 +70,8 @@ __device__ __forceinline__ f32x16 mma(float a, float b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
-constexpr int kTileM = 256;      // rows per tile
 constexpr int kTileN = 256;      // weight rows per tile (gate/up: 128 + 128)
 constexpr int kRowBytes = 144;   // LDS row pitch: 128 data bytes + 16 pad
-constexpr int kStageBytes = (kTileM + kTileN) * kRowBytes;
 constexpr int kGroupM = 8;       // row tiles per raster group
 
 struct GemmArgs {
@@ -98,14 +99,27 @@ __device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, int off) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-template <bool kBf16, int NMAT, int EPI>
+// BM rows x 256 weight rows per block; the 4 waves form a WM x (4/WM) grid.
+// BM = 256, WM = 2: each wave owns 128 x 128 (4 x 4 MFMA tiles).
+// BM = 64,  WM = 1: each wave owns  64 x 64  (2 x 2 MFMA tiles).
+template <bool kBf16, int NMAT, int EPI, int BM, int WM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_kernel(GemmArgs g) {
   using TR = Tr<kBf16>;
   using T = typename TR::T;
   using Frag = typename TR::Frag;
   constexpr int S = sizeof(T);
   constexpr int BK = TR::BK;
-  constexpr int NSUB = kTileN / NMAT;  // output columns per tile
+  constexpr int KS = BK / TR::MK;          // MFMA sub-steps per K step
+  constexpr int NSUB = kTileN / NMAT;      // output columns per tile
+  constexpr int WN = 4 / WM;
+  constexpr int TM = BM / WM / 32;         // MFMA tiles per wave along M
+  constexpr int TN = kTileN / WN / 32;     // ... along the weight rows
+  constexpr int PA = BM / 32;              // 16-byte load passes for A (32 rows each)
+  constexpr int P = PA + kTileN / 32;      // passes per K step
+  constexpr int NR = TM + TN;              // fragment reads per sub-step
+  constexpr int NM = TM * TN;              // MFMAs per sub-step
+  constexpr int kStageBytes = (BM + kTileN) * kRowBytes;
+  static_assert(NM >= NR, "sub-step pattern assumes at least one MFMA per fragment read");
   __shared__ __align__(16) char lds[2 * kStageBytes];
 
   // ---- which tile: XCD-contiguous runs, grouped raster inside a run --------
@@ -129,7 +143,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   if (r0 >= rend || e < 0 || e >= g.E) return;
   const int K = g.K, N = g.N;
   const int n0 = nt * NSUB;
-  const int m_valid = static_cast<int>(min<int64_t>(kTileM, rend - r0));
+  const int m_valid = static_cast<int>(min<int64_t>(BM, rend - r0));
   const int n_valid = min(NSUB, N - n0);
   const int64_t row_b = static_cast<int64_t>(K) * S;  // bytes per operand row
 
@@ -140,84 +154,66 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const __amdgpu_buffer_rsrc_t rb1 =
       NMAT > 1 ? rsrc(static_cast<const T*>(g.B1) + wofs, n_valid * row_b) : rb0;
 
-  // ---- global -> register staging: 16 x 16 bytes per thread per step ------
+  // ---- global -> register staging: P x 16 bytes per thread per step -------
+  // pass p < PA: A rows 32p..; then 8 passes of weight rows (gate/up: 4 + 4)
   const int tid = threadIdx.x;
   const int lrow = tid >> 3, lchunk = tid & 7;
   const int goff = lrow * static_cast<int>(row_b) + lchunk * 16;  // + pass*32 rows + step*128
   const int pass_b = 32 * static_cast<int>(row_b);
   const int loff = lrow * kRowBytes + lchunk * 16;
-  uint4 st[16];
-
-  const int nk = K / BK;
+  uint4 st[P];
+  auto issue_one = [&](int p, int o) {
+    if (p < PA) st[p] = bload(ra, o + p * pass_b);
+    else if (NMAT == 1 || p < PA + 4) st[p] = bload(rb0, o + (p - PA) * pass_b);
+    else st[p] = bload(rb1, o + (p - PA - 4) * pass_b);
+  };
   auto issue = [&](int kt) {
-    const int o = goff + kt * 128;
 #pragma unroll
-    for (int p = 0; p < 8; ++p) st[p] = bload(ra, o + p * pass_b);
-    if constexpr (NMAT == 2) {
-#pragma unroll
-      for (int p = 0; p < 4; ++p) st[8 + p] = bload(rb0, o + p * pass_b);
-#pragma unroll
-      for (int p = 0; p < 4; ++p) st[12 + p] = bload(rb1, o + p * pass_b);
-    } else {
-#pragma unroll
-      for (int p = 0; p < 8; ++p) st[8 + p] = bload(rb0, o + p * pass_b);
-    }
+    for (int p = 0; p < P; ++p) issue_one(p, goff + kt * 128);
   };
   auto stash = [&](int stage) {
     char* base = lds + stage * kStageBytes + loff;
 #pragma unroll
-    for (int p = 0; p < 16; ++p) *reinterpret_cast<uint4*>(base + p * 32 * kRowBytes) = st[p];
+    for (int p = 0; p < P; ++p) *reinterpret_cast<uint4*>(base + p * 32 * kRowBytes) = st[p];
   };
 
   // ---- MFMA mapping --------------------------------------------------------
   const int wave = tid >> 6, lane = tid & 63;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
   const int lr = lane & 31, lg = lane >> 5;
-  // B row (within the tile) of N-subtile j for this wave.
+  constexpr int CW = kTileN / WN;  // weight rows per wave
+  // weight row (within the tile) of this wave's N-subtile j; with gate and up
+  // side by side, subtiles 0 .. TN/2-1 are gate rows, the rest the same up rows
   auto brow = [&](int j) {
-    return NMAT == 2 ? (j >> 1) * 128 + wn * 64 + (j & 1) * 32 : wn * 128 + j * 32;
+    return NMAT == 2 ? (j / (TN / 2)) * 128 + wn * (CW / 2) + (j % (TN / 2)) * 32 : wn * CW + j * 32;
   };
-  const int a_rd = (wm * 128 + lr) * kRowBytes + lg * TR::KV * S;
-  const int b_rd0 = (kTileM + brow(0) + lr) * kRowBytes + lg * TR::KV * S;
-  const int b_rd1 = (kTileM + brow(1) + lr) * kRowBytes + lg * TR::KV * S;
-  const int b_rd2 = (kTileM + brow(2) + lr) * kRowBytes + lg * TR::KV * S;
-  const int b_rd3 = (kTileM + brow(3) + lr) * kRowBytes + lg * TR::KV * S;
-
-  f32x16 acc[4][4];
+  const int a_rd = (wm * (BM / WM) + lr) * kRowBytes + lg * TR::KV * S;
+  int b_rd[TN];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+  for (int j = 0; j < TN; ++j) b_rd[j] = (BM + brow(j) + lr) * kRowBytes + lg * TR::KV * S;
 
-  constexpr int KS = BK / TR::MK;  // MFMA sub-steps per K step
-  static_assert(KS == 4 || KS == 16, "unexpected K split");
-  Frag fa[2][4], fb[2][4];
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
+
+  Frag fa[2][TM], fb[2][TN];
   auto frags = [&](const char* sb, int kk, int buf) {
     const int ko = kk * TR::MK * S;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fa[buf][i] = *reinterpret_cast<const Frag*>(sb + a_rd + i * 32 * kRowBytes + ko);
-    fb[buf][0] = *reinterpret_cast<const Frag*>(sb + b_rd0 + ko);
-    fb[buf][1] = *reinterpret_cast<const Frag*>(sb + b_rd1 + ko);
-    fb[buf][2] = *reinterpret_cast<const Frag*>(sb + b_rd2 + ko);
-    fb[buf][3] = *reinterpret_cast<const Frag*>(sb + b_rd3 + ko);
+    for (int i = 0; i < TM; ++i) fa[buf][i] = *reinterpret_cast<const Frag*>(sb + a_rd + i * 32 * kRowBytes + ko);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) fb[buf][j] = *reinterpret_cast<const Frag*>(sb + b_rd[j] + ko);
   };
   auto mfmas = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mma(fa[buf][i], fb[buf][j], acc[i][j]);
-  };
-  // out-of-range offset: the buffer load returns zeros without touching memory
-  auto issue_one = [&](int p, int o) {
-    if constexpr (NMAT == 2) {
-      if (p < 8) st[p] = bload(ra, o + p * pass_b);
-      else if (p < 12) st[p] = bload(rb0, o + (p - 8) * pass_b);
-      else st[p] = bload(rb1, o + (p - 12) * pass_b);
-    } else {
-      st[p] = p < 8 ? bload(ra, o + p * pass_b) : bload(rb0, o + (p - 8) * pass_b);
-    }
+      for (int j = 0; j < TN; ++j) acc[i][j] = mma(fa[buf][i], fb[buf][j], acc[i][j]);
   };
 
+  const int nk = K / BK;
   issue(0);
   stash(0);
   if (nk > 1) issue(1);
@@ -226,33 +222,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   for (int kt = 0; kt < nk; ++kt) {
     const char* sb = lds + (kt & 1) * kStageBytes;
     char* wb = lds + ((kt + 1) & 1) * kStageBytes + loff;
+    // past the last step the offset is out of range: the loads return zeros
+    // without touching memory
     const int o2 = (kt + 2 < nk) ? goff + (kt + 2) * 128 : 0x7ffff000;
     // sub-steps 0 .. KS-2: MFMAs + next fragments + LDS writes of step kt+1 + loads of step kt+2
 #pragma unroll
     for (int kk = 0; kk < KS - 1; ++kk) {
-      constexpr int PER = (16 + KS - 2) / (KS - 1);
+      constexpr int PER = (P + KS - 2) / (KS - 1);
       frags(sb, kk + 1, (kk + 1) & 1);
       mfmas(kk & 1);
       int nw = 0;
 #pragma unroll
-      for (int p = kk * PER; p < (kk + 1) * PER && p < 16; ++p) {
+      for (int p = kk * PER; p < (kk + 1) * PER && p < P; ++p) {
         *reinterpret_cast<uint4*>(wb + p * 32 * kRowBytes) = st[p];
         issue_one(p, o2);
         ++nw;
       }
-      // interleave: 8 x (fragment read, MFMA), nw x (LDS write, global load, MFMA), rest MFMA
+      // interleave: NR x (fragment read, MFMA), then (LDS write, global load,
+      // MFMA) while MFMAs last, then the remaining writes/loads and MFMAs
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
+      for (int t = 0; t < NR; ++t) {
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       }
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
+      for (int t = 0; t < NM - NR || t < PER; ++t) {
         if (t < nw) {
           __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (t < NM - NR) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -262,30 +261,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     frags(lds + ((kt + 1) & 1) * kStageBytes, 0, KS & 1);
     mfmas((KS - 1) & 1);
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
+    for (int t = 0; t < NR; ++t) {
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
     __builtin_amdgcn_sched_barrier(0);
   }
 
   // ---- epilogue: lane holds column lr of each 32 x 32 tile, rows
   // 8*(r/4) + 4*lg + r%4 --------------------------------------------------
   T* C = static_cast<T*>(g.C);
-  constexpr int JO = NMAT == 2 ? 2 : 4;  // output column subtiles per wave
+  constexpr int JO = NMAT == 2 ? TN / 2 : TN;  // output column subtiles per wave
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < JO; ++j) {
-      const int col = n0 + (NMAT == 2 ? wn * 64 + j * 32 : wn * 128 + j * 32) + lr;
+      const int col = n0 + (NMAT == 2 ? wn * (CW / 2) : wn * CW) + j * 32 + lr;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int lrow_out = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * lg + (r & 3);
+        const int lrow_out = wm * (BM / WM) + i * 32 + 8 * (r >> 2) + 4 * lg + (r & 3);
         if (lrow_out >= m_valid || col >= N) continue;
         float v;
         if constexpr (EPI == kEpiSwiGLU) {
-          const float gt = acc[i][j][r], up = acc[i][j + 2][r];
+          const float gt = acc[i][j][r], up = acc[i][j + TN / 2][r];
           v = gt / (1.f + expf(-gt)) * up;
         } else if constexpr (EPI == kEpiGELU) {
           const float z = acc[i][j][r];
@@ -300,11 +299,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
 }
 
-// Lists every (slot, row tile) of the grouped path: tile rows start at the
-// slot's first row and step by BM; the last tile of a slot may be partial.
+// Lists the row tiles of the GEMMs.  Grouped (m_pad == 0): each slot's rows
+// are covered from its first row in steps of BM; the last tile of a slot may
+// be partial.  Dense (m_pad > 0): every slot with rows gets m_pad / BM tiles,
+// the uniform padded batch; tiles wholly past the slot's last row exit as soon
+// as the GEMM reads them.
 __global__ __launch_bounds__(256) void tiles_kernel(const int32_t* __restrict__ slot_off,
                                                     const int32_t* __restrict__ n_slots_p, int max_slots, int64_t M,
-                                                    int BM, int max_tiles, int32_t* __restrict__ tile_slot,
+                                                    int BM, int m_pad, int max_tiles, int32_t* __restrict__ tile_slot,
                                                     int32_t* __restrict__ tile_row0, int32_t* __restrict__ n_tiles) {
   __shared__ int32_t scan[256];
   __shared__ int32_t carry;
@@ -318,7 +320,7 @@ __global__ __launch_bounds__(256) void tiles_kernel(const int32_t* __restrict__ 
     if (s < n) {
       start = min<int64_t>(max(slot_off[s], 0), M);
       const int64_t end = min<int64_t>(max(slot_off[s + 1], 0), M);
-      cnt = end > start ? (end - start + BM - 1) / BM : 0;
+      if (end > start) cnt = m_pad > 0 ? m_pad / BM : (end - start + BM - 1) / BM;
     }
     scan[tid] = static_cast<int32_t>(cnt);
     __syncthreads();
@@ -333,7 +335,7 @@ __global__ __launch_bounds__(256) void tiles_kernel(const int32_t* __restrict__ 
       const int j = first + q;
       if (j < max_tiles) {
         tile_slot[j] = s;
-        tile_row0[j] = static_cast<int32_t>(start + static_cast<int64_t>(q) * BM);
+        tile_row0[j] = static_cast<int32_t>(min<int64_t>(start + static_cast<int64_t>(q) * BM, M));
       }
     }
     __syncthreads();
@@ -343,22 +345,31 @@ __global__ __launch_bounds__(256) void tiles_kernel(const int32_t* __restrict__ 
   if (tid == 0) *n_tiles = min(carry, max_tiles);
 }
 
-constexpr int kBM = kTileM;
+constexpr int kBigM = 256;    // grouped path: 256-row tiles
+constexpr int kSmallM = 64;   // dense path: 64-row tiles
 
 struct WsLayout {
-  size_t h, tile_slot, tile_row0, n_tiles, bytes;
-  int max_tiles;
+  size_t h, big_slot, big_row0, small_slot, small_row0, n_tiles, bytes;
+  int max_big, max_small;
 };
 
+// Two tile tables: 256-row tiles (at most ceil(M/256) + slots) and 64-row tiles
+// of the dense padded batch (at most slots x ceil(largest slot / 64), and the
+// largest slot has at most M rows).
 WsLayout ws_layout(moe_dtype dt, int64_t M, int I, int max_slots) {
   WsLayout w{};
-  w.max_tiles = static_cast<int>(moe::ceil_div(M, kBM) + max_slots);
+  const int64_t big = moe::ceil_div(M, kBigM) + max_slots;
+  const int64_t small = static_cast<int64_t>(max_slots) * moe::ceil_div(std::max<int64_t>(M, 1), kSmallM);
+  w.max_big = static_cast<int>(std::min<int64_t>(big, 0x3fffffff));
+  w.max_small = static_cast<int>(std::min<int64_t>(small, 0x3fffffff));
   size_t at = 0;
   auto take = [&](size_t n) { size_t p = at; at = moe::align_up(at + n, 256); return p; };
   w.h = take(static_cast<size_t>(M) * I * moe::elem_bytes(dt));
-  w.tile_slot = take(sizeof(int32_t) * w.max_tiles);
-  w.tile_row0 = take(sizeof(int32_t) * w.max_tiles);
-  w.n_tiles = take(sizeof(int32_t));
+  w.big_slot = take(sizeof(int32_t) * w.max_big);
+  w.big_row0 = take(sizeof(int32_t) * w.max_big);
+  w.small_slot = take(sizeof(int32_t) * w.max_small);
+  w.small_row0 = take(sizeof(int32_t) * w.max_small);
+  w.n_tiles = take(2 * sizeof(int32_t));
   w.bytes = at;
   return w;
 }
@@ -368,16 +379,32 @@ thread_local hipEvent_t g_timing[3] = {nullptr, nullptr, nullptr};
 
 hipError_t mark(int i, hipStream_t s) { return g_timing[i] ? hipEventRecord(g_timing[i], s) : hipSuccess; }
 
+template <bool kBf16, int EPI, int NMAT>
+void launch_gemm(bool small, const GemmArgs& p, unsigned grid, hipStream_t s) {
+  if (small) gemm_kernel<kBf16, NMAT, EPI, kSmallM, 1><<<grid, 256, 0, s>>>(p);
+  else gemm_kernel<kBf16, NMAT, EPI, kBigM, 2><<<grid, 256, 0, s>>>(p);
+}
+
+// Phase 1 (gate/up or W1) and phase 2 (down or W2), each on its own tile table.
 template <bool kBf16>
-int launch_ffn(const GemmArgs& p1, const GemmArgs& p2, bool swiglu, unsigned grid1, unsigned grid2, hipStream_t s) {
+int launch_ffn(const GemmArgs& p1, bool small1, unsigned grid1, const GemmArgs& p2, bool small2, unsigned grid2,
+               bool swiglu, hipStream_t s) {
   if (int rc = moe::hip_status(mark(0, s), "moe_expert_ffn timing event")) return rc;
-  if (swiglu) gemm_kernel<kBf16, 2, kEpiSwiGLU><<<grid1, 256, 0, s>>>(p1);
-  else gemm_kernel<kBf16, 1, kEpiGELU><<<grid1, 256, 0, s>>>(p1);
+  if (swiglu) launch_gemm<kBf16, kEpiSwiGLU, 2>(small1, p1, grid1, s);
+  else launch_gemm<kBf16, kEpiGELU, 1>(small1, p1, grid1, s);
   if (int rc = moe::hip_status(hipGetLastError(), "moe_expert_ffn gate/up launch")) return rc;
   if (int rc = moe::hip_status(mark(1, s), "moe_expert_ffn timing event")) return rc;
-  gemm_kernel<kBf16, 1, kEpiStore><<<grid2, 256, 0, s>>>(p2);
+  launch_gemm<kBf16, kEpiStore, 1>(small2, p2, grid2, s);
   if (int rc = moe::hip_status(hipGetLastError(), "moe_expert_ffn down launch")) return rc;
   return moe::hip_status(mark(2, s), "moe_expert_ffn timing event");
+}
+
+// AUTO rule, per GEMM: take the dense padded batch when the grouped grid would
+// leave more than a quarter of the 256 CUs idle and at most half of the padded
+// batch's tiles are padding.
+constexpr int kComputeUnits = 256;
+bool prefer_dense(int64_t grouped_tiles, int64_t dense_tiles, int64_t dense_real_tiles, int col_tiles) {
+  return grouped_tiles * col_tiles * 4 < 3 * kComputeUnits && 2 * dense_real_tiles >= dense_tiles;
 }
 
 }  // namespace
@@ -401,6 +428,8 @@ extern "C" int moe_expert_ffn(const void* x_perm, moe_dtype dt, int64_t M, int H
   if (M < 0 || M >= (int64_t(1) << 31)) return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn: M out of range");
   if (H < 64 || I < 64 || H % 64 || I % 64)
     return fail(MOE_ERR_UNSUPPORTED, "moe_expert_ffn: H and I must be positive multiples of 64 (H=%d I=%d)", H, I);
+  if (static_cast<int64_t>(std::max(H, I)) * elem_bytes(dt) * kBigM >= (int64_t(1) << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "moe_expert_ffn: H or I too large for 32-bit tile offsets");
   if (E < 1 || max_slots < E) return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn: need 1 <= E <= max_slots");
   if (act == MOE_SWIGLU && !w_up) return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn: SwiGLU needs w_up");
   if (act == MOE_GELU && w_up) return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn: GELU takes no w_up (pass NULL)");
@@ -415,11 +444,55 @@ extern "C" int moe_expert_ffn(const void* x_perm, moe_dtype dt, int64_t M, int H
   if (M == 0) return MOE_OK;
 
   const hipStream_t s = as_stream(stream);
+  const int nt1 = static_cast<int>(ceil_div(I, act == MOE_SWIGLU ? kTileN / 2 : kTileN));
+  const int nt2 = static_cast<int>(ceil_div(H, kTileN));
+  // GROUPED: 256-row tiles for both GEMMs.  DENSE: the padded batch in 64-row
+  // tiles for both.  AUTO: per GEMM, from the slot sizes read back here.
+  bool small1 = path == MOE_GEMM_DENSE, small2 = small1;
+  int m_pad = 0;
+  int64_t dense_tiles = 0;
+  if (path != MOE_GEMM_GROUPED) {
+    std::vector<int32_t> off(static_cast<size_t>(max_slots) + 2);
+    if (int rc = hip_status(hipMemcpyAsync(off.data(), slot_off, sizeof(int32_t) * (max_slots + 1),
+                                           hipMemcpyDeviceToHost, s), "moe_expert_ffn slot readback")) return rc;
+    if (int rc = hip_status(hipMemcpyAsync(&off[max_slots + 1], n_slots, sizeof(int32_t), hipMemcpyDeviceToHost, s),
+                            "moe_expert_ffn slot readback")) return rc;
+    if (int rc = hip_status(hipStreamSynchronize(s), "moe_expert_ffn slot readback")) return rc;
+    const int n = std::min(std::max(off[max_slots + 1], 0), max_slots);
+    int64_t largest = 0, active = 0, big_tiles = 0, small_real = 0;
+    for (int i = 0; i < n; ++i) {
+      const int64_t r = std::max<int64_t>(0, std::min<int64_t>(off[i + 1], M) - std::max<int64_t>(off[i], 0));
+      largest = std::max(largest, r);
+      if (r > 0) ++active;
+      big_tiles += ceil_div(r, kBigM);
+      small_real += ceil_div(r, kSmallM);
+    }
+    m_pad = static_cast<int>(ceil_div(std::max<int64_t>(largest, 1), kSmallM) * kSmallM);
+    dense_tiles = active * (m_pad / kSmallM);
+    if (path == MOE_GEMM_AUTO) {
+      small1 = prefer_dense(big_tiles, dense_tiles, small_real, nt1);
+      small2 = prefer_dense(big_tiles, dense_tiles, small_real, nt2);
+    }
+  }
+  if ((small1 || small2) && dense_tiles > w.max_small)
+    return fail(MOE_ERR_WORKSPACE, "moe_expert_ffn: dense path needs %lld tiles", (long long)dense_tiles);
+
   char* ws = static_cast<char*>(workspace);
-  int32_t* tile_slot = reinterpret_cast<int32_t*>(ws + w.tile_slot);
-  int32_t* tile_row0 = reinterpret_cast<int32_t*>(ws + w.tile_row0);
   int32_t* n_tiles = reinterpret_cast<int32_t*>(ws + w.n_tiles);
-  tiles_kernel<<<1, 256, 0, s>>>(slot_off, n_slots, max_slots, M, kBM, w.max_tiles, tile_slot, tile_row0, n_tiles);
+  int32_t* big_slot = reinterpret_cast<int32_t*>(ws + w.big_slot);
+  int32_t* big_row0 = reinterpret_cast<int32_t*>(ws + w.big_row0);
+  int32_t* small_slot = reinterpret_cast<int32_t*>(ws + w.small_slot);
+  int32_t* small_row0 = reinterpret_cast<int32_t*>(ws + w.small_row0);
+  if (!small1 || !small2) {
+    tiles_kernel<<<1, 256, 0, s>>>(slot_off, n_slots, max_slots, M, kBigM, 0, w.max_big, big_slot, big_row0,
+                                   n_tiles);
+    if (int rc = hip_status(hipGetLastError(), "moe_expert_ffn tile-table launch")) return rc;
+  }
+  if (small1 || small2) {
+    tiles_kernel<<<1, 256, 0, s>>>(slot_off, n_slots, max_slots, M, kSmallM, m_pad, w.max_small, small_slot,
+                                   small_row0, n_tiles + 1);
+    if (int rc = hip_status(hipGetLastError(), "moe_expert_ffn tile-table launch")) return rc;
+  }
 
   GemmArgs p1{};
   p1.A = x_perm;
@@ -432,10 +505,10 @@ extern "C" int moe_expert_ffn(const void* x_perm, moe_dtype dt, int64_t M, int H
   p1.E = E;
   p1.slot_off = slot_off;
   p1.slot_expert = slot_expert;
-  p1.tile_slot = tile_slot;
-  p1.tile_row0 = tile_row0;
-  p1.n_tiles = n_tiles;
-  p1.n_col_tiles = static_cast<int>(ceil_div(I, act == MOE_SWIGLU ? kTileN / 2 : kTileN));
+  p1.tile_slot = small1 ? small_slot : big_slot;
+  p1.tile_row0 = small1 ? small_row0 : big_row0;
+  p1.n_tiles = small1 ? n_tiles + 1 : n_tiles;
+  p1.n_col_tiles = nt1;
   GemmArgs p2 = p1;
   p2.A = ws + w.h;
   p2.B0 = w_down;
@@ -443,12 +516,18 @@ extern "C" int moe_expert_ffn(const void* x_perm, moe_dtype dt, int64_t M, int H
   p2.C = y_perm;
   p2.K = I;
   p2.N = H;
-  p2.n_col_tiles = static_cast<int>(ceil_div(H, kTileN));
-  const unsigned grid1 = static_cast<unsigned>(w.max_tiles) * p1.n_col_tiles;
-  const unsigned grid2 = static_cast<unsigned>(w.max_tiles) * p2.n_col_tiles;
-  if (int rc = hip_status(hipGetLastError(), "moe_expert_ffn tile-table launch")) return rc;
-  return dt == MOE_BF16 ? launch_ffn<true>(p1, p2, act == MOE_SWIGLU, grid1, grid2, s)
-                        : launch_ffn<false>(p1, p2, act == MOE_SWIGLU, grid1, grid2, s);
+  p2.tile_slot = small2 ? small_slot : big_slot;
+  p2.tile_row0 = small2 ? small_row0 : big_row0;
+  p2.n_tiles = small2 ? n_tiles + 1 : n_tiles;
+  p2.n_col_tiles = nt2;
+  // grouped: an upper bound on the tiles (blocks past the count exit at once);
+  // dense: the exact padded batch
+  const int64_t big_bound = ceil_div(M, kBigM) + max_slots;
+  const unsigned grid1 = static_cast<unsigned>(std::max<int64_t>(1, (small1 ? dense_tiles : big_bound) * nt1));
+  const unsigned grid2 = static_cast<unsigned>(std::max<int64_t>(1, (small2 ? dense_tiles : big_bound) * nt2));
+  const bool swiglu = act == MOE_SWIGLU;
+  return dt == MOE_BF16 ? launch_ffn<true>(p1, small1, grid1, p2, small2, grid2, swiglu, s)
+                        : launch_ffn<false>(p1, small1, grid1, p2, small2, grid2, swiglu, s);
 }
 
 extern "C" int moe_ffn_set_timing_events(void* before_gateup, void* after_gateup, void* after_down) {
