@@ -4,56 +4,80 @@
 // review, section 3 (memory-bound, overlappable): out[t] = sum_i w[t,i] *
 // y_perm[inv_pos[t,i]], with the renormalised gate weights of the top-k gate.
 //
-// One 16-byte chunk of one output row per thread: k 16-byte gathers from the
-// expert-ordered rows, fp32 FMAs in slot order, one rounding to the dtype, one
-// 16-byte store.  HBM-bound: (k + 1) * H * s bytes per token.
+// Four 16-byte chunks of one output row per thread (strided so a wave's
+// accesses stay contiguous): k gathers each from the expert-ordered rows, fp32
+// FMAs in slot order, one rounding to the dtype, 16-byte stores.  HBM-bound:
+// (k + 1) * H * s bytes per token.
 #include "common.h"
 
 namespace {
 
+constexpr int kChunksPerThread = 4;
+
+// Thread (t, c0) handles chunks c0, c0 + stride, ... of token t's row: the
+// token's k row indices and weights are read once, and its k x 4 gathers are
+// independent loads in flight together.
 template <bool kBf16>
 __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ y, int64_t M,
                                                       const int32_t* __restrict__ inv_pos,
                                                       const float* __restrict__ w, int64_t T, int k, int chunks,
                                                       uint4* __restrict__ out) {
+  const int groups = (chunks + kChunksPerThread - 1) / kChunksPerThread;  // threads per token
   const int64_t g = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (g >= T * chunks) return;
-  const int64_t t = g / chunks;
-  const int c = static_cast<int>(g - t * chunks);
+  if (g >= T * groups) return;
+  const int64_t t = g / groups;
+  const int c0 = static_cast<int>(g - t * groups);
   constexpr int V = kBf16 ? 8 : 4;
-  float acc[V];
+  float acc[kChunksPerThread][V];
 #pragma unroll
-  for (int j = 0; j < V; ++j) acc[j] = 0.f;
+  for (int u = 0; u < kChunksPerThread; ++u)
+#pragma unroll
+    for (int j = 0; j < V; ++j) acc[u][j] = 0.f;
   for (int i = 0; i < k; ++i) {
     const int32_t r = inv_pos[t * k + i];
     if (r < 0 || r >= M) continue;
     const float wi = w[t * k + i];
-    const uint4 q = y[static_cast<int64_t>(r) * chunks + c];
-    const uint32_t u[4] = {q.x, q.y, q.z, q.w};
-    if constexpr (kBf16) {
+    const uint4* row = y + static_cast<int64_t>(r) * chunks;
+    uint4 q[kChunksPerThread];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        acc[2 * j] = fmaf(wi, bf16_bits_to_f32(u[j] & 0xffffu), acc[2 * j]);
-        acc[2 * j + 1] = fmaf(wi, bf16_bits_to_f32(u[j] >> 16), acc[2 * j + 1]);
+    for (int u = 0; u < kChunksPerThread; ++u) {
+      const int c = c0 + u * groups;
+      q[u] = c < chunks ? row[c] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < kChunksPerThread; ++u) {
+      const uint32_t v[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
+      if constexpr (kBf16) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc[u][2 * j] = fmaf(wi, bf16_bits_to_f32(v[j] & 0xffffu), acc[u][2 * j]);
+          acc[u][2 * j + 1] = fmaf(wi, bf16_bits_to_f32(v[j] >> 16), acc[u][2 * j + 1]);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[u][j] = fmaf(wi, __uint_as_float(v[j]), acc[u][j]);
       }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[j] = fmaf(wi, __uint_as_float(u[j]), acc[j]);
     }
   }
-  uint4 o;
-  if constexpr (kBf16) {
-    o.x = f32_to_bf16_bits(acc[0]) | (f32_to_bf16_bits(acc[1]) << 16);
-    o.y = f32_to_bf16_bits(acc[2]) | (f32_to_bf16_bits(acc[3]) << 16);
-    o.z = f32_to_bf16_bits(acc[4]) | (f32_to_bf16_bits(acc[5]) << 16);
-    o.w = f32_to_bf16_bits(acc[6]) | (f32_to_bf16_bits(acc[7]) << 16);
-  } else {
-    o.x = __float_as_uint(acc[0]);
-    o.y = __float_as_uint(acc[1]);
-    o.z = __float_as_uint(acc[2]);
-    o.w = __float_as_uint(acc[3]);
+  uint4* orow = out + t * chunks;
+#pragma unroll
+  for (int u = 0; u < kChunksPerThread; ++u) {
+    const int c = c0 + u * groups;
+    if (c >= chunks) continue;
+    uint4 o;
+    if constexpr (kBf16) {
+      o.x = f32_to_bf16_bits(acc[u][0]) | (f32_to_bf16_bits(acc[u][1]) << 16);
+      o.y = f32_to_bf16_bits(acc[u][2]) | (f32_to_bf16_bits(acc[u][3]) << 16);
+      o.z = f32_to_bf16_bits(acc[u][4]) | (f32_to_bf16_bits(acc[u][5]) << 16);
+      o.w = f32_to_bf16_bits(acc[u][6]) | (f32_to_bf16_bits(acc[u][7]) << 16);
+    } else {
+      o.x = __float_as_uint(acc[u][0]);
+      o.y = __float_as_uint(acc[u][1]);
+      o.z = __float_as_uint(acc[u][2]);
+      o.w = __float_as_uint(acc[u][3]);
+    }
+    orow[c] = o;
   }
-  out[g] = o;
 }
 
 }  // namespace
@@ -71,7 +95,8 @@ extern "C" int moe_combine(const void* y_perm, moe_dtype dt, int64_t M, const in
   if (!aligned16(out) || (y_perm && !aligned16(y_perm)))
     return fail(MOE_ERR_INVALID_ARG, "moe_combine: y_perm and out must be 16-byte aligned");
   const int chunks = static_cast<int>(static_cast<int64_t>(H) * elem_bytes(dt) / 16);
-  const unsigned blocks = static_cast<unsigned>(ceil_div(T * chunks, 256));
+  const int64_t groups = ceil_div(chunks, kChunksPerThread);
+  const unsigned blocks = static_cast<unsigned>(ceil_div(T * groups, 256));
   const hipStream_t s = as_stream(stream);
   if (dt == MOE_BF16)
     combine_kernel<true><<<blocks, 256, 0, s>>>(static_cast<const uint4*>(y_perm), M, inv_pos, topk_w, T, k, chunks,

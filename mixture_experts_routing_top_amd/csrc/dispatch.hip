@@ -16,7 +16,7 @@
 //               ballots (order = token order, so the permutation is stable and
 //               independent of scheduling).  Block 0 also writes expert_off
 //               and the slot table.
-//   3. permute: x_perm[inv_pos[t,i]] = x[t], one 16-byte chunk per thread;
+//   3. permute: x_perm[inv_pos[t,i]] = x[t], four 16-byte chunks per thread;
 //               every source row is read once and written k times.
 #include "common.h"
 
@@ -145,18 +145,34 @@ __global__ __launch_bounds__(kTok) void rank_kernel(const int32_t* __restrict__ 
   }
 }
 
-// One 16-byte chunk of one source row per thread; k destination rows.
+// Four 16-byte chunks of one source row per thread (strided so a wave's
+// accesses stay contiguous); each chunk is read once and written to the k
+// destination rows.
+constexpr int kChunksPerThread = 4;
+
 __global__ __launch_bounds__(256) void permute_kernel(const uint4* __restrict__ x, int64_t T, int chunks, int k,
                                                       int64_t M, const int32_t* __restrict__ inv_pos,
                                                       uint4* __restrict__ x_perm) {
+  const int groups = (chunks + kChunksPerThread - 1) / kChunksPerThread;
   const int64_t g = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (g >= T * chunks) return;
-  const int64_t t = g / chunks;
-  const int c = static_cast<int>(g - t * chunks);
-  const uint4 v = x[g];
+  if (g >= T * groups) return;
+  const int64_t t = g / groups;
+  const int c0 = static_cast<int>(g - t * groups);
+  uint4 v[kChunksPerThread];
+#pragma unroll
+  for (int u = 0; u < kChunksPerThread; ++u) {
+    const int c = c0 + u * groups;
+    if (c < chunks) v[u] = x[t * chunks + c];
+  }
   for (int i = 0; i < k; ++i) {
     const int32_t r = inv_pos[t * k + i];
-    if (r >= 0 && r < M) x_perm[static_cast<int64_t>(r) * chunks + c] = v;
+    if (r < 0 || r >= M) continue;
+    uint4* dst = x_perm + static_cast<int64_t>(r) * chunks;
+#pragma unroll
+    for (int u = 0; u < kChunksPerThread; ++u) {
+      const int c = c0 + u * groups;
+      if (c < chunks) dst[c] = v[u];
+    }
   }
 }
 
@@ -199,7 +215,7 @@ extern "C" int moe_dispatch(const void* x, moe_dtype dt, int64_t T, int H, const
                                                  inv_pos, expert_off, slot_off, slot_expert, n_slots);
   if (T > 0) {
     const int chunks = static_cast<int>(static_cast<int64_t>(H) * elem_bytes(dt) / 16);
-    const int64_t threads = T * chunks;
+    const int64_t threads = T * ceil_div(chunks, kChunksPerThread);
     permute_kernel<<<static_cast<unsigned>(ceil_div(threads, 256)), 256, 0, s>>>(
         static_cast<const uint4*>(x), T, chunks, k, T * k, inv_pos, static_cast<uint4*>(x_perm));
   }

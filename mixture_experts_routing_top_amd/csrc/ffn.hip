@@ -299,15 +299,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
 }
 
-// Lists the row tiles of the GEMMs.  Grouped (m_pad == 0): each slot's rows
-// are covered from its first row in steps of BM; the last tile of a slot may
-// be partial.  Dense (m_pad > 0): every slot with rows gets m_pad / BM tiles,
-// the uniform padded batch; tiles wholly past the slot's last row exit as soon
-// as the GEMM reads them.
+// Lists the row tiles of the GEMMs, per slot s with n rows from `start`:
+//   kCover:  ceil(n / BM) tiles from start (the last one may be partial);
+//   kPadded: m_pad / BM tiles for every slot with rows, the uniform padded
+//            batch (tiles wholly past the slot's last row exit as soon as the
+//            GEMM reads them).
+enum TileMode { kCover = 0, kPadded = 1 };
+
 __global__ __launch_bounds__(256) void tiles_kernel(const int32_t* __restrict__ slot_off,
                                                     const int32_t* __restrict__ n_slots_p, int max_slots, int64_t M,
-                                                    int BM, int m_pad, int max_tiles, int32_t* __restrict__ tile_slot,
-                                                    int32_t* __restrict__ tile_row0, int32_t* __restrict__ n_tiles) {
+                                                    int mode, int BM, int m_pad, int max_tiles,
+                                                    int32_t* __restrict__ tile_slot, int32_t* __restrict__ tile_row0,
+                                                    int32_t* __restrict__ n_tiles) {
   __shared__ int32_t scan[256];
   __shared__ int32_t carry;
   const int tid = threadIdx.x;
@@ -320,7 +323,9 @@ __global__ __launch_bounds__(256) void tiles_kernel(const int32_t* __restrict__ 
     if (s < n) {
       start = min<int64_t>(max(slot_off[s], 0), M);
       const int64_t end = min<int64_t>(max(slot_off[s + 1], 0), M);
-      if (end > start) cnt = m_pad > 0 ? m_pad / BM : (end - start + BM - 1) / BM;
+      const int64_t rows = end > start ? end - start : 0;
+      if (mode == kCover) cnt = (rows + BM - 1) / BM;
+      else if (rows > 0) cnt = m_pad / BM;
     }
     scan[tid] = static_cast<int32_t>(cnt);
     __syncthreads();
@@ -349,26 +354,27 @@ constexpr int kBigM = 256;    // grouped path: 256-row tiles
 constexpr int kSmallM = 64;   // dense path: 64-row tiles
 
 struct WsLayout {
-  size_t h, big_slot, big_row0, small_slot, small_row0, n_tiles, bytes;
-  int max_big, max_small;
+  size_t h, tab_slot[2], tab_row0[2], n_tiles, bytes;
+  int cap[2];  // tile capacity of each table
 };
 
-// Two tile tables: 256-row tiles (at most ceil(M/256) + slots) and 64-row tiles
-// of the dense padded batch (at most slots x ceil(largest slot / 64), and the
-// largest slot has at most M rows).
+enum Table { kTabGrouped = 0, kTabPadded = 1 };
+
+// Two tile tables: the grouped 256-row tiles (at most ceil(M/256) + slots) and
+// the dense padded batch in 64-row tiles (at most slots x ceil(largest slot /
+// 64), the largest slot having at most M rows).
 WsLayout ws_layout(moe_dtype dt, int64_t M, int I, int max_slots) {
   WsLayout w{};
-  const int64_t big = moe::ceil_div(M, kBigM) + max_slots;
-  const int64_t small = static_cast<int64_t>(max_slots) * moe::ceil_div(std::max<int64_t>(M, 1), kSmallM);
-  w.max_big = static_cast<int>(std::min<int64_t>(big, 0x3fffffff));
-  w.max_small = static_cast<int>(std::min<int64_t>(small, 0x3fffffff));
+  const int64_t cap[2] = {moe::ceil_div(M, kBigM) + max_slots,
+                          static_cast<int64_t>(max_slots) * moe::ceil_div(std::max<int64_t>(M, 1), kSmallM)};
   size_t at = 0;
   auto take = [&](size_t n) { size_t p = at; at = moe::align_up(at + n, 256); return p; };
   w.h = take(static_cast<size_t>(M) * I * moe::elem_bytes(dt));
-  w.big_slot = take(sizeof(int32_t) * w.max_big);
-  w.big_row0 = take(sizeof(int32_t) * w.max_big);
-  w.small_slot = take(sizeof(int32_t) * w.max_small);
-  w.small_row0 = take(sizeof(int32_t) * w.max_small);
+  for (int t = 0; t < 2; ++t) {
+    w.cap[t] = static_cast<int>(std::min<int64_t>(cap[t], 0x3fffffff));
+    w.tab_slot[t] = take(sizeof(int32_t) * w.cap[t]);
+    w.tab_row0[t] = take(sizeof(int32_t) * w.cap[t]);
+  }
   w.n_tiles = take(2 * sizeof(int32_t));
   w.bytes = at;
   return w;
@@ -380,21 +386,21 @@ thread_local hipEvent_t g_timing[3] = {nullptr, nullptr, nullptr};
 hipError_t mark(int i, hipStream_t s) { return g_timing[i] ? hipEventRecord(g_timing[i], s) : hipSuccess; }
 
 template <bool kBf16, int EPI, int NMAT>
-void launch_gemm(bool small, const GemmArgs& p, unsigned grid, hipStream_t s) {
-  if (small) gemm_kernel<kBf16, NMAT, EPI, kSmallM, 1><<<grid, 256, 0, s>>>(p);
+void launch_gemm(bool dense, const GemmArgs& p, unsigned grid, hipStream_t s) {
+  if (dense) gemm_kernel<kBf16, NMAT, EPI, kSmallM, 1><<<grid, 256, 0, s>>>(p);
   else gemm_kernel<kBf16, NMAT, EPI, kBigM, 2><<<grid, 256, 0, s>>>(p);
 }
 
 // Phase 1 (gate/up or W1) and phase 2 (down or W2), each on its own tile table.
 template <bool kBf16>
-int launch_ffn(const GemmArgs& p1, bool small1, unsigned grid1, const GemmArgs& p2, bool small2, unsigned grid2,
+int launch_ffn(const GemmArgs& p1, bool dense1, unsigned grid1, const GemmArgs& p2, bool dense2, unsigned grid2,
                bool swiglu, hipStream_t s) {
   if (int rc = moe::hip_status(mark(0, s), "moe_expert_ffn timing event")) return rc;
-  if (swiglu) launch_gemm<kBf16, kEpiSwiGLU, 2>(small1, p1, grid1, s);
-  else launch_gemm<kBf16, kEpiGELU, 1>(small1, p1, grid1, s);
+  if (swiglu) launch_gemm<kBf16, kEpiSwiGLU, 2>(dense1, p1, grid1, s);
+  else launch_gemm<kBf16, kEpiGELU, 1>(dense1, p1, grid1, s);
   if (int rc = moe::hip_status(hipGetLastError(), "moe_expert_ffn gate/up launch")) return rc;
   if (int rc = moe::hip_status(mark(1, s), "moe_expert_ffn timing event")) return rc;
-  launch_gemm<kBf16, kEpiStore, 1>(small2, p2, grid2, s);
+  launch_gemm<kBf16, kEpiStore, 1>(dense2, p2, grid2, s);
   if (int rc = moe::hip_status(hipGetLastError(), "moe_expert_ffn down launch")) return rc;
   return moe::hip_status(mark(2, s), "moe_expert_ffn timing event");
 }
@@ -446,9 +452,9 @@ extern "C" int moe_expert_ffn(const void* x_perm, moe_dtype dt, int64_t M, int H
   const hipStream_t s = as_stream(stream);
   const int nt1 = static_cast<int>(ceil_div(I, act == MOE_SWIGLU ? kTileN / 2 : kTileN));
   const int nt2 = static_cast<int>(ceil_div(H, kTileN));
-  // GROUPED: 256-row tiles for both GEMMs.  DENSE: the padded batch in 64-row
-  // tiles for both.  AUTO: per GEMM, from the slot sizes read back here.
-  bool small1 = path == MOE_GEMM_DENSE, small2 = small1;
+  // GROUPED: 256-row tiles covering each slot.  DENSE: the padded batch in
+  // 64-row tiles.  AUTO: per GEMM, from the slot sizes read back here.
+  bool dense1 = path == MOE_GEMM_DENSE, dense2 = dense1;
   int m_pad = 0;
   int64_t dense_tiles = 0;
   if (path != MOE_GEMM_GROUPED) {
@@ -470,29 +476,26 @@ extern "C" int moe_expert_ffn(const void* x_perm, moe_dtype dt, int64_t M, int H
     m_pad = static_cast<int>(ceil_div(std::max<int64_t>(largest, 1), kSmallM) * kSmallM);
     dense_tiles = active * (m_pad / kSmallM);
     if (path == MOE_GEMM_AUTO) {
-      small1 = prefer_dense(big_tiles, dense_tiles, small_real, nt1);
-      small2 = prefer_dense(big_tiles, dense_tiles, small_real, nt2);
+      dense1 = prefer_dense(big_tiles, dense_tiles, small_real, nt1);
+      dense2 = prefer_dense(big_tiles, dense_tiles, small_real, nt2);
     }
   }
-  if ((small1 || small2) && dense_tiles > w.max_small)
+  if ((dense1 || dense2) && dense_tiles > w.cap[kTabPadded])
     return fail(MOE_ERR_WORKSPACE, "moe_expert_ffn: dense path needs %lld tiles", (long long)dense_tiles);
 
   char* ws = static_cast<char*>(workspace);
   int32_t* n_tiles = reinterpret_cast<int32_t*>(ws + w.n_tiles);
-  int32_t* big_slot = reinterpret_cast<int32_t*>(ws + w.big_slot);
-  int32_t* big_row0 = reinterpret_cast<int32_t*>(ws + w.big_row0);
-  int32_t* small_slot = reinterpret_cast<int32_t*>(ws + w.small_slot);
-  int32_t* small_row0 = reinterpret_cast<int32_t*>(ws + w.small_row0);
-  if (!small1 || !small2) {
-    tiles_kernel<<<1, 256, 0, s>>>(slot_off, n_slots, max_slots, M, kBigM, 0, w.max_big, big_slot, big_row0,
-                                   n_tiles);
-    if (int rc = hip_status(hipGetLastError(), "moe_expert_ffn tile-table launch")) return rc;
-  }
-  if (small1 || small2) {
-    tiles_kernel<<<1, 256, 0, s>>>(slot_off, n_slots, max_slots, M, kSmallM, m_pad, w.max_small, small_slot,
-                                   small_row0, n_tiles + 1);
-    if (int rc = hip_status(hipGetLastError(), "moe_expert_ffn tile-table launch")) return rc;
-  }
+  auto tab_slot = [&](int t) { return reinterpret_cast<int32_t*>(ws + w.tab_slot[t]); };
+  auto tab_row0 = [&](int t) { return reinterpret_cast<int32_t*>(ws + w.tab_row0[t]); };
+  auto build = [&](int t, int mode, int bm) {
+    tiles_kernel<<<1, 256, 0, s>>>(slot_off, n_slots, max_slots, M, mode, bm, m_pad, w.cap[t], tab_slot(t),
+                                   tab_row0(t), n_tiles + t);
+    return hip_status(hipGetLastError(), "moe_expert_ffn tile-table launch");
+  };
+  if (!dense1 || !dense2)
+    if (int rc = build(kTabGrouped, kCover, kBigM)) return rc;
+  if (dense1 || dense2)
+    if (int rc = build(kTabPadded, kPadded, kSmallM)) return rc;
 
   GemmArgs p1{};
   p1.A = x_perm;
@@ -505,9 +508,6 @@ extern "C" int moe_expert_ffn(const void* x_perm, moe_dtype dt, int64_t M, int H
   p1.E = E;
   p1.slot_off = slot_off;
   p1.slot_expert = slot_expert;
-  p1.tile_slot = small1 ? small_slot : big_slot;
-  p1.tile_row0 = small1 ? small_row0 : big_row0;
-  p1.n_tiles = small1 ? n_tiles + 1 : n_tiles;
   p1.n_col_tiles = nt1;
   GemmArgs p2 = p1;
   p2.A = ws + w.h;
@@ -516,18 +516,23 @@ extern "C" int moe_expert_ffn(const void* x_perm, moe_dtype dt, int64_t M, int H
   p2.C = y_perm;
   p2.K = I;
   p2.N = H;
-  p2.tile_slot = small2 ? small_slot : big_slot;
-  p2.tile_row0 = small2 ? small_row0 : big_row0;
-  p2.n_tiles = small2 ? n_tiles + 1 : n_tiles;
   p2.n_col_tiles = nt2;
+  auto on = [&](GemmArgs& g, bool dense) {
+    const int t = dense ? kTabPadded : kTabGrouped;
+    g.tile_slot = tab_slot(t);
+    g.tile_row0 = tab_row0(t);
+    g.n_tiles = n_tiles + t;
+  };
+  on(p1, dense1);
+  on(p2, dense2);
   // grouped: an upper bound on the tiles (blocks past the count exit at once);
   // dense: the exact padded batch
-  const int64_t big_bound = ceil_div(M, kBigM) + max_slots;
-  const unsigned grid1 = static_cast<unsigned>(std::max<int64_t>(1, (small1 ? dense_tiles : big_bound) * nt1));
-  const unsigned grid2 = static_cast<unsigned>(std::max<int64_t>(1, (small2 ? dense_tiles : big_bound) * nt2));
+  const int64_t bound = w.cap[kTabGrouped];
+  const unsigned grid1 = static_cast<unsigned>(std::max<int64_t>(1, (dense1 ? dense_tiles : bound) * nt1));
+  const unsigned grid2 = static_cast<unsigned>(std::max<int64_t>(1, (dense2 ? dense_tiles : bound) * nt2));
   const bool swiglu = act == MOE_SWIGLU;
-  return dt == MOE_BF16 ? launch_ffn<true>(p1, small1, grid1, p2, small2, grid2, swiglu, s)
-                        : launch_ffn<false>(p1, small1, grid1, p2, small2, grid2, swiglu, s);
+  return dt == MOE_BF16 ? launch_ffn<true>(p1, dense1, grid1, p2, dense2, grid2, swiglu, s)
+                        : launch_ffn<false>(p1, dense1, grid1, p2, dense2, grid2, swiglu, s);
 }
 
 extern "C" int moe_ffn_set_timing_events(void* before_gateup, void* after_gateup, void* after_down) {
