@@ -46,6 +46,7 @@ def lib():
         _lib = ctypes.CDLL(_LIB_PATH)
         for name in ("oracle_route", "oracle_histogram", "oracle_cooccurrence", "oracle_popularity",
                      "oracle_conditional", "oracle_predict_next", "oracle_replicas", "oracle_dispatch",
+                     "oracle_predicted_counts", "oracle_plan_replicas", "oracle_prediction_quality",
                      "oracle_permute", "oracle_ffn_rows", "oracle_combine", "oracle_bf16_round_bits"):
             getattr(_lib, name).restype = ctypes.c_int
     return _lib
@@ -128,6 +129,34 @@ def replicas(counts: np.ndarray, T: int, k: int, R: int) -> np.ndarray:
     r = np.empty(counts.shape[0], np.int32)
     lib().oracle_replicas(_p(counts), counts.shape[0], _i64(T), k, R, _p(r))
     return r
+
+
+def predicted_counts(p_hat: np.ndarray, total: int) -> np.ndarray:
+    p_hat = np.ascontiguousarray(p_hat, dtype=np.float32)
+    out = np.empty(p_hat.shape[0], np.int32)
+    lib().oracle_predicted_counts(_p(p_hat), p_hat.shape[0], _i64(total), _p(out))
+    return out
+
+
+def plan_replicas(p_hat: np.ndarray, total: int, R: int):
+    """(predicted counts, replicas) planned from a predicted distribution."""
+    p_hat = np.ascontiguousarray(p_hat, dtype=np.float32)
+    E = p_hat.shape[0]
+    c_hat = np.empty(E, np.int32)
+    r = np.empty(E, np.int32)
+    _check(lib().oracle_plan_replicas(_p(p_hat), E, _i64(total), R, _p(c_hat), _p(r)), "plan_replicas")
+    return c_hat, r
+
+
+def prediction_quality(p_hat: np.ndarray, counts: np.ndarray, reps: np.ndarray | None, top_n: int) -> np.ndarray:
+    """[tv distance, top-n hit rate, slot-load std, max/mean slot load] as float32."""
+    p_hat = np.ascontiguousarray(p_hat, dtype=np.float32)
+    counts = np.ascontiguousarray(counts, dtype=np.int32)
+    out = np.empty(4, np.float32)
+    rp = None if reps is None else np.ascontiguousarray(reps, dtype=np.int32)
+    _check(lib().oracle_prediction_quality(_p(p_hat), _p(counts), p_hat.shape[0],
+                                           None if rp is None else _p(rp), top_n, _p(out)), "prediction_quality")
+    return out
 
 
 class WindowStats:

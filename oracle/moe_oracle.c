@@ -218,6 +218,114 @@ int oracle_replicas(const int32_t* counts, int E, int64_t T, int k, int R, int32
 }
 
 /*
+ * Replicas planned ahead of routing.  [MPMC] contribution 2-3 and [PF] plan the
+ * replica placement from predicted expert activity before the layer runs; the
+ * prediction here is [PF] Eq.(3)'s next-layer popularity p_hat.  Reading
+ * taken: predicted rows c_hat[e] = p_hat[e] * total (total = T*k of the layer
+ * to come), the product taken in double and rounded to the nearest integer
+ * with halves to even; NaN, zero or negative shares give 0 and values at or
+ * past 2^31 - 1 clamp there.  The plan is then the greedy rule of
+ * oracle_replicas applied to c_hat with sum(c_hat) standing for T*k.
+ */
+int oracle_predicted_counts(const float* p_hat, int E, int64_t total, int32_t* c_hat) {
+    for (int e = 0; e < E; ++e) {
+        double v = (double)p_hat[e] * (double)total;
+        if (!(v > 0.0)) c_hat[e] = 0;
+        else if (v >= 2147483647.0) c_hat[e] = 2147483647;
+        else c_hat[e] = (int32_t)nearbyint(v);
+    }
+    return 0;
+}
+
+int oracle_plan_replicas(const float* p_hat, int E, int64_t total, int R, int32_t* c_hat, int32_t* r) {
+    oracle_predicted_counts(p_hat, E, total, c_hat);
+    int64_t sum = 0;
+    for (int e = 0; e < E; ++e) sum += c_hat[e];
+    return oracle_replicas(c_hat, E, sum, 1, R, r);
+}
+
+/* rank order of the top-n: value descending, then expert index ascending; NaN counts as -inf */
+static double rank_value(double v) { return v != v ? -INFINITY : v; }
+
+static void top_n_set(const double* v, int E, int n, unsigned char* in) {
+    for (int e = 0; e < E; ++e) in[e] = 0;
+    for (int j = 0; j < n; ++j) {
+        int best = -1;
+        for (int e = 0; e < E; ++e)
+            if (!in[e] && (best < 0 || rank_value(v[e]) > rank_value(v[best]))) best = e;
+        in[best] = 1;
+    }
+}
+
+/*
+ * How well a prediction matched the routing that followed, and how evenly a
+ * replica plan spread the rows ([MPMC] reports prediction accuracy and load
+ * balance; the load-prediction study measures prediction error of expert
+ * load; [GPS] 2.1 targets per-copy load near the mean).  Definitions taken:
+ *   out[0] total-variation distance 0.5 * sum_e |q_e - a_e| between the
+ *          prediction normalised to sum one (q = p_hat / sum p_hat) and the
+ *          actual shares a = counts / sum counts; 1 if either sum is not > 0;
+ *   out[1] top-n hit rate: |top_n(p_hat) & top_n(counts)| / n, n = min(top_n, E);
+ *   out[2] population standard deviation of the per-slot row loads, expert e
+ *          with r_e replicas being cut into r_e + 1 chunks as dispatch cuts it
+ *          (chunk rho holds floor((rho+1) n_e/(r_e+1)) - floor(rho n_e/(r_e+1)));
+ *   out[3] largest slot load over the mean slot load sum(counts)/slots (0 if
+ *          there are no rows).
+ * Sums run in expert (slot) order in double; each output is rounded to fp32 once.
+ * replicas == NULL means one slot per expert.
+ */
+int oracle_prediction_quality(const float* p_hat, const int32_t* counts, int E, const int32_t* replicas,
+                              int top_n, float* out) {
+    if (E < 1 || top_n < 1) return -1;
+    double S = 0.0;
+    int64_t A = 0;
+    for (int e = 0; e < E; ++e) {
+        S += (double)p_hat[e];
+        A += counts[e];
+    }
+    double tv = 1.0;
+    if (S > 0.0 && A > 0) {
+        double acc = 0.0;
+        for (int e = 0; e < E; ++e) acc += fabs((double)p_hat[e] / S - (double)counts[e] / (double)A);
+        tv = 0.5 * acc;
+    }
+    const int n = top_n < E ? top_n : E;
+    double* vp = (double*)malloc(sizeof(double) * (size_t)E);
+    double* vc = (double*)malloc(sizeof(double) * (size_t)E);
+    unsigned char* ip = (unsigned char*)malloc((size_t)E);
+    unsigned char* ic = (unsigned char*)malloc((size_t)E);
+    for (int e = 0; e < E; ++e) {
+        vp[e] = (double)p_hat[e];
+        vc[e] = (double)counts[e];
+    }
+    top_n_set(vp, E, n, ip);
+    top_n_set(vc, E, n, ic);
+    int hit = 0;
+    for (int e = 0; e < E; ++e) hit += ip[e] && ic[e];
+    free(vp); free(vc); free(ip); free(ic);
+
+    int64_t slots = 0, mx = 0;
+    for (int e = 0; e < E; ++e) slots += 1 + (replicas && replicas[e] > 0 ? replicas[e] : 0);
+    const double mean = (double)A / (double)slots;
+    double var = 0.0;
+    for (int e = 0; e < E; ++e) {
+        const int64_t copies = 1 + (replicas && replicas[e] > 0 ? replicas[e] : 0);
+        const int64_t ne = counts[e];
+        for (int64_t rho = 0; rho < copies; ++rho) {
+            const int64_t load = ((rho + 1) * ne) / copies - (rho * ne) / copies;
+            const double d = (double)load - mean;
+            var += d * d;
+            if (load > mx) mx = load;
+        }
+    }
+    out[0] = (float)tv;
+    out[1] = (float)((double)hit / (double)n);
+    out[2] = (float)sqrt(var / (double)slots);
+    out[3] = A > 0 ? (float)((double)mx / mean) : 0.0f;
+    return 0;
+}
+
+/*
  * Dispatch: group the (token, slot) pairs by expert into contiguous rows.
  * Experts occupy consecutive row ranges (exclusive prefix sum of the counts);
  * inside an expert the rows follow ascending token index.  perm_src[row] is

@@ -384,3 +384,101 @@ def test_token_forward_matches_full_layer():
     sample = np.array([0, 7, 100, 255])
     _, out = oracle.token_forward(x[sample], full["idx"][sample], full["w"][sample], wts, cfg.act)
     assert np.array_equal(out, full["out"][sample])
+
+
+# ------------------------------------------------ replicas planned from a prediction
+def _round_half_even(fr: Fraction) -> int:
+    fl = math.floor(fr)
+    rem = fr - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        return fl + 1
+    return fl
+
+
+def test_predicted_counts_exact_rational_rounding():
+    """c_hat = p*total rounded half-to-even, checked in exact rational arithmetic
+    (totals below 2^29 keep the double product exact)."""
+    rng = np.random.default_rng(11)
+    for trial in range(50):
+        E = int(rng.integers(1, 40))
+        total = int(rng.integers(0, 1 << 28))
+        p = rng.random(E).astype(np.float32)
+        got = oracle.predicted_counts(p, total)
+        ref = [_round_half_even(Fraction(float(v)) * total) for v in p]
+        assert got.tolist() == ref
+    halves = np.array([0.5, 0.5, 0.25, 0.75], np.float32)
+    assert oracle.predicted_counts(halves, 3).tolist() == [2, 2, 1, 2]   # 1.5->2, 0.75->1, 2.25->2
+    assert oracle.predicted_counts(halves, 5).tolist() == [2, 2, 1, 4]   # 2.5->2, 1.25->1, 3.75->4
+    odd = np.array([np.nan, -1.0, 0.0, np.inf, 3.0e9], np.float32)
+    assert oracle.predicted_counts(odd, 1).tolist() == [0, 0, 0, 2147483647, 2147483647]
+
+
+def test_plan_from_exact_shares_equals_plan_from_counts():
+    """When the prediction is the exact share vector of some counts (a power-of-two
+    total keeps n/total exact in fp32), the predicted plan is the counts plan."""
+    rng = np.random.default_rng(12)
+    for trial in range(40):
+        E = int(rng.integers(2, 33))
+        total = 1 << int(rng.integers(6, 16))
+        cuts = np.sort(rng.integers(0, total + 1, size=E - 1))
+        counts = np.diff(np.concatenate([[0], cuts, [total]])).astype(np.int32)
+        p = (counts.astype(np.float64) / total).astype(np.float32)
+        R = int(rng.integers(0, 2 * E))
+        c_hat, r = oracle.plan_replicas(p, total, R)
+        assert np.array_equal(c_hat, counts)
+        assert np.array_equal(r, oracle.replicas(counts, total, 1, R))
+
+
+def test_prediction_quality_hand_example():
+    """counts 32/16/8/8 predicted exactly: tv 0, top-2 hit 1, loads (32,16,8,8) have
+    std sqrt(96) and max/mean 2; one replica of expert 0 gives loads (16,16,16,8,8):
+    mean 12.8, variance 15.36, max/mean 1.25."""
+    p = np.array([0.5, 0.25, 0.125, 0.125], np.float32)
+    n = np.array([32, 16, 8, 8], np.int32)
+    q = oracle.prediction_quality(p, n, None, 2)
+    assert q[0] == 0.0 and q[1] == 1.0
+    assert q[2] == np.float32(math.sqrt(96.0)) and q[3] == 2.0
+    q = oracle.prediction_quality(p, n, np.array([1, 0, 0, 0], np.int32), 2)
+    assert q[2] == np.float32(math.sqrt(15.36)) and q[3] == np.float32(1.25)
+
+
+def test_prediction_quality_against_independent_definitions():
+    """tv in exact rationals, top-n by Python sorting, slot loads from the dispatch
+    oracle's slot offsets with numpy's population std."""
+    rng = np.random.default_rng(13)
+    for trial in range(60):
+        E = int(rng.integers(1, 24))
+        k = int(rng.integers(1, min(E, 4) + 1))
+        T = int(rng.integers(1, 300))
+        idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+        counts = oracle.histogram(idx, E)
+        p = rng.random(E).astype(np.float32)
+        if trial % 5 == 0:
+            p[rng.integers(0, E)] = p.max()  # ties in the ranking
+        reps = rng.integers(0, 3, size=E).astype(np.int32) if trial % 2 else None
+        top_n = int(rng.integers(1, 7))
+        q = oracle.prediction_quality(p, counts, reps, top_n)
+        S = sum(Fraction(float(v)) for v in p)
+        A = int(counts.sum())
+        tv = sum(abs(Fraction(float(v)) / S - Fraction(int(c), A)) for v, c in zip(p, counts)) / 2
+        assert abs(float(q[0]) - float(tv)) <= 2e-7 * max(1.0, float(tv))
+        n = min(top_n, E)
+        tp = set(sorted(range(E), key=lambda e: (-float(p[e]), e))[:n])
+        tc = set(sorted(range(E), key=lambda e: (-int(counts[e]), e))[:n])
+        assert q[1] == np.float32(len(tp & tc) / n)
+        d = oracle.dispatch(idx, E, reps)
+        loads = np.diff(d["slot_off"][: d["n_slots"] + 1]).astype(np.float64)
+        assert len(loads) == E + (0 if reps is None else int(reps.sum()))
+        assert abs(float(q[2]) - np.std(loads)) <= 1e-6 * max(1.0, np.std(loads))
+        assert abs(float(q[3]) - loads.max() / loads.mean()) <= 1e-6 * loads.max() / loads.mean()
+
+
+def test_prediction_quality_extremes():
+    p = np.array([1.0, 0.0, 0.0], np.float32)
+    n = np.array([0, 5, 7], np.int32)
+    q = oracle.prediction_quality(p, n, None, 1)
+    assert q[0] == 1.0 and q[1] == 0.0             # disjoint supports
+    q = oracle.prediction_quality(np.zeros(3, np.float32), n, None, 3)
+    assert q[0] == 1.0 and q[1] == 1.0             # no prediction mass; top-3 of 3 always hits
+    q = oracle.prediction_quality(p, np.zeros(3, np.int32), None, 2)
+    assert q[0] == 1.0 and q[2] == 0.0 and q[3] == 0.0
