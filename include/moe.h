@@ -4,6 +4,10 @@
  *
  *   moe_route -> moe_stats -> moe_dispatch -> moe_expert_ffn -> moe_combine
  *
+ * plus moe_plan_replicas (a replica plan for the next layer from moe_stats'
+ * prediction, made before that layer routes) and moe_prediction_quality (how
+ * well the prediction and the plan matched the routing that followed).
+ *
  * Sources (page title, section):
  *   [PF]   "PopFetcher: Towards Accelerated Mixture-of-Experts Training Via
  *           Popularity Based Expert-Wise Prefetch (ATC 2025)", wiki summary
@@ -116,6 +120,44 @@ int moe_stats(void* state, size_t state_bytes, int L, int E, int window, int lay
               const int32_t* topk_idx, const int32_t* prev_topk_idx, int64_t T, int k,
               int32_t* counts, float* p_seq, float* cond, float* pred_next,
               int replica_budget, int32_t* replicas, void* stream);
+
+/* ------------------------------------------------ planning ahead of routing
+ * moe_plan_replicas -- replica counts for a layer planned before it routes,
+ * from a predicted expert distribution ([PF] method: Eq.(3) predicts the next
+ * layer's popularity and the plan acts on it ahead of time; [MPMC]
+ * contributions 2-3: replicas placed from predicted activity, within a budget).
+ *   pred         fp32 [E]: predicted shares, e.g. moe_stats' pred_next of the
+ *                layer before;
+ *   total        rows the layer will route (T*k);
+ *   pred_counts  int32 [E] out (may be NULL): pred[e] * total in double,
+ *                rounded to the nearest integer with halves to even; NaN, zero
+ *                or negative shares give 0, values from 2^31 - 1 up clamp there;
+ *   replicas     int32 [E] out: the greedy plan moe_stats applies to counts,
+ *                applied to pred_counts with their sum standing for T*k.
+ * Limits: 1 <= E <= 256, 0 <= total < 2^31, 0 <= replica_budget <= 4096.
+ *
+ * moe_prediction_quality -- how well a prediction matched the routing that
+ * followed and how evenly a replica plan spread its rows ([MPMC] evaluation:
+ * prediction accuracy and load balance; [GPS] 2.1: per-copy load near the
+ * mean).  Writes fp32 out[4]:
+ *   out[0]  total-variation distance 0.5 * sum_e |q_e - a_e| between
+ *           q = pred / sum(pred) and the actual shares a = counts / sum(counts)
+ *           (1 when either sum is not positive);
+ *   out[1]  top-n hit rate |top_n(pred) & top_n(counts)| / n, n = min(top_n, E),
+ *           ranking by value descending then index ascending (NaN as -inf);
+ *   out[2]  population standard deviation of the per-slot row loads, expert e
+ *           with r_e replicas being cut into r_e + 1 chunks as moe_dispatch
+ *           cuts it (replicas NULL: one slot per expert; r_e clamped to
+ *           [0, 4096]);
+ *   out[3]  largest slot load over the mean slot load (0 with no rows).
+ * Sums are taken in expert order in double and rounded to fp32 once.
+ * Limits: 1 <= E <= 256, top_n >= 1.  Both calls are one small kernel on
+ * `stream`; pointers are device pointers.
+ */
+int moe_plan_replicas(const float* pred, int E, int64_t total, int replica_budget, int32_t* pred_counts,
+                      int32_t* replicas, void* stream);
+int moe_prediction_quality(const float* pred, const int32_t* counts, int E, const int32_t* replicas, int top_n,
+                           float* out, void* stream);
 
 /* --------------------------------------------------------------- dispatch
  * moe_dispatch -- permute tokens into expert/replica-contiguous rows (the

@@ -9,6 +9,7 @@ call fails, an exception is raised.
 
     idx, w = moe_route(logits, k)
     stats  = moe_stats(state, ...)          # counts, popularity, conditional, prediction, replicas
+    plan   = moe_plan_replicas(pred_next, T*k, R)   # replicas for the next layer, ahead of its routing
     d      = moe_dispatch(x, idx, E, replicas, max_slots)
     y_perm = moe_expert_ffn(d["x_perm"], d["slot_off"], ..., w_gate, w_up, w_down)
     out    = moe_combine(y_perm, d["inv_pos"], w)
@@ -21,7 +22,8 @@ import torch
 
 from ._native import LIB_PATH, MoEError, lib
 
-__all__ = ["moe_route", "moe_stats_state_bytes", "moe_stats_init", "moe_stats", "moe_dispatch_workspace_bytes",
+__all__ = ["moe_route", "moe_stats_state_bytes", "moe_stats_init", "moe_stats", "moe_plan_replicas",
+           "moe_prediction_quality", "moe_dispatch_workspace_bytes",
            "moe_dispatch", "moe_expert_ffn_workspace_bytes", "moe_expert_ffn", "moe_combine", "moe_layer_forward",
            "MoEError", "LIB_PATH", "MOE_F32", "MOE_BF16", "SWIGLU", "GELU", "GEMM_AUTO", "GEMM_GROUPED",
            "GEMM_DENSE"]
@@ -104,6 +106,32 @@ def moe_stats(state: torch.Tensor, L: int, E: int, window: int, layer: int, it: 
     return dict(counts=counts, p_seq=p_seq, cond=cond, pred_next=pred_next, replicas=replicas)
 
 
+def moe_plan_replicas(pred: torch.Tensor, total: int, replica_budget: int, pred_counts=None, replicas=None,
+                      stream=None):
+    """Replica counts planned from a predicted distribution (e.g. moe_stats' pred_next)
+    for a layer that will route `total` = T*k rows; returns (pred_counts, replicas)."""
+    E = pred.numel()
+    if pred.dtype != torch.float32:
+        raise TypeError("the prediction must be float32")
+    pred_counts = _i32(E, pred.device) if pred_counts is None else pred_counts
+    replicas = _i32(E, pred.device) if replicas is None else replicas
+    _call("moe_plan_replicas", _ptr(pred), E, ctypes.c_int64(total), replica_budget, _ptr(pred_counts),
+          _ptr(replicas), _stream(stream))
+    return pred_counts, replicas
+
+
+def moe_prediction_quality(pred: torch.Tensor, counts: torch.Tensor, replicas=None, top_n: int = 5, out=None,
+                           stream=None):
+    """float32 [4] on the device: total-variation distance of the prediction to the
+    actual shares, top-n hit rate, per-slot load std, max/mean slot load."""
+    E = pred.numel()
+    if pred.dtype != torch.float32 or counts.dtype != torch.int32:
+        raise TypeError("pred must be float32 and counts int32")
+    out = torch.empty(4, dtype=torch.float32, device=pred.device) if out is None else out
+    _call("moe_prediction_quality", _ptr(pred), _ptr(counts), E, _ptr(replicas), top_n, _ptr(out), _stream(stream))
+    return out
+
+
 # ----------------------------------------------------------------- dispatch
 def moe_dispatch_workspace_bytes(T: int, k: int, E: int) -> int:
     return int(lib().moe_dispatch_workspace_bytes(ctypes.c_int64(T), k, E))
@@ -166,12 +194,16 @@ def moe_combine(y_perm: torch.Tensor, inv_pos: torch.Tensor, topk_w: torch.Tenso
 
 # ------------------------------------------------------ one layer, composed
 def moe_layer_forward(x, logits, k, w_gate, w_up, w_down, act="swiglu", replica_budget=0, stats_state=None,
-                      stats_dims=None, layer=0, it=0, prev_topk_idx=None, path="grouped", bufs=None, stream=None):
+                      stats_dims=None, layer=0, it=0, prev_topk_idx=None, path="grouped", bufs=None, stream=None,
+                      planned_replicas=None):
     """route -> stats (+ replicas) -> dispatch -> FFN -> combine, all on `stream`.
 
     stats_state/stats_dims=(L, E, window) enable the windowed statistics; the
     replica budget needs this iteration's counts, which moe_stats produces.
-    `bufs` (a dict) caches outputs and workspaces between calls."""
+    planned_replicas (int32 [E], e.g. from moe_plan_replicas on the previous
+    layer's prediction) replaces that count-based plan; it must hand out at
+    most replica_budget copies.  `bufs` (a dict) caches outputs and workspaces
+    between calls."""
     T, E = logits.shape
     dev = x.device
     b = bufs if bufs is not None else {}
@@ -196,9 +228,13 @@ def moe_layer_forward(x, logits, k, w_gate, w_up, w_down, act="swiglu", replica_
             b.setdefault("pred_next", torch.empty(E, dtype=torch.float32, device=dev))
         st = moe_stats(stats_state, L_, E_, win, layer, it, idx, prev_topk_idx, k, b["counts"], b["p_seq"],
                        b.get("cond") if layer + 1 < L_ else None, b.get("pred_next") if layer + 1 < L_ else None,
-                       replica_budget, b["replicas"] if replica_budget > 0 else None, stream)
+                       replica_budget, b["replicas"] if replica_budget > 0 and planned_replicas is None else None,
+                       stream)
         res.update({kk: v for kk, v in st.items() if v is not None})
         replicas = b["replicas"] if replica_budget > 0 else None
+    if planned_replicas is not None:
+        replicas = planned_replicas
+        res["replicas"] = planned_replicas
     max_slots = E + replica_budget
     if "ws_d" not in b:
         b["ws_d"] = torch.empty(moe_dispatch_workspace_bytes(T, k, E), dtype=torch.uint8, device=dev)

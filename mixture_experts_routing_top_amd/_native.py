@@ -13,6 +13,8 @@ SIGNATURES = {
     "moe_stats_state_bytes": (_sz, [_i, _i, _i]),
     "moe_stats_init": (_i, [_p, _sz, _i, _i, _i, _p]),
     "moe_stats": (_i, [_p, _sz, _i, _i, _i, _i, _i64, _p, _p, _i64, _i, _p, _p, _p, _p, _i, _p, _p]),
+    "moe_plan_replicas": (_i, [_p, _i, _i64, _i, _p, _p, _p]),
+    "moe_prediction_quality": (_i, [_p, _p, _i, _p, _i, _p, _p]),
     "moe_dispatch_workspace_bytes": (_sz, [_i64, _i, _i]),
     "moe_dispatch": (_i, [_p, _i, _i64, _i, _p, _i, _i, _p, _i, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
     "moe_expert_ffn_workspace_bytes": (_sz, [_i, _i64, _i, _i, _i]),

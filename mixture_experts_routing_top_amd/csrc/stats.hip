@@ -19,6 +19,7 @@
 // prediction is a double sum in expert order, so the results do not depend on
 // the order in which blocks finish.
 #include "common.h"
+#include "replica_plan.h"
 
 namespace {
 
@@ -56,14 +57,6 @@ struct Args {
   float* pred;
   int32_t* replicas;
 };
-
-// (n_a, r_a, a) has a larger per-copy load than (n_b, r_b, b); ties -> lower index.
-__device__ __forceinline__ bool heavier(int64_t na, int ra, int a, int64_t nb, int rb, int b) {
-  if (b < 0) return a >= 0;
-  if (a < 0) return false;
-  const int64_t l = na * (rb + 1), r = nb * (ra + 1);
-  return l > r || (l == r && a < b);
-}
 
 __global__ __launch_bounds__(kThreads) void stats_kernel(Args a) {
   __shared__ int32_t hist[moe::kMaxExperts];
@@ -199,36 +192,11 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(Args a) {
 
   // Replica plan from this iteration's counts (wave 0: 64 lanes x 4 experts).
   if (a.idx && a.replicas && tid < 64) {
-    const int64_t tk = a.T * static_cast<int64_t>(k);
     int64_t n[4];
     int r[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = tid + 64 * j;
-      n[j] = e < E ? hist[e] : 0;
-      r[j] = 0;
-    }
-    for (int step = 0; step < a.budget; ++step) {
-      int64_t bn = 0;
-      int br = 0, be = -1;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int e = tid + 64 * j;
-        const bool above = e < E && n[j] * E > tk * (r[j] + 1);
-        if (above && heavier(n[j], r[j], e, bn, br, be)) { bn = n[j]; br = r[j]; be = e; }
-      }
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int64_t on = __shfl_xor(bn, off);
-        const int orr = __shfl_xor(br, off);
-        const int oe = __shfl_xor(be, off);
-        if (heavier(on, orr, oe, bn, br, be)) { bn = on; br = orr; be = oe; }
-      }
-      if (be < 0) break;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (tid + 64 * j == be) r[j] += 1;
-    }
+    for (int j = 0; j < 4; ++j) n[j] = tid + 64 * j < E ? hist[tid + 64 * j] : 0;
+    moe::plan_replicas_wave(n, E, a.T * static_cast<int64_t>(k), a.budget, tid, r);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       if (tid + 64 * j < E) a.replicas[tid + 64 * j] = r[j];

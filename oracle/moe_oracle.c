@@ -272,8 +272,15 @@ static void top_n_set(const double* v, int E, int n, unsigned char* in) {
  *   out[3] largest slot load over the mean slot load sum(counts)/slots (0 if
  *          there are no rows).
  * Sums run in expert (slot) order in double; each output is rounded to fp32 once.
- * replicas == NULL means one slot per expert.
+ * replicas == NULL means one slot per expert; replica counts are clamped to
+ * [0, 4096] (the largest budget a plan hands out).
  */
+static int64_t copies_of(const int32_t* replicas, int e) {
+    if (!replicas) return 1;
+    int32_t r = replicas[e] < 0 ? 0 : replicas[e];
+    return 1 + (r > 4096 ? 4096 : r);
+}
+
 int oracle_prediction_quality(const float* p_hat, const int32_t* counts, int E, const int32_t* replicas,
                               int top_n, float* out) {
     if (E < 1 || top_n < 1) return -1;
@@ -305,11 +312,11 @@ int oracle_prediction_quality(const float* p_hat, const int32_t* counts, int E, 
     free(vp); free(vc); free(ip); free(ic);
 
     int64_t slots = 0, mx = 0;
-    for (int e = 0; e < E; ++e) slots += 1 + (replicas && replicas[e] > 0 ? replicas[e] : 0);
+    for (int e = 0; e < E; ++e) slots += copies_of(replicas, e);
     const double mean = (double)A / (double)slots;
     double var = 0.0;
     for (int e = 0; e < E; ++e) {
-        const int64_t copies = 1 + (replicas && replicas[e] > 0 ? replicas[e] : 0);
+        const int64_t copies = copies_of(replicas, e);
         const int64_t ne = counts[e];
         for (int64_t rho = 0; rho < copies; ++rho) {
             const int64_t load = ((rho + 1) * ne) / copies - (rho * ne) / copies;

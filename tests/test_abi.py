@@ -72,6 +72,14 @@ N = None
     ("moe_expert_ffn", (16, 1, 100, 128, 128, 8, 16, 16, 16, 8, 16, N, 16, 0, 1, 16, 16, 1 << 30, N), -1, "w_up"),
     ("moe_expert_ffn", (16, 1, 100, 128, 128, 8, 16, 16, 16, 8, 16, 16, 16, 1, 1, 16, 16, 1 << 30, N), -1, "GELU"),
     ("moe_expert_ffn", (16, 1, 100, 128, 128, 8, 16, 16, 16, 8, 16, 16, 16, 0, 1, 16, 16, 10, N), -3, "workspace"),
+    ("moe_plan_replicas", (16, 0, 10, 2, N, 16, N), -1, "E=0"),
+    ("moe_plan_replicas", (16, 300, 10, 2, N, 16, N), -2, "E=300"),
+    ("moe_plan_replicas", (16, 8, -1, 2, N, 16, N), -1, "total"),
+    ("moe_plan_replicas", (16, 8, 10, 5000, N, 16, N), -1, "replica_budget"),
+    ("moe_plan_replicas", (16, 8, 10, 2, N, N, N), -1, "null"),
+    ("moe_prediction_quality", (16, 16, 8, N, 0, 16, N), -1, "top_n"),
+    ("moe_prediction_quality", (16, N, 8, N, 5, 16, N), -1, "null"),
+    ("moe_prediction_quality", (16, 16, 257, N, 5, 16, N), -2, "E=257"),
     ("moe_combine", (16, 1, 10, 16, 16, 10, 9, 64, 16, N), -1, "k=9"),
     ("moe_combine", (16, 1, 10, 16, 16, 10, 2, 12, 16, N), -1, "multiple of 16"),
 ])
