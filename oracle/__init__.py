@@ -47,6 +47,7 @@ def lib():
         for name in ("oracle_route", "oracle_histogram", "oracle_cooccurrence", "oracle_popularity",
                      "oracle_conditional", "oracle_predict_next", "oracle_replicas", "oracle_dispatch",
                      "oracle_predicted_counts", "oracle_plan_replicas", "oracle_prediction_quality",
+                     "oracle_decayed_popularity", "oracle_load_anomalies",
                      "oracle_permute", "oracle_ffn_rows", "oracle_combine", "oracle_bf16_round_bits"):
             getattr(_lib, name).restype = ctypes.c_int
     return _lib
@@ -159,6 +160,25 @@ def prediction_quality(p_hat: np.ndarray, counts: np.ndarray, reps: np.ndarray |
     return out
 
 
+def decayed_popularity(hist: np.ndarray, lam: float) -> np.ndarray:
+    """hist [m, E] youngest first (row 0 = the current iteration)."""
+    hist = np.ascontiguousarray(hist, dtype=np.int32)
+    m, E = hist.shape
+    p = np.empty(E, np.float32)
+    lib().oracle_decayed_popularity(_p(hist), m, E, ctypes.c_double(lam), _p(p))
+    return p
+
+
+def load_anomalies(hist: np.ndarray):
+    """(flags int32 [E], [n_flagged, transient]) for hist [m, E] youngest first."""
+    hist = np.ascontiguousarray(hist, dtype=np.int32)
+    m, E = hist.shape
+    flags = np.empty(E, np.int32)
+    summary = np.empty(2, np.int32)
+    lib().oracle_load_anomalies(_p(hist), m, E, _p(flags), _p(summary))
+    return flags, summary
+
+
 class WindowStats:
     """The sliding-window statistics state of a chain of L MoE layers.
 
@@ -183,6 +203,12 @@ class WindowStats:
                 raise ValueError("layer > 0 needs the previous layer's routing")
             self.cooc[s, layer - 1] = cooccurrence(prev_idx, idx, self.E)
         return self.cnt[s, layer].astype(np.int32)
+
+    def history(self, layer: int, it: int) -> np.ndarray:
+        """The recorded counts of `layer` for iterations it, it-1, ... still in the
+        window (youngest first): [min(window, it+1), E]."""
+        m = min(self.window, it + 1)
+        return np.stack([self.cnt[(it - a) % self.window, layer] for a in range(m)]).astype(np.int32)
 
     def window_counts(self, layer: int) -> np.ndarray:
         return self.cnt[:, layer].sum(axis=0)

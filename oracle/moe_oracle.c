@@ -190,6 +190,69 @@ int oracle_predict_next(const float* p_seq, const float* P, int E, float* p_hat)
 }
 
 /*
+ * Decayed window popularity ([GPS] 2.1: the sliding-window average is given a
+ * decay factor against distribution drift).  Reading taken: the m recorded
+ * iterations of the window, youngest first (hist[age*E + e], age 0 = the
+ * current iteration), weigh lambda^age; the weights are formed by repeated
+ * multiplication w_0 = 1, w_{j+1} = w_j * lambda and D[e] = sum_age w_age *
+ * n_e(age) is taken in age order, all in double; p[e] = D[e] / sum_e D[e]
+ * (expert order; 0 when the sum is 0), rounded to fp32.  lambda = 1 is the
+ * plain window of Eq.(1); lambda = 0 keeps the current iteration only.
+ */
+int oracle_decayed_popularity(const int32_t* hist, int m, int E, double lambda, float* p) {
+    double* D = (double*)calloc((size_t)E, sizeof(double));
+    double w = 1.0;
+    for (int age = 0; age < m; ++age) {
+        for (int e = 0; e < E; ++e) D[e] = D[e] + w * (double)hist[(int64_t)age * E + e];
+        w = w * lambda;
+    }
+    double tot = 0.0;
+    for (int e = 0; e < E; ++e) tot = tot + D[e];
+    for (int e = 0; e < E; ++e) p[e] = tot > 0.0 ? (float)(D[e] / tot) : 0.0f;
+    free(D);
+    return 0;
+}
+
+/*
+ * Load-state check ([GPS] 6.1: a load departing from its expectation by more
+ * than twice the history's standard deviation triggers re-evaluation; the
+ * load-prediction study's transient state of obvious load fluctuation versus
+ * the stable state of temporal locality).  Reading taken: the history is the
+ * m - 1 window iterations before the current one (ages 1 .. m-1); with h = m-1
+ * >= 2, expert e is anomalous when (n_e - mu_e)^2 > 4 var_e, mu_e and var_e
+ * being the history's mean and population variance (double, age order; the
+ * square form avoids a square root); with h < 2 every expert is flagged, there
+ * being no history to trust.  The layer is transient when more than a fifth of
+ * its experts are flagged (5 * n_flagged > E; the fraction is a chosen
+ * constant, the pages print none).
+ */
+int oracle_load_anomalies(const int32_t* hist, int m, int E, int32_t* flags, int32_t* summary) {
+    const int h = m - 1;
+    int32_t n = 0;
+    for (int e = 0; e < E; ++e) {
+        int f = 1;
+        if (h >= 2) {
+            double s = 0.0;
+            for (int age = 1; age < m; ++age) s = s + (double)hist[(int64_t)age * E + e];
+            const double mu = s / (double)h;
+            double v = 0.0;
+            for (int age = 1; age < m; ++age) {
+                const double d = (double)hist[(int64_t)age * E + e] - mu;
+                v = v + d * d;
+            }
+            v = v / (double)h;
+            const double d0 = (double)hist[e] - mu;
+            f = d0 * d0 > 4.0 * v;
+        }
+        flags[e] = f;
+        n += f;
+    }
+    summary[0] = n;
+    summary[1] = 5 * n > E;
+    return 0;
+}
+
+/*
  * Replica counts for hot experts.  [GPS] 2.1's duplicate_experts rule gives an
  * expert whose load exceeds the target ceil(load/target) - 1 extra copies;
  * [MPMC] contribution 3 bounds the replica count by a memory budget, and [PF]

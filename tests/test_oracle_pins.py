@@ -482,3 +482,96 @@ def test_prediction_quality_extremes():
     assert q[0] == 1.0 and q[1] == 1.0             # no prediction mass; top-3 of 3 always hits
     q = oracle.prediction_quality(p, np.zeros(3, np.int32), None, 2)
     assert q[0] == 1.0 and q[2] == 0.0 and q[3] == 0.0
+
+
+# ------------------------------------------------------------ window variants
+def _rand_hist(rng, m, E, hi=5000):
+    return rng.integers(0, hi, size=(m, E)).astype(np.int32)
+
+
+def test_decayed_popularity_limits_are_plain_windows():
+    """lambda = 1 is Eq.(1)'s plain window (bit-exact: the double quotient rounds to
+    the same fp32 as the fp32 quotient of exact integers); lambda = 0 keeps only the
+    current iteration."""
+    rng = np.random.default_rng(21)
+    for trial in range(40):
+        m, E = int(rng.integers(1, 12)), int(rng.integers(1, 40))
+        hist = _rand_hist(rng, m, E)
+        assert np.array_equal(oracle.decayed_popularity(hist, 1.0), oracle.popularity(hist.sum(axis=0)))
+        assert np.array_equal(oracle.decayed_popularity(hist, 0.0), oracle.popularity(hist[0].astype(np.int64)))
+
+
+def test_decayed_popularity_exact_rationals():
+    rng = np.random.default_rng(22)
+    for trial in range(40):
+        m, E = int(rng.integers(1, 12)), int(rng.integers(1, 20))
+        lam = float(rng.choice([0.5, 0.75, 0.9, 0.99, 0.3]))
+        hist = _rand_hist(rng, m, E)
+        p = oracle.decayed_popularity(hist, lam)
+        D = [sum(Fraction(lam) ** a * int(hist[a, e]) for a in range(m)) for e in range(E)]
+        tot = sum(D)
+        for e in range(E):
+            ref = float(D[e] / tot) if tot else 0.0
+            assert abs(float(p[e]) - ref) <= 6e-8 * max(ref, 1e-30) + 1e-45
+
+
+def test_decayed_popularity_stationary_counts_ignore_lambda():
+    """Identical counts in every iteration: every decay gives the same shares."""
+    c = np.array([7, 0, 3, 90, 1], np.int32)
+    hist = np.tile(c, (6, 1))
+    ref = oracle.popularity(c.astype(np.int64))
+    for lam in (0.0, 0.2, 0.9, 1.0):
+        assert np.max(np.abs(oracle.decayed_popularity(hist, lam) - ref)) <= 1e-7
+
+
+def test_load_anomalies_hand_cases():
+    flags, summ = oracle.load_anomalies(np.array([[11, 10], [10, 10], [10, 10], [10, 10]], np.int32))
+    assert flags.tolist() == [1, 0] and summ.tolist() == [1, 1]      # zero variance: any change flags
+    flags, summ = oracle.load_anomalies(np.array([[5, 5, 5]], np.int32))
+    assert flags.tolist() == [1, 1, 1] and summ.tolist() == [3, 1]   # no history yet
+    flags, _ = oracle.load_anomalies(np.array([[4, 9], [4, 4], [4, 4]], np.int32))
+    assert flags.tolist() == [0, 1]                                 # h = 2 is enough history
+    # history 0, 10, 0, 10: mean 5, std 5; a load of 15 is at 2 std (not above), 16 is above
+    h = np.array([[15, 16, 5], [0, 0, 0], [10, 10, 10], [0, 0, 0], [10, 10, 10]], np.int32)
+    flags, summ = oracle.load_anomalies(h)
+    assert flags.tolist() == [0, 1, 0] and summ.tolist() == [1, 1]
+    E = 20
+    h = np.tile(np.arange(E, dtype=np.int32), (5, 1))
+    h[0, :4] += 1                                                    # 4 of 20 flagged: not transient
+    assert oracle.load_anomalies(h)[1].tolist() == [4, 0]
+    h[0, 4] += 1                                                     # 5 of 20: 5*5 > 20, transient
+    assert oracle.load_anomalies(h)[1].tolist() == [5, 1]
+
+
+def test_load_anomalies_exact_rationals():
+    rng = np.random.default_rng(23)
+    checked = 0
+    for trial in range(60):
+        m, E = int(rng.integers(3, 12)), int(rng.integers(1, 30))
+        hist = _rand_hist(rng, m, E, hi=int(rng.choice([5, 100, 10000])))
+        flags, summ = oracle.load_anomalies(hist)
+        for e in range(E):
+            hs = [Fraction(int(v)) for v in hist[1:, e]]
+            mu = sum(hs) / len(hs)
+            var = sum((v - mu) ** 2 for v in hs) / len(hs)
+            lhs, rhs = (int(hist[0, e]) - mu) ** 2, 4 * var
+            if lhs != rhs and abs(lhs - rhs) <= Fraction(1, 10 ** 9) * max(lhs, rhs):
+                continue   # too close to call in double
+            assert flags[e] == int(lhs > rhs)
+            checked += 1
+        assert summ[0] == flags.sum() and summ[1] == int(5 * flags.sum() > E)
+    assert checked > 500
+
+
+def test_window_history_matches_ring_order():
+    ws = oracle.WindowStats(1, 3, 4)
+    rng = np.random.default_rng(24)
+    seen = []
+    for it in range(7):
+        idx = rng.integers(0, 3, size=(10, 1)).astype(np.int32)
+        seen.append(oracle.histogram(idx, 3))
+        ws.record(0, it, idx)
+        hist = ws.history(0, it)
+        assert hist.shape[0] == min(4, it + 1)
+        for a in range(hist.shape[0]):
+            assert np.array_equal(hist[a], seen[it - a])
