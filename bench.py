@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--crossover", action="store_true",
                     help="time the grouped and the dense expert-FFN paths on the DeepSeek-V2 T sweep and on the "
                          "GEMM shapes profiled by EPS-MoE, print one JSON line per case, and exit")
+    ap.add_argument("--predict", action="store_true",
+                    help="score the next-layer prediction and the replica plans on the 12-layer chain")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only copy a 256 MiB buffer 3 times (reference for the HBM byte counters) and exit")
     return ap.parse_args()
@@ -182,6 +184,75 @@ def crossover(moe, synth, torch, np):
         time_paths(x, so, se, ns, g1, u1, d1, f"gemm_{M}x{K_}x{N_}", {"M": M, "K": K_, "N": N_})
 
 
+def predict_quality(moe, synth, torch, np, name="popfetcher", R=8, iters=None):
+    """Prediction quality and load balance on a chained workload, all on the GPU.
+
+    Per iteration and layer l >= 1: layer l-1's statistics predict layer l's
+    popularity (moe_stats pred_next); moe_plan_replicas plans R copies from it
+    before layer l routes; after routing, moe_prediction_quality scores the
+    prediction and three plans against the actual counts: no replicas, the
+    predicted plan, and the plan from the actual counts (moe_stats replicas)."""
+    cfg = synth.CONFIGS[name]
+    L, E, k, win, T = cfg.L, cfg.E, cfg.k, cfg.window, cfg.T
+    iters = cfg.iters if iters is None else iters
+    dev = torch.device("cuda:0")
+    state = torch.empty(moe.moe_stats_state_bytes(L, E, win), dtype=torch.uint8, device=dev)
+    moe.moe_stats_init(state, L, E, win)
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    pred = torch.empty(E, dtype=torch.float32, device=dev)
+    reps_now = torch.empty(E, dtype=torch.int32, device=dev)
+    rows = []
+    plan_ev, qual_ev = [], []
+    for it in range(iters):
+        prev_idx, plan, pred_prev = None, None, None
+        top1 = None
+        for layer in range(L):
+            lg = synth.logits(cfg, layer, it, top1)
+            idx, _ = moe.moe_route(torch.from_numpy(lg).to(dev), k)
+            last = layer + 1 >= L
+            moe.moe_stats(state, L, E, win, layer, it, idx, prev_idx, k, counts, None, None,
+                          None if last else pred, R, reps_now)
+            if plan is not None:
+                q = [moe.moe_prediction_quality(pred_prev, counts, r, 5) for r in (None, plan, reps_now)]
+                rows.append((it, layer, torch.stack(q).cpu().numpy()))
+            if not last:
+                pred_prev = pred.clone()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                _, plan = moe.moe_plan_replicas(pred_prev, T * k, R)
+                e1.record()
+                plan_ev.append((e0, e1))
+                q0, q1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                q0.record()
+                moe.moe_prediction_quality(pred_prev, counts, plan, 5)
+                q1.record()
+                qual_ev.append((q0, q1))
+            top1 = idx[:, 0].cpu().numpy()
+            prev_idx = idx
+    torch.cuda.synchronize()
+
+    def summary(sel):
+        a = np.stack([r[2] for r in rows if sel(r)])  # [n, 3 plans, 4 measures]
+        return {"samples": int(a.shape[0]),
+                "tv_distance_mean": round(float(a[:, 1, 0].mean()), 5),
+                "top5_hit_mean": round(float(a[:, 1, 1].mean()), 4),
+                "slot_load_std": {"none": round(float(a[:, 0, 2].mean()), 1),
+                                  "predicted_plan": round(float(a[:, 1, 2].mean()), 1),
+                                  "counts_plan": round(float(a[:, 2, 2].mean()), 1)},
+                "max_over_mean_load": {"none": round(float(a[:, 0, 3].mean()), 3),
+                                       "predicted_plan": round(float(a[:, 1, 3].mean()), 3),
+                                       "counts_plan": round(float(a[:, 2, 3].mean()), 3)}}
+
+    return {"prediction": {
+        "workload": f"{name}-shaped chain: L={L} E={E} k={k} T={T} window={win} iterations={iters} "
+                    f"gamma={cfg.gamma} c={cfg.c}",
+        "replica_budget": R,
+        "all_layers_iterations": summary(lambda r: True),
+        "after_first_iteration": summary(lambda r: r[0] >= 1),
+        "plan_kernel_us": round(float(np.median([a.elapsed_time(b) for a, b in plan_ev])) * 1e3, 2),
+        "quality_kernel_us": round(float(np.median([a.elapsed_time(b) for a, b in qual_ev])) * 1e3, 2)}}
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -207,6 +278,10 @@ def main():
 
     if a.crossover:
         crossover(moe, synth, torch, np)
+        return
+    if a.predict:
+        for name, R in (("popfetcher", 8), ("tiny", 4)):
+            print(json.dumps(predict_quality(moe, synth, torch, np, name, R)), flush=True)
         return
 
     dev = torch.device("cuda:0")

@@ -121,6 +121,32 @@ int moe_stats(void* state, size_t state_bytes, int L, int E, int window, int lay
               int32_t* counts, float* p_seq, float* cond, float* pred_next,
               int replica_budget, int32_t* replicas, void* stream);
 
+/*
+ * moe_stats_load_state -- window variants of layer `layer` after iteration
+ * `iter` has been recorded by moe_stats (read-only on the state):
+ *   p_decay    fp32 [E] (may be NULL): decayed-window popularity ([GPS] 2.1: a
+ *              decay factor on the sliding-window average against drift):
+ *              over the m = min(window, iter+1) recorded iterations, age 0 =
+ *              `iter`, D[e] = sum_age decay^age * n_e(age) (weights by repeated
+ *              multiplication, age order, double), p_decay = D / sum(D)
+ *              (0 when the sum is 0); decay = 1 gives p_seq, decay = 0 this
+ *              iteration's shares;
+ *   anomalous  int32 [E] (may be NULL): 1 where the load of `iter` leaves its
+ *              history by more than twice the standard deviation ([GPS] 6.1),
+ *              (n_e - mean)^2 > 4 var over the m-1 earlier window iterations;
+ *              every expert is flagged while fewer than 2 earlier iterations
+ *              exist;
+ *   summary    int32 [2] (may be NULL): the number of flagged experts, and 1
+ *              if the layer is in a transient state (more than a fifth of its
+ *              experts flagged, a chosen fraction) or 0 if stable (the
+ *              load-prediction study's transient/stable load states).
+ * The ring must hold iterations iter-m+1 .. iter of `layer` (recorded in
+ * order).  Limits: those of moe_stats, 0 <= decay <= 1.
+ */
+int moe_stats_load_state(const void* state, size_t state_bytes, int L, int E, int window, int layer,
+                         int64_t iter, double decay, float* p_decay, int32_t* anomalous, int32_t* summary,
+                         void* stream);
+
 /* ------------------------------------------------ planning ahead of routing
  * moe_plan_replicas -- replica counts for a layer planned before it routes,
  * from a predicted expert distribution ([PF] method: Eq.(3) predicts the next

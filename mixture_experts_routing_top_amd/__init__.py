@@ -22,7 +22,8 @@ import torch
 
 from ._native import LIB_PATH, MoEError, lib
 
-__all__ = ["moe_route", "moe_stats_state_bytes", "moe_stats_init", "moe_stats", "moe_plan_replicas",
+__all__ = ["moe_route", "moe_stats_state_bytes", "moe_stats_init", "moe_stats", "moe_stats_load_state",
+           "moe_plan_replicas",
            "moe_prediction_quality", "moe_dispatch_workspace_bytes",
            "moe_dispatch", "moe_expert_ffn_workspace_bytes", "moe_expert_ffn", "moe_combine", "moe_layer_forward",
            "MoEError", "LIB_PATH", "MOE_F32", "MOE_BF16", "SWIGLU", "GELU", "GEMM_AUTO", "GEMM_GROUPED",
@@ -104,6 +105,20 @@ def moe_stats(state: torch.Tensor, L: int, E: int, window: int, layer: int, it: 
           ctypes.c_int64(it), _ptr(topk_idx), _ptr(prev_topk_idx), ctypes.c_int64(T), k, _ptr(counts), _ptr(p_seq),
           _ptr(cond), _ptr(pred_next), replica_budget, _ptr(replicas), _stream(stream))
     return dict(counts=counts, p_seq=p_seq, cond=cond, pred_next=pred_next, replicas=replicas)
+
+
+def moe_stats_load_state(state: torch.Tensor, L: int, E: int, window: int, layer: int, it: int, decay: float = 0.9,
+                         p_decay=None, anomalous=None, summary=None, stream=None):
+    """Decayed-window popularity, per-expert anomaly flags and [n_flagged, transient]
+    of `layer` after iteration `it` was recorded."""
+    dev = state.device
+    p_decay = torch.empty(E, dtype=torch.float32, device=dev) if p_decay is None else p_decay
+    anomalous = _i32(E, dev) if anomalous is None else anomalous
+    summary = _i32(2, dev) if summary is None else summary
+    _call("moe_stats_load_state", _ptr(state), ctypes.c_size_t(state.numel() * state.element_size()), L, E, window,
+          layer, ctypes.c_int64(it), ctypes.c_double(decay), _ptr(p_decay), _ptr(anomalous), _ptr(summary),
+          _stream(stream))
+    return dict(p_decay=p_decay, anomalous=anomalous, summary=summary)
 
 
 def moe_plan_replicas(pred: torch.Tensor, total: int, replica_budget: int, pred_counts=None, replicas=None,

@@ -13,6 +13,7 @@ SIGNATURES = {
     "moe_stats_state_bytes": (_sz, [_i, _i, _i]),
     "moe_stats_init": (_i, [_p, _sz, _i, _i, _i, _p]),
     "moe_stats": (_i, [_p, _sz, _i, _i, _i, _i, _i64, _p, _p, _i64, _i, _p, _p, _p, _p, _i, _p, _p]),
+    "moe_stats_load_state": (_i, [_p, _sz, _i, _i, _i, _i, _i64, ctypes.c_double, _p, _p, _p, _p]),
     "moe_plan_replicas": (_i, [_p, _i, _i64, _i, _p, _p, _p]),
     "moe_prediction_quality": (_i, [_p, _p, _i, _p, _i, _p, _p]),
     "moe_dispatch_workspace_bytes": (_sz, [_i64, _i, _i]),

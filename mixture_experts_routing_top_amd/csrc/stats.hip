@@ -204,6 +204,72 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(Args a) {
   if (a.idx && tid == 0) atomicExch(ticket, 0u);
 }
 
+// Decayed-window popularity and the load-state check of one layer, read from
+// the count ring (MoE-GPS blog, section 2.1: a decay factor on the sliding
+// window; section 6.1: a load more than twice the history's standard
+// deviation from its expectation; the load-prediction study: transient versus
+// stable load states).  Thread e walks its expert's window youngest first:
+//   D[e] = sum_age decay^age * n_e(age), weights by repeated multiplication;
+//   anomalous when the window holds >= 2 earlier iterations and
+//   (n_e(0) - mean)^2 > 4 * variance over those (else flagged: no history);
+// p_decay = D / sum(D) in expert order; the layer is transient when more than a
+// fifth of the experts are flagged.  Double arithmetic with explicitly rounded
+// operations, in a fixed order, so the results do not depend on scheduling.
+__global__ __launch_bounds__(kThreads) void load_state_kernel(const int32_t* __restrict__ cnt_ring, int L, int E,
+                                                              int window, int layer, int slot0, int m,
+                                                              double decay, float* __restrict__ p_decay,
+                                                              int32_t* __restrict__ flags,
+                                                              int32_t* __restrict__ summary) {
+  __shared__ double D[moe::kMaxExperts];
+  __shared__ double total;
+  __shared__ int n_flagged;
+  const int tid = threadIdx.x;
+  if (tid == 0) n_flagged = 0;
+  __syncthreads();
+  auto at = [&](int age, int e) {
+    int s = slot0 - age;
+    if (s < 0) s += window;
+    return static_cast<double>(cnt_ring[(static_cast<size_t>(s) * L + layer) * E + e]);
+  };
+  if (tid < E) {
+    double d = 0.0, w = 1.0;
+    for (int age = 0; age < m; ++age) {
+      d = __dadd_rn(d, __dmul_rn(w, at(age, tid)));
+      w = __dmul_rn(w, decay);
+    }
+    D[tid] = d;
+    int f = 1;
+    const int h = m - 1;
+    if (h >= 2) {
+      double sum = 0.0;
+      for (int age = 1; age < m; ++age) sum = __dadd_rn(sum, at(age, tid));
+      const double mu = __ddiv_rn(sum, static_cast<double>(h));
+      double var = 0.0;
+      for (int age = 1; age < m; ++age) {
+        const double dd = __dsub_rn(at(age, tid), mu);
+        var = __dadd_rn(var, __dmul_rn(dd, dd));
+      }
+      var = __ddiv_rn(var, static_cast<double>(h));
+      const double d0 = __dsub_rn(at(0, tid), mu);
+      f = __dmul_rn(d0, d0) > __dmul_rn(4.0, var) ? 1 : 0;
+    }
+    if (flags) flags[tid] = f;
+    if (f) atomicAdd(&n_flagged, 1);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    double t = 0.0;
+    for (int e = 0; e < E; ++e) t = __dadd_rn(t, D[e]);
+    total = t;
+    if (summary) {
+      summary[0] = n_flagged;
+      summary[1] = 5 * n_flagged > E ? 1 : 0;
+    }
+  }
+  __syncthreads();
+  if (tid < E && p_decay) p_decay[tid] = total > 0.0 ? static_cast<float>(__ddiv_rn(D[tid], total)) : 0.0f;
+}
+
 __global__ void zero_words(int32_t* p, size_t n) {
   for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
        i += static_cast<size_t>(gridDim.x) * blockDim.x)
@@ -272,4 +338,25 @@ extern "C" int moe_stats(void* state, size_t state_bytes, int L, int E, int wind
   const unsigned blocks = topk_idx ? static_cast<unsigned>(std::max<int64_t>(1, ceil_div(T, kTokPerBlock))) : 1u;
   stats_kernel<<<blocks, kThreads, 0, as_stream(stream)>>>(a);
   return hip_status(hipGetLastError(), "moe_stats launch");
+}
+
+extern "C" int moe_stats_load_state(const void* state, size_t state_bytes, int L, int E, int window, int layer,
+                                    int64_t iter, double decay, float* p_decay, int32_t* anomalous,
+                                    int32_t* summary, void* stream) {
+  using namespace moe;
+  if (!dims_ok(L, E, window)) return fail(E > kMaxExperts ? MOE_ERR_UNSUPPORTED : MOE_ERR_INVALID_ARG,
+                                          "moe_stats_load_state: bad L=%d E=%d window=%d", L, E, window);
+  if (!state) return fail(MOE_ERR_INVALID_ARG, "moe_stats_load_state: null state");
+  if (state_bytes < moe_stats_state_bytes(L, E, window))
+    return fail(MOE_ERR_WORKSPACE, "moe_stats_load_state: state too small (%zu bytes)", state_bytes);
+  if (layer < 0 || layer >= L)
+    return fail(MOE_ERR_INVALID_ARG, "moe_stats_load_state: layer=%d outside [0, %d)", layer, L);
+  if (iter < 0) return fail(MOE_ERR_INVALID_ARG, "moe_stats_load_state: iter < 0");
+  if (!(decay >= 0.0 && decay <= 1.0)) return fail(MOE_ERR_INVALID_ARG, "moe_stats_load_state: decay outside [0, 1]");
+  const Layout lay = layout(L, E, window);
+  const int m = static_cast<int>(std::min<int64_t>(window, iter + 1));
+  load_state_kernel<<<1, kThreads, 0, as_stream(stream)>>>(static_cast<const int32_t*>(state) + lay.cnt_ring, L, E,
+                                                            window, layer, static_cast<int>(iter % window), m, decay,
+                                                            p_decay, anomalous, summary);
+  return hip_status(hipGetLastError(), "moe_stats_load_state launch");
 }

@@ -72,6 +72,10 @@ N = None
     ("moe_expert_ffn", (16, 1, 100, 128, 128, 8, 16, 16, 16, 8, 16, N, 16, 0, 1, 16, 16, 1 << 30, N), -1, "w_up"),
     ("moe_expert_ffn", (16, 1, 100, 128, 128, 8, 16, 16, 16, 8, 16, 16, 16, 1, 1, 16, 16, 1 << 30, N), -1, "GELU"),
     ("moe_expert_ffn", (16, 1, 100, 128, 128, 8, 16, 16, 16, 8, 16, 16, 16, 0, 1, 16, 16, 10, N), -3, "workspace"),
+    ("moe_stats_load_state", (1, 1 << 20, 2, 8, 10, 0, 0, 1.5, N, N, N, N), -1, "decay"),
+    ("moe_stats_load_state", (1, 1 << 20, 2, 8, 10, 2, 0, 0.9, N, N, N, N), -1, "layer=2"),
+    ("moe_stats_load_state", (1, 8, 2, 8, 10, 0, 0, 0.9, N, N, N, N), -3, "too small"),
+    ("moe_stats_load_state", (1, 1 << 20, 2, 8, 10, 0, -1, 0.9, N, N, N, N), -1, "iter"),
     ("moe_plan_replicas", (16, 0, 10, 2, N, 16, N), -1, "E=0"),
     ("moe_plan_replicas", (16, 300, 10, 2, N, 16, N), -2, "E=300"),
     ("moe_plan_replicas", (16, 8, -1, 2, N, 16, N), -1, "total"),
