@@ -21,6 +21,7 @@ the CPU oracle timed on a bounded sample on this host.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -49,6 +50,8 @@ def parse():
     ap.add_argument("--crossover", action="store_true",
                     help="time the grouped and the dense expert-FFN paths on the DeepSeek-V2 T sweep and on the "
                          "GEMM shapes profiled by EPS-MoE, print one JSON line per case, and exit")
+    ap.add_argument("--pipeline", action="store_true",
+                    help="horizontal-split pipeline and memory kernels on CU-masked streams (Mixtral layer)")
     ap.add_argument("--predict", action="store_true",
                     help="score the next-layer prediction and the replica plans on the 12-layer chain")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -253,6 +256,97 @@ def predict_quality(moe, synth, torch, np, name="popfetcher", R=8, iters=None):
         "quality_kernel_us": round(float(np.median([a.elapsed_time(b) for a, b in qual_ev])) * 1e3, 2)}}
 
 
+def cu_masked_stream(torch, n_cu, total):
+    """A stream limited to n_cu compute units, spread evenly over the 8 XCDs under
+    either CU numbering (XCD-major or XCD-interleaved bits); None if refused."""
+    words = [0] * (total // 32)
+    per = n_cu // 8
+    if n_cu >= total:
+        words = [0xFFFFFFFF] * (total // 32)
+    else:
+        for x in range(8):
+            for m in range(per):
+                words[x] |= 1 << ((x + 8 * m) % 32 if per <= 4 else m)
+    hip = ctypes.CDLL("libamdhip64.so")
+    arr = (ctypes.c_uint32 * len(words))(*words)
+    handle = ctypes.c_void_p()
+    if hip.hipExtStreamCreateWithCUMask(ctypes.byref(handle), ctypes.c_uint32(len(words)), arr) != 0:
+        return None, None
+    return torch.cuda.ExternalStream(handle.value), (hip, handle)
+
+
+def pipeline_bench(moe, synth, torch, np, steps=10, warmup=3):
+    """EPS-MoE's horizontal split on one GPU: the Mixtral layer unsplit versus split
+    into n chunks over a compute and a memory stream; and the memory-bound kernels
+    alone on streams limited to n CUs (do they, like communication kernels, need
+    only a few?).  No replication, grouped GEMM path."""
+    cfg = synth.CONFIGS["mixtral"]
+    T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
+    dev = torch.device("cuda:0")
+
+    def dev_bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    wg, wu, wd = (dev_bf16(w) for w in synth.expert_weights(cfg, threads=16))
+    x = dev_bf16(synth.hidden0(cfg, 0))
+    logits = torch.from_numpy(synth.logits(cfg, 0, 0)).to(dev)
+    cs = torch.cuda.current_stream()
+
+    def timed(fn, stream):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(steps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    res = {"workload": f"Mixtral-shaped layer T={T} H={H} I={I} E={E} k={k} bf16, no replication"}
+    bufs = {}
+    ref = None
+    base = timed(lambda: moe.moe_layer_forward(x, logits, k, wg, wu, wd, "swiglu", 0, bufs=bufs, stream=cs), cs)
+    ref = bufs["out"].clone()
+    res["unsplit_ms"] = round(base, 4)
+    total_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    ms = torch.cuda.Stream()
+    split = {}
+    for n in (1, 2, 4, 8):
+        pb = {}
+        t = timed(lambda: moe.moe_layer_forward_pipelined(x, logits, k, wg, wu, wd, "swiglu", n, cs, ms, pb), cs)
+        split[n] = {"ms": round(t, 4), "speedup": round(base / t, 4), "bit_identical": bool(torch.equal(pb["out"], ref))}
+    res["split_two_streams"] = split
+    sweep, handles = {}, []
+    d = moe.moe_dispatch(x, bufs["idx"], E, None, E)
+    y = d["x_perm"]
+    ws = torch.empty(moe.moe_dispatch_workspace_bytes(T, k, E), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(x)
+    row_bytes = (k + 1) * T * H * 2   # permute: x + x_perm; combine: y_perm + out
+    for n_cu in (8, 16, 32, 64, 128, total_cu):
+        st, h = cu_masked_stream(torch, n_cu, total_cu)
+        if st is None:
+            sweep[n_cu] = "stream creation refused"
+            continue
+        handles.append(h)
+        td = timed(lambda: moe.moe_dispatch(x, bufs["idx"], E, None, E, d, ws, st), st)
+        tc = timed(lambda: moe.moe_combine(y, d["inv_pos"], bufs["w"], out, st), st)
+        sweep[n_cu] = {"dispatch_us": round(td * 1e3, 1), "combine_us": round(tc * 1e3, 1),
+                       "dispatch_TBps": round(row_bytes / (td * 1e-3) / 1e12, 2),
+                       "combine_TBps": round(row_bytes / (tc * 1e-3) / 1e12, 2)}
+        if n_cu in (32, 64):
+            pb = {}
+            t = timed(lambda: moe.moe_layer_forward_pipelined(x, logits, k, wg, wu, wd, "swiglu", 4, cs, st, pb), cs)
+            sweep[n_cu]["split4_memory_stream_ms"] = round(t, 4)
+            sweep[n_cu]["split4_bit_identical"] = bool(torch.equal(pb["out"], ref))
+    torch.cuda.synchronize()
+    for hip, h in handles:
+        hip.hipStreamDestroy(h)
+    res["memory_kernels_on_n_cus"] = sweep
+    return {"pipeline": res}
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -278,6 +372,9 @@ def main():
 
     if a.crossover:
         crossover(moe, synth, torch, np)
+        return
+    if a.pipeline:
+        print(json.dumps(pipeline_bench(moe, synth, torch, np)), flush=True)
         return
     if a.predict:
         for name, R in (("popfetcher", 8), ("tiny", 4)):

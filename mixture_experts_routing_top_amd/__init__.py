@@ -26,6 +26,7 @@ __all__ = ["moe_route", "moe_stats_state_bytes", "moe_stats_init", "moe_stats", 
            "moe_plan_replicas",
            "moe_prediction_quality", "moe_dispatch_workspace_bytes",
            "moe_dispatch", "moe_expert_ffn_workspace_bytes", "moe_expert_ffn", "moe_combine", "moe_layer_forward",
+           "moe_layer_forward_pipelined",
            "MoEError", "LIB_PATH", "MOE_F32", "MOE_BF16", "SWIGLU", "GELU", "GEMM_AUTO", "GEMM_GROUPED",
            "GEMM_DENSE"]
 
@@ -267,3 +268,71 @@ def moe_layer_forward(x, logits, k, w_gate, w_up, w_down, act="swiglu", replica_
     res.update(d)
     res.update(y_perm=y, out=out)
     return res
+
+
+# ------------------------------------------- one layer, horizontally split
+def moe_layer_forward_pipelined(x, logits, k, w_gate, w_up, w_down, act="swiglu", n_chunks=2, compute_stream=None,
+                                memory_stream=None, bufs=None):
+    """The layer split by rows into n_chunks token chunks, pipelined over two streams
+    (EPS-MoE review, section 3: horizontal split of the input by rows, weights
+    split by expert; the memory-bound kernels need few SMs and overlap the
+    expert GEMMs).
+
+    memory_stream: route, then every chunk's dispatch, then every chunk's
+    combine (each waiting for its chunk's FFN); compute_stream: every chunk's
+    expert FFN (each waiting for its dispatch).  Chunk c+1's dispatch can run
+    while chunk c's GEMMs run, and chunk c's combine while chunk c+1's run.  The
+    grouped GEMM path is used (no host readback), without replication; every
+    output row depends only on its token, so the result equals
+    moe_layer_forward's bit for bit.  The compute stream waits for the whole
+    layer at the end; `bufs` caches the per-chunk buffers between calls."""
+    T, E = logits.shape
+    H = x.shape[1]
+    I = w_gate.shape[1]
+    dev = x.device
+    cs = compute_stream if compute_stream is not None else torch.cuda.current_stream()
+    ms = memory_stream if memory_stream is not None else cs
+    b = bufs if bufs is not None else {}
+    start = torch.cuda.Event()
+    start.record(cs)
+    ms.wait_event(start)
+    idx, w = moe_route(logits, k, b.get("idx"), b.get("w"), ms)
+    b["idx"], b["w"] = idx, w
+    out = b.get("out")
+    if out is None or out.shape != (T, H) or out.dtype != x.dtype:
+        out = b["out"] = torch.empty((T, H), dtype=x.dtype, device=dev)
+    bounds = [T * c // n_chunks for c in range(n_chunks + 1)]
+    chunks = [(c, bounds[c], bounds[c + 1]) for c in range(n_chunks) if bounds[c + 1] > bounds[c]]
+    t_max = max(t1 - t0 for _, t0, t1 in chunks) if chunks else 0
+    if b.get("_ws_key") != (t_max, k, E, H, I, x.dtype):
+        b["ws_d"] = torch.empty(moe_dispatch_workspace_bytes(t_max, k, E), dtype=torch.uint8, device=dev)
+        b["ws_f"] = torch.empty(moe_expert_ffn_workspace_bytes(x.dtype, t_max * k, H, I, E), dtype=torch.uint8,
+                                device=dev)
+        b["_ws_key"] = (t_max, k, E, H, I, x.dtype)
+        for c in range(n_chunks):
+            b.pop(("chunk", c), None)
+    disp, done_d = {}, {}
+    for c, t0, t1 in chunks:
+        cb = b.setdefault(("chunk", c), {})
+        disp[c] = moe_dispatch(x[t0:t1], idx[t0:t1], E, None, E, cb.get("disp"), b["ws_d"], ms)
+        cb["disp"] = disp[c]
+        done_d[c] = torch.cuda.Event()
+        done_d[c].record(ms)
+    done_f = {}
+    for c, t0, t1 in chunks:
+        cb = b[("chunk", c)]
+        d = disp[c]
+        if "y_perm" not in cb or cb["y_perm"].shape != d["x_perm"].shape:
+            cb["y_perm"] = torch.empty_like(d["x_perm"])
+        cs.wait_event(done_d[c])
+        moe_expert_ffn(d["x_perm"], d["slot_off"], d["slot_expert"], d["n_slots"], w_gate, w_up, w_down, act,
+                       "grouped", cb["y_perm"], b["ws_f"], cs)
+        done_f[c] = torch.cuda.Event()
+        done_f[c].record(cs)
+    for c, t0, t1 in chunks:
+        ms.wait_event(done_f[c])
+        moe_combine(b[("chunk", c)]["y_perm"], disp[c]["inv_pos"], w[t0:t1], out[t0:t1], ms)
+    end = torch.cuda.Event()
+    end.record(ms)
+    cs.wait_event(end)
+    return {"idx": idx, "w": w, "out": out}
