@@ -575,3 +575,88 @@ def test_window_history_matches_ring_order():
         assert hist.shape[0] == min(4, it + 1)
         for a in range(hist.shape[0]):
             assert np.array_equal(hist[a], seen[it - a])
+
+
+# ------------------------------------------------------------------ backward
+def _torch_layer_grads(x, logits, idx, weights, act, d_out):
+    """Gradients by torch autograd in float64 of the forward written as plain tensor
+    ops: kept-logit softmax, per-(token, slot) expert FFN, weighted sum."""
+    f = lambda a: torch.tensor(synth.bf16_bits_to_f32(a) if a.dtype == np.uint16 else a, dtype=torch.float64,
+                               requires_grad=True)
+    X, Lg = f(x), torch.tensor(logits, dtype=torch.float64, requires_grad=True)
+    Wg, Wd = f(weights[0]), f(weights[2])
+    Wu = None if weights[1] is None else f(weights[1])
+    it = torch.from_numpy(idx.astype(np.int64))
+    w = torch.softmax(torch.gather(Lg, 1, it), dim=1)
+    out = torch.zeros_like(X)
+    for i in range(idx.shape[1]):
+        e = it[:, i]
+        if Wu is not None:
+            h = torch.nn.functional.silu(torch.einsum("th,tih->ti", X, Wg[e])) * torch.einsum("th,tih->ti", X, Wu[e])
+        else:
+            z = torch.einsum("th,tih->ti", X, Wg[e])
+            h = 0.5 * z * (1 + torch.erf(z / math.sqrt(2.0)))
+        out = out + w[:, i:i + 1] * torch.einsum("ti,thi->th", h, Wd[e])
+    dO = torch.tensor(synth.bf16_bits_to_f32(d_out) if d_out.dtype == np.uint16 else d_out, dtype=torch.float64)
+    (out * dO).sum().backward()
+    return dict(d_x=X.grad.numpy(), d_logits=Lg.grad.numpy(), d_w_gate=Wg.grad.numpy(),
+                d_w_up=None if Wu is None else Wu.grad.numpy(), d_w_down=Wd.grad.numpy())
+
+
+def _bw_case(name, T, seed):
+    from oracle import backward as ob
+    cfg = {"swiglu-f32": synth.CONFIGS["tiny"].scaled(T=T),
+           "gelu-f32": synth.CONFIGS["popfetcher"].scaled(T=T, H=64, I=96, E=6, L=1),
+           "swiglu-bf16": synth.CONFIGS["dbrx"].scaled(T=T, H=64, I=128, E=5)}[name]
+    rng = np.random.default_rng(seed)
+    x = synth.hidden0(cfg, seed)
+    lg = synth.logits(cfg, 0, seed)
+    idx, w = oracle.route(lg, cfg.k)
+    wts = synth.expert_weights(cfg, 0)
+    d_out = rng.standard_normal((cfg.T, cfg.H)).astype(np.float32)
+    if cfg.dtype == "bf16":
+        d_out = synth.f32_to_bf16_bits(d_out)
+    return cfg, x, lg, idx, w, wts, d_out, ob.layer_backward(x, idx, w, wts, cfg.act, d_out)
+
+
+@pytest.mark.parametrize("name", ["swiglu-f32", "gelu-f32", "swiglu-bf16"])
+def test_backward_matches_torch_autograd_fp64(name):
+    """An independent implementation of the gradients (torch autograd in float64 on
+    plain tensor ops) agrees with the oracle's written-out chain rule to the
+    dtype's rounding of the intermediates."""
+    cfg, x, lg, idx, w, wts, d_out, got = _bw_case(name, 40, 5)
+    ref = _torch_layer_grads(x, lg, idx, wts, cfg.act, d_out)
+    tol = 1e-5 if cfg.dtype == "f32" else 2e-2
+    for key in ("d_x", "d_w_gate", "d_w_up", "d_w_down", "d_logits"):
+        if ref[key] is None:
+            assert got[key] is None
+            continue
+        g = got[key]
+        g = synth.bf16_bits_to_f32(g).astype(np.float64) if g.dtype == np.uint16 else g.astype(np.float64)
+        rel = np.linalg.norm(g - ref[key]) / np.linalg.norm(ref[key])
+        assert rel <= tol, (key, rel)
+
+
+def test_backward_gate_invariants():
+    """Softmax-Jacobian rows sum to zero; only kept experts get a logit gradient;
+    a single expert (k = E = 1) has none at all."""
+    cfg, x, lg, idx, w, wts, d_out, got = _bw_case("swiglu-f32", 64, 6)
+    dl = got["d_logits"].astype(np.float64)
+    assert np.all(np.abs(dl.sum(axis=1)) <= 1e-6 * (1 + np.abs(dl).sum(axis=1)))
+    kept = np.zeros_like(dl, dtype=bool)
+    np.put_along_axis(kept, idx.astype(np.int64), True, axis=1)
+    assert np.all(dl[~kept] == 0)
+    from oracle import backward as ob
+    one = synth.CONFIGS["tiny"].scaled(T=16, E=1, k=1)
+    x1, w1 = synth.hidden0(one, 0), synth.expert_weights(one, 0)
+    i1, g1 = oracle.route(synth.logits(one, 0, 0), 1)
+    r = ob.layer_backward(x1, i1, g1, w1, "swiglu", np.ones((16, one.H), np.float32))
+    assert np.all(r["d_logits"] == 0)
+
+
+def test_backward_is_linear_in_d_out():
+    from oracle import backward as ob
+    cfg, x, lg, idx, w, wts, d_out, got = _bw_case("gelu-f32", 24, 7)
+    twice = ob.layer_backward(x, idx, w, wts, cfg.act, (2 * d_out).astype(np.float32))
+    for key in ("d_x", "d_w_gate", "d_w_down"):
+        assert np.array_equal(twice[key], 2 * got[key])   # power-of-two scaling is exact
