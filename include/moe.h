@@ -5,8 +5,9 @@
  *   moe_route -> moe_stats -> moe_dispatch -> moe_expert_ffn -> moe_combine
  *
  * plus moe_plan_replicas (a replica plan for the next layer from moe_stats'
- * prediction, made before that layer routes) and moe_prediction_quality (how
- * well the prediction and the plan matched the routing that followed).
+ * prediction, made before that layer routes), moe_prediction_quality (how
+ * well the prediction and the plan matched the routing that followed),
+ * moe_stats_load_state (window variants) and moe_backward (the gradients).
  *
  * Sources (page title, section):
  *   [PF]   "PopFetcher: Towards Accelerated Mixture-of-Experts Training Via
@@ -273,6 +274,38 @@ int moe_combine(const void* y_perm, moe_dtype dt, int64_t M, const int32_t* inv_
  * NULL or none is (MOE_ERR_INVALID_ARG otherwise).
  */
 int moe_ffn_set_timing_events(void* before_gateup, void* after_gateup, void* after_down);
+
+/* ----------------------------------------------------------------- backward
+ * moe_backward -- gradients of the layer w.r.t. its tokens, router logits and
+ * expert weights, given d_out = dLoss/d out (training, as in [PF] method: the
+ * backward pass of MoE training with its reverse All-to-All, here local).  The
+ * chain rule through the forward above:
+ *   dw[t,i]      = <d_out[t], y_perm[inv_pos[t,i]]>            (fp32)
+ *   d_logits     fp32 [T, E]: w_j (dw_j - sum_i w_i dw_i) at e = topk_idx[t,j],
+ *                0 elsewhere (softmax over the kept logits);
+ *   d_y[r]       = w[t,i] d_out[t] for r = inv_pos[t,i]       (dtype);
+ *   pre-activations g = x Wg^T, u = x Wu^T (GELU: z = x W1^T) recomputed by
+ *   the grouped GEMM and kept in fp32;
+ *   d_g | d_u    = d_h u silu'(g) | d_h silu(g) with d_h = d_y Wd (GELU:
+ *                d_z = d_h gelu'(z)), rounded to the dtype;
+ *   d_x[t]       = sum_i d_x_perm[inv_pos[t,i]], d_x_perm = d_g Wg + d_u Wu;
+ *   d_w_down[e]  = sum over expert e's rows of d_y^T h ([E, H, I]);
+ *   d_w_gate[e], d_w_up[e] = sum over the rows of d_g^T x_perm, d_u^T x_perm
+ *                ([E, I, H]; GELU: d_w_gate is d_W1, w_up and d_w_up NULL).
+ * Inputs are the forward's own: x_perm and expert_off from moe_dispatch (rows
+ * grouped by expert; replica slots do not matter here), y_perm from
+ * moe_expert_ffn, topk_idx/topk_w from moe_route, inv_pos from moe_dispatch.
+ * All gradients are written whole (experts with no rows get zero weight
+ * gradients).  Workspace: moe_backward_workspace_bytes(...) bytes (fp32
+ * pre-activations, transposed weights, expert-padded transposed activations).
+ * Limits: those of moe_expert_ffn; T*k < 2^30.
+ */
+size_t moe_backward_workspace_bytes(moe_dtype dt, int64_t T, int k, int H, int I, int E, moe_act act); /* [host] */
+int moe_backward(const void* x_perm, const void* y_perm, moe_dtype dt, int64_t T, int k, int H, int I, int E,
+                 const int32_t* topk_idx, const float* topk_w, const int32_t* inv_pos, const int32_t* expert_off,
+                 const void* w_gate, const void* w_up, const void* w_down, moe_act act, const void* d_out,
+                 void* d_x, float* d_logits, void* d_w_gate, void* d_w_up, void* d_w_down, void* workspace,
+                 size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------- errors */
 const char* moe_status_string(int status); /* [host] static text */

@@ -26,7 +26,7 @@ __all__ = ["moe_route", "moe_stats_state_bytes", "moe_stats_init", "moe_stats", 
            "moe_plan_replicas",
            "moe_prediction_quality", "moe_dispatch_workspace_bytes",
            "moe_dispatch", "moe_expert_ffn_workspace_bytes", "moe_expert_ffn", "moe_combine", "moe_layer_forward",
-           "moe_layer_forward_pipelined",
+           "moe_layer_forward_pipelined", "moe_backward_workspace_bytes", "moe_backward",
            "MoEError", "LIB_PATH", "MOE_F32", "MOE_BF16", "SWIGLU", "GELU", "GEMM_AUTO", "GEMM_GROUPED",
            "GEMM_DENSE"]
 
@@ -206,6 +206,38 @@ def moe_combine(y_perm: torch.Tensor, inv_pos: torch.Tensor, topk_w: torch.Tenso
     _call("moe_combine", _ptr(y_perm), _dtype_code(y_perm), ctypes.c_int64(M), _ptr(inv_pos), _ptr(topk_w),
           ctypes.c_int64(T), k, H, _ptr(out), _stream(stream))
     return out
+
+
+# ----------------------------------------------------------------- backward
+def moe_backward_workspace_bytes(dtype, T: int, k: int, H: int, I: int, E: int, act="swiglu") -> int:
+    code = dtype if isinstance(dtype, int) else (MOE_BF16 if dtype == torch.bfloat16 else MOE_F32)
+    return int(lib().moe_backward_workspace_bytes(code, ctypes.c_int64(T), k, H, I, E, _ACT[act]))
+
+
+def moe_backward(x_perm, y_perm, topk_idx, topk_w, inv_pos, expert_off, w_gate, w_up, w_down, d_out, act="swiglu",
+                 out=None, workspace=None, stream=None):
+    """Gradients of the layer given d_out: dict(d_x, d_logits, d_w_gate, d_w_up, d_w_down).
+    x_perm, inv_pos, expert_off from moe_dispatch; y_perm from moe_expert_ffn; the
+    routing from moe_route."""
+    T, k = topk_idx.shape
+    M, H = x_perm.shape
+    E, I, _ = w_gate.shape
+    dev = x_perm.device
+    o = dict(out or {})
+    o.setdefault("d_x", torch.empty((T, H), dtype=x_perm.dtype, device=dev))
+    o.setdefault("d_logits", torch.empty((T, E), dtype=torch.float32, device=dev))
+    o.setdefault("d_w_gate", torch.empty_like(w_gate))
+    if w_up is not None:
+        o.setdefault("d_w_up", torch.empty_like(w_up))
+    o.setdefault("d_w_down", torch.empty_like(w_down))
+    if workspace is None:
+        workspace = torch.empty(moe_backward_workspace_bytes(x_perm.dtype, T, k, H, I, E, act), dtype=torch.uint8,
+                                device=dev)
+    _call("moe_backward", _ptr(x_perm), _ptr(y_perm), _dtype_code(x_perm), ctypes.c_int64(T), k, H, I, E,
+          _ptr(topk_idx), _ptr(topk_w), _ptr(inv_pos), _ptr(expert_off), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
+          _ACT[act], _ptr(d_out), _ptr(o["d_x"]), _ptr(o["d_logits"]), _ptr(o["d_w_gate"]), _ptr(o.get("d_w_up")),
+          _ptr(o["d_w_down"]), _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream(stream))
+    return o
 
 
 # ------------------------------------------------------ one layer, composed

@@ -21,6 +21,9 @@ SIGNATURES = {
     "moe_expert_ffn_workspace_bytes": (_sz, [_i, _i64, _i, _i, _i]),
     "moe_expert_ffn": (_i, [_p, _i, _i64, _i, _i, _i, _p, _p, _p, _i, _p, _p, _p, _i, _i, _p, _p, _sz, _p]),
     "moe_combine": (_i, [_p, _i, _i64, _p, _p, _i64, _i, _i, _p, _p]),
+    "moe_backward_workspace_bytes": (_sz, [_i, _i64, _i, _i, _i, _i, _i]),
+    "moe_backward": (_i, [_p, _p, _i, _i64, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _i, _p, _p, _p, _p, _p, _p,
+                          _p, _sz, _p]),
     "moe_ffn_set_timing_events": (_i, [_p, _p, _p]),
     "moe_status_string": (ctypes.c_char_p, [_i]),
     "moe_last_error": (ctypes.c_char_p, []),

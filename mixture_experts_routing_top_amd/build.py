@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe_mi355x.so")
-SOURCES = ["status.cpp", "route.hip", "stats.hip", "plan.hip", "dispatch.hip", "ffn.hip", "combine.hip"]
+SOURCES = ["status.cpp", "route.hip", "stats.hip", "plan.hip", "dispatch.hip", "ffn.hip", "combine.hip", "backward.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 CFLAGS = ["-x", "hip", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

@@ -1,0 +1,439 @@
+// moe_backward: gradients of one MoE layer's forward pass w.r.t. its input
+// tokens, its router logits and its expert weights, given d_out.
+//
+// Sources: PopFetcher wiki, method (MoE training: the backward pass follows
+// the forward, with its own All-to-All in the opposite direction); the
+// expert-load prediction study (training iterations); EPS-MoE review, section
+// 3 (the expert GEMMs are the compute-bound part; GroupGemm per expert).  The
+// gradients themselves are the chain rule through the forward's definition.
+//
+// Stream-ordered steps (M = T*k rows in expert-contiguous order, as dispatched):
+//   1. gate + combine transpose, one block per token: dw[t,i] = <d_out[t],
+//      y_perm[r]>, d_y[r] = w[t,i] d_out[t] for r = inv_pos[t,i], and the
+//      softmax Jacobian over the kept logits, d_l[t,e_j] = w_j (dw_j - sum_i
+//      w_i dw_i) (zero for the other experts);
+//   2. the gate/up (or W1) pre-activations recomputed by the grouped GEMM and
+//      kept in fp32 (activation recomputation rather than a saved [M, 2I]);
+//   3. d_h = d_y Wd by the grouped GEMM on transposed down weights, with the
+//      activation gradient in its epilogue -> d_g | d_u (or d_z), in the dtype;
+//   4. weight gradient of Wd: d_y and h (from the fp32 pre-activations, rounded
+//      exactly as the forward rounds it) transposed into per-expert K ranges
+//      padded to the K step, then one expert-grouped GEMM;
+//   5. d_x_perm = d_g Wg + d_u Wu as one GEMM with K = 2I over [Wg; Wu]^T;
+//   6. d_x = the unweighted sum of each token's k rows (the combine kernel);
+//   7. weight gradients of Wg, Wu (or W1) from d_g | d_u and x_perm, transposed
+//      the same way.
+#include <algorithm>
+
+#include "common.h"
+#include "gemm.h"
+
+namespace {
+
+constexpr int kTok = 256;  // threads per token block in step 1
+
+// Step 1.  Thread tid handles 16-byte chunks tid, tid + 256, ... of the row.
+template <bool kBf16>
+__global__ __launch_bounds__(kTok) void gate_backward_kernel(const uint4* __restrict__ d_out,
+                                                             const uint4* __restrict__ y_perm, int64_t M,
+                                                             const int32_t* __restrict__ topk_idx,
+                                                             const float* __restrict__ topk_w,
+                                                             const int32_t* __restrict__ inv_pos, int k, int E,
+                                                             int chunks, uint4* __restrict__ d_y,
+                                                             float* __restrict__ d_logits) {
+  __shared__ float part[kTok / 64][moe::kMaxTopK];
+  __shared__ float dw[moe::kMaxTopK];
+  const int64_t t = blockIdx.x;
+  const int tid = threadIdx.x;
+  int32_t rows[moe::kMaxTopK];
+  float wi[moe::kMaxTopK], acc[moe::kMaxTopK];
+#pragma unroll
+  for (int i = 0; i < moe::kMaxTopK; ++i) {
+    rows[i] = -1;
+    wi[i] = 0.f;
+    acc[i] = 0.f;
+    if (i < k) {
+      const int32_t r = inv_pos[t * k + i];
+      rows[i] = (r >= 0 && r < M) ? r : -1;
+      wi[i] = topk_w[t * k + i];
+    }
+  }
+  constexpr int V = kBf16 ? 8 : 4;
+  for (int c = tid; c < chunks; c += kTok) {
+    const uint4 q = d_out[t * chunks + c];
+    const uint32_t qv[4] = {q.x, q.y, q.z, q.w};
+    float o[V];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (kBf16) {
+        o[2 * j] = bf16_bits_to_f32(qv[j] & 0xffffu);
+        o[2 * j + 1] = bf16_bits_to_f32(qv[j] >> 16);
+      } else {
+        o[j] = __uint_as_float(qv[j]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < moe::kMaxTopK; ++i) {
+      if (i >= k || rows[i] < 0) continue;
+      const uint4 yq = y_perm[static_cast<int64_t>(rows[i]) * chunks + c];
+      const uint32_t yv[4] = {yq.x, yq.y, yq.z, yq.w};
+      uint32_t dv[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if constexpr (kBf16) {
+          acc[i] = fmaf(o[2 * j], bf16_bits_to_f32(yv[j] & 0xffffu), acc[i]);
+          acc[i] = fmaf(o[2 * j + 1], bf16_bits_to_f32(yv[j] >> 16), acc[i]);
+          dv[j] = f32_to_bf16_bits(wi[i] * o[2 * j]) | (f32_to_bf16_bits(wi[i] * o[2 * j + 1]) << 16);
+        } else {
+          acc[i] = fmaf(o[j], __uint_as_float(yv[j]), acc[i]);
+          dv[j] = __float_as_uint(wi[i] * o[j]);
+        }
+      }
+      d_y[static_cast<int64_t>(rows[i]) * chunks + c] = make_uint4(dv[0], dv[1], dv[2], dv[3]);
+    }
+  }
+  // block reduction of the k dot products, in a fixed order
+  const int lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+  for (int i = 0; i < moe::kMaxTopK; ++i) {
+    if (i >= k) break;
+    float v = acc[i];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+    if (lane == 0) part[wave][i] = v;
+  }
+  __syncthreads();
+  if (tid < k) {
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < kTok / 64; ++w) v += part[w][tid];
+    dw[tid] = v;
+  }
+  __syncthreads();
+  float s = 0.f;
+  for (int i = 0; i < k; ++i) s = fmaf(wi[i], dw[i], s);
+  for (int e = tid; e < E; e += kTok) {
+    float v = 0.f;
+    for (int i = 0; i < k; ++i)
+      if (topk_idx[t * k + i] == e && rows[i] >= 0) v = wi[i] * (dw[i] - s);
+    d_logits[t * E + e] = v;
+  }
+}
+
+// dst[b][c][col_off + r] = src[b][r][c] for a batch of R x C matrices; dst rows
+// are ld elements long.  64 x 64 tiles through LDS.
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ src, int R, int C, T* __restrict__ dst,
+                                                        int ld, int col_off) {
+  __shared__ T tile[64][65];
+  const int b = blockIdx.z;
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const T* s = src + static_cast<int64_t>(b) * R * C;
+  T* d = dst + static_cast<int64_t>(b) * C * ld;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int y = ty; y < 64; y += 4)
+    if (r0 + y < R && c0 + tx < C) tile[y][tx] = s[static_cast<int64_t>(r0 + y) * C + c0 + tx];
+  __syncthreads();
+  for (int y = ty; y < 64; y += 4)
+    if (c0 + y < C && r0 + tx < R) d[static_cast<int64_t>(c0 + y) * ld + col_off + r0 + tx] = tile[tx][y];
+}
+
+enum TMode { kCopy = 0, kSwiGLUAct = 1, kGELUAct = 2 };
+
+// Expert-padded transpose of row-major [M, C] activations into [C, ld]: expert
+// e's rows off[e] .. off[e+1] become columns seg[e] .. (zero to seg[e+1]).
+// kSwiGLUAct / kGELUAct read the fp32 pre-activations ([M, 2C] g | u, or
+// [M, C] z) and write h rounded to the dtype exactly as the forward epilogue
+// does.  Column blocks of 64 never straddle experts (segments are multiples of 64).
+template <bool kBf16, int MODE>
+__global__ __launch_bounds__(256) void transpose_padded_kernel(const void* __restrict__ src, int C,
+                                                               const int32_t* __restrict__ off,
+                                                               const int32_t* __restrict__ seg, int E,
+                                                               void* __restrict__ dst, int ld) {
+  using T = typename Tr<kBf16>::T;
+  __shared__ T tile[64][65];
+  const int j0 = blockIdx.y * 64;  // destination column block (padded row index)
+  const int c0 = blockIdx.x * 64;  // source column block
+  if (j0 >= seg[E]) return;
+  int e = 0;
+  while (e + 1 < E && seg[e + 1] <= j0) ++e;
+  const int64_t n_e = off[e + 1] - off[e];
+  const int64_t base = off[e] + (j0 - seg[e]);
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int y = ty; y < 64; y += 4) {
+    const int64_t row = base + y;
+    const bool ok = (j0 - seg[e]) + y < n_e && c0 + tx < C;
+    T v = T(0);
+    if (ok) {
+      if constexpr (MODE == kCopy) {
+        v = static_cast<const T*>(src)[row * C + c0 + tx];
+      } else {
+        float h;
+        if constexpr (MODE == kSwiGLUAct) {
+          const float* gu = static_cast<const float*>(src) + row * 2 * C;
+          const float gt = gu[c0 + tx], up = gu[C + c0 + tx];
+          h = gt / (1.f + expf(-gt)) * up;
+        } else {
+          const float z = static_cast<const float*>(src)[row * C + c0 + tx];
+          h = 0.5f * z * (1.f + erff(z * 0.70710678118654752f));
+        }
+        if constexpr (kBf16) v = static_cast<uint16_t>(f32_to_bf16_bits(h));
+        else v = h;
+      }
+    }
+    tile[y][tx] = v;
+  }
+  __syncthreads();
+  T* d = static_cast<T*>(dst);
+  for (int y = ty; y < 64; y += 4)
+    if (c0 + y < C) d[static_cast<int64_t>(c0 + y) * ld + j0 + tx] = tile[tx][y];
+}
+
+// seg[e] = sum over e' < e of n_e' rounded up to 64; slot table = experts; ones.
+__global__ void bwd_setup_kernel(const int32_t* __restrict__ off, int E, int32_t* __restrict__ seg,
+                                 int32_t* __restrict__ slot_expert, int32_t* __restrict__ n_slots,
+                                 float* __restrict__ ones, int64_t n_ones) {
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    int32_t s = 0;
+    for (int e = 0; e < E; ++e) {
+      seg[e] = s;
+      s += (off[e + 1] - off[e] + 63) / 64 * 64;
+    }
+    seg[E] = s;
+    *n_slots = E;
+  }
+  for (int e = tid; e < E; e += blockDim.x) slot_expert[e] = e;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + tid; i < n_ones;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+    ones[i] = 1.f;
+}
+
+struct BwdLayout {
+  size_t gu, dgu, dy, wdT, wguT, ta, tb, ones, seg, slot_expert, n_slots, tab_slot, tab_row0, n_tiles, bytes;
+  int64_t ld;  // padded row length of the transposed activations
+  int tiles_cap;
+};
+
+BwdLayout bwd_layout(moe_dtype dt, int64_t T, int k, int H, int I, int E, moe_act act) {
+  BwdLayout w{};
+  const size_t s = moe::elem_bytes(dt);
+  const int64_t M = T * k;
+  const int64_t nI = act == MOE_SWIGLU ? 2 * static_cast<int64_t>(I) : I;  // gate|up columns
+  w.ld = moe::ceil_div(M, 64) * 64 + 64 * static_cast<int64_t>(E);
+  w.tiles_cap = static_cast<int>(moe::ceil_div(M, 256) + E);
+  size_t at = 0;
+  auto take = [&](size_t n) { size_t p = at; at = moe::align_up(at + n, 256); return p; };
+  w.gu = take(static_cast<size_t>(M) * nI * 4);
+  w.dgu = take(static_cast<size_t>(M) * nI * s);
+  w.dy = take(static_cast<size_t>(M) * H * s);
+  w.wdT = take(static_cast<size_t>(E) * I * H * s);
+  w.wguT = take(static_cast<size_t>(E) * H * nI * s);
+  w.ta = take(static_cast<size_t>(std::max<int64_t>(H, nI)) * w.ld * s);
+  w.tb = take(static_cast<size_t>(std::max<int64_t>(I, H)) * w.ld * s);
+  w.ones = take(static_cast<size_t>(M) * 4);
+  w.seg = take(sizeof(int32_t) * (E + 1));
+  w.slot_expert = take(sizeof(int32_t) * E);
+  w.n_slots = take(sizeof(int32_t));
+  w.tab_slot = take(sizeof(int32_t) * w.tiles_cap);
+  w.tab_row0 = take(sizeof(int32_t) * w.tiles_cap);
+  w.n_tiles = take(sizeof(int32_t));
+  w.bytes = at;
+  return w;
+}
+
+template <bool kBf16>
+int run_backward(const void* x_perm, const void* y_perm, int64_t n_tok, int k, int H, int I, int E,
+                 const int32_t* topk_idx, const float* topk_w, const int32_t* inv_pos, const int32_t* expert_off,
+                 const void* w_gate, const void* w_up, const void* w_down, bool swiglu, const void* d_out,
+                 void* d_x, float* d_logits, void* d_w_gate, void* d_w_up, void* d_w_down, char* ws,
+                 const BwdLayout& L, hipStream_t s) {
+  using namespace moe;
+  using T = typename Tr<kBf16>::T;
+  const int64_t M = n_tok * k;
+  const int S = sizeof(T);
+  const int nI = swiglu ? 2 * I : I;
+  auto at = [&](size_t o) { return ws + o; };
+  float* gu = reinterpret_cast<float*>(at(L.gu));
+  T* dgu = reinterpret_cast<T*>(at(L.dgu));
+  T* dy = reinterpret_cast<T*>(at(L.dy));
+  T* wdT = reinterpret_cast<T*>(at(L.wdT));
+  T* wguT = reinterpret_cast<T*>(at(L.wguT));
+  T* ta = reinterpret_cast<T*>(at(L.ta));
+  T* tb = reinterpret_cast<T*>(at(L.tb));
+  float* ones = reinterpret_cast<float*>(at(L.ones));
+  int32_t* seg = reinterpret_cast<int32_t*>(at(L.seg));
+  int32_t* slot_expert = reinterpret_cast<int32_t*>(at(L.slot_expert));
+  int32_t* n_slots = reinterpret_cast<int32_t*>(at(L.n_slots));
+  int32_t* tab_slot = reinterpret_cast<int32_t*>(at(L.tab_slot));
+  int32_t* tab_row0 = reinterpret_cast<int32_t*>(at(L.tab_row0));
+  int32_t* n_tiles = reinterpret_cast<int32_t*>(at(L.n_tiles));
+  auto check = [&](const char* what) { return hip_status(hipGetLastError(), what); };
+
+  bwd_setup_kernel<<<static_cast<unsigned>(std::min<int64_t>(1024, ceil_div(M, 256)) + 1), 256, 0, s>>>(
+      expert_off, E, seg, slot_expert, n_slots, ones, M);
+  tiles_kernel<<<1, 256, 0, s>>>(expert_off, n_slots, E, M, kCover, 256, 0, L.tiles_cap, tab_slot, tab_row0,
+                                 n_tiles);
+  if (int rc = check("moe_backward setup")) return rc;
+
+  // 1. gate + combine transpose
+  const int chunks = static_cast<int>(static_cast<int64_t>(H) * S / 16);
+  if (n_tok > 0)
+    gate_backward_kernel<kBf16><<<static_cast<unsigned>(n_tok), kTok, 0, s>>>(
+        static_cast<const uint4*>(d_out), static_cast<const uint4*>(y_perm), M, topk_idx, topk_w, inv_pos, k, E,
+        chunks, reinterpret_cast<uint4*>(dy), d_logits);
+  if (int rc = check("moe_backward gate")) return rc;
+
+  // transposed weights: WdT [E, I, H]; WguT [E, H, 2I] = [Wg^T | Wu^T] (or W1^T [E, H, I])
+  const dim3 tb_d(ceil_div(I, 64), ceil_div(H, 64), E), tb_g(ceil_div(H, 64), ceil_div(I, 64), E);
+  transpose_kernel<T><<<tb_d, 256, 0, s>>>(static_cast<const T*>(w_down), H, I, wdT, H, 0);
+  transpose_kernel<T><<<tb_g, 256, 0, s>>>(static_cast<const T*>(w_gate), I, H, wguT, nI, 0);
+  if (swiglu) transpose_kernel<T><<<tb_g, 256, 0, s>>>(static_cast<const T*>(w_up), I, H, wguT, nI, I);
+  if (int rc = check("moe_backward weight transposes")) return rc;
+
+  GemmArgs base{};
+  base.M = M;
+  base.E = E;
+  base.slot_off = expert_off;
+  base.slot_expert = slot_expert;
+  base.tile_slot = tab_slot;
+  base.tile_row0 = tab_row0;
+  base.n_tiles = n_tiles;
+  const unsigned grid_rows = static_cast<unsigned>(L.tiles_cap);
+
+  // 2. recompute the pre-activations in fp32
+  GemmArgs p = base;
+  p.A = x_perm;
+  p.B0 = w_gate;
+  p.B1 = w_up;
+  p.C = gu;
+  p.K = H;
+  p.N = I;
+  if (swiglu) {
+    p.n_col_tiles = static_cast<int>(ceil_div(I, kTileN / 2));
+    gemm_kernel<kBf16, 2, kEpiStoreGU, 256, 2><<<grid_rows * p.n_col_tiles, 256, 0, s>>>(p);
+  } else {
+    p.n_col_tiles = static_cast<int>(ceil_div(I, kTileN));
+    gemm_kernel<kBf16, 1, kEpiStoreF32, 256, 2><<<grid_rows * p.n_col_tiles, 256, 0, s>>>(p);
+  }
+  if (int rc = check("moe_backward recompute")) return rc;
+
+  // 3. d_h = d_y Wd, activation gradient in the epilogue
+  p = base;
+  p.A = dy;
+  p.B0 = wdT;
+  p.C = dgu;
+  p.aux = gu;
+  p.K = H;
+  p.N = I;
+  p.n_col_tiles = static_cast<int>(ceil_div(I, kTileN));
+  if (swiglu) gemm_kernel<kBf16, 1, kEpiSwiGLUBwd, 256, 2><<<grid_rows * p.n_col_tiles, 256, 0, s>>>(p);
+  else gemm_kernel<kBf16, 1, kEpiGELUBwd, 256, 2><<<grid_rows * p.n_col_tiles, 256, 0, s>>>(p);
+  if (int rc = check("moe_backward d_h")) return rc;
+
+  // 4. d_Wd = sum over each expert's rows of d_y^T h
+  const int ld = static_cast<int>(L.ld);
+  const unsigned ldb = static_cast<unsigned>(ceil_div(L.ld, 64));
+  transpose_padded_kernel<kBf16, kCopy><<<dim3(ceil_div(H, 64), ldb), 256, 0, s>>>(dy, H, expert_off, seg, E, ta,
+                                                                                  ld);
+  if (swiglu)
+    transpose_padded_kernel<kBf16, kSwiGLUAct><<<dim3(ceil_div(I, 64), ldb), 256, 0, s>>>(gu, I, expert_off, seg,
+                                                                                          E, tb, ld);
+  else
+    transpose_padded_kernel<kBf16, kGELUAct><<<dim3(ceil_div(I, 64), ldb), 256, 0, s>>>(gu, I, expert_off, seg, E,
+                                                                                        tb, ld);
+  GemmArgs q{};
+  q.A = ta;
+  q.B0 = tb;
+  q.C = d_w_down;
+  q.C2 = d_w_down;
+  q.E = E;
+  q.N = I;
+  q.Mw = H;
+  q.c_split = H;
+  q.ld = ld;
+  q.seg = seg;
+  q.n_col_tiles = static_cast<int>(ceil_div(I, kTileN));
+  gemm_kernel<kBf16, 1, kEpiStore, 256, 2, true>
+      <<<static_cast<unsigned>(E * ceil_div(H, 256) * q.n_col_tiles), 256, 0, s>>>(q);
+  if (int rc = check("moe_backward d_Wd")) return rc;
+
+  // 5. d_x_perm = [d_g | d_u] [Wg ; Wu] (into the d_y buffer, no longer needed)
+  p = base;
+  p.A = dgu;
+  p.B0 = wguT;
+  p.C = dy;
+  p.K = nI;
+  p.N = H;
+  p.n_col_tiles = static_cast<int>(ceil_div(H, kTileN));
+  gemm_kernel<kBf16, 1, kEpiStore, 256, 2><<<grid_rows * p.n_col_tiles, 256, 0, s>>>(p);
+  if (int rc = check("moe_backward d_x_perm")) return rc;
+
+  // 6. d_x[t] = sum of the token's k rows
+  if (int rc = moe_combine(dy, kBf16 ? MOE_BF16 : MOE_F32, M, inv_pos, ones, n_tok, k, H, d_x, s)) return rc;
+
+  // 7. d_Wg | d_Wu (or d_W1) = sum over each expert's rows of [d_g | d_u]^T x_perm
+  transpose_padded_kernel<kBf16, kCopy><<<dim3(ceil_div(nI, 64), ldb), 256, 0, s>>>(dgu, nI, expert_off, seg, E,
+                                                                                   ta, ld);
+  transpose_padded_kernel<kBf16, kCopy><<<dim3(ceil_div(H, 64), ldb), 256, 0, s>>>(x_perm, H, expert_off, seg, E,
+                                                                                  tb, ld);
+  q.A = ta;
+  q.B0 = tb;
+  q.C = d_w_gate;
+  q.C2 = swiglu ? d_w_up : d_w_gate;
+  q.N = H;
+  q.Mw = nI;
+  q.c_split = I;
+  q.n_col_tiles = static_cast<int>(ceil_div(H, kTileN));
+  gemm_kernel<kBf16, 1, kEpiStore, 256, 2, true>
+      <<<static_cast<unsigned>(E * ceil_div(nI, 256) * q.n_col_tiles), 256, 0, s>>>(q);
+  return check("moe_backward d_Wg/d_Wu");
+}
+
+}  // namespace
+
+extern "C" size_t moe_backward_workspace_bytes(moe_dtype dt, int64_t T, int k, int H, int I, int E, moe_act act) {
+  if (T < 0 || k < 1 || H < 1 || I < 1 || E < 1 || (dt != MOE_F32 && dt != MOE_BF16)) return 0;
+  return bwd_layout(dt, T, k, H, I, E, act).bytes;
+}
+
+extern "C" int moe_backward(const void* x_perm, const void* y_perm, moe_dtype dt, int64_t T, int k, int H, int I,
+                            int E, const int32_t* topk_idx, const float* topk_w, const int32_t* inv_pos,
+                            const int32_t* expert_off, const void* w_gate, const void* w_up, const void* w_down,
+                            moe_act act, const void* d_out, void* d_x, float* d_logits, void* d_w_gate,
+                            void* d_w_up, void* d_w_down, void* workspace, size_t workspace_bytes, void* stream) {
+  using namespace moe;
+  if (dt != MOE_F32 && dt != MOE_BF16) return fail(MOE_ERR_INVALID_ARG, "moe_backward: unknown dtype %d", (int)dt);
+  if (act != MOE_SWIGLU && act != MOE_GELU) return fail(MOE_ERR_INVALID_ARG, "moe_backward: unknown activation");
+  if (E < 1 || E > kMaxExperts)
+    return fail(E < 1 ? MOE_ERR_INVALID_ARG : MOE_ERR_UNSUPPORTED, "moe_backward: E=%d outside [1, %d]", E,
+                kMaxExperts);
+  if (k < 1 || k > E || k > kMaxTopK) return fail(MOE_ERR_INVALID_ARG, "moe_backward: k=%d outside [1, min(E, 8)]", k);
+  if (T < 0 || T * k >= (int64_t(1) << 30)) return fail(MOE_ERR_INVALID_ARG, "moe_backward: T*k must stay below 2^30");
+  if (H < 64 || I < 64 || H % 64 || I % 64)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_backward: H and I must be positive multiples of 64 (H=%d I=%d)", H, I);
+  const int nI = act == MOE_SWIGLU ? 2 * I : I;
+  const BwdLayout L = bwd_layout(dt, T, k, H, I, E, act);
+  if (static_cast<int64_t>(std::max(H, nI)) * elem_bytes(dt) * 256 >= (int64_t(1) << 31) ||
+      L.ld * elem_bytes(dt) * 256 >= (int64_t(1) << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "moe_backward: sizes too large for 32-bit tile offsets");
+  if (act == MOE_SWIGLU && !w_up) return fail(MOE_ERR_INVALID_ARG, "moe_backward: SwiGLU needs w_up");
+  if (act == MOE_GELU && (w_up || d_w_up)) return fail(MOE_ERR_INVALID_ARG, "moe_backward: GELU takes no w_up/d_w_up");
+  if (!expert_off || !w_gate || !w_down || !d_w_gate || !d_w_down || !workspace || (act == MOE_SWIGLU && !d_w_up))
+    return fail(MOE_ERR_INVALID_ARG, "moe_backward: null pointer");
+  if (T > 0 && (!x_perm || !y_perm || !topk_idx || !topk_w || !inv_pos || !d_out || !d_x || !d_logits))
+    return fail(MOE_ERR_INVALID_ARG, "moe_backward: null pointer");
+  const void* ptrs[] = {x_perm, y_perm, w_gate, w_up, w_down, d_out, d_x, d_w_gate, d_w_up, d_w_down, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(MOE_ERR_INVALID_ARG, "moe_backward: operands must be 16-byte aligned");
+  if (workspace_bytes < L.bytes)
+    return fail(MOE_ERR_WORKSPACE, "moe_backward: workspace has %zu bytes, needs %zu", workspace_bytes, L.bytes);
+  const hipStream_t s = as_stream(stream);
+  char* ws = static_cast<char*>(workspace);
+  return dt == MOE_BF16
+             ? run_backward<true>(x_perm, y_perm, T, k, H, I, E, topk_idx, topk_w, inv_pos, expert_off, w_gate, w_up,
+                                  w_down, act == MOE_SWIGLU, d_out, d_x, d_logits, d_w_gate, d_w_up, d_w_down, ws, L, s)
+             : run_backward<false>(x_perm, y_perm, T, k, H, I, E, topk_idx, topk_w, inv_pos, expert_off, w_gate,
+                                   w_up, w_down, act == MOE_SWIGLU, d_out, d_x, d_logits, d_w_gate, d_w_up, d_w_down,
+                                   ws, L, s);
+}

@@ -84,6 +84,14 @@ N = None
     ("moe_prediction_quality", (16, 16, 8, N, 0, 16, N), -1, "top_n"),
     ("moe_prediction_quality", (16, N, 8, N, 5, 16, N), -1, "null"),
     ("moe_prediction_quality", (16, 16, 257, N, 5, 16, N), -2, "E=257"),
+    ("moe_backward", (16, 16, 1, 10, 2, 96, 128, 8, 16, 16, 16, 16, 16, 16, 16, 0, 16, 16, 16, 16, 16, 16, 16,
+                      1 << 40, N), -2, "multiples of 64"),
+    ("moe_backward", (16, 16, 1, 10, 2, 128, 128, 8, 16, 16, 16, 16, 16, N, 16, 0, 16, 16, 16, 16, 16, 16, 16,
+                      1 << 40, N), -1, "w_up"),
+    ("moe_backward", (16, 16, 1, 10, 2, 128, 128, 8, 16, 16, 16, 16, 16, 16, 16, 0, 16, 16, 16, 16, 16, 16, 16,
+                      10, N), -3, "workspace"),
+    ("moe_backward", (16, 16, 1, 10, 9, 128, 128, 8, 16, 16, 16, 16, 16, 16, 16, 0, 16, 16, 16, 16, 16, 16, 16,
+                      1 << 40, N), -1, "k=9"),
     ("moe_combine", (16, 1, 10, 16, 16, 10, 9, 64, 16, N), -1, "k=9"),
     ("moe_combine", (16, 1, 10, 16, 16, 10, 2, 12, 16, N), -1, "multiple of 16"),
 ])
