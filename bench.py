@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--crossover", action="store_true",
                     help="time the grouped and the dense expert-FFN paths on the DeepSeek-V2 T sweep and on the "
                          "GEMM shapes profiled by EPS-MoE, print one JSON line per case, and exit")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the layer's backward pass (moe_backward) on the Mixtral layer")
     ap.add_argument("--pipeline", action="store_true",
                     help="horizontal-split pipeline and memory kernels on CU-masked streams (Mixtral layer)")
     ap.add_argument("--predict", action="store_true",
@@ -347,6 +349,48 @@ def pipeline_bench(moe, synth, torch, np, steps=10, warmup=3):
     return {"pipeline": res}
 
 
+def backward_bench(moe, synth, torch, np, steps=5, warmup=2):
+    """The layer's backward pass on the Mixtral-shaped layer (no replication):
+    gradients w.r.t. x, the router logits and all expert weights."""
+    cfg = synth.CONFIGS["mixtral"]
+    T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
+    dev = torch.device("cuda:0")
+
+    def dev_bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    wg, wu, wd = (dev_bf16(w) for w in synth.expert_weights(cfg, threads=16))
+    x = dev_bf16(synth.hidden0(cfg, 0))
+    logits = torch.from_numpy(synth.logits(cfg, 0, 0)).to(dev)
+    d_out = torch.randn(T, H, device=dev).to(torch.bfloat16)
+    fw = moe.moe_layer_forward(x, logits, k, wg, wu, wd, "swiglu", 0)
+    ws = torch.empty(moe.moe_backward_workspace_bytes(torch.bfloat16, T, k, H, I, E), dtype=torch.uint8, device=dev)
+    out = {}
+    stream = torch.cuda.current_stream()
+
+    def run():
+        return moe.moe_backward(fw["x_perm"], fw["y_perm"], fw["idx"], fw["w"], fw["inv_pos"], fw["expert_off"],
+                                wg, wu, wd, d_out, "swiglu", out, ws, stream)
+
+    for _ in range(warmup):
+        out.update(run())
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        run()
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    M = T * k
+    gemm_flop = 16.0 * M * H * I   # recompute g|u, d_h, d_x_perm, d_Wd, d_Wg|d_Wu
+    return {"backward": {"workload": f"Mixtral-shaped layer T={T} H={H} I={I} E={E} k={k} bf16, no replication",
+                         "ms": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1),
+                         "gemm_tflop": round(gemm_flop / 1e12, 3),
+                         "gemm_tflops_over_whole_backward": round(gemm_flop / (ms * 1e-3) / 1e12, 1),
+                         "workspace_gb": round(ws.numel() / 1e9, 2)}}
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -372,6 +416,9 @@ def main():
 
     if a.crossover:
         crossover(moe, synth, torch, np)
+        return
+    if a.backward:
+        print(json.dumps(backward_bench(moe, synth, torch, np)), flush=True)
         return
     if a.pipeline:
         print(json.dumps(pipeline_bench(moe, synth, torch, np)), flush=True)

@@ -121,21 +121,34 @@ __global__ __launch_bounds__(kTok) void gate_backward_kernel(const uint4* __rest
 }
 
 // dst[b][c][col_off + r] = src[b][r][c] for a batch of R x C matrices; dst rows
-// are ld elements long.  64 x 64 tiles through LDS.
+// are ld elements long.  64 x 64 tiles through LDS, 16-byte global accesses
+// (R, C, ld and col_off are multiples of 64).
 template <typename T>
 __global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ src, int R, int C, T* __restrict__ dst,
                                                         int ld, int col_off) {
-  __shared__ T tile[64][65];
+  constexpr int V = 16 / sizeof(T);   // elements per 16-byte chunk
+  constexpr int CH = 64 / V;          // chunks per 64-element row
+  __shared__ T tile[64][64 + 2];
   const int b = blockIdx.z;
   const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
   const T* s = src + static_cast<int64_t>(b) * R * C;
   T* d = dst + static_cast<int64_t>(b) * C * ld;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int y = ty; y < 64; y += 4)
-    if (r0 + y < R && c0 + tx < C) tile[y][tx] = s[static_cast<int64_t>(r0 + y) * C + c0 + tx];
+  for (int q = threadIdx.x; q < 64 * CH; q += 256) {
+    const int y = q / CH, x = (q % CH) * V;
+    const uint4 v = *reinterpret_cast<const uint4*>(s + static_cast<int64_t>(r0 + y) * C + c0 + x);
+    const T* e = reinterpret_cast<const T*>(&v);
+#pragma unroll
+    for (int u = 0; u < V; ++u) tile[y][x + u] = e[u];
+  }
   __syncthreads();
-  for (int y = ty; y < 64; y += 4)
-    if (c0 + y < C && r0 + tx < R) d[static_cast<int64_t>(c0 + y) * ld + col_off + r0 + tx] = tile[tx][y];
+  for (int q = threadIdx.x; q < 64 * CH; q += 256) {
+    const int y = q / CH, x = (q % CH) * V;   // destination row c0 + y, columns r0 + x ..
+    uint4 v;
+    T* e = reinterpret_cast<T*>(&v);
+#pragma unroll
+    for (int u = 0; u < V; ++u) e[u] = tile[x + u][y];
+    *reinterpret_cast<uint4*>(d + static_cast<int64_t>(c0 + y) * ld + col_off + r0 + x) = v;
+  }
 }
 
 enum TMode { kCopy = 0, kSwiGLUAct = 1, kGELUAct = 2 };
@@ -207,6 +220,13 @@ __global__ void bwd_setup_kernel(const int32_t* __restrict__ off, int E, int32_t
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + tid; i < n_ones;
        i += static_cast<int64_t>(gridDim.x) * blockDim.x)
     ones[i] = 1.f;
+}
+
+// blocks of a weight-gradient launch: 8 equal shares of each expert's
+// (256-row x 256-column) tiles
+unsigned wgrad_grid(int E, int64_t rows, int col_tiles) {
+  const int64_t per_e = moe::ceil_div(rows, 256) * col_tiles;
+  return static_cast<unsigned>(8 * E * moe::ceil_div(per_e, 8));
 }
 
 struct BwdLayout {
@@ -354,8 +374,7 @@ int run_backward(const void* x_perm, const void* y_perm, int64_t n_tok, int k, i
   q.ld = ld;
   q.seg = seg;
   q.n_col_tiles = static_cast<int>(ceil_div(I, kTileN));
-  gemm_kernel<kBf16, 1, kEpiStore, 256, 2, true>
-      <<<static_cast<unsigned>(E * ceil_div(H, 256) * q.n_col_tiles), 256, 0, s>>>(q);
+  gemm_kernel<kBf16, 1, kEpiStore, 256, 2, true><<<wgrad_grid(E, H, q.n_col_tiles), 256, 0, s>>>(q);
   if (int rc = check("moe_backward d_Wd")) return rc;
 
   // 5. d_x_perm = [d_g | d_u] [Wg ; Wu] (into the d_y buffer, no longer needed)
@@ -385,8 +404,7 @@ int run_backward(const void* x_perm, const void* y_perm, int64_t n_tok, int k, i
   q.Mw = nI;
   q.c_split = I;
   q.n_col_tiles = static_cast<int>(ceil_div(H, kTileN));
-  gemm_kernel<kBf16, 1, kEpiStore, 256, 2, true>
-      <<<static_cast<unsigned>(E * ceil_div(nI, 256) * q.n_col_tiles), 256, 0, s>>>(q);
+  gemm_kernel<kBf16, 1, kEpiStore, 256, 2, true><<<wgrad_grid(E, nI, q.n_col_tiles), 256, 0, s>>>(q);
   return check("moe_backward d_Wg/d_Wu");
 }
 

@@ -135,16 +135,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int NT = g.n_col_tiles;
   const int MTw = kWgrad ? (g.Mw + BM - 1) / BM : 0;       // row tiles per expert (weight gradients)
   const int total_m = kWgrad ? g.E * MTw : *g.n_tiles;
-  const int total = total_m * NT;
+  // weight gradients: 8 equal shares of each expert's tiles (grid rounded up to them)
+  const int total = kWgrad ? 8 * g.E * ((MTw * NT + 7) >> 3) : total_m * NT;
   const int b = blockIdx.x;
   if (b >= total) return;
-  const int xcd = b & 7, q = total >> 3, rem = total & 7;
-  const int l = xcd * q + min(xcd, rem) + (b >> 3);
-  const int grp = l / (kGroupM * NT);
-  const int gsz = min(kGroupM, total_m - grp * kGroupM);
-  const int li = l - grp * kGroupM * NT;
-  const int mt = grp * kGroupM + li % gsz;
-  const int nt = li / gsz;
+  int mt, nt;
+  if constexpr (kWgrad) {
+    // experts differ in K (their row counts): give each XCD an equal, contiguous
+    // share of every expert's tiles, so no XCD holds all of a hot expert
+    const int per_e = MTw * NT;
+    const int xcd = b & 7, pos = b >> 3;
+    const int e_ = pos / ((per_e + 7) >> 3);
+    const int in_e = pos - e_ * ((per_e + 7) >> 3);
+    const int t_ = xcd * ((per_e + 7) >> 3) + in_e;     // tile index inside the expert
+    if (e_ >= g.E || t_ >= per_e) return;
+    const int gm = t_ / (kGroupM * NT);
+    const int gs = min(kGroupM, MTw - gm * kGroupM);
+    const int li_ = t_ - gm * kGroupM * NT;
+    mt = e_ * MTw + gm * kGroupM + li_ % gs;
+    nt = li_ / gs;
+  } else {
+    const int xcd = b & 7, q = total >> 3, rem = total & 7;
+    const int l = xcd * q + min(xcd, rem) + (b >> 3);
+    const int grp = l / (kGroupM * NT);
+    const int gsz = min(kGroupM, total_m - grp * kGroupM);
+    const int li = l - grp * kGroupM * NT;
+    mt = grp * kGroupM + li % gsz;
+    nt = li / gsz;
+  }
 
   int K, e, m_valid;
   int64_t r0;
@@ -154,11 +172,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const T* A;
   int64_t wofs, row_b;
   if constexpr (kWgrad) {
-    e = mt / MTw;
-    r0 = static_cast<int64_t>(mt - e * MTw) * BM;
-    const int k0 = g.seg[e];
-    K = g.seg[e + 1] - k0;
-    m_valid = static_cast<int>(min<int64_t>(BM, g.Mw - r0));
+    e = __builtin_amdgcn_readfirstlane(mt / MTw);
+    r0 = __builtin_amdgcn_readfirstlane((mt - e * MTw) * BM);
+    // uniform across the block: keep the buffer descriptors in scalar registers
+    const int k0 = __builtin_amdgcn_readfirstlane(g.seg[e]);
+    K = __builtin_amdgcn_readfirstlane(g.seg[e + 1]) - k0;
+    m_valid = __builtin_amdgcn_readfirstlane(static_cast<int>(min<int64_t>(BM, g.Mw - r0)));
     row_b = static_cast<int64_t>(g.ld) * S;
     A = static_cast<const T*>(g.A) + r0 * g.ld + k0;
     wofs = static_cast<int64_t>(n0) * g.ld + k0;
@@ -295,6 +314,96 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     __builtin_amdgcn_sched_barrier(0);
   }
 
+  // ---- epilogues with heavy per-element math: stage the fp32 accumulators
+  // through LDS, BM/WM rows at a time, then let every thread walk one column
+  // of the 256-column tile (row-contiguous, coalesced reads of the
+  // pre-activations and stores of the result).  Keeps the register epilogue
+  // small enough to stay unrolled.
+  if constexpr (!kWgrad && (EPI == kEpiGELU || EPI == kEpiSwiGLUBwd || EPI == kEpiGELUBwd)) {
+    static_assert(NMAT == 1, "staged epilogues take one weight matrix");
+    constexpr int RH = BM / WM;  // rows staged per round
+    static_assert(RH * kTileN * 4 <= 2 * kStageBytes, "staging tile must fit in LDS");
+    float* stage = reinterpret_cast<float*>(lds);
+    __syncthreads();  // every wave is done with the operand stages
+#pragma unroll
+    for (int h = 0; h < WM; ++h) {
+      if (wm == h) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              stage[(i * 32 + 8 * (r >> 2) + 4 * lg + (r & 3)) * kTileN + wn * CW + j * 32 + lr] = acc[i][j][r];
+      }
+      __syncthreads();
+      // thread (ty, tx): columns 4 tx .. 4 tx + 3 of rows ty, ty + 4, ... (N is a
+      // multiple of 64, so a group of four is wholly inside or outside)
+      const int tx = tid & 63, ty = tid >> 6;
+      const int col = n0 + 4 * tx;
+      T* __restrict__ C = static_cast<T*>(g.C);
+      const float* __restrict__ aux = g.aux;
+      const int rows = min(RH, m_valid - h * RH);
+      if (col < N) {
+        for (int nb = ty; nb < rows; nb += 16) {
+          float4 a[4], p0[4], p1[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {   // rows nb, nb + 4, nb + 8, nb + 12: loads first
+            const int n = min(nb + 4 * u, rows - 1);
+            const int64_t row = r0 + h * RH + n;
+            a[u] = *reinterpret_cast<const float4*>(stage + n * kTileN + 4 * tx);
+            if constexpr (EPI == kEpiSwiGLUBwd) {
+              p0[u] = *reinterpret_cast<const float4*>(aux + row * 2 * N + col);
+              p1[u] = *reinterpret_cast<const float4*>(aux + row * 2 * N + N + col);
+            } else if constexpr (EPI == kEpiGELUBwd) {
+              p0[u] = *reinterpret_cast<const float4*>(aux + row * N + col);
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            if (nb + 4 * u >= rows) break;
+            const int64_t row = r0 + h * RH + nb + 4 * u;
+            const float av[4] = {a[u].x, a[u].y, a[u].z, a[u].w};
+            float o0[4], o1[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              if constexpr (EPI == kEpiGELU) {
+                o0[c] = 0.5f * av[c] * (1.f + erff(av[c] * 0.70710678118654752f));
+              } else if constexpr (EPI == kEpiSwiGLUBwd) {
+                // d_g = d_h * u * silu'(g), d_u = d_h * silu(g); silu'(g) = s (1 + g (1 - s))
+                const float gt = (&p0[u].x)[c], up = (&p1[u].x)[c];
+                const float sg = 1.f / (1.f + expf(-gt));
+                o0[c] = av[c] * up * (sg * (1.f + gt * (1.f - sg)));
+                o1[c] = av[c] * (gt / (1.f + expf(-gt)));
+              } else {
+                // d_z = d_h * (Phi(z) + z phi(z))
+                const float z = (&p0[u].x)[c];
+                o0[c] = av[c] * (0.5f * (1.f + erff(z * 0.70710678118654752f)) +
+                                 z * expf(-0.5f * z * z) * 0.39894228040143268f);
+              }
+            }
+            const int64_t o = EPI == kEpiSwiGLUBwd ? row * 2 * N + col : row * N + col;
+            if constexpr (kBf16) {
+              *reinterpret_cast<uint2*>(C + o) =
+                  make_uint2(f32_to_bf16_bits(o0[0]) | (f32_to_bf16_bits(o0[1]) << 16),
+                             f32_to_bf16_bits(o0[2]) | (f32_to_bf16_bits(o0[3]) << 16));
+              if constexpr (EPI == kEpiSwiGLUBwd)
+                *reinterpret_cast<uint2*>(C + o + N) =
+                    make_uint2(f32_to_bf16_bits(o1[0]) | (f32_to_bf16_bits(o1[1]) << 16),
+                               f32_to_bf16_bits(o1[2]) | (f32_to_bf16_bits(o1[3]) << 16));
+            } else {
+              *reinterpret_cast<float4*>(C + o) = make_float4(o0[0], o0[1], o0[2], o0[3]);
+              if constexpr (EPI == kEpiSwiGLUBwd)
+                *reinterpret_cast<float4*>(C + o + N) = make_float4(o1[0], o1[1], o1[2], o1[3]);
+            }
+          }
+        }
+      }
+      __syncthreads();
+    }
+    return;
+  }
+
   // ---- epilogue: lane holds column lr of each 32 x 32 tile, rows
   // 8*(r/4) + 4*lg + r%4 --------------------------------------------------
   constexpr int JO = NMAT == 2 ? TN / 2 : TN;  // output column subtiles per wave
@@ -321,37 +430,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
           C[N + col] = acc[i][j + TN / 2][r];
         } else if constexpr (EPI == kEpiStoreF32) {
           static_cast<float*>(g.C)[row * N + col] = acc[i][j][r];
-        } else if constexpr (EPI == kEpiSwiGLUBwd) {
-          // d_g = d_h * u * silu'(g), d_u = d_h * silu(g); silu'(g) = s (1 + g (1 - s))
-          const float dh = acc[i][j][r];
-          const float gt = g.aux[row * 2 * N + col], up = g.aux[row * 2 * N + N + col];
-          const float sg = 1.f / (1.f + expf(-gt));
-          const float dg = dh * up * (sg * (1.f + gt * (1.f - sg)));
-          const float du = dh * (gt / (1.f + expf(-gt)));
-          T* C = static_cast<T*>(g.C) + row * 2 * N;
-          if constexpr (kBf16) {
-            C[col] = static_cast<uint16_t>(f32_to_bf16_bits(dg));
-            C[N + col] = static_cast<uint16_t>(f32_to_bf16_bits(du));
-          } else {
-            C[col] = dg;
-            C[N + col] = du;
-          }
-        } else if constexpr (EPI == kEpiGELUBwd) {
-          // d_z = d_h * (Phi(z) + z phi(z))
-          const float z = g.aux[row * N + col];
-          const float dz = acc[i][j][r] * (0.5f * (1.f + erff(z * 0.70710678118654752f)) +
-                                           z * expf(-0.5f * z * z) * 0.39894228040143268f);
-          T* C = static_cast<T*>(g.C) + row * N;
-          if constexpr (kBf16) C[col] = static_cast<uint16_t>(f32_to_bf16_bits(dz));
-          else C[col] = dz;
         } else {
           float v;
           if constexpr (EPI == kEpiSwiGLU) {
             const float gt = acc[i][j][r], up = acc[i][j + TN / 2][r];
             v = gt / (1.f + expf(-gt)) * up;
-          } else if constexpr (EPI == kEpiGELU) {
-            const float z = acc[i][j][r];
-            v = 0.5f * z * (1.f + erff(z * 0.70710678118654752f));
           } else {
             v = acc[i][j][r];
           }
