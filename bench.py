@@ -35,7 +35,7 @@ METRIC = "routed tokens/s per MoE layer (Mixtral shape, T=8192) + % of roofline"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_gateup_mixtral_traffic.json")
-FFN_SOURCE = os.path.join(ROOT, "mixture_experts_routing_top_amd", "csrc", "ffn.hip")
+GEMM_SOURCES = [os.path.join(ROOT, "mixture_experts_routing_top_amd", "csrc", f) for f in ("gemm.h", "ffn.hip")]
 
 
 def parse():
@@ -62,7 +62,11 @@ def parse():
 
 
 def kernel_source_hash() -> str:
-    return hashlib.sha256(open(FFN_SOURCE, "rb").read()).hexdigest()[:16]
+    """Hash of the sources the gate/up GEMM is built from (the kernel template and its launcher)."""
+    h = hashlib.sha256()
+    for path in GEMM_SOURCES:
+        h.update(open(path, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(flop_unit_rows: int):
@@ -71,7 +75,7 @@ def measured_traffic(flop_unit_rows: int):
     if not os.path.exists(TRAFFIC_FILE):
         return None
     rec = json.load(open(TRAFFIC_FILE))
-    if rec.get("ffn_source_sha256_16") != kernel_source_hash():
+    if rec.get("gemm_source_sha256_16") != kernel_source_hash():
         return None
     return rec.get("bytes_per_launch")
 
