@@ -127,3 +127,74 @@ def layer_backward(x, idx, w, weights, act, d_out):
     return dict(d_x=_round(dX, bf16), d_w_gate=_round(dWg, bf16),
                 d_w_up=None if dWu is None else _round(dWu, bf16), d_w_down=_round(dWd, bf16),
                 d_logits=d_logits.astype(np.float32), dw=dw, y_perm=Yp, d_y=dY, d_x_perm=dXp)
+
+
+def sampled_backward(x, idx, w, weights, act, d_out, tokens, entries):
+    """The same gradients as layer_backward, computed only where asked, for
+    shapes too large to run whole: rows of d_x and d_logits for `tokens`, and
+    weight-gradient entries `entries` = [(name, e, a, b)] with name in
+    'd_w_gate', 'd_w_up', 'd_w_down' ([e][a, b] of that gradient).  Each value
+    is formed by the definitions above from the rows that reach it (a token's
+    own slots; all rows of expert e for a weight-gradient entry), in float64,
+    with the same rounding points.  Returns (d_x [n, H], d_logits [n, E],
+    {entry: value})."""
+    bf16 = np.asarray(x).dtype == np.uint16
+    wg_, wu_, wd_ = weights
+    E, I, H = wg_.shape
+    T, k = idx.shape
+    dO = _f64(d_out)
+    wt = np.asarray(w, dtype=np.float64)
+    swiglu = wu_ is not None
+    rd = lambda v: _f64(_round(v, bf16))
+    tokens = np.asarray(tokens)
+    dX = np.zeros((len(tokens), H))
+    dL = np.zeros((len(tokens), E))
+    dw = np.zeros((len(tokens), k))
+    vals = {}
+    for e in range(E):
+        sel = [(n, i) for n, t in enumerate(tokens) for i in range(k) if idx[t, i] == e]
+        want = [en for en in entries if en[1] == e]
+        if not sel and not want:
+            continue
+        Wg, Wd = _f64(wg_[e]), _f64(wd_[e])
+        Wu = _f64(wu_[e]) if swiglu else None
+        for n, i in sel:
+            t = tokens[n]
+            xr = _f64(x[t])
+            g = Wg @ xr
+            if swiglu:
+                u = Wu @ xr
+                h = rd(silu(g) * u)
+            else:
+                h = rd(gelu(g))
+            dw[n, i] = rd(Wd @ h) @ dO[t]
+            dy = rd(wt[t, i] * dO[t])
+            dh = dy @ Wd
+            if swiglu:
+                dXp = rd(rd(dh * u * silu_grad(g)) @ Wg + rd(dh * silu(g)) @ Wu)
+            else:
+                dXp = rd(rd(dh * gelu_grad(g)) @ Wg)
+            dX[n] += dXp
+        if want:
+            rows = np.argwhere(idx == e)                       # (t, i) of expert e's rows
+            Xe = _f64(x[rows[:, 0]])
+            dYe = rd(wt[rows[:, 0], rows[:, 1]][:, None] * dO[rows[:, 0]])
+            for name, _, a, b in want:
+                if name == "d_w_down":
+                    gb = Xe @ Wg[b]
+                    hb = rd(silu(gb) * (Xe @ Wu[b])) if swiglu else rd(gelu(gb))
+                    v = dYe[:, a] @ hb
+                else:
+                    ga = Xe @ Wg[a]
+                    dha = dYe @ Wd[:, a]
+                    if name == "d_w_gate" and swiglu:
+                        d = rd(dha * (Xe @ Wu[a]) * silu_grad(ga))
+                    elif name == "d_w_gate":
+                        d = rd(dha * gelu_grad(ga))
+                    else:
+                        d = rd(dha * silu(ga))
+                    v = d @ Xe[:, b]
+                vals[(name, e, a, b)] = float(_f64(_round(np.array([v]), bf16))[0])
+    s = (wt[tokens] * dw).sum(axis=1, keepdims=True)
+    np.put_along_axis(dL, idx[tokens].astype(np.int64), wt[tokens] * (dw - s), axis=1)
+    return _f64(_round(dX, bf16)), dL.astype(np.float32), vals

@@ -87,3 +87,43 @@ def test_backward_twice_reuses_workspace():
         outs.append({kk: from_dev(v).copy() for kk, v in g.items()})
     for key in outs[0]:
         assert np.array_equal(outs[0][key], outs[2][key]), key
+
+
+def test_backward_full_size_mixtral_sampled():
+    """The full Mixtral-shaped layer (T=8192, H=4096, I=14336, E=8, top-2, bf16) in the
+    configuration bench.py --backward times: d_x and d_logits on sampled tokens and
+    sampled entries of every weight gradient, each computed by the oracle from the
+    rows that reach it; whole-tensor structure checked exactly."""
+    cfg = synth.CONFIGS["mixtral"]
+    x = synth.hidden0(cfg, 0)
+    lg = synth.logits(cfg, 0, 0)
+    wts = synth.expert_weights(cfg, 0, threads=16)
+    wg, wu, wd = (to_dev(w) for w in wts)
+    d_out = synth.f32_to_bf16_bits(np.random.default_rng(42).standard_normal((cfg.T, cfg.H)).astype(np.float32))
+    fw = moe.moe_layer_forward(to_dev(x), to_dev(lg), cfg.k, wg, wu, wd, cfg.act, 0)
+    g = moe.moe_backward(fw["x_perm"], fw["y_perm"], fw["idx"], fw["w"], fw["inv_pos"], fw["expert_off"], wg, wu, wd,
+                         to_dev(d_out), cfg.act)
+    torch.cuda.synchronize()
+    idx_o, w_o = oracle.route(lg, cfg.k)
+    assert np.array_equal(from_dev(fw["idx"]), idx_o)
+    rng = np.random.default_rng(7)
+    toks = np.sort(rng.choice(cfg.T, size=6, replace=False))
+    E, I, H = cfg.E, cfg.I, cfg.H
+    entries = []
+    for e in range(E):
+        entries.append(("d_w_down", e, int(rng.integers(H)), int(rng.integers(I))))
+        entries.append(("d_w_gate", e, int(rng.integers(I)), int(rng.integers(H))))
+        entries.append(("d_w_up", e, int(rng.integers(I)), int(rng.integers(H))))
+    dX, dL, vals = ob.sampled_backward(x, idx_o, w_o, wts, cfg.act, d_out, toks, entries)
+    assert_close(from_dev(g["d_x"])[toks], synth.f32_to_bf16_bits(dX.astype(np.float32)), "bf16", "d_x rows")
+    assert_close(from_dev(g["d_logits"])[toks], dL, "bf16", "d_logits rows")
+    got = np.array([float(synth.bf16_bits_to_f32(from_dev(g[nm][e, a:a + 1, b:b + 1]).reshape(1))[0])
+                    for (nm, e, a, b) in vals])
+    ref = np.array(list(vals.values()))
+    rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    assert rel <= 1e-2, f"sampled weight-gradient entries rel-L2 {rel:.3e}"
+    dl = from_dev(g["d_logits"])
+    kept = np.zeros_like(dl, dtype=bool)
+    np.put_along_axis(kept, idx_o.astype(np.int64), True, axis=1)
+    assert np.all(dl[~kept] == 0)
+    assert np.all(np.abs(dl.astype(np.float64).sum(axis=1)) <= 1e-3 * (1 + np.abs(dl).sum(axis=1)))

@@ -660,3 +660,25 @@ def test_backward_is_linear_in_d_out():
     twice = ob.layer_backward(x, idx, w, wts, cfg.act, (2 * d_out).astype(np.float32))
     for key in ("d_x", "d_w_gate", "d_w_down"):
         assert np.array_equal(twice[key], 2 * got[key])   # power-of-two scaling is exact
+
+
+@pytest.mark.parametrize("name", ["swiglu-f32", "gelu-f32", "swiglu-bf16"])
+def test_sampled_backward_equals_full_backward(name):
+    """The sampled form (for full-size checks) reproduces the whole-layer oracle."""
+    from oracle import backward as ob
+    cfg, x, lg, idx, w, wts, d_out, full = _bw_case(name, 48, 8)
+    rng = np.random.default_rng(9)
+    toks = rng.choice(cfg.T, size=7, replace=False)
+    E, I, H = wts[0].shape
+    entries = [("d_w_down", int(rng.integers(E)), int(rng.integers(H)), int(rng.integers(I))) for _ in range(6)]
+    entries += [("d_w_gate", int(rng.integers(E)), int(rng.integers(I)), int(rng.integers(H))) for _ in range(6)]
+    if wts[1] is not None:
+        entries += [("d_w_up", int(rng.integers(E)), int(rng.integers(I)), int(rng.integers(H))) for _ in range(6)]
+    dX, dL, vals = ob.sampled_backward(x, idx, w, wts, cfg.act, d_out, toks, entries)
+    f64 = lambda a: synth.bf16_bits_to_f32(a).astype(np.float64) if a.dtype == np.uint16 else a.astype(np.float64)
+    tol = 1e-12 if cfg.dtype == "f32" else 0.0
+    assert np.max(np.abs(dX - f64(full["d_x"])[toks])) <= tol + 1e-6 * np.max(np.abs(dX))
+    assert np.max(np.abs(dL - full["d_logits"][toks])) <= 1e-6 * (1 + np.max(np.abs(dL)))
+    for (nm, e, a, b), v in vals.items():
+        ref = f64(full[nm])[e, a, b]
+        assert abs(v - ref) <= 1e-6 * max(1.0, abs(ref)) + (4e-3 * abs(ref) if cfg.dtype == "bf16" else 0), (nm, e, a, b, v, ref)
