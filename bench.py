@@ -92,6 +92,19 @@ def algorithmic_layer_work(T, H, I, E, k, n_mat):
     return flops, w_bytes, mem
 
 
+def memory_phase_summary(T, H, E, k, warm, cold):
+    """Routing, dispatch and combine against HBM: their algorithmic bytes (route 4E in
+    + 8k out per token; dispatch and combine (k+1)*H*2 each) over their event-timed
+    phase times (which also hold dispatch's index kernels and launch gaps)."""
+    b = T * (4 * E + 8 * k) + 2 * T * (k + 1) * H * 2
+    out = {"bytes": b}
+    for label, ph in (("warm", warm), ("cold", cold)):
+        us = ph["route"] + ph["dispatch"] + ph["combine"]
+        out[label] = {"us": round(us, 2), "GBps": round(b / (us * 1e-6) / 1e9, 1),
+                      "frac_of_hbm": round(b / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 3)}
+    return out
+
+
 def cpu_baseline(cfg, x, logits, wts, prev_idx_np, rows):
     """The oracle (single-threaded C) on a bounded sample of the same workload:
     routing, statistics, replicas, dispatch/permute and combine at full size, and
@@ -486,11 +499,18 @@ def main():
     gateup_ms = float(np.mean([ev[i][0].elapsed_time(ev[i][1]) for i in range(a.steps)]))
     down_ms = float(np.mean([ev[i][1].elapsed_time(ev[i][2]) for i in range(a.steps)]))
 
-    # Per-phase split (diagnostic, outside the timed region): median of 5 passes.
+    # Per-phase split (diagnostic, outside the timed region): median of 5 passes
+    # warm, then 5 cold passes, each after streaming a 512 MiB buffer through the
+    # memory system (more than the 256 MB Infinity Cache plus the L2s) so every
+    # phase starts with its inputs in HBM only.
     names = ["route", "stats", "dispatch", "expert_ffn", "combine"]
     samples = {n: [] for n in names}
-    for rep in range(5):
+    cold = {n: [] for n in names}
+    flush = torch.empty(128 << 20, dtype=torch.float32, device=dev)
+    for rep in range(10):
         phase_ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        if rep >= 5:
+            flush.fill_(float(rep))
         torch.cuda.synchronize()
         phase_ev[0].record(stream)
         idx, w = moe.moe_route(logits, k, bufs["idx"], bufs["w"], stream)
@@ -507,8 +527,10 @@ def main():
         phase_ev[5].record(stream)
         torch.cuda.synchronize()
         for j, n in enumerate(names):
-            samples[n].append(phase_ev[j].elapsed_time(phase_ev[j + 1]) * 1e3)
+            (samples if rep < 5 else cold)[n].append(phase_ev[j].elapsed_time(phase_ev[j + 1]) * 1e3)
     phase_us = {n: round(float(np.median(v)), 2) for n, v in samples.items()}
+    phase_us_cold = {n: round(float(np.median(v)), 2) for n, v in cold.items()}
+    del flush
     n_slots = int(d["n_slots"].item())
 
     flops, w_bytes, mem = algorithmic_layer_work(T, H, I, E, k, 3)
@@ -542,6 +564,11 @@ def main():
         "down_gemm": {"ms": round(down_ms, 4),
                       "tflops": round(2.0 * M * I * H / (down_ms * 1e-3) / 1e12, 1)},
         "phase_us": phase_us,
+        "phase_us_cold": phase_us_cold,
+        "cold_layer": {"ms": round(sum(phase_us_cold.values()) / 1e3, 4),
+                       "tokens_per_s": round(T / (sum(phase_us_cold.values()) * 1e-6), 1),
+                       "note": "sum of the per-phase medians, each phase starting with caches flushed"},
+        "memory_phases": memory_phase_summary(T, H, E, k, phase_us, phase_us_cold),
         "wall_s_timed": round(wall, 3),
     }
     if not a.no_cpu_baseline:
