@@ -127,3 +127,22 @@ def test_backward_full_size_mixtral_sampled():
     np.put_along_axis(kept, idx_o.astype(np.int64), True, axis=1)
     assert np.all(dl[~kept] == 0)
     assert np.all(np.abs(dl.astype(np.float64).sum(axis=1)) <= 1e-3 * (1 + np.abs(dl).sum(axis=1)))
+
+
+def test_empty_batch_forward_and_backward():
+    """T = 0: the layer returns an empty output and the backward writes all-zero
+    weight gradients (every expert has no rows) without launching empty grids."""
+    cfg = CASES["mixtral-mini"]
+    wts = synth.expert_weights(cfg, 0)
+    wg, wu, wd = (to_dev(w) for w in wts)
+    x = torch.empty((0, cfg.H), dtype=torch.bfloat16, device="cuda")
+    lg = torch.empty((0, cfg.E), dtype=torch.float32, device="cuda")
+    fw = moe.moe_layer_forward(x, lg, cfg.k, wg, wu, wd, cfg.act, 0)
+    g = moe.moe_backward(fw["x_perm"], fw["y_perm"], fw["idx"], fw["w"], fw["inv_pos"], fw["expert_off"], wg, wu, wd,
+                         torch.empty((0, cfg.H), dtype=torch.bfloat16, device="cuda"), cfg.act,
+                         out={"d_w_gate": torch.full_like(wg, 1.0), "d_w_up": torch.full_like(wu, 1.0),
+                              "d_w_down": torch.full_like(wd, 1.0)})
+    torch.cuda.synchronize()
+    assert fw["out"].shape == (0, cfg.H) and g["d_x"].shape == (0, cfg.H)
+    for key in ("d_w_gate", "d_w_up", "d_w_down"):
+        assert not torch.any(g[key].float() != 0), key
