@@ -159,7 +159,7 @@ enum TMode { kCopy = 0, kSwiGLUAct = 1, kGELUAct = 2 };
 // [M, C] z) and write h rounded to the dtype exactly as the forward epilogue
 // does.  Column blocks of 64 never straddle experts (segments are multiples of 64).
 template <bool kBf16, int MODE>
-__global__ __launch_bounds__(256) void transpose_padded_kernel(const void* __restrict__ src, int C,
+__global__ __launch_bounds__(256) void transpose_padded_kernel(const void* __restrict__ src, int64_t M, int C,
                                                                const int32_t* __restrict__ off,
                                                                const int32_t* __restrict__ seg, int E,
                                                                void* __restrict__ dst, int ld) {
@@ -170,12 +170,12 @@ __global__ __launch_bounds__(256) void transpose_padded_kernel(const void* __res
   if (j0 >= seg[E]) return;
   int e = 0;
   while (e + 1 < E && seg[e + 1] <= j0) ++e;
-  const int64_t n_e = off[e + 1] - off[e];
+  const int64_t n_e = min<int64_t>(static_cast<int64_t>(off[e + 1]) - off[e], seg[e + 1] - seg[e]);
   const int64_t base = off[e] + (j0 - seg[e]);
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
   for (int y = ty; y < 64; y += 4) {
     const int64_t row = base + y;
-    const bool ok = (j0 - seg[e]) + y < n_e && c0 + tx < C;
+    const bool ok = (j0 - seg[e]) + y < n_e && row >= 0 && row < M && c0 + tx < C;
     T v = T(0);
     if (ok) {
       if constexpr (MODE == kCopy) {
@@ -202,18 +202,21 @@ __global__ __launch_bounds__(256) void transpose_padded_kernel(const void* __res
     if (c0 + y < C) d[static_cast<int64_t>(c0 + y) * ld + j0 + tx] = tile[tx][y];
 }
 
-// seg[e] = sum over e' < e of n_e' rounded up to 64; slot table = experts; ones.
-__global__ void bwd_setup_kernel(const int32_t* __restrict__ off, int E, int32_t* __restrict__ seg,
-                                 int32_t* __restrict__ slot_expert, int32_t* __restrict__ n_slots,
-                                 float* __restrict__ ones, int64_t n_ones) {
+// seg[e] = sum over e' < e of n_e' rounded up to 64 (n_e clamped to [0, M], the
+// sum to the transposed row length ld, so malformed offsets cannot reach past
+// the buffers); slot table = experts; ones.
+__global__ void bwd_setup_kernel(const int32_t* __restrict__ off, int E, int64_t M, int64_t ld,
+                                 int32_t* __restrict__ seg, int32_t* __restrict__ slot_expert,
+                                 int32_t* __restrict__ n_slots, float* __restrict__ ones, int64_t n_ones) {
   const int tid = threadIdx.x;
   if (tid == 0) {
-    int32_t s = 0;
+    int64_t s = 0;
     for (int e = 0; e < E; ++e) {
-      seg[e] = s;
-      s += (off[e + 1] - off[e] + 63) / 64 * 64;
+      seg[e] = static_cast<int32_t>(s);
+      const int64_t n = min<int64_t>(max<int64_t>(static_cast<int64_t>(off[e + 1]) - off[e], 0), M);
+      s = min<int64_t>(s + (n + 63) / 64 * 64, ld / 64 * 64);
     }
-    seg[E] = s;
+    seg[E] = static_cast<int32_t>(s);
     *n_slots = E;
   }
   for (int e = tid; e < E; e += blockDim.x) slot_expert[e] = e;
@@ -291,7 +294,7 @@ int run_backward(const void* x_perm, const void* y_perm, int64_t n_tok, int k, i
   auto check = [&](const char* what) { return hip_status(hipGetLastError(), what); };
 
   bwd_setup_kernel<<<static_cast<unsigned>(std::min<int64_t>(1024, ceil_div(M, 256)) + 1), 256, 0, s>>>(
-      expert_off, E, seg, slot_expert, n_slots, ones, M);
+      expert_off, E, M, L.ld, seg, slot_expert, n_slots, ones, M);
   tiles_kernel<<<1, 256, 0, s>>>(expert_off, n_slots, E, M, kCover, 256, 0, L.tiles_cap, tab_slot, tab_row0,
                                  n_tiles);
   if (int rc = check("moe_backward setup")) return rc;
@@ -354,13 +357,13 @@ int run_backward(const void* x_perm, const void* y_perm, int64_t n_tok, int k, i
   // 4. d_Wd = sum over each expert's rows of d_y^T h
   const int ld = static_cast<int>(L.ld);
   const unsigned ldb = static_cast<unsigned>(ceil_div(L.ld, 64));
-  transpose_padded_kernel<kBf16, kCopy><<<dim3(ceil_div(H, 64), ldb), 256, 0, s>>>(dy, H, expert_off, seg, E, ta,
+  transpose_padded_kernel<kBf16, kCopy><<<dim3(ceil_div(H, 64), ldb), 256, 0, s>>>(dy, M, H, expert_off, seg, E, ta,
                                                                                   ld);
   if (swiglu)
-    transpose_padded_kernel<kBf16, kSwiGLUAct><<<dim3(ceil_div(I, 64), ldb), 256, 0, s>>>(gu, I, expert_off, seg,
+    transpose_padded_kernel<kBf16, kSwiGLUAct><<<dim3(ceil_div(I, 64), ldb), 256, 0, s>>>(gu, M, I, expert_off, seg,
                                                                                           E, tb, ld);
   else
-    transpose_padded_kernel<kBf16, kGELUAct><<<dim3(ceil_div(I, 64), ldb), 256, 0, s>>>(gu, I, expert_off, seg, E,
+    transpose_padded_kernel<kBf16, kGELUAct><<<dim3(ceil_div(I, 64), ldb), 256, 0, s>>>(gu, M, I, expert_off, seg, E,
                                                                                         tb, ld);
   GemmArgs q{};
   q.A = ta;
@@ -392,9 +395,9 @@ int run_backward(const void* x_perm, const void* y_perm, int64_t n_tok, int k, i
   if (int rc = moe_combine(dy, kBf16 ? MOE_BF16 : MOE_F32, M, inv_pos, ones, n_tok, k, H, d_x, s)) return rc;
 
   // 7. d_Wg | d_Wu (or d_W1) = sum over each expert's rows of [d_g | d_u]^T x_perm
-  transpose_padded_kernel<kBf16, kCopy><<<dim3(ceil_div(nI, 64), ldb), 256, 0, s>>>(dgu, nI, expert_off, seg, E,
+  transpose_padded_kernel<kBf16, kCopy><<<dim3(ceil_div(nI, 64), ldb), 256, 0, s>>>(dgu, M, nI, expert_off, seg, E,
                                                                                    ta, ld);
-  transpose_padded_kernel<kBf16, kCopy><<<dim3(ceil_div(H, 64), ldb), 256, 0, s>>>(x_perm, H, expert_off, seg, E,
+  transpose_padded_kernel<kBf16, kCopy><<<dim3(ceil_div(H, 64), ldb), 256, 0, s>>>(x_perm, M, H, expert_off, seg, E,
                                                                                   tb, ld);
   q.A = ta;
   q.B0 = tb;
