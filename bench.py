@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--crossover", action="store_true",
                     help="time the grouped and the dense expert-FFN paths on the DeepSeek-V2 T sweep and on the "
                          "GEMM shapes profiled by EPS-MoE, print one JSON line per case, and exit")
+    ap.add_argument("--configs", action="store_true",
+                    help="routed tokens/s and roofline fraction of every workload (one line each)")
     ap.add_argument("--backward", action="store_true",
                     help="time the layer's backward pass (moe_backward) on the Mixtral layer")
     ap.add_argument("--pipeline", action="store_true",
@@ -158,7 +160,11 @@ def crossover(moe, synth, torch, np):
                          dtype=torch.uint8, device=dev)
         y = torch.empty_like(x_perm)
         res = dict(case=label, **extra)
-        for path in ("grouped", "dense", "auto"):
+        offs = slot_off.cpu().numpy()[: int(n_slots.item()) + 1].astype(np.int64)
+        rows = np.diff(offs)
+        res["tiles"] = {"g256": int(np.sum((rows + 255) // 256)), "g64": int(np.sum((rows + 63) // 64)),
+                        "d64": int(np.count_nonzero(rows) * ((rows.max() + 63) // 64))}
+        for path in ("grouped", "grouped_small", "dense", "auto"):
             for _ in range(2):
                 moe.moe_expert_ffn(x_perm, slot_off, slot_expert, n_slots, wg, wu, wd, "swiglu", path, y, ws)
             torch.cuda.synchronize()
@@ -176,7 +182,7 @@ def crossover(moe, synth, torch, np):
             d = float(np.median([ev[i][1].elapsed_time(ev[i][2]) for i in range(5)]))
             res[path] = {"gateup_ms": round(g, 4), "down_ms": round(d, 4), "ffn_ms": round(g + d, 4)}
         # which path AUTO takes (it reads the slot sizes back): compare its output timing-free
-        res["faster"] = min(("grouped", "dense"), key=lambda p: res[p]["ffn_ms"])
+        res["fastest"] = min(("grouped", "grouped_small", "dense"), key=lambda p: res[p]["ffn_ms"])
         print(json.dumps(res), flush=True)
 
     cfg0 = synth.CONFIGS["dsv2"]
@@ -194,6 +200,23 @@ def crossover(moe, synth, torch, np):
                    {"E": E, "k": k, "H": H, "I": I, "rows": int(T * k), "max_rows": int(counts.max()),
                     "mean_rows": round(float(counts.mean()), 1), "empty_experts": int((counts == 0).sum())})
     del wg, wu, wd
+    # coarse-grained layers: Mixtral- and DBRX-shaped routing (large per-expert counts)
+    for name in ("mixtral", "dbrx"):
+        cfg = synth.CONFIGS[name]
+        E, H, I, k = cfg.E, cfg.H, cfg.I, cfg.k
+        wg = (torch.randn(E, I, H, device=dev) * H ** -0.5).to(torch.bfloat16)
+        wu = (torch.randn(E, I, H, device=dev) * H ** -0.5).to(torch.bfloat16)
+        wd = (torch.randn(E, H, I, device=dev) * I ** -0.5).to(torch.bfloat16)
+        for T in (cfg.T // 8, cfg.T):
+            c = cfg.with_T(T)
+            idx, _ = moe.moe_route(torch.from_numpy(synth.logits(c, 0, 0)).to(dev), k)
+            x = torch.randn(T, H, device=dev).to(torch.bfloat16)
+            d = moe.moe_dispatch(x, idx, E, None, E)
+            counts = np.diff(d["expert_off"].cpu().numpy())
+            time_paths(d["x_perm"], d["slot_off"], d["slot_expert"], d["n_slots"], wg, wu, wd, f"{name}_T{T}",
+                       {"E": E, "k": k, "H": H, "I": I, "rows": int(T * k), "max_rows": int(counts.max()),
+                        "mean_rows": round(float(counts.mean()), 1)})
+        del wg, wu, wd
     # single-expert GEMM shapes M x K x N printed by EPS-MoE (K = H; N = I of one projection)
     for M, K_, N_ in ((512, 5120, 1536), (2048, 5120, 1536), (512, 5120, 14336)):
         x = torch.randn(M, K_, device=dev).to(torch.bfloat16)
@@ -366,6 +389,136 @@ def pipeline_bench(moe, synth, torch, np, steps=10, warmup=3):
     return {"pipeline": res}
 
 
+PEAK_FP32_TFLOPS = 157.3         # MI355X dense fp32 MFMA
+
+
+def configs_bench(moe, synth, torch, np, steps=10, warmup=3):
+    """Every workload's layer forward on the GPU: routed tokens/s per layer and the
+    fraction of its roofline, t_roof = max(flop / MFMA peak, active expert weights /
+    HBM) + memory-phase bytes / HBM (routing, dispatch, combine; algorithmic)."""
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+
+    def to_dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(steps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    def roofline(cfg, counts):
+        s = cfg.elem_bytes
+        flop = 2.0 * cfg.T * cfg.k * cfg.H * cfg.I * cfg.n_mat
+        active = int(np.count_nonzero(counts))
+        w_bytes = active * cfg.n_mat * cfg.I * cfg.H * s
+        mem = cfg.T * (4 * cfg.E + 8 * cfg.k) + 2 * cfg.T * (cfg.k + 1) * cfg.H * s
+        peak = (PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_FP32_TFLOPS) * 1e12
+        t = max(flop / peak, w_bytes / (PEAK_HBM_GBS * 1e9)) + mem / (PEAK_HBM_GBS * 1e9)
+        bound = "mfma" if flop / peak >= w_bytes / (PEAK_HBM_GBS * 1e9) else "hbm (weight streaming)"
+        return t, bound
+
+    def report(name, cfg, ms, counts, extra):
+        t_roof, bound = roofline(cfg, counts)
+        rec = {"workload": name, "T": cfg.T, "H": cfg.H, "I": cfg.I, "E": cfg.E, "k": cfg.k, "act": cfg.act,
+               "dtype": cfg.dtype, "ms_per_layer": round(ms, 4),
+               "routed_tokens_per_s_per_layer": round(cfg.T / (ms * 1e-3), 1),
+               "roofline_ms": round(t_roof * 1e3, 4), "roofline_frac": round(t_roof / (ms * 1e-3), 4),
+               "roofline_bound": bound}
+        rec.update(extra)
+        print(json.dumps({"config": rec}), flush=True)
+
+    cache = {}
+
+    def weights_of(cfg):
+        # weights do not depend on T: one upload per workload
+        if cache.get("name") != cfg.name:
+            cache.clear()
+            torch.cuda.empty_cache()
+            cache["name"] = cfg.name
+            cache["w"] = tuple(None if w is None else to_dev(w) for w in synth.expert_weights(cfg, threads=16))
+        return cache["w"]
+
+    def single_layer(name, cfg, R, path="grouped"):
+        wg, wu, wd = weights_of(cfg)
+        x = to_dev(synth.hidden0(cfg, 0))
+        lg = to_dev(synth.logits(cfg, 0, 0))
+        win = 10
+        state = torch.empty(moe.moe_stats_state_bytes(1, cfg.E, win), dtype=torch.uint8, device=dev)
+        moe.moe_stats_init(state, 1, cfg.E, win)
+        bufs = {}
+        it = [0]
+
+        def step():
+            it[0] += 1
+            return moe.moe_layer_forward(x, lg, cfg.k, wg, wu, wd, cfg.act, R, stats_state=state,
+                                         stats_dims=(1, cfg.E, win), layer=0, it=it[0], path=path, bufs=bufs,
+                                         stream=stream)
+        ms = timed(step)
+        counts = bufs["counts"].cpu().numpy()
+        report(name, cfg, ms, counts, {"replica_budget": R, "gemm_path": path,
+                                       "slots_used": int(bufs["disp"]["n_slots"].item())})
+        del x, bufs
+
+    def chain(name, cfg, R):
+        """All L layers of one iteration, statistics and prediction included; the
+        time per layer is the chain time over L."""
+        cache.clear()
+        torch.cuda.empty_cache()
+        L, E, k, win = cfg.L, cfg.E, cfg.k, cfg.window
+        weights = [tuple(None if w is None else to_dev(w) for w in synth.expert_weights(cfg, l, threads=16))
+                   for l in range(L)]
+        state = torch.empty(moe.moe_stats_state_bytes(L, E, win), dtype=torch.uint8, device=dev)
+        moe.moe_stats_init(state, L, E, win)
+        x0 = to_dev(synth.hidden0(cfg, 0))
+        # the logits of a chained layer depend on the previous layer's routing: take the
+        # routing of an oracle-free first pass on the GPU and keep the logits fixed
+        lgs, prev = [], None
+        for l in range(L):
+            lg = synth.logits(cfg, l, 0, None if prev is None else prev)
+            lgs.append(to_dev(lg))
+            idx, _ = moe.moe_route(lgs[-1], k)
+            prev = idx[:, 0].cpu().numpy()
+        bufs = [dict() for _ in range(L)]
+        it = [0]
+
+        def step():
+            it[0] += 1
+            xx, prev_idx = x0, None
+            for l in range(L):
+                r = moe.moe_layer_forward(xx, lgs[l], k, *weights[l], cfg.act, R, stats_state=state,
+                                          stats_dims=(L, E, win), layer=l, it=it[0], prev_topk_idx=prev_idx,
+                                          bufs=bufs[l], stream=stream)
+                xx, prev_idx = r["out"], r["idx"]
+        ms = timed(step) / L
+        counts = np.mean([b["counts"].cpu().numpy() for b in bufs], axis=0)
+        report(name, cfg, ms, counts, {"layers": L, "replica_budget": R, "window": win,
+                                       "note": "time per layer of the full chain, statistics and prediction included"})
+        del weights, bufs
+        torch.cuda.empty_cache()
+
+    C = synth.CONFIGS
+    chain("tiny (2-layer chain)", C["tiny"], C["tiny"].R)
+    single_layer("Mixtral-shaped, R=0", C["mixtral"], 0)
+    single_layer("Mixtral-shaped, R=8", C["mixtral"], 8)
+    for T in synth.DSV2_T_SWEEP:
+        for path in ("grouped", "auto"):
+            single_layer(f"DeepSeek-V2-shaped, T={T}", C["dsv2"].with_T(T), 0, path)
+    single_layer("DBRX-shaped, R=0", C["dbrx"], 0)
+    single_layer("DBRX-shaped, R=16", C["dbrx"], 16)
+    chain("PopFetcher-shaped (12-layer chain)", C["popfetcher"], 0)
+
+
 def backward_bench(moe, synth, torch, np, steps=5, warmup=2):
     """The layer's backward pass on the Mixtral-shaped layer (no replication):
     gradients w.r.t. x, the router logits and all expert weights."""
@@ -433,6 +586,9 @@ def main():
 
     if a.crossover:
         crossover(moe, synth, torch, np)
+        return
+    if a.configs:
+        configs_bench(moe, synth, torch, np)
         return
     if a.backward:
         print(json.dumps(backward_bench(moe, synth, torch, np)), flush=True)

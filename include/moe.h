@@ -58,7 +58,7 @@ typedef enum {
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;       /* activations and weights */
 typedef enum { MOE_SWIGLU = 0, MOE_GELU = 1 } moe_act;
-typedef enum { MOE_GEMM_AUTO = 0, MOE_GEMM_GROUPED = 1, MOE_GEMM_DENSE = 2 } moe_gemm_path;
+typedef enum { MOE_GEMM_AUTO = 0, MOE_GEMM_GROUPED = 1, MOE_GEMM_DENSE = 2, MOE_GEMM_GROUPED_SMALL = 3 } moe_gemm_path;
 
 /* ---------------------------------------------------------------- routing
  * moe_route -- top-k softmax gate ([PF] observations and trade-offs: the naive
@@ -234,14 +234,16 @@ int moe_dispatch(const void* x, moe_dtype dt, int64_t T, int H, const int32_t* t
  * non-replicated dispatches give bit-identical y_perm.
  *   path  GROUPED: 256-row tiles cover each slot's rows exactly (no host
  *                  sync): the large-batch form.
+ *         GROUPED_SMALL: 64-row tiles cover each slot's rows exactly (no
+ *                  host sync): less padding when slots hold few rows.
  *         DENSE:   every slot with rows is padded to the largest slot's row
  *                  count (rounded up to 64) and the uniform batch runs in
  *                  64-row tiles; tiles wholly in the padding exit at once.
  *                  Reads the slot table back (synchronises `stream`).
- *         AUTO:    reads the slot table back and picks per GEMM: DENSE when
- *                  the grouped grid would leave over a quarter of the 256 CUs
- *                  idle and at most half of the padded batch is padding,
- *                  else GROUPED.
+ *         AUTO:    reads the slot table back and picks per GEMM the tiling
+ *                  with the lowest modelled cost (tile count x per-tile cost,
+ *                  a 64-row tile costing 0.55 of a 256-row one, at least one
+ *                  wave of 256 CUs per grid), fitted to measured crossovers.
  *         All paths give bit-identical y_perm.
  *   workspace  at least moe_expert_ffn_workspace_bytes(...) bytes.
  * Limits: dtype F32 or BF16; H and I multiples of 64; E <= max_slots;

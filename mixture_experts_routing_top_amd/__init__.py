@@ -28,14 +28,15 @@ __all__ = ["moe_route", "moe_stats_state_bytes", "moe_stats_init", "moe_stats", 
            "moe_dispatch", "moe_expert_ffn_workspace_bytes", "moe_expert_ffn", "moe_combine", "moe_layer_forward",
            "moe_layer_forward_pipelined", "moe_backward_workspace_bytes", "moe_backward",
            "MoEError", "LIB_PATH", "MOE_F32", "MOE_BF16", "SWIGLU", "GELU", "GEMM_AUTO", "GEMM_GROUPED",
-           "GEMM_DENSE"]
+           "GEMM_DENSE", "GEMM_GROUPED_SMALL"]
 
 MOE_F32, MOE_BF16 = 0, 1
 SWIGLU, GELU = 0, 1
-GEMM_AUTO, GEMM_GROUPED, GEMM_DENSE = 0, 1, 2
+GEMM_AUTO, GEMM_GROUPED, GEMM_DENSE, GEMM_GROUPED_SMALL = 0, 1, 2, 3
 _ACT = {"swiglu": SWIGLU, "gelu": GELU, SWIGLU: SWIGLU, GELU: GELU}
-_PATH = {"auto": GEMM_AUTO, "grouped": GEMM_GROUPED, "dense": GEMM_DENSE,
-         GEMM_AUTO: GEMM_AUTO, GEMM_GROUPED: GEMM_GROUPED, GEMM_DENSE: GEMM_DENSE}
+_PATH = {"auto": GEMM_AUTO, "grouped": GEMM_GROUPED, "dense": GEMM_DENSE, "grouped_small": GEMM_GROUPED_SMALL,
+         GEMM_AUTO: GEMM_AUTO, GEMM_GROUPED: GEMM_GROUPED, GEMM_DENSE: GEMM_DENSE,
+         GEMM_GROUPED_SMALL: GEMM_GROUPED_SMALL}
 
 
 def _ptr(t):

@@ -42,28 +42,30 @@ constexpr int kBigM = 256;    // grouped path: 256-row tiles
 constexpr int kSmallM = 64;   // dense path: 64-row tiles
 
 struct WsLayout {
-  size_t h, tab_slot[2], tab_row0[2], n_tiles, bytes;
-  int cap[2];  // tile capacity of each table
+  size_t h, tab_slot[3], tab_row0[3], n_tiles, bytes;
+  int cap[3];  // tile capacity of each table
 };
 
-enum Table { kTabGrouped = 0, kTabPadded = 1 };
+// The row tilings a GEMM can run on, each with its own tile table:
+//   kG256: 256-row tiles covering each slot (at most ceil(M/256) + slots);
+//   kD64:  the dense padded batch in 64-row tiles (at most slots x ceil(M/64));
+//   kG64:  64-row tiles covering each slot (at most ceil(M/64) + slots).
+enum Kind { kG256 = 0, kD64 = 1, kG64 = 2 };
 
-// Two tile tables: the grouped 256-row tiles (at most ceil(M/256) + slots) and
-// the dense padded batch in 64-row tiles (at most slots x ceil(largest slot /
-// 64), the largest slot having at most M rows).
 WsLayout ws_layout(moe_dtype dt, int64_t M, int I, int max_slots) {
   WsLayout w{};
-  const int64_t cap[2] = {moe::ceil_div(M, kBigM) + max_slots,
-                          static_cast<int64_t>(max_slots) * moe::ceil_div(std::max<int64_t>(M, 1), kSmallM)};
+  const int64_t cap[3] = {moe::ceil_div(M, kBigM) + max_slots,
+                          static_cast<int64_t>(max_slots) * moe::ceil_div(std::max<int64_t>(M, 1), kSmallM),
+                          moe::ceil_div(M, kSmallM) + max_slots};
   size_t at = 0;
   auto take = [&](size_t n) { size_t p = at; at = moe::align_up(at + n, 256); return p; };
   w.h = take(static_cast<size_t>(M) * I * moe::elem_bytes(dt));
-  for (int t = 0; t < 2; ++t) {
+  for (int t = 0; t < 3; ++t) {
     w.cap[t] = static_cast<int>(std::min<int64_t>(cap[t], 0x3fffffff));
     w.tab_slot[t] = take(sizeof(int32_t) * w.cap[t]);
     w.tab_row0[t] = take(sizeof(int32_t) * w.cap[t]);
   }
-  w.n_tiles = take(2 * sizeof(int32_t));
+  w.n_tiles = take(3 * sizeof(int32_t));
   w.bytes = at;
   return w;
 }
@@ -74,31 +76,43 @@ thread_local hipEvent_t g_timing[3] = {nullptr, nullptr, nullptr};
 hipError_t mark(int i, hipStream_t s) { return g_timing[i] ? hipEventRecord(g_timing[i], s) : hipSuccess; }
 
 template <bool kBf16, int EPI, int NMAT>
-void launch_gemm(bool dense, const GemmArgs& p, unsigned grid, hipStream_t s) {
-  if (dense) gemm_kernel<kBf16, NMAT, EPI, kSmallM, 1><<<grid, 256, 0, s>>>(p);
+void launch_gemm(bool small, const GemmArgs& p, unsigned grid, hipStream_t s) {
+  if (small) gemm_kernel<kBf16, NMAT, EPI, kSmallM, 1><<<grid, 256, 0, s>>>(p);
   else gemm_kernel<kBf16, NMAT, EPI, kBigM, 2><<<grid, 256, 0, s>>>(p);
 }
 
 // Phase 1 (gate/up or W1) and phase 2 (down or W2), each on its own tile table.
 template <bool kBf16>
-int launch_ffn(const GemmArgs& p1, bool dense1, unsigned grid1, const GemmArgs& p2, bool dense2, unsigned grid2,
+int launch_ffn(const GemmArgs& p1, bool small1, unsigned grid1, const GemmArgs& p2, bool small2, unsigned grid2,
                bool swiglu, hipStream_t s) {
   if (int rc = moe::hip_status(mark(0, s), "moe_expert_ffn timing event")) return rc;
-  if (swiglu) launch_gemm<kBf16, kEpiSwiGLU, 2>(dense1, p1, grid1, s);
-  else launch_gemm<kBf16, kEpiGELU, 1>(dense1, p1, grid1, s);
+  if (swiglu) launch_gemm<kBf16, kEpiSwiGLU, 2>(small1, p1, grid1, s);
+  else launch_gemm<kBf16, kEpiGELU, 1>(small1, p1, grid1, s);
   if (int rc = moe::hip_status(hipGetLastError(), "moe_expert_ffn gate/up launch")) return rc;
   if (int rc = moe::hip_status(mark(1, s), "moe_expert_ffn timing event")) return rc;
-  launch_gemm<kBf16, kEpiStore, 1>(dense2, p2, grid2, s);
+  launch_gemm<kBf16, kEpiStore, 1>(small2, p2, grid2, s);
   if (int rc = moe::hip_status(hipGetLastError(), "moe_expert_ffn down launch")) return rc;
   return moe::hip_status(mark(2, s), "moe_expert_ffn timing event");
 }
 
-// AUTO rule, per GEMM: take the dense padded batch when the grouped grid would
-// leave more than a quarter of the 256 CUs idle and at most half of the padded
-// batch's tiles are padding.
+// AUTO rule, per GEMM, from the slot sizes.  Cost model in "row-tile units":
+// a 256-row tile costs 1, a 64-row tile kSmallCost (a quarter of the work at a
+// lower MFMA efficiency); a grid is charged at least one full wave of the 256
+// CUs.  The cheapest tiling wins; ties keep the 256-row tiles.  kSmallCost is
+// fitted to the measured crossover table (DeepSeek-V2-, Mixtral- and
+// DBRX-shaped routing and EPS-MoE's single-expert shapes): every case's fastest
+// tiling is the model's pick for values in (0.475, 0.667).
 constexpr int kComputeUnits = 256;
-bool prefer_dense(int64_t grouped_tiles, int64_t dense_tiles, int64_t dense_real_tiles, int col_tiles) {
-  return grouped_tiles * col_tiles * 4 < 3 * kComputeUnits && 2 * dense_real_tiles >= dense_tiles;
+constexpr double kSmallCost = 0.55;
+Kind pick_kind(int64_t g256, int64_t d64, int64_t g64, int col_tiles) {
+  auto cost = [&](int64_t tiles, double unit) {
+    const double blocks = static_cast<double>(tiles) * col_tiles;
+    return unit * std::max(blocks, static_cast<double>(kComputeUnits));
+  };
+  const double c256 = cost(g256, 1.0), cd64 = cost(d64, kSmallCost), cg64 = cost(g64, kSmallCost);
+  if (cg64 < c256 && cg64 <= cd64) return kG64;
+  if (cd64 < c256) return kD64;
+  return kG256;
 }
 
 }  // namespace
@@ -117,7 +131,7 @@ extern "C" int moe_expert_ffn(const void* x_perm, moe_dtype dt, int64_t M, int H
   using namespace moe;
   if (dt != MOE_F32 && dt != MOE_BF16) return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn: unknown dtype %d", (int)dt);
   if (act != MOE_SWIGLU && act != MOE_GELU) return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn: unknown activation");
-  if (path != MOE_GEMM_AUTO && path != MOE_GEMM_GROUPED && path != MOE_GEMM_DENSE)
+  if (path != MOE_GEMM_AUTO && path != MOE_GEMM_GROUPED && path != MOE_GEMM_DENSE && path != MOE_GEMM_GROUPED_SMALL)
     return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn: unknown path");
   if (M < 0 || M >= (int64_t(1) << 31)) return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn: M out of range");
   if (H < 64 || I < 64 || H % 64 || I % 64)
@@ -140,12 +154,13 @@ extern "C" int moe_expert_ffn(const void* x_perm, moe_dtype dt, int64_t M, int H
   const hipStream_t s = as_stream(stream);
   const int nt1 = static_cast<int>(ceil_div(I, act == MOE_SWIGLU ? kTileN / 2 : kTileN));
   const int nt2 = static_cast<int>(ceil_div(H, kTileN));
-  // GROUPED: 256-row tiles covering each slot.  DENSE: the padded batch in
-  // 64-row tiles.  AUTO: per GEMM, from the slot sizes read back here.
-  bool dense1 = path == MOE_GEMM_DENSE, dense2 = dense1;
+  // GROUPED: 256-row tiles covering each slot.  GROUPED_SMALL: 64-row tiles
+  // covering each slot.  DENSE: the padded batch in 64-row tiles.  AUTO: per
+  // GEMM, from the slot sizes read back here.
+  Kind k1 = path == MOE_GEMM_DENSE ? kD64 : path == MOE_GEMM_GROUPED_SMALL ? kG64 : kG256, k2 = k1;
   int m_pad = 0;
-  int64_t dense_tiles = 0;
-  if (path != MOE_GEMM_GROUPED) {
+  int64_t exact[3] = {-1, -1, -1};  // tiles per kind, when known on the host
+  if (path == MOE_GEMM_DENSE || path == MOE_GEMM_AUTO) {
     std::vector<int32_t> off(static_cast<size_t>(max_slots) + 2);
     if (int rc = hip_status(hipMemcpyAsync(off.data(), slot_off, sizeof(int32_t) * (max_slots + 1),
                                            hipMemcpyDeviceToHost, s), "moe_expert_ffn slot readback")) return rc;
@@ -153,37 +168,40 @@ extern "C" int moe_expert_ffn(const void* x_perm, moe_dtype dt, int64_t M, int H
                             "moe_expert_ffn slot readback")) return rc;
     if (int rc = hip_status(hipStreamSynchronize(s), "moe_expert_ffn slot readback")) return rc;
     const int n = std::min(std::max(off[max_slots + 1], 0), max_slots);
-    int64_t largest = 0, active = 0, big_tiles = 0, small_real = 0;
+    int64_t largest = 0, active = 0, g256 = 0, g64 = 0;
     for (int i = 0; i < n; ++i) {
       const int64_t r = std::max<int64_t>(0, std::min<int64_t>(off[i + 1], M) - std::max<int64_t>(off[i], 0));
       largest = std::max(largest, r);
       if (r > 0) ++active;
-      big_tiles += ceil_div(r, kBigM);
-      small_real += ceil_div(r, kSmallM);
+      g256 += ceil_div(r, kBigM);
+      g64 += ceil_div(r, kSmallM);
     }
     m_pad = static_cast<int>(ceil_div(std::max<int64_t>(largest, 1), kSmallM) * kSmallM);
-    dense_tiles = active * (m_pad / kSmallM);
+    exact[kG256] = g256;
+    exact[kD64] = active * (m_pad / kSmallM);
+    exact[kG64] = g64;
     if (path == MOE_GEMM_AUTO) {
-      dense1 = prefer_dense(big_tiles, dense_tiles, small_real, nt1);
-      dense2 = prefer_dense(big_tiles, dense_tiles, small_real, nt2);
+      k1 = pick_kind(g256, exact[kD64], g64, nt1);
+      k2 = pick_kind(g256, exact[kD64], g64, nt2);
     }
   }
-  if ((dense1 || dense2) && dense_tiles > w.cap[kTabPadded])
-    return fail(MOE_ERR_WORKSPACE, "moe_expert_ffn: dense path needs %lld tiles", (long long)dense_tiles);
+  if ((k1 == kD64 || k2 == kD64) && exact[kD64] > w.cap[kD64])
+    return fail(MOE_ERR_WORKSPACE, "moe_expert_ffn: dense path needs %lld tiles", (long long)exact[kD64]);
 
   char* ws = static_cast<char*>(workspace);
   int32_t* n_tiles = reinterpret_cast<int32_t*>(ws + w.n_tiles);
   auto tab_slot = [&](int t) { return reinterpret_cast<int32_t*>(ws + w.tab_slot[t]); };
   auto tab_row0 = [&](int t) { return reinterpret_cast<int32_t*>(ws + w.tab_row0[t]); };
-  auto build = [&](int t, int mode, int bm) {
+  auto build = [&](Kind t) {
+    const int mode = t == kD64 ? kPadded : kCover;
+    const int bm = t == kG256 ? kBigM : kSmallM;
     tiles_kernel<<<1, 256, 0, s>>>(slot_off, n_slots, max_slots, M, mode, bm, m_pad, w.cap[t], tab_slot(t),
                                    tab_row0(t), n_tiles + t);
     return hip_status(hipGetLastError(), "moe_expert_ffn tile-table launch");
   };
-  if (!dense1 || !dense2)
-    if (int rc = build(kTabGrouped, kCover, kBigM)) return rc;
-  if (dense1 || dense2)
-    if (int rc = build(kTabPadded, kPadded, kSmallM)) return rc;
+  if (int rc = build(k1)) return rc;
+  if (k2 != k1)
+    if (int rc = build(k2)) return rc;
 
   GemmArgs p1{};
   p1.A = x_perm;
@@ -205,22 +223,21 @@ extern "C" int moe_expert_ffn(const void* x_perm, moe_dtype dt, int64_t M, int H
   p2.K = I;
   p2.N = H;
   p2.n_col_tiles = nt2;
-  auto on = [&](GemmArgs& g, bool dense) {
-    const int t = dense ? kTabPadded : kTabGrouped;
+  auto on = [&](GemmArgs& g, Kind t) {
     g.tile_slot = tab_slot(t);
     g.tile_row0 = tab_row0(t);
     g.n_tiles = n_tiles + t;
   };
-  on(p1, dense1);
-  on(p2, dense2);
-  // grouped: an upper bound on the tiles (blocks past the count exit at once);
-  // dense: the exact padded batch
-  const int64_t bound = w.cap[kTabGrouped];
-  const unsigned grid1 = static_cast<unsigned>(std::max<int64_t>(1, (dense1 ? dense_tiles : bound) * nt1));
-  const unsigned grid2 = static_cast<unsigned>(std::max<int64_t>(1, (dense2 ? dense_tiles : bound) * nt2));
+  on(p1, k1);
+  on(p2, k2);
+  // exact tile counts when read back, else the table's capacity (blocks past the
+  // count exit at once)
+  auto tiles = [&](Kind t) { return exact[t] >= 0 ? exact[t] : static_cast<int64_t>(w.cap[t]); };
+  const unsigned grid1 = static_cast<unsigned>(std::max<int64_t>(1, tiles(k1) * nt1));
+  const unsigned grid2 = static_cast<unsigned>(std::max<int64_t>(1, tiles(k2) * nt2));
   const bool swiglu = act == MOE_SWIGLU;
-  return dt == MOE_BF16 ? launch_ffn<true>(p1, dense1, grid1, p2, dense2, grid2, swiglu, s)
-                        : launch_ffn<false>(p1, dense1, grid1, p2, dense2, grid2, swiglu, s);
+  return dt == MOE_BF16 ? launch_ffn<true>(p1, k1 != kG256, grid1, p2, k2 != kG256, grid2, swiglu, s)
+                        : launch_ffn<false>(p1, k1 != kG256, grid1, p2, k2 != kG256, grid2, swiglu, s);
 }
 
 extern "C" int moe_ffn_set_timing_events(void* before_gateup, void* after_gateup, void* after_down) {

@@ -290,7 +290,7 @@ def test_popfetcher_full_chain_sampled():
 # ------------------------------------------------ grouped vs dense vs auto
 @pytest.mark.parametrize("name", ["tiny", "mixtral-mini", "dsv2-mini", "popf-mini"])
 def test_gemm_paths_are_bit_identical(name):
-    """The dense padded batch (64-row tiles) and the grouped tiles (256 rows)
+    """The dense padded batch (64-row tiles), the grouped 64-row and 256-row tiles
     compute every row with the same K order: identical bits."""
     cfg = MINI[name]
     x = synth.hidden0(cfg, 2)
@@ -298,10 +298,10 @@ def test_gemm_paths_are_bit_identical(name):
     wts = synth.expert_weights(cfg)
     ref = oracle.moe_layer(x, lg, cfg.k, wts, cfg.act)
     outs = {}
-    for path in ("grouped", "dense", "auto"):
+    for path in ("grouped", "dense", "grouped_small", "auto"):
         res = _gpu_layer(cfg, x, lg, wts, 0, path=path)
         outs[path] = (from_dev(res["y_perm"]), from_dev(res["out"]))
-    for path in ("dense", "auto"):
+    for path in ("dense", "grouped_small", "auto"):
         assert np.array_equal(outs[path][0], outs["grouped"][0]), path
         assert np.array_equal(outs[path][1], outs["grouped"][1]), path
     kind = "bf16" if cfg.dtype == "bf16" else "fp32_gemm"
@@ -310,13 +310,15 @@ def test_gemm_paths_are_bit_identical(name):
 
 def test_dense_path_full_size_dsv2_small_batch():
     """DeepSeek-V2 shape at T=1024: many small and some empty experts, where the
-    dense path is meant to win; it must equal the grouped path bit for bit."""
+    64-row tilings win; the dense, grouped-small and auto paths must equal the
+    grouped path bit for bit."""
     cfg = synth.CONFIGS["dsv2"].with_T(1024)
     x = synth.hidden0(cfg, 0)
     lg = synth.logits(cfg, 0, 0)
     wts = synth.expert_weights(cfg, threads=16)
     g = _gpu_layer(cfg, x, lg, wts, 0, path="grouped")
     yg, og = from_dev(g["y_perm"]), from_dev(g["out"])
-    d = _gpu_layer(cfg, x, lg, wts, 0, path="dense")
-    assert np.array_equal(from_dev(d["y_perm"]), yg)
-    assert np.array_equal(from_dev(d["out"]), og)
+    for path in ("dense", "grouped_small", "auto"):
+        d = _gpu_layer(cfg, x, lg, wts, 0, path=path)
+        assert np.array_equal(from_dev(d["y_perm"]), yg), path
+        assert np.array_equal(from_dev(d["out"]), og), path
