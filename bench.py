@@ -64,10 +64,15 @@ def parse():
 
 
 def kernel_source_hash() -> str:
-    """Hash of the sources the gate/up GEMM is built from (the kernel template and its launcher)."""
+    """Hash of the code the gate/up GEMM is built from (the kernel template and its
+    launcher), comments and whitespace removed: comment edits keep the counters valid."""
+    import re
     h = hashlib.sha256()
     for path in GEMM_SOURCES:
-        h.update(open(path, "rb").read())
+        text = open(path).read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -7,29 +7,18 @@
 // SwiGLU h = silu(x Wg^T) * (x Wu^T), y = h Wd^T; GELU h = gelu(x W1^T),
 // y = h W2^T.
 //
-// A tile-table pass, then two launches of one tiled kernel:
-//   tiles:   lists every (slot, 256-row tile); tiles cover each slot's rows
-//            exactly, no host sync.
+// A tile-table pass, then two launches of the tiled MFMA kernel of gemm.h:
+//   tiles:   lists the row tiles of a GEMM: 256-row tiles covering each slot
+//            (GROUPED), 64-row tiles covering each slot (GROUPED_SMALL), or
+//            every active slot padded to the largest (DENSE); AUTO reads the
+//            slot sizes back and picks per GEMM by a fitted cost model.
 //   phase 1: per tile and per 128 columns of I, the gate and up weight tiles
 //            are multiplied side by side so one lane holds g and u of the same
 //            element; the activation runs in the epilogue and h is rounded to
 //            the dtype once (GELU: one 256-column weight tile).
 //   phase 2: y = h Wd^T per tile and 256 columns of H, rounded to the dtype.
-//
-// gfx950 mapping.  A block is 256 threads (4 waves, one per SIMD) computing a
-// 256 x 256 output tile; each wave owns 128 x 128 as 4 x 4 MFMA tiles of
-// 32 x 32 (v_mfma_f32_32x32x16_bf16, or v_mfma_f32_32x32x2f32 for fp32), 256
-// accumulator registers.  K advances 128 bytes per row per step (64 bf16 / 32
-// fp32) through two LDS stages (2 x 144 KB-ish of padded rows, conflict-free
-// 16-byte fragment reads); the next step's tiles travel global -> registers
-// while the current one is multiplied, one barrier per step.  Operands are
-// read with raw buffer loads whose range ends at the slot's (or matrix's)
-// last valid row, so rows past the end read as zero and need no clamping.
-// Blocks are remapped so each of the 8 XCDs works on a contiguous run of
-// tiles, ordered 8 row tiles by N columns, which keeps the A and B tiles that
-// neighbouring blocks share inside that XCD's L2.  Each output row depends
-// only on its own input row and the fixed K order, so a row's value does not
-// depend on the tile, slot or path that computes it.
+// Each output row depends only on its own input row and the fixed K order, so
+// a row's value does not depend on the tile, slot or path that computes it.
 #include <algorithm>
 #include <vector>
 
