@@ -118,10 +118,18 @@ def test_stats_dsv2_replicas_large_E():
     _run_stats_chain(cfg, 4)
 
 
+def test_stats_maximum_E_and_k():
+    """E = 256 experts, top-8, a 3-layer chain: the largest expert count and k the
+    library accepts (co-occurrence kept in global atomics rather than LDS)."""
+    cfg = synth.CONFIGS["dsv2"].scaled(T=900, E=256, k=8, L=3, R=100, window=4)
+    _run_stats_chain(cfg, 5)
+
+
 # ----------------------------------------------------------------- dispatch
 @pytest.mark.parametrize("T,E,k,H,dt,R", [(256, 8, 2, 64, "f32", 4), (1000, 160, 6, 96, "bf16", 0),
                                           (513, 16, 4, 64, "bf16", 16), (1, 8, 2, 8, "bf16", 3),
-                                          (300, 32, 2, 40, "f32", 5), (4100, 8, 2, 128, "bf16", 8)])
+                                          (300, 32, 2, 40, "f32", 5), (4100, 8, 2, 128, "bf16", 8),
+                                          (777, 256, 8, 64, "bf16", 64)])
 def test_dispatch_matches_oracle(T, E, k, H, dt, R):
     lg = _logits(T, E, 7 * T + E, skew=2.0)
     idx_o, _ = oracle.route(lg, k)
