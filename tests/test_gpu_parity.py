@@ -170,6 +170,7 @@ MINI = {
     "dsv2-mini": synth.CONFIGS["dsv2"].scaled(T=200, H=320, I=192),
     "dbrx-mini": synth.CONFIGS["dbrx"].scaled(T=257, H=384, I=640),
     "popf-mini": synth.CONFIGS["popfetcher"].scaled(T=500, H=128, I=256, L=1),
+    "max-E-mini": synth.CONFIGS["dsv2"].scaled(T=150, E=256, k=8, H=128, I=192, R=32),
 }
 
 
