@@ -233,7 +233,8 @@ unsigned wgrad_grid(int E, int64_t rows, int col_tiles) {
 }
 
 struct BwdLayout {
-  size_t gu, dgu, dy, wdT, wguT, ta, tb, ones, seg, slot_expert, n_slots, tab_slot, tab_row0, n_tiles, bytes;
+  size_t gu, dgu, dy, wdT, wguT, ta, tb, ones, seg, slot_expert, n_slots, tab_slot, tab_row0, tab_rend, n_tiles,
+      bytes;
   int64_t ld;  // padded row length of the transposed activations
   int tiles_cap;
 };
@@ -260,6 +261,7 @@ BwdLayout bwd_layout(moe_dtype dt, int64_t T, int k, int H, int I, int E, moe_ac
   w.n_slots = take(sizeof(int32_t));
   w.tab_slot = take(sizeof(int32_t) * w.tiles_cap);
   w.tab_row0 = take(sizeof(int32_t) * w.tiles_cap);
+  w.tab_rend = take(sizeof(int32_t) * w.tiles_cap);
   w.n_tiles = take(sizeof(int32_t));
   w.bytes = at;
   return w;
@@ -290,13 +292,14 @@ int run_backward(const void* x_perm, const void* y_perm, int64_t n_tok, int k, i
   int32_t* n_slots = reinterpret_cast<int32_t*>(at(L.n_slots));
   int32_t* tab_slot = reinterpret_cast<int32_t*>(at(L.tab_slot));
   int32_t* tab_row0 = reinterpret_cast<int32_t*>(at(L.tab_row0));
+  int32_t* tab_rend = reinterpret_cast<int32_t*>(at(L.tab_rend));
   int32_t* n_tiles = reinterpret_cast<int32_t*>(at(L.n_tiles));
   auto check = [&](const char* what) { return hip_status(hipGetLastError(), what); };
 
   bwd_setup_kernel<<<static_cast<unsigned>(std::min<int64_t>(1024, ceil_div(M, 256)) + 1), 256, 0, s>>>(
       expert_off, E, M, L.ld, seg, slot_expert, n_slots, ones, M);
-  tiles_kernel<<<1, 256, 0, s>>>(expert_off, n_slots, E, M, kCover, 256, 0, L.tiles_cap, tab_slot, tab_row0,
-                                 n_tiles);
+  tiles_kernel<<<1, 256, 0, s>>>(expert_off, slot_expert, n_slots, E, M, kCover, 256, 0, 0, L.tiles_cap, tab_slot,
+                                 tab_row0, tab_rend, n_tiles);
   if (int rc = check("moe_backward setup")) return rc;
 
   // 1. gate + combine transpose
@@ -321,6 +324,7 @@ int run_backward(const void* x_perm, const void* y_perm, int64_t n_tok, int k, i
   base.slot_expert = slot_expert;
   base.tile_slot = tab_slot;
   base.tile_row0 = tab_row0;
+  base.tile_rend = tab_rend;
   base.n_tiles = n_tiles;
   const unsigned grid_rows = static_cast<unsigned>(L.tiles_cap);
 

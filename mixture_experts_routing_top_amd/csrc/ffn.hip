@@ -31,7 +31,7 @@ constexpr int kBigM = 256;    // grouped path: 256-row tiles
 constexpr int kSmallM = 64;   // dense path: 64-row tiles
 
 struct WsLayout {
-  size_t h, tab_slot[3], tab_row0[3], n_tiles, bytes;
+  size_t h, tab_slot[3], tab_row0[3], tab_rend[3], n_tiles, bytes;
   int cap[3];  // tile capacity of each table
 };
 
@@ -53,6 +53,7 @@ WsLayout ws_layout(moe_dtype dt, int64_t M, int I, int max_slots) {
     w.cap[t] = static_cast<int>(std::min<int64_t>(cap[t], 0x3fffffff));
     w.tab_slot[t] = take(sizeof(int32_t) * w.cap[t]);
     w.tab_row0[t] = take(sizeof(int32_t) * w.cap[t]);
+    w.tab_rend[t] = take(sizeof(int32_t) * w.cap[t]);
   }
   w.n_tiles = take(3 * sizeof(int32_t));
   w.bytes = at;
@@ -150,20 +151,28 @@ extern "C" int moe_expert_ffn(const void* x_perm, moe_dtype dt, int64_t M, int H
   int m_pad = 0;
   int64_t exact[3] = {-1, -1, -1};  // tiles per kind, when known on the host
   if (path == MOE_GEMM_DENSE || path == MOE_GEMM_AUTO) {
-    std::vector<int32_t> off(static_cast<size_t>(max_slots) + 2);
+    // slot sizes, with consecutive slots of one expert merged into one range
+    // exactly as the tile tables merge them
+    std::vector<int32_t> off(static_cast<size_t>(max_slots) + 2), se(static_cast<size_t>(max_slots));
     if (int rc = hip_status(hipMemcpyAsync(off.data(), slot_off, sizeof(int32_t) * (max_slots + 1),
                                            hipMemcpyDeviceToHost, s), "moe_expert_ffn slot readback")) return rc;
     if (int rc = hip_status(hipMemcpyAsync(&off[max_slots + 1], n_slots, sizeof(int32_t), hipMemcpyDeviceToHost, s),
                             "moe_expert_ffn slot readback")) return rc;
+    if (int rc = hip_status(hipMemcpyAsync(se.data(), slot_expert, sizeof(int32_t) * max_slots,
+                                           hipMemcpyDeviceToHost, s), "moe_expert_ffn slot readback")) return rc;
     if (int rc = hip_status(hipStreamSynchronize(s), "moe_expert_ffn slot readback")) return rc;
     const int n = std::min(std::max(off[max_slots + 1], 0), max_slots);
     int64_t largest = 0, active = 0, g256 = 0, g64 = 0;
-    for (int i = 0; i < n; ++i) {
-      const int64_t r = std::max<int64_t>(0, std::min<int64_t>(off[i + 1], M) - std::max<int64_t>(off[i], 0));
+    for (int i = 0; i < n;) {
+      int last = i + 1;
+      while (last < n && se[last] == se[i]) ++last;
+      const int64_t r = std::max<int64_t>(0, std::min<int64_t>(std::max(off[last], 0), M) -
+                                                 std::min<int64_t>(std::max(off[i], 0), M));
       largest = std::max(largest, r);
       if (r > 0) ++active;
       g256 += ceil_div(r, kBigM);
       g64 += ceil_div(r, kSmallM);
+      i = last;
     }
     m_pad = static_cast<int>(ceil_div(std::max<int64_t>(largest, 1), kSmallM) * kSmallM);
     exact[kG256] = g256;
@@ -181,11 +190,12 @@ extern "C" int moe_expert_ffn(const void* x_perm, moe_dtype dt, int64_t M, int H
   int32_t* n_tiles = reinterpret_cast<int32_t*>(ws + w.n_tiles);
   auto tab_slot = [&](int t) { return reinterpret_cast<int32_t*>(ws + w.tab_slot[t]); };
   auto tab_row0 = [&](int t) { return reinterpret_cast<int32_t*>(ws + w.tab_row0[t]); };
+  auto tab_rend = [&](int t) { return reinterpret_cast<int32_t*>(ws + w.tab_rend[t]); };
   auto build = [&](Kind t) {
     const int mode = t == kD64 ? kPadded : kCover;
     const int bm = t == kG256 ? kBigM : kSmallM;
-    tiles_kernel<<<1, 256, 0, s>>>(slot_off, n_slots, max_slots, M, mode, bm, m_pad, w.cap[t], tab_slot(t),
-                                   tab_row0(t), n_tiles + t);
+    tiles_kernel<<<1, 256, 0, s>>>(slot_off, slot_expert, n_slots, max_slots, M, mode, bm, m_pad, 1, w.cap[t],
+                                   tab_slot(t), tab_row0(t), tab_rend(t), n_tiles + t);
     return hip_status(hipGetLastError(), "moe_expert_ffn tile-table launch");
   };
   if (int rc = build(k1)) return rc;
@@ -215,6 +225,7 @@ extern "C" int moe_expert_ffn(const void* x_perm, moe_dtype dt, int64_t M, int H
   auto on = [&](GemmArgs& g, Kind t) {
     g.tile_slot = tab_slot(t);
     g.tile_row0 = tab_row0(t);
+    g.tile_rend = tab_rend(t);
     g.n_tiles = n_tiles + t;
   };
   on(p1, k1);

@@ -82,6 +82,7 @@ struct GemmArgs {
   const int32_t* slot_expert;
   const int32_t* tile_slot;
   const int32_t* tile_row0;
+  const int32_t* tile_rend;  // end row of the range the tile belongs to
   const int32_t* n_tiles;
   int n_col_tiles;
   // backward only
@@ -184,7 +185,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   } else {
     const int s = g.tile_slot[mt];
     r0 = g.tile_row0[mt];
-    const int64_t rend = min<int64_t>(g.slot_off[s + 1], g.M);
+    const int64_t rend = min<int64_t>(g.tile_rend[mt], g.M);
     e = g.slot_expert[s];
     if (r0 >= rend || e < 0 || e >= g.E) return;
     K = g.K;
@@ -447,18 +448,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
 }
 
-// Lists the row tiles of the GEMMs, per slot s with n rows from `start`:
-//   kCover:  ceil(n / BM) tiles from start (the last one may be partial);
-//   kPadded: m_pad / BM tiles for every slot with rows, the uniform padded
-//            batch (tiles wholly past the slot's last row exit as soon as the
+// Lists the row tiles of the GEMMs.  With `merge`, consecutive slots of one
+// expert (its replica chunks) form one row range: on one GPU they share the
+// same weights, so tiling the run as a whole avoids a partial tile per chunk
+// (each row's result does not depend on its tile).  Per range with n rows:
+//   kCover:  ceil(n / BM) tiles from its first row (the last may be partial);
+//   kPadded: m_pad / BM tiles for every range with rows, the uniform padded
+//            batch (tiles wholly past the range's last row exit as soon as the
 //            GEMM reads them).
+// A tile records its range's first slot, first row and end row.
 enum TileMode { kCover = 0, kPadded = 1 };
 
 __global__ __launch_bounds__(256) void tiles_kernel(const int32_t* __restrict__ slot_off,
+                                                    const int32_t* __restrict__ slot_expert,
                                                     const int32_t* __restrict__ n_slots_p, int max_slots, int64_t M,
-                                                    int mode, int BM, int m_pad, int max_tiles,
+                                                    int mode, int BM, int m_pad, int merge, int max_tiles,
                                                     int32_t* __restrict__ tile_slot, int32_t* __restrict__ tile_row0,
-                                                    int32_t* __restrict__ n_tiles) {
+                                                    int32_t* __restrict__ tile_rend, int32_t* __restrict__ n_tiles) {
   __shared__ int32_t scan[256];
   __shared__ int32_t carry;
   const int tid = threadIdx.x;
@@ -467,10 +473,13 @@ __global__ __launch_bounds__(256) void tiles_kernel(const int32_t* __restrict__ 
   __syncthreads();
   for (int c = 0; c < n; c += 256) {
     const int s = c + tid;
-    int64_t start = 0, cnt = 0;
-    if (s < n) {
+    int64_t start = 0, end = 0, cnt = 0;
+    if (s < n && !(merge && s > 0 && slot_expert[s] == slot_expert[s - 1])) {
+      int last = s + 1;  // one past the range's last slot
+      if (merge)
+        while (last < n && slot_expert[last] == slot_expert[s]) ++last;
       start = min<int64_t>(max(slot_off[s], 0), M);
-      const int64_t end = min<int64_t>(max(slot_off[s + 1], 0), M);
+      end = min<int64_t>(max(slot_off[last], 0), M);
       const int64_t rows = end > start ? end - start : 0;
       if (mode == kCover) cnt = (rows + BM - 1) / BM;
       else if (rows > 0) cnt = m_pad / BM;
@@ -489,6 +498,7 @@ __global__ __launch_bounds__(256) void tiles_kernel(const int32_t* __restrict__ 
       if (j < max_tiles) {
         tile_slot[j] = s;
         tile_row0[j] = static_cast<int32_t>(min<int64_t>(start + static_cast<int64_t>(q) * BM, M));
+        tile_rend[j] = static_cast<int32_t>(end);
       }
     }
     __syncthreads();
