@@ -18,6 +18,9 @@
 // read as zero and need no clamping.  Blocks are remapped so each of the 8 XCDs
 // works on a contiguous run of tiles, ordered 8 row tiles by N columns, which
 // keeps the A and B tiles that neighbouring blocks share inside that XCD's L2.
+// The weight fragment is the MFMA's first operand, so the accumulators come out
+// transposed: each lane holds four adjacent output columns of one row, which
+// the epilogue writes with one 8-byte (bf16) or 16-byte (fp32) store.
 // Each output row depends only on its own input row and the fixed K order, so
 // a row's value does not depend on the tile, slot or path that computes it.
 #pragma once
@@ -102,6 +105,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t
 __device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, int off) {
   const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
   return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Four adjacent outputs: fp32 as one 16-byte store, bf16 rounded to nearest
+// even (v_cvt_pk_bf16_f32) as one 8-byte store.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void store4(float* p, const float v[4]) {
+  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void store4(uint16_t* p, const float v[4]) {
+  const bf16x2 lo = __builtin_convertvector((f32x2{v[0], v[1]}), bf16x2);
+  const bf16x2 hi = __builtin_convertvector((f32x2{v[2], v[3]}), bf16x2);
+  *reinterpret_cast<uint2*>(p) = make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
 }
 
 // BM rows x 256 weight rows per block; the 4 waves form a WM x (4/WM) grid.
@@ -256,7 +272,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j) acc[i][j] = mma(fa[buf][i], fb[buf][j], acc[i][j]);
+      for (int j = 0; j < TN; ++j) acc[i][j] = mma(fb[buf][j], fa[buf][i], acc[i][j]);
   };
 
   const int nk = K / BK;
@@ -323,7 +339,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   if constexpr (!kWgrad && (EPI == kEpiGELU || EPI == kEpiSwiGLUBwd || EPI == kEpiGELUBwd)) {
     static_assert(NMAT == 1, "staged epilogues take one weight matrix");
     constexpr int RH = BM / WM;  // rows staged per round
-    static_assert(RH * kTileN * 4 <= 2 * kStageBytes, "staging tile must fit in LDS");
+    constexpr int kPitch = kTileN + 4;  // floats per staged row (padded: rows start 4 banks apart)
+    static_assert(RH * kPitch * 4 <= 2 * kStageBytes, "staging tile must fit in LDS");
     float* stage = reinterpret_cast<float*>(lds);
     __syncthreads();  // every wave is done with the operand stages
 #pragma unroll
@@ -334,8 +351,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
           for (int j = 0; j < TN; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-              stage[(i * 32 + 8 * (r >> 2) + 4 * lg + (r & 3)) * kTileN + wn * CW + j * 32 + lr] = acc[i][j][r];
+            for (int q = 0; q < 4; ++q)
+              *reinterpret_cast<float4*>(stage + (i * 32 + lr) * kPitch + wn * CW + j * 32 + 8 * q + 4 * lg) =
+                  make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
       }
       __syncthreads();
       // thread (ty, tx): columns 4 tx .. 4 tx + 3 of rows ty, ty + 4, ... (N is a
@@ -352,7 +370,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
           for (int u = 0; u < 4; ++u) {   // rows nb, nb + 4, nb + 8, nb + 12: loads first
             const int n = min(nb + 4 * u, rows - 1);
             const int64_t row = r0 + h * RH + n;
-            a[u] = *reinterpret_cast<const float4*>(stage + n * kTileN + 4 * tx);
+            a[u] = *reinterpret_cast<const float4*>(stage + n * kPitch + 4 * tx);
             if constexpr (EPI == kEpiSwiGLUBwd) {
               p0[u] = *reinterpret_cast<const float4*>(aux + row * 2 * N + col);
               p1[u] = *reinterpret_cast<const float4*>(aux + row * 2 * N + N + col);
@@ -405,47 +423,50 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     return;
   }
 
-  // ---- epilogue: lane holds column lr of each 32 x 32 tile, rows
-  // 8*(r/4) + 4*lg + r%4 --------------------------------------------------
+  // ---- epilogue: the weight fragment is the MFMA's first operand, so lane
+  // (lr, lg) of a 32 x 32 tile holds row lr and columns 8 q + 4 lg + c for
+  // element 4 q + c: four adjacent outputs, stored with one 8- or 16-byte write
   constexpr int JO = NMAT == 2 ? TN / 2 : TN;  // output column subtiles per wave
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+  for (int i = 0; i < TM; ++i) {
+    const int lrow_out = wm * (BM / WM) + i * 32 + lr;
+    if (lrow_out >= m_valid) continue;
+    const int64_t row = r0 + lrow_out;
 #pragma unroll
     for (int j = 0; j < JO; ++j) {
-      const int col = n0 + (NMAT == 2 ? wn * (CW / 2) : wn * CW) + j * 32 + lr;
+      const int cb = n0 + (NMAT == 2 ? wn * (CW / 2) : wn * CW) + j * 32;
+      if (cb >= N) continue;  // N is a multiple of 64: whole 32-column blocks are in or out
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int lrow_out = wm * (BM / WM) + i * 32 + 8 * (r >> 2) + 4 * lg + (r & 3);
-        if (lrow_out >= m_valid || col >= N) continue;
-        const int64_t row = r0 + lrow_out;
+      for (int q = 0; q < 4; ++q) {
+        const int col = cb + 8 * q + 4 * lg;
+        float v[4], w[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          v[c] = acc[i][j][4 * q + c];
+          if constexpr (EPI == kEpiStoreGU) w[c] = acc[i][j + TN / 2][4 * q + c];
+          if constexpr (EPI == kEpiSwiGLU) {
+            // silu(g) u with g / (1 + 2^(-g log2 e)); an infinite exponent gives 0
+            const float up = acc[i][j + TN / 2][4 * q + c];
+            v[c] = v[c] * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(v[c] * -1.4426950408889634f)) * up;
+          }
+        }
         if constexpr (kWgrad) {
           T* C = row < g.c_split
                      ? static_cast<T*>(g.C) + (static_cast<int64_t>(e) * g.c_split + row) * N
                      : static_cast<T*>(g.C2) + (static_cast<int64_t>(e) * (g.Mw - g.c_split) + row - g.c_split) * N;
-          const float v = acc[i][j][r];
-          if constexpr (kBf16) C[col] = static_cast<uint16_t>(f32_to_bf16_bits(v));
-          else C[col] = v;
+          store4(C + col, v);
         } else if constexpr (EPI == kEpiStoreGU) {
           float* C = static_cast<float*>(g.C) + row * 2 * N;
-          C[col] = acc[i][j][r];
-          C[N + col] = acc[i][j + TN / 2][r];
+          store4(C + col, v);
+          store4(C + N + col, w);
         } else if constexpr (EPI == kEpiStoreF32) {
-          static_cast<float*>(g.C)[row * N + col] = acc[i][j][r];
+          store4(static_cast<float*>(g.C) + row * N + col, v);
         } else {
-          float v;
-          if constexpr (EPI == kEpiSwiGLU) {
-            const float gt = acc[i][j][r], up = acc[i][j + TN / 2][r];
-            v = gt / (1.f + expf(-gt)) * up;
-          } else {
-            v = acc[i][j][r];
-          }
-          T* C = static_cast<T*>(g.C);
-          const int64_t o = row * N + col;
-          if constexpr (kBf16) C[o] = static_cast<uint16_t>(f32_to_bf16_bits(v));
-          else C[o] = v;
+          store4(static_cast<T*>(g.C) + row * N + col, v);
         }
       }
     }
+  }
 }
 
 // Lists the row tiles of the GEMMs.  With `merge`, consecutive slots of one
