@@ -245,7 +245,10 @@ int moe_dispatch(const void* x, moe_dtype dt, int64_t T, int H, const int32_t* t
  *                  a 64-row tile costing 0.55 of a 256-row one, at least one
  *                  wave of 256 CUs per grid), fitted to measured crossovers.
  *         All paths give bit-identical y_perm.  In every path consecutive
- *         slots of one expert (replicas) are tiled as one row range.
+ *         slots of one expert (replicas) are tiled as one row range.  Where a
+ *         GEMM runs on 256-row tiles whose blocks end in a partial wave of the
+ *         256 CUs, the row tiles of that wave are re-run as 64-row tiles when
+ *         the same cost model says so (decided on the device, no host sync).
  *   workspace  at least moe_expert_ffn_workspace_bytes(...) bytes.
  * Limits: dtype F32 or BF16; H and I multiples of 64; E <= max_slots;
  * M <= 2^31 - 1; rows referenced by slot_off lie in [0, M).

@@ -299,7 +299,7 @@ int run_backward(const void* x_perm, const void* y_perm, int64_t n_tok, int k, i
   bwd_setup_kernel<<<static_cast<unsigned>(std::min<int64_t>(1024, ceil_div(M, 256)) + 1), 256, 0, s>>>(
       expert_off, E, M, L.ld, seg, slot_expert, n_slots, ones, M);
   tiles_kernel<<<1, 256, 0, s>>>(expert_off, slot_expert, n_slots, E, M, kCover, 256, 0, 0, L.tiles_cap, tab_slot,
-                                 tab_row0, tab_rend, n_tiles);
+                                 tab_row0, tab_rend, n_tiles, TileSplit{});
   if (int rc = check("moe_backward setup")) return rc;
 
   // 1. gate + combine transpose

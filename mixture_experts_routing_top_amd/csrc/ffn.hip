@@ -31,9 +31,13 @@ constexpr int kBigM = 256;    // grouped path: 256-row tiles
 constexpr int kSmallM = 64;   // dense path: 64-row tiles
 
 struct WsLayout {
-  size_t h, tab_slot[3], tab_row0[3], tab_rend[3], n_tiles, bytes;
+  size_t h, tab_slot[3], tab_row0[3], tab_rend[3], n_tiles, split_slot, split_row0, split_rend, split_counts, bytes;
   int cap[3];  // tile capacity of each table
 };
+
+// 64-row tiles that re-tile the last, partial wave of a 256-row GEMM: they fit
+// in one wave of 256 blocks, so at most 256 / (column tiles) of them.
+constexpr int kSplitCap = 256;
 
 // The row tilings a GEMM can run on, each with its own tile table:
 //   kG256: 256-row tiles covering each slot (at most ceil(M/256) + slots);
@@ -56,6 +60,10 @@ WsLayout ws_layout(moe_dtype dt, int64_t M, int I, int max_slots) {
     w.tab_rend[t] = take(sizeof(int32_t) * w.cap[t]);
   }
   w.n_tiles = take(3 * sizeof(int32_t));
+  w.split_slot = take(2 * sizeof(int32_t) * kSplitCap);
+  w.split_row0 = take(2 * sizeof(int32_t) * kSplitCap);
+  w.split_rend = take(2 * sizeof(int32_t) * kSplitCap);
+  w.split_counts = take(4 * sizeof(int32_t));
   w.bytes = at;
   return w;
 }
@@ -72,15 +80,24 @@ void launch_gemm(bool small, const GemmArgs& p, unsigned grid, hipStream_t s) {
 }
 
 // Phase 1 (gate/up or W1) and phase 2 (down or W2), each on its own tile table.
+// The two GEMMs, each optionally followed by the 64-row tiles that re-tile its
+// last partial wave (tail grid 0: none).
 template <bool kBf16>
-int launch_ffn(const GemmArgs& p1, bool small1, unsigned grid1, const GemmArgs& p2, bool small2, unsigned grid2,
-               bool swiglu, hipStream_t s) {
+int launch_ffn(const GemmArgs& p1, bool small1, unsigned grid1, const GemmArgs& t1, unsigned tgrid1,
+               const GemmArgs& p2, bool small2, unsigned grid2, const GemmArgs& t2, unsigned tgrid2, bool swiglu,
+               hipStream_t s) {
   if (int rc = moe::hip_status(mark(0, s), "moe_expert_ffn timing event")) return rc;
-  if (swiglu) launch_gemm<kBf16, kEpiSwiGLU, 2>(small1, p1, grid1, s);
-  else launch_gemm<kBf16, kEpiGELU, 1>(small1, p1, grid1, s);
+  if (swiglu) {
+    launch_gemm<kBf16, kEpiSwiGLU, 2>(small1, p1, grid1, s);
+    if (tgrid1) launch_gemm<kBf16, kEpiSwiGLU, 2>(true, t1, tgrid1, s);
+  } else {
+    launch_gemm<kBf16, kEpiGELU, 1>(small1, p1, grid1, s);
+    if (tgrid1) launch_gemm<kBf16, kEpiGELU, 1>(true, t1, tgrid1, s);
+  }
   if (int rc = moe::hip_status(hipGetLastError(), "moe_expert_ffn gate/up launch")) return rc;
   if (int rc = moe::hip_status(mark(1, s), "moe_expert_ffn timing event")) return rc;
   launch_gemm<kBf16, kEpiStore, 1>(small2, p2, grid2, s);
+  if (tgrid2) launch_gemm<kBf16, kEpiStore, 1>(true, t2, tgrid2, s);
   if (int rc = moe::hip_status(hipGetLastError(), "moe_expert_ffn down launch")) return rc;
   return moe::hip_status(mark(2, s), "moe_expert_ffn timing event");
 }
@@ -191,11 +208,24 @@ extern "C" int moe_expert_ffn(const void* x_perm, moe_dtype dt, int64_t M, int H
   auto tab_slot = [&](int t) { return reinterpret_cast<int32_t*>(ws + w.tab_slot[t]); };
   auto tab_row0 = [&](int t) { return reinterpret_cast<int32_t*>(ws + w.tab_row0[t]); };
   auto tab_rend = [&](int t) { return reinterpret_cast<int32_t*>(ws + w.tab_rend[t]); };
+  // 256-row tables also list, per GEMM that runs on them, the 64-row tiles that
+  // replace the row tiles of its last partial wave when that is cheaper
+  int32_t* split_counts = reinterpret_cast<int32_t*>(ws + w.split_counts);
+  TileSplit split{};
+  split.nt[0] = k1 == kG256 ? nt1 : 0;
+  split.nt[1] = k2 == kG256 ? nt2 : 0;
+  split.cap = kSplitCap;
+  split.small_cost = static_cast<float>(kSmallCost);
+  split.slot = reinterpret_cast<int32_t*>(ws + w.split_slot);
+  split.row0 = reinterpret_cast<int32_t*>(ws + w.split_row0);
+  split.rend = reinterpret_cast<int32_t*>(ws + w.split_rend);
+  split.counts = split_counts;
   auto build = [&](Kind t) {
     const int mode = t == kD64 ? kPadded : kCover;
     const int bm = t == kG256 ? kBigM : kSmallM;
     tiles_kernel<<<1, 256, 0, s>>>(slot_off, slot_expert, n_slots, max_slots, M, mode, bm, m_pad, 1, w.cap[t],
-                                   tab_slot(t), tab_row0(t), tab_rend(t), n_tiles + t);
+                                   tab_slot(t), tab_row0(t), tab_rend(t), n_tiles + t,
+                                   t == kG256 ? split : TileSplit{});
     return hip_status(hipGetLastError(), "moe_expert_ffn tile-table launch");
   };
   if (int rc = build(k1)) return rc;
@@ -222,22 +252,39 @@ extern "C" int moe_expert_ffn(const void* x_perm, moe_dtype dt, int64_t M, int H
   p2.K = I;
   p2.N = H;
   p2.n_col_tiles = nt2;
-  auto on = [&](GemmArgs& g, Kind t) {
+  auto on = [&](GemmArgs& g, Kind t, int which) {
     g.tile_slot = tab_slot(t);
     g.tile_row0 = tab_row0(t);
     g.tile_rend = tab_rend(t);
-    g.n_tiles = n_tiles + t;
+    g.n_tiles = t == kG256 ? split_counts + 2 * which : n_tiles + t;
   };
-  on(p1, k1);
-  on(p2, k2);
+  on(p1, k1, 0);
+  on(p2, k2, 1);
+  // the tail launches: 64-row tiles from the split tables
+  auto tail = [&](const GemmArgs& g, int which) {
+    GemmArgs q = g;
+    q.tile_slot = split.slot + which * kSplitCap;
+    q.tile_row0 = split.row0 + which * kSplitCap;
+    q.tile_rend = split.rend + which * kSplitCap;
+    q.n_tiles = split_counts + 2 * which + 1;
+    return q;
+  };
+  const GemmArgs t1 = tail(p1, 0), t2 = tail(p2, 1);
+  // at most 256 / nt tail tiles per GEMM (one wave); blocks past the count exit
+  auto tail_grid = [&](int nt, Kind t) {
+    if (t != kG256 || nt > kWaveBlocks) return 0u;
+    return static_cast<unsigned>((kWaveBlocks / nt) * nt);
+  };
   // exact tile counts when read back, else the table's capacity (blocks past the
   // count exit at once)
   auto tiles = [&](Kind t) { return exact[t] >= 0 ? exact[t] : static_cast<int64_t>(w.cap[t]); };
   const unsigned grid1 = static_cast<unsigned>(std::max<int64_t>(1, tiles(k1) * nt1));
   const unsigned grid2 = static_cast<unsigned>(std::max<int64_t>(1, tiles(k2) * nt2));
   const bool swiglu = act == MOE_SWIGLU;
-  return dt == MOE_BF16 ? launch_ffn<true>(p1, k1 != kG256, grid1, p2, k2 != kG256, grid2, swiglu, s)
-                        : launch_ffn<false>(p1, k1 != kG256, grid1, p2, k2 != kG256, grid2, swiglu, s);
+  const unsigned tg1 = tail_grid(nt1, k1), tg2 = tail_grid(nt2, k2);
+  return dt == MOE_BF16
+             ? launch_ffn<true>(p1, k1 != kG256, grid1, t1, tg1, p2, k2 != kG256, grid2, t2, tg2, swiglu, s)
+             : launch_ffn<false>(p1, k1 != kG256, grid1, t1, tg1, p2, k2 != kG256, grid2, t2, tg2, swiglu, s);
 }
 
 extern "C" int moe_ffn_set_timing_events(void* before_gateup, void* after_gateup, void* after_down) {

@@ -480,12 +480,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // A tile records its range's first slot, first row and end row.
 enum TileMode { kCover = 0, kPadded = 1 };
 
+// Optional re-tiling of a 256-row cover table's last, partial wave of blocks,
+// per GEMM g (its column-tile count nt[g]; 0 = never): the row tiles whose
+// blocks form the partial wave are listed again as 64-row tiles when that
+// lowers the modelled cost (waves of 256-row blocks cost 1, waves of 64-row
+// blocks small_cost < 1).  Removing the partial wave saves at most one wave,
+// so the 64-row blocks must fit in one wave: at most 256 / nt[g] tiles.
+// counts[2g] is then the number of 256-row tiles to run, counts[2g + 1] the
+// number of 64-row tiles in table g ([g * cap, ...)).
+struct TileSplit {
+  int nt[2];
+  int cap;
+  float small_cost;
+  int32_t* slot;
+  int32_t* row0;
+  int32_t* rend;
+  int32_t* counts;
+};
+constexpr int kWaveBlocks = 256;  // one block per CU
+
 __global__ __launch_bounds__(256) void tiles_kernel(const int32_t* __restrict__ slot_off,
                                                     const int32_t* __restrict__ slot_expert,
                                                     const int32_t* __restrict__ n_slots_p, int max_slots, int64_t M,
                                                     int mode, int BM, int m_pad, int merge, int max_tiles,
                                                     int32_t* __restrict__ tile_slot, int32_t* __restrict__ tile_row0,
-                                                    int32_t* __restrict__ tile_rend, int32_t* __restrict__ n_tiles) {
+                                                    int32_t* __restrict__ tile_rend, int32_t* __restrict__ n_tiles,
+                                                    TileSplit split) {
   __shared__ int32_t scan[256];
   __shared__ int32_t carry;
   const int tid = threadIdx.x;
@@ -526,7 +546,41 @@ __global__ __launch_bounds__(256) void tiles_kernel(const int32_t* __restrict__ 
     if (tid == 255) carry += scan[255];
     __syncthreads();
   }
-  if (tid == 0) *n_tiles = min(carry, max_tiles);
+  const int total = min(carry, max_tiles);
+  if (tid == 0) *n_tiles = total;
+  if (split.counts == nullptr || tid != 0) return;
+  // the table's writes by the other threads are visible after the last barrier
+  for (int g = 0; g < 2; ++g) {
+    int big = total, small = 0;
+    const int nt = split.nt[g];
+    const int64_t blocks = static_cast<int64_t>(total) * nt;
+    if (nt > 0 && mode == kCover && BM == 256 && blocks % kWaveBlocks != 0) {
+      const int r = min<int64_t>(total, (blocks % kWaveBlocks + nt - 1) / nt);  // row tiles of the partial wave
+      int64_t rows_small = 0;
+      for (int t = total - r; t < total; ++t)
+        rows_small += (min(BM, tile_rend[t] - tile_row0[t]) + 63) / 64;
+      const auto waves = [](int64_t b) { return static_cast<float>((b + kWaveBlocks - 1) / kWaveBlocks); };
+      const float keep = waves(blocks);
+      const float cut = waves(static_cast<int64_t>(total - r) * nt) + split.small_cost * waves(rows_small * nt);
+      if (cut < keep && rows_small * nt <= kWaveBlocks && rows_small <= split.cap) {
+        big = total - r;
+        int32_t* sl = split.slot + g * split.cap;
+        int32_t* r0 = split.row0 + g * split.cap;
+        int32_t* re = split.rend + g * split.cap;
+        for (int t = big; t < total; ++t) {
+          const int end = min(tile_row0[t] + BM, tile_rend[t]);
+          for (int row = tile_row0[t]; row < end; row += 64) {
+            sl[small] = tile_slot[t];
+            r0[small] = row;
+            re[small] = tile_rend[t];
+            ++small;
+          }
+        }
+      }
+    }
+    split.counts[2 * g] = big;
+    split.counts[2 * g + 1] = small;
+  }
 }
 
 }  // namespace

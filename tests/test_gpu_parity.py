@@ -317,6 +317,27 @@ def test_gemm_paths_are_bit_identical(name):
     assert_close(outs["dense"][1], ref["out"], kind, "dense out")
 
 
+def test_tail_retiling_full_size_mixtral():
+    """Mixtral shape: the down GEMM's 256-row tiles fill 4.25 waves of the 256
+    CUs, so the grouped path re-runs the last partial wave's row tiles as 64-row
+    tiles.  Every row keeps its K order: the grouped output equals the all-64-row
+    path bit for bit, with and without replica slots."""
+    cfg = synth.CONFIGS["mixtral"]
+    x = synth.hidden0(cfg, 0)
+    lg = synth.logits(cfg, 0, 0)
+    wts = synth.expert_weights(cfg, threads=16)
+    wg, wu, wd = (to_dev(w) for w in wts)
+    xd, lgd = to_dev(x), to_dev(lg)
+    for R in (0, 8):
+        outs = {}
+        for path in ("grouped", "grouped_small"):
+            res = moe.moe_layer_forward(xd, lgd, cfg.k, wg, wu, wd, cfg.act, R, path=path)
+            _sync()
+            outs[path] = (res["y_perm"], res["out"])
+        assert torch.equal(outs["grouped"][0], outs["grouped_small"][0]), R
+        assert torch.equal(outs["grouped"][1], outs["grouped_small"][1]), R
+
+
 def test_dense_path_full_size_dsv2_small_batch():
     """DeepSeek-V2 shape at T=1024: many small and some empty experts, where the
     64-row tilings win; the dense, grouped-small and auto paths must equal the
