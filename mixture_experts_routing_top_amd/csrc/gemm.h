@@ -25,6 +25,8 @@
 // a row's value does not depend on the tile, slot or path that computes it.
 #pragma once
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace {
@@ -223,20 +225,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int goff = lrow * static_cast<int>(row_b) + lchunk * 16;  // + pass*32 rows + step*128
   const int pass_b = 32 * static_cast<int>(row_b);
   const int loff = lrow * kRowBytes + lchunk * 16;
-  uint4 st[P];
-  auto issue_one = [&](int p, int o) {
-    if (p < PA) st[p] = bload(ra, o + p * pass_b);
-    else if (NMAT == 1 || p < PA + 4) st[p] = bload(rb0, o + (p - PA) * pass_b);
-    else st[p] = bload(rb1, o + (p - PA - 4) * pass_b);
+  // NST register stages: 64-row tiles keep two steps of loads in flight (one
+  // of their K steps is shorter than the load latency); 256-row tiles one
+  constexpr int NST = BM == 64 ? 2 : 1;
+  uint4 st[NST][P];
+  auto issue_one = [&](int w, int p, int o) {
+    if (p < PA) st[w][p] = bload(ra, o + p * pass_b);
+    else if (NMAT == 1 || p < PA + 4) st[w][p] = bload(rb0, o + (p - PA) * pass_b);
+    else st[w][p] = bload(rb1, o + (p - PA - 4) * pass_b);
   };
-  auto issue = [&](int kt) {
+  // steps past the last one load from an offset out of range: zeros, no memory access
+  auto issue = [&](int w, int kt, int nk) {
+    const int o = kt < nk ? goff + kt * 128 : 0x7ffff000;
 #pragma unroll
-    for (int p = 0; p < P; ++p) issue_one(p, goff + kt * 128);
+    for (int p = 0; p < P; ++p) issue_one(w, p, o);
   };
   auto stash = [&](int stage) {
     char* base = lds + stage * kStageBytes + loff;
 #pragma unroll
-    for (int p = 0; p < P; ++p) *reinterpret_cast<uint4*>(base + p * 32 * kRowBytes) = st[p];
+    for (int p = 0; p < P; ++p) *reinterpret_cast<uint4*>(base + p * 32 * kRowBytes) = st[0][p];
   };
 
   // ---- MFMA mapping --------------------------------------------------------
@@ -276,18 +283,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   };
 
   const int nk = K / BK;
-  issue(0);
+  // register stage (kt & 1) ^ 1 holds step kt + 1 when NST == 2
+  // unconditional, step 1's loads older than step 2's as in the loop: the wait
+  // before each LDS write then covers only the loads issued NST steps earlier
+  issue(0, 0, nk);
   stash(0);
-  if (nk > 1) issue(1);
+  issue(NST - 1, 1, nk);
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (NST == 2) issue(0, 2, nk);
   __syncthreads();
   frags(lds, 0, 0);
-  for (int kt = 0; kt < nk; ++kt) {
+  auto step = [&](int kt, auto parity) {
+    constexpr int W = NST == 2 ? (decltype(parity)::value ^ 1) : 0;
     const char* sb = lds + (kt & 1) * kStageBytes;
     char* wb = lds + ((kt + 1) & 1) * kStageBytes + loff;
     // past the last step the offset is out of range: the loads return zeros
     // without touching memory
-    const int o2 = (kt + 2 < nk) ? goff + (kt + 2) * 128 : 0x7ffff000;
-    // sub-steps 0 .. KS-2: MFMAs + next fragments + LDS writes of step kt+1 + loads of step kt+2
+    const int o2 = (kt + 1 + NST < nk) ? goff + (kt + 1 + NST) * 128 : 0x7ffff000;
+    // sub-steps 0 .. KS-2: MFMAs + next fragments + LDS writes of step kt+1 + loads of step kt+1+NST
 #pragma unroll
     for (int kk = 0; kk < KS - 1; ++kk) {
       constexpr int PER = (P + KS - 2) / (KS - 1);
@@ -296,8 +309,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       int nw = 0;
 #pragma unroll
       for (int p = kk * PER; p < (kk + 1) * PER && p < P; ++p) {
-        *reinterpret_cast<uint4*>(wb + p * 32 * kRowBytes) = st[p];
-        issue_one(p, o2);
+        *reinterpret_cast<uint4*>(wb + p * 32 * kRowBytes) = st[W][p];
+        issue_one(W, p, o2);
         ++nw;
       }
       // interleave: NR x (fragment read, MFMA), then (LDS write, global load,
@@ -329,6 +342,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
     __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
     __builtin_amdgcn_sched_barrier(0);
+  };
+  if constexpr (NST == 1) {
+    for (int kt = 0; kt < nk; ++kt) step(kt, std::integral_constant<int, 0>{});
+  } else {
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+      step(kt, std::integral_constant<int, 0>{});
+      step(kt + 1, std::integral_constant<int, 1>{});
+    }
+    if (kt < nk) step(kt, std::integral_constant<int, 0>{});
   }
 
   // ---- epilogues with heavy per-element math: stage the fp32 accumulators
