@@ -10,11 +10,13 @@
 // BM x 256 output tile; with BM = 256 each wave owns 128 x 128 as 4 x 4 MFMA
 // tiles of 32 x 32 (v_mfma_f32_32x32x16_bf16, or v_mfma_f32_32x32x2f32 for
 // fp32), 256 accumulator registers.  K advances 128 bytes per row per step (64
-// bf16 / 32 fp32) through two LDS stages of padded rows (144-byte pitch:
-// conflict-free 16-byte fragment reads); the next step's tiles travel global ->
-// registers while the current one is multiplied, one barrier per step, with
-// the instruction order pinned by sched_group_barrier.  Operands are read with
-// raw buffer loads whose range ends at the last valid row, so rows past the end
+// bf16 / 32 fp32).  bf16 256-row tiles fetch their operands straight into LDS
+// (buffer_load ... lds: no register staging, no LDS write instructions), into
+// two A stages and three weight stages of swizzled 128-byte rows; the other
+// tiles stage the next step through registers into two LDS stages of padded
+// rows (144-byte pitch).  Both read conflict-free 16-byte fragments, take one
+// barrier per step and pin the instruction order.  Operands are read with raw
+// buffer loads whose range ends at the last valid row, so rows past the end
 // read as zero and need no clamping.  Blocks are remapped so each of the 8 XCDs
 // works on a contiguous run of tiles, ordered 8 row tiles by N columns, which
 // keeps the A and B tiles that neighbouring blocks share inside that XCD's L2.
@@ -109,6 +111,46 @@ __device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, int off) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Buffer descriptor in four SGPRs for the LDS-DMA loads below: offsets at or
+// past `bytes` read as zero without touching memory.
+__device__ __forceinline__ u32x4 dma_rsrc(const void* base, int64_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const unsigned n = bytes > 0x7fffffff ? 0x7fffffffu : static_cast<unsigned>(bytes);
+  u32x4 d;
+  d.x = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(a));
+  d.y = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(a >> 32) & 0xffffu);
+  d.z = __builtin_amdgcn_readfirstlane(n);
+  d.w = 0x00020000u;
+  return d;
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane i writes
+// lds_block + 16 i.  The instruction has no register result; its completion
+// is counted by vmcnt and awaited explicitly (wait_vm) before the barrier that
+// publishes the stage.
+// M0 is set here and nowhere else in these kernels.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void load_lds(const u32x4& r, int off, unsigned lds_block) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_block), "v"(off), "s"(r)
+               : "m0");
+}
+#pragma clang diagnostic pop
+
+// s_waitcnt vmcnt(n) with the other counters left alone (n < 64).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0xF70);
+}
+
+// Direct-to-LDS stage rows hold 128 bytes (one K step) as eight 16-byte chunks,
+// chunk c stored at c ^ swz(row): any 16 consecutive rows read at one logical
+// chunk hit 16 distinct 16-byte bank groups.  swz depends on row % 32 only.
+__device__ __forceinline__ int swz(int row) { return (row ^ ((row >> 3) & 3)) & 7; }
+
 // Four adjacent outputs: fp32 as one 16-byte store, bf16 rounded to nearest
 // even (v_cvt_pk_bf16_f32) as one 8-byte store.
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -148,7 +190,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   constexpr int NM = TM * TN;              // MFMAs per sub-step
   constexpr int kStageBytes = (BM + kTileN) * kRowBytes;
   static_assert(NM >= NR, "sub-step pattern assumes at least one MFMA per fragment read");
-  __shared__ __align__(16) char lds[2 * kStageBytes];
+  // bf16 256-row tiles (not weight gradients) load their operands straight into
+  // LDS (160 KiB: two A stages and three weight stages, unpadded); the others
+  // stage them through registers into two padded stages
+  constexpr bool kDTL = kBf16 && BM == 256 && !kWgrad;
+  constexpr int kStagedEpi = (!kWgrad && (EPI == kEpiGELU || EPI == kEpiSwiGLUBwd || EPI == kEpiGELUBwd))
+                                 ? (BM / WM) * (kTileN + 4) * 4 : 0;
+  constexpr int kDtlBytes = 2 * BM * 128 + 3 * kTileN * 128;  // two A stages, three weight stages
+  constexpr int kLdsBytes = kDTL ? (kDtlBytes > kStagedEpi ? kDtlBytes : kStagedEpi) : 2 * kStageBytes;
+  __shared__ __align__(1024) char lds[kLdsBytes];
 
   // ---- which tile: XCD-contiguous runs, grouped raster inside a run --------
   const int NT = g.n_col_tiles;
@@ -282,6 +332,140 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       for (int j = 0; j < TN; ++j) acc[i][j] = mma(fb[buf][j], fa[buf][i], acc[i][j]);
   };
 
+  // ---- direct-to-LDS main loop (bf16, 256-row tiles) ------------------------
+  // LDS holds two stages of the A rows and three of the 256 weight rows, 128
+  // bytes (one K step) per row, swizzled.  Wave w fills the 1 KiB blocks (8
+  // rows) 4p + w of a stage, lane i taking row i / 8 and the chunk that lands at
+  // i % 8.  A is fetched one step ahead, the weights two steps ahead, and the
+  // 16 blocks a wave fetches per step are spread over its four sub-steps.
+  auto dtl_main_loop = [&]() {
+    constexpr int SA = BM * 128;       // one A stage (two of them)
+    constexpr int SBW = kTileN * 128;  // one weight stage (three of them, after the A stages)
+    constexpr int PA_ = BM / 32;       // A blocks (8 rows) per wave per step
+    constexpr int PB_ = kTileN / 32;   // weight blocks per wave per step
+    static_assert(!kDTL || (PA_ == 8 && PB_ == 8), "issue pattern assumes 8 + 8 blocks per wave");
+    const int rb_ = static_cast<int>(row_b);
+    const u32x4 da = dma_rsrc(A, static_cast<int64_t>(m_valid) * row_b);
+    const u32x4 db0 = dma_rsrc(static_cast<const T*>(g.B0) + wofs, static_cast<int64_t>(n_valid) * row_b);
+    const u32x4 db1 = NMAT > 1 ? dma_rsrc(static_cast<const T*>(g.B1) + wofs, static_cast<int64_t>(n_valid) * row_b) : db0;
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    int offA[PA_], offB[PB_];
+#pragma unroll
+    for (int p = 0; p < PA_; ++p) {
+      const int row = 8 * (4 * p + wv) + (lane >> 3);
+      offA[p] = row * rb_ + (((lane & 7) ^ swz(row)) << 4);
+    }
+#pragma unroll
+    for (int p = 0; p < PB_; ++p) {
+      const int row = 8 * (4 * p + wv) + (lane >> 3);
+      const int src = (NMAT == 2 && row >= 128) ? row - 128 : row;
+      offB[p] = src * rb_ + (((lane & 7) ^ swz(row)) << 4);
+    }
+    const unsigned lds0 = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(reinterpret_cast<uintptr_t>(lds)));
+    auto dmaA = [&](int p, int st, int koff) { load_lds(da, offA[p] + koff, lds0 + st * SA + (4 * p + wv) * 1024); };
+    auto dmaB = [&](int p, int st, int koff) {
+      const unsigned dst = lds0 + 2 * SA + st * SBW + (4 * p + wv) * 1024;
+      if (NMAT == 1 || p < PB_ / 2) load_lds(db0, offB[p] + koff, dst);
+      else load_lds(db1, offB[p] + koff, dst);
+    };
+    const int nk = K / 64;
+    auto koff = [&](int kt) { return kt < nk ? kt * 128 : 0x7ffff000; };
+    const int sw = swz(lr);
+    const int a_rd2 = (wm * (BM / WM) + lr) * 128;
+    int b_rd2[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) b_rd2[j] = 2 * SA + (brow(j) + lr) * 128;
+    int kofs[KS];
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) kofs[kk] = ((2 * kk + lg) ^ sw) << 4;
+    // fragment read r of a sub-step in the order the MFMAs consume them:
+    // A tile 0, weight tiles 0 .. TN-1, A tiles 1 .. TM-1
+    auto frag = [&](int sa, int sbw, int kk, int buf, int r) {
+      if (r >= 1 && r <= TN) fb[buf][r - 1] = *reinterpret_cast<const Frag*>(lds + sbw * SBW + b_rd2[r - 1] + kofs[kk]);
+      else {
+        const int i = r == 0 ? 0 : r - TN;
+        fa[buf][i] = *reinterpret_cast<const Frag*>(lds + sa * SA + a_rd2 + i * 32 * 128 + kofs[kk]);
+      }
+    };
+    auto mfma1 = [&](int buf, int m) {
+      const int i = m / TN, j = m % TN;
+      acc[i][j] = mma(fb[buf][j], fa[buf][i], acc[i][j]);
+    };
+
+    // Per step kt (A stage kt % 2, weight stage kt % 3), blocks issued:
+    //   sub-step 0: A(kt+1) 4..7, W(kt+2) 2..3;  sub-steps 1, 2: W(kt+2) 4..5, 6..7;
+    //   barrier (A(kt+1) and W(kt+1) complete: only the 6 newest loads, all
+    //   of W(kt+2), may still be in flight);
+    //   sub-step 3: A(kt+2) 0..3 into the A stage step kt freed, W(kt+3) 0..1
+    //   into the weight stage step kt freed.
+    // prologue: A(0), W(0), W(1) whole, then the sub-step-3 share of step -1
+#pragma unroll
+    for (int p = 0; p < PA_; ++p) dmaA(p, 0, koff(0));
+#pragma unroll
+    for (int p = 0; p < PB_; ++p) dmaB(p, 0, koff(0));
+#pragma unroll
+    for (int p = 0; p < PB_; ++p) dmaB(p, 1, koff(1));
+    wait_vm<PB_>();
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < NR; ++r) frag(0, 0, 0, 0, r);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) dmaA(p, 1, koff(1));
+    dmaB(0, 2, koff(2));
+    dmaB(1, 2, koff(2));
+
+    int wcur = 0;  // weight stage of step kt
+    for (int kt = 0; kt < nk; ++kt) {
+      const int u = kt & 1;
+      const int w1 = wcur == 2 ? 0 : wcur + 1, w2 = w1 == 2 ? 0 : w1 + 1;
+      const int k1 = koff(kt + 1), k2 = koff(kt + 2);
+#pragma unroll
+      for (int kk = 0; kk < KS - 1; ++kk) {
+        int rd = 0, qa = 4, qb = 2 * kk + 2;
+        const int qbe = 2 * kk + 4;
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+          mfma1(kk & 1, m);
+          if (rd < NR) frag(u, wcur, kk + 1, (kk + 1) & 1, rd++);
+          if (m & 1) {
+            if (kk == 0 && qa < PA_) dmaA(qa++, u ^ 1, k1);
+            else if (qb < qbe) dmaB(qb++, w2, k2);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        while (rd < NR) frag(u, wcur, kk + 1, (kk + 1) & 1, rd++);
+        if (kk == 0)
+          while (qa < PA_) dmaA(qa++, u ^ 1, k1);
+        while (qb < qbe) dmaB(qb++, w2, k2);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      wait_vm<6>();
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+      const int k3 = koff(kt + 3);
+      int rd = 0, qa = 0, qb = 0;
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        mfma1((KS - 1) & 1, m);
+        if (rd < NR) frag(u ^ 1, w1, 0, KS & 1, rd++);
+        if (m & 1) {
+          if (qa < 4) dmaA(qa++, u, k2);
+          else if (qb < 2) dmaB(qb++, wcur, k3);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      while (rd < NR) frag(u ^ 1, w1, 0, KS & 1, rd++);
+      while (qa < 4) dmaA(qa++, u, k2);
+      while (qb < 2) dmaB(qb++, wcur, k3);
+      __builtin_amdgcn_sched_barrier(0);
+      wcur = w1;
+    }
+    // no load may still be writing LDS when an epilogue reuses it
+    wait_vm<0>();
+  };
+  if constexpr (kDTL) {
+    dtl_main_loop();
+  } else {
   const int nk = K / BK;
   // register stage (kt & 1) ^ 1 holds step kt + 1 when NST == 2
   // unconditional, step 1's loads older than step 2's as in the loop: the wait
@@ -353,6 +537,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
     if (kt < nk) step(kt, std::integral_constant<int, 0>{});
   }
+  }
 
   // ---- epilogues with heavy per-element math: stage the fp32 accumulators
   // through LDS, BM/WM rows at a time, then let every thread walk one column
@@ -363,7 +548,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     static_assert(NMAT == 1, "staged epilogues take one weight matrix");
     constexpr int RH = BM / WM;  // rows staged per round
     constexpr int kPitch = kTileN + 4;  // floats per staged row (padded: rows start 4 banks apart)
-    static_assert(RH * kPitch * 4 <= 2 * kStageBytes, "staging tile must fit in LDS");
+    static_assert(RH * kPitch * 4 <= kLdsBytes, "staging tile must fit in LDS");
     float* stage = reinterpret_cast<float*>(lds);
     __syncthreads();  // every wave is done with the operand stages
 #pragma unroll
