@@ -336,8 +336,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // LDS holds two stages of the A rows and three of the 256 weight rows, 128
   // bytes (one K step) per row, swizzled.  Wave w fills the 1 KiB blocks (8
   // rows) 4p + w of a stage, lane i taking row i / 8 and the chunk that lands at
-  // i % 8.  A is fetched one step ahead, the weights two steps ahead, and the
-  // 16 blocks a wave fetches per step are spread over its four sub-steps.
+  // i % 8.  A is fetched right after the barrier that frees its stage, the
+  // weights a step earlier, and the 16 blocks a wave fetches per step are
+  // spread over its four sub-steps.
   auto dtl_main_loop = [&]() {
     constexpr int SA = BM * 128;       // one A stage (two of them)
     constexpr int SBW = kTileN * 128;  // one weight stage (three of them, after the A stages)
@@ -370,6 +371,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     };
     const int nk = K / 64;
     auto koff = [&](int kt) { return kt < nk ? kt * 128 : 0x7ffff000; };
+    constexpr int BS0[4] = {0, 3, 6, 8};  // weight blocks issued in sub-steps 0, 1, 2
     const int sw = swz(lr);
     const int a_rd2 = (wm * (BM / WM) + lr) * 128;
     int b_rd2[TN];
@@ -393,12 +395,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     };
 
     // Per step kt (A stage kt % 2, weight stage kt % 3), blocks issued:
-    //   sub-step 0: A(kt+1) 4..7, W(kt+2) 2..3;  sub-steps 1, 2: W(kt+2) 4..5, 6..7;
-    //   barrier (A(kt+1) and W(kt+1) complete: only the 6 newest loads, all
-    //   of W(kt+2), may still be in flight);
-    //   sub-step 3: A(kt+2) 0..3 into the A stage step kt freed, W(kt+3) 0..1
-    //   into the weight stage step kt freed.
-    // prologue: A(0), W(0), W(1) whole, then the sub-step-3 share of step -1
+    //   sub-steps 0, 1, 2: W(kt+2) 0..2, 3..5, 6..7 into the weight stage step
+    //   kt-1 freed;
+    //   barrier (A(kt+1) and W(kt+1) complete: only the 8 newest loads, all of
+    //   W(kt+2), may still be in flight);
+    //   sub-step 3: A(kt+2) 0..7 into the A stage step kt freed.
+    // prologue: A(0), W(0), W(1) whole, then A(1) (the sub-step-3 share of step -1)
 #pragma unroll
     for (int p = 0; p < PA_; ++p) dmaA(p, 0, koff(0));
 #pragma unroll
@@ -410,53 +412,41 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
     for (int r = 0; r < NR; ++r) frag(0, 0, 0, 0, r);
 #pragma unroll
-    for (int p = 0; p < 4; ++p) dmaA(p, 1, koff(1));
-    dmaB(0, 2, koff(2));
-    dmaB(1, 2, koff(2));
+    for (int p = 0; p < PA_; ++p) dmaA(p, 1, koff(1));
 
     int wcur = 0;  // weight stage of step kt
     for (int kt = 0; kt < nk; ++kt) {
       const int u = kt & 1;
       const int w1 = wcur == 2 ? 0 : wcur + 1, w2 = w1 == 2 ? 0 : w1 + 1;
-      const int k1 = koff(kt + 1), k2 = koff(kt + 2);
+      const int k2 = koff(kt + 2);
 #pragma unroll
       for (int kk = 0; kk < KS - 1; ++kk) {
-        int rd = 0, qa = 4, qb = 2 * kk + 2;
-        const int qbe = 2 * kk + 4;
+        int rd = 0, qb = BS0[kk];
+        const int qbe = BS0[kk + 1];
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
           mfma1(kk & 1, m);
           if (rd < NR) frag(u, wcur, kk + 1, (kk + 1) & 1, rd++);
-          if (m & 1) {
-            if (kk == 0 && qa < PA_) dmaA(qa++, u ^ 1, k1);
-            else if (qb < qbe) dmaB(qb++, w2, k2);
-          }
+          if ((m & 1) && qb < qbe) dmaB(qb++, w2, k2);
           __builtin_amdgcn_sched_barrier(0);
         }
         while (rd < NR) frag(u, wcur, kk + 1, (kk + 1) & 1, rd++);
-        if (kk == 0)
-          while (qa < PA_) dmaA(qa++, u ^ 1, k1);
         while (qb < qbe) dmaB(qb++, w2, k2);
         __builtin_amdgcn_sched_barrier(0);
       }
-      wait_vm<6>();
+      wait_vm<PB_>();
       __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
-      const int k3 = koff(kt + 3);
-      int rd = 0, qa = 0, qb = 0;
+      int rd = 0, qa = 0;
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
         mfma1((KS - 1) & 1, m);
         if (rd < NR) frag(u ^ 1, w1, 0, KS & 1, rd++);
-        if (m & 1) {
-          if (qa < 4) dmaA(qa++, u, k2);
-          else if (qb < 2) dmaB(qb++, wcur, k3);
-        }
+        if ((m & 1) && qa < PA_) dmaA(qa++, u, k2);
         __builtin_amdgcn_sched_barrier(0);
       }
       while (rd < NR) frag(u ^ 1, w1, 0, KS & 1, rd++);
-      while (qa < 4) dmaA(qa++, u, k2);
-      while (qb < 2) dmaB(qb++, wcur, k3);
+      while (qa < PA_) dmaA(qa++, u, k2);
       __builtin_amdgcn_sched_barrier(0);
       wcur = w1;
     }
