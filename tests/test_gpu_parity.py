@@ -317,6 +317,24 @@ def test_gemm_paths_are_bit_identical(name):
     assert_close(outs["dense"][1], ref["out"], kind, "dense out")
 
 
+def test_direct_to_lds_tiles_partial_columns_odd_k():
+    """The bf16 256-row tiles (operands fetched straight into LDS) on a shape with
+    partial column tiles (I = 320: the last gate/up tile holds 64 of 128 columns;
+    H = 192: the down tile holds 192 of 256) and odd K-step counts (3 and 5).  Two
+    experts, top-2: 86 row tiles of 256, so the grid keeps them (only the gate/up
+    GEMM's last row tile is re-tiled).  Sampled tokens match the oracle and the
+    whole output equals the all-64-row path bit for bit."""
+    cfg = synth.CONFIGS["mixtral"].scaled(T=11008, E=2, H=192, I=320)
+    res = _sampled_layer_check(cfg, 0, n_sample=16)
+    y_g, out_g = res["y_perm"], res["out"]
+    x = synth.hidden0(cfg, 0)
+    lg = synth.logits(cfg, 0, 0)
+    wts = synth.expert_weights(cfg, threads=16)
+    small = _gpu_layer(cfg, x, lg, wts, 0, path="grouped_small")
+    assert torch.equal(small["y_perm"], y_g)
+    assert torch.equal(small["out"], out_g)
+
+
 def test_tail_retiling_full_size_mixtral():
     """Mixtral shape: the down GEMM's 256-row tiles fill 4.25 waves of the 256
     CUs, so the grouped path re-runs the last partial wave's row tiles as 64-row
