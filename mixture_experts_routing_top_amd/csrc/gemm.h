@@ -190,14 +190,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   constexpr int NM = TM * TN;              // MFMAs per sub-step
   constexpr int kStageBytes = (BM + kTileN) * kRowBytes;
   static_assert(NM >= NR, "sub-step pattern assumes at least one MFMA per fragment read");
-  // bf16 256-row tiles (not weight gradients) load their operands straight into
-  // LDS (160 KiB: two A stages and three weight stages, unpadded); the others
+  // bf16 tiles (not weight gradients) load their operands straight into LDS
+  // (160 KiB, unpadded rows): 256-row tiles in two A stages and three weight
+  // stages, 64-row tiles in four stages of both; fp32 and weight-gradient tiles
   // stage them through registers into two padded stages
   constexpr bool kDTL = kBf16 && BM == 256 && !kWgrad;
+  constexpr bool kDTL64 = kBf16 && BM == 64 && !kWgrad;
   constexpr int kStagedEpi = (!kWgrad && (EPI == kEpiGELU || EPI == kEpiSwiGLUBwd || EPI == kEpiGELUBwd))
                                  ? (BM / WM) * (kTileN + 4) * 4 : 0;
-  constexpr int kDtlBytes = 2 * BM * 128 + 3 * kTileN * 128;  // two A stages, three weight stages
-  constexpr int kLdsBytes = kDTL ? (kDtlBytes > kStagedEpi ? kDtlBytes : kStagedEpi) : 2 * kStageBytes;
+  constexpr int kDtlBytes = kDTL ? 2 * BM * 128 + 3 * kTileN * 128 : 4 * (BM + kTileN) * 128;
+  constexpr int kLdsBytes =
+      (kDTL || kDTL64) ? (kDtlBytes > kStagedEpi ? kDtlBytes : kStagedEpi) : 2 * kStageBytes;
   __shared__ __align__(1024) char lds[kLdsBytes];
 
   // ---- which tile: XCD-contiguous runs, grouped raster inside a run --------
@@ -453,8 +456,113 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // no load may still be writing LDS when an epilogue reuses it
     wait_vm<0>();
   };
+  // ---- direct-to-LDS main loop (bf16, 64-row tiles) -------------------------
+  // Four stages of 64 A rows and 256 weight rows, 128 bytes per row, swizzled;
+  // a stage's 40 blocks of 1 KiB go to wave w as blocks 4p + w.  Step kt + 3 is
+  // fetched during step kt (3, 3, 2 blocks in sub-steps 0-2 and 2 after the
+  // barrier) into the stage step kt - 1 freed, so each load has about three of
+  // these short steps to land.
+  auto dtl64_main_loop = [&]() {
+    constexpr int SB = (BM + kTileN) * 128;
+    constexpr int PW = (BM + kTileN) / 32;  // blocks per wave per step
+    constexpr int D[5] = {0, 3, 6, 8, PW};  // blocks issued up to the end of sub-steps 0, 1, 2, 3
+    static_assert(!kDTL64 || PW == 10, "issue pattern assumes 10 blocks per wave");
+    const int rb_ = static_cast<int>(row_b);
+    const u32x4 da = dma_rsrc(A, static_cast<int64_t>(m_valid) * row_b);
+    const u32x4 db0 = dma_rsrc(static_cast<const T*>(g.B0) + wofs, static_cast<int64_t>(n_valid) * row_b);
+    const u32x4 db1 = NMAT > 1 ? dma_rsrc(static_cast<const T*>(g.B1) + wofs, static_cast<int64_t>(n_valid) * row_b) : db0;
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    int doff[PW];
+#pragma unroll
+    for (int p = 0; p < PW; ++p) {
+      const int row = 8 * (4 * p + wv) + (lane >> 3);  // stage row: A rows, then weight rows
+      int src = row < BM ? row : row - BM;
+      if (NMAT == 2 && row >= BM + 128) src -= 128;
+      doff[p] = src * rb_ + (((lane & 7) ^ swz(row)) << 4);
+    }
+    const unsigned lds0 = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(reinterpret_cast<uintptr_t>(lds)));
+    // block 4p + w of a stage: A for p < BM / 32, then gate (or the only) weight
+    // rows, then up rows; which one is fixed by p alone
+    auto dma = [&](int p, int st, int koff) {
+      const unsigned dst = lds0 + st * SB + (4 * p + wv) * 1024;
+      if (4 * p < BM / 8) load_lds(da, doff[p] + koff, dst);
+      else if (NMAT == 1 || 4 * p < BM / 8 + 16) load_lds(db0, doff[p] + koff, dst);
+      else load_lds(db1, doff[p] + koff, dst);
+    };
+    const int nk = K / 64;
+    auto koff = [&](int kt) { return kt < nk ? kt * 128 : 0x7ffff000; };
+    const int sw = swz(lr);
+    const int a_rd2 = (wm * (BM / WM) + lr) * 128;
+    int b_rd2[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) b_rd2[j] = (BM + brow(j) + lr) * 128;
+    int kofs[KS];
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) kofs[kk] = ((2 * kk + lg) ^ sw) << 4;
+    auto frag = [&](int st, int kk, int buf, int r) {
+      const char* sb = lds + st * SB;
+      if (r >= 1 && r <= TN) fb[buf][r - 1] = *reinterpret_cast<const Frag*>(sb + b_rd2[r - 1] + kofs[kk]);
+      else {
+        const int i = r == 0 ? 0 : r - TN;
+        fa[buf][i] = *reinterpret_cast<const Frag*>(sb + a_rd2 + i * 32 * 128 + kofs[kk]);
+      }
+    };
+    auto mfma1 = [&](int buf, int m) {
+      const int i = m / TN, j = m % TN;
+      acc[i][j] = mma(fb[buf][j], fa[buf][i], acc[i][j]);
+    };
+    // prologue: steps 0, 1, 2 in flight, step 0 published
+#pragma unroll
+    for (int st = 0; st < 3; ++st)
+#pragma unroll
+      for (int p = 0; p < PW; ++p) dma(p, st, koff(st));
+    wait_vm<2 * PW>();
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < NR; ++r) frag(0, 0, 0, r);
+    int st0 = 0;  // stage of step kt
+    for (int kt = 0; kt < nk; ++kt) {
+      const int st1 = (st0 + 1) & 3, st3 = (st0 + 3) & 3;
+      const int k3 = koff(kt + 3);
+#pragma unroll
+      for (int kk = 0; kk < KS - 1; ++kk) {
+        int rd = 0, dq = D[kk];
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+          mfma1(kk & 1, m);
+          if (rd < NR) frag(st0, kk + 1, (kk + 1) & 1, rd++);
+          if (dq < D[kk + 1]) dma(dq++, st3, k3);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        while (rd < NR) frag(st0, kk + 1, (kk + 1) & 1, rd++);
+        while (dq < D[kk + 1]) dma(dq++, st3, k3);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // step kt + 1 has landed: the newer loads are step kt + 2's (issued during
+      // step kt - 1) and the 8 of step kt + 3 issued so far
+      wait_vm<PW + 8>();
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+      int rd = 0, dq = D[3];
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        mfma1((KS - 1) & 1, m);
+        if (rd < NR) frag(st1, 0, KS & 1, rd++);
+        if (dq < D[4]) dma(dq++, st3, k3);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      while (rd < NR) frag(st1, 0, KS & 1, rd++);
+      while (dq < D[4]) dma(dq++, st3, k3);
+      __builtin_amdgcn_sched_barrier(0);
+      st0 = st1;
+    }
+    // no load may still be writing LDS when an epilogue reuses it
+    wait_vm<0>();
+  };
   if constexpr (kDTL) {
     dtl_main_loop();
+  } else if constexpr (kDTL64) {
+    dtl64_main_loop();
   } else {
   const int nk = K / BK;
   // register stage (kt & 1) ^ 1 holds step kt + 1 when NST == 2
