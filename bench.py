@@ -44,7 +44,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--replicas", type=int, default=8)
-    ap.add_argument("--path", default="grouped", choices=["grouped", "dense", "auto"])
+    ap.add_argument("--path", default="grouped", choices=["grouped", "grouped_small", "dense", "auto"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=96, help="FFN rows the CPU oracle runs (sample)")
     ap.add_argument("--crossover", action="store_true",
