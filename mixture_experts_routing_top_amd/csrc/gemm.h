@@ -854,17 +854,28 @@ __global__ __launch_bounds__(256) void tiles_kernel(const int32_t* __restrict__ 
   }
   const int total = min(carry, max_tiles);
   if (tid == 0) *n_tiles = total;
-  if (split.counts == nullptr || tid != 0) return;
-  // the table's writes by the other threads are visible after the last barrier
+  if (split.counts == nullptr) return;
+  // the last (up to) 256 tiles, staged in LDS by all threads at once: the
+  // table's writes by the other threads are visible after the last barrier
+  __shared__ int32_t last_slot[256], last_row0[256], last_rend[256];
+  const int base = max(total - 256, 0);
+  if (base + tid < total) {
+    last_slot[tid] = tile_slot[base + tid];
+    last_row0[tid] = tile_row0[base + tid];
+    last_rend[tid] = tile_rend[base + tid];
+  }
+  __syncthreads();
+  if (tid != 0) return;
   for (int g = 0; g < 2; ++g) {
     int big = total, small = 0;
     const int nt = split.nt[g];
     const int64_t blocks = static_cast<int64_t>(total) * nt;
     if (nt > 0 && mode == kCover && BM == 256 && blocks % kWaveBlocks != 0) {
-      const int r = min<int64_t>(total, (blocks % kWaveBlocks + nt - 1) / nt);  // row tiles of the partial wave
+      // row tiles of the partial wave (fewer than 256 of them, all staged)
+      const int r = min<int64_t>(total, (blocks % kWaveBlocks + nt - 1) / nt);
       int64_t rows_small = 0;
       for (int t = total - r; t < total; ++t)
-        rows_small += (min(BM, tile_rend[t] - tile_row0[t]) + 63) / 64;
+        rows_small += (min(BM, last_rend[t - base] - last_row0[t - base]) + 63) / 64;
       const auto waves = [](int64_t b) { return static_cast<float>((b + kWaveBlocks - 1) / kWaveBlocks); };
       const float keep = waves(blocks);
       const float cut = waves(static_cast<int64_t>(total - r) * nt) + split.small_cost * waves(rows_small * nt);
@@ -874,11 +885,11 @@ __global__ __launch_bounds__(256) void tiles_kernel(const int32_t* __restrict__ 
         int32_t* r0 = split.row0 + g * split.cap;
         int32_t* re = split.rend + g * split.cap;
         for (int t = big; t < total; ++t) {
-          const int end = min(tile_row0[t] + BM, tile_rend[t]);
-          for (int row = tile_row0[t]; row < end; row += 64) {
-            sl[small] = tile_slot[t];
+          const int end = min(last_row0[t - base] + BM, last_rend[t - base]);
+          for (int row = last_row0[t - base]; row < end; row += 64) {
+            sl[small] = last_slot[t - base];
             r0[small] = row;
-            re[small] = tile_rend[t];
+            re[small] = last_rend[t - base];
             ++small;
           }
         }

@@ -146,6 +146,8 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(Args a) {
   // Eq.(1): windowed popularity of this layer.
   for (int e = tid; e < E; e += kThreads) {
     int32_t s = 0;
+    // unrolled so the window's loads are in flight together (exact integer sum)
+#pragma unroll 8
     for (int w = 0; w < window; ++w) s += cnt_ring[(static_cast<size_t>(w) * L + layer) * E + e];
     nw[e] = s;
     atomicAdd(&total, static_cast<unsigned long long>(s));
@@ -164,6 +166,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(Args a) {
     const size_t ring_stride = static_cast<size_t>(L - 1) * EE;
     auto window_cooc = [&](int q) {
       int32_t s = 0;
+#pragma unroll 8
       for (int w = 0; w < window; ++w) s += ring[w * ring_stride + q];
       return s;
     };
@@ -233,6 +236,7 @@ __global__ __launch_bounds__(kThreads) void load_state_kernel(const int32_t* __r
   };
   if (tid < E) {
     double d = 0.0, w = 1.0;
+#pragma unroll 8
     for (int age = 0; age < m; ++age) {
       d = __dadd_rn(d, __dmul_rn(w, at(age, tid)));
       w = __dmul_rn(w, decay);
@@ -242,9 +246,11 @@ __global__ __launch_bounds__(kThreads) void load_state_kernel(const int32_t* __r
     const int h = m - 1;
     if (h >= 2) {
       double sum = 0.0;
+#pragma unroll 8
       for (int age = 1; age < m; ++age) sum = __dadd_rn(sum, at(age, tid));
       const double mu = __ddiv_rn(sum, static_cast<double>(h));
       double var = 0.0;
+#pragma unroll 8
       for (int age = 1; age < m; ++age) {
         const double dd = __dsub_rn(at(age, tid), mu);
         var = __dadd_rn(var, __dmul_rn(dd, dd));
