@@ -57,6 +57,8 @@ __global__ __launch_bounds__(kTok) void rank_kernel(const int32_t* __restrict__ 
   const int b = blockIdx.x;
   for (int e = tid; e < E; e += kTok) {
     int32_t s = 0, pre = 0;
+    // unrolled so the column's loads are in flight together (exact integer sums)
+#pragma unroll 8
     for (int j = 0; j < nblk; ++j) {
       const int32_t c = blk_cnt[static_cast<int64_t>(j) * E + e];
       if (j < b) pre += c;

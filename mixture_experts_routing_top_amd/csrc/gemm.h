@@ -190,11 +190,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   constexpr int NM = TM * TN;              // MFMAs per sub-step
   constexpr int kStageBytes = (BM + kTileN) * kRowBytes;
   static_assert(NM >= NR, "sub-step pattern assumes at least one MFMA per fragment read");
-  // bf16 tiles (not weight gradients) load their operands straight into LDS
-  // (160 KiB, unpadded rows): 256-row tiles in two A stages and three weight
-  // stages, 64-row tiles in four stages of both; fp32 and weight-gradient tiles
-  // stage them through registers into two padded stages
-  constexpr bool kDTL = kBf16 && BM == 256 && !kWgrad;
+  // bf16 tiles load their operands straight into LDS (160 KiB, unpadded rows):
+  // 256-row tiles (weight gradients included) in two A stages and three weight
+  // stages, 64-row tiles in four stages of both; fp32 tiles stage them through
+  // registers into two padded stages
+  constexpr bool kDTL = kBf16 && BM == 256;
   constexpr bool kDTL64 = kBf16 && BM == 64 && !kWgrad;
   constexpr int kStagedEpi = (!kWgrad && (EPI == kEpiGELU || EPI == kEpiSwiGLUBwd || EPI == kEpiGELUBwd))
                                  ? (BM / WM) * (kTileN + 4) * 4 : 0;
