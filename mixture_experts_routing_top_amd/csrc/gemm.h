@@ -417,10 +417,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
     for (int p = 0; p < PA_; ++p) dmaA(p, 1, koff(1));
 
-    int wcur = 0;  // weight stage of step kt
-    for (int kt = 0; kt < nk; ++kt) {
-      const int u = kt & 1;
-      const int w1 = wcur == 2 ? 0 : wcur + 1, w2 = w1 == 2 ? 0 : w1 + 1;
+    // one K step; the stage indices are compile-time (the loop runs six steps
+    // per iteration: the A stages repeat every 2 steps, the weight stages every 3)
+    auto step = [&](int kt, auto U, auto WC) {
+      constexpr int u = decltype(U)::value, wcur = decltype(WC)::value;
+      constexpr int w1 = (wcur + 1) % 3, w2 = (wcur + 2) % 3;
       const int k2 = koff(kt + 2);
 #pragma unroll
       for (int kk = 0; kk < KS - 1; ++kk) {
@@ -451,8 +452,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       while (rd < NR) frag(u ^ 1, w1, 0, KS & 1, rd++);
       while (qa < PA_) dmaA(qa++, u, k2);
       __builtin_amdgcn_sched_barrier(0);
-      wcur = w1;
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    int kt = 0;
+    for (; kt + 6 <= nk; kt += 6) {
+      step(kt, I0{}, I0{});
+      step(kt + 1, I1{}, I1{});
+      step(kt + 2, I0{}, I2{});
+      step(kt + 3, I1{}, I0{});
+      step(kt + 4, I0{}, I1{});
+      step(kt + 5, I1{}, I2{});
     }
+    // the remaining steps (kt is a multiple of 6 here)
+    if (kt < nk) step(kt, I0{}, I0{});
+    if (kt + 1 < nk) step(kt + 1, I1{}, I1{});
+    if (kt + 2 < nk) step(kt + 2, I0{}, I2{});
+    if (kt + 3 < nk) step(kt + 3, I1{}, I0{});
+    if (kt + 4 < nk) step(kt + 4, I0{}, I1{});
     // no load may still be writing LDS when an epilogue reuses it
     wait_vm<0>();
   };
@@ -520,9 +538,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     __syncthreads();
 #pragma unroll
     for (int r = 0; r < NR; ++r) frag(0, 0, 0, r);
-    int st0 = 0;  // stage of step kt
-    for (int kt = 0; kt < nk; ++kt) {
-      const int st1 = (st0 + 1) & 3, st3 = (st0 + 3) & 3;
+    // one K step; its stage index is compile-time (the loop runs four steps per
+    // iteration, one per stage)
+    auto step = [&](int kt, auto ST) {
+      constexpr int st0 = decltype(ST)::value;
+      constexpr int st1 = (st0 + 1) & 3, st3 = (st0 + 3) & 3;
       const int k3 = koff(kt + 3);
 #pragma unroll
       for (int kk = 0; kk < KS - 1; ++kk) {
@@ -554,8 +574,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       while (rd < NR) frag(st1, 0, KS & 1, rd++);
       while (dq < D[4]) dma(dq++, st3, k3);
       __builtin_amdgcn_sched_barrier(0);
-      st0 = st1;
+    };
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
+    using S3 = std::integral_constant<int, 3>;
+    int kt = 0;
+    for (; kt + 4 <= nk; kt += 4) {
+      step(kt, S0{});
+      step(kt + 1, S1{});
+      step(kt + 2, S2{});
+      step(kt + 3, S3{});
     }
+    if (kt < nk) step(kt, S0{});
+    if (kt + 1 < nk) step(kt + 1, S1{});
+    if (kt + 2 < nk) step(kt + 2, S2{});
     // no load may still be writing LDS when an epilogue reuses it
     wait_vm<0>();
   };
