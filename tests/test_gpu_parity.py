@@ -317,14 +317,16 @@ def test_gemm_paths_are_bit_identical(name):
     assert_close(outs["dense"][1], ref["out"], kind, "dense out")
 
 
-def test_direct_to_lds_tiles_partial_columns_odd_k():
-    """The bf16 256-row tiles (operands fetched straight into LDS) on a shape with
-    partial column tiles (I = 320: the last gate/up tile holds 64 of 128 columns;
-    H = 192: the down tile holds 192 of 256) and odd K-step counts (3 and 5).  Two
-    experts, top-2: 86 row tiles of 256, so the grid keeps them (only the gate/up
-    GEMM's last row tile is re-tiled).  Sampled tokens match the oracle and the
-    whole output equals the all-64-row path bit for bit."""
-    cfg = synth.CONFIGS["mixtral"].scaled(T=11008, E=2, H=192, I=320)
+@pytest.mark.parametrize("H,I", [(192, 320), (448, 128), (64, 384)])
+def test_direct_to_lds_tiles_partial_columns_odd_k(H, I):
+    """The bf16 256-row tiles (operands fetched straight into LDS, the K loop
+    unrolled six steps at a time) on shapes with partial column tiles and K-step
+    counts 1, 2, 3, 5, 6 and 7 (every remainder of the unrolled loop but 4, which
+    the Mixtral shape covers): e.g. I = 320 leaves the last gate/up tile 64 of 128
+    columns and H = 192 the down tile 192 of 256.  Two experts, top-2: 86 row
+    tiles of 256, so the grid keeps most of them.  Sampled tokens match the oracle
+    and the whole output equals the all-64-row path bit for bit."""
+    cfg = synth.CONFIGS["mixtral"].scaled(T=11008, E=2, H=H, I=I)
     res = _sampled_layer_check(cfg, 0, n_sample=16)
     y_g, out_g = res["y_perm"], res["out"]
     x = synth.hidden0(cfg, 0)
