@@ -337,6 +337,38 @@ def test_direct_to_lds_tiles_partial_columns_odd_k(H, I):
     assert torch.equal(small["out"], out_g)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("M", [900, 30000])
+def test_expert_ffn_hand_made_slot_table(M, dtype):
+    """moe_expert_ffn on a slot table dispatch never produces: expert 0's rows in
+    two non-adjacent slots, two adjacent slots of expert 1 (tiled as one range),
+    an empty slot and unused slot capacity.  Every row matches the oracle's FFN of
+    its slot's expert, and the four paths give the same bits.  At M = 30000 the
+    256-row tiles stay (their blocks do not fit one wave as 64-row tiles)."""
+    cfg = synth.CONFIGS["mixtral"].scaled(T=M, E=3, H=128, I=192, dtype=dtype)
+    x = synth.hidden0(cfg, 3)
+    wts = synth.expert_weights(cfg)
+    cuts = [0, M // 9, M // 9, M // 3, (2 * M) // 3, (2 * M) // 3 + 1, M]
+    experts = [0, 2, 1, 1, 0, 2]
+    max_slots = 8
+    slot_off = np.full(max_slots + 1, M, np.int32)
+    slot_off[:len(cuts)] = cuts
+    slot_expert = np.zeros(max_slots, np.int32)
+    slot_expert[:len(experts)] = experts
+    n_slots = np.array([len(experts)], np.int32)
+    ref = oracle.ffn_rows(x, np.repeat(np.array(experts, np.int32), np.diff(cuts)), *wts, act="swiglu")
+    wg, wu, wd = (to_dev(w) for w in wts)
+    xd, so, se, ns = to_dev(x), to_dev(slot_off), to_dev(slot_expert), to_dev(n_slots)
+    outs = {}
+    for path in ("grouped", "grouped_small", "dense", "auto"):
+        y = moe.moe_expert_ffn(xd, so, se, ns, wg, wu, wd, act="swiglu", path=path)
+        _sync()
+        outs[path] = from_dev(y)
+    assert_close(outs["grouped"], ref, "bf16" if dtype == "bf16" else "fp32_gemm", "y_perm")
+    for path in ("grouped_small", "dense", "auto"):
+        assert np.array_equal(outs[path], outs["grouped"]), path
+
+
 def test_tail_retiling_full_size_mixtral():
     """Mixtral shape: the down GEMM's 256-row tiles fill 4.25 waves of the 256
     CUs, so the grouped path re-runs the last partial wave's row tiles as 64-row
