@@ -58,6 +58,9 @@ def parse():
                     help="horizontal-split pipeline and memory kernels on CU-masked streams (Mixtral layer)")
     ap.add_argument("--predict", action="store_true",
                     help="score the next-layer prediction and the replica plans on the 12-layer chain")
+    ap.add_argument("--vs-hipblaslt", action="store_true",
+                    help="dense single-expert gate/up and down GEMMs of the Mixtral shape next to hipBLASLt "
+                         "(torch.matmul) on the same shapes, in one process")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only copy a 256 MiB buffer 3 times (reference for the HBM byte counters) and exit")
     return ap.parse_args()
@@ -566,6 +569,67 @@ def backward_bench(moe, synth, torch, np, steps=5, warmup=2):
                          "workspace_gb": round(ws.numel() / 1e9, 2)}}
 
 
+def vs_hipblaslt(moe, torch, np, reps=10):
+    """The library's GEMMs next to the vendor library on the same dense shapes
+    (one expert holding all M = 16384 rows, so no partial tiles): the gate/up GEMM
+    (the library's includes the SwiGLU epilogue, torch's is a plain product) and
+    the down GEMM.  Times are medians of `reps` launches, HIP events."""
+    dev = "cuda"
+    M, H, I = 16384, 4096, 14336
+    torch.manual_seed(0)
+    x = torch.randn(M, H, device=dev).to(torch.bfloat16)
+    wg = (torch.randn(1, I, H, device=dev) / H ** 0.5).to(torch.bfloat16)
+    wu = (torch.randn(1, I, H, device=dev) / H ** 0.5).to(torch.bfloat16)
+    wd = (torch.randn(1, H, I, device=dev) / I ** 0.5).to(torch.bfloat16)
+    wgu = torch.cat([wg[0], wu[0]], 0).contiguous()
+    h = torch.randn(M, I, device=dev).to(torch.bfloat16)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for s_, e_ in ev:
+            s_.record()
+            fn()
+            e_.record()
+        torch.cuda.synchronize()
+        return float(np.median([s_.elapsed_time(e_) for s_, e_ in ev]))
+
+    t_gu = timed(lambda: torch.matmul(x, wgu.t()))
+    t_d = timed(lambda: torch.matmul(h, wd[0].t()))
+    slot_off = torch.tensor([0, M], dtype=torch.int32, device=dev)
+    slot_expert = torch.zeros(1, dtype=torch.int32, device=dev)
+    n_slots = torch.ones(1, dtype=torch.int32, device=dev)
+    ws = torch.empty(moe.moe_expert_ffn_workspace_bytes(torch.bfloat16, M, H, I, 1), dtype=torch.uint8, device=dev)
+    y = torch.empty(M, H, device=dev, dtype=torch.bfloat16)
+    lib = moe.lib()
+    for _ in range(3):
+        moe.moe_expert_ffn(x, slot_off, slot_expert, n_slots, wg, wu, wd, "swiglu", "grouped", y, ws)
+    torch.cuda.synchronize()
+    g1, g2 = [], []
+    for _ in range(reps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        for e_ in ev:
+            e_.record()
+        torch.cuda.synchronize()
+        lib.moe_ffn_set_timing_events(*(e_.cuda_event for e_ in ev))
+        moe.moe_expert_ffn(x, slot_off, slot_expert, n_slots, wg, wu, wd, "swiglu", "grouped", y, ws)
+        torch.cuda.synchronize()
+        lib.moe_ffn_set_timing_events(None, None, None)
+        g1.append(ev[0].elapsed_time(ev[1]))
+        g2.append(ev[1].elapsed_time(ev[2]))
+    f_gu, f_d = 2.0 * M * H * 2 * I, 2.0 * M * H * I
+    o_gu, o_d = float(np.median(g1)), float(np.median(g2))
+    return {"vs_hipblaslt": {
+        "shape": "one expert, M=16384, H=4096, I=14336, bf16",
+        "gateup": {"hipblaslt_ms": round(t_gu, 4), "hipblaslt_tflops": round(f_gu / t_gu / 1e9, 1),
+                   "library_ms": round(o_gu, 4), "library_tflops": round(f_gu / o_gu / 1e9, 1),
+                   "note": "the library's launch includes the SwiGLU epilogue; torch's is the plain product"},
+        "down": {"hipblaslt_ms": round(t_d, 4), "hipblaslt_tflops": round(f_d / t_d / 1e9, 1),
+                 "library_ms": round(o_d, 4), "library_tflops": round(f_d / o_d / 1e9, 1)}}}
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -591,6 +655,9 @@ def main():
 
     if a.crossover:
         crossover(moe, synth, torch, np)
+        return
+    if a.vs_hipblaslt:
+        print(json.dumps(vs_hipblaslt(moe, torch, np)), flush=True)
         return
     if a.configs:
         configs_bench(moe, synth, torch, np)
