@@ -102,10 +102,24 @@ def algorithmic_layer_work(T, H, I, E, k, n_mat):
     return flops, w_bytes, mem
 
 
+def spin_cycles(torch, stream, ms):
+    """Argument of torch.cuda._sleep that keeps the GPU busy for about `ms`
+    milliseconds (its counter's rate differs between devices: measured here)."""
+    n = 1 << 20
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    torch.cuda._sleep(n)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return max(1, int(n * ms / max(a.elapsed_time(b), 1e-3)))
+
+
 def memory_phase_summary(T, H, E, k, warm, cold):
     """Routing, dispatch and combine against HBM: their algorithmic bytes (route 4E in
     + 8k out per token; dispatch and combine (k+1)*H*2 each) over their event-timed
-    phase times (which also hold dispatch's index kernels and launch gaps)."""
+    GPU phase times (which also hold dispatch's two index kernels and the GPU's
+    gaps between launches)."""
     b = T * (4 * E + 8 * k) + 2 * T * (k + 1) * H * 2
     out = {"bytes": b}
     for label, ph in (("warm", warm), ("cold", cold)):
@@ -730,16 +744,21 @@ def main():
     # Per-phase split (diagnostic, outside the timed region): median of 5 passes
     # warm, then 5 cold passes, each after streaming a 512 MiB buffer through the
     # memory system (more than the 256 MB Infinity Cache plus the L2s) so every
-    # phase starts with its inputs in HBM only.
+    # phase starts with its inputs in HBM only.  Each pass waits behind a GPU-side
+    # spin of a few ms, so the host has issued every phase before the first one
+    # starts and the events time the kernels (and the GPU's own gaps between them),
+    # not the host's argument marshalling between launches.
     names = ["route", "stats", "dispatch", "expert_ffn", "combine"]
     samples = {n: [] for n in names}
     cold = {n: [] for n in names}
     flush = torch.empty(128 << 20, dtype=torch.float32, device=dev)
+    spin = spin_cycles(torch, stream, 3.0)
     for rep in range(10):
         phase_ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
         if rep >= 5:
             flush.fill_(float(rep))
         torch.cuda.synchronize()
+        torch.cuda._sleep(spin)
         phase_ev[0].record(stream)
         idx, w = moe.moe_route(logits, k, bufs["idx"], bufs["w"], stream)
         phase_ev[1].record(stream)
