@@ -184,7 +184,11 @@ def crossover(moe, synth, torch, np):
         res = dict(case=label, **extra)
         offs = slot_off.cpu().numpy()[: int(n_slots.item()) + 1].astype(np.int64)
         rows = np.diff(offs)
-        res["tiles"] = {"g256": int(np.sum((rows + 255) // 256)), "g64": int(np.sum((rows + 63) // 64)),
+        # the grouped tiling: full 256-row tiles, and a remainder of <= 64 rows as
+        # one 64-row tile (else one more 256-row tile)
+        rem64 = (rows % 256 > 0) & (rows % 256 <= 64)
+        res["tiles"] = {"g256": int(np.sum(rows // 256 + ((rows % 256 > 0) & ~rem64))),
+                        "g256_rem64": int(np.count_nonzero(rem64)), "g64": int(np.sum((rows + 63) // 64)),
                         "d64": int(np.count_nonzero(rows) * ((rows.max() + 63) // 64))}
         for path in ("grouped", "grouped_small", "dense", "auto"):
             for _ in range(2):

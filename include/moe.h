@@ -233,7 +233,9 @@ int moe_dispatch(const void* x, moe_dtype dt, int64_t T, int H, const int32_t* t
  * or path computes it (fixed reduction order, no split-K), so replicated and
  * non-replicated dispatches give bit-identical y_perm.
  *   path  GROUPED: 256-row tiles cover each slot's rows exactly (no host
- *                  sync): the large-batch form.
+ *                  sync): the large-batch form.  A remainder of at most 64
+ *                  rows (after the full 256-row tiles) runs as one 64-row tile
+ *                  in the same launch, after the 256-row tiles.
  *         GROUPED_SMALL: 64-row tiles cover each slot's rows exactly (no
  *                  host sync): less padding when slots hold few rows.
  *         DENSE:   every slot with rows is padded to the largest slot's row
@@ -246,9 +248,10 @@ int moe_dispatch(const void* x, moe_dtype dt, int64_t T, int H, const int32_t* t
  *                  wave of 256 CUs per grid), fitted to measured crossovers.
  *         All paths give bit-identical y_perm.  In every path consecutive
  *         slots of one expert (replicas) are tiled as one row range.  Where a
- *         GEMM runs on 256-row tiles whose blocks end in a partial wave of the
- *         256 CUs, the row tiles of that wave are re-run as 64-row tiles when
- *         the same cost model says so (decided on the device, no host sync).
+ *         GEMM runs on 256-row tiles whose blocks leave the launch's last
+ *         round of the 256 CUs mostly idle, its trailing row tiles are listed
+ *         again as 64-row tiles when the same cost model says so (decided on
+ *         the device, no host sync).
  *   workspace  at least moe_expert_ffn_workspace_bytes(...) bytes.
  * Limits: dtype F32 or BF16; H and I multiples of 64; E <= max_slots;
  * M <= 2^31 - 1; rows referenced by slot_off lie in [0, M).

@@ -9,9 +9,12 @@
 //
 // A tile-table pass, then two launches of the tiled MFMA kernel of gemm.h:
 //   tiles:   lists the row tiles of a GEMM: 256-row tiles covering each slot
-//            (GROUPED), 64-row tiles covering each slot (GROUPED_SMALL), or
-//            every active slot padded to the largest (DENSE); AUTO reads the
-//            slot sizes back and picks per GEMM by a fitted cost model.
+//            (GROUPED; a short remainder and, when the launch's last round
+//            would be mostly idle, the trailing row tiles go to a 64-row
+//            companion table run by the same launch), 64-row tiles covering
+//            each slot (GROUPED_SMALL), or every active slot padded to the
+//            largest (DENSE); AUTO reads the slot sizes back and picks per
+//            GEMM by a fitted cost model.
 //   phase 1: per tile and per 128 columns of I, the gate and up weight tiles
 //            are multiplied side by side so one lane holds g and u of the same
 //            element; the activation runs in the epilogue and h is rounded to
@@ -32,12 +35,18 @@ constexpr int kSmallM = 64;   // dense path: 64-row tiles
 
 struct WsLayout {
   size_t h, tab_slot[3], tab_row0[3], tab_rend[3], n_tiles, split_slot, split_row0, split_rend, split_counts, bytes;
-  int cap[3];  // tile capacity of each table
+  int cap[3];     // tile capacity of each table
+  int split_cap;  // entries of each GEMM's 64-row companion table
 };
 
-// 64-row tiles that re-tile the last, partial wave of a 256-row GEMM: they fit
-// in one wave of 256 blocks, so at most 256 / (column tiles) of them.
-constexpr int kSplitCap = 256;
+// AUTO's cost of a 64-row tile in 256-row tiles (see pick_kind), and the most
+// 64-row tiles a range's remainder may take in a 256-row tiling: while they
+// cost less than one 256-row tile (1 at 0.55, i.e. remainders of <= 64 rows).
+constexpr double kSmallCost = 0.55;
+constexpr int kRemTiles = kSmallCost >= 0.5 ? 1 : kSmallCost >= 1.0 / 3 ? 2 : 3;
+// 64-row tiles re-listing a 256-row table's trailing row tiles: at most
+// ceil(256 / column tiles) of them, four each.
+constexpr int kConvCap = 4 * 256;
 
 // The row tilings a GEMM can run on, each with its own tile table:
 //   kG256: 256-row tiles covering each slot (at most ceil(M/256) + slots);
@@ -60,9 +69,10 @@ WsLayout ws_layout(moe_dtype dt, int64_t M, int I, int max_slots) {
     w.tab_rend[t] = take(sizeof(int32_t) * w.cap[t]);
   }
   w.n_tiles = take(3 * sizeof(int32_t));
-  w.split_slot = take(2 * sizeof(int32_t) * kSplitCap);
-  w.split_row0 = take(2 * sizeof(int32_t) * kSplitCap);
-  w.split_rend = take(2 * sizeof(int32_t) * kSplitCap);
+  w.split_cap = static_cast<int>(std::min<int64_t>(static_cast<int64_t>(max_slots) * kRemTiles + kConvCap, 0x3fffffff));
+  w.split_slot = take(2 * sizeof(int32_t) * w.split_cap);
+  w.split_row0 = take(2 * sizeof(int32_t) * w.split_cap);
+  w.split_rend = take(2 * sizeof(int32_t) * w.split_cap);
   w.split_counts = take(4 * sizeof(int32_t));
   w.bytes = at;
   return w;
@@ -73,31 +83,24 @@ thread_local hipEvent_t g_timing[3] = {nullptr, nullptr, nullptr};
 
 hipError_t mark(int i, hipStream_t s) { return g_timing[i] ? hipEventRecord(g_timing[i], s) : hipSuccess; }
 
+// A 256-row tiling runs with its 64-row companion table in one mixed launch;
+// the 64-row tilings run alone.
 template <bool kBf16, int EPI, int NMAT>
-void launch_gemm(bool small, const GemmArgs& p, unsigned grid, hipStream_t s) {
+void launch_gemm(bool small, const GemmArgs& p, const GemmArgs& companion, unsigned grid, hipStream_t s) {
   if (small) gemm_kernel<kBf16, NMAT, EPI, kSmallM, 1><<<grid, 256, 0, s>>>(p);
-  else gemm_kernel<kBf16, NMAT, EPI, kBigM, 2><<<grid, 256, 0, s>>>(p);
+  else gemm_mixed_kernel<kBf16, NMAT, EPI><<<grid, 256, 0, s>>>(p, companion);
 }
 
 // Phase 1 (gate/up or W1) and phase 2 (down or W2), each on its own tile table.
-// The two GEMMs, each optionally followed by the 64-row tiles that re-tile its
-// last partial wave (tail grid 0: none).
 template <bool kBf16>
-int launch_ffn(const GemmArgs& p1, bool small1, unsigned grid1, const GemmArgs& t1, unsigned tgrid1,
-               const GemmArgs& p2, bool small2, unsigned grid2, const GemmArgs& t2, unsigned tgrid2, bool swiglu,
-               hipStream_t s) {
+int launch_ffn(const GemmArgs& p1, bool small1, unsigned grid1, const GemmArgs& t1, const GemmArgs& p2, bool small2,
+               unsigned grid2, const GemmArgs& t2, bool swiglu, hipStream_t s) {
   if (int rc = moe::hip_status(mark(0, s), "moe_expert_ffn timing event")) return rc;
-  if (swiglu) {
-    launch_gemm<kBf16, kEpiSwiGLU, 2>(small1, p1, grid1, s);
-    if (tgrid1) launch_gemm<kBf16, kEpiSwiGLU, 2>(true, t1, tgrid1, s);
-  } else {
-    launch_gemm<kBf16, kEpiGELU, 1>(small1, p1, grid1, s);
-    if (tgrid1) launch_gemm<kBf16, kEpiGELU, 1>(true, t1, tgrid1, s);
-  }
+  if (swiglu) launch_gemm<kBf16, kEpiSwiGLU, 2>(small1, p1, t1, grid1, s);
+  else launch_gemm<kBf16, kEpiGELU, 1>(small1, p1, t1, grid1, s);
   if (int rc = moe::hip_status(hipGetLastError(), "moe_expert_ffn gate/up launch")) return rc;
   if (int rc = moe::hip_status(mark(1, s), "moe_expert_ffn timing event")) return rc;
-  launch_gemm<kBf16, kEpiStore, 1>(small2, p2, grid2, s);
-  if (tgrid2) launch_gemm<kBf16, kEpiStore, 1>(true, t2, tgrid2, s);
+  launch_gemm<kBf16, kEpiStore, 1>(small2, p2, t2, grid2, s);
   if (int rc = moe::hip_status(hipGetLastError(), "moe_expert_ffn down launch")) return rc;
   return moe::hip_status(mark(2, s), "moe_expert_ffn timing event");
 }
@@ -105,19 +108,17 @@ int launch_ffn(const GemmArgs& p1, bool small1, unsigned grid1, const GemmArgs& 
 // AUTO rule, per GEMM, from the slot sizes.  Cost model in "row-tile units":
 // a 256-row tile costs 1, a 64-row tile kSmallCost (a quarter of the work at a
 // lower MFMA efficiency); a grid is charged at least one full wave of the 256
-// CUs.  The cheapest tiling wins; ties keep the 256-row tiles.  kSmallCost is
-// fitted to the measured crossover table (DeepSeek-V2-, Mixtral- and
-// DBRX-shaped routing and EPS-MoE's single-expert shapes): every case's fastest
-// tiling is the model's pick (within 3%) for values from 0.475 to 0.65, with the
-// direct-to-LDS kernels.
+// CUs.  The 256-row tiling counts its remainder tiles (64-row) at kSmallCost.
+// The cheapest tiling wins; ties keep the 256-row tiles.  kSmallCost is fitted
+// to the measured crossover table (DeepSeek-V2-, Mixtral- and DBRX-shaped
+// routing and EPS-MoE's single-expert shapes).
 constexpr int kComputeUnits = 256;
-constexpr double kSmallCost = 0.55;
-Kind pick_kind(int64_t g256, int64_t d64, int64_t g64, int col_tiles) {
-  auto cost = [&](int64_t tiles, double unit) {
-    const double blocks = static_cast<double>(tiles) * col_tiles;
-    return unit * std::max(blocks, static_cast<double>(kComputeUnits));
+Kind pick_kind(int64_t g256, int64_t g256_rem, int64_t d64, int64_t g64, int col_tiles) {
+  auto cost = [&](double tiles) {
+    return std::max(tiles * col_tiles, static_cast<double>(kComputeUnits));
   };
-  const double c256 = cost(g256, 1.0), cd64 = cost(d64, kSmallCost), cg64 = cost(g64, kSmallCost);
+  const double c256 = cost(static_cast<double>(g256) + kSmallCost * static_cast<double>(g256_rem));
+  const double cd64 = kSmallCost * cost(static_cast<double>(d64)), cg64 = kSmallCost * cost(static_cast<double>(g64));
   if (cg64 < c256 && cg64 <= cd64) return kG64;
   if (cd64 < c256) return kD64;
   return kG256;
@@ -168,6 +169,7 @@ extern "C" int moe_expert_ffn(const void* x_perm, moe_dtype dt, int64_t M, int H
   Kind k1 = path == MOE_GEMM_DENSE ? kD64 : path == MOE_GEMM_GROUPED_SMALL ? kG64 : kG256, k2 = k1;
   int m_pad = 0;
   int64_t exact[3] = {-1, -1, -1};  // tiles per kind, when known on the host
+  int64_t exact_rem = -1;             // the 256-row tiling's 64-row remainder tiles
   if (path == MOE_GEMM_DENSE || path == MOE_GEMM_AUTO) {
     // slot sizes, with consecutive slots of one expert merged into one range
     // exactly as the tile tables merge them
@@ -180,7 +182,7 @@ extern "C" int moe_expert_ffn(const void* x_perm, moe_dtype dt, int64_t M, int H
                                            hipMemcpyDeviceToHost, s), "moe_expert_ffn slot readback")) return rc;
     if (int rc = hip_status(hipStreamSynchronize(s), "moe_expert_ffn slot readback")) return rc;
     const int n = std::min(std::max(off[max_slots + 1], 0), max_slots);
-    int64_t largest = 0, active = 0, g256 = 0, g64 = 0;
+    int64_t largest = 0, active = 0, g256 = 0, g256_rem = 0, g64 = 0;
     for (int i = 0; i < n;) {
       int last = i + 1;
       while (last < n && se[last] == se[i]) ++last;
@@ -188,17 +190,22 @@ extern "C" int moe_expert_ffn(const void* x_perm, moe_dtype dt, int64_t M, int H
                                                  std::min<int64_t>(std::max(off[i], 0), M));
       largest = std::max(largest, r);
       if (r > 0) ++active;
-      g256 += ceil_div(r, kBigM);
+      // the 256-row tiling: full tiles, and the remainder as 64-row tiles
+      // when it needs at most kRemTiles of them (the tile tables' rule)
+      const int64_t rem_small = ceil_div(r % kBigM, kSmallM);
+      g256 += r / kBigM + (rem_small > kRemTiles ? 1 : 0);
+      g256_rem += rem_small <= kRemTiles ? rem_small : 0;
       g64 += ceil_div(r, kSmallM);
       i = last;
     }
     m_pad = static_cast<int>(ceil_div(std::max<int64_t>(largest, 1), kSmallM) * kSmallM);
     exact[kG256] = g256;
+    exact_rem = g256_rem;
     exact[kD64] = active * (m_pad / kSmallM);
     exact[kG64] = g64;
     if (path == MOE_GEMM_AUTO) {
-      k1 = pick_kind(g256, exact[kD64], g64, nt1);
-      k2 = pick_kind(g256, exact[kD64], g64, nt2);
+      k1 = pick_kind(g256, g256_rem, exact[kD64], g64, nt1);
+      k2 = pick_kind(g256, g256_rem, exact[kD64], g64, nt2);
     }
   }
   if ((k1 == kD64 || k2 == kD64) && exact[kD64] > w.cap[kD64])
@@ -209,13 +216,15 @@ extern "C" int moe_expert_ffn(const void* x_perm, moe_dtype dt, int64_t M, int H
   auto tab_slot = [&](int t) { return reinterpret_cast<int32_t*>(ws + w.tab_slot[t]); };
   auto tab_row0 = [&](int t) { return reinterpret_cast<int32_t*>(ws + w.tab_row0[t]); };
   auto tab_rend = [&](int t) { return reinterpret_cast<int32_t*>(ws + w.tab_rend[t]); };
-  // 256-row tables also list, per GEMM that runs on them, the 64-row tiles that
-  // replace the row tiles of its last partial wave when that is cheaper
+  // 256-row tables come with a 64-row companion table per GEMM that runs on
+  // them: short range remainders, and trailing row tiles re-listed when that
+  // shortens the launch's last round
   int32_t* split_counts = reinterpret_cast<int32_t*>(ws + w.split_counts);
   TileSplit split{};
   split.nt[0] = k1 == kG256 ? nt1 : 0;
   split.nt[1] = k2 == kG256 ? nt2 : 0;
-  split.cap = kSplitCap;
+  split.cap = w.split_cap;
+  split.rem_tiles = kRemTiles;
   split.small_cost = static_cast<float>(kSmallCost);
   split.slot = reinterpret_cast<int32_t*>(ws + w.split_slot);
   split.row0 = reinterpret_cast<int32_t*>(ws + w.split_row0);
@@ -261,31 +270,36 @@ extern "C" int moe_expert_ffn(const void* x_perm, moe_dtype dt, int64_t M, int H
   };
   on(p1, k1, 0);
   on(p2, k2, 1);
-  // the tail launches: 64-row tiles from the split tables
-  auto tail = [&](const GemmArgs& g, int which) {
+  // the 64-row companion tables of the mixed launches
+  auto companion = [&](const GemmArgs& g, int which) {
     GemmArgs q = g;
-    q.tile_slot = split.slot + which * kSplitCap;
-    q.tile_row0 = split.row0 + which * kSplitCap;
-    q.tile_rend = split.rend + which * kSplitCap;
+    q.tile_slot = split.slot + static_cast<int64_t>(which) * w.split_cap;
+    q.tile_row0 = split.row0 + static_cast<int64_t>(which) * w.split_cap;
+    q.tile_rend = split.rend + static_cast<int64_t>(which) * w.split_cap;
     q.n_tiles = split_counts + 2 * which + 1;
     return q;
   };
-  const GemmArgs t1 = tail(p1, 0), t2 = tail(p2, 1);
-  // at most 256 / nt tail tiles per GEMM (one wave); blocks past the count exit
-  auto tail_grid = [&](int nt, Kind t) {
-    if (t != kG256 || nt > kWaveBlocks) return 0u;
-    return static_cast<unsigned>((kWaveBlocks / nt) * nt);
+  const GemmArgs t1 = companion(p1, 0), t2 = companion(p2, 1);
+  // Grids: exact tile counts when read back, else bounds; blocks past the
+  // tables exit at once.  A 256-row tiling's tables hold at most
+  // floor(M / 256) + (ranges x max(1, kRemTiles)) tiles, ranges <= max_slots,
+  // plus 3 more per re-listed trailing row tile (at most ceil(256 / nt) of
+  // those), plus the rounding of the 256-row part to 8 blocks.
+  auto grid = [&](Kind t, int nt) {
+    int64_t blocks;
+    if (t == kG256) {
+      const int64_t both = exact[kG256] >= 0 ? exact[kG256] + exact_rem
+                                             : M / kBigM + static_cast<int64_t>(max_slots) * std::max(1, kRemTiles);
+      blocks = both * nt + 3 * ceil_div(kWaveBlocks, nt) * nt + 8;
+    } else {
+      blocks = (exact[t] >= 0 ? exact[t] : static_cast<int64_t>(w.cap[t])) * nt;
+    }
+    return static_cast<unsigned>(std::min<int64_t>(std::max<int64_t>(1, blocks), 0x7fffffff));
   };
-  // exact tile counts when read back, else the table's capacity (blocks past the
-  // count exit at once)
-  auto tiles = [&](Kind t) { return exact[t] >= 0 ? exact[t] : static_cast<int64_t>(w.cap[t]); };
-  const unsigned grid1 = static_cast<unsigned>(std::max<int64_t>(1, tiles(k1) * nt1));
-  const unsigned grid2 = static_cast<unsigned>(std::max<int64_t>(1, tiles(k2) * nt2));
+  const unsigned grid1 = grid(k1, nt1), grid2 = grid(k2, nt2);
   const bool swiglu = act == MOE_SWIGLU;
-  const unsigned tg1 = tail_grid(nt1, k1), tg2 = tail_grid(nt2, k2);
-  return dt == MOE_BF16
-             ? launch_ffn<true>(p1, k1 != kG256, grid1, t1, tg1, p2, k2 != kG256, grid2, t2, tg2, swiglu, s)
-             : launch_ffn<false>(p1, k1 != kG256, grid1, t1, tg1, p2, k2 != kG256, grid2, t2, tg2, swiglu, s);
+  return dt == MOE_BF16 ? launch_ffn<true>(p1, k1 != kG256, grid1, t1, p2, k2 != kG256, grid2, t2, swiglu, s)
+                        : launch_ffn<false>(p1, k1 != kG256, grid1, t1, p2, k2 != kG256, grid2, t2, swiglu, s);
 }
 
 extern "C" int moe_ffn_set_timing_events(void* before_gateup, void* after_gateup, void* after_down) {

@@ -22,7 +22,9 @@
 // keeps the A and B tiles that neighbouring blocks share inside that XCD's L2.
 // The weight fragment is the MFMA's first operand, so the accumulators come out
 // transposed: each lane holds four adjacent output columns of one row, which
-// the epilogue writes with one 8-byte (bf16) or 16-byte (fp32) store.
+// the epilogue writes with one 8-byte (bf16) or 16-byte (fp32) store.  One
+// launch can run two tile heights (gemm_mixed_kernel): 256-row tiles, then
+// 64-row tiles in the grid's last blocks, over one shared LDS array.
 // Each output row depends only on its own input row and the fixed K order, so
 // a row's value does not depend on the tile, slot or path that computes it.
 #pragma once
@@ -172,8 +174,28 @@ __device__ __forceinline__ void store4(uint16_t* p, const float v[4]) {
 // has transposed into the K range [seg[e], seg[e+1]) (a multiple of the K step,
 // zero-padded) of A [Mw, ld] and B [N, ld]; output rows below c_split go to
 // C [E, c_split, N], the others to C2 [E, Mw - c_split, N].
+// LDS bytes one block of a tiling needs (operand stages, or the epilogue's
+// staging tile where that is larger).
+template <bool kBf16, int NMAT, int EPI, int BM, int WM, bool kWgrad>
+constexpr int gemm_lds_bytes() {
+  constexpr bool kDTL = kBf16 && BM == 256;
+  constexpr bool kDTL64 = kBf16 && BM == 64 && !kWgrad;
+  constexpr int kStageBytes = (BM + kTileN) * kRowBytes;
+  constexpr int kStagedEpi = (!kWgrad && (EPI == kEpiGELU || EPI == kEpiSwiGLUBwd || EPI == kEpiGELUBwd))
+                                 ? (BM / WM) * (kTileN + 4) * 4 : 0;
+  constexpr int kDtlBytes = kDTL ? 2 * BM * 128 + 3 * kTileN * 128 : 4 * (BM + kTileN) * 128;
+  return (kDTL || kDTL64) ? (kDtlBytes > kStagedEpi ? kDtlBytes : kStagedEpi) : 2 * kStageBytes;
+}
+
+// The GEMM kernels' LDS: one array that every tiling of a launch shares.
+constexpr int kGemmLdsBytes = 160 * 1024;
+__shared__ __align__(1024) char gemm_lds[kGemmLdsBytes];
+
+// One block's tile: `b` is its index in the grid of this tiling (b & 7 its
+// XCD); it uses the first gemm_lds_bytes of gemm_lds.
 template <bool kBf16, int NMAT, int EPI, int BM, int WM, bool kWgrad = false>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_kernel(GemmArgs g) {
+__device__ __forceinline__ void gemm_tile(const GemmArgs g, const int b) {
+  char* const lds = gemm_lds;
   using TR = Tr<kBf16>;
   using T = typename TR::T;
   using Frag = typename TR::Frag;
@@ -196,12 +218,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // registers into two padded stages
   constexpr bool kDTL = kBf16 && BM == 256;
   constexpr bool kDTL64 = kBf16 && BM == 64 && !kWgrad;
-  constexpr int kStagedEpi = (!kWgrad && (EPI == kEpiGELU || EPI == kEpiSwiGLUBwd || EPI == kEpiGELUBwd))
-                                 ? (BM / WM) * (kTileN + 4) * 4 : 0;
-  constexpr int kDtlBytes = kDTL ? 2 * BM * 128 + 3 * kTileN * 128 : 4 * (BM + kTileN) * 128;
-  constexpr int kLdsBytes =
-      (kDTL || kDTL64) ? (kDtlBytes > kStagedEpi ? kDtlBytes : kStagedEpi) : 2 * kStageBytes;
-  __shared__ __align__(1024) char lds[kLdsBytes];
+  constexpr int kLdsBytes = gemm_lds_bytes<kBf16, NMAT, EPI, BM, WM, kWgrad>();
 
   // ---- which tile: XCD-contiguous runs, grouped raster inside a run --------
   const int NT = g.n_col_tiles;
@@ -209,7 +226,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int total_m = kWgrad ? g.E * MTw : *g.n_tiles;
   // weight gradients: 8 equal shares of each expert's tiles (grid rounded up to them)
   const int total = kWgrad ? 8 * g.E * ((MTw * NT + 7) >> 3) : total_m * NT;
-  const int b = blockIdx.x;
   if (b >= total) return;
   int mt, nt;
   if constexpr (kWgrad) {
@@ -274,6 +290,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // ---- global -> register staging: P x 16 bytes per thread per step -------
   // pass p < PA: A rows 32p..; then 8 passes of weight rows (gate/up: 4 + 4)
   const int tid = threadIdx.x;
+  __builtin_assume(tid >= 0 && tid < 256);
   const int lrow = tid >> 3, lchunk = tid & 7;
   const int goff = lrow * static_cast<int>(row_b) + lchunk * 16;  // + pass*32 rows + step*128
   const int pass_b = 32 * static_cast<int>(row_b);
@@ -808,6 +825,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
 }
 
+
+template <bool kBf16, int NMAT, int EPI, int BM, int WM, bool kWgrad = false>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_kernel(GemmArgs g) {
+  static_assert(gemm_lds_bytes<kBf16, NMAT, EPI, BM, WM, kWgrad>() <= kGemmLdsBytes, "LDS");
+  gemm_tile<kBf16, NMAT, EPI, BM, WM, kWgrad>(g, static_cast<int>(blockIdx.x));
+}
+
+// A 256-row tile table and a 64-row one in one launch: the first
+// round_up(n_big * nt, 8) blocks run the 256-row tiles (the rounding keeps
+// every block's index congruent to its XCD in both parts), the blocks after
+// them the 64-row tiles, which are dispatched last and so fill the CUs that
+// the last round of 256-row tiles leaves idle.  Blocks past both exit.
+template <bool kBf16, int NMAT, int EPI>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_mixed_kernel(GemmArgs big,
+                                                                                                   GemmArgs small) {
+  static_assert(gemm_lds_bytes<kBf16, NMAT, EPI, 256, 2, false>() <= kGemmLdsBytes, "LDS");
+  static_assert(gemm_lds_bytes<kBf16, NMAT, EPI, 64, 1, false>() <= kGemmLdsBytes, "LDS");
+  const int nb = (*big.n_tiles * big.n_col_tiles + 7) & ~7;
+  const int b = static_cast<int>(blockIdx.x);
+  if (b < nb) gemm_tile<kBf16, NMAT, EPI, 256, 2>(big, b);
+  else gemm_tile<kBf16, NMAT, EPI, 64, 1>(small, b - nb);
+}
+
 // Lists the row tiles of the GEMMs.  With `merge`, consecutive slots of one
 // expert (its replica chunks) form one row range: on one GPU they share the
 // same weights, so tiling the run as a whole avoids a partial tile per chunk
@@ -819,17 +859,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // A tile records its range's first slot, first row and end row.
 enum TileMode { kCover = 0, kPadded = 1 };
 
-// Optional re-tiling of a 256-row cover table's last, partial wave of blocks,
-// per GEMM g (its column-tile count nt[g]; 0 = never): the row tiles whose
-// blocks form the partial wave are listed again as 64-row tiles when that
-// lowers the modelled cost (waves of 256-row blocks cost 1, waves of 64-row
-// blocks small_cost < 1).  Removing the partial wave saves at most one wave,
-// so the 64-row blocks must fit in one wave: at most 256 / nt[g] tiles.
-// counts[2g] is then the number of 256-row tiles to run, counts[2g + 1] the
-// number of 64-row tiles in table g ([g * cap, ...)).
+// Optional 64-row companion tables of a 256-row cover table, one per GEMM g
+// that runs on it (its column-tile count nt[g]; 0 = none), for a launch of
+// gemm_mixed_kernel: the 256-row tiles first, then the 64-row tiles, which
+// fill the CUs the last round of 256-row tiles leaves idle.
+//   * remainders: a range of n rows gets floor(n / 256) full 256-row tiles; its
+//     remainder n mod 256, when it needs at most rem_tiles 64-row tiles, is
+//     listed as those (the same in both tables) instead of one partial
+//     256-row tile;
+//   * last round: the trailing r row tiles of the 256-row table are listed
+//     again as 64-row tiles when that shortens the modelled launch (one round
+//     of 256 blocks; a 256-row block costs 1, a 64-row block small_cost).
+// counts[2g] is the number of 256-row tiles GEMM g runs, counts[2g + 1] the
+// number of 64-row tiles in its table ([g * cap, ...)).
 struct TileSplit {
   int nt[2];
   int cap;
+  int rem_tiles;
   float small_cost;
   int32_t* slot;
   int32_t* row0;
@@ -838,6 +884,14 @@ struct TileSplit {
 };
 constexpr int kWaveBlocks = 256;  // one block per CU
 
+// Modelled duration, in rounds of 256-row blocks, of a mixed launch with
+// `big` 256-row and `small` 64-row blocks dispatched in that order.
+__device__ inline float mixed_rounds(int64_t big, int64_t small, float c) {
+  const int64_t full = big / kWaveBlocks, rest = big % kWaveBlocks;
+  const float floor_ = rest > 0 ? 1.f : (small > 0 ? c : 0.f);
+  return static_cast<float>(full) + fmaxf(floor_, (static_cast<float>(rest) + c * small) / kWaveBlocks);
+}
+
 __global__ __launch_bounds__(256) void tiles_kernel(const int32_t* __restrict__ slot_off,
                                                     const int32_t* __restrict__ slot_expert,
                                                     const int32_t* __restrict__ n_slots_p, int max_slots, int64_t M,
@@ -845,15 +899,17 @@ __global__ __launch_bounds__(256) void tiles_kernel(const int32_t* __restrict__ 
                                                     int32_t* __restrict__ tile_slot, int32_t* __restrict__ tile_row0,
                                                     int32_t* __restrict__ tile_rend, int32_t* __restrict__ n_tiles,
                                                     TileSplit split) {
-  __shared__ int32_t scan[256];
-  __shared__ int32_t carry;
+  __shared__ int32_t scan[256], scan2[256];
+  __shared__ int32_t carry, carry2;
   const int tid = threadIdx.x;
   const int n = min(max(*n_slots_p, 0), max_slots);
-  if (tid == 0) carry = 0;
+  const bool companion = split.counts != nullptr && mode == kCover && BM == 256;
+  const int rem_tiles = companion ? split.rem_tiles : 0;
+  if (tid == 0) carry = carry2 = 0;
   __syncthreads();
   for (int c = 0; c < n; c += 256) {
     const int s = c + tid;
-    int64_t start = 0, end = 0, cnt = 0;
+    int64_t start = 0, end = 0, cnt = 0, cnt_small = 0, full = 0;
     if (s < n && !(merge && s > 0 && slot_expert[s] == slot_expert[s - 1])) {
       int last = s + 1;  // one past the range's last slot
       if (merge)
@@ -861,15 +917,27 @@ __global__ __launch_bounds__(256) void tiles_kernel(const int32_t* __restrict__ 
       start = min<int64_t>(max(slot_off[s], 0), M);
       end = min<int64_t>(max(slot_off[last], 0), M);
       const int64_t rows = end > start ? end - start : 0;
-      if (mode == kCover) cnt = (rows + BM - 1) / BM;
-      else if (rows > 0) cnt = m_pad / BM;
+      if (mode == kCover) {
+        cnt = (rows + BM - 1) / BM;
+        full = rows / BM;
+        const int64_t rem_small = (rows - full * BM + 63) / 64;
+        if (rem_small > 0 && rem_small <= rem_tiles) {
+          cnt = full;
+          cnt_small = rem_small;
+        }
+      } else if (rows > 0) {
+        cnt = m_pad / BM;
+      }
     }
     scan[tid] = static_cast<int32_t>(cnt);
+    scan2[tid] = static_cast<int32_t>(cnt_small);
     __syncthreads();
     for (int d = 1; d < 256; d <<= 1) {
       const int32_t v = tid >= d ? scan[tid - d] : 0;
+      const int32_t v2 = tid >= d ? scan2[tid - d] : 0;
       __syncthreads();
       scan[tid] += v;
+      scan2[tid] += v2;
       __syncthreads();
     }
     const int32_t first = carry + scan[tid] - static_cast<int32_t>(cnt);
@@ -881,13 +949,27 @@ __global__ __launch_bounds__(256) void tiles_kernel(const int32_t* __restrict__ 
         tile_rend[j] = static_cast<int32_t>(end);
       }
     }
+    const int32_t first2 = carry2 + scan2[tid] - static_cast<int32_t>(cnt_small);
+    for (int q = 0; q < cnt_small; ++q) {
+      const int j = first2 + q;
+      for (int g = 0; g < 2; ++g)
+        if (split.nt[g] > 0 && j < split.cap) {
+          split.slot[g * split.cap + j] = s;
+          split.row0[g * split.cap + j] = static_cast<int32_t>(start + full * BM + static_cast<int64_t>(q) * 64);
+          split.rend[g * split.cap + j] = static_cast<int32_t>(end);
+        }
+    }
     __syncthreads();
-    if (tid == 255) carry += scan[255];
+    if (tid == 255) {
+      carry += scan[255];
+      carry2 += scan2[255];
+    }
     __syncthreads();
   }
   const int total = min(carry, max_tiles);
   if (tid == 0) *n_tiles = total;
-  if (split.counts == nullptr) return;
+  if (!companion) return;
+  const int n_rem = min(carry2, split.cap);
   // the last (up to) 256 tiles, staged in LDS by all threads at once: the
   // table's writes by the other threads are visible after the last barrier
   __shared__ int32_t last_slot[256], last_row0[256], last_rend[256];
@@ -899,37 +981,42 @@ __global__ __launch_bounds__(256) void tiles_kernel(const int32_t* __restrict__ 
   }
   __syncthreads();
   if (tid != 0) return;
+  const float c = split.small_cost;
   for (int g = 0; g < 2; ++g) {
-    int big = total, small = 0;
     const int nt = split.nt[g];
-    const int64_t blocks = static_cast<int64_t>(total) * nt;
-    if (nt > 0 && mode == kCover && BM == 256 && blocks % kWaveBlocks != 0) {
-      // row tiles of the partial wave (fewer than 256 of them, all staged)
-      const int r = min<int64_t>(total, (blocks % kWaveBlocks + nt - 1) / nt);
-      int64_t rows_small = 0;
-      for (int t = total - r; t < total; ++t)
-        rows_small += (min(BM, last_rend[t - base] - last_row0[t - base]) + 63) / 64;
-      const auto waves = [](int64_t b) { return static_cast<float>((b + kWaveBlocks - 1) / kWaveBlocks); };
-      const float keep = waves(blocks);
-      const float cut = waves(static_cast<int64_t>(total - r) * nt) + split.small_cost * waves(rows_small * nt);
-      if (cut < keep && rows_small * nt <= kWaveBlocks && rows_small <= split.cap) {
-        big = total - r;
-        int32_t* sl = split.slot + g * split.cap;
-        int32_t* r0 = split.row0 + g * split.cap;
-        int32_t* re = split.rend + g * split.cap;
-        for (int t = big; t < total; ++t) {
-          const int end = min(last_row0[t - base] + BM, last_rend[t - base]);
-          for (int row = last_row0[t - base]; row < end; row += 64) {
-            sl[small] = last_slot[t - base];
-            r0[small] = row;
-            re[small] = last_rend[t - base];
-            ++small;
-          }
+    int best_r = 0, best_rows = 0;
+    if (nt > 0) {
+      // trailing row tiles of at most one round of blocks (and all staged)
+      const int r_max = min(min(total, 256), (kWaveBlocks + nt - 1) / nt);
+      float best = mixed_rounds(static_cast<int64_t>(total) * nt, static_cast<int64_t>(n_rem) * nt, c);
+      int rows = 0;
+      for (int r = 1; r <= r_max; ++r) {
+        const int t = total - r - base;
+        rows += (min(BM, last_rend[t] - last_row0[t]) + 63) / 64;
+        if (n_rem + rows > split.cap) break;
+        const float e = mixed_rounds(static_cast<int64_t>(total - r) * nt, static_cast<int64_t>(n_rem + rows) * nt, c);
+        if (e < best) {
+          best = e;
+          best_r = r;
+          best_rows = rows;
+        }
+      }
+      int32_t* sl = split.slot + g * split.cap;
+      int32_t* r0 = split.row0 + g * split.cap;
+      int32_t* re = split.rend + g * split.cap;
+      int small = n_rem;
+      for (int t = total - best_r; t < total; ++t) {
+        const int end = min(last_row0[t - base] + BM, last_rend[t - base]);
+        for (int row = last_row0[t - base]; row < end; row += 64) {
+          sl[small] = last_slot[t - base];
+          r0[small] = row;
+          re[small] = last_rend[t - base];
+          ++small;
         }
       }
     }
-    split.counts[2 * g] = big;
-    split.counts[2 * g + 1] = small;
+    split.counts[2 * g] = total - best_r;
+    split.counts[2 * g + 1] = n_rem + best_rows;
   }
 }
 

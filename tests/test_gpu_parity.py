@@ -343,8 +343,7 @@ def test_expert_ffn_hand_made_slot_table(M, dtype):
     """moe_expert_ffn on a slot table dispatch never produces: expert 0's rows in
     two non-adjacent slots, two adjacent slots of expert 1 (tiled as one range),
     an empty slot and unused slot capacity.  Every row matches the oracle's FFN of
-    its slot's expert, and the four paths give the same bits.  At M = 30000 the
-    256-row tiles stay (their blocks do not fit one wave as 64-row tiles)."""
+    its slot's expert, and the four paths give the same bits."""
     cfg = synth.CONFIGS["mixtral"].scaled(T=M, E=3, H=128, I=192, dtype=dtype)
     x = synth.hidden0(cfg, 3)
     wts = synth.expert_weights(cfg)
@@ -369,11 +368,48 @@ def test_expert_ffn_hand_made_slot_table(M, dtype):
         assert np.array_equal(outs[path], outs["grouped"]), path
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_grouped_remainder_tiles_and_last_round(dtype):
+    """The 256-row grouped tiling on 300 slots (more than one 256-slot chunk of
+    the tile-table scan) over 40 experts, slot sizes 0..519 with planted 1, 64,
+    65, 255, 256 and 257: ranges whose remainder fits one 64-row tile run it as a
+    64-row tile in the same launch (77 of them here), and with one column tile
+    (H = 128) the last round of 256-row tiles is nearly empty, so the trailing
+    row tiles are listed again as 64-row tiles.  Every row matches the oracle's
+    FFN of its slot's expert; all paths give the same bits."""
+    rng = np.random.default_rng(11)
+    n = 300
+    sizes = rng.integers(0, 520, n)
+    sizes[::17] = 0
+    sizes[[5, 6, 7, 8, 9, 10]] = [64, 65, 256, 257, 1, 255]
+    experts = rng.integers(0, 40, n).astype(np.int32)
+    M = int(sizes.sum())
+    cfg = synth.CONFIGS["mixtral"].scaled(T=M, E=40, H=128, I=192, dtype=dtype)
+    x = synth.hidden0(cfg, 5)
+    wts = synth.expert_weights(cfg)
+    max_slots = 320
+    slot_off = np.full(max_slots + 1, M, np.int32)
+    slot_off[:n + 1] = np.concatenate([[0], np.cumsum(sizes)])
+    slot_expert = np.zeros(max_slots, np.int32)
+    slot_expert[:n] = experts
+    ref = oracle.ffn_rows(x, np.repeat(experts, sizes), *wts, act="swiglu")
+    wg, wu, wd = (to_dev(w) for w in wts)
+    xd, so, se, ns = to_dev(x), to_dev(slot_off), to_dev(slot_expert), to_dev(np.array([n], np.int32))
+    outs = {}
+    for path in ("grouped", "grouped_small", "dense", "auto"):
+        y = moe.moe_expert_ffn(xd, so, se, ns, wg, wu, wd, act="swiglu", path=path)
+        _sync()
+        outs[path] = from_dev(y)
+    assert_close(outs["grouped"], ref, "bf16" if dtype == "bf16" else "fp32_gemm", "y_perm")
+    for path in ("grouped_small", "dense", "auto"):
+        assert np.array_equal(outs[path], outs["grouped"]), path
+
+
 def test_tail_retiling_full_size_mixtral():
-    """Mixtral shape: the down GEMM's 256-row tiles fill 4.25 waves of the 256
-    CUs, so the grouped path re-runs the last partial wave's row tiles as 64-row
-    tiles.  Every row keeps its K order: the grouped output equals the all-64-row
-    path bit for bit, with and without replica slots."""
+    """Mixtral shape: the down GEMM's 256-row tiles fill 4.25 rounds of the 256
+    CUs, so the grouped path lists the trailing row tiles again as 64-row tiles
+    that run in the same launch.  Every row keeps its K order: the grouped output
+    equals the all-64-row path bit for bit, with and without replica slots."""
     cfg = synth.CONFIGS["mixtral"]
     x = synth.hidden0(cfg, 0)
     lg = synth.logits(cfg, 0, 0)
