@@ -233,9 +233,9 @@ int moe_dispatch(const void* x, moe_dtype dt, int64_t T, int H, const int32_t* t
  * or path computes it (fixed reduction order, no split-K), so replicated and
  * non-replicated dispatches give bit-identical y_perm.
  *   path  GROUPED: 256-row tiles cover each slot's rows exactly (no host
- *                  sync): the large-batch form.  A remainder of at most 64
- *                  rows (after the full 256-row tiles) runs as one 64-row tile
- *                  in the same launch, after the 256-row tiles.
+ *                  sync): the large-batch form.  A slot range of at most 64
+ *                  rows runs as one 64-row tile in the same launch, after the
+ *                  256-row tiles.
  *         GROUPED_SMALL: 64-row tiles cover each slot's rows exactly (no
  *                  host sync): less padding when slots hold few rows.
  *         DENSE:   every slot with rows is padded to the largest slot's row

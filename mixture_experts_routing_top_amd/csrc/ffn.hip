@@ -9,8 +9,8 @@
 //
 // A tile-table pass, then two launches of the tiled MFMA kernel of gemm.h:
 //   tiles:   lists the row tiles of a GEMM: 256-row tiles covering each slot
-//            (GROUPED; a short remainder and, when the launch's last round
-//            would be mostly idle, the trailing row tiles go to a 64-row
+//            (GROUPED; a range of <= 64 rows and, when the launch's last
+//            round would be mostly idle, the trailing row tiles go to a 64-row
 //            companion table run by the same launch), 64-row tiles covering
 //            each slot (GROUPED_SMALL), or every active slot padded to the
 //            largest (DENSE); AUTO reads the slot sizes back and picks per
@@ -40,8 +40,8 @@ struct WsLayout {
 };
 
 // AUTO's cost of a 64-row tile in 256-row tiles (see pick_kind), and the most
-// 64-row tiles a range's remainder may take in a 256-row tiling: while they
-// cost less than one 256-row tile (1 at 0.55, i.e. remainders of <= 64 rows).
+// 64-row tiles a short range may take in a 256-row tiling: while they cost
+// less than one 256-row tile (1 at 0.55, i.e. ranges of <= 64 rows).
 constexpr double kSmallCost = 0.55;
 constexpr int kRemTiles = kSmallCost >= 0.5 ? 1 : kSmallCost >= 1.0 / 3 ? 2 : 3;
 // 64-row tiles re-listing a 256-row table's trailing row tiles: at most
@@ -108,7 +108,7 @@ int launch_ffn(const GemmArgs& p1, bool small1, unsigned grid1, const GemmArgs& 
 // AUTO rule, per GEMM, from the slot sizes.  Cost model in "row-tile units":
 // a 256-row tile costs 1, a 64-row tile kSmallCost (a quarter of the work at a
 // lower MFMA efficiency); a grid is charged at least one full wave of the 256
-// CUs.  The 256-row tiling counts its remainder tiles (64-row) at kSmallCost.
+// CUs.  The 256-row tiling counts its short-range tiles (64-row) at kSmallCost.
 // The cheapest tiling wins; ties keep the 256-row tiles.  kSmallCost is fitted
 // to the measured crossover table (DeepSeek-V2-, Mixtral- and DBRX-shaped
 // routing and EPS-MoE's single-expert shapes).
@@ -169,7 +169,7 @@ extern "C" int moe_expert_ffn(const void* x_perm, moe_dtype dt, int64_t M, int H
   Kind k1 = path == MOE_GEMM_DENSE ? kD64 : path == MOE_GEMM_GROUPED_SMALL ? kG64 : kG256, k2 = k1;
   int m_pad = 0;
   int64_t exact[3] = {-1, -1, -1};  // tiles per kind, when known on the host
-  int64_t exact_rem = -1;             // the 256-row tiling's 64-row remainder tiles
+  int64_t exact_rem = -1;             // the 256-row tiling's 64-row short-range tiles
   if (path == MOE_GEMM_DENSE || path == MOE_GEMM_AUTO) {
     // slot sizes, with consecutive slots of one expert merged into one range
     // exactly as the tile tables merge them
@@ -190,11 +190,11 @@ extern "C" int moe_expert_ffn(const void* x_perm, moe_dtype dt, int64_t M, int H
                                                  std::min<int64_t>(std::max(off[i], 0), M));
       largest = std::max(largest, r);
       if (r > 0) ++active;
-      // the 256-row tiling: full tiles, and the remainder as 64-row tiles
-      // when it needs at most kRemTiles of them (the tile tables' rule)
-      const int64_t rem_small = ceil_div(r % kBigM, kSmallM);
-      g256 += r / kBigM + (rem_small > kRemTiles ? 1 : 0);
-      g256_rem += rem_small <= kRemTiles ? rem_small : 0;
+      // the 256-row tiling: a range of at most kRemTiles x 64 rows as 64-row
+      // tiles, else 256-row tiles (the tile tables' rule)
+      const bool short_range = r > 0 && r <= static_cast<int64_t>(kRemTiles) * kSmallM;
+      g256 += short_range ? 0 : ceil_div(r, kBigM);
+      g256_rem += short_range ? ceil_div(r, kSmallM) : 0;
       g64 += ceil_div(r, kSmallM);
       i = last;
     }
@@ -217,7 +217,7 @@ extern "C" int moe_expert_ffn(const void* x_perm, moe_dtype dt, int64_t M, int H
   auto tab_row0 = [&](int t) { return reinterpret_cast<int32_t*>(ws + w.tab_row0[t]); };
   auto tab_rend = [&](int t) { return reinterpret_cast<int32_t*>(ws + w.tab_rend[t]); };
   // 256-row tables come with a 64-row companion table per GEMM that runs on
-  // them: short range remainders, and trailing row tiles re-listed when that
+  // them: ranges of <= 64 rows, and trailing row tiles re-listed when that
   // shortens the launch's last round
   int32_t* split_counts = reinterpret_cast<int32_t*>(ws + w.split_counts);
   TileSplit split{};

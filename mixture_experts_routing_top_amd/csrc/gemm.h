@@ -863,10 +863,11 @@ enum TileMode { kCover = 0, kPadded = 1 };
 // that runs on it (its column-tile count nt[g]; 0 = none), for a launch of
 // gemm_mixed_kernel: the 256-row tiles first, then the 64-row tiles, which
 // fill the CUs the last round of 256-row tiles leaves idle.
-//   * remainders: a range of n rows gets floor(n / 256) full 256-row tiles; its
-//     remainder n mod 256, when it needs at most rem_tiles 64-row tiles, is
-//     listed as those (the same in both tables) instead of one partial
-//     256-row tile;
+//   * short ranges: a range of at most 64 * rem_tiles rows is listed as
+//     64-row tiles (the same in both tables) instead of one mostly empty
+//     256-row tile.  Longer ranges keep their partial 256-row tile: it runs in
+//     step with the range's other tiles and shares their weight reads in L2,
+//     where a faster 64-row tile would fetch the weights again;
 //   * last round: the trailing r row tiles of the 256-row table are listed
 //     again as 64-row tiles when that shortens the modelled launch (one round
 //     of 256 blocks; a 256-row block costs 1, a 64-row block small_cost).
@@ -909,7 +910,7 @@ __global__ __launch_bounds__(256) void tiles_kernel(const int32_t* __restrict__ 
   __syncthreads();
   for (int c = 0; c < n; c += 256) {
     const int s = c + tid;
-    int64_t start = 0, end = 0, cnt = 0, cnt_small = 0, full = 0;
+    int64_t start = 0, end = 0, cnt = 0, cnt_small = 0;
     if (s < n && !(merge && s > 0 && slot_expert[s] == slot_expert[s - 1])) {
       int last = s + 1;  // one past the range's last slot
       if (merge)
@@ -919,11 +920,9 @@ __global__ __launch_bounds__(256) void tiles_kernel(const int32_t* __restrict__ 
       const int64_t rows = end > start ? end - start : 0;
       if (mode == kCover) {
         cnt = (rows + BM - 1) / BM;
-        full = rows / BM;
-        const int64_t rem_small = (rows - full * BM + 63) / 64;
-        if (rem_small > 0 && rem_small <= rem_tiles) {
-          cnt = full;
-          cnt_small = rem_small;
+        if (rows > 0 && rows <= 64 * rem_tiles) {
+          cnt = 0;
+          cnt_small = (rows + 63) / 64;
         }
       } else if (rows > 0) {
         cnt = m_pad / BM;
@@ -955,7 +954,7 @@ __global__ __launch_bounds__(256) void tiles_kernel(const int32_t* __restrict__ 
       for (int g = 0; g < 2; ++g)
         if (split.nt[g] > 0 && j < split.cap) {
           split.slot[g * split.cap + j] = s;
-          split.row0[g * split.cap + j] = static_cast<int32_t>(start + full * BM + static_cast<int64_t>(q) * 64);
+          split.row0[g * split.cap + j] = static_cast<int32_t>(start + static_cast<int64_t>(q) * 64);
           split.rend[g * split.cap + j] = static_cast<int32_t>(end);
         }
     }

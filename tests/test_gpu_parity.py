@@ -372,11 +372,11 @@ def test_expert_ffn_hand_made_slot_table(M, dtype):
 def test_grouped_remainder_tiles_and_last_round(dtype):
     """The 256-row grouped tiling on 300 slots (more than one 256-slot chunk of
     the tile-table scan) over 40 experts, slot sizes 0..519 with planted 1, 64,
-    65, 255, 256 and 257: ranges whose remainder fits one 64-row tile run it as a
-    64-row tile in the same launch (77 of them here), and with one column tile
-    (H = 128) the last round of 256-row tiles is nearly empty, so the trailing
-    row tiles are listed again as 64-row tiles.  Every row matches the oracle's
-    FFN of its slot's expert; all paths give the same bits."""
+    65, 255, 256 and 257: the 41 ranges of at most 64 rows run as 64-row tiles
+    in the same launch, and both GEMMs (two and one column tiles) list trailing
+    row tiles again as 64-row tiles to fill the launch's last round.  Every row
+    matches the oracle's FFN of its slot's expert; all paths give the same
+    bits."""
     rng = np.random.default_rng(11)
     n = 300
     sizes = rng.integers(0, 520, n)
