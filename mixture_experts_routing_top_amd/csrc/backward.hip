@@ -442,6 +442,16 @@ extern "C" int moe_backward(const void* x_perm, const void* y_perm, moe_dtype dt
   if (static_cast<int64_t>(std::max(H, nI)) * elem_bytes(dt) * 256 >= (int64_t(1) << 31) ||
       L.ld * elem_bytes(dt) * 256 >= (int64_t(1) << 31))
     return fail(MOE_ERR_UNSUPPORTED, "moe_backward: sizes too large for 32-bit tile offsets");
+  {
+    // block and tile indices are 32-bit in the kernels: bound every GEMM grid
+    // (at most 128 output columns per column tile)
+    const int64_t wide = std::max<int64_t>(H, nI);
+    const int64_t max_nt = ceil_div(wide, 128);
+    const int64_t rows_grid = static_cast<int64_t>(L.tiles_cap) * max_nt;
+    const int64_t wgrad_blocks = static_cast<int64_t>(E) * (ceil_div(wide, 256) * max_nt + 8);
+    if (std::max(rows_grid, wgrad_blocks) >= (int64_t(1) << 31) - 256)
+      return fail(MOE_ERR_UNSUPPORTED, "moe_backward: sizes exceed 32-bit grid indexing");
+  }
   if (act == MOE_SWIGLU && !w_up) return fail(MOE_ERR_INVALID_ARG, "moe_backward: SwiGLU needs w_up");
   if (act == MOE_GELU && (w_up || d_w_up)) return fail(MOE_ERR_INVALID_ARG, "moe_backward: GELU takes no w_up/d_w_up");
   if (!expert_off || !w_gate || !w_down || !d_w_gate || !d_w_down || !workspace || (act == MOE_SWIGLU && !d_w_up))

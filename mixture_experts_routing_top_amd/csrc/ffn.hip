@@ -211,6 +211,29 @@ extern "C" int moe_expert_ffn(const void* x_perm, moe_dtype dt, int64_t M, int H
   if ((k1 == kD64 || k2 == kD64) && exact[kD64] > w.cap[kD64])
     return fail(MOE_ERR_WORKSPACE, "moe_expert_ffn: dense path needs %lld tiles", (long long)exact[kD64]);
 
+  // Grids: exact tile counts when read back, else bounds; blocks past the
+  // tables exit at once.  A 256-row tiling's tables hold at most
+  // floor(M / 256) + (ranges x max(1, kRemTiles)) tiles, ranges <= max_slots,
+  // plus 3 more per re-listed trailing row tile (at most ceil(256 / nt) of
+  // those), plus the rounding of the 256-row part to 8 blocks.
+  auto grid = [&](Kind t, int nt) {
+    int64_t blocks;
+    if (t == kG256) {
+      const int64_t both = exact[kG256] >= 0 ? exact[kG256] + exact_rem
+                                             : M / kBigM + static_cast<int64_t>(max_slots) * std::max(1, kRemTiles);
+      blocks = both * nt + 3 * ceil_div(kWaveBlocks, nt) * nt + 8;
+    } else {
+      blocks = (exact[t] >= 0 ? exact[t] : static_cast<int64_t>(w.cap[t])) * nt;
+    }
+    return std::max<int64_t>(1, blocks);
+  };
+  // block and tile indices are 32-bit in the kernels
+  const int64_t blocks1 = grid(k1, nt1), blocks2 = grid(k2, nt2);
+  if (std::max(blocks1, blocks2) >= (int64_t(1) << 31) - kWaveBlocks)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_expert_ffn: %lld blocks exceed 32-bit grid indexing",
+                static_cast<long long>(std::max(blocks1, blocks2)));
+  const unsigned grid1 = static_cast<unsigned>(blocks1), grid2 = static_cast<unsigned>(blocks2);
+
   char* ws = static_cast<char*>(workspace);
   int32_t* n_tiles = reinterpret_cast<int32_t*>(ws + w.n_tiles);
   auto tab_slot = [&](int t) { return reinterpret_cast<int32_t*>(ws + w.tab_slot[t]); };
@@ -280,23 +303,6 @@ extern "C" int moe_expert_ffn(const void* x_perm, moe_dtype dt, int64_t M, int H
     return q;
   };
   const GemmArgs t1 = companion(p1, 0), t2 = companion(p2, 1);
-  // Grids: exact tile counts when read back, else bounds; blocks past the
-  // tables exit at once.  A 256-row tiling's tables hold at most
-  // floor(M / 256) + (ranges x max(1, kRemTiles)) tiles, ranges <= max_slots,
-  // plus 3 more per re-listed trailing row tile (at most ceil(256 / nt) of
-  // those), plus the rounding of the 256-row part to 8 blocks.
-  auto grid = [&](Kind t, int nt) {
-    int64_t blocks;
-    if (t == kG256) {
-      const int64_t both = exact[kG256] >= 0 ? exact[kG256] + exact_rem
-                                             : M / kBigM + static_cast<int64_t>(max_slots) * std::max(1, kRemTiles);
-      blocks = both * nt + 3 * ceil_div(kWaveBlocks, nt) * nt + 8;
-    } else {
-      blocks = (exact[t] >= 0 ? exact[t] : static_cast<int64_t>(w.cap[t])) * nt;
-    }
-    return static_cast<unsigned>(std::min<int64_t>(std::max<int64_t>(1, blocks), 0x7fffffff));
-  };
-  const unsigned grid1 = grid(k1, nt1), grid2 = grid(k2, nt2);
   const bool swiglu = act == MOE_SWIGLU;
   return dt == MOE_BF16 ? launch_ffn<true>(p1, k1 != kG256, grid1, t1, p2, k2 != kG256, grid2, t2, swiglu, s)
                         : launch_ffn<false>(p1, k1 != kG256, grid1, t1, p2, k2 != kG256, grid2, t2, swiglu, s);

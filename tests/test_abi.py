@@ -72,6 +72,9 @@ N = None
     ("moe_expert_ffn", (16, 1, 100, 128, 128, 8, 16, 16, 16, 8, 16, N, 16, 0, 1, 16, 16, 1 << 30, N), -1, "w_up"),
     ("moe_expert_ffn", (16, 1, 100, 128, 128, 8, 16, 16, 16, 8, 16, 16, 16, 1, 1, 16, 16, 1 << 30, N), -1, "GELU"),
     ("moe_expert_ffn", (16, 1, 100, 128, 128, 8, 16, 16, 16, 8, 16, 16, 16, 0, 1, 16, 16, 10, N), -3, "workspace"),
+    # 2^27 rows x 2^21 columns: more blocks than 32-bit grid indexing covers
+    ("moe_expert_ffn", (16, 1, 1 << 27, 64, 1 << 21, 8, 16, 16, 16, 8, 16, 16, 16, 0, 1, 16, 16, 1 << 62, N), -2,
+     "32-bit grid"),
     ("moe_stats_load_state", (1, 1 << 20, 2, 8, 10, 0, 0, 1.5, N, N, N, N), -1, "decay"),
     ("moe_stats_load_state", (1, 1 << 20, 2, 8, 10, 2, 0, 0.9, N, N, N, N), -1, "layer=2"),
     ("moe_stats_load_state", (1, 8, 2, 8, 10, 0, 0, 0.9, N, N, N, N), -3, "too small"),
@@ -92,6 +95,9 @@ N = None
                       10, N), -3, "workspace"),
     ("moe_backward", (16, 16, 1, 10, 9, 128, 128, 8, 16, 16, 16, 16, 16, 16, 16, 0, 16, 16, 16, 16, 16, 16, 16,
                       1 << 40, N), -1, "k=9"),
+    # 16 experts with I = 2^20: the weight-gradient grid exceeds 32-bit indexing
+    ("moe_backward", (16, 16, 1, 10, 2, 64, 1 << 20, 16, 16, 16, 16, 16, 16, 16, 16, 0, 16, 16, 16, 16, 16, 16, 16,
+                      1 << 62, N), -2, "32-bit grid"),
     ("moe_combine", (16, 1, 10, 16, 16, 10, 9, 64, 16, N), -1, "k=9"),
     ("moe_combine", (16, 1, 10, 16, 16, 10, 2, 12, 16, N), -1, "multiple of 16"),
 ])
