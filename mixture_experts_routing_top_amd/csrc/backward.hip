@@ -156,15 +156,19 @@ enum TMode { kCopy = 0, kSwiGLUAct = 1, kGELUAct = 2 };
 // Expert-padded transpose of row-major [M, C] activations into [C, ld]: expert
 // e's rows off[e] .. off[e+1] become columns seg[e] .. (zero to seg[e+1]).
 // kSwiGLUAct / kGELUAct read the fp32 pre-activations ([M, 2C] g | u, or
-// [M, C] z) and write h rounded to the dtype exactly as the forward epilogue
-// does.  Column blocks of 64 never straddle experts (segments are multiples of 64).
+// [M, C] z) and write h rounded to the dtype from the forward's own activation
+// (swiglu_h / gelu_h).  Column blocks of 64 never straddle experts (segments
+// are multiples of 64); C is a multiple of 64.  64 x 64 tiles through LDS with
+// 16-byte global loads and stores.
 template <bool kBf16, int MODE>
 __global__ __launch_bounds__(256) void transpose_padded_kernel(const void* __restrict__ src, int64_t M, int C,
                                                                const int32_t* __restrict__ off,
                                                                const int32_t* __restrict__ seg, int E,
                                                                void* __restrict__ dst, int ld) {
   using T = typename Tr<kBf16>::T;
-  __shared__ T tile[64][65];
+  constexpr int V = 16 / sizeof(T);            // elements of T per 16-byte store
+  constexpr int RV = MODE == kCopy ? V : 4;    // source elements per 16-byte load (fp32 pre-activations: 4)
+  __shared__ T tile[64][64 + 2];
   const int j0 = blockIdx.y * 64;  // destination column block (padded row index)
   const int c0 = blockIdx.x * 64;  // source column block
   if (j0 >= seg[E]) return;
@@ -172,34 +176,54 @@ __global__ __launch_bounds__(256) void transpose_padded_kernel(const void* __res
   while (e + 1 < E && seg[e + 1] <= j0) ++e;
   const int64_t n_e = min<int64_t>(static_cast<int64_t>(off[e + 1]) - off[e], seg[e + 1] - seg[e]);
   const int64_t base = off[e] + (j0 - seg[e]);
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int y = ty; y < 64; y += 4) {
+  for (int q = threadIdx.x; q < 64 * (64 / RV); q += 256) {
+    const int y = q / (64 / RV), x = (q % (64 / RV)) * RV;  // source row base + y, columns c0 + x ..
     const int64_t row = base + y;
-    const bool ok = (j0 - seg[e]) + y < n_e && row >= 0 && row < M && c0 + tx < C;
-    T v = T(0);
-    if (ok) {
-      if constexpr (MODE == kCopy) {
-        v = static_cast<const T*>(src)[row * C + c0 + tx];
-      } else {
-        float h;
+    const bool ok = (j0 - seg[e]) + y < n_e && row >= 0 && row < M;
+    T v[RV];
+    if constexpr (MODE == kCopy) {
+      const uint4 raw = ok ? *reinterpret_cast<const uint4*>(static_cast<const T*>(src) + row * C + c0 + x)
+                           : make_uint4(0, 0, 0, 0);
+      __builtin_memcpy(v, &raw, sizeof(raw));
+    } else {
+      float h[4] = {0.f, 0.f, 0.f, 0.f};
+      if (ok) {
         if constexpr (MODE == kSwiGLUAct) {
           const float* gu = static_cast<const float*>(src) + row * 2 * C;
-          const float gt = gu[c0 + tx], up = gu[C + c0 + tx];
-          h = gt / (1.f + expf(-gt)) * up;
+          const float4 gt = *reinterpret_cast<const float4*>(gu + c0 + x);
+          const float4 up = *reinterpret_cast<const float4*>(gu + C + c0 + x);
+          h[0] = swiglu_h(gt.x, up.x);
+          h[1] = swiglu_h(gt.y, up.y);
+          h[2] = swiglu_h(gt.z, up.z);
+          h[3] = swiglu_h(gt.w, up.w);
         } else {
-          const float z = static_cast<const float*>(src)[row * C + c0 + tx];
-          h = 0.5f * z * (1.f + erff(z * 0.70710678118654752f));
+          const float4 z = *reinterpret_cast<const float4*>(static_cast<const float*>(src) + row * C + c0 + x);
+          h[0] = gelu_h(z.x);
+          h[1] = gelu_h(z.y);
+          h[2] = gelu_h(z.z);
+          h[3] = gelu_h(z.w);
         }
-        if constexpr (kBf16) v = static_cast<uint16_t>(f32_to_bf16_bits(h));
-        else v = h;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if constexpr (kBf16) v[u] = static_cast<uint16_t>(f32_to_bf16_bits(h[u]));
+        else v[u] = h[u];
       }
     }
-    tile[y][tx] = v;
+#pragma unroll
+    for (int u = 0; u < RV; ++u) tile[y][x + u] = v[u];
   }
   __syncthreads();
   T* d = static_cast<T*>(dst);
-  for (int y = ty; y < 64; y += 4)
-    if (c0 + y < C) d[static_cast<int64_t>(c0 + y) * ld + j0 + tx] = tile[tx][y];
+  for (int q = threadIdx.x; q < 64 * (64 / V); q += 256) {
+    const int y = q / (64 / V), x = (q % (64 / V)) * V;  // destination row c0 + y, columns j0 + x ..
+    T v[V];
+#pragma unroll
+    for (int u = 0; u < V; ++u) v[u] = tile[x + u][y];
+    uint4 raw;
+    __builtin_memcpy(&raw, v, sizeof(raw));
+    *reinterpret_cast<uint4*>(d + static_cast<int64_t>(c0 + y) * ld + j0 + x) = raw;
+  }
 }
 
 // seg[e] = sum over e' < e of n_e' rounded up to 64 (n_e clamped to [0, M], the

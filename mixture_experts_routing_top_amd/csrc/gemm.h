@@ -160,6 +160,15 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ void store4(float* p, const float v[4]) {
   *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
 }
+// The forward activations, shared with the backward pass that rebuilds h from
+// the fp32 pre-activations, so both round the same value.  SwiGLU: silu(g) u
+// with g / (1 + 2^(-g log2 e)) on the hardware exp2 and reciprocal (an
+// infinite exponent gives 0); GELU: the exact erf form.
+__device__ __forceinline__ float swiglu_h(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(g * -1.4426950408889634f)) * u;
+}
+__device__ __forceinline__ float gelu_h(float z) { return 0.5f * z * (1.f + erff(z * 0.70710678118654752f)); }
+
 __device__ __forceinline__ void store4(uint16_t* p, const float v[4]) {
   const bf16x2 lo = __builtin_convertvector((f32x2{v[0], v[1]}), bf16x2);
   const bf16x2 hi = __builtin_convertvector((f32x2{v[2], v[3]}), bf16x2);
@@ -743,7 +752,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs g, const int b) {
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
               if constexpr (EPI == kEpiGELU) {
-                o0[c] = 0.5f * av[c] * (1.f + erff(av[c] * 0.70710678118654752f));
+                o0[c] = gelu_h(av[c]);
               } else if constexpr (EPI == kEpiSwiGLUBwd) {
                 // d_g = d_h * u * silu'(g), d_u = d_h * silu(g); silu'(g) = s (1 + g (1 - s))
                 const float gt = (&p0[u].x)[c], up = (&p1[u].x)[c];
@@ -800,11 +809,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs g, const int b) {
         for (int c = 0; c < 4; ++c) {
           v[c] = acc[i][j][4 * q + c];
           if constexpr (EPI == kEpiStoreGU) w[c] = acc[i][j + TN / 2][4 * q + c];
-          if constexpr (EPI == kEpiSwiGLU) {
-            // silu(g) u with g / (1 + 2^(-g log2 e)); an infinite exponent gives 0
-            const float up = acc[i][j + TN / 2][4 * q + c];
-            v[c] = v[c] * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(v[c] * -1.4426950408889634f)) * up;
-          }
+          if constexpr (EPI == kEpiSwiGLU) v[c] = swiglu_h(v[c], acc[i][j + TN / 2][4 * q + c]);
         }
         if constexpr (kWgrad) {
           T* C = row < g.c_split
