@@ -293,10 +293,12 @@ int moe_ffn_set_timing_events(void* before_gateup, void* after_gateup, void* aft
  *   d_logits     fp32 [T, E]: w_j (dw_j - sum_i w_i dw_i) at e = topk_idx[t,j],
  *                0 elsewhere (softmax over the kept logits);
  *   d_y[r]       = w[t,i] d_out[t] for r = inv_pos[t,i]       (dtype);
+ *   d_h          = d_y Wd, kept in fp32;
  *   pre-activations g = x Wg^T, u = x Wu^T (GELU: z = x W1^T) recomputed by
- *   the grouped GEMM and kept in fp32;
- *   d_g | d_u    = d_h u silu'(g) | d_h silu(g) with d_h = d_y Wd (GELU:
- *                d_z = d_h gelu'(z)), rounded to the dtype;
+ *   the grouped GEMM, whose epilogue meets their fp32 values with d_h:
+ *   d_g | d_u    = d_h u silu'(g) | d_h silu(g) (GELU: d_z = d_h gelu'(z)),
+ *                rounded to the dtype, and h rebuilt as the forward computes
+ *                and rounds it;
  *   d_x[t]       = sum_i d_x_perm[inv_pos[t,i]], d_x_perm = d_g Wg + d_u Wu;
  *   d_w_down[e]  = sum over expert e's rows of d_y^T h ([E, H, I]);
  *   d_w_gate[e], d_w_up[e] = sum over the rows of d_g^T x_perm, d_u^T x_perm
@@ -305,8 +307,8 @@ int moe_ffn_set_timing_events(void* before_gateup, void* after_gateup, void* aft
  * grouped by expert; replica slots do not matter here), y_perm from
  * moe_expert_ffn, topk_idx/topk_w from moe_route, inv_pos from moe_dispatch.
  * All gradients are written whole (experts with no rows get zero weight
- * gradients).  Workspace: moe_backward_workspace_bytes(...) bytes (fp32
- * pre-activations, transposed weights, expert-padded transposed activations).
+ * gradients).  Workspace: moe_backward_workspace_bytes(...) bytes (fp32 d_h,
+ * h, transposed weights, expert-padded transposed activations).
  * Limits: those of moe_expert_ffn; T*k < 2^30.
  */
 size_t moe_backward_workspace_bytes(moe_dtype dt, int64_t T, int k, int H, int I, int E, moe_act act); /* [host] */

@@ -12,12 +12,14 @@
 //      y_perm[r]>, d_y[r] = w[t,i] d_out[t] for r = inv_pos[t,i], and the
 //      softmax Jacobian over the kept logits, d_l[t,e_j] = w_j (dw_j - sum_i
 //      w_i dw_i) (zero for the other experts);
-//   2. the gate/up (or W1) pre-activations recomputed by the grouped GEMM and
-//      kept in fp32 (activation recomputation rather than a saved [M, 2I]);
-//   3. d_h = d_y Wd by the grouped GEMM on transposed down weights, with the
-//      activation gradient in its epilogue -> d_g | d_u (or d_z), in the dtype;
-//   4. weight gradient of Wd: d_y and h (from the fp32 pre-activations, rounded
-//      exactly as the forward rounds it) transposed into per-expert K ranges
+//   2. d_h = d_y Wd by the grouped GEMM on transposed down weights, kept in
+//      fp32 [M, I];
+//   3. the gate/up (or W1) pre-activations recomputed by the grouped GEMM
+//      (activation recomputation rather than a saved [M, 2I]); its epilogue
+//      meets their fp32 accumulators with d_h: the activation gradient
+//      d_g | d_u (or d_z) and h, rebuilt with the forward's own activation so
+//      it rounds as the forward rounded it, both in the dtype;
+//   4. weight gradient of Wd: d_y and h transposed into per-expert K ranges
 //      padded to the K step, then one expert-grouped GEMM;
 //   5. d_x_perm = d_g Wg + d_u Wu as one GEMM with K = 2I over [Wg; Wu]^T;
 //   6. d_x = the unweighted sum of each token's k rows (the combine kernel);
@@ -151,23 +153,18 @@ __global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ sr
   }
 }
 
-enum TMode { kCopy = 0, kSwiGLUAct = 1, kGELUAct = 2 };
-
 // Expert-padded transpose of row-major [M, C] activations into [C, ld]: expert
 // e's rows off[e] .. off[e+1] become columns seg[e] .. (zero to seg[e+1]).
-// kSwiGLUAct / kGELUAct read the fp32 pre-activations ([M, 2C] g | u, or
-// [M, C] z) and write h rounded to the dtype from the forward's own activation
-// (swiglu_h / gelu_h).  Column blocks of 64 never straddle experts (segments
-// are multiples of 64); C is a multiple of 64.  64 x 64 tiles through LDS with
-// 16-byte global loads and stores.
-template <bool kBf16, int MODE>
+// Column blocks of 64 never straddle experts (segments are multiples of 64); C
+// is a multiple of 64.  64 x 64 tiles through LDS with 16-byte global loads and
+// stores.
+template <bool kBf16>
 __global__ __launch_bounds__(256) void transpose_padded_kernel(const void* __restrict__ src, int64_t M, int C,
                                                                const int32_t* __restrict__ off,
                                                                const int32_t* __restrict__ seg, int E,
                                                                void* __restrict__ dst, int ld) {
   using T = typename Tr<kBf16>::T;
-  constexpr int V = 16 / sizeof(T);            // elements of T per 16-byte store
-  constexpr int RV = MODE == kCopy ? V : 4;    // source elements per 16-byte load (fp32 pre-activations: 4)
+  constexpr int V = 16 / sizeof(T);  // elements per 16-byte access
   __shared__ T tile[64][64 + 2];
   const int j0 = blockIdx.y * 64;  // destination column block (padded row index)
   const int c0 = blockIdx.x * 64;  // source column block
@@ -176,42 +173,16 @@ __global__ __launch_bounds__(256) void transpose_padded_kernel(const void* __res
   while (e + 1 < E && seg[e + 1] <= j0) ++e;
   const int64_t n_e = min<int64_t>(static_cast<int64_t>(off[e + 1]) - off[e], seg[e + 1] - seg[e]);
   const int64_t base = off[e] + (j0 - seg[e]);
-  for (int q = threadIdx.x; q < 64 * (64 / RV); q += 256) {
-    const int y = q / (64 / RV), x = (q % (64 / RV)) * RV;  // source row base + y, columns c0 + x ..
+  for (int q = threadIdx.x; q < 64 * (64 / V); q += 256) {
+    const int y = q / (64 / V), x = (q % (64 / V)) * V;  // source row base + y, columns c0 + x ..
     const int64_t row = base + y;
     const bool ok = (j0 - seg[e]) + y < n_e && row >= 0 && row < M;
-    T v[RV];
-    if constexpr (MODE == kCopy) {
-      const uint4 raw = ok ? *reinterpret_cast<const uint4*>(static_cast<const T*>(src) + row * C + c0 + x)
-                           : make_uint4(0, 0, 0, 0);
-      __builtin_memcpy(v, &raw, sizeof(raw));
-    } else {
-      float h[4] = {0.f, 0.f, 0.f, 0.f};
-      if (ok) {
-        if constexpr (MODE == kSwiGLUAct) {
-          const float* gu = static_cast<const float*>(src) + row * 2 * C;
-          const float4 gt = *reinterpret_cast<const float4*>(gu + c0 + x);
-          const float4 up = *reinterpret_cast<const float4*>(gu + C + c0 + x);
-          h[0] = swiglu_h(gt.x, up.x);
-          h[1] = swiglu_h(gt.y, up.y);
-          h[2] = swiglu_h(gt.z, up.z);
-          h[3] = swiglu_h(gt.w, up.w);
-        } else {
-          const float4 z = *reinterpret_cast<const float4*>(static_cast<const float*>(src) + row * C + c0 + x);
-          h[0] = gelu_h(z.x);
-          h[1] = gelu_h(z.y);
-          h[2] = gelu_h(z.z);
-          h[3] = gelu_h(z.w);
-        }
-      }
+    const uint4 raw = ok ? *reinterpret_cast<const uint4*>(static_cast<const T*>(src) + row * C + c0 + x)
+                         : make_uint4(0, 0, 0, 0);
+    T v[V];
+    __builtin_memcpy(v, &raw, sizeof(raw));
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if constexpr (kBf16) v[u] = static_cast<uint16_t>(f32_to_bf16_bits(h[u]));
-        else v[u] = h[u];
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < RV; ++u) tile[y][x + u] = v[u];
+    for (int u = 0; u < V; ++u) tile[y][x + u] = v[u];
   }
   __syncthreads();
   T* d = static_cast<T*>(dst);
@@ -257,7 +228,7 @@ unsigned wgrad_grid(int E, int64_t rows, int col_tiles) {
 }
 
 struct BwdLayout {
-  size_t gu, dgu, dy, wdT, wguT, ta, tb, ones, seg, slot_expert, n_slots, tab_slot, tab_row0, tab_rend, n_tiles,
+  size_t dh, h, dgu, dy, wdT, wguT, ta, tb, ones, seg, slot_expert, n_slots, tab_slot, tab_row0, tab_rend, n_tiles,
       bytes;
   int64_t ld;  // padded row length of the transposed activations
   int tiles_cap;
@@ -272,7 +243,8 @@ BwdLayout bwd_layout(moe_dtype dt, int64_t T, int k, int H, int I, int E, moe_ac
   w.tiles_cap = static_cast<int>(moe::ceil_div(M, 256) + E);
   size_t at = 0;
   auto take = [&](size_t n) { size_t p = at; at = moe::align_up(at + n, 256); return p; };
-  w.gu = take(static_cast<size_t>(M) * nI * 4);
+  w.dh = take(static_cast<size_t>(M) * I * 4);
+  w.h = take(static_cast<size_t>(M) * I * s);
   w.dgu = take(static_cast<size_t>(M) * nI * s);
   w.dy = take(static_cast<size_t>(M) * H * s);
   w.wdT = take(static_cast<size_t>(E) * I * H * s);
@@ -303,7 +275,8 @@ int run_backward(const void* x_perm, const void* y_perm, int64_t n_tok, int k, i
   const int S = sizeof(T);
   const int nI = swiglu ? 2 * I : I;
   auto at = [&](size_t o) { return ws + o; };
-  float* gu = reinterpret_cast<float*>(at(L.gu));
+  float* dh = reinterpret_cast<float*>(at(L.dh));
+  T* hbuf = reinterpret_cast<T*>(at(L.h));
   T* dgu = reinterpret_cast<T*>(at(L.dgu));
   T* dy = reinterpret_cast<T*>(at(L.dy));
   T* wdT = reinterpret_cast<T*>(at(L.wdT));
@@ -352,47 +325,44 @@ int run_backward(const void* x_perm, const void* y_perm, int64_t n_tok, int k, i
   base.n_tiles = n_tiles;
   const unsigned grid_rows = static_cast<unsigned>(L.tiles_cap);
 
-  // 2. recompute the pre-activations in fp32
+  // 2. d_h = d_y Wd in fp32
   GemmArgs p = base;
+  p.A = dy;
+  p.B0 = wdT;
+  p.C = dh;
+  p.K = H;
+  p.N = I;
+  p.n_col_tiles = static_cast<int>(ceil_div(I, kTileN));
+  gemm_kernel<kBf16, 1, kEpiStoreF32, 256, 2><<<grid_rows * p.n_col_tiles, 256, 0, s>>>(p);
+  if (int rc = check("moe_backward d_h")) return rc;
+
+  // 3. recompute the pre-activations; the epilogue turns d_h into d_g | d_u
+  //    (or d_z) and rebuilds h
+  p = base;
   p.A = x_perm;
   p.B0 = w_gate;
   p.B1 = w_up;
-  p.C = gu;
+  p.C = dgu;
+  p.C2 = hbuf;
+  p.aux = dh;
   p.K = H;
   p.N = I;
   if (swiglu) {
     p.n_col_tiles = static_cast<int>(ceil_div(I, kTileN / 2));
-    gemm_kernel<kBf16, 2, kEpiStoreGU, 256, 2><<<grid_rows * p.n_col_tiles, 256, 0, s>>>(p);
+    gemm_kernel<kBf16, 2, kEpiSwiGLUGrad, 256, 2><<<grid_rows * p.n_col_tiles, 256, 0, s>>>(p);
   } else {
     p.n_col_tiles = static_cast<int>(ceil_div(I, kTileN));
-    gemm_kernel<kBf16, 1, kEpiStoreF32, 256, 2><<<grid_rows * p.n_col_tiles, 256, 0, s>>>(p);
+    gemm_kernel<kBf16, 1, kEpiGELUGrad, 256, 2><<<grid_rows * p.n_col_tiles, 256, 0, s>>>(p);
   }
   if (int rc = check("moe_backward recompute")) return rc;
-
-  // 3. d_h = d_y Wd, activation gradient in the epilogue
-  p = base;
-  p.A = dy;
-  p.B0 = wdT;
-  p.C = dgu;
-  p.aux = gu;
-  p.K = H;
-  p.N = I;
-  p.n_col_tiles = static_cast<int>(ceil_div(I, kTileN));
-  if (swiglu) gemm_kernel<kBf16, 1, kEpiSwiGLUBwd, 256, 2><<<grid_rows * p.n_col_tiles, 256, 0, s>>>(p);
-  else gemm_kernel<kBf16, 1, kEpiGELUBwd, 256, 2><<<grid_rows * p.n_col_tiles, 256, 0, s>>>(p);
-  if (int rc = check("moe_backward d_h")) return rc;
 
   // 4. d_Wd = sum over each expert's rows of d_y^T h
   const int ld = static_cast<int>(L.ld);
   const unsigned ldb = static_cast<unsigned>(ceil_div(L.ld, 64));
-  transpose_padded_kernel<kBf16, kCopy><<<dim3(ceil_div(H, 64), ldb), 256, 0, s>>>(dy, M, H, expert_off, seg, E, ta,
+  transpose_padded_kernel<kBf16><<<dim3(ceil_div(H, 64), ldb), 256, 0, s>>>(dy, M, H, expert_off, seg, E, ta,
                                                                                   ld);
-  if (swiglu)
-    transpose_padded_kernel<kBf16, kSwiGLUAct><<<dim3(ceil_div(I, 64), ldb), 256, 0, s>>>(gu, M, I, expert_off, seg,
-                                                                                          E, tb, ld);
-  else
-    transpose_padded_kernel<kBf16, kGELUAct><<<dim3(ceil_div(I, 64), ldb), 256, 0, s>>>(gu, M, I, expert_off, seg, E,
-                                                                                        tb, ld);
+  transpose_padded_kernel<kBf16><<<dim3(ceil_div(I, 64), ldb), 256, 0, s>>>(hbuf, M, I, expert_off, seg, E,
+                                                                                  tb, ld);
   GemmArgs q{};
   q.A = ta;
   q.B0 = tb;
@@ -423,9 +393,9 @@ int run_backward(const void* x_perm, const void* y_perm, int64_t n_tok, int k, i
   if (int rc = moe_combine(dy, kBf16 ? MOE_BF16 : MOE_F32, M, inv_pos, ones, n_tok, k, H, d_x, s)) return rc;
 
   // 7. d_Wg | d_Wu (or d_W1) = sum over each expert's rows of [d_g | d_u]^T x_perm
-  transpose_padded_kernel<kBf16, kCopy><<<dim3(ceil_div(nI, 64), ldb), 256, 0, s>>>(dgu, M, nI, expert_off, seg, E,
+  transpose_padded_kernel<kBf16><<<dim3(ceil_div(nI, 64), ldb), 256, 0, s>>>(dgu, M, nI, expert_off, seg, E,
                                                                                    ta, ld);
-  transpose_padded_kernel<kBf16, kCopy><<<dim3(ceil_div(H, 64), ldb), 256, 0, s>>>(x_perm, M, H, expert_off, seg, E,
+  transpose_padded_kernel<kBf16><<<dim3(ceil_div(H, 64), ldb), 256, 0, s>>>(x_perm, M, H, expert_off, seg, E,
                                                                                   tb, ld);
   q.A = ta;
   q.B0 = tb;

@@ -40,13 +40,12 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // Epilogues.  Forward: SwiGLU / GELU activation to the dtype, or a plain store.
-// Backward: the gate/up pre-activations kept in fp32 ([M, 2I] with g then u,
-// or [M, I] for GELU's z), and the activation gradients computed from the
-// d_h accumulators and those pre-activations ([M, 2I] d_g then d_u, or d_z),
-// rounded to the dtype.
+// Backward: an fp32 store (d_h), and the recomputed gate/up (or W1)
+// pre-activations met with d_h (read from aux, fp32 [M, I]): the activation
+// gradient ([M, 2I] d_g then d_u, or [M, I] d_z, into C) and h ([M, I], into
+// C2), rounded to the dtype.
 enum Epi {
-  kEpiSwiGLU = 0, kEpiGELU = 1, kEpiStore = 2,
-  kEpiStoreGU = 3, kEpiStoreF32 = 4, kEpiSwiGLUBwd = 5, kEpiGELUBwd = 6
+  kEpiSwiGLU = 0, kEpiGELU = 1, kEpiStore = 2, kEpiStoreF32 = 3, kEpiSwiGLUGrad = 4, kEpiGELUGrad = 5
 };
 
 template <bool kBf16>
@@ -190,7 +189,7 @@ constexpr int gemm_lds_bytes() {
   constexpr bool kDTL = kBf16 && BM == 256;
   constexpr bool kDTL64 = kBf16 && BM == 64 && !kWgrad;
   constexpr int kStageBytes = (BM + kTileN) * kRowBytes;
-  constexpr int kStagedEpi = (!kWgrad && (EPI == kEpiGELU || EPI == kEpiSwiGLUBwd || EPI == kEpiGELUBwd))
+  constexpr int kStagedEpi = (!kWgrad && (EPI == kEpiGELU || EPI == kEpiSwiGLUGrad || EPI == kEpiGELUGrad))
                                  ? (BM / WM) * (kTileN + 4) * 4 : 0;
   constexpr int kDtlBytes = kDTL ? 2 * BM * 128 + 3 * kTileN * 128 : 4 * (BM + kTileN) * 128;
   return (kDTL || kDTL64) ? (kDtlBytes > kStagedEpi ? kDtlBytes : kStagedEpi) : 2 * kStageBytes;
@@ -697,11 +696,90 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs g, const int b) {
   }
 
   // ---- epilogues with heavy per-element math: stage the fp32 accumulators
-  // through LDS, BM/WM rows at a time, then let every thread walk one column
-  // of the 256-column tile (row-contiguous, coalesced reads of the
-  // pre-activations and stores of the result).  Keeps the register epilogue
-  // small enough to stay unrolled.
-  if constexpr (!kWgrad && (EPI == kEpiGELU || EPI == kEpiSwiGLUBwd || EPI == kEpiGELUBwd)) {
+  // through LDS, BM/WM rows at a time, then let every thread walk a few
+  // columns of the tile (row-contiguous, coalesced reads of d_h and stores of
+  // the results).  Keeps the register epilogue small enough to stay unrolled.
+  if constexpr (!kWgrad && EPI == kEpiSwiGLUGrad) {
+    // the recompute of g | u with the SwiGLU gradient: g and u of an output
+    // column sit CW / 2 stage columns apart; thread (ty, tx) walks output
+    // columns 4 tx .. 4 tx + 3 (of NSUB = 128) over rows ty, ty + 8, ...
+    static_assert(NMAT == 2, "g and u come from the two weight matrices");
+    constexpr int RH = BM / WM;
+    constexpr int kPitch = kTileN + 4;
+    static_assert(RH * kPitch * 4 <= kLdsBytes, "staging tile must fit in LDS");
+    float* stage = reinterpret_cast<float*>(lds);
+    __syncthreads();  // every wave is done with the operand stages
+#pragma unroll
+    for (int h = 0; h < WM; ++h) {
+      if (wm == h) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              *reinterpret_cast<float4*>(stage + (i * 32 + lr) * kPitch + wn * CW + j * 32 + 8 * q + 4 * lg) =
+                  make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+      }
+      __syncthreads();
+      const int tx = tid & 31, ty = tid >> 5;
+      const int oc = 4 * tx;
+      const int gc = (oc / (CW / 2)) * CW + oc % (CW / 2);  // stage column of g; u is CW / 2 further
+      const int col = n0 + oc;
+      T* __restrict__ C = static_cast<T*>(g.C);
+      T* __restrict__ C2 = static_cast<T*>(g.C2);
+      const float* __restrict__ aux = g.aux;
+      const int rows = min(RH, m_valid - h * RH);
+      if (col < N) {
+        for (int nb = ty; nb < rows; nb += 32) {
+          float4 gv[4], uv[4], dv[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {   // rows nb, nb + 8, nb + 16, nb + 24: loads first
+            const int n = min(nb + 8 * u, rows - 1);
+            const int64_t row = r0 + h * RH + n;
+            gv[u] = *reinterpret_cast<const float4*>(stage + n * kPitch + gc);
+            uv[u] = *reinterpret_cast<const float4*>(stage + n * kPitch + gc + CW / 2);
+            dv[u] = *reinterpret_cast<const float4*>(aux + row * N + col);
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            if (nb + 8 * u >= rows) break;
+            const int64_t row = r0 + h * RH + nb + 8 * u;
+            float o0[4], o1[4], hv[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              // d_g = d_h * u * silu'(g), d_u = d_h * silu(g); silu'(g) = s (1 + g (1 - s))
+              const float gt = (&gv[u].x)[c], up = (&uv[u].x)[c], av = (&dv[u].x)[c];
+              const float sg = 1.f / (1.f + expf(-gt));
+              o0[c] = av * up * (sg * (1.f + gt * (1.f - sg)));
+              o1[c] = av * (gt / (1.f + expf(-gt)));
+              hv[c] = swiglu_h(gt, up);
+            }
+            const int64_t o = row * 2 * N + col;
+            if constexpr (kBf16) {
+              *reinterpret_cast<uint2*>(C + o) =
+                  make_uint2(f32_to_bf16_bits(o0[0]) | (f32_to_bf16_bits(o0[1]) << 16),
+                             f32_to_bf16_bits(o0[2]) | (f32_to_bf16_bits(o0[3]) << 16));
+              *reinterpret_cast<uint2*>(C + o + N) =
+                  make_uint2(f32_to_bf16_bits(o1[0]) | (f32_to_bf16_bits(o1[1]) << 16),
+                             f32_to_bf16_bits(o1[2]) | (f32_to_bf16_bits(o1[3]) << 16));
+              *reinterpret_cast<uint2*>(C2 + row * N + col) =
+                  make_uint2(f32_to_bf16_bits(hv[0]) | (f32_to_bf16_bits(hv[1]) << 16),
+                             f32_to_bf16_bits(hv[2]) | (f32_to_bf16_bits(hv[3]) << 16));
+            } else {
+              *reinterpret_cast<float4*>(C + o) = make_float4(o0[0], o0[1], o0[2], o0[3]);
+              *reinterpret_cast<float4*>(C + o + N) = make_float4(o1[0], o1[1], o1[2], o1[3]);
+              *reinterpret_cast<float4*>(C2 + row * N + col) = make_float4(hv[0], hv[1], hv[2], hv[3]);
+            }
+          }
+        }
+      }
+      __syncthreads();
+    }
+    return;
+  }
+
+  if constexpr (!kWgrad && (EPI == kEpiGELU || EPI == kEpiGELUGrad)) {
     static_assert(NMAT == 1, "staged epilogues take one weight matrix");
     constexpr int RH = BM / WM;  // rows staged per round
     constexpr int kPitch = kTileN + 4;  // floats per staged row (padded: rows start 4 banks apart)
@@ -730,18 +808,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs g, const int b) {
       const int rows = min(RH, m_valid - h * RH);
       if (col < N) {
         for (int nb = ty; nb < rows; nb += 16) {
-          float4 a[4], p0[4], p1[4];
+          float4 a[4], p0[4];
 #pragma unroll
           for (int u = 0; u < 4; ++u) {   // rows nb, nb + 4, nb + 8, nb + 12: loads first
             const int n = min(nb + 4 * u, rows - 1);
             const int64_t row = r0 + h * RH + n;
             a[u] = *reinterpret_cast<const float4*>(stage + n * kPitch + 4 * tx);
-            if constexpr (EPI == kEpiSwiGLUBwd) {
-              p0[u] = *reinterpret_cast<const float4*>(aux + row * 2 * N + col);
-              p1[u] = *reinterpret_cast<const float4*>(aux + row * 2 * N + N + col);
-            } else if constexpr (EPI == kEpiGELUBwd) {
-              p0[u] = *reinterpret_cast<const float4*>(aux + row * N + col);
-            }
+            if constexpr (EPI == kEpiGELUGrad) p0[u] = *reinterpret_cast<const float4*>(aux + row * N + col);
           }
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
@@ -753,32 +826,28 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs g, const int b) {
             for (int c = 0; c < 4; ++c) {
               if constexpr (EPI == kEpiGELU) {
                 o0[c] = gelu_h(av[c]);
-              } else if constexpr (EPI == kEpiSwiGLUBwd) {
-                // d_g = d_h * u * silu'(g), d_u = d_h * silu(g); silu'(g) = s (1 + g (1 - s))
-                const float gt = (&p0[u].x)[c], up = (&p1[u].x)[c];
-                const float sg = 1.f / (1.f + expf(-gt));
-                o0[c] = av[c] * up * (sg * (1.f + gt * (1.f - sg)));
-                o1[c] = av[c] * (gt / (1.f + expf(-gt)));
               } else {
-                // d_z = d_h * (Phi(z) + z phi(z))
-                const float z = (&p0[u].x)[c];
-                o0[c] = av[c] * (0.5f * (1.f + erff(z * 0.70710678118654752f)) +
-                                 z * expf(-0.5f * z * z) * 0.39894228040143268f);
+                // the recompute of z with the GELU gradient: d_z = d_h (Phi(z) + z phi(z))
+                // from the read d_h, and h = gelu(z)
+                const float z = av[c], dh = (&p0[u].x)[c];
+                o0[c] = dh * (0.5f * (1.f + erff(z * 0.70710678118654752f)) +
+                              z * expf(-0.5f * z * z) * 0.39894228040143268f);
+                o1[c] = gelu_h(z);
               }
             }
-            const int64_t o = EPI == kEpiSwiGLUBwd ? row * 2 * N + col : row * N + col;
+            const int64_t o = row * N + col;
             if constexpr (kBf16) {
               *reinterpret_cast<uint2*>(C + o) =
                   make_uint2(f32_to_bf16_bits(o0[0]) | (f32_to_bf16_bits(o0[1]) << 16),
                              f32_to_bf16_bits(o0[2]) | (f32_to_bf16_bits(o0[3]) << 16));
-              if constexpr (EPI == kEpiSwiGLUBwd)
-                *reinterpret_cast<uint2*>(C + o + N) =
+              if constexpr (EPI == kEpiGELUGrad)
+                *reinterpret_cast<uint2*>(static_cast<T*>(g.C2) + o) =
                     make_uint2(f32_to_bf16_bits(o1[0]) | (f32_to_bf16_bits(o1[1]) << 16),
                                f32_to_bf16_bits(o1[2]) | (f32_to_bf16_bits(o1[3]) << 16));
             } else {
               *reinterpret_cast<float4*>(C + o) = make_float4(o0[0], o0[1], o0[2], o0[3]);
-              if constexpr (EPI == kEpiSwiGLUBwd)
-                *reinterpret_cast<float4*>(C + o + N) = make_float4(o1[0], o1[1], o1[2], o1[3]);
+              if constexpr (EPI == kEpiGELUGrad)
+                *reinterpret_cast<float4*>(static_cast<T*>(g.C2) + o) = make_float4(o1[0], o1[1], o1[2], o1[3]);
             }
           }
         }
@@ -804,11 +873,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs g, const int b) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int col = cb + 8 * q + 4 * lg;
-        float v[4], w[4];
+        float v[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           v[c] = acc[i][j][4 * q + c];
-          if constexpr (EPI == kEpiStoreGU) w[c] = acc[i][j + TN / 2][4 * q + c];
           if constexpr (EPI == kEpiSwiGLU) v[c] = swiglu_h(v[c], acc[i][j + TN / 2][4 * q + c]);
         }
         if constexpr (kWgrad) {
@@ -816,10 +884,6 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs g, const int b) {
                      ? static_cast<T*>(g.C) + (static_cast<int64_t>(e) * g.c_split + row) * N
                      : static_cast<T*>(g.C2) + (static_cast<int64_t>(e) * (g.Mw - g.c_split) + row - g.c_split) * N;
           store4(C + col, v);
-        } else if constexpr (EPI == kEpiStoreGU) {
-          float* C = static_cast<float*>(g.C) + row * 2 * N;
-          store4(C + col, v);
-          store4(C + N + col, w);
         } else if constexpr (EPI == kEpiStoreF32) {
           store4(static_cast<float*>(g.C) + row * N + col, v);
         } else {
