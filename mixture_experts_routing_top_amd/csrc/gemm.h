@@ -748,11 +748,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs g, const int b) {
             float o0[4], o1[4], hv[4];
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-              // d_g = d_h * u * silu'(g), d_u = d_h * silu(g); silu'(g) = s (1 + g (1 - s))
+              // d_g = d_h * u * silu'(g), d_u = d_h * silu(g), silu'(g) = s (1 + g (1 - s)),
+              // with the sigmoid s the forward's activation uses (one exp2 and one
+              // reciprocal per element, shared with h)
               const float gt = (&gv[u].x)[c], up = (&uv[u].x)[c], av = (&dv[u].x)[c];
-              const float sg = 1.f / (1.f + expf(-gt));
+              const float sg = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(gt * -1.4426950408889634f));
               o0[c] = av * up * (sg * (1.f + gt * (1.f - sg)));
-              o1[c] = av * (gt / (1.f + expf(-gt)));
+              o1[c] = av * (gt * sg);
               hv[c] = swiglu_h(gt, up);
             }
             const int64_t o = row * 2 * N + col;
