@@ -10,8 +10,9 @@
 // Three launches, no host sync:
 //   1. count:   per block of 256 tokens, per-expert counts (LDS atomics) into
 //               a [blocks, E] table in the workspace.
-//   2. rank:    every block sums the table's columns to get the expert totals,
-//               the exclusive expert offsets and its own per-expert prefix;
+//   2. rank:    every block sums the table (all threads, LDS atomics) to get
+//               the expert totals, the exclusive expert offsets and its own
+//               per-expert prefix;
 //               inside the block, each wave ranks its tokens per expert with
 //               ballots (order = token order, so the permutation is stable and
 //               independent of scheduling).  Block 0 also writes expert_off
@@ -56,16 +57,21 @@ __global__ __launch_bounds__(kTok) void rank_kernel(const int32_t* __restrict__ 
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
   for (int e = tid; e < E; e += kTok) {
-    int32_t s = 0, pre = 0;
-    // unrolled so the column's loads are in flight together (exact integer sums)
-#pragma unroll 8
-    for (int j = 0; j < nblk; ++j) {
-      const int32_t c = blk_cnt[static_cast<int64_t>(j) * E + e];
-      if (j < b) pre += c;
-      s += c;
-    }
-    tot[e] = s;
-    base[e] = pre;
+    tot[e] = 0;
+    base[e] = 0;
+  }
+  __syncthreads();
+  // every thread reads its share of the [nblk, E] count table (loads in flight
+  // together) and adds it into the expert totals and this block's prefix:
+  // exact integer sums, so the order of the LDS atomics does not matter
+  const int64_t cells = static_cast<int64_t>(nblk) * E;
+#pragma unroll 4
+  for (int64_t q = tid; q < cells; q += kTok) {
+    const int32_t c = blk_cnt[q];
+    if (c == 0) continue;
+    const int j = static_cast<int>(q / E), e = static_cast<int>(q - static_cast<int64_t>(j) * E);
+    atomicAdd(&tot[e], c);
+    if (j < b) atomicAdd(&base[e], c);
   }
   __syncthreads();
   if (tid == 0) {  // E <= 256: a short serial scan

@@ -973,21 +973,32 @@ __global__ __launch_bounds__(256) void tiles_kernel(const int32_t* __restrict__ 
                                                     TileSplit split) {
   __shared__ int32_t scan[256], scan2[256];
   __shared__ int32_t carry, carry2;
+  // slot tables of up to kLdsSlots slots are read from LDS: the merge walk over
+  // an expert's consecutive slots is a chain of dependent reads
+  constexpr int kLdsSlots = 1024;
+  __shared__ int32_t se_lds[kLdsSlots], so_lds[kLdsSlots + 1];
   const int tid = threadIdx.x;
   const int n = min(max(*n_slots_p, 0), max_slots);
   const bool companion = split.counts != nullptr && mode == kCover && BM == 256;
   const int rem_tiles = companion ? split.rem_tiles : 0;
+  const bool staged = n <= kLdsSlots;
+  if (staged) {
+    for (int i = tid; i < n; i += 256) se_lds[i] = slot_expert[i];
+    for (int i = tid; i <= n; i += 256) so_lds[i] = slot_off[i];
+  }
+  const int32_t* se = staged ? se_lds : slot_expert;
+  const int32_t* so = staged ? so_lds : slot_off;
   if (tid == 0) carry = carry2 = 0;
   __syncthreads();
   for (int c = 0; c < n; c += 256) {
     const int s = c + tid;
     int64_t start = 0, end = 0, cnt = 0, cnt_small = 0;
-    if (s < n && !(merge && s > 0 && slot_expert[s] == slot_expert[s - 1])) {
+    if (s < n && !(merge && s > 0 && se[s] == se[s - 1])) {
       int last = s + 1;  // one past the range's last slot
       if (merge)
-        while (last < n && slot_expert[last] == slot_expert[s]) ++last;
-      start = min<int64_t>(max(slot_off[s], 0), M);
-      end = min<int64_t>(max(slot_off[last], 0), M);
+        while (last < n && se[last] == se[s]) ++last;
+      start = min<int64_t>(max(so[s], 0), M);
+      end = min<int64_t>(max(so[last], 0), M);
       const int64_t rows = end > start ? end - start : 0;
       if (mode == kCover) {
         cnt = (rows + BM - 1) / BM;
