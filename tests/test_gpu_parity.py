@@ -368,18 +368,18 @@ def test_expert_ffn_hand_made_slot_table(M, dtype):
         assert np.array_equal(outs[path], outs["grouped"]), path
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_grouped_remainder_tiles_and_last_round(dtype):
+@pytest.mark.parametrize("dtype,n,max_rows", [("bf16", 300, 520), ("f32", 300, 520), ("bf16", 1100, 100)])
+def test_grouped_remainder_tiles_and_last_round(dtype, n, max_rows):
     """The 256-row grouped tiling on 300 slots (more than one 256-slot chunk of
     the tile-table scan) over 40 experts, slot sizes 0..519 with planted 1, 64,
     65, 255, 256 and 257: the 41 ranges of at most 64 rows run as 64-row tiles
     in the same launch, and both GEMMs (two and one column tiles) list trailing
-    row tiles again as 64-row tiles to fill the launch's last round.  Every row
-    matches the oracle's FFN of its slot's expert; all paths give the same
-    bits."""
+    row tiles again as 64-row tiles to fill the launch's last round.  With 1100
+    slots (sizes 0..99) the tile-table kernel reads the slot table from global
+    memory instead of LDS.  Every row matches the oracle's FFN of its slot's
+    expert; all paths give the same bits."""
     rng = np.random.default_rng(11)
-    n = 300
-    sizes = rng.integers(0, 520, n)
+    sizes = rng.integers(0, max_rows, n)
     sizes[::17] = 0
     sizes[[5, 6, 7, 8, 9, 10]] = [64, 65, 256, 257, 1, 255]
     experts = rng.integers(0, 40, n).astype(np.int32)
@@ -387,7 +387,7 @@ def test_grouped_remainder_tiles_and_last_round(dtype):
     cfg = synth.CONFIGS["mixtral"].scaled(T=M, E=40, H=128, I=192, dtype=dtype)
     x = synth.hidden0(cfg, 5)
     wts = synth.expert_weights(cfg)
-    max_slots = 320
+    max_slots = n + 20
     slot_off = np.full(max_slots + 1, M, np.int32)
     slot_off[:n + 1] = np.concatenate([[0], np.cumsum(sizes)])
     slot_expert = np.zeros(max_slots, np.int32)
