@@ -146,3 +146,34 @@ def test_empty_batch_forward_and_backward():
     assert fw["out"].shape == (0, cfg.H) and g["d_x"].shape == (0, cfg.H)
     for key in ("d_w_gate", "d_w_up", "d_w_down"):
         assert not torch.any(g[key].float() != 0), key
+
+
+@pytest.mark.parametrize("name", ["mixtral-mini", "popf-mini", "dbrx-mini"])
+def test_backward_rebuilds_the_forward_h(name):
+    """h for d_Wd is rebuilt from the recomputed pre-activations with the
+    forward's own activation, so it equals, bit for bit, the h the forward FFN
+    kept.  Reads both workspaces at their internal offsets: the FFN workspace
+    starts with h [M, I]; the backward workspace with fp32 d_h [M, I], then h
+    [M, I] at the next 256-byte boundary."""
+    cfg = CASES[name]
+    dev = torch.device("cuda:0")
+    x = to_dev(synth.hidden0(cfg, 1))
+    lg = to_dev(synth.logits(cfg, 0, 1))
+    wts = synth.expert_weights(cfg, 0)
+    wg, wu, wd = (None if w is None else to_dev(w) for w in wts)
+    idx, w = moe.moe_route(lg, cfg.k)
+    d = moe.moe_dispatch(x, idx, cfg.E, None, cfg.E)
+    M, H = d["x_perm"].shape
+    I, dt = cfg.I, d["x_perm"].dtype
+    esz = d["x_perm"].element_size()
+    ws_f = torch.empty(moe.moe_expert_ffn_workspace_bytes(dt, M, H, I, cfg.E), dtype=torch.uint8, device=dev)
+    y = moe.moe_expert_ffn(d["x_perm"], d["slot_off"], d["slot_expert"], d["n_slots"], wg, wu, wd, cfg.act,
+                           "grouped", None, ws_f)
+    ws_b = torch.empty(moe.moe_backward_workspace_bytes(dt, cfg.T, cfg.k, H, I, cfg.E, cfg.act), dtype=torch.uint8,
+                       device=dev)
+    d_out = torch.randn(cfg.T, H, device=dev).to(dt)
+    moe.moe_backward(d["x_perm"], y, idx, w, d["inv_pos"], d["expert_off"], wg, wu, wd, d_out, cfg.act,
+                     workspace=ws_b)
+    torch.cuda.synchronize()
+    off = (M * I * 4 + 255) // 256 * 256
+    assert torch.equal(ws_f[:M * I * esz], ws_b[off:off + M * I * esz])
