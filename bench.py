@@ -46,10 +46,15 @@ def parse():
     ap.add_argument("--replicas", type=int, default=8)
     ap.add_argument("--path", default="grouped", choices=["grouped", "grouped_small", "dense", "auto"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=96, help="FFN rows the CPU oracle runs (sample)")
+    ap.add_argument("--cpu-rows", type=int, default=12,
+                    help="FFN rows each CPU-baseline process runs (sample)")
     ap.add_argument("--crossover", action="store_true",
                     help="time the grouped and the dense expert-FFN paths on the DeepSeek-V2 T sweep and on the "
                          "GEMM shapes profiled by EPS-MoE, print one JSON line per case, and exit")
+    ap.add_argument("--cases", default="",
+                    help="with --crossover: comma-separated case labels to run (e.g. dsv2_T4096); default all")
+    ap.add_argument("--paths", default="grouped,grouped_small,dense,auto",
+                    help="with --crossover: comma-separated tilings to time")
     ap.add_argument("--configs", action="store_true",
                     help="routed tokens/s and roofline fraction of every workload (one line each)")
     ap.add_argument("--backward", action="store_true",
@@ -130,53 +135,104 @@ def memory_phase_summary(T, H, E, k, warm, cold):
     return out
 
 
-def cpu_baseline(cfg, x, logits, wts, prev_idx_np, rows):
-    """The oracle (single-threaded C) on a bounded sample of the same workload:
-    routing, statistics, replicas, dispatch/permute and combine at full size, and
-    the expert FFN on `rows` dispatched rows, extrapolated to all T*k rows."""
+_CPU = {}   # inputs of the CPU baseline's FFN workers (inherited by the forked processes)
+
+
+def _cpu_ffn_worker(span):
+    """One process of the N-core leg: the oracle's FFN (plain single-threaded C)
+    on its own disjoint run of the sampled rows."""
+    import oracle
+    lo, hi = span
+    sel = _CPU["sel"][lo:hi]
+    t0 = time.perf_counter()
+    oracle.ffn_rows(_CPU["x_perm"][sel], _CPU["expert"][sel], *_CPU["wts"], act=_CPU["act"])
+    return time.perf_counter() - t0
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(cfg, x, logits, wts, prev_logits, R, rows_per_proc):
+    """The oracle on this host, on a bounded sample of the same workload.
+
+    One core: routing, window statistics, replicas, dispatch/permute and combine
+    at full size (the oracle is single-threaded).  N cores: the expert FFN -- the
+    same single-threaded oracle code -- in N processes over disjoint runs of
+    rows (rows are independent after dispatch), each process `rows_per_proc`
+    rows of an even sample of the T*k rows; its wall time is extrapolated to all
+    rows.  Must run before the GPU is touched (the workers are forked)."""
+    import multiprocessing
+
     import numpy as np
 
     import oracle
 
     T, E, k = cfg.T, cfg.E, cfg.k
     t0 = time.perf_counter()
+    prev_idx, _ = oracle.route(prev_logits, k)
     idx, w = oracle.route(logits, k)
     st = oracle.WindowStats(3, E, 10)
-    st.record(0, 0, prev_idx_np)
-    counts = st.record(1, 0, idx, prev_idx_np)
+    st.record(0, 0, prev_idx)
+    counts = st.record(1, 0, idx, prev_idx)
     st.outputs(1)
-    reps = oracle.replicas(counts, T, k, 8)
+    reps = oracle.replicas(counts, T, k, R) if R else None
     d = oracle.dispatch(idx, E, reps)
     x_perm = oracle.permute(x, d["perm_src"])
     t_mem = time.perf_counter() - t0
-    sel = np.linspace(0, T * k - 1, rows).astype(np.int64)
-    row_expert = np.repeat(np.arange(E, dtype=np.int32), np.diff(d["expert_off"]))
-    t1 = time.perf_counter()
-    y_rows = oracle.ffn_rows(x_perm[sel], row_expert[sel], *wts, act=cfg.act)
-    t_rows = time.perf_counter() - t1
-    # combine at full size needs every y row; its cost does not depend on the values
-    y_fake = np.zeros_like(x_perm)
-    y_fake[sel] = y_rows
+    y_fake = np.zeros_like(x_perm)       # combine's cost does not depend on the values
     t2 = time.perf_counter()
     oracle.combine(y_fake, d["inv_pos"], w)
     t_comb = time.perf_counter() - t2
-    per_row = t_rows / rows
-    total = t_mem + t_comb + per_row * T * k
-    return {"value": T / total, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": (f"routing, window statistics, replicas, dispatch and combine at full size "
-                       f"(T={T}); expert FFN on {rows} of {T * k} rows, extrapolated "
-                       f"({per_row:.3f} s/row); measured CPU time {t_mem + t_rows + t_comb:.1f} s")}
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = os.cpu_count() or 1
+    n_proc = max(1, min(16, affinity))
+    n_rows = n_proc * rows_per_proc
+    _CPU.update(x_perm=x_perm, expert=np.repeat(np.arange(E, dtype=np.int32), np.diff(d["expert_off"])),
+                sel=np.linspace(0, T * k - 1, n_rows).astype(np.int64), wts=wts, act=cfg.act)
+    oracle.lib()                          # built and loaded once, before the fork
+    with multiprocessing.get_context("fork").Pool(n_proc) as pool:
+        pool.map(len, [()] * n_proc)      # workers up before timing
+        t1 = time.perf_counter()
+        per_proc = pool.map(_cpu_ffn_worker, [(i * rows_per_proc, (i + 1) * rows_per_proc) for i in range(n_proc)])
+        wall_ffn = time.perf_counter() - t1
+    _CPU.clear()
+    t_ffn_n = wall_ffn * (T * k) / n_rows                     # all rows on n_proc cores
+    t_ffn_1 = float(np.mean(per_proc)) / rows_per_proc * (T * k)  # all rows on one core
+    total_n = t_mem + t_comb + t_ffn_n
+    total_1 = t_mem + t_comb + t_ffn_1
+    return {"value": round(T / total_n, 3), "unit": "tokens/s", "cores": n_proc, "kind": "oracle",
+            "one_core_value": round(T / total_1, 3),
+            "n_core_wall_s": round(total_n, 1), "one_core_wall_s": round(total_1, 1),
+            "host": {"nproc": os.cpu_count(), "affinity_cpus": affinity, "cpu_model": cpu_model()},
+            "sample": (f"routing, window statistics, replicas, dispatch and combine at full size (T={T}) on one "
+                       f"core ({t_mem + t_comb:.1f} s); expert FFN on {n_rows} of {T * k} rows, {rows_per_proc} "
+                       f"per process in {n_proc} processes ({wall_ffn:.1f} s wall, "
+                       f"{float(np.sum(per_proc)):.1f} s CPU), extrapolated to all rows")}
 
 
-def crossover(moe, synth, torch, np):
+def crossover(moe, synth, torch, np, cases=(), paths=("grouped", "grouped_small", "dense", "auto")):
     """Grouped (256-row tiles) vs dense padded (64-row tiles) expert FFN.  Routing
     and slot tables come from the seeded generators; weights and activations are
-    random device tensors (values do not change the timing)."""
+    random device tensors (values do not change the timing).  `cases` limits the
+    run to those case labels (all when empty), `paths` to those tilings."""
     dev = torch.device("cuda:0")
     torch.manual_seed(0)
-    lib = moe.lib()
+
+    def wanted(label):
+        return not cases or label in cases
 
     def time_paths(x_perm, slot_off, slot_expert, n_slots, wg, wu, wd, label, extra):
+        if not wanted(label):
+            return
         M, H = x_perm.shape
         I = wg.shape[1]
         ws = torch.empty(moe.moe_expert_ffn_workspace_bytes(x_perm.dtype, M, H, I, slot_expert.numel()),
@@ -190,25 +246,22 @@ def crossover(moe, synth, torch, np):
         res["tiles"] = {"g256": int(np.sum(np.where(short, 0, (rows + 255) // 256))),
                         "g256_short64": int(np.count_nonzero(short)), "g64": int(np.sum((rows + 63) // 64)),
                         "d64": int(np.count_nonzero(rows) * ((rows.max() + 63) // 64))}
-        for path in ("grouped", "grouped_small", "dense", "auto"):
+        for path in paths:
             for _ in range(2):
                 moe.moe_expert_ffn(x_perm, slot_off, slot_expert, n_slots, wg, wu, wd, "swiglu", path, y, ws)
             torch.cuda.synchronize()
             ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(5)]
-            for tr in ev:
-                for e in tr:
-                    e.record()
-            torch.cuda.synchronize()
             for i in range(5):
-                lib.moe_ffn_set_timing_events(*(ev[i][j].cuda_event for j in range(3)))
-                moe.moe_expert_ffn(x_perm, slot_off, slot_expert, n_slots, wg, wu, wd, "swiglu", path, y, ws)
+                moe.moe_expert_ffn_profiled(x_perm, slot_off, slot_expert, n_slots, wg, wu, wd, ev[i], "swiglu", path,
+                                            y, ws)
             torch.cuda.synchronize()
-            lib.moe_ffn_set_timing_events(None, None, None)
             g = float(np.median([ev[i][0].elapsed_time(ev[i][1]) for i in range(5)]))
             d = float(np.median([ev[i][1].elapsed_time(ev[i][2]) for i in range(5)]))
             res[path] = {"gateup_ms": round(g, 4), "down_ms": round(d, 4), "ffn_ms": round(g + d, 4)}
         # which path AUTO takes (it reads the slot sizes back): compare its output timing-free
-        res["fastest"] = min(("grouped", "grouped_small", "dense"), key=lambda p: res[p]["ffn_ms"])
+        fixed = [p for p in ("grouped", "grouped_small", "dense") if p in res]
+        if fixed:
+            res["fastest"] = min(fixed, key=lambda p: res[p]["ffn_ms"])
         print(json.dumps(res), flush=True)
 
     cfg0 = synth.CONFIGS["dsv2"]
@@ -217,6 +270,8 @@ def crossover(moe, synth, torch, np):
     wu = (torch.randn(E, I, H, device=dev) * H ** -0.5).to(torch.bfloat16)
     wd = (torch.randn(E, H, I, device=dev) * I ** -0.5).to(torch.bfloat16)
     for T in synth.DSV2_T_SWEEP:
+        if not wanted(f"dsv2_T{T}"):
+            continue
         cfg = cfg0.with_T(T)
         idx, _ = moe.moe_route(torch.from_numpy(synth.logits(cfg, 0, 0)).to(dev), k)
         x = torch.randn(T, H, device=dev).to(torch.bfloat16)
@@ -229,11 +284,15 @@ def crossover(moe, synth, torch, np):
     # coarse-grained layers: Mixtral- and DBRX-shaped routing (large per-expert counts)
     for name in ("mixtral", "dbrx"):
         cfg = synth.CONFIGS[name]
+        if not any(wanted(f"{name}_T{T}") for T in (cfg.T // 8, cfg.T)):
+            continue
         E, H, I, k = cfg.E, cfg.H, cfg.I, cfg.k
         wg = (torch.randn(E, I, H, device=dev) * H ** -0.5).to(torch.bfloat16)
         wu = (torch.randn(E, I, H, device=dev) * H ** -0.5).to(torch.bfloat16)
         wd = (torch.randn(E, H, I, device=dev) * I ** -0.5).to(torch.bfloat16)
         for T in (cfg.T // 8, cfg.T):
+            if not wanted(f"{name}_T{T}"):
+                continue
             c = cfg.with_T(T)
             idx, _ = moe.moe_route(torch.from_numpy(synth.logits(c, 0, 0)).to(dev), k)
             x = torch.randn(T, H, device=dev).to(torch.bfloat16)
@@ -245,6 +304,8 @@ def crossover(moe, synth, torch, np):
         del wg, wu, wd
     # single-expert GEMM shapes M x K x N printed by EPS-MoE (K = H; N = I of one projection)
     for M, K_, N_ in ((512, 5120, 1536), (2048, 5120, 1536), (512, 5120, 14336)):
+        if not wanted(f"gemm_{M}x{K_}x{N_}"):
+            continue
         x = torch.randn(M, K_, device=dev).to(torch.bfloat16)
         g1 = (torch.randn(1, N_, K_, device=dev) * K_ ** -0.5).to(torch.bfloat16)
         u1 = (torch.randn(1, N_, K_, device=dev) * K_ ** -0.5).to(torch.bfloat16)
@@ -621,20 +682,14 @@ def vs_hipblaslt(moe, torch, np, reps=10):
     n_slots = torch.ones(1, dtype=torch.int32, device=dev)
     ws = torch.empty(moe.moe_expert_ffn_workspace_bytes(torch.bfloat16, M, H, I, 1), dtype=torch.uint8, device=dev)
     y = torch.empty(M, H, device=dev, dtype=torch.bfloat16)
-    lib = moe.lib()
     for _ in range(3):
         moe.moe_expert_ffn(x, slot_off, slot_expert, n_slots, wg, wu, wd, "swiglu", "grouped", y, ws)
     torch.cuda.synchronize()
     g1, g2 = [], []
     for _ in range(reps):
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-        for e_ in ev:
-            e_.record()
+        moe.moe_expert_ffn_profiled(x, slot_off, slot_expert, n_slots, wg, wu, wd, ev, "swiglu", "grouped", y, ws)
         torch.cuda.synchronize()
-        lib.moe_ffn_set_timing_events(*(e_.cuda_event for e_ in ev))
-        moe.moe_expert_ffn(x, slot_off, slot_expert, n_slots, wg, wu, wd, "swiglu", "grouped", y, ws)
-        torch.cuda.synchronize()
-        lib.moe_ffn_set_timing_events(None, None, None)
         g1.append(ev[0].elapsed_time(ev[1]))
         g2.append(ev[1].elapsed_time(ev[2]))
     f_gu, f_d = 2.0 * M * H * 2 * I, 2.0 * M * H * I
@@ -672,7 +727,8 @@ def main():
     import synth
 
     if a.crossover:
-        crossover(moe, synth, torch, np)
+        crossover(moe, synth, torch, np, tuple(c for c in a.cases.split(",") if c),
+                  tuple(p for p in a.paths.split(",") if p))
         return
     if a.vs_hipblaslt:
         print(json.dumps(vs_hipblaslt(moe, torch, np)), flush=True)
@@ -691,85 +747,111 @@ def main():
             print(json.dumps(predict_quality(moe, synth, torch, np, name, R)), flush=True)
         return
 
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
     cfg = synth.CONFIGS["mixtral"]
     T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
     R = a.replicas
     L, win = 3, 10
+    wts = synth.expert_weights(cfg, threads=16)
+    x_np = synth.hidden0(cfg, 0)
+    prev_logits = synth.logits(cfg, 0, 0)
+    logits_np = synth.logits(cfg, 1, 0)  # this workload has no layer-to-layer gamma term
+    cpu = None
+    if not a.no_cpu_baseline:
+        # before anything touches the GPU: the N-core leg forks worker processes
+        cpu = cpu_baseline(cfg, x_np, logits_np, wts, prev_logits, R, a.cpu_rows)
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
 
     def dev_bf16(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
-    wts = synth.expert_weights(cfg, threads=16)
     wg, wu, wd = (dev_bf16(w) for w in wts)
-    x_np = synth.hidden0(cfg, 0)
     x = dev_bf16(x_np)
-    prev_logits = synth.logits(cfg, 0, 0)
-    logits_np = synth.logits(cfg, 1, 0)  # this workload has no layer-to-layer gamma term
     logits = torch.from_numpy(logits_np).to(dev)
     prev_idx, _ = moe.moe_route(torch.from_numpy(prev_logits).to(dev), k)
-    state = torch.empty(moe.moe_stats_state_bytes(L, E, win), dtype=torch.uint8, device=dev)
-    moe.moe_stats_init(state, L, E, win)
-    bufs = {}
     stream = torch.cuda.current_stream()
+    flush = torch.empty(128 << 20, dtype=torch.float32, device=dev)   # 512 MiB > 256 MB MALL + L2s
+    spin = spin_cycles(torch, stream, 1.5)
 
-    def step(i):
-        return moe.moe_layer_forward(x, logits, k, wg, wu, wd, "swiglu", R, stats_state=state,
-                                     stats_dims=(L, E, win), layer=1, it=i, prev_topk_idx=prev_idx,
-                                     path=a.path, bufs=bufs, stream=stream)
+    def make_layer(R_):
+        state = torch.empty(moe.moe_stats_state_bytes(L, E, win), dtype=torch.uint8, device=dev)
+        moe.moe_stats_init(state, L, E, win)
+        bufs = {}
 
+        def step(i, ffn_events=None):
+            return moe.moe_layer_forward(x, logits, k, wg, wu, wd, "swiglu", R_, stats_state=state,
+                                         stats_dims=(L, E, win), layer=1, it=i, prev_topk_idx=prev_idx,
+                                         path=a.path, bufs=bufs, stream=stream, ffn_events=ffn_events)
+        return step, state, bufs
+
+    def timed_cold(step, K, first):
+        """K steps, each on flushed caches: the 512 MiB flush, then a GPU-side spin
+        while the host issues the step (so the events time the GPU, not the host's
+        argument marshalling), then the step between two events."""
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(K):
+            flush.fill_(float(i))
+            torch.cuda._sleep(spin)
+            ev[i][0].record(stream)
+            step(first + i, ffn_events=ev[i][1:4])
+            ev[i][4].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms = [ev[i][0].elapsed_time(ev[i][4]) for i in range(K)]
+        gu = [ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]
+        dn = [ev[i][2].elapsed_time(ev[i][3]) for i in range(K)]
+        return float(np.mean(ms)), float(np.mean(gu)), float(np.mean(dn)), wall
+
+    def timed_warm(step, K, first):
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for i in range(K):
+            step(first + i)
+        end.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / K
+
+    step, state, bufs = make_layer(R)
     for i in range(a.warmup):
         step(i)
     torch.cuda.synchronize()
-
-    # Timed region: exactly K steps, events on the library's stream; the fused
-    # gate/up GEMM of every step is bracketed by events the library records.
-    lib = moe.lib()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(a.steps)]
-    for trio in ev:
-        for e in trio:
-            e.record(stream)           # materialise the handles
-    torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    start.record(stream)
-    for i in range(a.steps):
-        lib.moe_ffn_set_timing_events(*(ev[i][j].cuda_event for j in range(3)))
-        step(a.warmup + i)
-    end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    lib.moe_ffn_set_timing_events(None, None, None)
-    ms_step = start.elapsed_time(end) / a.steps
-    gateup_ms = float(np.mean([ev[i][0].elapsed_time(ev[i][1]) for i in range(a.steps)]))
-    down_ms = float(np.mean([ev[i][1].elapsed_time(ev[i][2]) for i in range(a.steps)]))
+    # Timed region: exactly K steps (the headline: cold caches before every step).
+    ms_step, gateup_ms, down_ms, wall = timed_cold(step, a.steps, a.warmup)
+    ms_warm = timed_warm(step, a.steps, a.warmup + a.steps)
+    n_slots = int(bufs["disp"]["n_slots"].item())
+    # the same layer without replication
+    step0, _, bufs0 = make_layer(0)
+    for i in range(a.warmup):
+        step0(i)
+    ms_step0, gateup_ms0, _, _ = timed_cold(step0, a.steps, a.warmup)
+    ms_warm0 = timed_warm(step0, a.steps, a.warmup + a.steps)
+    same_out = bool(torch.equal(bufs0["out"], bufs["out"]))
+    del bufs0
 
     # Per-phase split (diagnostic, outside the timed region): median of 5 passes
-    # warm, then 5 cold passes, each after streaming a 512 MiB buffer through the
-    # memory system (more than the 256 MB Infinity Cache plus the L2s) so every
-    # phase starts with its inputs in HBM only.  Each pass waits behind a GPU-side
-    # spin of a few ms, so the host has issued every phase before the first one
-    # starts and the events time the kernels (and the GPU's own gaps between them),
-    # not the host's argument marshalling between launches.
+    # warm, then 5 cold passes (caches flushed first), each behind a GPU-side spin
+    # so the host has issued every phase before the first one starts.
     names = ["route", "stats", "dispatch", "expert_ffn", "combine"]
     samples = {n: [] for n in names}
     cold = {n: [] for n in names}
-    flush = torch.empty(128 << 20, dtype=torch.float32, device=dev)
-    spin = spin_cycles(torch, stream, 3.0)
+    spin3 = spin_cycles(torch, stream, 3.0)
     for rep in range(10):
         phase_ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
         if rep >= 5:
             flush.fill_(float(rep))
         torch.cuda.synchronize()
-        torch.cuda._sleep(spin)
+        torch.cuda._sleep(spin3)
         phase_ev[0].record(stream)
         idx, w = moe.moe_route(logits, k, bufs["idx"], bufs["w"], stream)
         phase_ev[1].record(stream)
         moe.moe_stats(state, L, E, win, 1, 10 ** 6 + rep, idx, prev_idx, k, bufs["counts"], bufs["p_seq"],
                       bufs["cond"], bufs["pred_next"], R, bufs["replicas"], stream)
         phase_ev[2].record(stream)
-        d = moe.moe_dispatch(x, idx, E, bufs["replicas"], E + R, bufs["disp"], bufs["ws_d"], stream)
+        d = moe.moe_dispatch(x, idx, E, bufs["replicas"], E + R, bufs["disp"], bufs["ws_d"], stream, bufs["counts"])
         phase_ev[3].record(stream)
         y = moe.moe_expert_ffn(d["x_perm"], d["slot_off"], d["slot_expert"], d["n_slots"], wg, wu, wd, "swiglu",
                                a.path, bufs["y_perm"], bufs["ws_f"], stream)
@@ -782,7 +864,6 @@ def main():
     phase_us = {n: round(float(np.median(v)), 2) for n, v in samples.items()}
     phase_us_cold = {n: round(float(np.median(v)), 2) for n, v in cold.items()}
     del flush
-    n_slots = int(d["n_slots"].item())
 
     flops, w_bytes, mem = algorithmic_layer_work(T, H, I, E, k, 3)
     M = T * k
@@ -805,27 +886,28 @@ def main():
         "data": "synthetic",
         "config": {"workload": "Mixtral-8x7B-shaped MoE layer", "T": T, "H": H, "I": I, "E": E, "k": k,
                    "act": "swiglu", "replica_budget": R, "slots_used": n_slots, "window": win,
-                   "gemm_path": a.path, "stats_chain_layers": L},
+                   "gemm_path": a.path, "stats_chain_layers": L,
+                   "timing": "cold: L2 and MALL flushed (512 MiB written) before every timed step"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "kernel": "fused gate/up grouped GEMM (SwiGLU epilogue)",
                      "kernel_ms": round(gateup_ms, 4), "flop_per_launch": gateup_flops},
         "layer_roofline_frac": round(t_roof / (ms_step * 1e-3), 4),
         "layer_roofline_ms": round(t_roof * 1e3, 4),
+        "warm": {"ms_per_step": round(ms_warm, 4), "value": round(T / (ms_warm * 1e-3), 1),
+                 "note": "K steps back to back, no flush"},
+        "replicas_off": {"replica_budget": 0, "ms_per_step": round(ms_step0, 4),
+                         "value": round(T / (ms_step0 * 1e-3), 1), "warm_ms_per_step": round(ms_warm0, 4),
+                         "gateup_ms": round(gateup_ms0, 4), "out_bit_identical_to_replicated": same_out},
         "down_gemm": {"ms": round(down_ms, 4),
                       "tflops": round(2.0 * M * I * H / (down_ms * 1e-3) / 1e12, 1)},
         "phase_us": phase_us,
         "phase_us_cold": phase_us_cold,
-        "cold_layer": {"ms": round(sum(phase_us_cold.values()) / 1e3, 4),
-                       "tokens_per_s": round(T / (sum(phase_us_cold.values()) * 1e-6), 1),
-                       "note": "sum of the per-phase medians, each phase starting with caches flushed"},
         "memory_phases": memory_phase_summary(T, H, E, k, phase_us, phase_us_cold),
         "wall_s_timed": round(wall, 3),
     }
-    if not a.no_cpu_baseline:
-        prev_np = prev_idx.cpu().numpy()
-        out["cpu_baseline"] = cpu_baseline(cfg, x_np, logits_np, wts, prev_np, a.cpu_rows)
-        out["cpu_baseline"]["cores"] = 1
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
     print(json.dumps(out))
 
 

@@ -35,6 +35,13 @@
  *   - Kernels never access memory outside the extents given, whatever the
  *     values in index arrays; out-of-range indices are skipped (results for
  *     such inputs are unspecified, but memory-safe).
+ *   - Device check.  Each of the five hot-path calls takes `check`, a device
+ *     pointer to one int32 word owned (and zeroed) by the caller, or NULL.
+ *     When it is not NULL, the call's kernels OR into it one MOE_CHECK_* bit
+ *     per kind of invalid input they meet (they still skip such entries), and
+ *     moe_check_device_error reads it back.  The word accumulates over calls
+ *     until the caller zeroes it again; calls on different streams may share
+ *     it.  With NULL no check is made.
  *   - Calls are reentrant.  Two in-flight calls must not share an output,
  *     workspace or statistics state.
  */
@@ -53,8 +60,21 @@ typedef enum {
     MOE_ERR_INVALID_ARG = -1, /* null pointer, negative size, k > E, misalignment ... */
     MOE_ERR_UNSUPPORTED = -2, /* valid but outside this build's limits (E > 256, H % 64 ...) */
     MOE_ERR_WORKSPACE = -3,   /* workspace or state smaller than the *_bytes query says */
-    MOE_ERR_HIP = -4          /* a HIP runtime call failed; moe_last_error() has its text */
+    MOE_ERR_HIP = -4,         /* a HIP runtime call failed; moe_last_error() has its text */
+    MOE_ERR_DEVICE_CHECK = -5 /* moe_check_device_error: the kernels flagged invalid input */
 } moe_status;
+
+/* Bits of the device-check word (see the conventions above). */
+enum {
+    MOE_CHECK_LOGITS = 1,     /* moe_route: a NaN or infinite router logit */
+    MOE_CHECK_INDEX = 2,      /* moe_stats, moe_dispatch: an expert index outside [0, E) */
+    MOE_CHECK_DUPLICATE = 4,  /* moe_stats, moe_dispatch: one token names the same expert twice */
+    MOE_CHECK_COUNTS = 8,     /* moe_dispatch: `counts` differs from the counts of topk_idx */
+    MOE_CHECK_REPLICAS = 16,  /* moe_dispatch: a negative replica count, or copies beyond max_slots */
+    MOE_CHECK_SLOTS = 32,     /* moe_expert_ffn: slot table not ascending inside [0, M], n_slots
+                                 outside [0, max_slots], or an expert outside [0, E) */
+    MOE_CHECK_ROWS = 64       /* moe_combine: an inv_pos entry outside [0, M) */
+};
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;       /* activations and weights */
 typedef enum { MOE_SWIGLU = 0, MOE_GELU = 1 } moe_act;
@@ -71,9 +91,10 @@ typedef enum { MOE_GEMM_AUTO = 0, MOE_GEMM_GROUPED = 1, MOE_GEMM_DENSE = 2, MOE_
  *             renormalised to sum to one (= softmax over the kept logits).
  * Limits: 1 <= E <= 256, 1 <= k <= min(E, 8), 0 <= T, T*k < 2^31.
  * Logits are expected finite; NaN is ordered as -inf (indices stay in range).
+ * check: MOE_CHECK_LOGITS for a NaN or infinite logit.
  */
 int moe_route(const float* logits, int64_t T, int E, int k, int32_t* topk_idx, float* topk_w,
-              void* stream);
+              int32_t* check, void* stream);
 
 /* ------------------------------------------------------------- statistics
  * Sliding-window routing statistics of a chain of L MoE layers ([PF] method:
@@ -114,13 +135,16 @@ int moe_route(const float* logits, int64_t T, int E, int k, int32_t* topk_idx, f
  * not written).
  * Limits: 1 <= E <= 256, 1 <= L, 1 <= window <= 1024, 0 <= layer < L,
  * iter >= 0, window * T * k * k < 2^31, 0 <= replica_budget <= 4096.
+ * check: MOE_CHECK_INDEX for an entry of topk_idx or prev_topk_idx outside
+ * [0, E) (not counted), MOE_CHECK_DUPLICATE for a token naming one expert
+ * twice in topk_idx (counted as often as named).
  */
 size_t moe_stats_state_bytes(int L, int E, int window); /* [host] */
 int moe_stats_init(void* state, size_t state_bytes, int L, int E, int window, void* stream);
 int moe_stats(void* state, size_t state_bytes, int L, int E, int window, int layer, int64_t iter,
               const int32_t* topk_idx, const int32_t* prev_topk_idx, int64_t T, int k,
               int32_t* counts, float* p_seq, float* cond, float* pred_next,
-              int replica_budget, int32_t* replicas, void* stream);
+              int replica_budget, int32_t* replicas, int32_t* check, void* stream);
 
 /*
  * moe_stats_load_state -- window variants of layer `layer` after iteration
@@ -194,7 +218,9 @@ int moe_prediction_quality(const float* pred, const int32_t* counts, int E, cons
  *   expert_off  int32 [E+1]: exclusive prefix sum of the per-expert counts;
  *               expert e owns rows [expert_off[e], expert_off[e+1]).
  *   perm_src    int32 [M]: source token of each row.  Inside an expert, rows
- *               follow ascending token index (a stable permutation).
+ *               follow ascending token index (a stable permutation: pairs
+ *               (t, i) in ascending t*k + i, so a token naming one expert
+ *               twice gets two rows, slot order).
  *   inv_pos     int32 [T, k]: the row holding (t, topk_idx[t, i]).
  *   x_perm      [M, H] in dtype `dt`: x_perm[r] = x[perm_src[r]] (byte copy).
  *   slot table  replicas[e] extra copies cut expert e's rows into
@@ -208,16 +234,27 @@ int moe_prediction_quality(const float* pred, const int32_t* counts, int E, cons
  *               means one slot per expert.  Copies beyond max_slots - E are
  *               dropped in expert order (the kernel never writes past
  *               max_slots); negative counts are taken as 0.
- *   workspace   at least moe_dispatch_workspace_bytes(T, k, E) bytes.
+ *   counts      int32 [E] (may be NULL): moe_stats' counts of this routing.
+ *               The offsets come from topk_idx itself (rows are ranked per
+ *               block of pairs, which needs the per-block counts anyway);
+ *               `counts` is only compared with them (MOE_CHECK_COUNTS).
+ *   workspace   at least moe_dispatch_workspace_bytes(T, k, E) bytes
+ *               (per-block counts and offsets, per-pair ranks); any contents.
+ * Three launches: per block of 512 (token, slot) pairs its counts and each
+ * pair's rank among the block's pairs of its expert (wave ballots); one block
+ * turning the block counts into offsets and the slot table; the row copy,
+ * which also writes perm_src and inv_pos.
+ * check: MOE_CHECK_INDEX (an index outside [0, E): inv_pos = -1, no row),
+ * MOE_CHECK_DUPLICATE, MOE_CHECK_COUNTS, MOE_CHECK_REPLICAS.
  * Limits: 1 <= E <= 256, 1 <= k <= min(E, 8), T*k < 2^31, E <= max_slots,
  * H*sizeof(dt) % 16 == 0, x and x_perm 16-byte aligned.
  */
 size_t moe_dispatch_workspace_bytes(int64_t T, int k, int E); /* [host] */
 int moe_dispatch(const void* x, moe_dtype dt, int64_t T, int H, const int32_t* topk_idx, int k, int E,
-                 const int32_t* replicas, int max_slots,
+                 const int32_t* counts, const int32_t* replicas, int max_slots,
                  void* x_perm, int32_t* perm_src, int32_t* inv_pos, int32_t* expert_off,
                  int32_t* slot_off, int32_t* slot_expert, int32_t* n_slots,
-                 void* workspace, size_t workspace_bytes, void* stream);
+                 void* workspace, size_t workspace_bytes, int32_t* check, void* stream);
 
 /* ------------------------------------------------------------- expert FFN
  * moe_expert_ffn -- every slot's rows through its expert's FFN ([EPS] section
@@ -254,35 +291,52 @@ int moe_dispatch(const void* x, moe_dtype dt, int64_t T, int H, const int32_t* t
  *         the device, no host sync).
  *   workspace  at least moe_expert_ffn_workspace_bytes(...) bytes.
  * Limits: dtype F32 or BF16; H and I multiples of 64; E <= max_slots;
- * M <= 2^31 - 1; rows referenced by slot_off lie in [0, M).
+ * M <= 2^31 - 1; rows referenced by slot_off lie in [0, M) (rows outside it
+ * are clamped away).
+ * check: MOE_CHECK_SLOTS.
  */
 size_t moe_expert_ffn_workspace_bytes(moe_dtype dt, int64_t M, int H, int I, int max_slots); /* [host] */
 int moe_expert_ffn(const void* x_perm, moe_dtype dt, int64_t M, int H, int I, int E,
                    const int32_t* slot_off, const int32_t* slot_expert, const int32_t* n_slots, int max_slots,
                    const void* w_gate, const void* w_up, const void* w_down, moe_act act, moe_gemm_path path,
-                   void* y_perm, void* workspace, size_t workspace_bytes, void* stream);
+                   void* y_perm, void* workspace, size_t workspace_bytes, int32_t* check, void* stream);
+
+/*
+ * moe_expert_ffn_profiled -- moe_expert_ffn that also records three caller-owned
+ * hipEvent_t handles (passed as void*) on `stream`: events[0] right before the
+ * gate/up (W1) GEMM launch, events[1] right after it and events[2] right after
+ * the down (W2) GEMM, so a profiler can time the two launches on the library's
+ * own stream.  events must hold three valid events.  Same results as
+ * moe_expert_ffn.
+ */
+int moe_expert_ffn_profiled(const void* x_perm, moe_dtype dt, int64_t M, int H, int I, int E,
+                            const int32_t* slot_off, const int32_t* slot_expert, const int32_t* n_slots,
+                            int max_slots, const void* w_gate, const void* w_up, const void* w_down, moe_act act,
+                            moe_gemm_path path, void* y_perm, void* workspace, size_t workspace_bytes,
+                            int32_t* check, void* const* events, void* stream);
 
 /* ---------------------------------------------------------------- combine
  * moe_combine -- weighted combine back to token order ([EPS] section 3: the
  * LocalReduce that follows the expert computation):
  *   out[t] = sum_{i<k} topk_w[t, i] * y_perm[inv_pos[t, i]]
  * accumulated in fp32 in slot order i = 0..k-1, rounded once to dtype.
- * inv_pos entries outside [0, M) contribute nothing.
+ * inv_pos entries outside [0, M) contribute nothing (MOE_CHECK_ROWS).
  * Limits: 1 <= k <= 8, H*sizeof(dt) % 16 == 0, y_perm and out 16-byte aligned.
  */
 int moe_combine(const void* y_perm, moe_dtype dt, int64_t M, const int32_t* inv_pos, const float* topk_w,
-                int64_t T, int k, int H, void* out, void* stream);
+                int64_t T, int k, int H, void* out, int32_t* check, void* stream);
 
-/* -------------------------------------------------------------- profiling
- * moe_ffn_set_timing_events -- measures the GEMM launches inside
- * moe_expert_ffn.  While set (per calling thread), every moe_expert_ffn call
- * records `before_gateup` on its stream right before the gate/up (W1) GEMM,
- * `after_gateup` right after it, and `after_down` right after the down (W2)
- * GEMM.  The three hipEvent_t handles (passed as void*) are created and owned
- * by the caller; all three NULL stops the recording.  Either all three are
- * NULL or none is (MOE_ERR_INVALID_ARG otherwise).
+/* ----------------------------------------------------------- device check
+ * moe_check_device_error -- waits for `stream`, then reads the device-check
+ * word `check` (see the conventions above).  Returns MOE_OK if it is zero,
+ * else MOE_ERR_DEVICE_CHECK with the flagged kinds named in moe_last_error().
+ * bits [host] (may be NULL) receives the word.  The word is left as it is.
+ * The stated source of the preconditions: softmax routing over finite logits
+ * ("Fast MoE Inference via Predictive Prefetching and Expert Replication",
+ * problem statement) picking k distinct experts per token ([PF] observations:
+ * the top-k gate).
  */
-int moe_ffn_set_timing_events(void* before_gateup, void* after_gateup, void* after_down);
+int moe_check_device_error(const int32_t* check, int32_t* bits, void* stream);
 
 /* ----------------------------------------------------------------- backward
  * moe_backward -- gradients of the layer w.r.t. its tokens, router logits and

@@ -13,6 +13,11 @@ call fails, an exception is raised.
     d      = moe_dispatch(x, idx, E, replicas, max_slots)
     y_perm = moe_expert_ffn(d["x_perm"], d["slot_off"], ..., w_gate, w_up, w_down)
     out    = moe_combine(y_perm, d["inv_pos"], w)
+
+Every hot-path call takes `check`: an int32 device tensor of one element
+(zeroed by the caller) that the kernels flag invalid input into;
+moe_check_device_error(check) reads it back.  Output tensors passed in by the
+caller are checked for shape, dtype and device before anything is launched.
 """
 from __future__ import annotations
 
@@ -26,7 +31,8 @@ __all__ = ["moe_route", "moe_stats_state_bytes", "moe_stats_init", "moe_stats", 
            "moe_plan_replicas",
            "moe_prediction_quality", "moe_dispatch_workspace_bytes",
            "moe_dispatch", "moe_expert_ffn_workspace_bytes", "moe_expert_ffn", "moe_combine", "moe_layer_forward",
-           "moe_layer_forward_pipelined", "moe_backward_workspace_bytes", "moe_backward",
+           "moe_layer_forward_pipelined", "moe_backward_workspace_bytes", "moe_backward", "moe_check_device_error",
+           "moe_expert_ffn_profiled", "new_check_word", "CHECK_BITS",
            "MoEError", "LIB_PATH", "MOE_F32", "MOE_BF16", "SWIGLU", "GELU", "GEMM_AUTO", "GEMM_GROUPED",
            "GEMM_DENSE", "GEMM_GROUPED_SMALL"]
 
@@ -34,6 +40,8 @@ MOE_F32, MOE_BF16 = 0, 1
 SWIGLU, GELU = 0, 1
 GEMM_AUTO, GEMM_GROUPED, GEMM_DENSE, GEMM_GROUPED_SMALL = 0, 1, 2, 3
 _ACT = {"swiglu": SWIGLU, "gelu": GELU, SWIGLU: SWIGLU, GELU: GELU}
+# bits of the device-check word (include/moe.h MOE_CHECK_*)
+CHECK_BITS = {"logits": 1, "index": 2, "duplicate": 4, "counts": 8, "replicas": 16, "slots": 32, "rows": 64}
 _PATH = {"auto": GEMM_AUTO, "grouped": GEMM_GROUPED, "dense": GEMM_DENSE, "grouped_small": GEMM_GROUPED_SMALL,
          GEMM_AUTO: GEMM_AUTO, GEMM_GROUPED: GEMM_GROUPED, GEMM_DENSE: GEMM_DENSE,
          GEMM_GROUPED_SMALL: GEMM_GROUPED_SMALL}
@@ -75,15 +83,54 @@ def _i32(n, dev):
     return torch.empty(n, dtype=torch.int32, device=dev)
 
 
+def _out(t, shape, dtype, dev, name):
+    """A caller-supplied (or cached) output must match what the kernels will
+    write: the same shape, dtype and device (the kernels bound-check only against
+    the sizes taken from the inputs).  None: allocate one."""
+    shape = tuple(int(v) for v in shape)
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=dev)
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch tensor")
+    if tuple(t.shape) != shape or t.dtype != dtype or t.device != torch.device(dev):
+        raise ValueError(f"{name}: expected {dtype} {shape} on {dev}, got {t.dtype} {tuple(t.shape)} on {t.device}")
+    return t
+
+
+def _bytes_of(t, need, name):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or t.numel() * t.element_size() < need:
+        have = t.numel() * t.element_size() if isinstance(t, torch.Tensor) else None
+        raise ValueError(f"{name}: needs {need} bytes, got {have}")
+    return t
+
+
+def new_check_word(device="cuda"):
+    """A zeroed device-check word (int32 [1]) for the `check` argument."""
+    return torch.zeros(1, dtype=torch.int32, device=device)
+
+
+def moe_check_device_error(check: torch.Tensor, stream=None) -> int:
+    """Waits for the stream and reads the check word: returns 0 if nothing was
+    flagged, else raises MoEError naming the flagged kinds (status -5)."""
+    bits = ctypes.c_int32(0)
+    rc = lib().moe_check_device_error(_ptr(check), ctypes.byref(bits), _stream(stream))
+    if rc != 0:
+        raise MoEError("moe_check_device_error", rc, lib().moe_last_error().decode(errors="replace"))
+    return bits.value
+
+
 # ------------------------------------------------------------------ routing
-def moe_route(logits: torch.Tensor, k: int, topk_idx=None, topk_w=None, stream=None):
+def moe_route(logits: torch.Tensor, k: int, topk_idx=None, topk_w=None, stream=None, check=None):
     T, E = logits.shape
     if logits.dtype != torch.float32:
         raise TypeError("router logits must be float32")
     dev = logits.device
-    topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev) if topk_idx is None else topk_idx
-    topk_w = torch.empty((T, k), dtype=torch.float32, device=dev) if topk_w is None else topk_w
-    _call("moe_route", _ptr(logits), ctypes.c_int64(T), E, k, _ptr(topk_idx), _ptr(topk_w), _stream(stream))
+    topk_idx = _out(topk_idx, (T, k), torch.int32, dev, "topk_idx")
+    topk_w = _out(topk_w, (T, k), torch.float32, dev, "topk_w")
+    _call("moe_route", _ptr(logits), ctypes.c_int64(T), E, k, _ptr(topk_idx), _ptr(topk_w), _ptr(check),
+          _stream(stream))
     return topk_idx, topk_w
 
 
@@ -99,13 +146,23 @@ def moe_stats_init(state: torch.Tensor, L: int, E: int, window: int, stream=None
 
 def moe_stats(state: torch.Tensor, L: int, E: int, window: int, layer: int, it: int, topk_idx=None,
               prev_topk_idx=None, k: int = 0, counts=None, p_seq=None, cond=None, pred_next=None,
-              replica_budget: int = 0, replicas=None, stream=None):
+              replica_budget: int = 0, replicas=None, stream=None, check=None):
+    """Outputs are optional (None: not written); those given must be int32/float32
+    tensors of E (cond: E x E) elements."""
     T = 0 if topk_idx is None else topk_idx.shape[0]
     if topk_idx is not None:
         k = topk_idx.shape[1]
+        if prev_topk_idx is not None and tuple(prev_topk_idx.shape) != tuple(topk_idx.shape):
+            raise ValueError("prev_topk_idx must have the shape of topk_idx")
+    dev = state.device
+    for t, n, dt, name in ((counts, E, torch.int32, "counts"), (p_seq, E, torch.float32, "p_seq"),
+                           (cond, E * E, torch.float32, "cond"), (pred_next, E, torch.float32, "pred_next"),
+                           (replicas, E, torch.int32, "replicas")):
+        if t is not None and (t.numel() != n or t.dtype != dt or t.device != dev):
+            raise ValueError(f"{name}: expected {n} elements of {dt} on {dev}")
     _call("moe_stats", _ptr(state), ctypes.c_size_t(state.numel() * state.element_size()), L, E, window, layer,
           ctypes.c_int64(it), _ptr(topk_idx), _ptr(prev_topk_idx), ctypes.c_int64(T), k, _ptr(counts), _ptr(p_seq),
-          _ptr(cond), _ptr(pred_next), replica_budget, _ptr(replicas), _stream(stream))
+          _ptr(cond), _ptr(pred_next), replica_budget, _ptr(replicas), _ptr(check), _stream(stream))
     return dict(counts=counts, p_seq=p_seq, cond=cond, pred_next=pred_next, replicas=replicas)
 
 
@@ -154,27 +211,37 @@ def moe_dispatch_workspace_bytes(T: int, k: int, E: int) -> int:
     return int(lib().moe_dispatch_workspace_bytes(ctypes.c_int64(T), k, E))
 
 
-def moe_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, E: int, replicas=None, max_slots=None, out=None,
-                 workspace=None, stream=None):
-    T, H = x.shape
-    k = topk_idx.shape[1]
+def _dispatch_outputs(out, T, k, H, E, max_slots, dtype, dev):
+    o = dict(out or {})
     M = T * k
+    for key, shape, dt in (("x_perm", (M, H), dtype), ("perm_src", (M,), torch.int32), ("inv_pos", (T, k), torch.int32),
+                           ("expert_off", (E + 1,), torch.int32), ("slot_off", (max_slots + 1,), torch.int32),
+                           ("slot_expert", (max_slots,), torch.int32), ("n_slots", (1,), torch.int32)):
+        o[key] = _out(o.get(key), shape, dt, dev, key)
+    return o
+
+
+def moe_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, E: int, replicas=None, max_slots=None, out=None,
+                 workspace=None, stream=None, counts=None, check=None):
+    """counts (int32 [E], e.g. moe_stats' counts of this routing) is only compared
+    with the routing when `check` is given."""
+    T, H = x.shape
+    if topk_idx.shape[0] != T or topk_idx.dtype != torch.int32:
+        raise ValueError("topk_idx must be int32 [T, k] for the T rows of x")
+    k = topk_idx.shape[1]
     dev = x.device
     max_slots = E if max_slots is None else max_slots
-    o = dict(out or {})
-    o.setdefault("x_perm", torch.empty((M, H), dtype=x.dtype, device=dev))
-    o.setdefault("perm_src", _i32(M, dev))
-    o.setdefault("inv_pos", torch.empty((T, k), dtype=torch.int32, device=dev))
-    o.setdefault("expert_off", _i32(E + 1, dev))
-    o.setdefault("slot_off", _i32(max_slots + 1, dev))
-    o.setdefault("slot_expert", _i32(max_slots, dev))
-    o.setdefault("n_slots", _i32(1, dev))
-    if workspace is None:
-        workspace = torch.empty(moe_dispatch_workspace_bytes(T, k, E), dtype=torch.uint8, device=dev)
-    _call("moe_dispatch", _ptr(x), _dtype_code(x), ctypes.c_int64(T), H, _ptr(topk_idx), k, E, _ptr(replicas),
-          max_slots, _ptr(o["x_perm"]), _ptr(o["perm_src"]), _ptr(o["inv_pos"]), _ptr(o["expert_off"]),
-          _ptr(o["slot_off"]), _ptr(o["slot_expert"]), _ptr(o["n_slots"]), _ptr(workspace),
-          ctypes.c_size_t(workspace.numel()), _stream(stream))
+    for t, name in ((replicas, "replicas"), (counts, "counts")):
+        if t is not None and (t.numel() != E or t.dtype != torch.int32):
+            raise ValueError(f"{name} must be int32 [E]")
+    o = _dispatch_outputs(out, T, k, H, E, max_slots, x.dtype, dev)
+    need = moe_dispatch_workspace_bytes(T, k, E)
+    workspace = torch.empty(need, dtype=torch.uint8, device=dev) if workspace is None else \
+        _bytes_of(workspace, need, "dispatch workspace")
+    _call("moe_dispatch", _ptr(x), _dtype_code(x), ctypes.c_int64(T), H, _ptr(topk_idx), k, E, _ptr(counts),
+          _ptr(replicas), max_slots, _ptr(o["x_perm"]), _ptr(o["perm_src"]), _ptr(o["inv_pos"]),
+          _ptr(o["expert_off"]), _ptr(o["slot_off"]), _ptr(o["slot_expert"]), _ptr(o["n_slots"]), _ptr(workspace),
+          ctypes.c_size_t(workspace.numel() * workspace.element_size()), _ptr(check), _stream(stream))
     return o
 
 
@@ -184,28 +251,59 @@ def moe_expert_ffn_workspace_bytes(dtype, M: int, H: int, I: int, max_slots: int
     return int(lib().moe_expert_ffn_workspace_bytes(code, ctypes.c_int64(M), H, I, max_slots))
 
 
-def moe_expert_ffn(x_perm: torch.Tensor, slot_off, slot_expert, n_slots, w_gate, w_up, w_down, act="swiglu",
-                   path="grouped", y_perm=None, workspace=None, stream=None):
+def _ffn_args(x_perm, slot_off, slot_expert, n_slots, w_gate, w_up, w_down, y_perm, workspace):
     M, H = x_perm.shape
-    E, I, _ = w_gate.shape
+    E, I, H_ = w_gate.shape
+    if H_ != H or tuple(w_down.shape) != (E, H, I) or (w_up is not None and tuple(w_up.shape) != (E, I, H)):
+        raise ValueError("expert weights must be [E, I, H] (gate, up) and [E, H, I] (down) for x_perm's H")
+    for w in (w_gate, w_up, w_down):
+        if w is not None and w.dtype != x_perm.dtype:
+            raise TypeError("expert weights must have the activation dtype")
     max_slots = slot_expert.numel()
-    y_perm = torch.empty_like(x_perm) if y_perm is None else y_perm
-    if workspace is None:
-        workspace = torch.empty(moe_expert_ffn_workspace_bytes(x_perm.dtype, M, H, I, max_slots), dtype=torch.uint8,
-                                device=x_perm.device)
+    if slot_off.numel() != max_slots + 1 or n_slots.numel() != 1:
+        raise ValueError("slot_off must hold max_slots + 1 entries and n_slots one")
+    y_perm = _out(y_perm, (M, H), x_perm.dtype, x_perm.device, "y_perm")
+    need = moe_expert_ffn_workspace_bytes(x_perm.dtype, M, H, I, max_slots)
+    workspace = torch.empty(need, dtype=torch.uint8, device=x_perm.device) if workspace is None else \
+        _bytes_of(workspace, need, "FFN workspace")
+    return M, H, I, E, max_slots, y_perm, workspace
+
+
+def moe_expert_ffn(x_perm: torch.Tensor, slot_off, slot_expert, n_slots, w_gate, w_up, w_down, act="swiglu",
+                   path="grouped", y_perm=None, workspace=None, stream=None, check=None):
+    M, H, I, E, max_slots, y_perm, workspace = _ffn_args(x_perm, slot_off, slot_expert, n_slots, w_gate, w_up,
+                                                         w_down, y_perm, workspace)
     _call("moe_expert_ffn", _ptr(x_perm), _dtype_code(x_perm), ctypes.c_int64(M), H, I, E, _ptr(slot_off),
           _ptr(slot_expert), _ptr(n_slots), max_slots, _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ACT[act],
-          _PATH[path], _ptr(y_perm), _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream(stream))
+          _PATH[path], _ptr(y_perm), _ptr(workspace), ctypes.c_size_t(workspace.numel() * workspace.element_size()),
+          _ptr(check), _stream(stream))
+    return y_perm
+
+
+def moe_expert_ffn_profiled(x_perm: torch.Tensor, slot_off, slot_expert, n_slots, w_gate, w_up, w_down, events,
+                            act="swiglu", path="grouped", y_perm=None, workspace=None, stream=None, check=None):
+    """moe_expert_ffn recording three torch.cuda.Event objects on the stream: before
+    the gate/up GEMM, after it, after the down GEMM."""
+    M, H, I, E, max_slots, y_perm, workspace = _ffn_args(x_perm, slot_off, slot_expert, n_slots, w_gate, w_up,
+                                                         w_down, y_perm, workspace)
+    evs = (ctypes.c_void_p * 3)(*(e.cuda_event for e in events))
+    _call("moe_expert_ffn_profiled", _ptr(x_perm), _dtype_code(x_perm), ctypes.c_int64(M), H, I, E, _ptr(slot_off),
+          _ptr(slot_expert), _ptr(n_slots), max_slots, _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ACT[act],
+          _PATH[path], _ptr(y_perm), _ptr(workspace), ctypes.c_size_t(workspace.numel() * workspace.element_size()),
+          _ptr(check), evs, _stream(stream))
     return y_perm
 
 
 # ---------------------------------------------------------------- combine
-def moe_combine(y_perm: torch.Tensor, inv_pos: torch.Tensor, topk_w: torch.Tensor, out=None, stream=None):
+def moe_combine(y_perm: torch.Tensor, inv_pos: torch.Tensor, topk_w: torch.Tensor, out=None, stream=None,
+                check=None):
     M, H = y_perm.shape
     T, k = topk_w.shape
-    out = torch.empty((T, H), dtype=y_perm.dtype, device=y_perm.device) if out is None else out
+    if inv_pos.numel() != T * k or inv_pos.dtype != torch.int32 or topk_w.dtype != torch.float32:
+        raise ValueError("inv_pos must be int32 [T, k] and topk_w float32 [T, k]")
+    out = _out(out, (T, H), y_perm.dtype, y_perm.device, "out")
     _call("moe_combine", _ptr(y_perm), _dtype_code(y_perm), ctypes.c_int64(M), _ptr(inv_pos), _ptr(topk_w),
-          ctypes.c_int64(T), k, H, _ptr(out), _stream(stream))
+          ctypes.c_int64(T), k, H, _ptr(out), _ptr(check), _stream(stream))
     return out
 
 
@@ -224,27 +322,30 @@ def moe_backward(x_perm, y_perm, topk_idx, topk_w, inv_pos, expert_off, w_gate, 
     M, H = x_perm.shape
     E, I, _ = w_gate.shape
     dev = x_perm.device
+    if M != T * k or tuple(y_perm.shape) != (M, H) or tuple(d_out.shape) != (T, H) or d_out.dtype != x_perm.dtype:
+        raise ValueError("x_perm and y_perm must be [T*k, H] and d_out [T, H] of the activation dtype")
     o = dict(out or {})
-    o.setdefault("d_x", torch.empty((T, H), dtype=x_perm.dtype, device=dev))
-    o.setdefault("d_logits", torch.empty((T, E), dtype=torch.float32, device=dev))
-    o.setdefault("d_w_gate", torch.empty_like(w_gate))
+    o["d_x"] = _out(o.get("d_x"), (T, H), x_perm.dtype, dev, "d_x")
+    o["d_logits"] = _out(o.get("d_logits"), (T, E), torch.float32, dev, "d_logits")
+    o["d_w_gate"] = _out(o.get("d_w_gate"), tuple(w_gate.shape), w_gate.dtype, dev, "d_w_gate")
     if w_up is not None:
-        o.setdefault("d_w_up", torch.empty_like(w_up))
-    o.setdefault("d_w_down", torch.empty_like(w_down))
-    if workspace is None:
-        workspace = torch.empty(moe_backward_workspace_bytes(x_perm.dtype, T, k, H, I, E, act), dtype=torch.uint8,
-                                device=dev)
+        o["d_w_up"] = _out(o.get("d_w_up"), tuple(w_up.shape), w_up.dtype, dev, "d_w_up")
+    o["d_w_down"] = _out(o.get("d_w_down"), tuple(w_down.shape), w_down.dtype, dev, "d_w_down")
+    need = moe_backward_workspace_bytes(x_perm.dtype, T, k, H, I, E, act)
+    workspace = torch.empty(need, dtype=torch.uint8, device=dev) if workspace is None else \
+        _bytes_of(workspace, need, "backward workspace")
     _call("moe_backward", _ptr(x_perm), _ptr(y_perm), _dtype_code(x_perm), ctypes.c_int64(T), k, H, I, E,
           _ptr(topk_idx), _ptr(topk_w), _ptr(inv_pos), _ptr(expert_off), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
           _ACT[act], _ptr(d_out), _ptr(o["d_x"]), _ptr(o["d_logits"]), _ptr(o["d_w_gate"]), _ptr(o.get("d_w_up")),
-          _ptr(o["d_w_down"]), _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream(stream))
+          _ptr(o["d_w_down"]), _ptr(workspace), ctypes.c_size_t(workspace.numel() * workspace.element_size()),
+          _stream(stream))
     return o
 
 
 # ------------------------------------------------------ one layer, composed
 def moe_layer_forward(x, logits, k, w_gate, w_up, w_down, act="swiglu", replica_budget=0, stats_state=None,
                       stats_dims=None, layer=0, it=0, prev_topk_idx=None, path="grouped", bufs=None, stream=None,
-                      planned_replicas=None):
+                      planned_replicas=None, check=None, ffn_events=None):
     """route -> stats (+ replicas) -> dispatch -> FFN -> combine, all on `stream`.
 
     stats_state/stats_dims=(L, E, window) enable the windowed statistics; the
@@ -252,14 +353,24 @@ def moe_layer_forward(x, logits, k, w_gate, w_up, w_down, act="swiglu", replica_
     planned_replicas (int32 [E], e.g. from moe_plan_replicas on the previous
     layer's prediction) replaces that count-based plan; it must hand out at
     most replica_budget copies.  `bufs` (a dict) caches outputs and workspaces
-    between calls."""
+    between calls; they are reallocated when the shapes change.  `check`: the
+    device-check word passed to all five calls.  ffn_events: three
+    torch.cuda.Event objects recorded around the two GEMM launches
+    (moe_expert_ffn_profiled)."""
     T, E = logits.shape
+    H = x.shape[1]
+    I = w_gate.shape[1]
     dev = x.device
+    max_slots = E + replica_budget
     b = bufs if bufs is not None else {}
-    idx, w = moe_route(logits, k, b.get("idx"), b.get("w"), stream)
+    key = (T, k, E, H, I, max_slots, x.dtype, str(dev))
+    if b.get("_key") != key:
+        b.clear()
+        b["_key"] = key
+    idx, w = moe_route(logits, k, b.get("idx"), b.get("w"), stream, check)
     b["idx"], b["w"] = idx, w
     res = {"idx": idx, "w": w}
-    replicas = None
+    replicas, counts = None, None
     if stats_state is not None or replica_budget > 0:
         if stats_state is None:
             stats_dims = (1, E, 1)
@@ -269,34 +380,38 @@ def moe_layer_forward(x, logits, k, w_gate, w_up, w_down, act="swiglu", replica_
                 moe_stats_init(stats_state, *stats_dims, stream=stream)
                 b["_state"] = stats_state
         L_, E_, win = stats_dims
-        for key, n, dt in (("counts", E, torch.int32), ("p_seq", E, torch.float32), ("replicas", E, torch.int32)):
-            if key not in b:
-                b[key] = torch.empty(n, dtype=dt, device=dev)
+        for name, n, dt in (("counts", E, torch.int32), ("p_seq", E, torch.float32), ("replicas", E, torch.int32)):
+            if name not in b:
+                b[name] = torch.empty(n, dtype=dt, device=dev)
         if layer + 1 < L_:
             b.setdefault("cond", torch.empty((E, E), dtype=torch.float32, device=dev))
             b.setdefault("pred_next", torch.empty(E, dtype=torch.float32, device=dev))
         st = moe_stats(stats_state, L_, E_, win, layer, it, idx, prev_topk_idx, k, b["counts"], b["p_seq"],
                        b.get("cond") if layer + 1 < L_ else None, b.get("pred_next") if layer + 1 < L_ else None,
                        replica_budget, b["replicas"] if replica_budget > 0 and planned_replicas is None else None,
-                       stream)
+                       stream, check)
         res.update({kk: v for kk, v in st.items() if v is not None})
         replicas = b["replicas"] if replica_budget > 0 else None
+        counts = b["counts"]
     if planned_replicas is not None:
         replicas = planned_replicas
         res["replicas"] = planned_replicas
-    max_slots = E + replica_budget
     if "ws_d" not in b:
         b["ws_d"] = torch.empty(moe_dispatch_workspace_bytes(T, k, E), dtype=torch.uint8, device=dev)
-    d = moe_dispatch(x, idx, E, replicas, max_slots, b.get("disp"), b["ws_d"], stream)
+    d = moe_dispatch(x, idx, E, replicas, max_slots, b.get("disp"), b["ws_d"], stream, counts, check)
     b["disp"] = d
     if "y_perm" not in b:
         b["y_perm"] = torch.empty_like(d["x_perm"])
     if "ws_f" not in b:
-        b["ws_f"] = torch.empty(moe_expert_ffn_workspace_bytes(x.dtype, T * k, x.shape[1], w_gate.shape[1], max_slots),
-                                dtype=torch.uint8, device=dev)
-    y = moe_expert_ffn(d["x_perm"], d["slot_off"], d["slot_expert"], d["n_slots"], w_gate, w_up, w_down, act, path,
-                       b["y_perm"], b["ws_f"], stream)
-    out = moe_combine(y, d["inv_pos"], w, b.get("out"), stream)
+        b["ws_f"] = torch.empty(moe_expert_ffn_workspace_bytes(x.dtype, T * k, H, I, max_slots), dtype=torch.uint8,
+                                device=dev)
+    if ffn_events is None:
+        y = moe_expert_ffn(d["x_perm"], d["slot_off"], d["slot_expert"], d["n_slots"], w_gate, w_up, w_down, act,
+                           path, b["y_perm"], b["ws_f"], stream, check)
+    else:
+        y = moe_expert_ffn_profiled(d["x_perm"], d["slot_off"], d["slot_expert"], d["n_slots"], w_gate, w_up, w_down,
+                                    ffn_events, act, path, b["y_perm"], b["ws_f"], stream, check)
+    out = moe_combine(y, d["inv_pos"], w, b.get("out"), stream, check)
     b["out"] = out
     res.update(d)
     res.update(y_perm=y, out=out)
@@ -342,11 +457,12 @@ def moe_layer_forward_pipelined(x, logits, k, w_gate, w_up, w_down, act="swiglu"
         b["ws_f"] = torch.empty(moe_expert_ffn_workspace_bytes(x.dtype, t_max * k, H, I, E), dtype=torch.uint8,
                                 device=dev)
         b["_ws_key"] = (t_max, k, E, H, I, x.dtype)
-        for c in range(n_chunks):
-            b.pop(("chunk", c), None)
     disp, done_d = {}, {}
     for c, t0, t1 in chunks:
         cb = b.setdefault(("chunk", c), {})
+        if cb.get("_key") != (t1 - t0, k, E, H, x.dtype):   # per-chunk buffers keyed on the chunk's own T
+            cb.clear()
+            cb["_key"] = (t1 - t0, k, E, H, x.dtype)
         disp[c] = moe_dispatch(x[t0:t1], idx[t0:t1], E, None, E, cb.get("disp"), b["ws_d"], ms)
         cb["disp"] = disp[c]
         done_d[c] = torch.cuda.Event()

@@ -9,22 +9,24 @@ _lib = None
 
 _p, _i, _i64, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
 SIGNATURES = {
-    "moe_route": (_i, [_p, _i64, _i, _i, _p, _p, _p]),
+    "moe_route": (_i, [_p, _i64, _i, _i, _p, _p, _p, _p]),
     "moe_stats_state_bytes": (_sz, [_i, _i, _i]),
     "moe_stats_init": (_i, [_p, _sz, _i, _i, _i, _p]),
-    "moe_stats": (_i, [_p, _sz, _i, _i, _i, _i, _i64, _p, _p, _i64, _i, _p, _p, _p, _p, _i, _p, _p]),
+    "moe_stats": (_i, [_p, _sz, _i, _i, _i, _i, _i64, _p, _p, _i64, _i, _p, _p, _p, _p, _i, _p, _p, _p]),
     "moe_stats_load_state": (_i, [_p, _sz, _i, _i, _i, _i, _i64, ctypes.c_double, _p, _p, _p, _p]),
     "moe_plan_replicas": (_i, [_p, _i, _i64, _i, _p, _p, _p]),
     "moe_prediction_quality": (_i, [_p, _p, _i, _p, _i, _p, _p]),
     "moe_dispatch_workspace_bytes": (_sz, [_i64, _i, _i]),
-    "moe_dispatch": (_i, [_p, _i, _i64, _i, _p, _i, _i, _p, _i, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
+    "moe_dispatch": (_i, [_p, _i, _i64, _i, _p, _i, _i, _p, _p, _i, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p, _p]),
     "moe_expert_ffn_workspace_bytes": (_sz, [_i, _i64, _i, _i, _i]),
-    "moe_expert_ffn": (_i, [_p, _i, _i64, _i, _i, _i, _p, _p, _p, _i, _p, _p, _p, _i, _i, _p, _p, _sz, _p]),
-    "moe_combine": (_i, [_p, _i, _i64, _p, _p, _i64, _i, _i, _p, _p]),
+    "moe_expert_ffn": (_i, [_p, _i, _i64, _i, _i, _i, _p, _p, _p, _i, _p, _p, _p, _i, _i, _p, _p, _sz, _p, _p]),
+    "moe_expert_ffn_profiled": (_i, [_p, _i, _i64, _i, _i, _i, _p, _p, _p, _i, _p, _p, _p, _i, _i, _p, _p, _sz, _p,
+                                     _p, _p]),
+    "moe_combine": (_i, [_p, _i, _i64, _p, _p, _i64, _i, _i, _p, _p, _p]),
     "moe_backward_workspace_bytes": (_sz, [_i, _i64, _i, _i, _i, _i, _i]),
     "moe_backward": (_i, [_p, _p, _i, _i64, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _i, _p, _p, _p, _p, _p, _p,
                           _p, _sz, _p]),
-    "moe_ffn_set_timing_events": (_i, [_p, _p, _p]),
+    "moe_check_device_error": (_i, [_p, _p, _p]),
     "moe_status_string": (ctypes.c_char_p, [_i]),
     "moe_last_error": (ctypes.c_char_p, []),
 }

@@ -295,8 +295,8 @@ int run_backward(const void* x_perm, const void* y_perm, int64_t n_tok, int k, i
 
   bwd_setup_kernel<<<static_cast<unsigned>(std::min<int64_t>(1024, ceil_div(M, 256)) + 1), 256, 0, s>>>(
       expert_off, E, M, L.ld, seg, slot_expert, n_slots, ones, M);
-  tiles_kernel<<<1, 256, 0, s>>>(expert_off, slot_expert, n_slots, E, M, kCover, 256, 0, 0, L.tiles_cap, tab_slot,
-                                 tab_row0, tab_rend, n_tiles, TileSplit{});
+  tiles_kernel<<<1, 256, 0, s>>>(expert_off, slot_expert, n_slots, E, M, E, kCover, 256, 0, 0, L.tiles_cap, tab_slot,
+                                 tab_row0, tab_rend, n_tiles, TileSplit{}, nullptr);
   if (int rc = check("moe_backward setup")) return rc;
 
   // 1. gate + combine transpose
@@ -390,7 +390,7 @@ int run_backward(const void* x_perm, const void* y_perm, int64_t n_tok, int k, i
   if (int rc = check("moe_backward d_x_perm")) return rc;
 
   // 6. d_x[t] = sum of the token's k rows
-  if (int rc = moe_combine(dy, kBf16 ? MOE_BF16 : MOE_F32, M, inv_pos, ones, n_tok, k, H, d_x, s)) return rc;
+  if (int rc = moe_combine(dy, kBf16 ? MOE_BF16 : MOE_F32, M, inv_pos, ones, n_tok, k, H, d_x, nullptr, s)) return rc;
 
   // 7. d_Wg | d_Wu (or d_W1) = sum over each expert's rows of [d_g | d_u]^T x_perm
   transpose_padded_kernel<kBf16><<<dim3(ceil_div(nI, 64), ldb), 256, 0, s>>>(dgu, M, nI, expert_off, seg, E,

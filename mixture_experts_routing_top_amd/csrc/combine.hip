@@ -7,7 +7,8 @@
 // Four 16-byte chunks of one output row per thread (strided so a wave's
 // accesses stay contiguous): k gathers each from the expert-ordered rows, fp32
 // FMAs in slot order, one rounding to the dtype, 16-byte stores.  HBM-bound:
-// (k + 1) * H * s bytes per token.
+// (k + 1) * H * s bytes per token.  With a check word, an inv_pos entry
+// outside [0, M) (skipped) raises MOE_CHECK_ROWS.
 #include "common.h"
 
 namespace {
@@ -21,9 +22,18 @@ template <bool kBf16>
 __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ y, int64_t M,
                                                       const int32_t* __restrict__ inv_pos,
                                                       const float* __restrict__ w, int64_t T, int k, int chunks,
-                                                      uint4* __restrict__ out) {
+                                                      uint4* __restrict__ out, int32_t* __restrict__ check) {
   const int groups = (chunks + kChunksPerThread - 1) / kChunksPerThread;  // threads per token
   const int64_t g = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (check) {  // one thread per token looks at its k rows (before any lane leaves)
+    bool bad = false;
+    if (g < T * groups && g % groups == 0)
+      for (int i = 0; i < k; ++i) {
+        const int32_t r = inv_pos[(g / groups) * k + i];
+        bad |= r < 0 || r >= M;
+      }
+    raise_check(check, bad, MOE_CHECK_ROWS);
+  }
   if (g >= T * groups) return;
   const int64_t t = g / groups;
   const int c0 = static_cast<int>(g - t * groups);
@@ -83,7 +93,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
 }  // namespace
 
 extern "C" int moe_combine(const void* y_perm, moe_dtype dt, int64_t M, const int32_t* inv_pos, const float* topk_w,
-                           int64_t T, int k, int H, void* out, void* stream) {
+                           int64_t T, int k, int H, void* out, int32_t* check, void* stream) {
   using namespace moe;
   if (dt != MOE_F32 && dt != MOE_BF16) return fail(MOE_ERR_INVALID_ARG, "moe_combine: unknown dtype %d", (int)dt);
   if (k < 1 || k > kMaxTopK) return fail(MOE_ERR_INVALID_ARG, "moe_combine: k=%d outside [1, 8]", k);
@@ -100,9 +110,9 @@ extern "C" int moe_combine(const void* y_perm, moe_dtype dt, int64_t M, const in
   const hipStream_t s = as_stream(stream);
   if (dt == MOE_BF16)
     combine_kernel<true><<<blocks, 256, 0, s>>>(static_cast<const uint4*>(y_perm), M, inv_pos, topk_w, T, k, chunks,
-                                               static_cast<uint4*>(out));
+                                               static_cast<uint4*>(out), check);
   else
     combine_kernel<false><<<blocks, 256, 0, s>>>(static_cast<const uint4*>(y_perm), M, inv_pos, topk_w, T, k, chunks,
-                                                static_cast<uint4*>(out));
+                                                static_cast<uint4*>(out), check);
   return hip_status(hipGetLastError(), "moe_combine launch");
 }

@@ -27,6 +27,15 @@ constexpr int kMaxTopK = 8;
 }  // namespace moe
 
 // ---- device helpers ------------------------------------------------------
+// Device check: OR `bits` into the caller's check word once per wave whose
+// lanes flag anything (a vector atomic from the first flagging lane).  Every
+// lane of the wave must call it (the ballot is wave-wide).
+__device__ __forceinline__ void raise_check(int32_t* check, bool flagged, int32_t bits) {
+  const uint64_t m = __ballot(flagged);
+  if (m != 0 && (__lane_id() == static_cast<unsigned>(__ffsll(static_cast<unsigned long long>(m)) - 1)))
+    atomicOr(check, bits);
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
 // fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.

@@ -7,163 +7,204 @@
 // Inference via Predictive Prefetching and Expert Replication", method
 // (physical replicas of one expert serve disjoint subsets of its tokens).
 //
-// Three launches, no host sync:
-//   1. count:   per block of 256 tokens, per-expert counts (LDS atomics) into
-//               a [blocks, E] table in the workspace.
-//   2. rank:    every block sums the table (all threads, LDS atomics) to get
-//               the expert totals, the exclusive expert offsets and its own
-//               per-expert prefix;
-//               inside the block, each wave ranks its tokens per expert with
-//               ballots (order = token order, so the permutation is stable and
-//               independent of scheduling).  Block 0 also writes expert_off
-//               and the slot table.
-//   3. permute: x_perm[inv_pos[t,i]] = x[t], four 16-byte chunks per thread;
-//               every source row is read once and written k times, with
-//               nontemporal stores (measured ~25% faster than cached stores
-//               on this write-heavy copy).
+// The (token, slot) pairs are numbered f = t*k + i; inside an expert the rows
+// follow ascending f (ascending token index; a token naming one expert twice
+// gets two rows in slot order).  Three launches, no host sync:
+//   1. rank:    per block of kPairs pairs, its per-expert counts (into a
+//               [blocks, E] table) and each pair's rank among the block's
+//               pairs of the same expert: wave ballots over the distinct
+//               experts of a wave, LDS counts across waves and rounds.
+//   2. scan:    one block: the expert totals, expert_off, and per block and
+//               expert the first row of the block's pairs (the column prefix
+//               of the count table, O(blocks x E)); the slot table; with a
+//               check word, the totals against `counts` and the replicas
+//               against the slot budget.
+//   3. permute: row = base[f / kPairs][e] + rank[f]; the threads of token t
+//               write inv_pos and perm_src and copy x[t] into each of its
+//               rows: four 16-byte chunks per thread, read once, written k
+//               times with nontemporal stores (measured ~25% faster than cached
+//               stores on this write-heavy copy).
 #include "common.h"
 
 namespace {
 
-constexpr int kTok = 256;  // tokens per count/rank block
+constexpr int kThreads = 256;
+constexpr int kPairs = 512;  // pairs per rank block (two rounds of 256)
+static_assert(kPairs % kThreads == 0, "whole rounds");
 
-__global__ __launch_bounds__(kTok) void count_kernel(const int32_t* __restrict__ idx, int64_t T, int k, int E,
-                                                     int32_t* __restrict__ blk_cnt) {
-  __shared__ int32_t hist[moe::kMaxExperts];
-  for (int e = threadIdx.x; e < E; e += kTok) hist[e] = 0;
-  __syncthreads();
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * kTok + threadIdx.x;
-  if (t < T)
-    for (int i = 0; i < k; ++i) {
-      const int e = idx[t * k + i];
-      if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
-    }
-  __syncthreads();
-  for (int e = threadIdx.x; e < E; e += kTok) blk_cnt[static_cast<int64_t>(blockIdx.x) * E + e] = hist[e];
+struct Ws {
+  size_t cnt, base, rank, bytes;
+};
+
+Ws ws_layout(int64_t T, int k, int E) {
+  Ws w{};
+  const int64_t P = T * k;
+  const int64_t nblk = std::max<int64_t>(1, moe::ceil_div(P, kPairs));
+  size_t at = 0;
+  auto take = [&](size_t n) { size_t p = at; at = moe::align_up(at + n, 256); return p; };
+  w.cnt = take(static_cast<size_t>(nblk) * E * sizeof(int32_t));
+  w.base = take(static_cast<size_t>(nblk) * E * sizeof(int32_t));
+  w.rank = take(static_cast<size_t>(std::max<int64_t>(P, 1)) * sizeof(int32_t));
+  w.bytes = at;
+  return w;
 }
 
-__global__ __launch_bounds__(kTok) void rank_kernel(const int32_t* __restrict__ idx, int64_t T, int k, int E,
-                                                    int nblk, const int32_t* __restrict__ blk_cnt,
-                                                    const int32_t* __restrict__ replicas, int max_slots,
-                                                    int32_t* __restrict__ perm_src, int32_t* __restrict__ inv_pos,
-                                                    int32_t* __restrict__ expert_off, int32_t* __restrict__ slot_off,
-                                                    int32_t* __restrict__ slot_expert, int32_t* __restrict__ n_slots) {
-  __shared__ int32_t tot[moe::kMaxExperts];
-  __shared__ int32_t base[moe::kMaxExperts];  // expert offset + this block's prefix
-  __shared__ int32_t off[moe::kMaxExperts + 1];
-  __shared__ int32_t wave_cnt[kTok / 64][moe::kMaxExperts];
-  __shared__ int64_t rep_pre[moe::kMaxExperts + 1];
-
-  const int tid = threadIdx.x;
-  const int b = blockIdx.x;
-  for (int e = tid; e < E; e += kTok) {
-    tot[e] = 0;
-    base[e] = 0;
-  }
-  __syncthreads();
-  // every thread reads its share of the [nblk, E] count table (loads in flight
-  // together) and adds it into the expert totals and this block's prefix:
-  // exact integer sums, so the order of the LDS atomics does not matter
-  const int64_t cells = static_cast<int64_t>(nblk) * E;
-#pragma unroll 4
-  for (int64_t q = tid; q < cells; q += kTok) {
-    const int32_t c = blk_cnt[q];
-    if (c == 0) continue;
-    const int j = static_cast<int>(q / E), e = static_cast<int>(q - static_cast<int64_t>(j) * E);
-    atomicAdd(&tot[e], c);
-    if (j < b) atomicAdd(&base[e], c);
-  }
-  __syncthreads();
-  if (tid == 0) {  // E <= 256: a short serial scan
-    int32_t run = 0;
-    for (int e = 0; e < E; ++e) { off[e] = run; run += tot[e]; }
-    off[E] = run;
-    int64_t rp = 0;
-    for (int e = 0; e < E; ++e) { rep_pre[e] = rp; rp += replicas ? max(replicas[e], 0) : 0; }
-    rep_pre[E] = rp;
-  }
-  __syncthreads();
-  for (int e = tid; e < E; e += kTok) base[e] += off[e];
-
-  if (b == 0) {
-    const int64_t budget = max_slots - E;
-    const int32_t M = off[E];
-    for (int e = tid; e <= E; e += kTok) expert_off[e] = off[e];
-    for (int e = tid; e < E; e += kTok) {
-      const int64_t want = replicas ? max(replicas[e], 0) : 0;
-      const int64_t r = max<int64_t>(0, min<int64_t>(want, budget - rep_pre[e]));
-      const int64_t s0 = e + min<int64_t>(rep_pre[e], budget);
-      const int64_t n = tot[e];
-      for (int64_t rho = 0; rho <= r; ++rho) {
-        slot_expert[s0 + rho] = e;
-        slot_off[s0 + rho] = off[e] + static_cast<int32_t>((rho * n) / (r + 1));
+__global__ __launch_bounds__(kThreads) void rank_kernel(const int32_t* __restrict__ idx, int64_t P, int k, int E,
+                                                        int32_t* __restrict__ blk_cnt, int32_t* __restrict__ rank,
+                                                        int32_t* __restrict__ check) {
+  __shared__ int32_t run[moe::kMaxExperts];                  // this block's pairs so far, per expert
+  __shared__ int32_t wave_cnt[kThreads / 64][moe::kMaxExperts];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  for (int e = tid; e < E; e += kThreads) run[e] = 0;
+  const int64_t f0 = static_cast<int64_t>(blockIdx.x) * kPairs;
+  const uint64_t lt = (uint64_t(1) << lane) - 1;
+  bool bad_index = false, bad_dup = false;
+  for (int r = 0; r < kPairs / kThreads; ++r) {
+    for (int q = tid; q < (kThreads / 64) * moe::kMaxExperts; q += kThreads) (&wave_cnt[0][0])[q] = 0;
+    const int64_t f = f0 + r * kThreads + tid;
+    int e = -1;
+    if (f < P) {
+      e = idx[f];
+      if (e < 0 || e >= E) {
+        bad_index = true;
+        e = -1;
+      } else if (check) {
+        const int64_t t = f / k;
+        for (int64_t j = t * k; j < f; ++j) bad_dup |= idx[j] == e;
       }
     }
-    const int64_t used = E + min<int64_t>(rep_pre[E], budget);
-    for (int64_t s = used + tid; s <= max_slots; s += kTok) {
-      slot_off[s] = M;
-      if (s < max_slots) slot_expert[s] = 0;
+    __syncthreads();
+    // rank inside the wave: one ballot per distinct expert of the wave
+    int local = 0;
+    uint64_t todo = __ballot(e >= 0);
+    while (todo) {
+      const int leader = __ffsll(static_cast<unsigned long long>(todo)) - 1;
+      const int v = __shfl(e, leader);
+      const uint64_t m = __ballot(e == v);
+      if (e == v) local = __popcll(m & lt);
+      if (lane == leader) wave_cnt[w][v] = __popcll(m);
+      todo &= ~m;
     }
-    if (tid == 0) n_slots[0] = static_cast<int32_t>(used);
+    __syncthreads();
+    if (e >= 0) {
+      int rk = run[e] + local;
+      for (int v = 0; v < w; ++v) rk += wave_cnt[v][e];
+      rank[f] = rk;
+    }
+    __syncthreads();
+    for (int x = tid; x < E; x += kThreads)
+      run[x] += wave_cnt[0][x] + wave_cnt[1][x] + wave_cnt[2][x] + wave_cnt[3][x];
+    __syncthreads();
   }
+  for (int e = tid; e < E; e += kThreads) blk_cnt[static_cast<int64_t>(blockIdx.x) * E + e] = run[e];
+  if (check) {
+    raise_check(check, bad_index, MOE_CHECK_INDEX);
+    raise_check(check, bad_dup, MOE_CHECK_DUPLICATE);
+  }
+}
 
-  // Rank inside the block: wave w ranks its 64 tokens per expert with ballots.
-  const int64_t t = static_cast<int64_t>(b) * kTok + tid;
-  const bool active = t < T;
-  const int lane = tid & 63, w = tid >> 6;
-  int cur[moe::kMaxTopK];
-  int rk[moe::kMaxTopK];
-#pragma unroll
-  for (int i = 0; i < moe::kMaxTopK; ++i) {
-    cur[i] = -1;
-    rk[i] = 0;
-    if (active && i < k) {
-      const int e = idx[t * k + i];
-      cur[i] = (e >= 0 && e < E) ? e : -1;
-    }
+// Inclusive prefix sum over the block's first n <= 256 values of v (in place,
+// LDS), every thread of the block taking part.
+__device__ void block_scan_inclusive(int64_t* v, int n) {
+  const int tid = threadIdx.x;
+  for (int d = 1; d < n; d <<= 1) {
+    const int64_t add = (tid < n && tid >= d) ? v[tid - d] : 0;
+    __syncthreads();
+    if (tid < n) v[tid] += add;
+    __syncthreads();
   }
-  const uint64_t lt = (uint64_t(1) << lane) - 1;
-  for (int e = 0; e < E; ++e) {
-    bool has = false;
-#pragma unroll
-    for (int i = 0; i < moe::kMaxTopK; ++i) has |= (cur[i] == e);
-    const uint64_t m = __ballot(has);
-    if (m == 0) {
-      if (lane == 0) wave_cnt[w][e] = 0;
-      continue;
-    }
-    const int r = __popcll(m & lt);
-#pragma unroll
-    for (int i = 0; i < moe::kMaxTopK; ++i)
-      if (cur[i] == e) rk[i] = r;
-    if (lane == 0) wave_cnt[w][e] = __popcll(m);
+}
+
+__global__ __launch_bounds__(kThreads) void scan_kernel(const int32_t* __restrict__ blk_cnt, int nblk, int E,
+                                                        const int32_t* __restrict__ counts,
+                                                        const int32_t* __restrict__ replicas, int max_slots,
+                                                        int32_t* __restrict__ blk_base, int32_t* __restrict__ expert_off,
+                                                        int32_t* __restrict__ slot_off,
+                                                        int32_t* __restrict__ slot_expert, int32_t* __restrict__ n_slots,
+                                                        int32_t* __restrict__ check) {
+  __shared__ int32_t part[kThreads];   // [group][expert] partial column sums
+  __shared__ int64_t off[moe::kMaxExperts];
+  __shared__ int64_t rep[moe::kMaxExperts];
+  __shared__ int32_t tot[moe::kMaxExperts];
+  const int tid = threadIdx.x;
+  // thread (g, e) = g*E + e sums column e over group g's run of blocks
+  const int G = kThreads / E;
+  const int g = tid / E, e = tid - g * E;
+  const int per = (nblk + G - 1) / G;
+  const int b0 = min(g * per, nblk), b1 = min(b0 + per, nblk);
+  int32_t s = 0;
+  if (g < G) {
+#pragma unroll 4
+    for (int b = b0; b < b1; ++b) s += blk_cnt[static_cast<int64_t>(b) * E + e];
+    part[tid] = s;
   }
   __syncthreads();
-  if (!active) return;
-#pragma unroll
-  for (int i = 0; i < moe::kMaxTopK; ++i) {
-    if (i >= k) break;
-    const int e = cur[i];
-    if (e < 0) {
-      inv_pos[t * k + i] = -1;
-      continue;
+  if (tid < E) {
+    int32_t t = 0;
+    for (int q = 0; q < G; ++q) t += part[q * E + tid];
+    tot[tid] = t;
+    off[tid] = t;
+    const int32_t want = replicas ? replicas[tid] : 0;
+    rep[tid] = max(want, 0);
+  }
+  __syncthreads();
+  // exclusive prefixes: expert offsets and replica counts
+  block_scan_inclusive(off, E);
+  block_scan_inclusive(rep, E);
+  const int32_t M = E > 0 ? static_cast<int32_t>(off[E - 1]) : 0;
+  // group prefix of each column, then this group's blocks
+  if (g < G) {
+    int32_t run = static_cast<int32_t>(off[e] - tot[e]);
+    for (int q = 0; q < g; ++q) run += part[q * E + e];
+    for (int b = b0; b < b1; ++b) {
+      blk_base[static_cast<int64_t>(b) * E + e] = run;
+      run += blk_cnt[static_cast<int64_t>(b) * E + e];
     }
-    int32_t row = base[e] + rk[i];
-    for (int v = 0; v < w; ++v) row += wave_cnt[v][e];
-    perm_src[row] = static_cast<int32_t>(t);
-    inv_pos[t * k + i] = row;
+  }
+  // expert offsets and the slot table
+  const int64_t budget = max_slots - E;
+  bool bad_counts = false, bad_reps = false;
+  for (int x = tid; x < E; x += kThreads) {
+    const int64_t excl = off[x] - tot[x];
+    expert_off[x] = static_cast<int32_t>(excl);
+    const int64_t rp = rep[x] - (replicas ? max(replicas[x], 0) : 0);  // copies of experts before x
+    const int64_t want = replicas ? max(replicas[x], 0) : 0;
+    const int64_t r = max<int64_t>(0, min<int64_t>(want, budget - rp));
+    const int64_t s0 = x + min<int64_t>(rp, budget);
+    const int64_t n = tot[x];
+    for (int64_t rho = 0; rho <= r; ++rho) {
+      slot_expert[s0 + rho] = x;
+      slot_off[s0 + rho] = static_cast<int32_t>(excl + (rho * n) / (r + 1));
+    }
+    bad_counts |= counts && counts[x] != tot[x];
+    bad_reps |= replicas && (replicas[x] < 0 || r < want);
+  }
+  if (tid == 0) expert_off[E] = M;
+  const int64_t all = E > 0 ? rep[E - 1] : 0;
+  const int64_t used = E + min<int64_t>(all, budget);
+  for (int64_t q = used + tid; q <= max_slots; q += kThreads) {
+    slot_off[q] = M;
+    if (q < max_slots) slot_expert[q] = 0;
+  }
+  if (tid == 0) n_slots[0] = static_cast<int32_t>(used);
+  if (check) {
+    raise_check(check, bad_counts, MOE_CHECK_COUNTS);
+    raise_check(check, bad_reps, MOE_CHECK_REPLICAS);
   }
 }
 
 // Four 16-byte chunks of one source row per thread (strided so a wave's
 // accesses stay contiguous); each chunk is read once and written to the k
-// destination rows.
+// destination rows.  The thread holding chunk group 0 of a token also writes
+// the token's inv_pos entries and perm_src of its rows.
 constexpr int kChunksPerThread = 4;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-__global__ __launch_bounds__(256) void permute_kernel(const uint4* __restrict__ x, int64_t T, int chunks, int k,
-                                                      int64_t M, const int32_t* __restrict__ inv_pos,
-                                                      uint4* __restrict__ x_perm) {
+__global__ __launch_bounds__(256) void permute_kernel(const uint4* __restrict__ x, int64_t T, int chunks, int k, int E,
+                                                      const int32_t* __restrict__ idx,
+                                                      const int32_t* __restrict__ blk_base,
+                                                      const int32_t* __restrict__ rank, int32_t* __restrict__ perm_src,
+                                                      int32_t* __restrict__ inv_pos, uint4* __restrict__ x_perm) {
   const int groups = (chunks + kChunksPerThread - 1) / kChunksPerThread;
   const int64_t g = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (g >= T * groups) return;
@@ -176,8 +217,14 @@ __global__ __launch_bounds__(256) void permute_kernel(const uint4* __restrict__ 
     if (c < chunks) v[u] = x[t * chunks + c];
   }
   for (int i = 0; i < k; ++i) {
-    const int32_t r = inv_pos[t * k + i];
-    if (r < 0 || r >= M) continue;
+    const int64_t f = t * k + i;
+    const int e = idx[f];
+    const int32_t r = (e >= 0 && e < E) ? blk_base[(f / kPairs) * E + e] + rank[f] : -1;
+    if (c0 == 0) {
+      inv_pos[f] = r;
+      if (r >= 0) perm_src[r] = static_cast<int32_t>(t);
+    }
+    if (r < 0) continue;
     uint4* dst = x_perm + static_cast<int64_t>(r) * chunks;
 #pragma unroll
     for (int u = 0; u < kChunksPerThread; ++u) {
@@ -191,16 +238,15 @@ __global__ __launch_bounds__(256) void permute_kernel(const uint4* __restrict__ 
 }  // namespace
 
 extern "C" size_t moe_dispatch_workspace_bytes(int64_t T, int k, int E) {
-  (void)k;
-  if (T < 0 || E < 1) return 0;
-  return moe::align_up(static_cast<size_t>(std::max<int64_t>(1, moe::ceil_div(T, kTok))) * E * sizeof(int32_t), 256);
+  if (T < 0 || E < 1 || E > moe::kMaxExperts || k < 1 || k > moe::kMaxTopK) return 0;
+  return ws_layout(T, k, E).bytes;
 }
 
 extern "C" int moe_dispatch(const void* x, moe_dtype dt, int64_t T, int H, const int32_t* topk_idx, int k, int E,
-                            const int32_t* replicas, int max_slots,
+                            const int32_t* counts, const int32_t* replicas, int max_slots,
                             void* x_perm, int32_t* perm_src, int32_t* inv_pos, int32_t* expert_off,
                             int32_t* slot_off, int32_t* slot_expert, int32_t* n_slots,
-                            void* workspace, size_t workspace_bytes, void* stream) {
+                            void* workspace, size_t workspace_bytes, int32_t* check, void* stream) {
   using namespace moe;
   if (E < 1 || E > kMaxExperts) return fail(E < 1 ? MOE_ERR_INVALID_ARG : MOE_ERR_UNSUPPORTED,
                                             "moe_dispatch: E=%d outside [1, %d]", E, kMaxExperts);
@@ -216,20 +262,25 @@ extern "C" int moe_dispatch(const void* x, moe_dtype dt, int64_t T, int H, const
     return fail(MOE_ERR_INVALID_ARG, "moe_dispatch: null pointer");
   if (T > 0 && (!aligned16(x) || !aligned16(x_perm)))
     return fail(MOE_ERR_INVALID_ARG, "moe_dispatch: x and x_perm must be 16-byte aligned");
-  if (workspace_bytes < moe_dispatch_workspace_bytes(T, k, E))
-    return fail(MOE_ERR_WORKSPACE, "moe_dispatch: workspace has %zu bytes, needs %zu", workspace_bytes,
-                moe_dispatch_workspace_bytes(T, k, E));
+  const Ws w = ws_layout(T, k, E);
+  if (workspace_bytes < w.bytes)
+    return fail(MOE_ERR_WORKSPACE, "moe_dispatch: workspace has %zu bytes, needs %zu", workspace_bytes, w.bytes);
   const hipStream_t s = as_stream(stream);
-  int32_t* blk_cnt = static_cast<int32_t*>(workspace);
-  const int nblk = static_cast<int>(ceil_div(T, kTok));
-  if (nblk > 0) count_kernel<<<nblk, kTok, 0, s>>>(topk_idx, T, k, E, blk_cnt);
-  rank_kernel<<<std::max(nblk, 1), kTok, 0, s>>>(topk_idx, T, k, E, nblk, blk_cnt, replicas, max_slots, perm_src,
-                                                 inv_pos, expert_off, slot_off, slot_expert, n_slots);
+  char* ws = static_cast<char*>(workspace);
+  int32_t* blk_cnt = reinterpret_cast<int32_t*>(ws + w.cnt);
+  int32_t* blk_base = reinterpret_cast<int32_t*>(ws + w.base);
+  int32_t* rank = reinterpret_cast<int32_t*>(ws + w.rank);
+  const int64_t P = T * k;
+  const int nblk = static_cast<int>(ceil_div(P, kPairs));
+  if (nblk > 0) rank_kernel<<<nblk, kThreads, 0, s>>>(topk_idx, P, k, E, blk_cnt, rank, check);
+  scan_kernel<<<1, kThreads, 0, s>>>(blk_cnt, nblk, E, counts, replicas, max_slots, blk_base, expert_off, slot_off,
+                                     slot_expert, n_slots, check);
   if (T > 0) {
     const int chunks = static_cast<int>(static_cast<int64_t>(H) * elem_bytes(dt) / 16);
     const int64_t threads = T * ceil_div(chunks, kChunksPerThread);
     permute_kernel<<<static_cast<unsigned>(ceil_div(threads, 256)), 256, 0, s>>>(
-        static_cast<const uint4*>(x), T, chunks, k, T * k, inv_pos, static_cast<uint4*>(x_perm));
+        static_cast<const uint4*>(x), T, chunks, k, E, topk_idx, blk_base, rank, perm_src, inv_pos,
+        static_cast<uint4*>(x_perm));
   }
   return hip_status(hipGetLastError(), "moe_dispatch launch");
 }

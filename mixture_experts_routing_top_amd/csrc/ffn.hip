@@ -78,10 +78,11 @@ WsLayout ws_layout(moe_dtype dt, int64_t M, int I, int max_slots) {
   return w;
 }
 
-// Caller-owned events recorded around the two GEMM launches (profiling only).
-thread_local hipEvent_t g_timing[3] = {nullptr, nullptr, nullptr};
-
-hipError_t mark(int i, hipStream_t s) { return g_timing[i] ? hipEventRecord(g_timing[i], s) : hipSuccess; }
+// Caller-owned events recorded around the two GEMM launches (profiling only;
+// null when not profiling).
+hipError_t mark(hipEvent_t const* ev, int i, hipStream_t s) {
+  return ev ? hipEventRecord(ev[i], s) : hipSuccess;
+}
 
 // A 256-row tiling runs with its 64-row companion table in one mixed launch;
 // the 64-row tilings run alone.
@@ -94,15 +95,15 @@ void launch_gemm(bool small, const GemmArgs& p, const GemmArgs& companion, unsig
 // Phase 1 (gate/up or W1) and phase 2 (down or W2), each on its own tile table.
 template <bool kBf16>
 int launch_ffn(const GemmArgs& p1, bool small1, unsigned grid1, const GemmArgs& t1, const GemmArgs& p2, bool small2,
-               unsigned grid2, const GemmArgs& t2, bool swiglu, hipStream_t s) {
-  if (int rc = moe::hip_status(mark(0, s), "moe_expert_ffn timing event")) return rc;
+               unsigned grid2, const GemmArgs& t2, bool swiglu, hipEvent_t const* ev, hipStream_t s) {
+  if (int rc = moe::hip_status(mark(ev, 0, s), "moe_expert_ffn timing event")) return rc;
   if (swiglu) launch_gemm<kBf16, kEpiSwiGLU, 2>(small1, p1, t1, grid1, s);
   else launch_gemm<kBf16, kEpiGELU, 1>(small1, p1, t1, grid1, s);
   if (int rc = moe::hip_status(hipGetLastError(), "moe_expert_ffn gate/up launch")) return rc;
-  if (int rc = moe::hip_status(mark(1, s), "moe_expert_ffn timing event")) return rc;
+  if (int rc = moe::hip_status(mark(ev, 1, s), "moe_expert_ffn timing event")) return rc;
   launch_gemm<kBf16, kEpiStore, 1>(small2, p2, t2, grid2, s);
   if (int rc = moe::hip_status(hipGetLastError(), "moe_expert_ffn down launch")) return rc;
-  return moe::hip_status(mark(2, s), "moe_expert_ffn timing event");
+  return moe::hip_status(mark(ev, 2, s), "moe_expert_ffn timing event");
 }
 
 // AUTO rule, per GEMM, from the slot sizes.  Cost model in "row-tile units":
@@ -124,6 +125,11 @@ Kind pick_kind(int64_t g256, int64_t g256_rem, int64_t d64, int64_t g64, int col
   return kG256;
 }
 
+int ffn_impl(const void* x_perm, moe_dtype dt, int64_t M, int H, int I, int E, const int32_t* slot_off,
+             const int32_t* slot_expert, const int32_t* n_slots, int max_slots, const void* w_gate, const void* w_up,
+             const void* w_down, moe_act act, moe_gemm_path path, void* y_perm, void* workspace,
+             size_t workspace_bytes, int32_t* check, hipEvent_t const* ev, void* stream);
+
 }  // namespace
 
 extern "C" size_t moe_expert_ffn_workspace_bytes(moe_dtype dt, int64_t M, int H, int I, int max_slots) {
@@ -136,7 +142,30 @@ extern "C" int moe_expert_ffn(const void* x_perm, moe_dtype dt, int64_t M, int H
                               const int32_t* slot_off, const int32_t* slot_expert, const int32_t* n_slots,
                               int max_slots, const void* w_gate, const void* w_up, const void* w_down, moe_act act,
                               moe_gemm_path path, void* y_perm, void* workspace, size_t workspace_bytes,
-                              void* stream) {
+                              int32_t* check, void* stream) {
+  return ffn_impl(x_perm, dt, M, H, I, E, slot_off, slot_expert, n_slots, max_slots, w_gate, w_up, w_down, act, path,
+                  y_perm, workspace, workspace_bytes, check, nullptr, stream);
+}
+
+extern "C" int moe_expert_ffn_profiled(const void* x_perm, moe_dtype dt, int64_t M, int H, int I, int E,
+                                       const int32_t* slot_off, const int32_t* slot_expert, const int32_t* n_slots,
+                                       int max_slots, const void* w_gate, const void* w_up, const void* w_down,
+                                       moe_act act, moe_gemm_path path, void* y_perm, void* workspace,
+                                       size_t workspace_bytes, int32_t* check, void* const* events, void* stream) {
+  if (!events || !events[0] || !events[1] || !events[2])
+    return moe::fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn_profiled: needs three events");
+  const hipEvent_t ev[3] = {static_cast<hipEvent_t>(events[0]), static_cast<hipEvent_t>(events[1]),
+                            static_cast<hipEvent_t>(events[2])};
+  return ffn_impl(x_perm, dt, M, H, I, E, slot_off, slot_expert, n_slots, max_slots, w_gate, w_up, w_down, act, path,
+                  y_perm, workspace, workspace_bytes, check, ev, stream);
+}
+
+namespace {
+
+int ffn_impl(const void* x_perm, moe_dtype dt, int64_t M, int H, int I, int E, const int32_t* slot_off,
+             const int32_t* slot_expert, const int32_t* n_slots, int max_slots, const void* w_gate, const void* w_up,
+             const void* w_down, moe_act act, moe_gemm_path path, void* y_perm, void* workspace,
+             size_t workspace_bytes, int32_t* check, hipEvent_t const* ev, void* stream) {
   using namespace moe;
   if (dt != MOE_F32 && dt != MOE_BF16) return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn: unknown dtype %d", (int)dt);
   if (act != MOE_SWIGLU && act != MOE_GELU) return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn: unknown activation");
@@ -256,9 +285,9 @@ extern "C" int moe_expert_ffn(const void* x_perm, moe_dtype dt, int64_t M, int H
   auto build = [&](Kind t) {
     const int mode = t == kD64 ? kPadded : kCover;
     const int bm = t == kG256 ? kBigM : kSmallM;
-    tiles_kernel<<<1, 256, 0, s>>>(slot_off, slot_expert, n_slots, max_slots, M, mode, bm, m_pad, 1, w.cap[t],
+    tiles_kernel<<<1, 256, 0, s>>>(slot_off, slot_expert, n_slots, max_slots, M, E, mode, bm, m_pad, 1, w.cap[t],
                                    tab_slot(t), tab_row0(t), tab_rend(t), n_tiles + t,
-                                   t == kG256 ? split : TileSplit{});
+                                   t == kG256 ? split : TileSplit{}, check);
     return hip_status(hipGetLastError(), "moe_expert_ffn tile-table launch");
   };
   if (int rc = build(k1)) return rc;
@@ -304,15 +333,8 @@ extern "C" int moe_expert_ffn(const void* x_perm, moe_dtype dt, int64_t M, int H
   };
   const GemmArgs t1 = companion(p1, 0), t2 = companion(p2, 1);
   const bool swiglu = act == MOE_SWIGLU;
-  return dt == MOE_BF16 ? launch_ffn<true>(p1, k1 != kG256, grid1, t1, p2, k2 != kG256, grid2, t2, swiglu, s)
-                        : launch_ffn<false>(p1, k1 != kG256, grid1, t1, p2, k2 != kG256, grid2, t2, swiglu, s);
+  return dt == MOE_BF16 ? launch_ffn<true>(p1, k1 != kG256, grid1, t1, p2, k2 != kG256, grid2, t2, swiglu, ev, s)
+                        : launch_ffn<false>(p1, k1 != kG256, grid1, t1, p2, k2 != kG256, grid2, t2, swiglu, ev, s);
 }
 
-extern "C" int moe_ffn_set_timing_events(void* before_gateup, void* after_gateup, void* after_down) {
-  const int set = (before_gateup != nullptr) + (after_gateup != nullptr) + (after_down != nullptr);
-  if (set != 0 && set != 3) return moe::fail(MOE_ERR_INVALID_ARG, "moe_ffn_set_timing_events: pass three events or none");
-  g_timing[0] = static_cast<hipEvent_t>(before_gateup);
-  g_timing[1] = static_cast<hipEvent_t>(after_gateup);
-  g_timing[2] = static_cast<hipEvent_t>(after_down);
-  return MOE_OK;
-}
+}  // namespace

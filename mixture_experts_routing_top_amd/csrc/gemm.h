@@ -967,10 +967,10 @@ __device__ inline float mixed_rounds(int64_t big, int64_t small, float c) {
 __global__ __launch_bounds__(256) void tiles_kernel(const int32_t* __restrict__ slot_off,
                                                     const int32_t* __restrict__ slot_expert,
                                                     const int32_t* __restrict__ n_slots_p, int max_slots, int64_t M,
-                                                    int mode, int BM, int m_pad, int merge, int max_tiles,
+                                                    int E, int mode, int BM, int m_pad, int merge, int max_tiles,
                                                     int32_t* __restrict__ tile_slot, int32_t* __restrict__ tile_row0,
                                                     int32_t* __restrict__ tile_rend, int32_t* __restrict__ n_tiles,
-                                                    TileSplit split) {
+                                                    TileSplit split, int32_t* __restrict__ check) {
   __shared__ int32_t scan[256], scan2[256];
   __shared__ int32_t carry, carry2;
   // slot tables of up to kLdsSlots slots are read from LDS: the merge walk over
@@ -990,6 +990,14 @@ __global__ __launch_bounds__(256) void tiles_kernel(const int32_t* __restrict__ 
   const int32_t* so = staged ? so_lds : slot_off;
   if (tid == 0) carry = carry2 = 0;
   __syncthreads();
+  if (check) {
+    // the slot table a dispatch writes: slot_off ascending inside [0, M],
+    // experts inside [0, E), n_slots inside [0, max_slots]
+    bool bad = tid == 0 && (*n_slots_p < 0 || *n_slots_p > max_slots);
+    for (int i = tid; i < n; i += 256)
+      bad |= so[i] < 0 || so[i] > so[i + 1] || so[i + 1] > M || se[i] < 0 || se[i] >= E;
+    raise_check(check, bad, MOE_CHECK_SLOTS);
+  }
   for (int c = 0; c < n; c += 256) {
     const int s = c + tid;
     int64_t start = 0, end = 0, cnt = 0, cnt_small = 0;

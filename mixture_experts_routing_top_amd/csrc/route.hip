@@ -13,7 +13,9 @@
 // token; each lane holds 4 consecutive logits (one 16-byte load when the row
 // allows it).  k rounds of a butterfly arg-max over the group's lanes, ordered
 // by (logit desc, index asc), pick the experts; the winner's owner lane masks
-// its entry.  HBM-bound: 4E bytes in, 8k bytes out per token.
+// its entry.  HBM-bound: 4E bytes in, 8k bytes out per token.  With a check
+// word, a NaN or infinite logit raises MOE_CHECK_LOGITS (the softmax routing
+// of the pages is defined over finite logits).
 #include <cfloat>
 
 #include "common.h"
@@ -27,7 +29,7 @@ __device__ __forceinline__ bool better(float v1, int i1, float v2, int i2) {
 template <int G>
 __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int64_t T, int E, int k,
                                                     bool vec4, int32_t* __restrict__ topk_idx,
-                                                    float* __restrict__ topk_w) {
+                                                    float* __restrict__ topk_w, int32_t* __restrict__ check) {
   constexpr int kTokPerBlock = 256 / G;
   const int g = threadIdx.x % G;
   const int64_t t = static_cast<int64_t>(blockIdx.x) * kTokPerBlock + threadIdx.x / G;
@@ -44,11 +46,14 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
 #pragma unroll
     for (int c = 0; c < 4; ++c) v[c] = (base + c < E) ? row[base + c] : -INFINITY;
   }
+  bool bad = false;
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     if (base + c >= E) taken |= 1u << c;
+    else bad |= active && !(fabsf(v[c]) <= FLT_MAX);  // NaN or +-inf
     if (!(v[c] == v[c])) v[c] = -INFINITY;  // NaN orders as -inf
   }
+  if (check) raise_check(check, bad, MOE_CHECK_LOGITS);
 
   float win_v[moe::kMaxTopK];
   int win_i[moe::kMaxTopK];
@@ -93,15 +98,16 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
 }
 
 template <int G>
-void launch(const float* logits, int64_t T, int E, int k, bool vec4, int32_t* idx, float* w, hipStream_t s) {
+void launch(const float* logits, int64_t T, int E, int k, bool vec4, int32_t* idx, float* w, int32_t* check,
+            hipStream_t s) {
   const int64_t blocks = moe::ceil_div(T, 256 / G);
-  route_kernel<G><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s>>>(logits, T, E, k, vec4, idx, w);
+  route_kernel<G><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s>>>(logits, T, E, k, vec4, idx, w, check);
 }
 
 }  // namespace
 
 extern "C" int moe_route(const float* logits, int64_t T, int E, int k, int32_t* topk_idx, float* topk_w,
-                         void* stream) {
+                         int32_t* check, void* stream) {
   using namespace moe;
   if (E < 1 || E > kMaxExperts) return fail(E < 1 ? MOE_ERR_INVALID_ARG : MOE_ERR_UNSUPPORTED,
                                             "moe_route: E=%d outside [1, %d]", E, kMaxExperts);
@@ -112,12 +118,12 @@ extern "C" int moe_route(const float* logits, int64_t T, int E, int k, int32_t* 
   const bool vec4 = (E % 4 == 0) && aligned16(logits);
   const hipStream_t s = as_stream(stream);
   const int lanes = static_cast<int>(ceil_div(E, 4));
-  if (lanes <= 1) launch<1>(logits, T, E, k, vec4, topk_idx, topk_w, s);
-  else if (lanes <= 2) launch<2>(logits, T, E, k, vec4, topk_idx, topk_w, s);
-  else if (lanes <= 4) launch<4>(logits, T, E, k, vec4, topk_idx, topk_w, s);
-  else if (lanes <= 8) launch<8>(logits, T, E, k, vec4, topk_idx, topk_w, s);
-  else if (lanes <= 16) launch<16>(logits, T, E, k, vec4, topk_idx, topk_w, s);
-  else if (lanes <= 32) launch<32>(logits, T, E, k, vec4, topk_idx, topk_w, s);
-  else launch<64>(logits, T, E, k, vec4, topk_idx, topk_w, s);
+  if (lanes <= 1) launch<1>(logits, T, E, k, vec4, topk_idx, topk_w, check, s);
+  else if (lanes <= 2) launch<2>(logits, T, E, k, vec4, topk_idx, topk_w, check, s);
+  else if (lanes <= 4) launch<4>(logits, T, E, k, vec4, topk_idx, topk_w, check, s);
+  else if (lanes <= 8) launch<8>(logits, T, E, k, vec4, topk_idx, topk_w, check, s);
+  else if (lanes <= 16) launch<16>(logits, T, E, k, vec4, topk_idx, topk_w, check, s);
+  else if (lanes <= 32) launch<32>(logits, T, E, k, vec4, topk_idx, topk_w, check, s);
+  else launch<64>(logits, T, E, k, vec4, topk_idx, topk_w, check, s);
   return hip_status(hipGetLastError(), "moe_route launch");
 }

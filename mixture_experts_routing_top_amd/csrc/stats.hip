@@ -17,7 +17,10 @@
 // matrix, the prediction and the replica counts.  All counts are exact
 // integers; the divisions are IEEE fp32 divisions of exact integers and the
 // prediction is a double sum in expert order, so the results do not depend on
-// the order in which blocks finish.
+// the order in which blocks finish.  With a check word, indices outside [0, E)
+// (skipped) raise MOE_CHECK_INDEX and a token naming one expert twice (counted
+// as often as named) MOE_CHECK_DUPLICATE: the top-k gate picks k distinct
+// experts.
 #include "common.h"
 #include "replica_plan.h"
 
@@ -56,6 +59,7 @@ struct Args {
   float* cond;
   float* pred;
   int32_t* replicas;
+  int32_t* check;
 };
 
 __global__ __launch_bounds__(kThreads) void stats_kernel(Args a) {
@@ -82,6 +86,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(Args a) {
     __syncthreads();
     const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kTokPerBlock;
     const int64_t t1 = min(a.T, t0 + kTokPerBlock);
+    bool bad_index = false, bad_dup = false;
     for (int64_t t = t0 + tid; t < t1; t += kThreads) {
       int cur[moe::kMaxTopK];
 #pragma unroll
@@ -90,14 +95,24 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(Args a) {
         if (i < k) {
           const int e = a.idx[t * k + i];
           if (e >= 0 && e < E) { cur[i] = e; atomicAdd(&hist[e], 1); }
+          else bad_index = true;
         }
+      }
+      if (a.check) {
+#pragma unroll
+        for (int i = 1; i < moe::kMaxTopK; ++i)
+#pragma unroll
+          for (int j = 0; j < i; ++j) bad_dup |= i < k && cur[i] >= 0 && cur[i] == cur[j];
       }
       if (do_cooc) {
 #pragma unroll
         for (int i = 0; i < moe::kMaxTopK; ++i) {
           if (i >= k) break;
           const int p = a.prev[t * k + i];
-          if (p < 0 || p >= E) continue;
+          if (p < 0 || p >= E) {
+            bad_index = true;
+            continue;
+          }
 #pragma unroll
           for (int j = 0; j < moe::kMaxTopK; ++j) {
             if (j < k && cur[j] >= 0) {
@@ -107,6 +122,10 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(Args a) {
           }
         }
       }
+    }
+    if (a.check) {
+      raise_check(a.check, bad_index, MOE_CHECK_INDEX);
+      raise_check(a.check, bad_dup, MOE_CHECK_DUPLICATE);
     }
     __syncthreads();
     for (int e = tid; e < E; e += kThreads)
@@ -308,7 +327,7 @@ extern "C" int moe_stats_init(void* state, size_t state_bytes, int L, int E, int
 extern "C" int moe_stats(void* state, size_t state_bytes, int L, int E, int window, int layer, int64_t iter,
                          const int32_t* topk_idx, const int32_t* prev_topk_idx, int64_t T, int k,
                          int32_t* counts, float* p_seq, float* cond, float* pred_next,
-                         int replica_budget, int32_t* replicas, void* stream) {
+                         int replica_budget, int32_t* replicas, int32_t* check, void* stream) {
   using namespace moe;
   if (!dims_ok(L, E, window)) return fail(E > kMaxExperts ? MOE_ERR_UNSUPPORTED : MOE_ERR_INVALID_ARG,
                                           "moe_stats: bad L=%d E=%d window=%d", L, E, window);
@@ -341,6 +360,7 @@ extern "C" int moe_stats(void* state, size_t state_bytes, int L, int E, int wind
   a.cond = layer + 1 < L ? cond : nullptr;
   a.pred = layer + 1 < L ? pred_next : nullptr;
   a.replicas = topk_idx ? replicas : nullptr;
+  a.check = topk_idx ? check : nullptr;
   const unsigned blocks = topk_idx ? static_cast<unsigned>(std::max<int64_t>(1, ceil_div(T, kTokPerBlock))) : 1u;
   stats_kernel<<<blocks, kThreads, 0, as_stream(stream)>>>(a);
   return hip_status(hipGetLastError(), "moe_stats launch");

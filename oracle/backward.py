@@ -7,8 +7,14 @@ combine.  The backward pass is what the training-side pages run after the
 forward they describe (PopFetcher wiki, method: the backward All-to-All; the
 expert-load prediction study traces training iterations).
 
-Plain numpy in float64, one expert at a time; intermediates are rounded to the
-activation dtype exactly where the HIP backward keeps them in that dtype:
+Plain numpy in float64, one expert at a time.  The pages say nothing about
+precision in the backward pass; the reading taken extends the workloads'
+"activations in the dtype, accumulation in fp32" to it: every tensor that is an
+activation of the layer or the gradient of one is stored in the activation
+dtype (rounded once, to nearest even), every product is accumulated exactly
+(float64 here), d_h -- the inner product of one chain, consumed at once by
+the activation gradient -- is never stored in the dtype, and the router-side
+quantities dw and d_logits are float32, like the gate weights they differentiate:
   d_y   = w * d_out                  (one row per (token, slot)), rounded
   d_h   = d_y Wd                     (float64)
   SwiGLU: d_g = d_h * u * silu'(g), d_u = d_h * silu(g); GELU: d_z = d_h * gelu'(z)
@@ -145,6 +151,7 @@ def sampled_backward(x, idx, w, weights, act, d_out, tokens, entries):
     dO = _f64(d_out)
     wt = np.asarray(w, dtype=np.float64)
     swiglu = wu_ is not None
+    memo = {}   # per-expert columns shared by several entries (same values, computed once)
     rd = lambda v: _f64(_round(v, bf16))
     tokens = np.asarray(tokens)
     dX = np.zeros((len(tokens), H))
@@ -181,19 +188,21 @@ def sampled_backward(x, idx, w, weights, act, d_out, tokens, entries):
             dYe = rd(wt[rows[:, 0], rows[:, 1]][:, None] * dO[rows[:, 0]])
             for name, _, a, b in want:
                 if name == "d_w_down":
-                    gb = Xe @ Wg[b]
-                    hb = rd(silu(gb) * (Xe @ Wu[b])) if swiglu else rd(gelu(gb))
-                    v = dYe[:, a] @ hb
+                    if ("h", e, b) not in memo:
+                        gb = Xe @ Wg[b]
+                        memo[("h", e, b)] = rd(silu(gb) * (Xe @ Wu[b])) if swiglu else rd(gelu(gb))
+                    v = dYe[:, a] @ memo[("h", e, b)]
                 else:
-                    ga = Xe @ Wg[a]
-                    dha = dYe @ Wd[:, a]
-                    if name == "d_w_gate" and swiglu:
-                        d = rd(dha * (Xe @ Wu[a]) * silu_grad(ga))
-                    elif name == "d_w_gate":
-                        d = rd(dha * gelu_grad(ga))
-                    else:
-                        d = rd(dha * silu(ga))
-                    v = d @ Xe[:, b]
+                    if (name, e, a) not in memo:
+                        ga = Xe @ Wg[a]
+                        dha = dYe @ Wd[:, a]
+                        if name == "d_w_gate" and swiglu:
+                            memo[(name, e, a)] = rd(dha * (Xe @ Wu[a]) * silu_grad(ga))
+                        elif name == "d_w_gate":
+                            memo[(name, e, a)] = rd(dha * gelu_grad(ga))
+                        else:
+                            memo[(name, e, a)] = rd(dha * silu(ga))
+                    v = memo[(name, e, a)] @ Xe[:, b]
                 vals[(name, e, a, b)] = float(_f64(_round(np.array([v]), bf16))[0])
     s = (wt[tokens] * dw).sum(axis=1, keepdims=True)
     np.put_along_axis(dL, idx[tokens].astype(np.int64), wt[tokens] * (dw - s), axis=1)

@@ -49,31 +49,32 @@ def test_status_strings():
     lib = _lib()
     assert lib.moe_status_string(0) == b"ok"
     assert lib.moe_status_string(-3) == b"workspace or state too small"
+    assert lib.moe_status_string(-5) == b"the device check flagged invalid input"
 
 
 N = None
 
 
 @pytest.mark.parametrize("call,args,status,msg", [
-    ("moe_route", (N, 10, 0, 2, N, N, N), -1, "E=0"),
-    ("moe_route", (N, 10, 300, 2, N, N, N), -2, "E=300"),
-    ("moe_route", (N, 10, 8, 9, N, N, N), -1, "k=9"),
-    ("moe_route", (N, 10, 8, 2, N, N, N), -1, "null"),
-    ("moe_route", (N, -1, 8, 2, N, N, N), -1, "T="),
-    ("moe_stats", (1, 1 << 20, 2, 8, 10, 2, 0, 1, N, 0, 2, N, N, N, N, 0, N, N), -1, "layer=2"),
-    ("moe_stats", (1, 8, 2, 8, 10, 1, 0, 1, N, 0, 2, N, N, N, N, 0, N, N), -3, "too small"),
-    ("moe_stats", (1, 1 << 20, 2, 8, 10, 1, 0, 1, N, 100, 2, N, N, N, N, 0, N, N), -1, "prev_topk_idx"),
+    ("moe_route", (N, 10, 0, 2, N, N, N, N), -1, "E=0"),
+    ("moe_route", (N, 10, 300, 2, N, N, N, N), -2, "E=300"),
+    ("moe_route", (N, 10, 8, 9, N, N, N, N), -1, "k=9"),
+    ("moe_route", (N, 10, 8, 2, N, N, N, N), -1, "null"),
+    ("moe_route", (N, -1, 8, 2, N, N, N, N), -1, "T="),
+    ("moe_stats", (1, 1 << 20, 2, 8, 10, 2, 0, 1, N, 0, 2, N, N, N, N, 0, N, N, N), -1, "layer=2"),
+    ("moe_stats", (1, 8, 2, 8, 10, 1, 0, 1, N, 0, 2, N, N, N, N, 0, N, N, N), -3, "too small"),
+    ("moe_stats", (1, 1 << 20, 2, 8, 10, 1, 0, 1, N, 100, 2, N, N, N, N, 0, N, N, N), -1, "prev_topk_idx"),
     ("moe_stats_init", (N, 0, 2, 8, 10, N), -1, "null state"),
-    ("moe_dispatch", (16, 0, 10, 64, 16, 2, 8, N, 8, 16, 16, 16, 16, 16, 16, 16, 16, 0, N), -3, "workspace"),
-    ("moe_dispatch", (1, 1, 10, 7, 1, 2, 8, N, 8, 1, 1, 1, 1, 1, 1, 1, 1, 1 << 20, N), -1, "multiple of 16"),
-    ("moe_dispatch", (1, 0, 10, 64, 1, 2, 8, N, 4, 1, 1, 1, 1, 1, 1, 1, 1, 1 << 20, N), -1, "max_slots"),
-    ("moe_dispatch", (8, 0, 10, 64, 8, 2, 8, N, 8, 8, 8, 8, 8, 8, 8, 8, 8, 1 << 20, N), -1, "aligned"),
-    ("moe_expert_ffn", (16, 1, 100, 96, 128, 8, 16, 16, 16, 8, 16, 16, 16, 0, 1, 16, 16, 1 << 30, N), -2, "multiples of 64"),
-    ("moe_expert_ffn", (16, 1, 100, 128, 128, 8, 16, 16, 16, 8, 16, N, 16, 0, 1, 16, 16, 1 << 30, N), -1, "w_up"),
-    ("moe_expert_ffn", (16, 1, 100, 128, 128, 8, 16, 16, 16, 8, 16, 16, 16, 1, 1, 16, 16, 1 << 30, N), -1, "GELU"),
-    ("moe_expert_ffn", (16, 1, 100, 128, 128, 8, 16, 16, 16, 8, 16, 16, 16, 0, 1, 16, 16, 10, N), -3, "workspace"),
+    ("moe_dispatch", (16, 0, 10, 64, 16, 2, 8, N, N, 8, 16, 16, 16, 16, 16, 16, 16, 16, 0, N, N), -3, "workspace"),
+    ("moe_dispatch", (1, 1, 10, 7, 1, 2, 8, N, N, 8, 1, 1, 1, 1, 1, 1, 1, 1, 1 << 20, N, N), -1, "multiple of 16"),
+    ("moe_dispatch", (1, 0, 10, 64, 1, 2, 8, N, N, 4, 1, 1, 1, 1, 1, 1, 1, 1, 1 << 20, N, N), -1, "max_slots"),
+    ("moe_dispatch", (8, 0, 10, 64, 8, 2, 8, N, N, 8, 8, 8, 8, 8, 8, 8, 8, 8, 1 << 20, N, N), -1, "aligned"),
+    ("moe_expert_ffn", (16, 1, 100, 96, 128, 8, 16, 16, 16, 8, 16, 16, 16, 0, 1, 16, 16, 1 << 30, N, N), -2, "multiples of 64"),
+    ("moe_expert_ffn", (16, 1, 100, 128, 128, 8, 16, 16, 16, 8, 16, N, 16, 0, 1, 16, 16, 1 << 30, N, N), -1, "w_up"),
+    ("moe_expert_ffn", (16, 1, 100, 128, 128, 8, 16, 16, 16, 8, 16, 16, 16, 1, 1, 16, 16, 1 << 30, N, N), -1, "GELU"),
+    ("moe_expert_ffn", (16, 1, 100, 128, 128, 8, 16, 16, 16, 8, 16, 16, 16, 0, 1, 16, 16, 10, N, N), -3, "workspace"),
     # 2^27 rows x 2^21 columns: more blocks than 32-bit grid indexing covers
-    ("moe_expert_ffn", (16, 1, 1 << 27, 64, 1 << 21, 8, 16, 16, 16, 8, 16, 16, 16, 0, 1, 16, 16, 1 << 62, N), -2,
+    ("moe_expert_ffn", (16, 1, 1 << 27, 64, 1 << 21, 8, 16, 16, 16, 8, 16, 16, 16, 0, 1, 16, 16, 1 << 62, N, N), -2,
      "32-bit grid"),
     ("moe_stats_load_state", (1, 1 << 20, 2, 8, 10, 0, 0, 1.5, N, N, N, N), -1, "decay"),
     ("moe_stats_load_state", (1, 1 << 20, 2, 8, 10, 2, 0, 0.9, N, N, N, N), -1, "layer=2"),
@@ -98,8 +99,11 @@ N = None
     # 16 experts with I = 2^20: the weight-gradient grid exceeds 32-bit indexing
     ("moe_backward", (16, 16, 1, 10, 2, 64, 1 << 20, 16, 16, 16, 16, 16, 16, 16, 16, 0, 16, 16, 16, 16, 16, 16, 16,
                       1 << 62, N), -2, "32-bit grid"),
-    ("moe_combine", (16, 1, 10, 16, 16, 10, 9, 64, 16, N), -1, "k=9"),
-    ("moe_combine", (16, 1, 10, 16, 16, 10, 2, 12, 16, N), -1, "multiple of 16"),
+    ("moe_combine", (16, 1, 10, 16, 16, 10, 9, 64, 16, N, N), -1, "k=9"),
+    ("moe_combine", (16, 1, 10, 16, 16, 10, 2, 12, 16, N, N), -1, "multiple of 16"),
+    ("moe_check_device_error", (N, N, N), -1, "null check"),
+    ("moe_expert_ffn_profiled", (16, 1, 100, 128, 128, 8, 16, 16, 16, 8, 16, 16, 16, 0, 1, 16, 16, 1 << 30, N, N, N),
+     -1, "three events"),
 ])
 def test_argument_errors_are_reported_before_any_hip_call(call, args, status, msg):
     lib = _lib()

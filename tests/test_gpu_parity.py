@@ -223,6 +223,26 @@ def test_single_expert_top1_is_dense_ffn():
 
 
 # --------------------------------------------- full workload shapes, sampled
+def tail_tile_rows(expert_off, tile=256, trailing=4, stride=64):
+    """Rows chosen where the grouped GEMM's tiles are partial or re-listed: the
+    first and last row of every expert's last `tile`-row tile (a range of at most
+    64 rows is one 64-row tile), and one row per `stride` rows (plus the last) of
+    the table's last `trailing` tiles, which the launch may run again as 64-row
+    tiles.  Consecutive replica slots of an expert are tiled as one range, so the
+    expert ranges are the tile ranges."""
+    off = np.asarray(expert_off, np.int64)
+    rows, tiles = set(), []
+    for e in range(len(off) - 1):
+        a, b = int(off[e]), int(off[e + 1])
+        if b > a:
+            rows.update((b - 1, a + (b - 1 - a) // tile * tile))
+            tiles.extend((t0, min(t0 + tile, b)) for t0 in range(a, b, tile))
+    for t0, t1 in tiles[-trailing:]:
+        rows.update(range(t0, t1, stride))
+        rows.add(t1 - 1)
+    return np.array(sorted(rows), np.int64)
+
+
 def _sampled_layer_check(cfg, R, n_sample=12, seed=0):
     x = synth.hidden0(cfg, 0)
     lg = synth.logits(cfg, 0, 0)
@@ -236,10 +256,16 @@ def _sampled_layer_check(cfg, R, n_sample=12, seed=0):
         assert np.array_equal(from_dev(res[key]), d[key]), key
     S = d["n_slots"]
     assert np.array_equal(from_dev(res["slot_off"])[:S + 1], d["slot_off"])
+    kind = "bf16" if cfg.dtype == "bf16" else "fp32_gemm"
+    # y_perm rows in every expert's partial last tile and in the trailing tiles
+    rows = tail_tile_rows(d["expert_off"])
+    row_expert = np.repeat(np.arange(cfg.E, dtype=np.int32), np.diff(d["expert_off"]))
+    y_rows = oracle.ffn_rows(x[d["perm_src"][rows]], row_expert[rows], *wts, act=cfg.act)
+    assert_close(from_dev(res["y_perm"])[rows], y_rows, kind, f"y_perm rows of the tail tiles ({rows.size})")
+    # whole tokens (all k slots, combine): seeded sample
     sample = np.random.default_rng(seed).choice(cfg.T, size=n_sample, replace=False)
     y_ref, out_ref = oracle.token_forward(x[sample], idx_o[sample], w_o[sample], wts, cfg.act)
     y_gpu = from_dev(res["y_perm"])[d["inv_pos"][sample].ravel()].reshape(y_ref.shape)
-    kind = "bf16" if cfg.dtype == "bf16" else "fp32_gemm"
     assert_close(y_gpu, y_ref, kind, "sampled y_perm rows")
     assert_close(from_dev(res["out"])[sample], out_ref, kind, "sampled out rows")
     x_perm = from_dev(res["x_perm"])

@@ -256,6 +256,25 @@ def test_dispatch_textbook_and_bijection(E, k, T):
         assert len(sizes) == reps[e] + 1 and sizes.sum() == n[e] and sizes.max() - sizes.min() <= 1
 
 
+def test_dispatch_duplicate_indices_follow_the_pair_order():
+    """A token naming one expert twice (not a routing the top-k gate makes, but
+    a valid permutation input): rows follow the stable order of the flattened
+    (token, slot) pairs, so the token gets two rows of that expert in slot
+    order -- the textbook stable argsort, checked against a brute-force walk."""
+    rng = np.random.default_rng(11)
+    T, k, E = 40, 3, 5
+    idx = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    idx[0] = [2, 2, 2]
+    idx[7] = [4, 1, 4]
+    d = oracle.dispatch(idx, E)
+    assert np.array_equal(d["perm_src"], np.argsort(idx.ravel(), kind="stable") // k)
+    rows = [(e, t, i) for e in range(E) for t in range(T) for i in range(k) if idx[t, i] == e]
+    brute = np.empty(T * k, np.int32)
+    for r, (_, t, i) in enumerate(rows):
+        brute[t * k + i] = r
+    assert np.array_equal(d["inv_pos"].ravel(), brute)
+
+
 def test_dispatch_empty_experts_and_no_replicas():
     idx = np.array([[3, 1]] * 5, np.int32)
     d = oracle.dispatch(idx, 6)
