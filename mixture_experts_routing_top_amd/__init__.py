@@ -286,6 +286,9 @@ def moe_expert_ffn_profiled(x_perm: torch.Tensor, slot_off, slot_expert, n_slots
     the gate/up GEMM, after it, after the down GEMM."""
     M, H, I, E, max_slots, y_perm, workspace = _ffn_args(x_perm, slot_off, slot_expert, n_slots, w_gate, w_up,
                                                          w_down, y_perm, workspace)
+    for e in events:          # torch creates an event's handle on its first record
+        if not e.cuda_event:
+            e.record(stream if stream is not None else torch.cuda.current_stream())
     evs = (ctypes.c_void_p * 3)(*(e.cuda_event for e in events))
     _call("moe_expert_ffn_profiled", _ptr(x_perm), _dtype_code(x_perm), ctypes.c_int64(M), H, I, E, _ptr(slot_off),
           _ptr(slot_expert), _ptr(n_slots), max_slots, _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ACT[act],
