@@ -256,6 +256,24 @@ int moe_dispatch(const void* x, moe_dtype dt, int64_t T, int H, const int32_t* t
                  int32_t* slot_off, int32_t* slot_expert, int32_t* n_slots,
                  void* workspace, size_t workspace_bytes, int32_t* check, void* stream);
 
+/*
+ * moe_dispatch_noalloc -- moe_dispatch for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same arguments without the workspace, which is a
+ * static 8 MiB device array of the library instead (held by each GPU the
+ * library runs on until the process ends; its address is looked up once per
+ * device).  Calls no allocating routine.  Limit: moe_dispatch_workspace_bytes(
+ * T, k, E) <= 8 MiB (e.g. T*k <= 2^20 pairs at E = 256), else
+ * MOE_ERR_WORKSPACE.  Every call on one GPU shares the array: calls that
+ * overlap on one GPU (different streams, or threads) race and must be
+ * serialised by the caller.  Nothing in it needs clearing between calls (each
+ * call writes every word it reads).  Same results as moe_dispatch.
+ */
+int moe_dispatch_noalloc(const void* x, moe_dtype dt, int64_t T, int H, const int32_t* topk_idx, int k, int E,
+                         const int32_t* counts, const int32_t* replicas, int max_slots,
+                         void* x_perm, int32_t* perm_src, int32_t* inv_pos, int32_t* expert_off,
+                         int32_t* slot_off, int32_t* slot_expert, int32_t* n_slots, int32_t* check, void* stream);
+
 /* ------------------------------------------------------------- expert FFN
  * moe_expert_ffn -- every slot's rows through its expert's FFN ([EPS] section
  * 3: the gate, up and down GEMMs; GroupGemm runs all experts in one kernel,

@@ -32,7 +32,7 @@ __all__ = ["moe_route", "moe_stats_state_bytes", "moe_stats_init", "moe_stats", 
            "moe_prediction_quality", "moe_dispatch_workspace_bytes",
            "moe_dispatch", "moe_expert_ffn_workspace_bytes", "moe_expert_ffn", "moe_combine", "moe_layer_forward",
            "moe_layer_forward_pipelined", "moe_backward_workspace_bytes", "moe_backward", "moe_check_device_error",
-           "moe_expert_ffn_profiled", "new_check_word", "CHECK_BITS",
+           "moe_expert_ffn_profiled", "new_check_word", "CHECK_BITS", "moe_dispatch_noalloc",
            "MoEError", "LIB_PATH", "MOE_F32", "MOE_BF16", "SWIGLU", "GELU", "GEMM_AUTO", "GEMM_GROUPED",
            "GEMM_DENSE", "GEMM_GROUPED_SMALL"]
 
@@ -242,6 +242,30 @@ def moe_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, E: int, replicas=None,
           _ptr(replicas), max_slots, _ptr(o["x_perm"]), _ptr(o["perm_src"]), _ptr(o["inv_pos"]),
           _ptr(o["expert_off"]), _ptr(o["slot_off"]), _ptr(o["slot_expert"]), _ptr(o["n_slots"]), _ptr(workspace),
           ctypes.c_size_t(workspace.numel() * workspace.element_size()), _ptr(check), _stream(stream))
+    return o
+
+
+def moe_dispatch_noalloc(x: torch.Tensor, topk_idx: torch.Tensor, E: int, replicas=None, max_slots=None, out=None,
+                         stream=None, counts=None, check=None):
+    """moe_dispatch on the library's static device scratch (no workspace): for
+    callers that cannot allocate.  `out` must hold every output (nothing is
+    allocated here).  Calls that overlap on one GPU race."""
+    T, H = x.shape
+    if topk_idx.shape[0] != T or topk_idx.dtype != torch.int32:
+        raise ValueError("topk_idx must be int32 [T, k] for the T rows of x")
+    k = topk_idx.shape[1]
+    max_slots = E if max_slots is None else max_slots
+    need = ("x_perm", "perm_src", "inv_pos", "expert_off", "slot_off", "slot_expert", "n_slots")
+    if out is None or any(key not in out for key in need):
+        raise ValueError(f"moe_dispatch_noalloc allocates nothing: out must hold {need}")
+    for t, name in ((replicas, "replicas"), (counts, "counts")):
+        if t is not None and (t.numel() != E or t.dtype != torch.int32):
+            raise ValueError(f"{name} must be int32 [E]")
+    o = _dispatch_outputs(out, T, k, H, E, max_slots, x.dtype, x.device)
+    _call("moe_dispatch_noalloc", _ptr(x), _dtype_code(x), ctypes.c_int64(T), H, _ptr(topk_idx), k, E, _ptr(counts),
+          _ptr(replicas), max_slots, _ptr(o["x_perm"]), _ptr(o["perm_src"]), _ptr(o["inv_pos"]),
+          _ptr(o["expert_off"]), _ptr(o["slot_off"]), _ptr(o["slot_expert"]), _ptr(o["n_slots"]), _ptr(check),
+          _stream(stream))
     return o
 
 

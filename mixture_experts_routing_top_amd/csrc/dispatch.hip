@@ -24,6 +24,8 @@
 //               rows: four 16-byte chunks per thread, read once, written k
 //               times with nontemporal stores (measured ~25% faster than cached
 //               stores on this write-heavy copy).
+#include <mutex>
+
 #include "common.h"
 
 namespace {
@@ -235,6 +237,33 @@ __global__ __launch_bounds__(256) void permute_kernel(const uint4* __restrict__ 
   }
 }
 
+// Device scratch of moe_dispatch_noalloc: the workspace of one call, in a
+// file-scope array each GPU holds for the life of the process (8 MiB: up to
+// 2^20 (token, slot) pairs at E = 256).  Host code uses it only through the
+// address hipGetSymbolAddress returns for the current device.
+constexpr size_t kScratchBytes = size_t(8) << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch address on the current device, looked up once per device.
+int scratch_on_current_device(void** out) {
+  int dev = -1;
+  if (int rc = moe::hip_status(hipGetDevice(&dev), "moe_dispatch_noalloc hipGetDevice")) return rc;
+  if (dev < 0 || dev >= kMaxDevices) return moe::fail(MOE_ERR_UNSUPPORTED, "moe_dispatch_noalloc: device %d", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (int rc = moe::hip_status(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "moe_dispatch_noalloc scratch"))
+      return rc;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" size_t moe_dispatch_workspace_bytes(int64_t T, int k, int E) {
@@ -283,4 +312,22 @@ extern "C" int moe_dispatch(const void* x, moe_dtype dt, int64_t T, int H, const
         static_cast<uint4*>(x_perm));
   }
   return hip_status(hipGetLastError(), "moe_dispatch launch");
+}
+
+extern "C" int moe_dispatch_noalloc(const void* x, moe_dtype dt, int64_t T, int H, const int32_t* topk_idx, int k,
+                                    int E, const int32_t* counts, const int32_t* replicas, int max_slots, void* x_perm,
+                                    int32_t* perm_src, int32_t* inv_pos, int32_t* expert_off, int32_t* slot_off,
+                                    int32_t* slot_expert, int32_t* n_slots, int32_t* check, void* stream) {
+  using namespace moe;
+  if (E >= 1 && E <= kMaxExperts && k >= 1 && k <= kMaxTopK && T >= 0 && T * k < (int64_t(1) << 31)) {
+    const size_t need = ws_layout(T, k, E).bytes;
+    if (need > kScratchBytes)
+      return fail(MOE_ERR_WORKSPACE, "moe_dispatch_noalloc: T=%lld, k=%d, E=%d needs %zu bytes of scratch; the "
+                  "static scratch holds %zu (use moe_dispatch with a workspace)", (long long)T, k, E, need,
+                  kScratchBytes);
+  }
+  void* ws = nullptr;
+  if (int rc = scratch_on_current_device(&ws)) return rc;
+  return moe_dispatch(x, dt, T, H, topk_idx, k, E, counts, replicas, max_slots, x_perm, perm_src, inv_pos, expert_off,
+                      slot_off, slot_expert, n_slots, ws, kScratchBytes, check, stream);
 }
