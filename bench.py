@@ -57,6 +57,8 @@ def parse():
                     help="with --crossover: comma-separated tilings to time")
     ap.add_argument("--configs", action="store_true",
                     help="routed tokens/s and roofline fraction of every workload (one line each)")
+    ap.add_argument("--stats", action="store_true",
+                    help="time moe_stats with co-occurrence (a chained layer) on the workloads' shapes")
     ap.add_argument("--backward", action="store_true",
                     help="time the layer's backward pass (moe_backward) on the Mixtral layer")
     ap.add_argument("--pipeline", action="store_true",
@@ -606,6 +608,41 @@ def configs_bench(moe, synth, torch, np, steps=10, warmup=3):
     chain("PopFetcher-shaped (12-layer chain)", C["popfetcher"], 0)
 
 
+def stats_bench(moe, synth, torch, np, reps=20):
+    """moe_stats of a chained layer (counts, co-occurrence with the previous
+    layer, window popularity, conditional matrix, prediction, replicas) on each
+    workload's routing shape; median of `reps` event-timed calls."""
+    dev = torch.device("cuda:0")
+    out = []
+    for name, T, E, k, R in (("Mixtral", 8192, 8, 2, 8), ("DBRX", 4096, 16, 4, 16), ("PopFetcher", 16384, 32, 2, 0),
+                             ("DeepSeek-V2", 16384, 160, 6, 0), ("DeepSeek-V2", 4096, 160, 6, 0),
+                             ("E=256 top-8", 16384, 256, 8, 0)):
+        rng = np.random.default_rng(T + E)
+        idx = [moe.moe_route(torch.from_numpy((rng.standard_normal((T, E)) -
+                                               np.log1p(rng.permutation(E))).astype(np.float32)).to(dev), k)[0]
+               for _ in range(2)]
+        L, win = 3, 10
+        state = torch.empty(moe.moe_stats_state_bytes(L, E, win), dtype=torch.uint8, device=dev)
+        moe.moe_stats_init(state, L, E, win)
+        o = {n: torch.empty(sz, dtype=dt, device=dev) for n, sz, dt in
+             (("c", E, torch.int32), ("p", E, torch.float32), ("P", E * E, torch.float32), ("h", E, torch.float32),
+              ("r", E, torch.int32))}
+        ts = []
+        for it in range(reps + 3):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            moe.moe_stats(state, L, E, win, 1, it, idx[1], idx[0], k, o["c"], o["p"], o["P"], o["h"], R,
+                          o["r"] if R else None)
+            b.record()
+            torch.cuda.synchronize()
+            if it >= 3:
+                ts.append(a.elapsed_time(b) * 1e3)
+        out.append({"workload": name, "T": T, "E": E, "k": k, "replica_budget": R,
+                    "cooccurrence_in": "lds (packed 16-bit)" if E * E <= 32768 else "global atomics",
+                    "us_median": round(float(np.median(ts)), 2)})
+    return {"stats": out}
+
+
 def backward_bench(moe, synth, torch, np, steps=5, warmup=2):
     """The layer's backward pass on the Mixtral-shaped layer (no replication):
     gradients w.r.t. x, the router logits and all expert weights."""
@@ -738,6 +775,9 @@ def main():
         return
     if a.backward:
         print(json.dumps(backward_bench(moe, synth, torch, np)), flush=True)
+        return
+    if a.stats:
+        print(json.dumps(stats_bench(moe, synth, torch, np)), flush=True)
         return
     if a.pipeline:
         print(json.dumps(pipeline_bench(moe, synth, torch, np)), flush=True)

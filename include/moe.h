@@ -103,8 +103,9 @@ int moe_route(const float* logits, int64_t T, int E, int k, int32_t* topk_idx, f
  *
  * The state is a caller-owned device buffer of moe_stats_state_bytes(L, E,
  * window) bytes holding, per layer, a ring of `window` per-iteration count
- * vectors, per adjacent layer pair a ring of E x E co-occurrence matrices, and
- * a small accumulator.  It is plain memory: a checkpoint is a byte copy.
+ * vectors, per adjacent layer pair a ring of E x E co-occurrence matrices and
+ * their running sum over the ring, and a small accumulator.  It is plain
+ * memory: a checkpoint is a byte copy.
  * moe_stats_init zeroes it (enqueued on `stream`).
  *
  * moe_stats records layer `layer` of iteration `iter` and reports:

@@ -28,10 +28,13 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kTokPerBlock = 512;
-constexpr int kLdsCooc = 128 * 128;  // co-occurrence kept in LDS when E*E fits
+// One block's co-occurrence counts are at most 512 tokens x k^2 = 32768 per
+// cell, so while recording, two 16-bit counters share one LDS word: E*E up to
+// 32768 cells (E <= 181) stays in LDS; larger E adds into global memory.
+constexpr int kLdsCooc = 128 * 128;  // LDS words for co-occurrence
 
 struct Layout {
-  size_t cnt_ring, cooc_ring, acc, acc_cooc, ticket, words;
+  size_t cnt_ring, cooc_ring, cooc_sum, acc, acc_cooc, ticket, words;
 };
 
 Layout layout(int L, int E, int window) {
@@ -40,6 +43,7 @@ Layout layout(int L, int E, int window) {
   auto take = [&](size_t n) { size_t at = w; w = moe::align_up(w + n, 64); return at; };
   q.cnt_ring = take(static_cast<size_t>(window) * L * E);
   q.cooc_ring = take(static_cast<size_t>(window) * (L - 1) * E * E);
+  q.cooc_sum = take(static_cast<size_t>(L - 1) * E * E);  // running sum of each pair's ring
   q.acc = take(E);
   q.acc_cooc = take(L > 1 ? static_cast<size_t>(E) * E : 0);
   q.ticket = take(1);
@@ -64,7 +68,7 @@ struct Args {
 
 __global__ __launch_bounds__(kThreads) void stats_kernel(Args a) {
   __shared__ int32_t hist[moe::kMaxExperts];
-  __shared__ int32_t cooc[kLdsCooc];
+  __shared__ int32_t cooc[kLdsCooc];   // packed 16-bit counters of one block
   __shared__ int32_t nw[moe::kMaxExperts];
   __shared__ int32_t rowsum[moe::kMaxExperts];
   __shared__ float ps[moe::kMaxExperts];
@@ -74,7 +78,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(Args a) {
   const int E = a.E, k = a.k, tid = threadIdx.x;
   const int EE = E * E;
   const bool do_cooc = a.idx && a.layer > 0;
-  const bool lds_cooc = EE <= kLdsCooc;
+  const bool lds_cooc = EE <= 2 * kLdsCooc;  // recording in LDS (packed)
   int32_t* acc = a.state + a.lay.acc;
   int32_t* acc_cooc = a.state + a.lay.acc_cooc;
   unsigned* ticket = reinterpret_cast<unsigned*>(a.state + a.lay.ticket);
@@ -82,7 +86,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(Args a) {
   if (a.idx) {
     for (int e = tid; e < E; e += kThreads) hist[e] = 0;
     if (do_cooc && lds_cooc)
-      for (int q = tid; q < EE; q += kThreads) cooc[q] = 0;
+      for (int q = tid; q < (EE + 1) / 2; q += kThreads) cooc[q] = 0;
     __syncthreads();
     const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kTokPerBlock;
     const int64_t t1 = min(a.T, t0 + kTokPerBlock);
@@ -116,8 +120,9 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(Args a) {
 #pragma unroll
           for (int j = 0; j < moe::kMaxTopK; ++j) {
             if (j < k && cur[j] >= 0) {
-              if (lds_cooc) atomicAdd(&cooc[p * E + cur[j]], 1);
-              else atomicAdd(&acc_cooc[p * E + cur[j]], 1);
+              const int q = p * E + cur[j];
+              if (lds_cooc) atomicAdd(reinterpret_cast<unsigned*>(&cooc[q >> 1]), 1u << (16 * (q & 1)));
+              else atomicAdd(&acc_cooc[q], 1);
             }
           }
         }
@@ -131,8 +136,11 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(Args a) {
     for (int e = tid; e < E; e += kThreads)
       if (hist[e]) atomicAdd(&acc[e], hist[e]);
     if (do_cooc && lds_cooc)
-      for (int q = tid; q < EE; q += kThreads)
-        if (cooc[q]) atomicAdd(&acc_cooc[q], cooc[q]);
+      for (int q = tid; q < (EE + 1) / 2; q += kThreads) {
+        const unsigned v = static_cast<unsigned>(cooc[q]);
+        if (v & 0xffffu) atomicAdd(&acc_cooc[2 * q], static_cast<int32_t>(v & 0xffffu));
+        if (v >> 16) atomicAdd(&acc_cooc[2 * q + 1], static_cast<int32_t>(v >> 16));
+      }
     __threadfence();
     __syncthreads();
     if (tid == 0) is_last = (atomicAdd(ticket, 1u) == gridDim.x - 1);
@@ -154,8 +162,15 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(Args a) {
       if (a.counts) a.counts[e] = c;
     }
     if (do_cooc) {
+      // the pair's ring slot is replaced and its running window sum updated by
+      // the difference (exact integers: the sum over the ring, one load per cell)
       int32_t* cdst = cooc_ring + (static_cast<size_t>(slot) * (L - 1) + (layer - 1)) * EE;
-      for (int q = tid; q < EE; q += kThreads) cdst[q] = atomicExch(&acc_cooc[q], 0);
+      int32_t* csum = a.state + a.lay.cooc_sum + static_cast<size_t>(layer - 1) * EE;
+      for (int q = tid; q < EE; q += kThreads) {
+        const int32_t c = atomicExch(&acc_cooc[q], 0);
+        csum[q] += c - cdst[q];
+        cdst[q] = c;
+      }
     }
     __threadfence();
   }
@@ -181,24 +196,16 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(Args a) {
 
   // Eq.(2)-(3): conditional matrix of pair (layer, layer+1) and the prediction.
   if (layer + 1 < L && (a.cond || a.pred)) {
-    const int32_t* ring = cooc_ring + static_cast<size_t>(layer) * EE;
-    const size_t ring_stride = static_cast<size_t>(L - 1) * EE;
-    auto window_cooc = [&](int q) {
-      int32_t s = 0;
-#pragma unroll 8
-      for (int w = 0; w < window; ++w) s += ring[w * ring_stride + q];
-      return s;
-    };
+    const int32_t* win = a.state + a.lay.cooc_sum + static_cast<size_t>(layer) * EE;  // window sums
     for (int e = tid; e < E; e += kThreads) rowsum[e] = 0;
     __syncthreads();
     for (int q = tid; q < EE; q += kThreads) {
-      const int32_t c = window_cooc(q);
-      if (lds_cooc) cooc[q] = c;
+      const int32_t c = win[q];
       if (c) atomicAdd(&rowsum[q / E], c);
     }
     __syncthreads();
     auto prob = [&](int q) {
-      const int32_t c = lds_cooc ? cooc[q] : window_cooc(q);
+      const int32_t c = win[q];
       const int32_t r = rowsum[q / E];
       return r ? __fdiv_rn(static_cast<float>(c), static_cast<float>(r)) : 0.f;
     };
@@ -207,6 +214,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(Args a) {
     if (a.pred)
       for (int b = tid; b < E; b += kThreads) {
         double s = 0.0;
+#pragma unroll 8
         for (int x = 0; x < E; ++x) s += static_cast<double>(ps[x]) * static_cast<double>(prob(x * E + b));
         a.pred[b] = static_cast<float>(s);
       }
