@@ -34,7 +34,8 @@ constexpr int kBigM = 256;    // grouped path: 256-row tiles
 constexpr int kSmallM = 64;   // dense path: 64-row tiles
 
 struct WsLayout {
-  size_t h, tab_slot[3], tab_row0[3], tab_rend[3], n_tiles, split_slot, split_row0, split_rend, split_counts, bytes;
+  size_t h, tab_slot[3], tab_row0[3], tab_rend[3], n_tiles, split_slot, split_row0, split_rend, split_counts,
+      mid_slot, mid_row0, mid_rend, alt_slot, alt_row0, alt_rend, bytes;
   int cap[3];     // tile capacity of each table
   int split_cap;  // entries of each GEMM's 64-row companion table
 };
@@ -73,7 +74,13 @@ WsLayout ws_layout(moe_dtype dt, int64_t M, int I, int max_slots) {
   w.split_slot = take(2 * sizeof(int32_t) * w.split_cap);
   w.split_row0 = take(2 * sizeof(int32_t) * w.split_cap);
   w.split_rend = take(2 * sizeof(int32_t) * w.split_cap);
-  w.split_counts = take(4 * sizeof(int32_t));
+  w.split_counts = take(8 * sizeof(int32_t));
+  w.mid_slot = take(sizeof(int32_t) * max_slots);  // at most one 128-row tile per range
+  w.mid_row0 = take(sizeof(int32_t) * max_slots);
+  w.mid_rend = take(sizeof(int32_t) * max_slots);
+  w.alt_slot = take(sizeof(int32_t) * w.cap[kG256]);  // the gate/up GEMM's 256-row table without 128-row tails
+  w.alt_row0 = take(sizeof(int32_t) * w.cap[kG256]);
+  w.alt_rend = take(sizeof(int32_t) * w.cap[kG256]);
   w.bytes = at;
   return w;
 }
@@ -84,24 +91,26 @@ hipError_t mark(hipEvent_t const* ev, int i, hipStream_t s) {
   return ev ? hipEventRecord(ev[i], s) : hipSuccess;
 }
 
-// A 256-row tiling runs with its 64-row companion table in one mixed launch;
-// the 64-row tilings run alone.
+// A 256-row tiling runs with its 128-row and 64-row companion tables in one
+// mixed launch; the 64-row tilings run alone.
 template <bool kBf16, int EPI, int NMAT>
-void launch_gemm(bool small, const GemmArgs& p, const GemmArgs& companion, unsigned grid, hipStream_t s) {
+void launch_gemm(bool small, const GemmArgs& p, const GemmArgs& mid, const GemmArgs& companion, unsigned grid,
+                 hipStream_t s) {
   if (small) gemm_kernel<kBf16, NMAT, EPI, kSmallM, 1><<<grid, 256, 0, s>>>(p);
-  else gemm_mixed_kernel<kBf16, NMAT, EPI><<<grid, 256, 0, s>>>(p, companion);
+  else gemm_mixed_kernel<kBf16, NMAT, EPI><<<grid, 256, 0, s>>>(p, mid, companion);
 }
 
 // Phase 1 (gate/up or W1) and phase 2 (down or W2), each on its own tile table.
 template <bool kBf16>
-int launch_ffn(const GemmArgs& p1, bool small1, unsigned grid1, const GemmArgs& t1, const GemmArgs& p2, bool small2,
-               unsigned grid2, const GemmArgs& t2, bool swiglu, hipEvent_t const* ev, hipStream_t s) {
+int launch_ffn(const GemmArgs& p1, bool small1, unsigned grid1, const GemmArgs& m1, const GemmArgs& t1,
+               const GemmArgs& p2, bool small2, unsigned grid2, const GemmArgs& m2, const GemmArgs& t2, bool swiglu,
+               hipEvent_t const* ev, hipStream_t s) {
   if (int rc = moe::hip_status(mark(ev, 0, s), "moe_expert_ffn timing event")) return rc;
-  if (swiglu) launch_gemm<kBf16, kEpiSwiGLU, 2>(small1, p1, t1, grid1, s);
-  else launch_gemm<kBf16, kEpiGELU, 1>(small1, p1, t1, grid1, s);
+  if (swiglu) launch_gemm<kBf16, kEpiSwiGLU, 2>(small1, p1, m1, t1, grid1, s);
+  else launch_gemm<kBf16, kEpiGELU, 1>(small1, p1, m1, t1, grid1, s);
   if (int rc = moe::hip_status(hipGetLastError(), "moe_expert_ffn gate/up launch")) return rc;
   if (int rc = moe::hip_status(mark(ev, 1, s), "moe_expert_ffn timing event")) return rc;
-  launch_gemm<kBf16, kEpiStore, 1>(small2, p2, t2, grid2, s);
+  launch_gemm<kBf16, kEpiStore, 1>(small2, p2, m2, t2, grid2, s);
   if (int rc = moe::hip_status(hipGetLastError(), "moe_expert_ffn down launch")) return rc;
   return moe::hip_status(mark(ev, 2, s), "moe_expert_ffn timing event");
 }
@@ -118,6 +127,7 @@ Kind pick_kind(int64_t g256, int64_t g256_rem, int64_t d64, int64_t g64, int col
   auto cost = [&](double tiles) {
     return std::max(tiles * col_tiles, static_cast<double>(kComputeUnits));
   };
+  // g256_rem: the 256-row tiling's 64- and 128-row tiles (both at kSmallCost)
   const double c256 = cost(static_cast<double>(g256) + kSmallCost * static_cast<double>(g256_rem));
   const double cd64 = kSmallCost * cost(static_cast<double>(d64)), cg64 = kSmallCost * cost(static_cast<double>(g64));
   if (cg64 < c256 && cg64 <= cd64) return kG64;
@@ -191,6 +201,14 @@ int ffn_impl(const void* x_perm, moe_dtype dt, int64_t M, int H, int I, int E, c
 
   const hipStream_t s = as_stream(stream);
   const int nt1 = static_cast<int>(ceil_div(I, act == MOE_SWIGLU ? kTileN / 2 : kTileN));
+  // The gate/up GEMM runs a range's last tile of at most 128 rows as a 128-row
+  // tile when it is bf16 SwiGLU (a register epilogue) and wide (>= 32 column
+  // tiles: its launch is many rounds long, so the saved MFMA work outweighs
+  // the tail the shorter tiles add).  The down GEMM keeps the 256-row tiles:
+  // there the extra blocks land in an already short last round (measured
+  // slower on the Mixtral shape).
+  const bool gateup_mid = dt == MOE_BF16 && act == MOE_SWIGLU && nt1 >= 32;
+  const int mid_cap_rows = gateup_mid ? 128 : 0;
   const int nt2 = static_cast<int>(ceil_div(H, kTileN));
   // GROUPED: 256-row tiles covering each slot.  GROUPED_SMALL: 64-row tiles
   // covering each slot.  DENSE: the padded batch in 64-row tiles.  AUTO: per
@@ -198,7 +216,7 @@ int ffn_impl(const void* x_perm, moe_dtype dt, int64_t M, int H, int I, int E, c
   Kind k1 = path == MOE_GEMM_DENSE ? kD64 : path == MOE_GEMM_GROUPED_SMALL ? kG64 : kG256, k2 = k1;
   int m_pad = 0;
   int64_t exact[3] = {-1, -1, -1};  // tiles per kind, when known on the host
-  int64_t exact_rem = -1;             // the 256-row tiling's 64-row short-range tiles
+  int64_t exact_rem = -1;             // the 256-row tiling's 64-row short-range and 128-row tiles
   if (path == MOE_GEMM_DENSE || path == MOE_GEMM_AUTO) {
     // slot sizes, with consecutive slots of one expert merged into one range
     // exactly as the tile tables merge them
@@ -211,7 +229,7 @@ int ffn_impl(const void* x_perm, moe_dtype dt, int64_t M, int H, int I, int E, c
                                            hipMemcpyDeviceToHost, s), "moe_expert_ffn slot readback")) return rc;
     if (int rc = hip_status(hipStreamSynchronize(s), "moe_expert_ffn slot readback")) return rc;
     const int n = std::min(std::max(off[max_slots + 1], 0), max_slots);
-    int64_t largest = 0, active = 0, g256 = 0, g256_rem = 0, g64 = 0;
+    int64_t largest = 0, active = 0, g256 = 0, g256_rem = 0, g256_mid = 0, g64 = 0;
     for (int i = 0; i < n;) {
       int last = i + 1;
       while (last < n && se[last] == se[i]) ++last;
@@ -220,10 +238,12 @@ int ffn_impl(const void* x_perm, moe_dtype dt, int64_t M, int H, int I, int E, c
       largest = std::max(largest, r);
       if (r > 0) ++active;
       // the 256-row tiling: a range of at most kRemTiles x 64 rows as 64-row
-      // tiles, else 256-row tiles (the tile tables' rule)
+      // tiles, else 256-row tiles; for the gate/up GEMM the last as a 128-row
+      // tile when it holds at most 128 rows (the tile tables' rule)
       const bool short_range = r > 0 && r <= static_cast<int64_t>(kRemTiles) * kSmallM;
       g256 += short_range ? 0 : ceil_div(r, kBigM);
       g256_rem += short_range ? ceil_div(r, kSmallM) : 0;
+      g256_mid += !short_range && mid_cap_rows > 0 && r % kBigM > 0 && r % kBigM <= mid_cap_rows;
       g64 += ceil_div(r, kSmallM);
       i = last;
     }
@@ -233,7 +253,7 @@ int ffn_impl(const void* x_perm, moe_dtype dt, int64_t M, int H, int I, int E, c
     exact[kD64] = active * (m_pad / kSmallM);
     exact[kG64] = g64;
     if (path == MOE_GEMM_AUTO) {
-      k1 = pick_kind(g256, g256_rem, exact[kD64], g64, nt1);
+      k1 = pick_kind(g256 - g256_mid, g256_rem + g256_mid, exact[kD64], g64, nt1);
       k2 = pick_kind(g256, g256_rem, exact[kD64], g64, nt2);
     }
   }
@@ -242,15 +262,16 @@ int ffn_impl(const void* x_perm, moe_dtype dt, int64_t M, int H, int I, int E, c
 
   // Grids: exact tile counts when read back, else bounds; blocks past the
   // tables exit at once.  A 256-row tiling's tables hold at most
-  // floor(M / 256) + (ranges x max(1, kRemTiles)) tiles, ranges <= max_slots,
-  // plus 3 more per re-listed trailing row tile (at most ceil(256 / nt) of
-  // those), plus the rounding of the 256-row part to 8 blocks.
+  // floor(M / 256) + (ranges x max(1, kRemTiles)) tiles, ranges <= max_slots
+  // (a range's 128-row tile takes the place of its last 256-row tile), plus 3
+  // more per re-listed trailing row tile (at most ceil(256 / nt) of those),
+  // plus the rounding of the 256- and 128-row parts to 8 blocks each.
   auto grid = [&](Kind t, int nt) {
     int64_t blocks;
     if (t == kG256) {
       const int64_t both = exact[kG256] >= 0 ? exact[kG256] + exact_rem
                                              : M / kBigM + static_cast<int64_t>(max_slots) * std::max(1, kRemTiles);
-      blocks = both * nt + 3 * ceil_div(kWaveBlocks, nt) * nt + 8;
+      blocks = both * nt + 3 * ceil_div(kWaveBlocks, nt) * nt + 16;
     } else {
       blocks = (exact[t] >= 0 ? exact[t] : static_cast<int64_t>(w.cap[t])) * nt;
     }
@@ -282,6 +303,14 @@ int ffn_impl(const void* x_perm, moe_dtype dt, int64_t M, int H, int I, int E, c
   split.row0 = reinterpret_cast<int32_t*>(ws + w.split_row0);
   split.rend = reinterpret_cast<int32_t*>(ws + w.split_rend);
   split.counts = split_counts;
+  const bool mid1 = gateup_mid && k1 == kG256;
+  split.mid_rows = mid1 ? 128 : 0;
+  split.mid_slot = reinterpret_cast<int32_t*>(ws + w.mid_slot);
+  split.mid_row0 = reinterpret_cast<int32_t*>(ws + w.mid_row0);
+  split.mid_rend = reinterpret_cast<int32_t*>(ws + w.mid_rend);
+  split.alt_slot = reinterpret_cast<int32_t*>(ws + w.alt_slot);
+  split.alt_row0 = reinterpret_cast<int32_t*>(ws + w.alt_row0);
+  split.alt_rend = reinterpret_cast<int32_t*>(ws + w.alt_rend);
   auto build = [&](Kind t) {
     const int mode = t == kD64 ? kPadded : kCover;
     const int bm = t == kG256 ? kBigM : kSmallM;
@@ -322,6 +351,11 @@ int ffn_impl(const void* x_perm, moe_dtype dt, int64_t M, int H, int I, int E, c
   };
   on(p1, k1, 0);
   on(p2, k2, 1);
+  if (mid1) {  // the gate/up GEMM's 256-row table without its 128-row tails
+    p1.tile_slot = split.alt_slot;
+    p1.tile_row0 = split.alt_row0;
+    p1.tile_rend = split.alt_rend;
+  }
   // the 64-row companion tables of the mixed launches
   auto companion = [&](const GemmArgs& g, int which) {
     GemmArgs q = g;
@@ -332,9 +366,21 @@ int ffn_impl(const void* x_perm, moe_dtype dt, int64_t M, int H, int I, int E, c
     return q;
   };
   const GemmArgs t1 = companion(p1, 0), t2 = companion(p2, 1);
+  // the 128-row table of the gate/up GEMM (count split_counts[4]; empty when
+  // not used); the down GEMM's is always empty (split_counts[5] = 0)
+  auto mid_table = [&](const GemmArgs& g, int which) {
+    GemmArgs q = g;
+    q.tile_slot = split.mid_slot;
+    q.tile_row0 = split.mid_row0;
+    q.tile_rend = split.mid_rend;
+    q.n_tiles = split_counts + 4 + which;
+    return q;
+  };
+  const GemmArgs m1 = mid_table(p1, 0), m2 = mid_table(p2, 1);
   const bool swiglu = act == MOE_SWIGLU;
-  return dt == MOE_BF16 ? launch_ffn<true>(p1, k1 != kG256, grid1, t1, p2, k2 != kG256, grid2, t2, swiglu, ev, s)
-                        : launch_ffn<false>(p1, k1 != kG256, grid1, t1, p2, k2 != kG256, grid2, t2, swiglu, ev, s);
+  return dt == MOE_BF16
+             ? launch_ffn<true>(p1, k1 != kG256, grid1, m1, t1, p2, k2 != kG256, grid2, m2, t2, swiglu, ev, s)
+             : launch_ffn<false>(p1, k1 != kG256, grid1, m1, t1, p2, k2 != kG256, grid2, m2, t2, swiglu, ev, s);
 }
 
 }  // namespace

@@ -186,7 +186,7 @@ __device__ __forceinline__ void store4(uint16_t* p, const float v[4]) {
 // staging tile where that is larger).
 template <bool kBf16, int NMAT, int EPI, int BM, int WM, bool kWgrad>
 constexpr int gemm_lds_bytes() {
-  constexpr bool kDTL = kBf16 && BM == 256;
+  constexpr bool kDTL = kBf16 && (BM == 256 || BM == 128);
   constexpr bool kDTL64 = kBf16 && BM == 64 && !kWgrad;
   constexpr int kStageBytes = (BM + kTileN) * kRowBytes;
   constexpr int kStagedEpi = (!kWgrad && (EPI == kEpiGELU || EPI == kEpiSwiGLUGrad || EPI == kEpiGELUGrad))
@@ -220,11 +220,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs g, const int b) {
   constexpr int NM = TM * TN;              // MFMAs per sub-step
   constexpr int kStageBytes = (BM + kTileN) * kRowBytes;
   static_assert(NM >= NR, "sub-step pattern assumes at least one MFMA per fragment read");
-  // bf16 tiles load their operands straight into LDS (160 KiB, unpadded rows):
-  // 256-row tiles (weight gradients included) in two A stages and three weight
+  // bf16 tiles load their operands straight into LDS (unpadded rows): 256- and
+  // 128-row tiles (weight gradients included) in two A stages and three weight
   // stages, 64-row tiles in four stages of both; fp32 tiles stage them through
   // registers into two padded stages
-  constexpr bool kDTL = kBf16 && BM == 256;
+  constexpr bool kDTL = kBf16 && (BM == 256 || BM == 128);
   constexpr bool kDTL64 = kBf16 && BM == 64 && !kWgrad;
   constexpr int kLdsBytes = gemm_lds_bytes<kBf16, NMAT, EPI, BM, WM, kWgrad>();
 
@@ -372,7 +372,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs g, const int b) {
     constexpr int SBW = kTileN * 128;  // one weight stage (three of them, after the A stages)
     constexpr int PA_ = BM / 32;       // A blocks (8 rows) per wave per step
     constexpr int PB_ = kTileN / 32;   // weight blocks per wave per step
-    static_assert(!kDTL || (PA_ == 8 && PB_ == 8), "issue pattern assumes 8 + 8 blocks per wave");
+    static_assert(!kDTL || ((PA_ == 8 || PA_ == 4) && PB_ == 8 && NM >= 8),
+                  "issue pattern: 8 or 4 A blocks and 8 weight blocks per wave, 3/3/2 weight blocks over the "
+                  "first three sub-steps and the A blocks in the fourth, one per odd MFMA");
     const int rb_ = static_cast<int>(row_b);
     const u32x4 da = dma_rsrc(A, static_cast<int64_t>(m_valid) * row_b);
     const u32x4 db0 = dma_rsrc(static_cast<const T*>(g.B0) + wofs, static_cast<int64_t>(n_valid) * row_b);
@@ -903,20 +905,40 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   gemm_tile<kBf16, NMAT, EPI, BM, WM, kWgrad>(g, static_cast<int>(blockIdx.x));
 }
 
-// A 256-row tile table and a 64-row one in one launch: the first
-// round_up(n_big * nt, 8) blocks run the 256-row tiles (the rounding keeps
-// every block's index congruent to its XCD in both parts), the blocks after
-// them the 64-row tiles, which are dispatched last and so fill the CUs that
-// the last round of 256-row tiles leaves idle.  Blocks past both exit.
+// 128-row tiles exist for bf16 operands with a register epilogue (the staged
+// GELU epilogue needs a 256-column staging tile of 128 rows that does not fit).
+template <bool kBf16, int EPI>
+constexpr bool kHasMidTiles = kBf16 && (EPI == kEpiSwiGLU || EPI == kEpiStore);
+
+// A 256-row tile table, a 128-row one and a 64-row one in one launch: the
+// first round_up(n_big * nt, 8) blocks run the 256-row tiles, the next
+// round_up(n_mid * nt, 8) the 128-row tiles (ranges' last tiles of at most 128
+// rows), the blocks after them the 64-row tiles (short ranges and re-listed
+// trailing tiles); the roundings keep every block's index congruent to its XCD
+// in each part.  The shorter tiles are dispatched last and so fill the CUs
+// that the last round of 256-row tiles leaves idle.  Blocks past all exit.
 template <bool kBf16, int NMAT, int EPI>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_mixed_kernel(GemmArgs big,
+                                                                                                   GemmArgs mid,
                                                                                                    GemmArgs small) {
   static_assert(gemm_lds_bytes<kBf16, NMAT, EPI, 256, 2, false>() <= kGemmLdsBytes, "LDS");
   static_assert(gemm_lds_bytes<kBf16, NMAT, EPI, 64, 1, false>() <= kGemmLdsBytes, "LDS");
   const int nb = (*big.n_tiles * big.n_col_tiles + 7) & ~7;
   const int b = static_cast<int>(blockIdx.x);
-  if (b < nb) gemm_tile<kBf16, NMAT, EPI, 256, 2>(big, b);
-  else gemm_tile<kBf16, NMAT, EPI, 64, 1>(small, b - nb);
+  if (b < nb) {
+    gemm_tile<kBf16, NMAT, EPI, 256, 2>(big, b);
+    return;
+  }
+  int nm = 0;
+  if constexpr (kHasMidTiles<kBf16, EPI>) {
+    static_assert(gemm_lds_bytes<kBf16, NMAT, EPI, 128, 1, false>() <= kGemmLdsBytes, "LDS");
+    nm = (*mid.n_tiles * mid.n_col_tiles + 7) & ~7;
+    if (b < nb + nm) {
+      gemm_tile<kBf16, NMAT, EPI, 128, 1>(mid, b - nb);
+      return;
+    }
+  }
+  gemm_tile<kBf16, NMAT, EPI, 64, 1>(small, b - nb - nm);
 }
 
 // Lists the row tiles of the GEMMs.  With `merge`, consecutive slots of one
@@ -953,6 +975,19 @@ struct TileSplit {
   int32_t* row0;
   int32_t* rend;
   int32_t* counts;
+  // 128-row tiles for GEMM 0 (mid_rows = 0: none): a range longer than the
+  // short ranges whose last 256-row tile would hold at most mid_rows rows lists
+  // that tile here instead (at most one per range; counts[4] is their number),
+  // and GEMM 0 runs the 256-row table without those tails (alt_*, the same
+  // capacity as the main table); GEMM 1 keeps the main table.  counts[5] stays 0
+  // (the empty 128-row table of GEMM 1).
+  int mid_rows;
+  int32_t* mid_slot;
+  int32_t* mid_row0;
+  int32_t* mid_rend;
+  int32_t* alt_slot;
+  int32_t* alt_row0;
+  int32_t* alt_rend;
 };
 constexpr int kWaveBlocks = 256;  // one block per CU
 
@@ -971,8 +1006,8 @@ __global__ __launch_bounds__(256) void tiles_kernel(const int32_t* __restrict__ 
                                                     int32_t* __restrict__ tile_slot, int32_t* __restrict__ tile_row0,
                                                     int32_t* __restrict__ tile_rend, int32_t* __restrict__ n_tiles,
                                                     TileSplit split, int32_t* __restrict__ check) {
-  __shared__ int32_t scan[256], scan2[256];
-  __shared__ int32_t carry, carry2;
+  __shared__ int32_t scan[256], scan2[256], scan3[256];
+  __shared__ int32_t carry, carry2, carry3;
   // slot tables of up to kLdsSlots slots are read from LDS: the merge walk over
   // an expert's consecutive slots is a chain of dependent reads
   constexpr int kLdsSlots = 1024;
@@ -981,6 +1016,7 @@ __global__ __launch_bounds__(256) void tiles_kernel(const int32_t* __restrict__ 
   const int n = min(max(*n_slots_p, 0), max_slots);
   const bool companion = split.counts != nullptr && mode == kCover && BM == 256;
   const int rem_tiles = companion ? split.rem_tiles : 0;
+  const int mid_rows = companion ? split.mid_rows : 0;
   const bool staged = n <= kLdsSlots;
   if (staged) {
     for (int i = tid; i < n; i += 256) se_lds[i] = slot_expert[i];
@@ -988,7 +1024,7 @@ __global__ __launch_bounds__(256) void tiles_kernel(const int32_t* __restrict__ 
   }
   const int32_t* se = staged ? se_lds : slot_expert;
   const int32_t* so = staged ? so_lds : slot_off;
-  if (tid == 0) carry = carry2 = 0;
+  if (tid == 0) carry = carry2 = carry3 = 0;
   __syncthreads();
   if (check) {
     // the slot table a dispatch writes: slot_off ascending inside [0, M],
@@ -1000,7 +1036,7 @@ __global__ __launch_bounds__(256) void tiles_kernel(const int32_t* __restrict__ 
   }
   for (int c = 0; c < n; c += 256) {
     const int s = c + tid;
-    int64_t start = 0, end = 0, cnt = 0, cnt_small = 0;
+    int64_t start = 0, end = 0, cnt = 0, cnt_small = 0, cnt_mid = 0;
     if (s < n && !(merge && s > 0 && se[s] == se[s - 1])) {
       int last = s + 1;  // one past the range's last slot
       if (merge)
@@ -1013,6 +1049,8 @@ __global__ __launch_bounds__(256) void tiles_kernel(const int32_t* __restrict__ 
         if (rows > 0 && rows <= 64 * rem_tiles) {
           cnt = 0;
           cnt_small = (rows + 63) / 64;
+        } else if (mid_rows > 0 && rows % BM > 0 && rows % BM <= mid_rows) {
+          cnt_mid = 1;  // GEMM 0 runs the range's last tile as one 128-row tile
         }
       } else if (rows > 0) {
         cnt = m_pad / BM;
@@ -1020,13 +1058,16 @@ __global__ __launch_bounds__(256) void tiles_kernel(const int32_t* __restrict__ 
     }
     scan[tid] = static_cast<int32_t>(cnt);
     scan2[tid] = static_cast<int32_t>(cnt_small);
+    scan3[tid] = static_cast<int32_t>(cnt_mid);
     __syncthreads();
     for (int d = 1; d < 256; d <<= 1) {
       const int32_t v = tid >= d ? scan[tid - d] : 0;
       const int32_t v2 = tid >= d ? scan2[tid - d] : 0;
+      const int32_t v3 = tid >= d ? scan3[tid - d] : 0;
       __syncthreads();
       scan[tid] += v;
       scan2[tid] += v2;
+      scan3[tid] += v3;
       __syncthreads();
     }
     const int32_t first = carry + scan[tid] - static_cast<int32_t>(cnt);
@@ -1048,10 +1089,30 @@ __global__ __launch_bounds__(256) void tiles_kernel(const int32_t* __restrict__ 
           split.rend[g * split.cap + j] = static_cast<int32_t>(end);
         }
     }
+    if (mid_rows > 0) {
+      // GEMM 0's table: this range's tiles but the 128-row tail, at the main
+      // table's position less the tails listed before it
+      const int32_t mid_before = carry3 + scan3[tid] - static_cast<int32_t>(cnt_mid);
+      const int64_t cnt_b = cnt - cnt_mid;
+      for (int q = 0; q < cnt_b; ++q) {
+        const int j = first - mid_before + q;
+        if (j < max_tiles) {
+          split.alt_slot[j] = s;
+          split.alt_row0[j] = static_cast<int32_t>(min<int64_t>(start + static_cast<int64_t>(q) * BM, M));
+          split.alt_rend[j] = static_cast<int32_t>(end);
+        }
+      }
+      if (cnt_mid > 0) {  // at most one per range, at most max_slots in all
+        split.mid_slot[mid_before] = s;
+        split.mid_row0[mid_before] = static_cast<int32_t>(start + cnt_b * BM);
+        split.mid_rend[mid_before] = static_cast<int32_t>(end);
+      }
+    }
     __syncthreads();
     if (tid == 255) {
       carry += scan[255];
       carry2 += scan2[255];
+      carry3 += scan3[255];
     }
     __syncthreads();
   }
@@ -1059,31 +1120,44 @@ __global__ __launch_bounds__(256) void tiles_kernel(const int32_t* __restrict__ 
   if (tid == 0) *n_tiles = total;
   if (!companion) return;
   const int n_rem = min(carry2, split.cap);
-  // the last (up to) 256 tiles, staged in LDS by all threads at once: the
-  // table's writes by the other threads are visible after the last barrier
-  __shared__ int32_t last_slot[256], last_row0[256], last_rend[256];
-  const int base = max(total - 256, 0);
-  if (base + tid < total) {
-    last_slot[tid] = tile_slot[base + tid];
-    last_row0[tid] = tile_row0[base + tid];
-    last_rend[tid] = tile_rend[base + tid];
+  const int n_mid = carry3;
+  // the last (up to) 256 tiles of each GEMM's 256-row table, staged in LDS by
+  // all threads at once: the tables' writes by the other threads are visible
+  // after the last barrier
+  __shared__ int32_t last_slot[2][256], last_row0[2][256], last_rend[2][256];
+  const int total_g[2] = {mid_rows > 0 ? max(total - n_mid, 0) : total, total};
+  for (int g = 0; g < 2; ++g) {
+    const int32_t* ts = (g == 0 && mid_rows > 0) ? split.alt_slot : tile_slot;
+    const int32_t* tr = (g == 0 && mid_rows > 0) ? split.alt_row0 : tile_row0;
+    const int32_t* te = (g == 0 && mid_rows > 0) ? split.alt_rend : tile_rend;
+    const int b0 = max(total_g[g] - 256, 0);
+    if (b0 + tid < total_g[g]) {
+      last_slot[g][tid] = ts[b0 + tid];
+      last_row0[g][tid] = tr[b0 + tid];
+      last_rend[g][tid] = te[b0 + tid];
+    }
   }
   __syncthreads();
   if (tid != 0) return;
   const float c = split.small_cost;
   for (int g = 0; g < 2; ++g) {
     const int nt = split.nt[g];
+    const int tot = total_g[g];
+    const int base = max(tot - 256, 0);
     int best_r = 0, best_rows = 0;
     if (nt > 0) {
       // trailing row tiles of at most one round of blocks (and all staged)
-      const int r_max = min(min(total, 256), (kWaveBlocks + nt - 1) / nt);
-      float best = mixed_rounds(static_cast<int64_t>(total) * nt, static_cast<int64_t>(n_rem) * nt, c);
+      const int r_max = min(min(tot, 256), (kWaveBlocks + nt - 1) / nt);
+      // GEMM 0's 128-row tiles and the short-range 64-row tiles run after the
+      // 256-row tiles, both modelled at cost c
+      const int64_t tail = static_cast<int64_t>(n_rem + (g == 0 ? n_mid : 0)) * nt;
+      float best = mixed_rounds(static_cast<int64_t>(tot) * nt, tail, c);
       int rows = 0;
       for (int r = 1; r <= r_max; ++r) {
-        const int t = total - r - base;
-        rows += (min(BM, last_rend[t] - last_row0[t]) + 63) / 64;
+        const int t = tot - r - base;
+        rows += (min(BM, last_rend[g][t] - last_row0[g][t]) + 63) / 64;
         if (n_rem + rows > split.cap) break;
-        const float e = mixed_rounds(static_cast<int64_t>(total - r) * nt, static_cast<int64_t>(n_rem + rows) * nt, c);
+        const float e = mixed_rounds(static_cast<int64_t>(tot - r) * nt, tail + static_cast<int64_t>(rows) * nt, c);
         if (e < best) {
           best = e;
           best_r = r;
@@ -1094,19 +1168,21 @@ __global__ __launch_bounds__(256) void tiles_kernel(const int32_t* __restrict__ 
       int32_t* r0 = split.row0 + g * split.cap;
       int32_t* re = split.rend + g * split.cap;
       int small = n_rem;
-      for (int t = total - best_r; t < total; ++t) {
-        const int end = min(last_row0[t - base] + BM, last_rend[t - base]);
-        for (int row = last_row0[t - base]; row < end; row += 64) {
-          sl[small] = last_slot[t - base];
+      for (int t = tot - best_r; t < tot; ++t) {
+        const int end = min(last_row0[g][t - base] + BM, last_rend[g][t - base]);
+        for (int row = last_row0[g][t - base]; row < end; row += 64) {
+          sl[small] = last_slot[g][t - base];
           r0[small] = row;
-          re[small] = last_rend[t - base];
+          re[small] = last_rend[g][t - base];
           ++small;
         }
       }
     }
-    split.counts[2 * g] = total - best_r;
+    split.counts[2 * g] = tot - best_r;
     split.counts[2 * g + 1] = n_rem + best_rows;
   }
+  split.counts[4] = n_mid;
+  split.counts[5] = 0;
 }
 
 }  // namespace

@@ -404,6 +404,41 @@ def test_expert_ffn_hand_made_slot_table(M, dtype):
         assert np.array_equal(outs[path], outs["grouped"]), path
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_grouped_128_row_tail_tiles(dtype):
+    """In a wide gate/up GEMM (I = 4096: 32 column tiles), ranges whose last
+    256-row tile holds at most 128 rows run it as a 128-row tile (bf16 SwiGLU;
+    the down GEMM keeps 256-row tiles): ranges of 64 (short), 65, 100, 128, 129,
+    256, 257 (a 1-row tail), 300, 384, 385 and 641 rows, with replicas of one
+    expert as adjacent slots.  Every row matches the oracle and all paths give
+    the same bits (fp32 has no 128-row tiles: the same table runs on 256-row
+    tiles)."""
+    sizes = [64, 65, 100, 128, 129, 256, 257, 300, 384, 385, 641]
+    experts = list(range(len(sizes)))
+    experts[-1] = experts[-2] = 9          # 385 + 641 rows of one expert (two replica slots)
+    E = 10
+    cuts = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    M = int(cuts[-1])
+    cfg = synth.CONFIGS["mixtral"].scaled(T=M, E=E, H=128, I=4096, dtype=dtype)
+    x = synth.hidden0(cfg, 5)
+    wts = synth.expert_weights(cfg)
+    max_slots = len(sizes) + 2
+    slot_off = np.full(max_slots + 1, M, np.int32)
+    slot_off[:len(cuts)] = cuts
+    slot_expert = np.zeros(max_slots, np.int32)
+    slot_expert[:len(experts)] = experts
+    ref = oracle.ffn_rows(x, np.repeat(np.array(experts, np.int32), sizes), *wts, act="swiglu")
+    wg, wu, wd = (to_dev(w) for w in wts)
+    args = (to_dev(x), to_dev(slot_off), to_dev(slot_expert), to_dev(np.array([len(sizes)], np.int32)))
+    outs = {}
+    for path in ("grouped", "grouped_small", "dense", "auto"):
+        outs[path] = from_dev(moe.moe_expert_ffn(*args, wg, wu, wd, act="swiglu", path=path))
+    _sync()
+    assert_close(outs["grouped"], ref, "bf16" if dtype == "bf16" else "fp32_gemm", "y_perm")
+    for path in ("grouped_small", "dense", "auto"):
+        assert np.array_equal(outs[path], outs["grouped"]), path
+
+
 @pytest.mark.parametrize("dtype,n,max_rows", [("bf16", 300, 520), ("f32", 300, 520), ("bf16", 1100, 100)])
 def test_grouped_remainder_tiles_and_last_round(dtype, n, max_rows):
     """The 256-row grouped tiling on 300 slots (more than one 256-slot chunk of
