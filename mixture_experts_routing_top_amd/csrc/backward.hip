@@ -12,19 +12,24 @@
 //      y_perm[r]>, d_y[r] = w[t,i] d_out[t] for r = inv_pos[t,i], and the
 //      softmax Jacobian over the kept logits, d_l[t,e_j] = w_j (dw_j - sum_i
 //      w_i dw_i) (zero for the other experts);
-//   2. d_h = d_y Wd by the grouped GEMM on transposed down weights, kept in
-//      fp32 [M, I];
+//   2. d_h = d_y Wd by the grouped GEMM, kept in fp32 [M, I];
 //   3. the gate/up (or W1) pre-activations recomputed by the grouped GEMM
 //      (activation recomputation rather than a saved [M, 2I]); its epilogue
 //      meets their fp32 accumulators with d_h: the activation gradient
 //      d_g | d_u (or d_z) and h, rebuilt with the forward's own activation so
 //      it rounds as the forward rounded it, both in the dtype;
-//   4. weight gradient of Wd: d_y and h transposed into per-expert K ranges
-//      padded to the K step, then one expert-grouped GEMM;
-//   5. d_x_perm = d_g Wg + d_u Wu as one GEMM with K = 2I over [Wg; Wu]^T;
+//   4. weight gradient of Wd: one expert-grouped GEMM whose K range is each
+//      expert's rows of d_y and h;
+//   5. d_x_perm = d_g Wg + d_u Wu as one GEMM with K = 2I over [Wg; Wu];
 //   6. d_x = the unweighted sum of each token's k rows (the combine kernel);
-//   7. weight gradients of Wg, Wu (or W1) from d_g | d_u and x_perm, transposed
-//      the same way.
+//   7. weight gradients of Wg, Wu (or W1) from d_g | d_u and x_perm, the same
+//      way.
+// Steps 2, 4, 5 and 7 contract over a dimension that is not contiguous in
+// memory (the weights' rows, the activations' rows).  bf16 tiles read those
+// operands in place, K-major, through the transposed LDS read (gemm.h); fp32
+// tiles take K-contiguous operands only, so for fp32 the weights are
+// transposed first and the activations transposed into per-expert K ranges
+// padded to the K step.
 #include <algorithm>
 
 #include "common.h"
@@ -237,6 +242,7 @@ struct BwdLayout {
 BwdLayout bwd_layout(moe_dtype dt, int64_t T, int k, int H, int I, int E, moe_act act) {
   BwdLayout w{};
   const size_t s = moe::elem_bytes(dt);
+  const bool tr = dt != MOE_BF16;  // transposed copies (fp32 only)
   const int64_t M = T * k;
   const int64_t nI = act == MOE_SWIGLU ? 2 * static_cast<int64_t>(I) : I;  // gate|up columns
   w.ld = moe::ceil_div(M, 64) * 64 + 64 * static_cast<int64_t>(E);
@@ -247,10 +253,10 @@ BwdLayout bwd_layout(moe_dtype dt, int64_t T, int k, int H, int I, int E, moe_ac
   w.h = take(static_cast<size_t>(M) * I * s);
   w.dgu = take(static_cast<size_t>(M) * nI * s);
   w.dy = take(static_cast<size_t>(M) * H * s);
-  w.wdT = take(static_cast<size_t>(E) * I * H * s);
-  w.wguT = take(static_cast<size_t>(E) * H * nI * s);
-  w.ta = take(static_cast<size_t>(std::max<int64_t>(H, nI)) * w.ld * s);
-  w.tb = take(static_cast<size_t>(std::max<int64_t>(I, H)) * w.ld * s);
+  w.wdT = take(tr ? static_cast<size_t>(E) * I * H * s : 0);
+  w.wguT = take(tr ? static_cast<size_t>(E) * H * nI * s : 0);
+  w.ta = take(tr ? static_cast<size_t>(std::max<int64_t>(H, nI)) * w.ld * s : 0);
+  w.tb = take(tr ? static_cast<size_t>(std::max<int64_t>(I, H)) * w.ld * s : 0);
   w.ones = take(static_cast<size_t>(M) * 4);
   w.seg = take(sizeof(int32_t) * (E + 1));
   w.slot_expert = take(sizeof(int32_t) * E);
@@ -307,12 +313,14 @@ int run_backward(const void* x_perm, const void* y_perm, int64_t n_tok, int k, i
         chunks, reinterpret_cast<uint4*>(dy), d_logits);
   if (int rc = check("moe_backward gate")) return rc;
 
-  // transposed weights: WdT [E, I, H]; WguT [E, H, 2I] = [Wg^T | Wu^T] (or W1^T [E, H, I])
-  const dim3 tb_d(ceil_div(I, 64), ceil_div(H, 64), E), tb_g(ceil_div(H, 64), ceil_div(I, 64), E);
-  transpose_kernel<T><<<tb_d, 256, 0, s>>>(static_cast<const T*>(w_down), H, I, wdT, H, 0);
-  transpose_kernel<T><<<tb_g, 256, 0, s>>>(static_cast<const T*>(w_gate), I, H, wguT, nI, 0);
-  if (swiglu) transpose_kernel<T><<<tb_g, 256, 0, s>>>(static_cast<const T*>(w_up), I, H, wguT, nI, I);
-  if (int rc = check("moe_backward weight transposes")) return rc;
+  // fp32: transposed weights WdT [E, I, H]; WguT [E, H, 2I] = [Wg^T | Wu^T] (or W1^T [E, H, I])
+  if constexpr (!kBf16) {
+    const dim3 tb_d(ceil_div(I, 64), ceil_div(H, 64), E), tb_g(ceil_div(H, 64), ceil_div(I, 64), E);
+    transpose_kernel<T><<<tb_d, 256, 0, s>>>(static_cast<const T*>(w_down), H, I, wdT, H, 0);
+    transpose_kernel<T><<<tb_g, 256, 0, s>>>(static_cast<const T*>(w_gate), I, H, wguT, nI, 0);
+    if (swiglu) transpose_kernel<T><<<tb_g, 256, 0, s>>>(static_cast<const T*>(w_up), I, H, wguT, nI, I);
+    if (int rc = check("moe_backward weight transposes")) return rc;
+  }
 
   GemmArgs base{};
   base.M = M;
@@ -325,15 +333,19 @@ int run_backward(const void* x_perm, const void* y_perm, int64_t n_tok, int k, i
   base.n_tiles = n_tiles;
   const unsigned grid_rows = static_cast<unsigned>(L.tiles_cap);
 
-  // 2. d_h = d_y Wd in fp32
+  // 2. d_h = d_y Wd in fp32 (bf16: Wd [E, H, I] read K-major)
   GemmArgs p = base;
   p.A = dy;
-  p.B0 = wdT;
+  p.B0 = kBf16 ? w_down : wdT;
+  p.ldb = I;
   p.C = dh;
   p.K = H;
   p.N = I;
   p.n_col_tiles = static_cast<int>(ceil_div(I, kTileN));
-  gemm_kernel<kBf16, 1, kEpiStoreF32, 256, 2><<<grid_rows * p.n_col_tiles, 256, 0, s>>>(p);
+  if constexpr (kBf16)
+    gemm_kernel<kBf16, 1, kEpiStoreF32, 256, 2, false, 2><<<grid_rows * p.n_col_tiles, 256, 0, s>>>(p);
+  else
+    gemm_kernel<kBf16, 1, kEpiStoreF32, 256, 2><<<grid_rows * p.n_col_tiles, 256, 0, s>>>(p);
   if (int rc = check("moe_backward d_h")) return rc;
 
   // 3. recompute the pre-activations; the epilogue turns d_h into d_g | d_u
@@ -356,56 +368,84 @@ int run_backward(const void* x_perm, const void* y_perm, int64_t n_tok, int k, i
   }
   if (int rc = check("moe_backward recompute")) return rc;
 
-  // 4. d_Wd = sum over each expert's rows of d_y^T h
+  // 4. d_Wd = sum over each expert's rows of d_y^T h (bf16: d_y [M, H] and h
+  //    [M, I] read K-major in place; fp32: both transposed into padded K ranges)
   const int ld = static_cast<int>(L.ld);
   const unsigned ldb = static_cast<unsigned>(ceil_div(L.ld, 64));
-  transpose_padded_kernel<kBf16><<<dim3(ceil_div(H, 64), ldb), 256, 0, s>>>(dy, M, H, expert_off, seg, E, ta,
-                                                                                  ld);
-  transpose_padded_kernel<kBf16><<<dim3(ceil_div(I, 64), ldb), 256, 0, s>>>(hbuf, M, I, expert_off, seg, E,
-                                                                                  tb, ld);
   GemmArgs q{};
-  q.A = ta;
-  q.B0 = tb;
   q.C = d_w_down;
   q.C2 = d_w_down;
+  q.M = M;
   q.E = E;
   q.N = I;
   q.Mw = H;
   q.c_split = H;
-  q.ld = ld;
-  q.seg = seg;
   q.n_col_tiles = static_cast<int>(ceil_div(I, kTileN));
-  gemm_kernel<kBf16, 1, kEpiStore, 256, 2, true><<<wgrad_grid(E, H, q.n_col_tiles), 256, 0, s>>>(q);
+  if constexpr (kBf16) {
+    q.A = dy;
+    q.lda = H;
+    q.B0 = hbuf;
+    q.ldb = I;
+    q.slot_off = expert_off;
+    gemm_kernel<kBf16, 1, kEpiStore, 256, 2, true, 3><<<wgrad_grid(E, H, q.n_col_tiles), 256, 0, s>>>(q);
+  } else {
+    transpose_padded_kernel<kBf16><<<dim3(ceil_div(H, 64), ldb), 256, 0, s>>>(dy, M, H, expert_off, seg, E, ta,
+                                                                                    ld);
+    transpose_padded_kernel<kBf16><<<dim3(ceil_div(I, 64), ldb), 256, 0, s>>>(hbuf, M, I, expert_off, seg, E,
+                                                                                    tb, ld);
+    q.A = ta;
+    q.B0 = tb;
+    q.ld = ld;
+    q.seg = seg;
+    gemm_kernel<kBf16, 1, kEpiStore, 256, 2, true><<<wgrad_grid(E, H, q.n_col_tiles), 256, 0, s>>>(q);
+  }
   if (int rc = check("moe_backward d_Wd")) return rc;
 
-  // 5. d_x_perm = [d_g | d_u] [Wg ; Wu] (into the d_y buffer, no longer needed)
+  // 5. d_x_perm = [d_g | d_u] [Wg ; Wu] (into the d_y buffer, no longer needed;
+  //    bf16: Wg and Wu [E, I, H] read K-major, K rows from Wg then Wu)
   p = base;
   p.A = dgu;
-  p.B0 = wguT;
   p.C = dy;
   p.K = nI;
   p.N = H;
   p.n_col_tiles = static_cast<int>(ceil_div(H, kTileN));
-  gemm_kernel<kBf16, 1, kEpiStore, 256, 2><<<grid_rows * p.n_col_tiles, 256, 0, s>>>(p);
+  if constexpr (kBf16) {
+    p.B0 = w_gate;
+    p.B1 = swiglu ? w_up : nullptr;
+    p.k_split = swiglu ? I : 0;
+    p.ldb = H;
+    gemm_kernel<kBf16, 1, kEpiStore, 256, 2, false, 2><<<grid_rows * p.n_col_tiles, 256, 0, s>>>(p);
+  } else {
+    p.B0 = wguT;
+    gemm_kernel<kBf16, 1, kEpiStore, 256, 2><<<grid_rows * p.n_col_tiles, 256, 0, s>>>(p);
+  }
   if (int rc = check("moe_backward d_x_perm")) return rc;
 
   // 6. d_x[t] = sum of the token's k rows
   if (int rc = moe_combine(dy, kBf16 ? MOE_BF16 : MOE_F32, M, inv_pos, ones, n_tok, k, H, d_x, nullptr, s)) return rc;
 
   // 7. d_Wg | d_Wu (or d_W1) = sum over each expert's rows of [d_g | d_u]^T x_perm
-  transpose_padded_kernel<kBf16><<<dim3(ceil_div(nI, 64), ldb), 256, 0, s>>>(dgu, M, nI, expert_off, seg, E,
-                                                                                   ta, ld);
-  transpose_padded_kernel<kBf16><<<dim3(ceil_div(H, 64), ldb), 256, 0, s>>>(x_perm, M, H, expert_off, seg, E,
-                                                                                  tb, ld);
-  q.A = ta;
-  q.B0 = tb;
   q.C = d_w_gate;
   q.C2 = swiglu ? d_w_up : d_w_gate;
   q.N = H;
   q.Mw = nI;
   q.c_split = I;
   q.n_col_tiles = static_cast<int>(ceil_div(H, kTileN));
-  gemm_kernel<kBf16, 1, kEpiStore, 256, 2, true><<<wgrad_grid(E, nI, q.n_col_tiles), 256, 0, s>>>(q);
+  if constexpr (kBf16) {
+    q.A = dgu;
+    q.lda = nI;
+    q.B0 = x_perm;
+    q.ldb = H;
+    gemm_kernel<kBf16, 1, kEpiStore, 256, 2, true, 3><<<wgrad_grid(E, nI, q.n_col_tiles), 256, 0, s>>>(q);
+  } else {
+    transpose_padded_kernel<kBf16><<<dim3(ceil_div(nI, 64), ldb), 256, 0, s>>>(dgu, M, nI, expert_off, seg, E,
+                                                                                     ta, ld);
+    transpose_padded_kernel<kBf16><<<dim3(ceil_div(H, 64), ldb), 256, 0, s>>>(x_perm, M, H, expert_off, seg, E,
+                                                                                    tb, ld);
+    q.A = ta;
+    q.B0 = tb;
+    gemm_kernel<kBf16, 1, kEpiStore, 256, 2, true><<<wgrad_grid(E, nI, q.n_col_tiles), 256, 0, s>>>(q);
+  }
   return check("moe_backward d_Wg/d_Wu");
 }
 

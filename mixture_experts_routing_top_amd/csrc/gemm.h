@@ -100,6 +100,13 @@ struct GemmArgs {
   int Mw;              // weight-gradient mode: rows of A (output rows per expert)
   int c_split;         // weight-gradient mode: output rows >= c_split go to C2
   void* C2;
+  // K-major operands (bf16 256-row tiles, template argument KM): A stored as
+  // [K rows, lda] (weight-gradient mode: the activations [M, lda], expert e's
+  // rows slot_off[e] .. slot_off[e+1] being its K range), the weights as
+  // [E, Kb, ldb] (weight-gradient mode: activations [M, ldb] like A).  With
+  // k_split > 0 the weights' K range is split: k < k_split reads B0 [E,
+  // k_split, ldb], k >= k_split reads B1 (its row k - k_split).
+  int lda, ldb, k_split;
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
@@ -152,6 +159,14 @@ __device__ __forceinline__ void wait_vm() {
 // chunk hit 16 distinct 16-byte bank groups.  swz depends on row % 32 only.
 __device__ __forceinline__ int swz(int row) { return (row ^ ((row >> 3) & 3)) & 7; }
 
+// K-major stage rows hold 512 bytes (256 elements of one K index) as 32
+// chunks of 16 bytes; logical chunk c is stored at c ^ kswz(row), which moves
+// whole 32-byte pairs of chunks: by 0, 5, 2, 7 pairs for row % 4 = 0..3.  A
+// transposed fragment read takes 32 bytes from each of four rows r..r+3 (r a
+// multiple of 4) per 16 lanes, and 64 bytes from each per 32 lanes; these
+// shifts put the four (or eight) pieces in distinct 32-byte bank groups.
+__device__ __forceinline__ int kswz(int row) { return (((row & 2) | ((row & 1) * 5)) << 1); }
+
 // Four adjacent outputs: fp32 as one 16-byte store, bf16 rounded to nearest
 // even (v_cvt_pk_bf16_f32) as one 8-byte store.
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -201,7 +216,7 @@ __shared__ __align__(1024) char gemm_lds[kGemmLdsBytes];
 
 // One block's tile: `b` is its index in the grid of this tiling (b & 7 its
 // XCD); it uses the first gemm_lds_bytes of gemm_lds.
-template <bool kBf16, int NMAT, int EPI, int BM, int WM, bool kWgrad = false>
+template <bool kBf16, int NMAT, int EPI, int BM, int WM, bool kWgrad = false, int KM = 0>
 __device__ __forceinline__ void gemm_tile(const GemmArgs g, const int b) {
   char* const lds = gemm_lds;
   using TR = Tr<kBf16>;
@@ -220,6 +235,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs g, const int b) {
   constexpr int NM = TM * TN;              // MFMAs per sub-step
   constexpr int kStageBytes = (BM + kTileN) * kRowBytes;
   static_assert(NM >= NR, "sub-step pattern assumes at least one MFMA per fragment read");
+  // K-major operands: bit 0 A (weight-gradient mode only), bit 1 the weights
+  constexpr bool kAK = (KM & 1) != 0, kBK = (KM & 2) != 0;
+  static_assert(KM == 0 || (kBf16 && BM == 256 && WM == 2 && NMAT == 1 && (!kAK || kWgrad)),
+                "K-major operands: bf16 256-row tiles of one weight matrix; K-major A in weight-gradient mode");
   // bf16 tiles load their operands straight into LDS (unpadded rows): 256- and
   // 128-row tiles (weight gradients included) in two A stages and three weight
   // stages, 64-row tiles in four stages of both; fp32 tiles stage them through
@@ -270,13 +289,23 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs g, const int b) {
   if constexpr (kWgrad) {
     e = __builtin_amdgcn_readfirstlane(mt / MTw);
     r0 = __builtin_amdgcn_readfirstlane((mt - e * MTw) * BM);
-    // uniform across the block: keep the buffer descriptors in scalar registers
-    const int k0 = __builtin_amdgcn_readfirstlane(g.seg[e]);
-    K = __builtin_amdgcn_readfirstlane(g.seg[e + 1]) - k0;
     m_valid = __builtin_amdgcn_readfirstlane(static_cast<int>(min<int64_t>(BM, g.Mw - r0)));
-    row_b = static_cast<int64_t>(g.ld) * S;
-    A = static_cast<const T*>(g.A) + r0 * g.ld + k0;
-    wofs = static_cast<int64_t>(n0) * g.ld + k0;
+    if constexpr (KM != 0) {
+      // expert e's rows of the activations, read in place: row k0 + k is K index k
+      const int64_t lo = min<int64_t>(max(__builtin_amdgcn_readfirstlane(g.slot_off[e]), 0), g.M);
+      const int64_t hi = min<int64_t>(max<int64_t>(__builtin_amdgcn_readfirstlane(g.slot_off[e + 1]), lo), g.M);
+      K = static_cast<int>(hi - lo);
+      row_b = 0;
+      A = static_cast<const T*>(g.A) + lo * g.lda + r0;
+      wofs = lo * g.ldb + n0;
+    } else {
+      // uniform across the block: keep the buffer descriptors in scalar registers
+      const int k0 = __builtin_amdgcn_readfirstlane(g.seg[e]);
+      K = __builtin_amdgcn_readfirstlane(g.seg[e + 1]) - k0;
+      row_b = static_cast<int64_t>(g.ld) * S;
+      A = static_cast<const T*>(g.A) + r0 * g.ld + k0;
+      wofs = static_cast<int64_t>(n0) * g.ld + k0;
+    }
   } else {
     const int s = g.tile_slot[mt];
     r0 = g.tile_row0[mt];
@@ -287,7 +316,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs g, const int b) {
     m_valid = static_cast<int>(min<int64_t>(BM, rend - r0));
     row_b = static_cast<int64_t>(K) * S;  // bytes per operand row
     A = static_cast<const T*>(g.A) + r0 * K;
-    wofs = (static_cast<int64_t>(e) * N + n0) * K;
+    if constexpr ((KM & 2) != 0)  // expert e's weights [Kb, ldb] from column n0
+      wofs = static_cast<int64_t>(e) * (g.k_split > 0 ? g.k_split : K) * g.ldb + n0;
+    else
+      wofs = (static_cast<int64_t>(e) * N + n0) * K;
   }
 
   const __amdgpu_buffer_rsrc_t ra = rsrc(A, m_valid * row_b);
@@ -380,27 +412,71 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs g, const int b) {
     const u32x4 db0 = dma_rsrc(static_cast<const T*>(g.B0) + wofs, static_cast<int64_t>(n_valid) * row_b);
     const u32x4 db1 = NMAT > 1 ? dma_rsrc(static_cast<const T*>(g.B1) + wofs, static_cast<int64_t>(n_valid) * row_b) : db0;
     const int wv = __builtin_amdgcn_readfirstlane(wave);
+    // K-major stages hold 64 K rows of 256 elements (512 bytes) each; block
+    // 4p + w of a stage is K rows 2(4p + w) and 2(4p + w) + 1, lane i writing
+    // 16-byte chunk i % 32 of row i / 32, which holds logical chunk (i % 32) ^
+    // kswz(row).  The source row pitch is lda or ldb elements.
+    const int ldaB = kAK ? g.lda * S : 0, ldbB = kBK ? g.ldb * S : 0;
     int offA[PA_], offB[PB_];
 #pragma unroll
     for (int p = 0; p < PA_; ++p) {
-      const int row = 8 * (4 * p + wv) + (lane >> 3);
-      offA[p] = row * rb_ + (((lane & 7) ^ swz(row)) << 4);
+      if constexpr (kAK) {
+        const int kr = 2 * (4 * p + wv) + (lane >> 5);
+        offA[p] = kr * ldaB + (((lane & 31) ^ kswz(kr)) << 4);
+      } else {
+        const int row = 8 * (4 * p + wv) + (lane >> 3);
+        offA[p] = row * rb_ + (((lane & 7) ^ swz(row)) << 4);
+      }
     }
 #pragma unroll
     for (int p = 0; p < PB_; ++p) {
-      const int row = 8 * (4 * p + wv) + (lane >> 3);
-      const int src = (NMAT == 2 && row >= 128) ? row - 128 : row;
-      offB[p] = src * rb_ + (((lane & 7) ^ swz(row)) << 4);
+      if constexpr (kBK) {
+        const int kr = 2 * (4 * p + wv) + (lane >> 5);
+        offB[p] = kr * ldbB + (((lane & 31) ^ kswz(kr)) << 4);
+      } else {
+        const int row = 8 * (4 * p + wv) + (lane >> 3);
+        const int src = (NMAT == 2 && row >= 128) ? row - 128 : row;
+        offB[p] = src * rb_ + (((lane & 7) ^ swz(row)) << 4);
+      }
     }
+    const int nk = KM != 0 ? (K + 63) / 64 : K / 64;
+    auto koff = [&](int kt) { return kt < nk ? kt * 128 : 0x7ffff000; };
+    // descriptors of step kt for the K-major operands, based at its first K
+    // row and ending where the operand's K range ends (an empty range past the
+    // last step: its loads read zeros)
+    auto kdescA = [&](int kt) -> u32x4 {
+      if (!kAK || kt >= nk) return dma_rsrc(A, 0);
+      const int64_t o = static_cast<int64_t>(kt) * 64 * g.lda;
+      return dma_rsrc(A + o, max<int64_t>(0, (static_cast<int64_t>(K) * g.lda - r0 - o) * S));
+    };
+    auto kdescB = [&](int kt) -> u32x4 {
+      if (!kBK || kt >= nk) return dma_rsrc(g.B0, 0);
+      int64_t kr = static_cast<int64_t>(kt) * 64, kend = K;
+      const T* base = static_cast<const T*>(g.B0) + wofs;
+      if (!kWgrad && g.k_split > 0) {
+        if (kr >= g.k_split) {
+          base = static_cast<const T*>(g.B1) + wofs;
+          kr -= g.k_split;
+          kend = K - g.k_split;
+        } else {
+          kend = g.k_split;
+        }
+      }
+      return dma_rsrc(base + kr * g.ldb, max<int64_t>(0, ((kend - kr) * g.ldb - n0) * S));
+    };
     const unsigned lds0 = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(reinterpret_cast<uintptr_t>(lds)));
-    auto dmaA = [&](int p, int st, int koff) { load_lds(da, offA[p] + koff, lds0 + st * SA + (4 * p + wv) * 1024); };
-    auto dmaB = [&](int p, int st, int koff) {
+    // koff: the K offset of a row-major operand's step; dk: a K-major operand's step descriptor
+    auto dmaA = [&](int p, int st, int koff, const u32x4& dk) {
+      const unsigned dst = lds0 + st * SA + (4 * p + wv) * 1024;
+      if constexpr (kAK) load_lds(dk, offA[p], dst);
+      else load_lds(da, offA[p] + koff, dst);
+    };
+    auto dmaB = [&](int p, int st, int koff, const u32x4& dk) {
       const unsigned dst = lds0 + 2 * SA + st * SBW + (4 * p + wv) * 1024;
-      if (NMAT == 1 || p < PB_ / 2) load_lds(db0, offB[p] + koff, dst);
+      if constexpr (kBK) load_lds(dk, offB[p], dst);
+      else if (NMAT == 1 || p < PB_ / 2) load_lds(db0, offB[p] + koff, dst);
       else load_lds(db1, offB[p] + koff, dst);
     };
-    const int nk = K / 64;
-    auto koff = [&](int kt) { return kt < nk ? kt * 128 : 0x7ffff000; };
     constexpr int BS0[4] = {0, 3, 6, 8};  // weight blocks issued in sub-steps 0, 1, 2
     const int sw = swz(lr);
     const int a_rd2 = (wm * (BM / WM) + lr) * 128;
@@ -410,13 +486,43 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs g, const int b) {
     int kofs[KS];
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) kofs[kk] = ((2 * kk + lg) ^ sw) << 4;
+    // K-major fragments: lane l = 16 q + s (q = l / 16) reads with the
+    // transposed 8-byte LDS read ds_read_b64_tr_b16, which hands lane s of a
+    // 16-lane group element s % 4 of what lanes 4j + s / 4 (j = 0..3) loaded.
+    // So lane s loads K row 8 (q / 2) + s / 4 (+4 for the second read) at
+    // columns c0 + 16 (q % 2) + 4 (s % 4) .. + 3, and ends up holding column
+    // c0 + l % 32 at K 8 (l / 32) + 0..7: the MFMA operand layout.  kswz
+    // depends on the K row mod 4 = s / 4 only, so the per-lane address of a
+    // 32-column block is fixed; sub-step kk and the half add immediates.
+    int akm_rd[TM], bkm_rd[TN];
+    {
+      const int q = lane >> 4, s4 = lane & 15;
+      const int kb = (8 * (q >> 1) + (s4 >> 2)) * 512 + 8 * (s4 & 3);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        akm_rd[i] = kb + 32 * ((((wm * (BM / WM) + 32 * i) >> 4) + (q & 1)) ^ (kswz(s4 >> 2) >> 1));
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        bkm_rd[j] = 2 * SA + kb + 32 * ((((wn * CW + 32 * j) >> 4) + (q & 1)) ^ (kswz(s4 >> 2) >> 1));
+    }
+    auto kfrag = [&](const char* p) {
+      typedef short s16x4 __attribute__((ext_vector_type(4)));
+      typedef __attribute__((address_space(3))) s16x4* lds_s16x4;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(p));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(p + 4 * 512));
+      const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+      return make_uint4(l2.x, l2.y, h2.x, h2.y);
+    };
     // fragment read r of a sub-step in the order the MFMAs consume them:
     // A tile 0, weight tiles 0 .. TN-1, A tiles 1 .. TM-1
     auto frag = [&](int sa, int sbw, int kk, int buf, int r) {
-      if (r >= 1 && r <= TN) fb[buf][r - 1] = *reinterpret_cast<const Frag*>(lds + sbw * SBW + b_rd2[r - 1] + kofs[kk]);
-      else {
+      if (r >= 1 && r <= TN) {
+        if constexpr (kBK) fb[buf][r - 1] = kfrag(lds + sbw * SBW + bkm_rd[r - 1] + kk * 16 * 512);
+        else fb[buf][r - 1] = *reinterpret_cast<const Frag*>(lds + sbw * SBW + b_rd2[r - 1] + kofs[kk]);
+      } else {
         const int i = r == 0 ? 0 : r - TN;
-        fa[buf][i] = *reinterpret_cast<const Frag*>(lds + sa * SA + a_rd2 + i * 32 * 128 + kofs[kk]);
+        if constexpr (kAK) fa[buf][i] = kfrag(lds + sa * SA + akm_rd[i] + kk * 16 * 512);
+        else fa[buf][i] = *reinterpret_cast<const Frag*>(lds + sa * SA + a_rd2 + i * 32 * 128 + kofs[kk]);
       }
     };
     auto mfma1 = [&](int buf, int m) {
@@ -431,18 +537,21 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs g, const int b) {
     //   W(kt+2), may still be in flight);
     //   sub-step 3: A(kt+2) 0..7 into the A stage step kt freed.
     // prologue: A(0), W(0), W(1) whole, then A(1) (the sub-step-3 share of step -1)
+    {
+      const u32x4 a0 = kdescA(0), b0 = kdescB(0), b1 = kdescB(1), a1 = kdescA(1);
 #pragma unroll
-    for (int p = 0; p < PA_; ++p) dmaA(p, 0, koff(0));
+      for (int p = 0; p < PA_; ++p) dmaA(p, 0, koff(0), a0);
 #pragma unroll
-    for (int p = 0; p < PB_; ++p) dmaB(p, 0, koff(0));
+      for (int p = 0; p < PB_; ++p) dmaB(p, 0, koff(0), b0);
 #pragma unroll
-    for (int p = 0; p < PB_; ++p) dmaB(p, 1, koff(1));
-    wait_vm<PB_>();
-    __syncthreads();
+      for (int p = 0; p < PB_; ++p) dmaB(p, 1, koff(1), b1);
+      wait_vm<PB_>();
+      __syncthreads();
 #pragma unroll
-    for (int r = 0; r < NR; ++r) frag(0, 0, 0, 0, r);
+      for (int r = 0; r < NR; ++r) frag(0, 0, 0, 0, r);
 #pragma unroll
-    for (int p = 0; p < PA_; ++p) dmaA(p, 1, koff(1));
+      for (int p = 0; p < PA_; ++p) dmaA(p, 1, koff(1), a1);
+    }
 
     // one K step; the stage indices are compile-time (the loop runs six steps
     // per iteration: the A stages repeat every 2 steps, the weight stages every 3)
@@ -450,6 +559,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs g, const int b) {
       constexpr int u = decltype(U)::value, wcur = decltype(WC)::value;
       constexpr int w1 = (wcur + 1) % 3, w2 = (wcur + 2) % 3;
       const int k2 = koff(kt + 2);
+      const u32x4 dA2 = kdescA(kt + 2), dB2 = kdescB(kt + 2);
 #pragma unroll
       for (int kk = 0; kk < KS - 1; ++kk) {
         int rd = 0, qb = BS0[kk];
@@ -458,11 +568,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs g, const int b) {
         for (int m = 0; m < NM; ++m) {
           mfma1(kk & 1, m);
           if (rd < NR) frag(u, wcur, kk + 1, (kk + 1) & 1, rd++);
-          if ((m & 1) && qb < qbe) dmaB(qb++, w2, k2);
+          if ((m & 1) && qb < qbe) dmaB(qb++, w2, k2, dB2);
           __builtin_amdgcn_sched_barrier(0);
         }
         while (rd < NR) frag(u, wcur, kk + 1, (kk + 1) & 1, rd++);
-        while (qb < qbe) dmaB(qb++, w2, k2);
+        while (qb < qbe) dmaB(qb++, w2, k2, dB2);
         __builtin_amdgcn_sched_barrier(0);
       }
       wait_vm<PB_>();
@@ -473,11 +583,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs g, const int b) {
       for (int m = 0; m < NM; ++m) {
         mfma1((KS - 1) & 1, m);
         if (rd < NR) frag(u ^ 1, w1, 0, KS & 1, rd++);
-        if ((m & 1) && qa < PA_) dmaA(qa++, u, k2);
+        if ((m & 1) && qa < PA_) dmaA(qa++, u, k2, dA2);
         __builtin_amdgcn_sched_barrier(0);
       }
       while (rd < NR) frag(u ^ 1, w1, 0, KS & 1, rd++);
-      while (qa < PA_) dmaA(qa++, u, k2);
+      while (qa < PA_) dmaA(qa++, u, k2, dA2);
       __builtin_amdgcn_sched_barrier(0);
     };
     using I0 = std::integral_constant<int, 0>;
@@ -899,10 +1009,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs g, const int b) {
 }
 
 
-template <bool kBf16, int NMAT, int EPI, int BM, int WM, bool kWgrad = false>
+template <bool kBf16, int NMAT, int EPI, int BM, int WM, bool kWgrad = false, int KM = 0>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_kernel(GemmArgs g) {
   static_assert(gemm_lds_bytes<kBf16, NMAT, EPI, BM, WM, kWgrad>() <= kGemmLdsBytes, "LDS");
-  gemm_tile<kBf16, NMAT, EPI, BM, WM, kWgrad>(g, static_cast<int>(blockIdx.x));
+  gemm_tile<kBf16, NMAT, EPI, BM, WM, kWgrad, KM>(g, static_cast<int>(blockIdx.x));
 }
 
 // 128-row tiles exist for bf16 operands with a register epilogue (the staged

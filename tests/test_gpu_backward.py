@@ -21,6 +21,10 @@ CASES = {
     "dbrx-mini": synth.CONFIGS["dbrx"].scaled(T=257, H=384, I=640),
     "popf-mini": synth.CONFIGS["popfetcher"].scaled(T=500, H=128, I=256, L=1),
     "mixtral-mid": synth.CONFIGS["mixtral"].scaled(T=1024, H=512, I=1024),
+    # bf16 GELU (one weight matrix in d_x_perm's K range), H and I below one tile
+    "gelu-bf16-mini": synth.CONFIGS["popfetcher"].scaled(T=300, H=192, I=320, L=1, dtype="bf16"),
+    # experts of ~512 rows: the weight-gradient K loops run past one unrolled cycle
+    "mixtral-rows": synth.CONFIGS["mixtral"].scaled(T=2048, H=256, I=320),
 }
 
 
