@@ -23,8 +23,12 @@
 // The weight fragment is the MFMA's first operand, so the accumulators come out
 // transposed: each lane holds four adjacent output columns of one row, which
 // the epilogue writes with one 8-byte (bf16) or 16-byte (fp32) store.  One
-// launch can run two tile heights (gemm_mixed_kernel): 256-row tiles, then
-// 64-row tiles in the grid's last blocks, over one shared LDS array.
+// launch can run three tile heights (gemm_mixed_kernel): 256-row tiles, then
+// 128- and 64-row tiles in the grid's last blocks, over one shared LDS array.
+// bf16 256-row tiles can also read an operand K-major ([K, N] with N
+// contiguous: the backward's weights and its weight gradients' activations):
+// its stages then hold 64 rows of one K index each, and the MFMA fragments
+// come from gfx950's transposed LDS read (ds_read_b64_tr_b16).
 // Each output row depends only on its own input row and the fixed K order, so
 // a row's value does not depend on the tile, slot or path that computes it.
 #pragma once
