@@ -232,9 +232,17 @@ int moe_prediction_quality(const float* pred, const int32_t* counts, int E, cons
  *               slot_expert [max_slots], slot_off [max_slots+1] (slot s owns
  *               rows [slot_off[s], slot_off[s+1])), n_slots [1].  Unused slots
  *               up to max_slots are empty (slot_off = M).  replicas == NULL
- *               means one slot per expert.  Copies beyond max_slots - E are
- *               dropped in expert order (the kernel never writes past
- *               max_slots); negative counts are taken as 0.
+ *               means one slot per expert, unless replica_budget > 0.  Copies
+ *               beyond max_slots - E are dropped in expert order (the kernel
+ *               never writes past max_slots); negative counts are taken as 0.
+ *   replica_budget  with replicas == NULL and replica_budget = R > 0, the
+ *               dispatch plans the replicas itself from this routing's
+ *               counts: the greedy capacity-bounded rule of moe_stats and
+ *               moe_plan_replicas ([GPS] section 2.1, [MPMC] method; total =
+ *               T*k), the same plan moe_stats writes for these counts.  So
+ *               the replicated layer needs no moe_stats before its dispatch,
+ *               and the statistics can run beside the rest of the layer.
+ *               Needs max_slots >= E + R; 0 with non-NULL replicas.
  *   counts      int32 [E] (may be NULL): moe_stats' counts of this routing.
  *               The offsets come from topk_idx itself (rows are ranked per
  *               block of pairs, which needs the per-block counts anyway);
@@ -243,16 +251,17 @@ int moe_prediction_quality(const float* pred, const int32_t* counts, int E, cons
  *               (per-block counts and offsets, per-pair ranks); any contents.
  * Three launches: per block of 512 (token, slot) pairs its counts and each
  * pair's rank among the block's pairs of its expert (wave ballots); one block
- * turning the block counts into offsets and the slot table; the row copy,
- * which also writes perm_src and inv_pos.
+ * turning the block counts into offsets, the replica plan (replica_budget)
+ * and the slot table; the row copy, which also writes perm_src and inv_pos.
  * check: MOE_CHECK_INDEX (an index outside [0, E): inv_pos = -1, no row),
  * MOE_CHECK_DUPLICATE, MOE_CHECK_COUNTS, MOE_CHECK_REPLICAS.
  * Limits: 1 <= E <= 256, 1 <= k <= min(E, 8), T*k < 2^31, E <= max_slots,
+ * 0 <= replica_budget <= max_slots - E (0 when replicas is given),
  * H*sizeof(dt) % 16 == 0, x and x_perm 16-byte aligned.
  */
 size_t moe_dispatch_workspace_bytes(int64_t T, int k, int E); /* [host] */
 int moe_dispatch(const void* x, moe_dtype dt, int64_t T, int H, const int32_t* topk_idx, int k, int E,
-                 const int32_t* counts, const int32_t* replicas, int max_slots,
+                 const int32_t* counts, const int32_t* replicas, int replica_budget, int max_slots,
                  void* x_perm, int32_t* perm_src, int32_t* inv_pos, int32_t* expert_off,
                  int32_t* slot_off, int32_t* slot_expert, int32_t* n_slots,
                  void* workspace, size_t workspace_bytes, int32_t* check, void* stream);
@@ -271,7 +280,7 @@ int moe_dispatch(const void* x, moe_dtype dt, int64_t T, int H, const int32_t* t
  * call writes every word it reads).  Same results as moe_dispatch.
  */
 int moe_dispatch_noalloc(const void* x, moe_dtype dt, int64_t T, int H, const int32_t* topk_idx, int k, int E,
-                         const int32_t* counts, const int32_t* replicas, int max_slots,
+                         const int32_t* counts, const int32_t* replicas, int replica_budget, int max_slots,
                          void* x_perm, int32_t* perm_src, int32_t* inv_pos, int32_t* expert_off,
                          int32_t* slot_off, int32_t* slot_expert, int32_t* n_slots, int32_t* check, void* stream);
 

@@ -222,15 +222,17 @@ def _dispatch_outputs(out, T, k, H, E, max_slots, dtype, dev):
 
 
 def moe_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, E: int, replicas=None, max_slots=None, out=None,
-                 workspace=None, stream=None, counts=None, check=None):
+                 workspace=None, stream=None, counts=None, check=None, replica_budget=0):
     """counts (int32 [E], e.g. moe_stats' counts of this routing) is only compared
-    with the routing when `check` is given."""
+    with the routing when `check` is given.  replica_budget > 0 with replicas None:
+    the dispatch plans the replicas from this routing's counts (max_slots defaults
+    to E + replica_budget)."""
     T, H = x.shape
     if topk_idx.shape[0] != T or topk_idx.dtype != torch.int32:
         raise ValueError("topk_idx must be int32 [T, k] for the T rows of x")
     k = topk_idx.shape[1]
     dev = x.device
-    max_slots = E if max_slots is None else max_slots
+    max_slots = E + replica_budget if max_slots is None else max_slots
     for t, name in ((replicas, "replicas"), (counts, "counts")):
         if t is not None and (t.numel() != E or t.dtype != torch.int32):
             raise ValueError(f"{name} must be int32 [E]")
@@ -239,14 +241,14 @@ def moe_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, E: int, replicas=None,
     workspace = torch.empty(need, dtype=torch.uint8, device=dev) if workspace is None else \
         _bytes_of(workspace, need, "dispatch workspace")
     _call("moe_dispatch", _ptr(x), _dtype_code(x), ctypes.c_int64(T), H, _ptr(topk_idx), k, E, _ptr(counts),
-          _ptr(replicas), max_slots, _ptr(o["x_perm"]), _ptr(o["perm_src"]), _ptr(o["inv_pos"]),
+          _ptr(replicas), replica_budget, max_slots, _ptr(o["x_perm"]), _ptr(o["perm_src"]), _ptr(o["inv_pos"]),
           _ptr(o["expert_off"]), _ptr(o["slot_off"]), _ptr(o["slot_expert"]), _ptr(o["n_slots"]), _ptr(workspace),
           ctypes.c_size_t(workspace.numel() * workspace.element_size()), _ptr(check), _stream(stream))
     return o
 
 
 def moe_dispatch_noalloc(x: torch.Tensor, topk_idx: torch.Tensor, E: int, replicas=None, max_slots=None, out=None,
-                         stream=None, counts=None, check=None):
+                         stream=None, counts=None, check=None, replica_budget=0):
     """moe_dispatch on the library's static device scratch (no workspace): for
     callers that cannot allocate.  `out` must hold every output (nothing is
     allocated here).  Calls that overlap on one GPU race."""
@@ -254,7 +256,7 @@ def moe_dispatch_noalloc(x: torch.Tensor, topk_idx: torch.Tensor, E: int, replic
     if topk_idx.shape[0] != T or topk_idx.dtype != torch.int32:
         raise ValueError("topk_idx must be int32 [T, k] for the T rows of x")
     k = topk_idx.shape[1]
-    max_slots = E if max_slots is None else max_slots
+    max_slots = E + replica_budget if max_slots is None else max_slots
     need = ("x_perm", "perm_src", "inv_pos", "expert_off", "slot_off", "slot_expert", "n_slots")
     if out is None or any(key not in out for key in need):
         raise ValueError(f"moe_dispatch_noalloc allocates nothing: out must hold {need}")
@@ -263,7 +265,7 @@ def moe_dispatch_noalloc(x: torch.Tensor, topk_idx: torch.Tensor, E: int, replic
             raise ValueError(f"{name} must be int32 [E]")
     o = _dispatch_outputs(out, T, k, H, E, max_slots, x.dtype, x.device)
     _call("moe_dispatch_noalloc", _ptr(x), _dtype_code(x), ctypes.c_int64(T), H, _ptr(topk_idx), k, E, _ptr(counts),
-          _ptr(replicas), max_slots, _ptr(o["x_perm"]), _ptr(o["perm_src"]), _ptr(o["inv_pos"]),
+          _ptr(replicas), replica_budget, max_slots, _ptr(o["x_perm"]), _ptr(o["perm_src"]), _ptr(o["inv_pos"]),
           _ptr(o["expert_off"]), _ptr(o["slot_off"]), _ptr(o["slot_expert"]), _ptr(o["n_slots"]), _ptr(check),
           _stream(stream))
     return o
@@ -373,16 +375,19 @@ def moe_backward(x_perm, y_perm, topk_idx, topk_w, inv_pos, expert_off, w_gate, 
 def moe_layer_forward(x, logits, k, w_gate, w_up, w_down, act="swiglu", replica_budget=0, stats_state=None,
                       stats_dims=None, layer=0, it=0, prev_topk_idx=None, path="grouped", bufs=None, stream=None,
                       planned_replicas=None, check=None, ffn_events=None):
-    """route -> stats (+ replicas) -> dispatch -> FFN -> combine, all on `stream`.
+    """route -> stats -> dispatch -> FFN -> combine, all on `stream`.
 
-    stats_state/stats_dims=(L, E, window) enable the windowed statistics; the
-    replica budget needs this iteration's counts, which moe_stats produces.
+    stats_state/stats_dims=(L, E, window) enable the windowed statistics
+    (counts, p_seq, the conditional matrix, the prediction) and the replica
+    plan from this iteration's counts, which the dispatch then takes.  Without
+    statistics a replica budget is planned by the dispatch itself from the
+    same counts (the same rule, so the same plan), and no moe_stats runs.
     planned_replicas (int32 [E], e.g. from moe_plan_replicas on the previous
-    layer's prediction) replaces that count-based plan; it must hand out at
-    most replica_budget copies.  `bufs` (a dict) caches outputs and workspaces
-    between calls; they are reallocated when the shapes change.  `check`: the
-    device-check word passed to all five calls.  ffn_events: three
-    torch.cuda.Event objects recorded around the two GEMM launches
+    layer's prediction) replaces the count-based plan; it must hand out at
+    most replica_budget copies.  `bufs` (a dict) caches outputs and
+    workspaces between calls; they are reallocated when the shapes change.
+    `check`: the device-check word passed to all five calls.  ffn_events:
+    three torch.cuda.Event objects recorded around the two GEMM launches
     (moe_expert_ffn_profiled)."""
     T, E = logits.shape
     H = x.shape[1]
@@ -398,14 +403,7 @@ def moe_layer_forward(x, logits, k, w_gate, w_up, w_down, act="swiglu", replica_
     b["idx"], b["w"] = idx, w
     res = {"idx": idx, "w": w}
     replicas, counts = None, None
-    if stats_state is not None or replica_budget > 0:
-        if stats_state is None:
-            stats_dims = (1, E, 1)
-            stats_state = b.get("_state")
-            if stats_state is None:
-                stats_state = torch.empty(moe_stats_state_bytes(*stats_dims), dtype=torch.uint8, device=dev)
-                moe_stats_init(stats_state, *stats_dims, stream=stream)
-                b["_state"] = stats_state
+    if stats_state is not None:
         L_, E_, win = stats_dims
         for name, n, dt in (("counts", E, torch.int32), ("p_seq", E, torch.float32), ("replicas", E, torch.int32)):
             if name not in b:
@@ -425,7 +423,8 @@ def moe_layer_forward(x, logits, k, w_gate, w_up, w_down, act="swiglu", replica_
         res["replicas"] = planned_replicas
     if "ws_d" not in b:
         b["ws_d"] = torch.empty(moe_dispatch_workspace_bytes(T, k, E), dtype=torch.uint8, device=dev)
-    d = moe_dispatch(x, idx, E, replicas, max_slots, b.get("disp"), b["ws_d"], stream, counts, check)
+    d = moe_dispatch(x, idx, E, replicas, max_slots, b.get("disp"), b["ws_d"], stream, counts, check,
+                     replica_budget=replica_budget if replicas is None else 0)
     b["disp"] = d
     if "y_perm" not in b:
         b["y_perm"] = torch.empty_like(d["x_perm"])

@@ -16,7 +16,8 @@
 //               experts of a wave, LDS counts across waves and rounds.
 //   2. scan:    one block: the expert totals, expert_off, and per block and
 //               expert the first row of the block's pairs (the column prefix
-//               of the count table, O(blocks x E)); the slot table; with a
+//               of the count table, O(blocks x E)); the replica plan from the
+//               totals when asked for (replica_budget); the slot table; with a
 //               check word, the totals against `counts` and the replicas
 //               against the slot budget.
 //   3. permute: row = base[f / kPairs][e] + rank[f]; the threads of token t
@@ -27,6 +28,7 @@
 #include <mutex>
 
 #include "common.h"
+#include "replica_plan.h"
 
 namespace {
 
@@ -118,8 +120,9 @@ __device__ void block_scan_inclusive(int64_t* v, int n) {
 }
 
 __global__ __launch_bounds__(kThreads) void scan_kernel(const int32_t* __restrict__ blk_cnt, int nblk, int E,
-                                                        const int32_t* __restrict__ counts,
-                                                        const int32_t* __restrict__ replicas, int max_slots,
+                                                        int64_t P, const int32_t* __restrict__ counts,
+                                                        const int32_t* __restrict__ replicas, int plan_budget,
+                                                        int max_slots,
                                                         int32_t* __restrict__ blk_base, int32_t* __restrict__ expert_off,
                                                         int32_t* __restrict__ slot_off,
                                                         int32_t* __restrict__ slot_expert, int32_t* __restrict__ n_slots,
@@ -128,6 +131,7 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const int32_t* __restric
   __shared__ int64_t off[moe::kMaxExperts];
   __shared__ int64_t rep[moe::kMaxExperts];
   __shared__ int32_t tot[moe::kMaxExperts];
+  __shared__ int32_t want_s[moe::kMaxExperts];   // replicas asked for, per expert
   const int tid = threadIdx.x;
   // thread (g, e) = g*E + e sums column e over group g's run of blocks
   const int G = kThreads / E;
@@ -146,9 +150,22 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const int32_t* __restric
     for (int q = 0; q < G; ++q) t += part[q * E + tid];
     tot[tid] = t;
     off[tid] = t;
-    const int32_t want = replicas ? replicas[tid] : 0;
-    rep[tid] = max(want, 0);
+    want_s[tid] = replicas ? replicas[tid] : 0;
   }
+  __syncthreads();
+  // this routing's replica plan (wave 0: 64 lanes x 4 experts; total = T*k)
+  if (plan_budget > 0 && tid < 64) {
+    int64_t n[4];
+    int r[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) n[j] = tid + 64 * j < E ? tot[tid + 64 * j] : 0;
+    moe::plan_replicas_wave(n, E, P, plan_budget, tid, r);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (tid + 64 * j < E) want_s[tid + 64 * j] = r[j];
+  }
+  __syncthreads();
+  if (tid < E) rep[tid] = max(want_s[tid], 0);
   __syncthreads();
   // exclusive prefixes: expert offsets and replica counts
   block_scan_inclusive(off, E);
@@ -169,8 +186,8 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const int32_t* __restric
   for (int x = tid; x < E; x += kThreads) {
     const int64_t excl = off[x] - tot[x];
     expert_off[x] = static_cast<int32_t>(excl);
-    const int64_t rp = rep[x] - (replicas ? max(replicas[x], 0) : 0);  // copies of experts before x
-    const int64_t want = replicas ? max(replicas[x], 0) : 0;
+    const int64_t want = max(want_s[x], 0);
+    const int64_t rp = rep[x] - want;  // copies of experts before x
     const int64_t r = max<int64_t>(0, min<int64_t>(want, budget - rp));
     const int64_t s0 = x + min<int64_t>(rp, budget);
     const int64_t n = tot[x];
@@ -179,7 +196,7 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const int32_t* __restric
       slot_off[s0 + rho] = static_cast<int32_t>(excl + (rho * n) / (r + 1));
     }
     bad_counts |= counts && counts[x] != tot[x];
-    bad_reps |= replicas && (replicas[x] < 0 || r < want);
+    bad_reps |= want_s[x] < 0 || r < want;
   }
   if (tid == 0) expert_off[E] = M;
   const int64_t all = E > 0 ? rep[E - 1] : 0;
@@ -272,7 +289,7 @@ extern "C" size_t moe_dispatch_workspace_bytes(int64_t T, int k, int E) {
 }
 
 extern "C" int moe_dispatch(const void* x, moe_dtype dt, int64_t T, int H, const int32_t* topk_idx, int k, int E,
-                            const int32_t* counts, const int32_t* replicas, int max_slots,
+                            const int32_t* counts, const int32_t* replicas, int replica_budget, int max_slots,
                             void* x_perm, int32_t* perm_src, int32_t* inv_pos, int32_t* expert_off,
                             int32_t* slot_off, int32_t* slot_expert, int32_t* n_slots,
                             void* workspace, size_t workspace_bytes, int32_t* check, void* stream) {
@@ -285,6 +302,9 @@ extern "C" int moe_dispatch(const void* x, moe_dtype dt, int64_t T, int H, const
   if (H < 1 || (static_cast<int64_t>(H) * elem_bytes(dt)) % 16 != 0)
     return fail(MOE_ERR_INVALID_ARG, "moe_dispatch: H*sizeof(dtype) must be a positive multiple of 16 (H=%d)", H);
   if (max_slots < E || max_slots > E + 65536) return fail(MOE_ERR_INVALID_ARG, "moe_dispatch: max_slots=%d outside [E, E+65536]", max_slots);
+  if (replica_budget < 0 || replica_budget > max_slots - E || (replicas && replica_budget != 0))
+    return fail(MOE_ERR_INVALID_ARG, "moe_dispatch: replica_budget=%d must lie in [0, max_slots - E] and be 0 "
+                "when replicas is given", replica_budget);
   if (!expert_off || !slot_off || !slot_expert || !n_slots || !workspace)
     return fail(MOE_ERR_INVALID_ARG, "moe_dispatch: null pointer");
   if (T > 0 && (!x || !topk_idx || !x_perm || !perm_src || !inv_pos))
@@ -302,8 +322,8 @@ extern "C" int moe_dispatch(const void* x, moe_dtype dt, int64_t T, int H, const
   const int64_t P = T * k;
   const int nblk = static_cast<int>(ceil_div(P, kPairs));
   if (nblk > 0) rank_kernel<<<nblk, kThreads, 0, s>>>(topk_idx, P, k, E, blk_cnt, rank, check);
-  scan_kernel<<<1, kThreads, 0, s>>>(blk_cnt, nblk, E, counts, replicas, max_slots, blk_base, expert_off, slot_off,
-                                     slot_expert, n_slots, check);
+  scan_kernel<<<1, kThreads, 0, s>>>(blk_cnt, nblk, E, P, counts, replicas, replica_budget, max_slots, blk_base,
+                                     expert_off, slot_off, slot_expert, n_slots, check);
   if (T > 0) {
     const int chunks = static_cast<int>(static_cast<int64_t>(H) * elem_bytes(dt) / 16);
     const int64_t threads = T * ceil_div(chunks, kChunksPerThread);
@@ -315,7 +335,8 @@ extern "C" int moe_dispatch(const void* x, moe_dtype dt, int64_t T, int H, const
 }
 
 extern "C" int moe_dispatch_noalloc(const void* x, moe_dtype dt, int64_t T, int H, const int32_t* topk_idx, int k,
-                                    int E, const int32_t* counts, const int32_t* replicas, int max_slots, void* x_perm,
+                                    int E, const int32_t* counts, const int32_t* replicas, int replica_budget,
+                                    int max_slots, void* x_perm,
                                     int32_t* perm_src, int32_t* inv_pos, int32_t* expert_off, int32_t* slot_off,
                                     int32_t* slot_expert, int32_t* n_slots, int32_t* check, void* stream) {
   using namespace moe;
@@ -328,6 +349,6 @@ extern "C" int moe_dispatch_noalloc(const void* x, moe_dtype dt, int64_t T, int 
   }
   void* ws = nullptr;
   if (int rc = scratch_on_current_device(&ws)) return rc;
-  return moe_dispatch(x, dt, T, H, topk_idx, k, E, counts, replicas, max_slots, x_perm, perm_src, inv_pos, expert_off,
-                      slot_off, slot_expert, n_slots, ws, kScratchBytes, check, stream);
+  return moe_dispatch(x, dt, T, H, topk_idx, k, E, counts, replicas, replica_budget, max_slots, x_perm, perm_src,
+                      inv_pos, expert_off, slot_off, slot_expert, n_slots, ws, kScratchBytes, check, stream);
 }

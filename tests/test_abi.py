@@ -65,10 +65,14 @@ N = None
     ("moe_stats", (1, 8, 2, 8, 10, 1, 0, 1, N, 0, 2, N, N, N, N, 0, N, N, N), -3, "too small"),
     ("moe_stats", (1, 1 << 20, 2, 8, 10, 1, 0, 1, N, 100, 2, N, N, N, N, 0, N, N, N), -1, "prev_topk_idx"),
     ("moe_stats_init", (N, 0, 2, 8, 10, N), -1, "null state"),
-    ("moe_dispatch", (16, 0, 10, 64, 16, 2, 8, N, N, 8, 16, 16, 16, 16, 16, 16, 16, 16, 0, N, N), -3, "workspace"),
-    ("moe_dispatch", (1, 1, 10, 7, 1, 2, 8, N, N, 8, 1, 1, 1, 1, 1, 1, 1, 1, 1 << 20, N, N), -1, "multiple of 16"),
-    ("moe_dispatch", (1, 0, 10, 64, 1, 2, 8, N, N, 4, 1, 1, 1, 1, 1, 1, 1, 1, 1 << 20, N, N), -1, "max_slots"),
-    ("moe_dispatch", (8, 0, 10, 64, 8, 2, 8, N, N, 8, 8, 8, 8, 8, 8, 8, 8, 8, 1 << 20, N, N), -1, "aligned"),
+    ("moe_dispatch", (16, 0, 10, 64, 16, 2, 8, N, N, 0, 8, 16, 16, 16, 16, 16, 16, 16, 16, 0, N, N), -3, "workspace"),
+    ("moe_dispatch", (1, 1, 10, 7, 1, 2, 8, N, N, 0, 8, 1, 1, 1, 1, 1, 1, 1, 1, 1 << 20, N, N), -1, "multiple of 16"),
+    ("moe_dispatch", (1, 0, 10, 64, 1, 2, 8, N, N, 0, 4, 1, 1, 1, 1, 1, 1, 1, 1, 1 << 20, N, N), -1, "max_slots"),
+    ("moe_dispatch", (8, 0, 10, 64, 8, 2, 8, N, N, 0, 8, 8, 8, 8, 8, 8, 8, 8, 8, 1 << 20, N, N), -1, "aligned"),
+    ("moe_dispatch", (16, 0, 10, 64, 16, 2, 8, N, N, 5, 12, 16, 16, 16, 16, 16, 16, 16, 16, 1 << 20, N, N), -1,
+     "replica_budget"),
+    ("moe_dispatch", (16, 0, 10, 64, 16, 2, 8, N, 16, 2, 12, 16, 16, 16, 16, 16, 16, 16, 16, 1 << 20, N, N), -1,
+     "replica_budget"),
     ("moe_expert_ffn", (16, 1, 100, 96, 128, 8, 16, 16, 16, 8, 16, 16, 16, 0, 1, 16, 16, 1 << 30, N, N), -2, "multiples of 64"),
     ("moe_expert_ffn", (16, 1, 100, 128, 128, 8, 16, 16, 16, 8, 16, N, 16, 0, 1, 16, 16, 1 << 30, N, N), -1, "w_up"),
     ("moe_expert_ffn", (16, 1, 100, 128, 128, 8, 16, 16, 16, 8, 16, 16, 16, 1, 1, 16, 16, 1 << 30, N, N), -1, "GELU"),

@@ -140,7 +140,10 @@ def test_stats_maximum_E_and_k():
                                           (513, 16, 4, 64, "bf16", 16), (1, 8, 2, 8, "bf16", 3),
                                           (300, 32, 2, 40, "f32", 5), (4100, 8, 2, 128, "bf16", 8),
                                           (777, 256, 8, 64, "bf16", 64)])
-def test_dispatch_matches_oracle(T, E, k, H, dt, R):
+@pytest.mark.parametrize("plan", [False, True])
+def test_dispatch_matches_oracle(T, E, k, H, dt, R, plan):
+    """plan: the dispatch plans the replicas itself from the routing's counts
+    (replica_budget = R) instead of taking the oracle's plan."""
     lg = _logits(T, E, 7 * T + E, skew=2.0)
     idx_o, _ = oracle.route(lg, k)
     rng = np.random.default_rng(T)
@@ -148,7 +151,10 @@ def test_dispatch_matches_oracle(T, E, k, H, dt, R):
     x = synth.f32_to_bf16_bits(x) if dt == "bf16" else x
     reps = oracle.replicas(oracle.histogram(idx_o, E), T, k, R) if R else None
     max_slots = E + R
-    d = moe.moe_dispatch(to_dev(x), to_dev(idx_o), E, None if reps is None else to_dev(reps), max_slots)
+    if plan:
+        d = moe.moe_dispatch(to_dev(x), to_dev(idx_o), E, None, max_slots, replica_budget=R)
+    else:
+        d = moe.moe_dispatch(to_dev(x), to_dev(idx_o), E, None if reps is None else to_dev(reps), max_slots)
     _sync()
     ref = oracle.dispatch(idx_o, E, reps)
     for key in ("expert_off", "perm_src", "inv_pos"):
@@ -159,6 +165,25 @@ def test_dispatch_matches_oracle(T, E, k, H, dt, R):
     assert np.all(from_dev(d["slot_off"])[S:] == T * k)
     assert np.array_equal(from_dev(d["slot_expert"])[:S], ref["slot_expert"])
     assert np.array_equal(from_dev(d["x_perm"]), oracle.permute(x, ref["perm_src"]))
+
+
+def test_dispatch_plan_binding_budget_and_ties():
+    """The dispatch's own plan where the budget binds (every copy is handed out)
+    and where experts tie on load (ties go to the lower index): the slot table
+    equals the oracle's for the oracle's plan of the same counts."""
+    T, E, k = 96, 8, 2
+    idx = np.zeros((T, k), np.int32)
+    idx[:, 0] = np.arange(T) % 4           # experts 0-3 take 24 rows each
+    idx[:, 1] = 4 + (np.arange(T) % 2)      # experts 4, 5 take 48 each; 6, 7 none
+    for R in (1, 2, 3, 7, 20):
+        reps = oracle.replicas(oracle.histogram(idx, E), T, k, R)
+        d = moe.moe_dispatch(to_dev(np.zeros((T, 8), np.float32)), to_dev(idx), E, None, E + R, replica_budget=R)
+        _sync()
+        ref = oracle.dispatch(idx, E, reps)
+        S = ref["n_slots"]
+        assert int(from_dev(d["n_slots"])[0]) == S, R
+        assert np.array_equal(from_dev(d["slot_off"])[:S + 1], ref["slot_off"]), R
+        assert np.array_equal(from_dev(d["slot_expert"])[:S], ref["slot_expert"]), R
 
 
 def test_dispatch_replicas_beyond_budget_are_dropped():
