@@ -109,6 +109,50 @@ def algorithmic_layer_work(T, H, I, E, k, n_mat):
     return flops, w_bytes, mem
 
 
+class TimingEvent:
+    """A HIP event for timestamps inside a step: created with
+    hipEventDisableSystemFence, so recording it between two kernels does not
+    write back and invalidate the caches as a default event does (about 6 us
+    per record here, and the next kernel starts on emptied caches).  Its times
+    are read only after a device synchronize.  Same interface as
+    torch.cuda.Event where bench.py and moe_expert_ffn_profiled use one."""
+    _hip = None
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        if TimingEvent._hip is None:
+            hip = ctypes.CDLL("libamdhip64.so")   # the HIP runtime torch has loaded
+            hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            TimingEvent._hip = hip
+        self.h = ctypes.c_void_p()
+        rc = self._hip.hipEventCreateWithFlags(ctypes.byref(self.h), self.DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed: {rc}")
+
+    @property
+    def cuda_event(self):
+        return self.h.value
+
+    def record(self, stream):
+        rc = self._hip.hipEventRecord(self.h, ctypes.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed: {rc}")
+
+    def elapsed_time(self, other):
+        ms = ctypes.c_float()
+        rc = self._hip.hipEventElapsedTime(ctypes.byref(ms), self.h, other.h)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return ms.value
+
+    def __del__(self):
+        if self.h.value and TimingEvent._hip is not None:
+            TimingEvent._hip.hipEventDestroy(self.h)
+
+
 def spin_cycles(torch, stream, ms):
     """Argument of torch.cuda._sleep that keeps the GPU busy for about `ms`
     milliseconds (its counter's rate differs between devices: measured here)."""
@@ -837,7 +881,7 @@ def main():
         """K steps, each on flushed caches: the 512 MiB flush, then a GPU-side spin
         while the host issues the step (so the events time the GPU, not the host's
         argument marshalling), then the step between two events."""
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
+        ev = [[TimingEvent() for _ in range(5)] for _ in range(K)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(K):
@@ -888,7 +932,7 @@ def main():
     cold = {n: [] for n in names}
     spin3 = spin_cycles(torch, stream, 3.0)
     for rep in range(10):
-        phase_ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        phase_ev = [TimingEvent() for _ in range(6)]
         if rep >= 5:
             evict(rep)
         torch.cuda.synchronize()
