@@ -1139,6 +1139,12 @@ __global__ __launch_bounds__(256) void tiles_kernel(const int32_t* __restrict__ 
   const int32_t* se = staged ? se_lds : slot_expert;
   const int32_t* so = staged ? so_lds : slot_off;
   if (tid == 0) carry = carry2 = carry3 = 0;
+  // each GEMM's last (up to) 256 tiles of its 256-row table, for the re-listing
+  // below: with one chunk of slots (n <= 256) they are captured as they are
+  // written (the totals are known once the chunk's scan is done), else read
+  // back from the tables
+  __shared__ int32_t last_slot[2][256], last_row0[2][256], last_rend[2][256];
+  const bool direct = companion && n <= 256;
   __syncthreads();
   if (check) {
     // the slot table a dispatch writes: slot_off ascending inside [0, M],
@@ -1184,13 +1190,28 @@ __global__ __launch_bounds__(256) void tiles_kernel(const int32_t* __restrict__ 
       scan3[tid] += v3;
       __syncthreads();
     }
+    // direct capture: GEMM g's table has tot_g[g] tiles, its last 256 from b0_g[g]
+    int tot_g[2] = {0, 0}, b0_g[2] = {0, 0};
+    if (direct) {
+      tot_g[1] = min(scan[255], max_tiles);
+      tot_g[0] = mid_rows > 0 ? max(tot_g[1] - scan3[255], 0) : tot_g[1];
+      b0_g[0] = max(tot_g[0] - 256, 0);
+      b0_g[1] = max(tot_g[1] - 256, 0);
+    }
     const int32_t first = carry + scan[tid] - static_cast<int32_t>(cnt);
     for (int q = 0; q < cnt; ++q) {
       const int j = first + q;
       if (j < max_tiles) {
+        const int32_t r0 = static_cast<int32_t>(min<int64_t>(start + static_cast<int64_t>(q) * BM, M));
         tile_slot[j] = s;
-        tile_row0[j] = static_cast<int32_t>(min<int64_t>(start + static_cast<int64_t>(q) * BM, M));
+        tile_row0[j] = r0;
         tile_rend[j] = static_cast<int32_t>(end);
+        for (int g = mid_rows > 0 ? 1 : 0; g < 2; ++g)
+          if (direct && j >= b0_g[g] && j < tot_g[g]) {
+            last_slot[g][j - b0_g[g]] = s;
+            last_row0[g][j - b0_g[g]] = r0;
+            last_rend[g][j - b0_g[g]] = static_cast<int32_t>(end);
+          }
       }
     }
     const int32_t first2 = carry2 + scan2[tid] - static_cast<int32_t>(cnt_small);
@@ -1211,9 +1232,15 @@ __global__ __launch_bounds__(256) void tiles_kernel(const int32_t* __restrict__ 
       for (int q = 0; q < cnt_b; ++q) {
         const int j = first - mid_before + q;
         if (j < max_tiles) {
+          const int32_t r0 = static_cast<int32_t>(min<int64_t>(start + static_cast<int64_t>(q) * BM, M));
           split.alt_slot[j] = s;
-          split.alt_row0[j] = static_cast<int32_t>(min<int64_t>(start + static_cast<int64_t>(q) * BM, M));
+          split.alt_row0[j] = r0;
           split.alt_rend[j] = static_cast<int32_t>(end);
+          if (direct && j >= b0_g[0] && j < tot_g[0]) {
+            last_slot[0][j - b0_g[0]] = s;
+            last_row0[0][j - b0_g[0]] = r0;
+            last_rend[0][j - b0_g[0]] = static_cast<int32_t>(end);
+          }
         }
       }
       if (cnt_mid > 0) {  // at most one per range, at most max_slots in all
@@ -1235,68 +1262,140 @@ __global__ __launch_bounds__(256) void tiles_kernel(const int32_t* __restrict__ 
   if (!companion) return;
   const int n_rem = min(carry2, split.cap);
   const int n_mid = carry3;
-  // the last (up to) 256 tiles of each GEMM's 256-row table, staged in LDS by
-  // all threads at once: the tables' writes by the other threads are visible
-  // after the last barrier
-  __shared__ int32_t last_slot[2][256], last_row0[2][256], last_rend[2][256];
   const int total_g[2] = {mid_rows > 0 ? max(total - n_mid, 0) : total, total};
-  for (int g = 0; g < 2; ++g) {
-    const int32_t* ts = (g == 0 && mid_rows > 0) ? split.alt_slot : tile_slot;
-    const int32_t* tr = (g == 0 && mid_rows > 0) ? split.alt_row0 : tile_row0;
-    const int32_t* te = (g == 0 && mid_rows > 0) ? split.alt_rend : tile_rend;
-    const int b0 = max(total_g[g] - 256, 0);
-    if (b0 + tid < total_g[g]) {
-      last_slot[g][tid] = ts[b0 + tid];
-      last_row0[g][tid] = tr[b0 + tid];
-      last_rend[g][tid] = te[b0 + tid];
+  if (!direct) {
+    // more than one chunk: read the last tiles back (the tables' writes by the
+    // other threads are visible after the last barrier)
+    for (int g = 0; g < 2; ++g) {
+      const int32_t* ts = (g == 0 && mid_rows > 0) ? split.alt_slot : tile_slot;
+      const int32_t* tr = (g == 0 && mid_rows > 0) ? split.alt_row0 : tile_row0;
+      const int32_t* te = (g == 0 && mid_rows > 0) ? split.alt_rend : tile_rend;
+      const int b0 = max(total_g[g] - 256, 0);
+      if (b0 + tid < total_g[g]) {
+        last_slot[g][tid] = ts[b0 + tid];
+        last_row0[g][tid] = tr[b0 + tid];
+        last_rend[g][tid] = te[b0 + tid];
+      }
     }
+    __syncthreads();
   }
-  __syncthreads();
-  if (tid != 0) return;
+  // Per GEMM: re-list its last r row tiles (1 <= r <= r_max) as 64-row tiles
+  // where the modelled launch is shortest; the smallest r of the shortest.
+  // Candidate r is evaluated by lane / thread r - 1: rows(r) = 64-row tiles of
+  // the last r tiles (an inclusive scan), valid while the companion table has
+  // room for them.  The order key of a candidate is its modelled rounds (a
+  // non-negative float orders as its bits), then r.  With r_max <= 64 (at least
+  // 4 column tiles) wave g plans GEMM g with shuffles, the two at once;
+  // otherwise the block plans them one after the other.
+  __shared__ int32_t rows_s[256];
+  __shared__ unsigned long long best_key[4];
   const float c = split.small_cost;
+  const int lane = tid & 63, wv = tid >> 6;
+  int r_max_g[2], tail_g[2];
   for (int g = 0; g < 2; ++g) {
     const int nt = split.nt[g];
-    const int tot = total_g[g];
-    const int base = max(tot - 256, 0);
-    int best_r = 0, best_rows = 0;
-    if (nt > 0) {
-      // trailing row tiles of at most one round of blocks (and all staged)
-      const int r_max = min(min(tot, 256), (kWaveBlocks + nt - 1) / nt);
-      // GEMM 0's 128-row tiles and the short-range 64-row tiles run after the
-      // 256-row tiles, both modelled at cost c
-      const int64_t tail = static_cast<int64_t>(n_rem + (g == 0 ? n_mid : 0)) * nt;
-      float best = mixed_rounds(static_cast<int64_t>(tot) * nt, tail, c);
-      int rows = 0;
-      for (int r = 1; r <= r_max; ++r) {
-        const int t = tot - r - base;
-        rows += (min(BM, last_rend[g][t] - last_row0[g][t]) + 63) / 64;
-        if (n_rem + rows > split.cap) break;
-        const float e = mixed_rounds(static_cast<int64_t>(tot - r) * nt, tail + static_cast<int64_t>(rows) * nt, c);
-        if (e < best) {
-          best = e;
-          best_r = r;
-          best_rows = rows;
+    // trailing row tiles of at most one round of blocks (and all staged)
+    r_max_g[g] = nt > 0 ? min(min(total_g[g], 256), (kWaveBlocks + nt - 1) / nt) : 0;
+    // GEMM 0's 128-row tiles and the short-range 64-row tiles run after the
+    // 256-row tiles, both modelled at cost c
+    tail_g[g] = n_rem + (g == 0 ? n_mid : 0);
+  }
+  auto cand_key = [&](int g, int r, int rows) {
+    const int nt = split.nt[g], tot = total_g[g];
+    const int64_t tail = static_cast<int64_t>(tail_g[g]) * nt;
+    float e = __int_as_float(0x7f800000);
+    if (r == 0) e = mixed_rounds(static_cast<int64_t>(tot) * nt, tail, c);
+    else if (r <= r_max_g[g] && n_rem + rows <= split.cap)
+      e = mixed_rounds(static_cast<int64_t>(tot - r) * nt, tail + static_cast<int64_t>(rows) * nt, c);
+    return (static_cast<unsigned long long>(__float_as_uint(e)) << 32) | static_cast<unsigned>(r);
+  };
+  auto own_rows = [&](int g, int r) {
+    const int t = total_g[g] - r - max(total_g[g] - 256, 0);
+    return r <= r_max_g[g] ? (min(BM, last_rend[g][t] - last_row0[g][t]) + 63) / 64 : 0;
+  };
+  // tile total_g[g] - r (r <= best_r) goes after the re-listed tiles before it
+  auto relist = [&](int g, int r, int rows, int best_rows) {
+    const int t = total_g[g] - r - max(total_g[g] - 256, 0);
+    int small = n_rem + best_rows - rows;
+    const int end = min(last_row0[g][t] + BM, last_rend[g][t]);
+    for (int row = last_row0[g][t]; row < end; row += 64) {
+      split.slot[g * split.cap + small] = last_slot[g][t];
+      split.row0[g * split.cap + small] = row;
+      split.rend[g * split.cap + small] = last_rend[g][t];
+      ++small;
+    }
+  };
+  if (r_max_g[0] <= 64 && r_max_g[1] <= 64) {
+    if (wv < 2) {
+      const int g = wv, r = lane + 1;
+      int best_r = 0, best_rows = 0;
+      if (split.nt[g] > 0) {
+        int rows = own_rows(g, r);
+        for (int d = 1; d < 64; d <<= 1) {
+          const int v = __shfl_up(rows, d);
+          if (lane >= d) rows += v;
         }
+        unsigned long long key = cand_key(g, r, rows);
+        if (lane == 0) {
+          const unsigned long long k0 = cand_key(g, 0, 0);
+          key = k0 < key ? k0 : key;
+        }
+        for (int off = 32; off >= 1; off >>= 1) {
+          const unsigned long long o = __shfl_xor(key, off);
+          key = o < key ? o : key;
+        }
+        best_r = static_cast<int>(key & 0xffffffffu);
+        best_rows = __shfl(rows, best_r > 0 ? best_r - 1 : 0);
+        if (best_r == 0) best_rows = 0;
+        if (r <= best_r) relist(g, r, rows, best_rows);
       }
-      int32_t* sl = split.slot + g * split.cap;
-      int32_t* r0 = split.row0 + g * split.cap;
-      int32_t* re = split.rend + g * split.cap;
-      int small = n_rem;
-      for (int t = tot - best_r; t < tot; ++t) {
-        const int end = min(last_row0[g][t - base] + BM, last_rend[g][t - base]);
-        for (int row = last_row0[g][t - base]; row < end; row += 64) {
-          sl[small] = last_slot[g][t - base];
-          r0[small] = row;
-          re[small] = last_rend[g][t - base];
-          ++small;
-        }
+      if (lane == 0) {
+        split.counts[2 * g] = total_g[g] - best_r;
+        split.counts[2 * g + 1] = n_rem + best_rows;
       }
     }
-    split.counts[2 * g] = tot - best_r;
-    split.counts[2 * g + 1] = n_rem + best_rows;
+  } else {
+    for (int g = 0; g < 2; ++g) {
+      int best_r = 0, best_rows = 0;
+      if (split.nt[g] > 0) {
+        const int r = tid + 1;
+        rows_s[tid] = own_rows(g, r);
+        __syncthreads();
+        for (int d = 1; d < 256; d <<= 1) {
+          const int32_t v = tid >= d ? rows_s[tid - d] : 0;
+          __syncthreads();
+          rows_s[tid] += v;
+          __syncthreads();
+        }
+        const int rows = rows_s[tid];
+        unsigned long long key = cand_key(g, r, rows);
+        if (tid == 0) {
+          const unsigned long long k0 = cand_key(g, 0, 0);
+          key = k0 < key ? k0 : key;
+        }
+        for (int off = 32; off >= 1; off >>= 1) {
+          const unsigned long long o = __shfl_xor(key, off);
+          key = o < key ? o : key;
+        }
+        if (lane == 0) best_key[wv] = key;
+        __syncthreads();
+        unsigned long long bk = best_key[0];
+        for (int q = 1; q < 4; ++q) bk = best_key[q] < bk ? best_key[q] : bk;
+        best_r = static_cast<int>(bk & 0xffffffffu);
+        best_rows = best_r > 0 ? rows_s[best_r - 1] : 0;
+        if (r <= best_r) relist(g, r, rows, best_rows);
+        __syncthreads();
+      }
+      if (tid == 0) {
+        split.counts[2 * g] = total_g[g] - best_r;
+        split.counts[2 * g + 1] = n_rem + best_rows;
+      }
+    }
   }
-  split.counts[4] = n_mid;
-  split.counts[5] = 0;
+  if (tid == 0) {
+    split.counts[4] = n_mid;
+    split.counts[5] = 0;
+  }
 }
 
 }  // namespace
