@@ -672,12 +672,13 @@ def stats_bench(moe, synth, torch, np, reps=20):
              (("c", E, torch.int32), ("p", E, torch.float32), ("P", E * E, torch.float32), ("h", E, torch.float32),
               ("r", E, torch.int32))}
         ts = []
+        st = torch.cuda.current_stream()
         for it in range(reps + 3):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
+            a, b = TimingEvent(), TimingEvent()
+            a.record(st)
             moe.moe_stats(state, L, E, win, 1, it, idx[1], idx[0], k, o["c"], o["p"], o["P"], o["h"], R,
-                          o["r"] if R else None)
-            b.record()
+                          o["r"] if R else None, st)
+            b.record(st)
             torch.cuda.synchronize()
             if it >= 3:
                 ts.append(a.elapsed_time(b) * 1e3)

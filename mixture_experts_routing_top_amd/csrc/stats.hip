@@ -150,41 +150,64 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(Args a) {
   }
 
   // ---- finalize: one block ------------------------------------------------
+  // Its global reads and writes are independent of one another (the ring
+  // slot's new counts are added from registers, and the conditional matrix
+  // reads the pair (layer, layer + 1), not the pair updated here), so they are
+  // issued together and no fence is needed before the kernel ends.
   const int L = a.L, layer = a.layer, slot = a.slot, window = a.window;
   int32_t* cnt_ring = a.state + a.lay.cnt_ring;
   int32_t* cooc_ring = a.state + a.lay.cooc_ring;
-  if (a.idx) {
-    int32_t* dst = cnt_ring + (static_cast<size_t>(slot) * L + layer) * E;
-    for (int e = tid; e < E; e += kThreads) {
-      const int32_t c = atomicExch(&acc[e], 0);
-      dst[e] = c;
-      hist[e] = c;
-      if (a.counts) a.counts[e] = c;
-    }
-    if (do_cooc) {
-      // the pair's ring slot is replaced and its running window sum updated by
-      // the difference (exact integers: the sum over the ring, one load per cell)
-      int32_t* cdst = cooc_ring + (static_cast<size_t>(slot) * (L - 1) + (layer - 1)) * EE;
-      int32_t* csum = a.state + a.lay.cooc_sum + static_cast<size_t>(layer - 1) * EE;
-      for (int q = tid; q < EE; q += kThreads) {
-        const int32_t c = atomicExch(&acc_cooc[q], 0);
-        csum[q] += c - cdst[q];
-        cdst[q] = c;
-      }
-    }
-    __threadfence();
-  }
   if (tid == 0) total = 0;
   __syncthreads();
-
-  // Eq.(1): windowed popularity of this layer.
+  // Eq.(1): windowed popularity of this layer.  With this iteration's routing
+  // the accumulator (zeroed for the next call) replaces the ring slot and the
+  // window sum takes it from registers; the other slots come from the ring.
   for (int e = tid; e < E; e += kThreads) {
+    const int32_t c = a.idx ? atomicExch(&acc[e], 0) : 0;
     int32_t s = 0;
     // unrolled so the window's loads are in flight together (exact integer sum)
 #pragma unroll 8
-    for (int w = 0; w < window; ++w) s += cnt_ring[(static_cast<size_t>(w) * L + layer) * E + e];
+    for (int w = 0; w < window; ++w)
+      if (!a.idx || w != slot) s += cnt_ring[(static_cast<size_t>(w) * L + layer) * E + e];
+    if (a.idx) {
+      cnt_ring[(static_cast<size_t>(slot) * L + layer) * E + e] = c;
+      hist[e] = c;
+      if (a.counts) a.counts[e] = c;
+      s += c;
+    }
     nw[e] = s;
     atomicAdd(&total, static_cast<unsigned long long>(s));
+  }
+  if (do_cooc) {
+    // the pair's ring slot is replaced and its running window sum updated by
+    // the difference (exact integers: the sum over the ring, one load per cell)
+    int32_t* cdst = cooc_ring + (static_cast<size_t>(slot) * (L - 1) + (layer - 1)) * EE;
+    int32_t* csum = a.state + a.lay.cooc_sum + static_cast<size_t>(layer - 1) * EE;
+    // eight cells per thread per round, every load and exchange issued before
+    // the stores
+    constexpr int U = 8;
+    for (int q0 = tid; q0 < EE; q0 += U * kThreads) {
+      int32_t old[U], sum[U], c[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int q = q0 + u * kThreads;
+        old[u] = q < EE ? cdst[q] : 0;
+        sum[u] = q < EE ? csum[q] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int q = q0 + u * kThreads;
+        c[u] = q < EE ? atomicExch(&acc_cooc[q], 0) : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int q = q0 + u * kThreads;
+        if (q < EE) {
+          csum[q] = sum[u] + c[u] - old[u];
+          cdst[q] = c[u];
+        }
+      }
+    }
   }
   __syncthreads();
   const unsigned long long tot = total;
@@ -195,29 +218,55 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(Args a) {
   }
 
   // Eq.(2)-(3): conditional matrix of pair (layer, layer+1) and the prediction.
+  // Up to E = 128 the window sums are read once and the matrix is kept in the
+  // (now unused) co-occurrence LDS for the prediction's column sums; above, the
+  // window sums are read from memory where needed.
   if (layer + 1 < L && (a.cond || a.pred)) {
     const int32_t* win = a.state + a.lay.cooc_sum + static_cast<size_t>(layer) * EE;  // window sums
     for (int e = tid; e < E; e += kThreads) rowsum[e] = 0;
     __syncthreads();
-    for (int q = tid; q < EE; q += kThreads) {
-      const int32_t c = win[q];
-      if (c) atomicAdd(&rowsum[q / E], c);
-    }
-    __syncthreads();
-    auto prob = [&](int q) {
-      const int32_t c = win[q];
+    auto ratio = [&](int32_t c, int q) {
       const int32_t r = rowsum[q / E];
       return r ? __fdiv_rn(static_cast<float>(c), static_cast<float>(r)) : 0.f;
     };
-    if (a.cond)
-      for (int q = tid; q < EE; q += kThreads) a.cond[q] = prob(q);
-    if (a.pred)
-      for (int b = tid; b < E; b += kThreads) {
-        double s = 0.0;
-#pragma unroll 8
-        for (int x = 0; x < E; ++x) s += static_cast<double>(ps[x]) * static_cast<double>(prob(x * E + b));
-        a.pred[b] = static_cast<float>(s);
+    if (EE <= kLdsCooc) {
+      for (int q = tid; q < EE; q += kThreads) {
+        const int32_t c = win[q];
+        cooc[q] = c;
+        if (c) atomicAdd(&rowsum[q / E], c);
       }
+      __syncthreads();
+      for (int q = tid; q < EE; q += kThreads) {
+        const float pq = ratio(cooc[q], q);
+        if (a.cond) a.cond[q] = pq;
+        cooc[q] = __float_as_int(pq);
+      }
+      __syncthreads();
+      if (a.pred)
+        for (int b = tid; b < E; b += kThreads) {
+          double s = 0.0;
+#pragma unroll 8
+          for (int x = 0; x < E; ++x)
+            s += static_cast<double>(ps[x]) * static_cast<double>(__int_as_float(cooc[x * E + b]));
+          a.pred[b] = static_cast<float>(s);
+        }
+    } else {
+      for (int q = tid; q < EE; q += kThreads) {
+        const int32_t c = win[q];
+        if (c) atomicAdd(&rowsum[q / E], c);
+      }
+      __syncthreads();
+      if (a.cond)
+        for (int q = tid; q < EE; q += kThreads) a.cond[q] = ratio(win[q], q);
+      if (a.pred)
+        for (int b = tid; b < E; b += kThreads) {
+          double s = 0.0;
+#pragma unroll 8
+          for (int x = 0; x < E; ++x)
+            s += static_cast<double>(ps[x]) * static_cast<double>(ratio(win[x * E + b], x * E + b));
+          a.pred[b] = static_cast<float>(s);
+        }
+    }
   }
 
   // Replica plan from this iteration's counts (wave 0: 64 lanes x 4 experts).
