@@ -9,12 +9,15 @@
 // for loads above target); "Fast MoE Inference via Predictive Prefetching and
 // Expert Replication", contribution 3 (replica counts bounded by a budget).
 //
-// One launch.  Every block histograms its token range into LDS (counts, and
-// the k*k co-occurrence pairs with the previous layer), then merges the
-// non-zero bins into a device accumulator with atomics.  The block that takes
-// the last ticket moves the accumulator into the ring slot (zeroing it for
-// the next call), sums the ring, and derives popularity, the conditional
-// matrix, the prediction and the replica counts.  All counts are exact
+// One launch (two above E = 64).  Every block histograms its token range
+// into LDS (counts, and the k*k co-occurrence pairs with the previous layer),
+// then merges the non-zero bins into a device accumulator with atomics.  The
+// block that takes the last ticket moves the accumulator into the ring slot
+// (zeroing it for the next call), sums the ring, and derives popularity, the
+// conditional matrix, the prediction and the replica counts.  Above E = 64 the
+// E*E work (the co-occurrence ring update, the conditional matrix) is too much
+// for one block: a second launch spreads it over blocks of 2048 cells and of
+// four rows, and the last of the row blocks (ticket) sums the prediction.  All counts are exact
 // integers; the divisions are IEEE fp32 divisions of exact integers and the
 // prediction is a double sum in expert order, so the results do not depend on
 // the order in which blocks finish.  With a check word, indices outside [0, E)
@@ -32,9 +35,10 @@ constexpr int kTokPerBlock = 512;
 // cell, so while recording, two 16-bit counters share one LDS word: E*E up to
 // 32768 cells (E <= 181) stays in LDS; larger E adds into global memory.
 constexpr int kLdsCooc = 128 * 128;  // LDS words for co-occurrence
+constexpr int kSplitE = 64;          // above: the E*E work runs in pair_kernel
 
 struct Layout {
-  size_t cnt_ring, cooc_ring, cooc_sum, acc, acc_cooc, ticket, words;
+  size_t cnt_ring, cooc_ring, cooc_sum, acc, acc_cooc, ticket, ps, pmat, ticket2, words;
 };
 
 Layout layout(int L, int E, int window) {
@@ -47,6 +51,10 @@ Layout layout(int L, int E, int window) {
   q.acc = take(E);
   q.acc_cooc = take(L > 1 ? static_cast<size_t>(E) * E : 0);
   q.ticket = take(1);
+  // E > kSplitE: p_seq and the conditional matrix handed to pair_kernel, and its ticket
+  q.ps = take(E);
+  q.pmat = take(L > 1 ? static_cast<size_t>(E) * E : 0);
+  q.ticket2 = take(1);
   q.words = w;
   return q;
 }
@@ -178,7 +186,8 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(Args a) {
     nw[e] = s;
     atomicAdd(&total, static_cast<unsigned long long>(s));
   }
-  if (do_cooc) {
+  const bool split = E > kSplitE;
+  if (do_cooc && !split) {
     // the pair's ring slot is replaced and its running window sum updated by
     // the difference (exact integers: the sum over the ring, one load per cell)
     int32_t* cdst = cooc_ring + (static_cast<size_t>(slot) * (L - 1) + (layer - 1)) * EE;
@@ -215,13 +224,14 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(Args a) {
     const float p = tot ? __fdiv_rn(static_cast<float>(nw[e]), static_cast<float>(tot)) : 0.f;
     ps[e] = p;
     if (a.p_seq) a.p_seq[e] = p;
+    if (split) reinterpret_cast<float*>(a.state + a.lay.ps)[e] = p;
   }
 
   // Eq.(2)-(3): conditional matrix of pair (layer, layer+1) and the prediction.
   // Up to E = 128 the window sums are read once and the matrix is kept in the
   // (now unused) co-occurrence LDS for the prediction's column sums; above, the
   // window sums are read from memory where needed.
-  if (layer + 1 < L && (a.cond || a.pred)) {
+  if (!split && layer + 1 < L && (a.cond || a.pred)) {
     const int32_t* win = a.state + a.lay.cooc_sum + static_cast<size_t>(layer) * EE;  // window sums
     for (int e = tid; e < E; e += kThreads) rowsum[e] = 0;
     __syncthreads();
@@ -281,6 +291,89 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(Args a) {
       if (tid + 64 * j < E) a.replicas[tid + 64 * j] = r[j];
   }
   if (a.idx && tid == 0) atomicExch(ticket, 0u);
+}
+
+// The E*E part of the finalize for E > kSplitE, after stats_kernel on the
+// same stream: blocks [0, n_ring) replace pair (layer-1, layer)'s ring slot
+// with the accumulator and update its running window sum (2048 cells each,
+// eight per thread in flight); the row blocks after them take four rows of
+// pair (layer, layer+1) each, one wave per row: the row's window sums, their
+// exact integer row sum (a wave reduction) and the row-normalised
+// probabilities, into cond and into the state for the prediction.  The last
+// row block (ticket) sums the prediction in expert order from p_seq, which
+// stats_kernel left in the state.  The same integers, fp32 divisions and
+// double sums as the one-block finalize.
+__global__ __launch_bounds__(kThreads) void pair_kernel(Args a, int n_ring, int n_rows) {
+  __shared__ int is_last;
+  const int E = a.E, EE = E * E, tid = threadIdx.x, L = a.L, layer = a.layer;
+  if (static_cast<int>(blockIdx.x) < n_ring) {
+    int32_t* cdst = a.state + a.lay.cooc_ring + (static_cast<size_t>(a.slot) * (L - 1) + (layer - 1)) * EE;
+    int32_t* csum = a.state + a.lay.cooc_sum + static_cast<size_t>(layer - 1) * EE;
+    int32_t* acc_cooc = a.state + a.lay.acc_cooc;
+    constexpr int U = 8;
+    const int q0 = blockIdx.x * (U * kThreads) + tid;
+    int32_t old[U], sum[U], c[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int q = q0 + u * kThreads;
+      old[u] = q < EE ? cdst[q] : 0;
+      sum[u] = q < EE ? csum[q] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int q = q0 + u * kThreads;
+      c[u] = q < EE ? atomicExch(&acc_cooc[q], 0) : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int q = q0 + u * kThreads;
+      if (q < EE) {
+        csum[q] = sum[u] + c[u] - old[u];
+        cdst[q] = c[u];
+      }
+    }
+    return;
+  }
+  const int32_t* win = a.state + a.lay.cooc_sum + static_cast<size_t>(layer) * EE;  // window sums
+  float* pmat = reinterpret_cast<float*>(a.state + a.lay.pmat);
+  const int lane = tid & 63;
+  const int x = (static_cast<int>(blockIdx.x) - n_ring) * (kThreads / 64) + (tid >> 6);
+  if (x < E) {
+    int32_t c[4];
+    int32_t rs = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int b = lane + 64 * j;
+      c[j] = b < E ? win[static_cast<size_t>(x) * E + b] : 0;
+      rs += c[j];
+    }
+    for (int off = 32; off >= 1; off >>= 1) rs += __shfl_xor(rs, off);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int b = lane + 64 * j;
+      if (b < E) {
+        const float p = rs ? __fdiv_rn(static_cast<float>(c[j]), static_cast<float>(rs)) : 0.f;
+        if (a.cond) a.cond[static_cast<size_t>(x) * E + b] = p;
+        if (a.pred) pmat[static_cast<size_t>(x) * E + b] = p;
+      }
+    }
+  }
+  if (!a.pred) return;
+  unsigned* ticket = reinterpret_cast<unsigned*>(a.state + a.lay.ticket2);
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) is_last = (atomicAdd(ticket, 1u) == static_cast<unsigned>(n_rows) - 1);
+  __syncthreads();
+  if (!is_last) return;
+  __threadfence();
+  const float* ps = reinterpret_cast<const float*>(a.state + a.lay.ps);
+  for (int b = tid; b < E; b += kThreads) {
+    double s = 0.0;
+#pragma unroll 32
+    for (int y = 0; y < E; ++y) s += static_cast<double>(ps[y]) * static_cast<double>(pmat[static_cast<size_t>(y) * E + b]);
+    a.pred[b] = static_cast<float>(s);
+  }
+  if (tid == 0) atomicExch(ticket, 0u);
 }
 
 // Decayed-window popularity and the load-state check of one layer, read from
@@ -420,6 +513,12 @@ extern "C" int moe_stats(void* state, size_t state_bytes, int L, int E, int wind
   a.check = topk_idx ? check : nullptr;
   const unsigned blocks = topk_idx ? static_cast<unsigned>(std::max<int64_t>(1, ceil_div(T, kTokPerBlock))) : 1u;
   stats_kernel<<<blocks, kThreads, 0, as_stream(stream)>>>(a);
+  if (E > kSplitE) {
+    const int EE = E * E;
+    const int n_ring = (topk_idx && layer > 0) ? static_cast<int>(ceil_div(EE, 8 * kThreads)) : 0;
+    const int n_rows = (layer + 1 < L && (a.cond || a.pred)) ? static_cast<int>(ceil_div(E, kThreads / 64)) : 0;
+    if (n_ring + n_rows > 0) pair_kernel<<<n_ring + n_rows, kThreads, 0, as_stream(stream)>>>(a, n_ring, n_rows);
+  }
   return hip_status(hipGetLastError(), "moe_stats launch");
 }
 
