@@ -33,6 +33,7 @@
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kScanThreads = 1024;  // the one scan block: kScanThreads / E threads per expert column
 constexpr int kPairs = 512;  // pairs per rank block (two rounds of 256)
 static_assert(kPairs % kThreads == 0, "whole rounds");
 
@@ -119,7 +120,7 @@ __device__ void block_scan_inclusive(int64_t* v, int n) {
   }
 }
 
-__global__ __launch_bounds__(kThreads) void scan_kernel(const int32_t* __restrict__ blk_cnt, int nblk, int E,
+__global__ __launch_bounds__(kScanThreads) void scan_kernel(const int32_t* __restrict__ blk_cnt, int nblk, int E,
                                                         int64_t P, const int32_t* __restrict__ counts,
                                                         const int32_t* __restrict__ replicas, int plan_budget,
                                                         int max_slots,
@@ -127,21 +128,28 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const int32_t* __restric
                                                         int32_t* __restrict__ slot_off,
                                                         int32_t* __restrict__ slot_expert, int32_t* __restrict__ n_slots,
                                                         int32_t* __restrict__ check) {
-  __shared__ int32_t part[kThreads];   // [group][expert] partial column sums
+  __shared__ int32_t part[kScanThreads];   // [group][expert] partial column sums
   __shared__ int64_t off[moe::kMaxExperts];
   __shared__ int64_t rep[moe::kMaxExperts];
   __shared__ int32_t tot[moe::kMaxExperts];
   __shared__ int32_t want_s[moe::kMaxExperts];   // replicas asked for, per expert
   const int tid = threadIdx.x;
-  // thread (g, e) = g*E + e sums column e over group g's run of blocks
-  const int G = kThreads / E;
+  // thread (g, e) = g*E + e sums column e over group g's run of blocks, eight
+  // loads in flight
+  constexpr int U = 8;
+  const int G = kScanThreads / E;
   const int g = tid / E, e = tid - g * E;
   const int per = (nblk + G - 1) / G;
   const int b0 = min(g * per, nblk), b1 = min(b0 + per, nblk);
   int32_t s = 0;
   if (g < G) {
-#pragma unroll 4
-    for (int b = b0; b < b1; ++b) s += blk_cnt[static_cast<int64_t>(b) * E + e];
+    for (int b = b0; b < b1; b += U) {
+      int32_t c[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) c[u] = b + u < b1 ? blk_cnt[static_cast<int64_t>(b + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < U; ++u) s += c[u];
+    }
     part[tid] = s;
   }
   __syncthreads();
@@ -175,15 +183,21 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const int32_t* __restric
   if (g < G) {
     int32_t run = static_cast<int32_t>(off[e] - tot[e]);
     for (int q = 0; q < g; ++q) run += part[q * E + e];
-    for (int b = b0; b < b1; ++b) {
-      blk_base[static_cast<int64_t>(b) * E + e] = run;
-      run += blk_cnt[static_cast<int64_t>(b) * E + e];
+    for (int b = b0; b < b1; b += U) {
+      int32_t c[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) c[u] = b + u < b1 ? blk_cnt[static_cast<int64_t>(b + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (b + u < b1) blk_base[static_cast<int64_t>(b + u) * E + e] = run;
+        run += c[u];
+      }
     }
   }
   // expert offsets and the slot table
   const int64_t budget = max_slots - E;
   bool bad_counts = false, bad_reps = false;
-  for (int x = tid; x < E; x += kThreads) {
+  for (int x = tid; x < E; x += kScanThreads) {
     const int64_t excl = off[x] - tot[x];
     expert_off[x] = static_cast<int32_t>(excl);
     const int64_t want = max(want_s[x], 0);
@@ -201,7 +215,7 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const int32_t* __restric
   if (tid == 0) expert_off[E] = M;
   const int64_t all = E > 0 ? rep[E - 1] : 0;
   const int64_t used = E + min<int64_t>(all, budget);
-  for (int64_t q = used + tid; q <= max_slots; q += kThreads) {
+  for (int64_t q = used + tid; q <= max_slots; q += kScanThreads) {
     slot_off[q] = M;
     if (q < max_slots) slot_expert[q] = 0;
   }
@@ -322,7 +336,7 @@ extern "C" int moe_dispatch(const void* x, moe_dtype dt, int64_t T, int H, const
   const int64_t P = T * k;
   const int nblk = static_cast<int>(ceil_div(P, kPairs));
   if (nblk > 0) rank_kernel<<<nblk, kThreads, 0, s>>>(topk_idx, P, k, E, blk_cnt, rank, check);
-  scan_kernel<<<1, kThreads, 0, s>>>(blk_cnt, nblk, E, P, counts, replicas, replica_budget, max_slots, blk_base,
+  scan_kernel<<<1, kScanThreads, 0, s>>>(blk_cnt, nblk, E, P, counts, replicas, replica_budget, max_slots, blk_base,
                                      expert_off, slot_off, slot_expert, n_slots, check);
   if (T > 0) {
     const int chunks = static_cast<int>(static_cast<int64_t>(H) * elem_bytes(dt) / 16);
