@@ -79,12 +79,13 @@ __global__ __launch_bounds__(kThreads) void rank_kernel(const int32_t* __restric
       }
     }
     __syncthreads();
-    // rank inside the wave: one ballot per distinct expert of the wave
+    // rank inside the wave: one ballot per distinct expert of the wave (the
+    // leader's expert read with v_readlane: the leader is wave-uniform)
     int local = 0;
     uint64_t todo = __ballot(e >= 0);
     while (todo) {
       const int leader = __ffsll(static_cast<unsigned long long>(todo)) - 1;
-      const int v = __shfl(e, leader);
+      const int v = __builtin_amdgcn_readlane(e, leader);
       const uint64_t m = __ballot(e == v);
       if (e == v) local = __popcll(m & lt);
       if (lane == leader) wave_cnt[w][v] = __popcll(m);
