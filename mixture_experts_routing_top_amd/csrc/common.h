@@ -36,6 +36,22 @@ __device__ __forceinline__ void raise_check(int32_t* check, bool flagged, int32_
     atomicOr(check, bits);
 }
 
+// The value of the lane OFF away in an all-reduce pairing inside a 16-lane
+// row, by a DPP move (a VALU operand modifier, no LDS round trip):
+// quad_perm(1,0,3,2) for OFF = 1, quad_perm(2,3,0,1) for 2, row_half_mirror
+// (i <-> 7 - i in eight lanes) for 4, row_mirror (i <-> 15 - i in sixteen)
+// for 8.  Combining with an associative, commutative operation after steps 1,
+// 2, ... up to G / 2 leaves every lane of an aligned group of G lanes with the
+// group's result.
+template <int OFF>
+__device__ __forceinline__ int dpp_partner(int x) {
+  static_assert(OFF == 1 || OFF == 2 || OFF == 4 || OFF == 8, "pairings inside one DPP row");
+  if constexpr (OFF == 1) return __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);
+  else if constexpr (OFF == 2) return __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);
+  else if constexpr (OFF == 4) return __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, false);
+  else return __builtin_amdgcn_mov_dpp(x, 0x140, 0xF, 0xF, false);
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
 // fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.

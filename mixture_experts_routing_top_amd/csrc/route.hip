@@ -27,20 +27,9 @@ __device__ __forceinline__ bool better(float v1, int i1, float v2, int i2) {
   return v1 > v2 || (v1 == v2 && i1 < i2);
 }
 
-// One step of the group arg-max with a DPP move (a VALU operand modifier, no
-// LDS round trip): each lane meets the lane OFF away in the pairing
-// quad_perm(1,0,3,2) for OFF = 1, quad_perm(2,3,0,1) for 2, row_half_mirror
-// (i <-> 7 - i in eight lanes) for 4, row_mirror (i <-> 15 - i in sixteen) for
-// 8.  After steps 1, 2, ... up to G / 2 every lane of an aligned group of G
-// lanes holds the group's best (value, index).
-template <int OFF>
-__device__ __forceinline__ int dpp_partner(int x) {
-  if constexpr (OFF == 1) return __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);
-  else if constexpr (OFF == 2) return __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);
-  else if constexpr (OFF == 4) return __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, false);
-  else return __builtin_amdgcn_mov_dpp(x, 0x140, 0xF, 0xF, false);
-}
-
+// One step of the group arg-max (dpp_partner): after steps 1, 2, ... up to
+// G / 2 every lane of an aligned group of G lanes holds the group's best
+// (value, index).
 template <int OFF>
 __device__ __forceinline__ void argmax_step(float& bv, int& bi) {
   const float ov = __int_as_float(dpp_partner<OFF>(__float_as_int(bv)));
