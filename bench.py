@@ -11,6 +11,9 @@ of the whole hot path through the C ABI on one stream:
   previous layer's routing, conditional matrix, next-layer prediction,
   replica plan) -> moe_dispatch -> moe_expert_ffn -> moe_combine
 
+The dispatch writes the row map (perm_src, inv_pos) and the slot table; the
+FFN's gate/up GEMM gathers its rows from x through perm_src (no x_perm copy).
+
 The timed layer is the middle layer of a three-layer statistics chain, so its
 stats call exercises every statistic; the previous layer's routing is computed
 once before timing.  Prints one JSON line: routed tokens/s (T / step time),
@@ -97,15 +100,24 @@ def measured_traffic(flop_unit_rows: int):
     return rec.get("bytes_per_launch")
 
 
+def memory_phase_bytes(T, H, E, k, s=2, copy_rows=False):
+    """Algorithmic bytes of the memory-bound phases: route (logits in, idx + w
+    out), dispatch (idx in, perm_src + inv_pos out; with copy_rows also x in and
+    x_perm out, the rows the gathering FFN otherwise reads from x itself) and
+    combine (y_perm in, out, inv_pos + w)."""
+    M = T * k
+    return (T * E * 4 + T * k * 8
+            + T * k * 4 + M * 8 + ((T * H * s + M * H * s) if copy_rows else 0)
+            + M * H * s + T * H * s + M * 8)
+
+
 def algorithmic_layer_work(T, H, I, E, k, n_mat):
     """Algorithmic flops and HBM bytes of one layer (intermediates and padding excluded)."""
     M = T * k
     flops = 2.0 * M * H * I * n_mat
     s = 2
     w_bytes = E * n_mat * H * I * s
-    mem = (T * E * 4 + T * k * 8            # route: logits in, idx + w out
-           + T * H * s + M * H * s + M * 8  # dispatch: x in, x_perm out, perm_src/inv_pos
-           + M * H * s + T * H * s + M * 8)  # combine: y_perm in, out, inv_pos + w
+    mem = memory_phase_bytes(T, H, E, k, s)
     return flops, w_bytes, mem
 
 
@@ -168,11 +180,11 @@ def spin_cycles(torch, stream, ms):
 
 
 def memory_phase_summary(T, H, E, k, warm, cold):
-    """Routing, dispatch and combine against HBM: their algorithmic bytes (route 4E in
-    + 8k out per token; dispatch and combine (k+1)*H*2 each) over their event-timed
-    GPU phase times (which also hold dispatch's two index kernels and the GPU's
-    gaps between launches)."""
-    b = T * (4 * E + 8 * k) + 2 * T * (k + 1) * H * 2
+    """Routing, dispatch and combine against HBM: their algorithmic bytes
+    (memory_phase_bytes: the layer's dispatch copies no rows, the FFN gathers
+    them from x) over their event-timed GPU phase times (which also hold the
+    GPU's gaps between launches)."""
+    b = memory_phase_bytes(T, H, E, k)
     out = {"bytes": b}
     for label, ph in (("warm", warm), ("cold", cold)):
         us = ph["route"] + ph["dispatch"] + ph["combine"]
@@ -555,7 +567,7 @@ def configs_bench(moe, synth, torch, np, steps=10, warmup=3):
         flop = 2.0 * cfg.T * cfg.k * cfg.H * cfg.I * cfg.n_mat
         active = int(np.count_nonzero(counts))
         w_bytes = active * cfg.n_mat * cfg.I * cfg.H * s
-        mem = cfg.T * (4 * cfg.E + 8 * cfg.k) + 2 * cfg.T * (cfg.k + 1) * cfg.H * s
+        mem = memory_phase_bytes(cfg.T, cfg.H, cfg.E, cfg.k, s)
         peak = (PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_FP32_TFLOPS) * 1e12
         t = max(flop / peak, w_bytes / (PEAK_HBM_GBS * 1e9)) + mem / (PEAK_HBM_GBS * 1e9)
         bound = "mfma" if flop / peak >= w_bytes / (PEAK_HBM_GBS * 1e9) else "hbm (weight streaming)"
@@ -702,7 +714,7 @@ def backward_bench(moe, synth, torch, np, steps=5, warmup=2):
     x = dev_bf16(synth.hidden0(cfg, 0))
     logits = torch.from_numpy(synth.logits(cfg, 0, 0)).to(dev)
     d_out = torch.randn(T, H, device=dev).to(torch.bfloat16)
-    fw = moe.moe_layer_forward(x, logits, k, wg, wu, wd, "swiglu", 0)
+    fw = moe.moe_layer_forward(x, logits, k, wg, wu, wd, "swiglu", 0, copy_rows=True)
     ws = torch.empty(moe.moe_backward_workspace_bytes(torch.bfloat16, T, k, H, I, E), dtype=torch.uint8, device=dev)
     out = {}
     stream = torch.cuda.current_stream()
@@ -944,10 +956,11 @@ def main():
         moe.moe_stats(state, L, E, win, 1, 10 ** 6 + rep, idx, prev_idx, k, bufs["counts"], bufs["p_seq"],
                       bufs["cond"], bufs["pred_next"], R, bufs["replicas"], stream)
         phase_ev[2].record(stream)
-        d = moe.moe_dispatch(x, idx, E, bufs["replicas"], E + R, bufs["disp"], bufs["ws_d"], stream, bufs["counts"])
+        d = moe.moe_dispatch(x, idx, E, bufs["replicas"], E + R, bufs["disp"], bufs["ws_d"], stream, bufs["counts"],
+                             copy=False)
         phase_ev[3].record(stream)
-        y = moe.moe_expert_ffn(d["x_perm"], d["slot_off"], d["slot_expert"], d["n_slots"], wg, wu, wd, "swiglu",
-                               a.path, bufs["y_perm"], bufs["ws_f"], stream)
+        y = moe.moe_expert_ffn(x, d["slot_off"], d["slot_expert"], d["n_slots"], wg, wu, wd, "swiglu",
+                               a.path, bufs["y_perm"], bufs["ws_f"], stream, row_src=d["perm_src"])
         phase_ev[4].record(stream)
         moe.moe_combine(y, d["inv_pos"], w, bufs["out"], stream)
         phase_ev[5].record(stream)

@@ -224,6 +224,9 @@ int moe_prediction_quality(const float* pred, const int32_t* counts, int E, cons
  *               twice gets two rows, slot order).
  *   inv_pos     int32 [T, k]: the row holding (t, topk_idx[t, i]).
  *   x_perm      [M, H] in dtype `dt`: x_perm[r] = x[perm_src[r]] (byte copy).
+ *               May be NULL (then x may be NULL too): no row is copied, and
+ *               moe_expert_ffn gathers the rows from x with perm_src as its
+ *               row map; every other output is written the same way.
  *   slot table  replicas[e] extra copies cut expert e's rows into
  *               replicas[e]+1 contiguous chunks in token order, chunk rho
  *               covering [floor(rho*n_e/(r_e+1)), floor((rho+1)*n_e/(r_e+1)))
@@ -317,6 +320,14 @@ int moe_dispatch_noalloc(const void* x, moe_dtype dt, int64_t T, int H, const in
  *         round of the 256 CUs mostly idle, its trailing row tiles are listed
  *         again as 64-row tiles when the same cost model says so (decided on
  *         the device, no host sync).
+ *   row_src    NULL: x_perm holds the M rows [M, H].  Otherwise int32 [M]:
+ *              x_perm is an [n_src, H] matrix (the tokens x) and row r of the
+ *              FFN's input is x_perm[row_src[r]] (moe_dispatch's perm_src):
+ *              the gate/up GEMM gathers its operand rows with per-lane
+ *              offsets of its direct-to-LDS loads, so a dispatch without the
+ *              row copy (x_perm NULL there) feeds the FFN directly.  Entries
+ *              outside [0, n_src) read as zero rows.  n_src * H * sizeof(dt)
+ *              must stay below 0x7e000000 bytes (MOE_ERR_UNSUPPORTED).
  *   workspace  at least moe_expert_ffn_workspace_bytes(...) bytes.
  * Limits: dtype F32 or BF16; H and I multiples of 64; E <= max_slots;
  * M <= 2^31 - 1; rows referenced by slot_off lie in [0, M) (rows outside it
@@ -324,8 +335,8 @@ int moe_dispatch_noalloc(const void* x, moe_dtype dt, int64_t T, int H, const in
  * check: MOE_CHECK_SLOTS.
  */
 size_t moe_expert_ffn_workspace_bytes(moe_dtype dt, int64_t M, int H, int I, int max_slots); /* [host] */
-int moe_expert_ffn(const void* x_perm, moe_dtype dt, int64_t M, int H, int I, int E,
-                   const int32_t* slot_off, const int32_t* slot_expert, const int32_t* n_slots, int max_slots,
+int moe_expert_ffn(const void* x_perm, const int32_t* row_src, int64_t n_src, moe_dtype dt, int64_t M, int H, int I,
+                   int E, const int32_t* slot_off, const int32_t* slot_expert, const int32_t* n_slots, int max_slots,
                    const void* w_gate, const void* w_up, const void* w_down, moe_act act, moe_gemm_path path,
                    void* y_perm, void* workspace, size_t workspace_bytes, int32_t* check, void* stream);
 
@@ -337,11 +348,11 @@ int moe_expert_ffn(const void* x_perm, moe_dtype dt, int64_t M, int H, int I, in
  * own stream.  events must hold three valid events.  Same results as
  * moe_expert_ffn.
  */
-int moe_expert_ffn_profiled(const void* x_perm, moe_dtype dt, int64_t M, int H, int I, int E,
-                            const int32_t* slot_off, const int32_t* slot_expert, const int32_t* n_slots,
-                            int max_slots, const void* w_gate, const void* w_up, const void* w_down, moe_act act,
-                            moe_gemm_path path, void* y_perm, void* workspace, size_t workspace_bytes,
-                            int32_t* check, void* const* events, void* stream);
+int moe_expert_ffn_profiled(const void* x_perm, const int32_t* row_src, int64_t n_src, moe_dtype dt, int64_t M,
+                            int H, int I, int E, const int32_t* slot_off, const int32_t* slot_expert,
+                            const int32_t* n_slots, int max_slots, const void* w_gate, const void* w_up,
+                            const void* w_down, moe_act act, moe_gemm_path path, void* y_perm, void* workspace,
+                            size_t workspace_bytes, int32_t* check, void* const* events, void* stream);
 
 /* ---------------------------------------------------------------- combine
  * moe_combine -- weighted combine back to token order ([EPS] section 3: the

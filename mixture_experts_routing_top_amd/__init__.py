@@ -211,22 +211,26 @@ def moe_dispatch_workspace_bytes(T: int, k: int, E: int) -> int:
     return int(lib().moe_dispatch_workspace_bytes(ctypes.c_int64(T), k, E))
 
 
-def _dispatch_outputs(out, T, k, H, E, max_slots, dtype, dev):
+def _dispatch_outputs(out, T, k, H, E, max_slots, dtype, dev, copy=True):
     o = dict(out or {})
     M = T * k
     for key, shape, dt in (("x_perm", (M, H), dtype), ("perm_src", (M,), torch.int32), ("inv_pos", (T, k), torch.int32),
                            ("expert_off", (E + 1,), torch.int32), ("slot_off", (max_slots + 1,), torch.int32),
                            ("slot_expert", (max_slots,), torch.int32), ("n_slots", (1,), torch.int32)):
+        if key == "x_perm" and not copy:
+            o[key] = None
+            continue
         o[key] = _out(o.get(key), shape, dt, dev, key)
     return o
 
 
 def moe_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, E: int, replicas=None, max_slots=None, out=None,
-                 workspace=None, stream=None, counts=None, check=None, replica_budget=0):
+                 workspace=None, stream=None, counts=None, check=None, replica_budget=0, copy=True):
     """counts (int32 [E], e.g. moe_stats' counts of this routing) is only compared
     with the routing when `check` is given.  replica_budget > 0 with replicas None:
     the dispatch plans the replicas from this routing's counts (max_slots defaults
-    to E + replica_budget)."""
+    to E + replica_budget).  copy=False: no x_perm (None in the result); the FFN
+    then gathers its rows from x with perm_src (moe_expert_ffn's row_src)."""
     T, H = x.shape
     if topk_idx.shape[0] != T or topk_idx.dtype != torch.int32:
         raise ValueError("topk_idx must be int32 [T, k] for the T rows of x")
@@ -236,7 +240,7 @@ def moe_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, E: int, replicas=None,
     for t, name in ((replicas, "replicas"), (counts, "counts")):
         if t is not None and (t.numel() != E or t.dtype != torch.int32):
             raise ValueError(f"{name} must be int32 [E]")
-    o = _dispatch_outputs(out, T, k, H, E, max_slots, x.dtype, dev)
+    o = _dispatch_outputs(out, T, k, H, E, max_slots, x.dtype, dev, copy)
     need = moe_dispatch_workspace_bytes(T, k, E)
     workspace = torch.empty(need, dtype=torch.uint8, device=dev) if workspace is None else \
         _bytes_of(workspace, need, "dispatch workspace")
@@ -277,8 +281,15 @@ def moe_expert_ffn_workspace_bytes(dtype, M: int, H: int, I: int, max_slots: int
     return int(lib().moe_expert_ffn_workspace_bytes(code, ctypes.c_int64(M), H, I, max_slots))
 
 
-def _ffn_args(x_perm, slot_off, slot_expert, n_slots, w_gate, w_up, w_down, y_perm, workspace):
-    M, H = x_perm.shape
+def _ffn_args(x_perm, slot_off, slot_expert, n_slots, w_gate, w_up, w_down, y_perm, workspace, row_src=None):
+    """row_src (int32 [M], e.g. moe_dispatch's perm_src): x_perm is then the token
+    matrix x [T, H] and the FFN gathers row r from x_perm[row_src[r]]."""
+    if row_src is not None:
+        if row_src.dtype != torch.int32 or row_src.dim() != 1:
+            raise ValueError("row_src must be int32 [M]")
+        M, H = row_src.numel(), x_perm.shape[1]
+    else:
+        M, H = x_perm.shape
     E, I, H_ = w_gate.shape
     if H_ != H or tuple(w_down.shape) != (E, H, I) or (w_up is not None and tuple(w_up.shape) != (E, I, H)):
         raise ValueError("expert weights must be [E, I, H] (gate, up) and [E, H, I] (down) for x_perm's H")
@@ -296,10 +307,12 @@ def _ffn_args(x_perm, slot_off, slot_expert, n_slots, w_gate, w_up, w_down, y_pe
 
 
 def moe_expert_ffn(x_perm: torch.Tensor, slot_off, slot_expert, n_slots, w_gate, w_up, w_down, act="swiglu",
-                   path="grouped", y_perm=None, workspace=None, stream=None, check=None):
+                   path="grouped", y_perm=None, workspace=None, stream=None, check=None, row_src=None):
+    """row_src: see _ffn_args (gathering the rows from x instead of x_perm)."""
     M, H, I, E, max_slots, y_perm, workspace = _ffn_args(x_perm, slot_off, slot_expert, n_slots, w_gate, w_up,
-                                                         w_down, y_perm, workspace)
-    _call("moe_expert_ffn", _ptr(x_perm), _dtype_code(x_perm), ctypes.c_int64(M), H, I, E, _ptr(slot_off),
+                                                         w_down, y_perm, workspace, row_src)
+    _call("moe_expert_ffn", _ptr(x_perm), _ptr(row_src), ctypes.c_int64(x_perm.shape[0]), _dtype_code(x_perm),
+          ctypes.c_int64(M), H, I, E, _ptr(slot_off),
           _ptr(slot_expert), _ptr(n_slots), max_slots, _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ACT[act],
           _PATH[path], _ptr(y_perm), _ptr(workspace), ctypes.c_size_t(workspace.numel() * workspace.element_size()),
           _ptr(check), _stream(stream))
@@ -307,16 +320,18 @@ def moe_expert_ffn(x_perm: torch.Tensor, slot_off, slot_expert, n_slots, w_gate,
 
 
 def moe_expert_ffn_profiled(x_perm: torch.Tensor, slot_off, slot_expert, n_slots, w_gate, w_up, w_down, events,
-                            act="swiglu", path="grouped", y_perm=None, workspace=None, stream=None, check=None):
+                            act="swiglu", path="grouped", y_perm=None, workspace=None, stream=None, check=None,
+                            row_src=None):
     """moe_expert_ffn recording three torch.cuda.Event objects on the stream: before
     the gate/up GEMM, after it, after the down GEMM."""
     M, H, I, E, max_slots, y_perm, workspace = _ffn_args(x_perm, slot_off, slot_expert, n_slots, w_gate, w_up,
-                                                         w_down, y_perm, workspace)
+                                                         w_down, y_perm, workspace, row_src)
     for e in events:          # torch creates an event's handle on its first record
         if not e.cuda_event:
             e.record(stream if stream is not None else torch.cuda.current_stream())
     evs = (ctypes.c_void_p * 3)(*(e.cuda_event for e in events))
-    _call("moe_expert_ffn_profiled", _ptr(x_perm), _dtype_code(x_perm), ctypes.c_int64(M), H, I, E, _ptr(slot_off),
+    _call("moe_expert_ffn_profiled", _ptr(x_perm), _ptr(row_src), ctypes.c_int64(x_perm.shape[0]),
+          _dtype_code(x_perm), ctypes.c_int64(M), H, I, E, _ptr(slot_off),
           _ptr(slot_expert), _ptr(n_slots), max_slots, _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ACT[act],
           _PATH[path], _ptr(y_perm), _ptr(workspace), ctypes.c_size_t(workspace.numel() * workspace.element_size()),
           _ptr(check), evs, _stream(stream))
@@ -374,8 +389,13 @@ def moe_backward(x_perm, y_perm, topk_idx, topk_w, inv_pos, expert_off, w_gate, 
 # ------------------------------------------------------ one layer, composed
 def moe_layer_forward(x, logits, k, w_gate, w_up, w_down, act="swiglu", replica_budget=0, stats_state=None,
                       stats_dims=None, layer=0, it=0, prev_topk_idx=None, path="grouped", bufs=None, stream=None,
-                      planned_replicas=None, check=None, ffn_events=None):
+                      planned_replicas=None, check=None, ffn_events=None, copy_rows=False):
     """route -> stats -> dispatch -> FFN -> combine, all on `stream`.
+
+    The dispatch writes the row map and the slot table but copies no rows: the
+    FFN's gate/up GEMM gathers its rows from x through perm_src.  copy_rows=True
+    runs the copying dispatch and hands the FFN x_perm (the result then holds
+    x_perm, e.g. for moe_backward); both give bit-identical outputs.
 
     stats_state/stats_dims=(L, E, window) enable the windowed statistics
     (counts, p_seq, the conditional matrix, the prediction) and the replica
@@ -395,7 +415,7 @@ def moe_layer_forward(x, logits, k, w_gate, w_up, w_down, act="swiglu", replica_
     dev = x.device
     max_slots = E + replica_budget
     b = bufs if bufs is not None else {}
-    key = (T, k, E, H, I, max_slots, x.dtype, str(dev))
+    key = (T, k, E, H, I, max_slots, x.dtype, str(dev), copy_rows)
     if b.get("_key") != key:
         b.clear()
         b["_key"] = key
@@ -424,19 +444,20 @@ def moe_layer_forward(x, logits, k, w_gate, w_up, w_down, act="swiglu", replica_
     if "ws_d" not in b:
         b["ws_d"] = torch.empty(moe_dispatch_workspace_bytes(T, k, E), dtype=torch.uint8, device=dev)
     d = moe_dispatch(x, idx, E, replicas, max_slots, b.get("disp"), b["ws_d"], stream, counts, check,
-                     replica_budget=replica_budget if replicas is None else 0)
+                     replica_budget=replica_budget if replicas is None else 0, copy=copy_rows)
     b["disp"] = d
     if "y_perm" not in b:
-        b["y_perm"] = torch.empty_like(d["x_perm"])
+        b["y_perm"] = torch.empty((T * k, H), dtype=x.dtype, device=dev)
+    ffn_in, row_src = (d["x_perm"], None) if copy_rows else (x, d["perm_src"])
     if "ws_f" not in b:
         b["ws_f"] = torch.empty(moe_expert_ffn_workspace_bytes(x.dtype, T * k, H, I, max_slots), dtype=torch.uint8,
                                 device=dev)
     if ffn_events is None:
-        y = moe_expert_ffn(d["x_perm"], d["slot_off"], d["slot_expert"], d["n_slots"], w_gate, w_up, w_down, act,
-                           path, b["y_perm"], b["ws_f"], stream, check)
+        y = moe_expert_ffn(ffn_in, d["slot_off"], d["slot_expert"], d["n_slots"], w_gate, w_up, w_down, act,
+                           path, b["y_perm"], b["ws_f"], stream, check, row_src=row_src)
     else:
-        y = moe_expert_ffn_profiled(d["x_perm"], d["slot_off"], d["slot_expert"], d["n_slots"], w_gate, w_up, w_down,
-                                    ffn_events, act, path, b["y_perm"], b["ws_f"], stream, check)
+        y = moe_expert_ffn_profiled(ffn_in, d["slot_off"], d["slot_expert"], d["n_slots"], w_gate, w_up, w_down,
+                                    ffn_events, act, path, b["y_perm"], b["ws_f"], stream, check, row_src=row_src)
     out = moe_combine(y, d["inv_pos"], w, b.get("out"), stream, check)
     b["out"] = out
     res.update(d)

@@ -20,8 +20,10 @@ SIGNATURES = {
     "moe_dispatch": (_i, [_p, _i, _i64, _i, _p, _i, _i, _p, _p, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p, _p]),
     "moe_dispatch_noalloc": (_i, [_p, _i, _i64, _i, _p, _i, _i, _p, _p, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p]),
     "moe_expert_ffn_workspace_bytes": (_sz, [_i, _i64, _i, _i, _i]),
-    "moe_expert_ffn": (_i, [_p, _i, _i64, _i, _i, _i, _p, _p, _p, _i, _p, _p, _p, _i, _i, _p, _p, _sz, _p, _p]),
-    "moe_expert_ffn_profiled": (_i, [_p, _i, _i64, _i, _i, _i, _p, _p, _p, _i, _p, _p, _p, _i, _i, _p, _p, _sz, _p,
+    "moe_expert_ffn": (_i, [_p, _p, _i64, _i, _i64, _i, _i, _i, _p, _p, _p, _i, _p, _p, _p, _i, _i, _p, _p, _sz, _p,
+                            _p]),
+    "moe_expert_ffn_profiled": (_i, [_p, _p, _i64, _i, _i64, _i, _i, _i, _p, _p, _p, _i, _p, _p, _p, _i, _i, _p, _p,
+                                     _sz, _p,
                                      _p, _p]),
     "moe_combine": (_i, [_p, _i, _i64, _p, _p, _i64, _i, _i, _p, _p, _p]),
     "moe_backward_workspace_bytes": (_sz, [_i, _i64, _i, _i, _i, _i, _i]),

@@ -24,7 +24,9 @@
 //               write inv_pos and perm_src and copy x[t] into each of its
 //               rows: four 16-byte chunks per thread, read once, written k
 //               times with nontemporal stores (measured ~25% faster than cached
-//               stores on this write-heavy copy).
+//               stores on this write-heavy copy).  Without x_perm only the
+//               indices are written (the expert FFN can gather its rows from
+//               x through perm_src instead).
 #include <mutex>
 
 #include "common.h"
@@ -269,6 +271,20 @@ __global__ __launch_bounds__(256) void permute_kernel(const uint4* __restrict__ 
   }
 }
 
+// Without a row copy (x_perm NULL): one thread per (token, slot) pair writes
+// its inv_pos and its row's perm_src.
+__global__ __launch_bounds__(256) void index_kernel(int64_t P, int k, int E, const int32_t* __restrict__ idx,
+                                                    const int32_t* __restrict__ blk_base,
+                                                    const int32_t* __restrict__ rank, int32_t* __restrict__ perm_src,
+                                                    int32_t* __restrict__ inv_pos) {
+  const int64_t f = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (f >= P) return;
+  const int e = idx[f];
+  const int32_t r = (e >= 0 && e < E) ? blk_base[(f / kPairs) * E + e] + rank[f] : -1;
+  inv_pos[f] = r;
+  if (r >= 0) perm_src[r] = static_cast<int32_t>(f / k);
+}
+
 // Device scratch of moe_dispatch_noalloc: the workspace of one call, in a
 // file-scope array each GPU holds for the life of the process (8 MiB: up to
 // 2^20 (token, slot) pairs at E = 256).  Host code uses it only through the
@@ -322,9 +338,9 @@ extern "C" int moe_dispatch(const void* x, moe_dtype dt, int64_t T, int H, const
                 "when replicas is given", replica_budget);
   if (!expert_off || !slot_off || !slot_expert || !n_slots || !workspace)
     return fail(MOE_ERR_INVALID_ARG, "moe_dispatch: null pointer");
-  if (T > 0 && (!x || !topk_idx || !x_perm || !perm_src || !inv_pos))
+  if (T > 0 && (!topk_idx || !perm_src || !inv_pos || (x_perm && !x)))
     return fail(MOE_ERR_INVALID_ARG, "moe_dispatch: null pointer");
-  if (T > 0 && (!aligned16(x) || !aligned16(x_perm)))
+  if (T > 0 && x_perm && (!aligned16(x) || !aligned16(x_perm)))
     return fail(MOE_ERR_INVALID_ARG, "moe_dispatch: x and x_perm must be 16-byte aligned");
   const Ws w = ws_layout(T, k, E);
   if (workspace_bytes < w.bytes)
@@ -339,12 +355,15 @@ extern "C" int moe_dispatch(const void* x, moe_dtype dt, int64_t T, int H, const
   if (nblk > 0) rank_kernel<<<nblk, kThreads, 0, s>>>(topk_idx, P, k, E, blk_cnt, rank, check);
   scan_kernel<<<1, kScanThreads, 0, s>>>(blk_cnt, nblk, E, P, counts, replicas, replica_budget, max_slots, blk_base,
                                      expert_off, slot_off, slot_expert, n_slots, check);
-  if (T > 0) {
+  if (T > 0 && x_perm) {
     const int chunks = static_cast<int>(static_cast<int64_t>(H) * elem_bytes(dt) / 16);
     const int64_t threads = T * ceil_div(chunks, kChunksPerThread);
     permute_kernel<<<static_cast<unsigned>(ceil_div(threads, 256)), 256, 0, s>>>(
         static_cast<const uint4*>(x), T, chunks, k, E, topk_idx, blk_base, rank, perm_src, inv_pos,
         static_cast<uint4*>(x_perm));
+  } else if (T > 0) {
+    index_kernel<<<static_cast<unsigned>(ceil_div(P, 256)), 256, 0, s>>>(P, k, E, topk_idx, blk_base, rank,
+                                                                          perm_src, inv_pos);
   }
   return hip_status(hipGetLastError(), "moe_dispatch launch");
 }

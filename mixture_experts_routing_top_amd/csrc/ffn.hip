@@ -135,10 +135,10 @@ Kind pick_kind(int64_t g256, int64_t g256_rem, int64_t d64, int64_t g64, int col
   return kG256;
 }
 
-int ffn_impl(const void* x_perm, moe_dtype dt, int64_t M, int H, int I, int E, const int32_t* slot_off,
-             const int32_t* slot_expert, const int32_t* n_slots, int max_slots, const void* w_gate, const void* w_up,
-             const void* w_down, moe_act act, moe_gemm_path path, void* y_perm, void* workspace,
-             size_t workspace_bytes, int32_t* check, hipEvent_t const* ev, void* stream);
+int ffn_impl(const void* x_perm, const int32_t* row_src, int64_t n_src, moe_dtype dt, int64_t M, int H, int I, int E,
+             const int32_t* slot_off, const int32_t* slot_expert, const int32_t* n_slots, int max_slots,
+             const void* w_gate, const void* w_up, const void* w_down, moe_act act, moe_gemm_path path, void* y_perm,
+             void* workspace, size_t workspace_bytes, int32_t* check, hipEvent_t const* ev, void* stream);
 
 }  // namespace
 
@@ -148,34 +148,35 @@ extern "C" size_t moe_expert_ffn_workspace_bytes(moe_dtype dt, int64_t M, int H,
   return ws_layout(dt, M, I, max_slots).bytes;
 }
 
-extern "C" int moe_expert_ffn(const void* x_perm, moe_dtype dt, int64_t M, int H, int I, int E,
-                              const int32_t* slot_off, const int32_t* slot_expert, const int32_t* n_slots,
-                              int max_slots, const void* w_gate, const void* w_up, const void* w_down, moe_act act,
-                              moe_gemm_path path, void* y_perm, void* workspace, size_t workspace_bytes,
-                              int32_t* check, void* stream) {
-  return ffn_impl(x_perm, dt, M, H, I, E, slot_off, slot_expert, n_slots, max_slots, w_gate, w_up, w_down, act, path,
-                  y_perm, workspace, workspace_bytes, check, nullptr, stream);
+extern "C" int moe_expert_ffn(const void* x_perm, const int32_t* row_src, int64_t n_src, moe_dtype dt, int64_t M,
+                              int H, int I, int E, const int32_t* slot_off, const int32_t* slot_expert,
+                              const int32_t* n_slots, int max_slots, const void* w_gate, const void* w_up,
+                              const void* w_down, moe_act act, moe_gemm_path path, void* y_perm, void* workspace,
+                              size_t workspace_bytes, int32_t* check, void* stream) {
+  return ffn_impl(x_perm, row_src, n_src, dt, M, H, I, E, slot_off, slot_expert, n_slots, max_slots, w_gate, w_up,
+                  w_down, act, path, y_perm, workspace, workspace_bytes, check, nullptr, stream);
 }
 
-extern "C" int moe_expert_ffn_profiled(const void* x_perm, moe_dtype dt, int64_t M, int H, int I, int E,
-                                       const int32_t* slot_off, const int32_t* slot_expert, const int32_t* n_slots,
-                                       int max_slots, const void* w_gate, const void* w_up, const void* w_down,
-                                       moe_act act, moe_gemm_path path, void* y_perm, void* workspace,
-                                       size_t workspace_bytes, int32_t* check, void* const* events, void* stream) {
+extern "C" int moe_expert_ffn_profiled(const void* x_perm, const int32_t* row_src, int64_t n_src, moe_dtype dt,
+                                       int64_t M, int H, int I, int E, const int32_t* slot_off,
+                                       const int32_t* slot_expert, const int32_t* n_slots, int max_slots,
+                                       const void* w_gate, const void* w_up, const void* w_down, moe_act act,
+                                       moe_gemm_path path, void* y_perm, void* workspace, size_t workspace_bytes,
+                                       int32_t* check, void* const* events, void* stream) {
   if (!events || !events[0] || !events[1] || !events[2])
     return moe::fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn_profiled: needs three events");
   const hipEvent_t ev[3] = {static_cast<hipEvent_t>(events[0]), static_cast<hipEvent_t>(events[1]),
                             static_cast<hipEvent_t>(events[2])};
-  return ffn_impl(x_perm, dt, M, H, I, E, slot_off, slot_expert, n_slots, max_slots, w_gate, w_up, w_down, act, path,
-                  y_perm, workspace, workspace_bytes, check, ev, stream);
+  return ffn_impl(x_perm, row_src, n_src, dt, M, H, I, E, slot_off, slot_expert, n_slots, max_slots, w_gate, w_up,
+                  w_down, act, path, y_perm, workspace, workspace_bytes, check, ev, stream);
 }
 
 namespace {
 
-int ffn_impl(const void* x_perm, moe_dtype dt, int64_t M, int H, int I, int E, const int32_t* slot_off,
-             const int32_t* slot_expert, const int32_t* n_slots, int max_slots, const void* w_gate, const void* w_up,
-             const void* w_down, moe_act act, moe_gemm_path path, void* y_perm, void* workspace,
-             size_t workspace_bytes, int32_t* check, hipEvent_t const* ev, void* stream) {
+int ffn_impl(const void* x_perm, const int32_t* row_src, int64_t n_src, moe_dtype dt, int64_t M, int H, int I, int E,
+             const int32_t* slot_off, const int32_t* slot_expert, const int32_t* n_slots, int max_slots,
+             const void* w_gate, const void* w_up, const void* w_down, moe_act act, moe_gemm_path path, void* y_perm,
+             void* workspace, size_t workspace_bytes, int32_t* check, hipEvent_t const* ev, void* stream) {
   using namespace moe;
   if (dt != MOE_F32 && dt != MOE_BF16) return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn: unknown dtype %d", (int)dt);
   if (act != MOE_SWIGLU && act != MOE_GELU) return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn: unknown activation");
@@ -192,6 +193,10 @@ int ffn_impl(const void* x_perm, moe_dtype dt, int64_t M, int H, int I, int E, c
   if (!slot_off || !slot_expert || !n_slots || !w_gate || !w_down || !workspace)
     return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn: null pointer");
   if (M > 0 && (!x_perm || !y_perm)) return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn: null pointer");
+  if (row_src && (n_src < 0 || n_src * H * elem_bytes(dt) >= kGatherLimit))
+    return fail(n_src < 0 ? MOE_ERR_INVALID_ARG : MOE_ERR_UNSUPPORTED,
+                "moe_expert_ffn: a gathered input of n_src=%lld rows must stay below %lld bytes", (long long)n_src,
+                (long long)kGatherLimit);
   for (const void* p : {x_perm, w_gate, w_up, w_down, static_cast<const void*>(y_perm), static_cast<const void*>(workspace)})
     if (p && !aligned16(p)) return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn: operands must be 16-byte aligned");
   const WsLayout w = ws_layout(dt, M, I, max_slots);
@@ -325,6 +330,8 @@ int ffn_impl(const void* x_perm, moe_dtype dt, int64_t M, int H, int I, int E, c
 
   GemmArgs p1{};
   p1.A = x_perm;
+  p1.a_rows = row_src;  // the gate/up GEMM gathers its rows when given a row map
+  p1.a_n = n_src;
   p1.B0 = w_gate;
   p1.B1 = w_up;
   p1.C = ws + w.h;
@@ -337,6 +344,7 @@ int ffn_impl(const void* x_perm, moe_dtype dt, int64_t M, int H, int I, int E, c
   p1.n_col_tiles = nt1;
   GemmArgs p2 = p1;
   p2.A = ws + w.h;
+  p2.a_rows = nullptr;
   p2.B0 = w_down;
   p2.B1 = nullptr;
   p2.C = y_perm;

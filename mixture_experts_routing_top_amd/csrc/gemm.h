@@ -111,7 +111,15 @@ struct GemmArgs {
   // k_split > 0 the weights' K range is split: k < k_split reads B0 [E,
   // k_split, ldb], k >= k_split reads B1 (its row k - k_split).
   int lda, ldb, k_split;
+  // Gathered A rows (not in weight-gradient or K-major mode): with a_rows set,
+  // row r of the M rows is row a_rows[r] of A = [a_n, K]; rows mapped outside
+  // [0, a_n) read as zero.  The caller keeps a_n * K * sizeof(T) below
+  // kGatherLimit so every offset stays in 31 bits.
+  const int32_t* a_rows;
+  int64_t a_n;
 };
+constexpr int64_t kGatherLimit = int64_t(0x7e000000);  // bytes of a gathered A
+constexpr int kGatherOut = 0x7f000000;                 // an A offset out of range: reads zero
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
   const int n = bytes > 0x7fffffff ? 0x7fffffff : static_cast<int>(bytes);
@@ -326,7 +334,17 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs g, const int b) {
       wofs = (static_cast<int64_t>(e) * N + n0) * K;
   }
 
-  const __amdgpu_buffer_rsrc_t ra = rsrc(A, m_valid * row_b);
+  // gathered A rows: offsets are taken from the row map against A's base
+  const bool gat = !kWgrad && KM == 0 && g.a_rows != nullptr;
+  if (gat) A = static_cast<const T*>(g.A);
+  // byte offset of tile row `row` of a gathered A (out of range past m_valid
+  // or for a row mapped outside A)
+  auto gather_off = [&](int row) -> int {
+    if (row >= m_valid) return kGatherOut;
+    const int src = g.a_rows[r0 + row];
+    return (src >= 0 && src < g.a_n) ? src * static_cast<int>(row_b) : kGatherOut;
+  };
+  const __amdgpu_buffer_rsrc_t ra = gat ? rsrc(A, g.a_n * row_b) : rsrc(A, m_valid * row_b);
   const __amdgpu_buffer_rsrc_t rb0 = rsrc(static_cast<const T*>(g.B0) + wofs, n_valid * row_b);
   const __amdgpu_buffer_rsrc_t rb1 =
       NMAT > 1 ? rsrc(static_cast<const T*>(g.B1) + wofs, n_valid * row_b) : rb0;
@@ -343,16 +361,23 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs g, const int b) {
   // of their K steps is shorter than the load latency); 256-row tiles one
   constexpr int NST = BM == 64 ? 2 : 1;
   uint4 st[NST][P];
-  auto issue_one = [&](int w, int p, int o) {
-    if (p < PA) st[w][p] = bload(ra, o + p * pass_b);
+  // gathered A: pass p's row offset of this thread (its row lrow + 32 p)
+  int aoff[PA];
+#pragma unroll
+  for (int p = 0; p < PA; ++p) aoff[p] = gat ? gather_off(lrow + 32 * p) + lchunk * 16 : 0;
+  auto issue_one = [&](int w, int p, int o, int ao) {
+    if (p < PA) st[w][p] = gat ? bload(ra, aoff[p] + ao) : bload(ra, o + p * pass_b);
     else if (NMAT == 1 || p < PA + 4) st[w][p] = bload(rb0, o + (p - PA) * pass_b);
     else st[w][p] = bload(rb1, o + (p - PA - 4) * pass_b);
   };
-  // steps past the last one load from an offset out of range: zeros, no memory access
+  // steps past the last one load from an offset out of range: zeros, no memory
+  // access (a gathered A reloads step 0's rows instead: no stage past the last
+  // step is consumed)
   auto issue = [&](int w, int kt, int nk) {
     const int o = kt < nk ? goff + kt * 128 : 0x7ffff000;
+    const int ao = kt < nk ? kt * 128 : 0;
 #pragma unroll
-    for (int p = 0; p < P; ++p) issue_one(w, p, o);
+    for (int p = 0; p < P; ++p) issue_one(w, p, o, ao);
   };
   auto stash = [&](int stage) {
     char* base = lds + stage * kStageBytes + loff;
@@ -412,7 +437,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs g, const int b) {
                   "issue pattern: 8 or 4 A blocks and 8 weight blocks per wave, 3/3/2 weight blocks over the "
                   "first three sub-steps and the A blocks in the fourth, one per odd MFMA");
     const int rb_ = static_cast<int>(row_b);
-    const u32x4 da = dma_rsrc(A, static_cast<int64_t>(m_valid) * row_b);
+    const u32x4 da = dma_rsrc(A, (gat ? g.a_n : static_cast<int64_t>(m_valid)) * row_b);
     const u32x4 db0 = dma_rsrc(static_cast<const T*>(g.B0) + wofs, static_cast<int64_t>(n_valid) * row_b);
     const u32x4 db1 = NMAT > 1 ? dma_rsrc(static_cast<const T*>(g.B1) + wofs, static_cast<int64_t>(n_valid) * row_b) : db0;
     const int wv = __builtin_amdgcn_readfirstlane(wave);
@@ -429,7 +454,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs g, const int b) {
         offA[p] = kr * ldaB + (((lane & 31) ^ kswz(kr)) << 4);
       } else {
         const int row = 8 * (4 * p + wv) + (lane >> 3);
-        offA[p] = row * rb_ + (((lane & 7) ^ swz(row)) << 4);
+        offA[p] = (gat ? gather_off(row) : row * rb_) + (((lane & 7) ^ swz(row)) << 4);
       }
     }
 #pragma unroll
@@ -445,6 +470,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs g, const int b) {
     }
     const int nk = KM != 0 ? (K + 63) / 64 : K / 64;
     auto koff = [&](int kt) { return kt < nk ? kt * 128 : 0x7ffff000; };
+    // a gathered A's step offset (past the last step: step 0's rows again,
+    // never consumed)
+    auto koffA = [&](int kt) { return gat ? (kt < nk ? kt * 128 : 0) : koff(kt); };
     // descriptors of step kt for the K-major operands, based at its first K
     // row and ending where the operand's K range ends (an empty range past the
     // last step: its loads read zeros)
@@ -544,7 +572,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs g, const int b) {
     {
       const u32x4 a0 = kdescA(0), b0 = kdescB(0), b1 = kdescB(1), a1 = kdescA(1);
 #pragma unroll
-      for (int p = 0; p < PA_; ++p) dmaA(p, 0, koff(0), a0);
+      for (int p = 0; p < PA_; ++p) dmaA(p, 0, koffA(0), a0);
 #pragma unroll
       for (int p = 0; p < PB_; ++p) dmaB(p, 0, koff(0), b0);
 #pragma unroll
@@ -554,7 +582,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs g, const int b) {
 #pragma unroll
       for (int r = 0; r < NR; ++r) frag(0, 0, 0, 0, r);
 #pragma unroll
-      for (int p = 0; p < PA_; ++p) dmaA(p, 1, koff(1), a1);
+      for (int p = 0; p < PA_; ++p) dmaA(p, 1, koffA(1), a1);
     }
 
     // one K step; the stage indices are compile-time (the loop runs six steps
@@ -562,7 +590,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs g, const int b) {
     auto step = [&](int kt, auto U, auto WC) {
       constexpr int u = decltype(U)::value, wcur = decltype(WC)::value;
       constexpr int w1 = (wcur + 1) % 3, w2 = (wcur + 2) % 3;
-      const int k2 = koff(kt + 2);
+      const int k2 = koff(kt + 2), k2a = koffA(kt + 2);
       const u32x4 dA2 = kdescA(kt + 2), dB2 = kdescB(kt + 2);
 #pragma unroll
       for (int kk = 0; kk < KS - 1; ++kk) {
@@ -587,11 +615,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs g, const int b) {
       for (int m = 0; m < NM; ++m) {
         mfma1((KS - 1) & 1, m);
         if (rd < NR) frag(u ^ 1, w1, 0, KS & 1, rd++);
-        if ((m & 1) && qa < PA_) dmaA(qa++, u, k2, dA2);
+        if ((m & 1) && qa < PA_) dmaA(qa++, u, k2a, dA2);
         __builtin_amdgcn_sched_barrier(0);
       }
       while (rd < NR) frag(u ^ 1, w1, 0, KS & 1, rd++);
-      while (qa < PA_) dmaA(qa++, u, k2, dA2);
+      while (qa < PA_) dmaA(qa++, u, k2a, dA2);
       __builtin_amdgcn_sched_barrier(0);
     };
     using I0 = std::integral_constant<int, 0>;
@@ -627,7 +655,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs g, const int b) {
     constexpr int D[5] = {0, 3, 6, 8, PW};  // blocks issued up to the end of sub-steps 0, 1, 2, 3
     static_assert(!kDTL64 || PW == 10, "issue pattern assumes 10 blocks per wave");
     const int rb_ = static_cast<int>(row_b);
-    const u32x4 da = dma_rsrc(A, static_cast<int64_t>(m_valid) * row_b);
+    const u32x4 da = dma_rsrc(A, (gat ? g.a_n : static_cast<int64_t>(m_valid)) * row_b);
     const u32x4 db0 = dma_rsrc(static_cast<const T*>(g.B0) + wofs, static_cast<int64_t>(n_valid) * row_b);
     const u32x4 db1 = NMAT > 1 ? dma_rsrc(static_cast<const T*>(g.B1) + wofs, static_cast<int64_t>(n_valid) * row_b) : db0;
     const int wv = __builtin_amdgcn_readfirstlane(wave);
@@ -637,19 +665,20 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs g, const int b) {
       const int row = 8 * (4 * p + wv) + (lane >> 3);  // stage row: A rows, then weight rows
       int src = row < BM ? row : row - BM;
       if (NMAT == 2 && row >= BM + 128) src -= 128;
-      doff[p] = src * rb_ + (((lane & 7) ^ swz(row)) << 4);
+      doff[p] = ((gat && row < BM) ? gather_off(row) : src * rb_) + (((lane & 7) ^ swz(row)) << 4);
     }
     const unsigned lds0 = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(reinterpret_cast<uintptr_t>(lds)));
     // block 4p + w of a stage: A for p < BM / 32, then gate (or the only) weight
     // rows, then up rows; which one is fixed by p alone
-    auto dma = [&](int p, int st, int koff) {
-      const unsigned dst = lds0 + st * SB + (4 * p + wv) * 1024;
-      if (4 * p < BM / 8) load_lds(da, doff[p] + koff, dst);
-      else if (NMAT == 1 || 4 * p < BM / 8 + 16) load_lds(db0, doff[p] + koff, dst);
-      else load_lds(db1, doff[p] + koff, dst);
-    };
     const int nk = K / 64;
     auto koff = [&](int kt) { return kt < nk ? kt * 128 : 0x7ffff000; };
+    // a gathered A reloads step 0's rows past the last step (never consumed)
+    auto dma = [&](int p, int st, int kt) {
+      const unsigned dst = lds0 + st * SB + (4 * p + wv) * 1024;
+      if (4 * p < BM / 8) load_lds(da, doff[p] + (gat ? (kt < nk ? kt * 128 : 0) : koff(kt)), dst);
+      else if (NMAT == 1 || 4 * p < BM / 8 + 16) load_lds(db0, doff[p] + koff(kt), dst);
+      else load_lds(db1, doff[p] + koff(kt), dst);
+    };
     const int sw = swz(lr);
     const int a_rd2 = (wm * (BM / WM) + lr) * 128;
     int b_rd2[TN];
@@ -674,7 +703,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs g, const int b) {
 #pragma unroll
     for (int st = 0; st < 3; ++st)
 #pragma unroll
-      for (int p = 0; p < PW; ++p) dma(p, st, koff(st));
+      for (int p = 0; p < PW; ++p) dma(p, st, st);
     wait_vm<2 * PW>();
     __syncthreads();
 #pragma unroll
@@ -684,7 +713,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs g, const int b) {
     auto step = [&](int kt, auto ST) {
       constexpr int st0 = decltype(ST)::value;
       constexpr int st1 = (st0 + 1) & 3, st3 = (st0 + 3) & 3;
-      const int k3 = koff(kt + 3);
+      const int k3 = kt + 3;  // the step whose loads this step issues
 #pragma unroll
       for (int kk = 0; kk < KS - 1; ++kk) {
         int rd = 0, dq = D[kk];
@@ -756,6 +785,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs g, const int b) {
     // past the last step the offset is out of range: the loads return zeros
     // without touching memory
     const int o2 = (kt + 1 + NST < nk) ? goff + (kt + 1 + NST) * 128 : 0x7ffff000;
+    const int ao2 = (kt + 1 + NST < nk) ? (kt + 1 + NST) * 128 : 0;
     // sub-steps 0 .. KS-2: MFMAs + next fragments + LDS writes of step kt+1 + loads of step kt+1+NST
 #pragma unroll
     for (int kk = 0; kk < KS - 1; ++kk) {
@@ -766,7 +796,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs g, const int b) {
 #pragma unroll
       for (int p = kk * PER; p < (kk + 1) * PER && p < P; ++p) {
         *reinterpret_cast<uint4*>(wb + p * 32 * kRowBytes) = st[W][p];
-        issue_one(W, p, o2);
+        issue_one(W, p, o2, ao2);
         ++nw;
       }
       // interleave: NR x (fragment read, MFMA), then (LDS write, global load,

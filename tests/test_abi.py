@@ -73,12 +73,15 @@ N = None
      "replica_budget"),
     ("moe_dispatch", (16, 0, 10, 64, 16, 2, 8, N, 16, 2, 12, 16, 16, 16, 16, 16, 16, 16, 16, 1 << 20, N, N), -1,
      "replica_budget"),
-    ("moe_expert_ffn", (16, 1, 100, 96, 128, 8, 16, 16, 16, 8, 16, 16, 16, 0, 1, 16, 16, 1 << 30, N, N), -2, "multiples of 64"),
-    ("moe_expert_ffn", (16, 1, 100, 128, 128, 8, 16, 16, 16, 8, 16, N, 16, 0, 1, 16, 16, 1 << 30, N, N), -1, "w_up"),
-    ("moe_expert_ffn", (16, 1, 100, 128, 128, 8, 16, 16, 16, 8, 16, 16, 16, 1, 1, 16, 16, 1 << 30, N, N), -1, "GELU"),
-    ("moe_expert_ffn", (16, 1, 100, 128, 128, 8, 16, 16, 16, 8, 16, 16, 16, 0, 1, 16, 16, 10, N, N), -3, "workspace"),
+    ("moe_expert_ffn", (16, N, 0, 1, 100, 96, 128, 8, 16, 16, 16, 8, 16, 16, 16, 0, 1, 16, 16, 1 << 30, N, N), -2, "multiples of 64"),
+    ("moe_expert_ffn", (16, N, 0, 1, 100, 128, 128, 8, 16, 16, 16, 8, 16, N, 16, 0, 1, 16, 16, 1 << 30, N, N), -1, "w_up"),
+    ("moe_expert_ffn", (16, N, 0, 1, 100, 128, 128, 8, 16, 16, 16, 8, 16, 16, 16, 1, 1, 16, 16, 1 << 30, N, N), -1, "GELU"),
+    ("moe_expert_ffn", (16, N, 0, 1, 100, 128, 128, 8, 16, 16, 16, 8, 16, 16, 16, 0, 1, 16, 16, 10, N, N), -3, "workspace"),
+    # a gathered input (row_src given) of 2^40 rows: offsets beyond 31 bits
+    ("moe_expert_ffn", (16, 16, 1 << 40, 1, 100, 128, 128, 8, 16, 16, 16, 8, 16, 16, 16, 0, 1, 16, 16, 1 << 30, N, N),
+     -2, "gathered input"),
     # 2^27 rows x 2^21 columns: more blocks than 32-bit grid indexing covers
-    ("moe_expert_ffn", (16, 1, 1 << 27, 64, 1 << 21, 8, 16, 16, 16, 8, 16, 16, 16, 0, 1, 16, 16, 1 << 62, N, N), -2,
+    ("moe_expert_ffn", (16, N, 0, 1, 1 << 27, 64, 1 << 21, 8, 16, 16, 16, 8, 16, 16, 16, 0, 1, 16, 16, 1 << 62, N, N), -2,
      "32-bit grid"),
     ("moe_stats_load_state", (1, 1 << 20, 2, 8, 10, 0, 0, 1.5, N, N, N, N), -1, "decay"),
     ("moe_stats_load_state", (1, 1 << 20, 2, 8, 10, 2, 0, 0.9, N, N, N, N), -1, "layer=2"),
@@ -106,7 +109,7 @@ N = None
     ("moe_combine", (16, 1, 10, 16, 16, 10, 9, 64, 16, N, N), -1, "k=9"),
     ("moe_combine", (16, 1, 10, 16, 16, 10, 2, 12, 16, N, N), -1, "multiple of 16"),
     ("moe_check_device_error", (N, N, N), -1, "null check"),
-    ("moe_expert_ffn_profiled", (16, 1, 100, 128, 128, 8, 16, 16, 16, 8, 16, 16, 16, 0, 1, 16, 16, 1 << 30, N, N, N),
+    ("moe_expert_ffn_profiled", (16, N, 0, 1, 100, 128, 128, 8, 16, 16, 16, 8, 16, 16, 16, 0, 1, 16, 16, 1 << 30, N, N, N),
      -1, "three events"),
 ])
 def test_argument_errors_are_reported_before_any_hip_call(call, args, status, msg):

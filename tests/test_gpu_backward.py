@@ -43,7 +43,7 @@ def test_backward_matches_oracle(name):
     d_out = rng.standard_normal((cfg.T, cfg.H)).astype(np.float32)
     if cfg.dtype == "bf16":
         d_out = synth.f32_to_bf16_bits(d_out)
-    fw = moe.moe_layer_forward(to_dev(x), to_dev(lg), cfg.k, wg, wu, wd, cfg.act, 0)
+    fw = moe.moe_layer_forward(to_dev(x), to_dev(lg), cfg.k, wg, wu, wd, cfg.act, 0, copy_rows=True)
     g = moe.moe_backward(fw["x_perm"], fw["y_perm"], fw["idx"], fw["w"], fw["inv_pos"], fw["expert_off"], wg, wu, wd,
                          to_dev(d_out), cfg.act)
     torch.cuda.synchronize()
@@ -79,7 +79,7 @@ def test_backward_twice_reuses_workspace():
     x, lg = synth.hidden0(cfg, 1), synth.logits(cfg, 0, 1)
     wts = synth.expert_weights(cfg, 0)
     wg, _, wd = (None if w is None else to_dev(w) for w in wts)
-    fw = moe.moe_layer_forward(to_dev(x), to_dev(lg), cfg.k, wg, None, wd, cfg.act, 0)
+    fw = moe.moe_layer_forward(to_dev(x), to_dev(lg), cfg.k, wg, None, wd, cfg.act, 0, copy_rows=True)
     ws = torch.empty(moe.moe_backward_workspace_bytes(torch.float32, cfg.T, cfg.k, cfg.H, cfg.I, cfg.E, "gelu"),
                      dtype=torch.uint8, device="cuda")
     outs = []
@@ -104,7 +104,7 @@ def test_backward_full_size_mixtral_sampled():
     wts = synth.expert_weights(cfg, 0, threads=16)
     wg, wu, wd = (to_dev(w) for w in wts)
     d_out = synth.f32_to_bf16_bits(np.random.default_rng(42).standard_normal((cfg.T, cfg.H)).astype(np.float32))
-    fw = moe.moe_layer_forward(to_dev(x), to_dev(lg), cfg.k, wg, wu, wd, cfg.act, 0)
+    fw = moe.moe_layer_forward(to_dev(x), to_dev(lg), cfg.k, wg, wu, wd, cfg.act, 0, copy_rows=True)
     g = moe.moe_backward(fw["x_perm"], fw["y_perm"], fw["idx"], fw["w"], fw["inv_pos"], fw["expert_off"], wg, wu, wd,
                          to_dev(d_out), cfg.act)
     torch.cuda.synchronize()
@@ -147,7 +147,7 @@ def test_empty_batch_forward_and_backward():
     wg, wu, wd = (to_dev(w) for w in wts)
     x = torch.empty((0, cfg.H), dtype=torch.bfloat16, device="cuda")
     lg = torch.empty((0, cfg.E), dtype=torch.float32, device="cuda")
-    fw = moe.moe_layer_forward(x, lg, cfg.k, wg, wu, wd, cfg.act, 0)
+    fw = moe.moe_layer_forward(x, lg, cfg.k, wg, wu, wd, cfg.act, 0, copy_rows=True)
     g = moe.moe_backward(fw["x_perm"], fw["y_perm"], fw["idx"], fw["w"], fw["inv_pos"], fw["expert_off"], wg, wu, wd,
                          torch.empty((0, cfg.H), dtype=torch.bfloat16, device="cuda"), cfg.act,
                          out={"d_w_gate": torch.full_like(wg, 1.0), "d_w_up": torch.full_like(wu, 1.0),

@@ -209,25 +209,33 @@ MINI = {
 }
 
 
-def _gpu_layer(cfg, x, lg, wts, R, path="grouped"):
+def _gpu_layer(cfg, x, lg, wts, R, path="grouped", copy_rows=False):
     wg, wu, wd = (None if w is None else to_dev(w) for w in wts)
-    res = moe.moe_layer_forward(to_dev(x), to_dev(lg), cfg.k, wg, wu, wd, cfg.act, R, path=path)
+    res = moe.moe_layer_forward(to_dev(x), to_dev(lg), cfg.k, wg, wu, wd, cfg.act, R, path=path,
+                                copy_rows=copy_rows)
     _sync()
     return res
 
 
 @pytest.mark.parametrize("name", list(MINI))
 @pytest.mark.parametrize("use_reps", [False, True])
-def test_layer_small_elementwise(name, use_reps):
+@pytest.mark.parametrize("copy_rows", [False, True])
+def test_layer_small_elementwise(name, use_reps, copy_rows):
+    """copy_rows=False: the FFN gathers its rows from x through perm_src (the
+    layer's default); True: the dispatch copies them into x_perm first."""
     cfg = MINI[name]
     R = (cfg.R or 8) if use_reps else 0
     x = synth.hidden0(cfg, 0)
     lg = synth.logits(cfg, 0, 0)
     wts = synth.expert_weights(cfg)
-    res = _gpu_layer(cfg, x, lg, wts, R)
+    res = _gpu_layer(cfg, x, lg, wts, R, copy_rows=copy_rows)
     ref = oracle.moe_layer(x, lg, cfg.k, wts, cfg.act, reps_budget=R)
     assert np.array_equal(from_dev(res["idx"]), ref["idx"])
-    assert np.array_equal(from_dev(res["x_perm"]), ref["x_perm"])
+    assert np.array_equal(from_dev(res["perm_src"]), ref["perm_src"])
+    if copy_rows:
+        assert np.array_equal(from_dev(res["x_perm"]), ref["x_perm"])
+    else:
+        assert res["x_perm"] is None
     kind = "bf16" if cfg.dtype == "bf16" else "fp32_gemm"
     assert_close(from_dev(res["y_perm"]), ref["y_perm"], kind, "y_perm")
     assert_close(from_dev(res["out"]), ref["out"], kind, "out")
@@ -278,11 +286,11 @@ def tail_tile_rows(expert_off, tile=256, trailing=4, stride=64):
     return np.array(sorted(rows), np.int64)
 
 
-def _sampled_layer_check(cfg, R, n_sample=12, seed=0):
+def _sampled_layer_check(cfg, R, n_sample=12, seed=0, copy_rows=False):
     x = synth.hidden0(cfg, 0)
     lg = synth.logits(cfg, 0, 0)
     wts = synth.expert_weights(cfg, threads=16)
-    res = _gpu_layer(cfg, x, lg, wts, R)
+    res = _gpu_layer(cfg, x, lg, wts, R, copy_rows=copy_rows)
     idx_o, w_o = oracle.route(lg, cfg.k)
     assert np.array_equal(from_dev(res["idx"]), idx_o)
     reps = oracle.replicas(oracle.histogram(idx_o, cfg.E), cfg.T, cfg.k, R) if R else None
@@ -303,9 +311,10 @@ def _sampled_layer_check(cfg, R, n_sample=12, seed=0):
     y_gpu = from_dev(res["y_perm"])[d["inv_pos"][sample].ravel()].reshape(y_ref.shape)
     assert_close(y_gpu, y_ref, kind, "sampled y_perm rows")
     assert_close(from_dev(res["out"])[sample], out_ref, kind, "sampled out rows")
-    x_perm = from_dev(res["x_perm"])
-    rows = np.random.default_rng(seed + 1).choice(cfg.T * cfg.k, size=256, replace=False)
-    assert np.array_equal(x_perm[rows], x[d["perm_src"][rows]])
+    if copy_rows:
+        x_perm = from_dev(res["x_perm"])
+        rows = np.random.default_rng(seed + 1).choice(cfg.T * cfg.k, size=256, replace=False)
+        assert np.array_equal(x_perm[rows], x[d["perm_src"][rows]])
     return res
 
 
@@ -396,6 +405,58 @@ def test_direct_to_lds_tiles_partial_columns_odd_k(H, I):
     small = _gpu_layer(cfg, x, lg, wts, 0, path="grouped_small")
     assert torch.equal(small["y_perm"], y_g)
     assert torch.equal(small["out"], out_g)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("M", [900, 30000])
+def test_expert_ffn_gathers_rows_like_a_copy(M, dtype):
+    """moe_expert_ffn with a row map (row_src) over a token matrix: repeated
+    rows, every row order, and map entries outside [0, n_src) (read as zero
+    rows).  Every path gives the bits of the FFN of the same rows copied out on
+    the host, and the rows match the oracle's FFN."""
+    n_src = M // 3 + 7
+    cfg = synth.CONFIGS["mixtral"].scaled(T=n_src, E=3, H=128, I=192, dtype=dtype)
+    x = synth.hidden0(cfg, 5)
+    wts = synth.expert_weights(cfg)
+    rng = np.random.default_rng(M)
+    row_src = rng.integers(0, n_src, size=M).astype(np.int32)
+    row_src[rng.choice(M, size=5, replace=False)] = np.array([-1, n_src, n_src + 100, -7, 2 ** 30], np.int32)
+    gathered = np.where((row_src >= 0)[:, None] & (row_src < n_src)[:, None],
+                        x[np.clip(row_src, 0, n_src - 1)], np.zeros_like(x[:1]))
+    cuts = [0, M // 4, M // 4, (3 * M) // 5, M]
+    experts = [1, 0, 2, 1]
+    max_slots = 6
+    slot_off = np.full(max_slots + 1, M, np.int32)
+    slot_off[:len(cuts)] = cuts
+    slot_expert = np.zeros(max_slots, np.int32)
+    slot_expert[:len(experts)] = experts
+    n_slots = np.array([len(experts)], np.int32)
+    wg, wu, wd = (to_dev(w) for w in wts)
+    so, se, ns = to_dev(slot_off), to_dev(slot_expert), to_dev(n_slots)
+    xd, rs, gd = to_dev(x), to_dev(row_src), to_dev(gathered)
+    ref = oracle.ffn_rows(gathered, np.repeat(np.array(experts, np.int32), np.diff(cuts)), *wts, act="swiglu")
+    for path in ("grouped", "grouped_small", "dense", "auto"):
+        y_gather = moe.moe_expert_ffn(xd, so, se, ns, wg, wu, wd, act="swiglu", path=path, row_src=rs)
+        y_copy = moe.moe_expert_ffn(gd, so, se, ns, wg, wu, wd, act="swiglu", path=path)
+        _sync()
+        assert torch.equal(y_gather, y_copy), path
+        if path == "grouped":
+            assert_close(from_dev(y_gather), ref, "bf16" if dtype == "bf16" else "fp32_gemm", "y_perm")
+
+
+def test_mixtral_full_size_gather_equals_copy():
+    """The full Mixtral-shaped layer (R = 8): the gathering FFN (the layer's
+    default) and the copying dispatch + FFN give the same bits."""
+    cfg = synth.CONFIGS["mixtral"]
+    x = synth.hidden0(cfg, 0)
+    lg = synth.logits(cfg, 0, 0)
+    wts = synth.expert_weights(cfg, threads=16)
+    a = _gpu_layer(cfg, x, lg, wts, 8)
+    out_a, y_a = a["out"].clone(), a["y_perm"].clone()
+    del a
+    b = _gpu_layer(cfg, x, lg, wts, 8, copy_rows=True)
+    assert torch.equal(b["y_perm"], y_a)
+    assert torch.equal(b["out"], out_a)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
