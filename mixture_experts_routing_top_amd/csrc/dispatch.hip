@@ -35,7 +35,10 @@
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kScanThreads = 1024;  // the one scan block: kScanThreads / E threads per expert column
+// the one scan block: NT / E threads per expert column; NT = 1024 for count
+// tables of more than kWideScan entries (the DeepSeek-V2 shape), 256 below (a
+// 1024-thread block costs a few microseconds more where there is little to sum)
+constexpr int kWideScan = 2048;
 constexpr int kPairs = 512;  // pairs per rank block (two rounds of 256)
 static_assert(kPairs % kThreads == 0, "whole rounds");
 
@@ -123,6 +126,7 @@ __device__ void block_scan_inclusive(int64_t* v, int n) {
   }
 }
 
+template <int kScanThreads>
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(const int32_t* __restrict__ blk_cnt, int nblk, int E,
                                                         int64_t P, const int32_t* __restrict__ counts,
                                                         const int32_t* __restrict__ replicas, int plan_budget,
@@ -140,7 +144,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(const int32_t* __res
   // thread (g, e) = g*E + e sums column e over group g's run of blocks, eight
   // loads in flight
   constexpr int U = 8;
-  const int G = kScanThreads / E;
+  const int G = max(1, min(kScanThreads / E, nblk));  // no more groups than blocks
   const int g = tid / E, e = tid - g * E;
   const int per = (nblk + G - 1) / G;
   const int b0 = min(g * per, nblk), b1 = min(b0 + per, nblk);
@@ -353,8 +357,12 @@ extern "C" int moe_dispatch(const void* x, moe_dtype dt, int64_t T, int H, const
   const int64_t P = T * k;
   const int nblk = static_cast<int>(ceil_div(P, kPairs));
   if (nblk > 0) rank_kernel<<<nblk, kThreads, 0, s>>>(topk_idx, P, k, E, blk_cnt, rank, check);
-  scan_kernel<<<1, kScanThreads, 0, s>>>(blk_cnt, nblk, E, P, counts, replicas, replica_budget, max_slots, blk_base,
-                                     expert_off, slot_off, slot_expert, n_slots, check);
+  if (static_cast<int64_t>(nblk) * E > kWideScan)
+    scan_kernel<1024><<<1, 1024, 0, s>>>(blk_cnt, nblk, E, P, counts, replicas, replica_budget, max_slots, blk_base,
+                                         expert_off, slot_off, slot_expert, n_slots, check);
+  else
+    scan_kernel<256><<<1, 256, 0, s>>>(blk_cnt, nblk, E, P, counts, replicas, replica_budget, max_slots, blk_base,
+                                       expert_off, slot_off, slot_expert, n_slots, check);
   if (T > 0 && x_perm) {
     const int chunks = static_cast<int>(static_cast<int64_t>(H) * elem_bytes(dt) / 16);
     const int64_t threads = T * ceil_div(chunks, kChunksPerThread);
