@@ -207,12 +207,12 @@ int ffn_impl(const void* x_perm, const int32_t* row_src, int64_t n_src, moe_dtyp
   const hipStream_t s = as_stream(stream);
   const int nt1 = static_cast<int>(ceil_div(I, act == MOE_SWIGLU ? kTileN / 2 : kTileN));
   // The gate/up GEMM runs a range's last tile of at most 128 rows as a 128-row
-  // tile when it is bf16 SwiGLU (a register epilogue) and wide (>= 32 column
-  // tiles: its launch is many rounds long, so the saved MFMA work outweighs
-  // the tail the shorter tiles add).  The down GEMM keeps the 256-row tiles:
-  // there the extra blocks land in an already short last round (measured
-  // slower on the Mixtral shape).
-  const bool gateup_mid = dt == MOE_BF16 && act == MOE_SWIGLU && nt1 >= 32;
+  // tile when it is bf16 SwiGLU (a register epilogue): half the MFMA work of a
+  // 256-row tile for the same weight reads (measured faster on the Mixtral
+  // shape and on DeepSeek-V2's 12 column tiles at T = 4096).  The down GEMM
+  // keeps the 256-row tiles: there the extra blocks land in an already short
+  // last round (measured slower on the Mixtral shape).
+  const bool gateup_mid = dt == MOE_BF16 && act == MOE_SWIGLU;
   const int mid_cap_rows = gateup_mid ? 128 : 0;
   const int nt2 = static_cast<int>(ceil_div(H, kTileN));
   // GROUPED: 256-row tiles covering each slot.  GROUPED_SMALL: 64-row tiles
