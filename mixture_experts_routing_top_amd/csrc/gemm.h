@@ -82,6 +82,7 @@ __device__ __forceinline__ f32x16 mma(float a, float b, const f32x16& c) {
 constexpr int kTileN = 256;      // weight rows per tile (gate/up: 128 + 128)
 constexpr int kRowBytes = 144;   // LDS row pitch: 128 data bytes + 16 pad
 constexpr int kGroupM = 8;       // row tiles per raster group
+constexpr int kStagedStoreMinBM = 128;  // bf16 forward tiles this tall store through LDS
 
 struct GemmArgs {
   const void* A;   // [M, K]; weight-gradient mode: [Mw, ld] (rows of transposed activations)
@@ -1009,6 +1010,47 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs g, const int b) {
   // (lr, lg) of a 32 x 32 tile holds row lr and columns 8 q + 4 lg + c for
   // element 4 q + c: four adjacent outputs, stored with one 8- or 16-byte write
   constexpr int JO = NMAT == 2 ? TN / 2 : TN;  // output column subtiles per wave
+  // bf16 outputs of a forward tile: each 8-byte group goes to an LDS copy of
+  // the output tile first (rows of NSUB values, 16-byte chunk c of row r at
+  // chunk c ^ (r mod chunks): conflict-free for the 32 rows a group write
+  // spans), then whole rows leave with 16 bytes per lane, one row segment of
+  // 256 or 512 contiguous bytes per 16 or 32 lanes.  Written straight from
+  // the accumulators, one 8-byte write covers 16 bytes of each of 32 rows.
+  if constexpr (kBf16 && !kWgrad && (EPI == kEpiSwiGLU || EPI == kEpiStore) && BM >= kStagedStoreMinBM) {
+    constexpr int RB = NSUB * 2;   // bytes per staged row
+    constexpr int CH = NSUB / 8;   // 16-byte chunks per row
+    static_assert(BM * RB <= kGemmLdsBytes, "staged output tile must fit in LDS");
+    __syncthreads();  // every wave is done with the operand stages
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int srow = wm * (BM / WM) + i * 32 + lr;
+      if (srow >= m_valid) continue;
+#pragma unroll
+      for (int j = 0; j < JO; ++j) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int cw = (NMAT == 2 ? wn * (CW / 2) : wn * CW) + j * 32 + 8 * q;  // first column of the chunk
+          float v[4];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            v[c] = acc[i][j][4 * q + c];
+            if constexpr (EPI == kEpiSwiGLU) v[c] = swiglu_h(v[c], acc[i][j + TN / 2][4 * q + c]);
+          }
+          store4(reinterpret_cast<uint16_t*>(lds + srow * RB + (((cw >> 3) ^ (srow & (CH - 1))) << 4) + 8 * lg), v);
+        }
+      }
+    }
+    __syncthreads();
+    const int ch = tid % CH;
+    const int col = n0 + 8 * ch;
+    if (col < N) {  // N is a multiple of 64: a chunk is wholly in or out
+      T* __restrict__ C = static_cast<T*>(g.C);
+      for (int r = tid / CH; r < m_valid; r += 256 / CH)
+        *reinterpret_cast<uint4*>(C + (r0 + r) * N + col) =
+            *reinterpret_cast<const uint4*>(lds + r * RB + ((ch ^ (r & (CH - 1))) << 4));
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     const int lrow_out = wm * (BM / WM) + i * 32 + lr;
