@@ -217,7 +217,8 @@ constexpr int gemm_lds_bytes() {
   constexpr bool kDTL = kBf16 && (BM == 256 || BM == 128);
   constexpr bool kDTL64 = kBf16 && BM == 64 && !kWgrad;
   constexpr int kStageBytes = (BM + kTileN) * kRowBytes;
-  constexpr int kStagedEpi = (!kWgrad && (EPI == kEpiGELU || EPI == kEpiSwiGLUGrad || EPI == kEpiGELUGrad))
+  constexpr int kStagedEpi = (!kWgrad && (EPI == kEpiGELU || EPI == kEpiSwiGLUGrad || EPI == kEpiGELUGrad ||
+                                          EPI == kEpiStoreF32))
                                  ? (BM / WM) * (kTileN + 4) * 4 : 0;
   constexpr int kDtlBytes = kDTL ? 2 * BM * 128 + 3 * kTileN * 128 : 4 * (BM + kTileN) * 128;
   return (kDTL || kDTL64) ? (kDtlBytes > kStagedEpi ? kDtlBytes : kStagedEpi) : 2 * kStageBytes;
@@ -928,7 +929,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs g, const int b) {
     return;
   }
 
-  if constexpr (!kWgrad && (EPI == kEpiGELU || EPI == kEpiGELUGrad)) {
+  // (the fp32 store takes the same path: its 16-byte stores then cover whole
+  // 1 KiB rows instead of 32 bytes in each of 32 rows)
+  if constexpr (!kWgrad && (EPI == kEpiGELU || EPI == kEpiGELUGrad || EPI == kEpiStoreF32)) {
     static_assert(NMAT == 1, "staged epilogues take one weight matrix");
     constexpr int RH = BM / WM;  // rows staged per round
     constexpr int kPitch = kTileN + 4;  // floats per staged row (padded: rows start 4 banks apart)
@@ -973,7 +976,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs g, const int b) {
             float o0[4], o1[4];
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-              if constexpr (EPI == kEpiGELU) {
+              if constexpr (EPI == kEpiStoreF32) {
+                o0[c] = av[c];
+              } else if constexpr (EPI == kEpiGELU) {
                 o0[c] = gelu_h(av[c]);
               } else {
                 // the recompute of z with the GELU gradient: d_z = d_h (Phi(z) + z phi(z))
@@ -985,7 +990,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs g, const int b) {
               }
             }
             const int64_t o = row * N + col;
-            if constexpr (kBf16) {
+            if constexpr (EPI == kEpiStoreF32) {
+              *reinterpret_cast<float4*>(static_cast<float*>(g.C) + o) = make_float4(o0[0], o0[1], o0[2], o0[3]);
+            } else if constexpr (kBf16) {
               *reinterpret_cast<uint2*>(C + o) =
                   make_uint2(f32_to_bf16_bits(o0[0]) | (f32_to_bf16_bits(o0[1]) << 16),
                              f32_to_bf16_bits(o0[2]) | (f32_to_bf16_bits(o0[3]) << 16));
@@ -1010,13 +1017,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs g, const int b) {
   // (lr, lg) of a 32 x 32 tile holds row lr and columns 8 q + 4 lg + c for
   // element 4 q + c: four adjacent outputs, stored with one 8- or 16-byte write
   constexpr int JO = NMAT == 2 ? TN / 2 : TN;  // output column subtiles per wave
-  // bf16 outputs of a forward tile: each 8-byte group goes to an LDS copy of
+  // bf16 outputs of a tall tile: each 8-byte group goes to an LDS copy of
   // the output tile first (rows of NSUB values, 16-byte chunk c of row r at
   // chunk c ^ (r mod chunks): conflict-free for the 32 rows a group write
   // spans), then whole rows leave with 16 bytes per lane, one row segment of
   // 256 or 512 contiguous bytes per 16 or 32 lanes.  Written straight from
   // the accumulators, one 8-byte write covers 16 bytes of each of 32 rows.
-  if constexpr (kBf16 && !kWgrad && (EPI == kEpiSwiGLU || EPI == kEpiStore) && BM >= kStagedStoreMinBM) {
+  if constexpr (kBf16 && (EPI == kEpiSwiGLU || EPI == kEpiStore) && BM >= kStagedStoreMinBM) {
     constexpr int RB = NSUB * 2;   // bytes per staged row
     constexpr int CH = NSUB / 8;   // 16-byte chunks per row
     static_assert(BM * RB <= kGemmLdsBytes, "staged output tile must fit in LDS");
@@ -1044,10 +1051,17 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs g, const int b) {
     const int ch = tid % CH;
     const int col = n0 + 8 * ch;
     if (col < N) {  // N is a multiple of 64: a chunk is wholly in or out
-      T* __restrict__ C = static_cast<T*>(g.C);
-      for (int r = tid / CH; r < m_valid; r += 256 / CH)
-        *reinterpret_cast<uint4*>(C + (r0 + r) * N + col) =
-            *reinterpret_cast<const uint4*>(lds + r * RB + ((ch ^ (r & (CH - 1))) << 4));
+      for (int r = tid / CH; r < m_valid; r += 256 / CH) {
+        const int64_t row = r0 + r;
+        T* Cr;
+        if constexpr (kWgrad)  // weight gradients: rows below c_split to C, the others to C2
+          Cr = row < g.c_split
+                   ? static_cast<T*>(g.C) + (static_cast<int64_t>(e) * g.c_split + row) * N
+                   : static_cast<T*>(g.C2) + (static_cast<int64_t>(e) * (g.Mw - g.c_split) + row - g.c_split) * N;
+        else
+          Cr = static_cast<T*>(g.C) + row * N;
+        *reinterpret_cast<uint4*>(Cr + col) = *reinterpret_cast<const uint4*>(lds + r * RB + ((ch ^ (r & (CH - 1))) << 4));
+      }
     }
     return;
   }
