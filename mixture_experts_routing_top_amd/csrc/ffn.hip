@@ -92,25 +92,31 @@ hipError_t mark(hipEvent_t const* ev, int i, hipStream_t s) {
 }
 
 // A 256-row tiling runs with its 128-row and 64-row companion tables in one
-// mixed launch; the 64-row tilings run alone.
+// mixed launch (wnt: bf16 weights loaded non-temporally); the 64-row tilings
+// run alone.
 template <bool kBf16, int EPI, int NMAT>
-void launch_gemm(bool small, const GemmArgs& p, const GemmArgs& mid, const GemmArgs& companion, unsigned grid,
-                 hipStream_t s) {
+void launch_gemm(bool small, bool wnt, const GemmArgs& p, const GemmArgs& mid, const GemmArgs& companion,
+                 unsigned grid, hipStream_t s) {
   if (small) gemm_kernel<kBf16, NMAT, EPI, kSmallM, 1><<<grid, 256, 0, s>>>(p);
-  else gemm_mixed_kernel<kBf16, NMAT, EPI><<<grid, 256, 0, s>>>(p, mid, companion);
+  else if constexpr (kBf16) {
+    if (wnt) gemm_mixed_kernel<kBf16, NMAT, EPI, true><<<grid, 256, 0, s>>>(p, mid, companion);
+    else gemm_mixed_kernel<kBf16, NMAT, EPI><<<grid, 256, 0, s>>>(p, mid, companion);
+  } else {
+    gemm_mixed_kernel<kBf16, NMAT, EPI><<<grid, 256, 0, s>>>(p, mid, companion);
+  }
 }
 
 // Phase 1 (gate/up or W1) and phase 2 (down or W2), each on its own tile table.
 template <bool kBf16>
 int launch_ffn(const GemmArgs& p1, bool small1, unsigned grid1, const GemmArgs& m1, const GemmArgs& t1,
                const GemmArgs& p2, bool small2, unsigned grid2, const GemmArgs& m2, const GemmArgs& t2, bool swiglu,
-               hipEvent_t const* ev, hipStream_t s) {
+               bool wnt1, bool wnt2, hipEvent_t const* ev, hipStream_t s) {
   if (int rc = moe::hip_status(mark(ev, 0, s), "moe_expert_ffn timing event")) return rc;
-  if (swiglu) launch_gemm<kBf16, kEpiSwiGLU, 2>(small1, p1, m1, t1, grid1, s);
-  else launch_gemm<kBf16, kEpiGELU, 1>(small1, p1, m1, t1, grid1, s);
+  if (swiglu) launch_gemm<kBf16, kEpiSwiGLU, 2>(small1, wnt1, p1, m1, t1, grid1, s);
+  else launch_gemm<kBf16, kEpiGELU, 1>(small1, wnt1, p1, m1, t1, grid1, s);
   if (int rc = moe::hip_status(hipGetLastError(), "moe_expert_ffn gate/up launch")) return rc;
   if (int rc = moe::hip_status(mark(ev, 1, s), "moe_expert_ffn timing event")) return rc;
-  launch_gemm<kBf16, kEpiStore, 1>(small2, p2, m2, t2, grid2, s);
+  launch_gemm<kBf16, kEpiStore, 1>(small2, wnt2, p2, m2, t2, grid2, s);
   if (int rc = moe::hip_status(hipGetLastError(), "moe_expert_ffn down launch")) return rc;
   return moe::hip_status(mark(ev, 2, s), "moe_expert_ffn timing event");
 }
@@ -386,9 +392,21 @@ int ffn_impl(const void* x_perm, const int32_t* row_src, int64_t n_src, moe_dtyp
   };
   const GemmArgs m1 = mid_table(p1, 0), m2 = mid_table(p2, 1);
   const bool swiglu = act == MOE_SWIGLU;
+  // Weight rows go through the caches with the non-temporal hint when few row
+  // tiles share an expert's weights (M / E rows per expert on average): they
+  // then give way to the activation rows, which every column tile of a row
+  // tile reads again.  Timed against plain loads on the DeepSeek-V2-, Mixtral-
+  // and DBRX-shaped routings: the hint pays on the gate/up GEMM up to 1024 rows
+  // per expert (four row tiles; its activation rows serve 2I / 256 column
+  // tiles) and on the down GEMM below 256 (H / 256 column tiles), and costs
+  // time above.
+  const int64_t per_expert = M / std::max(E, 1);
+  const bool wnt1 = per_expert <= 1024, wnt2 = per_expert < 256;
   return dt == MOE_BF16
-             ? launch_ffn<true>(p1, k1 != kG256, grid1, m1, t1, p2, k2 != kG256, grid2, m2, t2, swiglu, ev, s)
-             : launch_ffn<false>(p1, k1 != kG256, grid1, m1, t1, p2, k2 != kG256, grid2, m2, t2, swiglu, ev, s);
+             ? launch_ffn<true>(p1, k1 != kG256, grid1, m1, t1, p2, k2 != kG256, grid2, m2, t2, swiglu, wnt1, wnt2,
+                                ev, s)
+             : launch_ffn<false>(p1, k1 != kG256, grid1, m1, t1, p2, k2 != kG256, grid2, m2, t2, swiglu, false, false,
+                                 ev, s);
 }
 
 }  // namespace

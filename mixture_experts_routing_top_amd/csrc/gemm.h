@@ -158,6 +158,19 @@ __device__ __forceinline__ void load_lds(const u32x4& r, int off, unsigned lds_b
                : "s"(lds_block), "v"(off), "s"(r)
                : "m0");
 }
+// The same with the non-temporal hint: the lines are the first the caches
+// give up, for data that no other tile will read again soon.
+__device__ __forceinline__ void load_lds_nt(const u32x4& r, int off, unsigned lds_block) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
+               :
+               : "s"(lds_block), "v"(off), "s"(r)
+               : "m0");
+}
+template <bool NT>
+__device__ __forceinline__ void load_lds_hint(const u32x4& r, int off, unsigned lds_block) {
+  if constexpr (NT) load_lds_nt(r, off, lds_block);
+  else load_lds(r, off, lds_block);
+}
 #pragma clang diagnostic pop
 
 // s_waitcnt vmcnt(n) with the other counters left alone (n < 64).
@@ -230,7 +243,8 @@ __shared__ __align__(1024) char gemm_lds[kGemmLdsBytes];
 
 // One block's tile: `b` is its index in the grid of this tiling (b & 7 its
 // XCD); it uses the first gemm_lds_bytes of gemm_lds.
-template <bool kBf16, int NMAT, int EPI, int BM, int WM, bool kWgrad = false, int KM = 0>
+// WNT: the bf16 weight rows are loaded with the non-temporal hint.
+template <bool kBf16, int NMAT, int EPI, int BM, int WM, bool kWgrad = false, int KM = 0, bool WNT = false>
 __device__ __forceinline__ void gemm_tile(const GemmArgs g, const int b) {
   char* const lds = gemm_lds;
   using TR = Tr<kBf16>;
@@ -508,8 +522,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs g, const int b) {
     auto dmaB = [&](int p, int st, int koff, const u32x4& dk) {
       const unsigned dst = lds0 + 2 * SA + st * SBW + (4 * p + wv) * 1024;
       if constexpr (kBK) load_lds(dk, offB[p], dst);
-      else if (NMAT == 1 || p < PB_ / 2) load_lds(db0, offB[p] + koff, dst);
-      else load_lds(db1, offB[p] + koff, dst);
+      else if (NMAT == 1 || p < PB_ / 2) load_lds_hint<WNT>(db0, offB[p] + koff, dst);
+      else load_lds_hint<WNT>(db1, offB[p] + koff, dst);
     };
     constexpr int BS0[4] = {0, 3, 6, 8};  // weight blocks issued in sub-steps 0, 1, 2
     const int sw = swz(lr);
@@ -678,8 +692,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs g, const int b) {
     auto dma = [&](int p, int st, int kt) {
       const unsigned dst = lds0 + st * SB + (4 * p + wv) * 1024;
       if (4 * p < BM / 8) load_lds(da, doff[p] + (gat ? (kt < nk ? kt * 128 : 0) : koff(kt)), dst);
-      else if (NMAT == 1 || 4 * p < BM / 8 + 16) load_lds(db0, doff[p] + koff(kt), dst);
-      else load_lds(db1, doff[p] + koff(kt), dst);
+      else if (NMAT == 1 || 4 * p < BM / 8 + 16) load_lds_hint<WNT>(db0, doff[p] + koff(kt), dst);
+      else load_lds_hint<WNT>(db1, doff[p] + koff(kt), dst);
     };
     const int sw = swz(lr);
     const int a_rd2 = (wm * (BM / WM) + lr) * 128;
@@ -1117,7 +1131,8 @@ constexpr bool kHasMidTiles = kBf16 && (EPI == kEpiSwiGLU || EPI == kEpiStore);
 // trailing tiles); the roundings keep every block's index congruent to its XCD
 // in each part.  The shorter tiles are dispatched last and so fill the CUs
 // that the last round of 256-row tiles leaves idle.  Blocks past all exit.
-template <bool kBf16, int NMAT, int EPI>
+// WNT: weights loaded non-temporally (bf16).
+template <bool kBf16, int NMAT, int EPI, bool WNT = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_mixed_kernel(GemmArgs big,
                                                                                                    GemmArgs mid,
                                                                                                    GemmArgs small) {
@@ -1126,7 +1141,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int nb = (*big.n_tiles * big.n_col_tiles + 7) & ~7;
   const int b = static_cast<int>(blockIdx.x);
   if (b < nb) {
-    gemm_tile<kBf16, NMAT, EPI, 256, 2>(big, b);
+    gemm_tile<kBf16, NMAT, EPI, 256, 2, false, 0, WNT>(big, b);
     return;
   }
   int nm = 0;
@@ -1134,11 +1149,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     static_assert(gemm_lds_bytes<kBf16, NMAT, EPI, 128, 1, false>() <= kGemmLdsBytes, "LDS");
     nm = (*mid.n_tiles * mid.n_col_tiles + 7) & ~7;
     if (b < nb + nm) {
-      gemm_tile<kBf16, NMAT, EPI, 128, 1>(mid, b - nb);
+      gemm_tile<kBf16, NMAT, EPI, 128, 1, false, 0, WNT>(mid, b - nb);
       return;
     }
   }
-  gemm_tile<kBf16, NMAT, EPI, 64, 1>(small, b - nb - nm);
+  gemm_tile<kBf16, NMAT, EPI, 64, 1, false, 0, WNT>(small, b - nb - nm);
 }
 
 // Lists the row tiles of the GEMMs.  With `merge`, consecutive slots of one
