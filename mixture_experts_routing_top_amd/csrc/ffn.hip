@@ -393,15 +393,19 @@ int ffn_impl(const void* x_perm, const int32_t* row_src, int64_t n_src, moe_dtyp
   const GemmArgs m1 = mid_table(p1, 0), m2 = mid_table(p2, 1);
   const bool swiglu = act == MOE_SWIGLU;
   // Weight rows go through the caches with the non-temporal hint when few row
-  // tiles share an expert's weights (M / E rows per expert on average): they
-  // then give way to the activation rows, which every column tile of a row
-  // tile reads again.  Timed against plain loads on the DeepSeek-V2-, Mixtral-
-  // and DBRX-shaped routings: the hint pays on the gate/up GEMM up to 1024 rows
-  // per expert (four row tiles; its activation rows serve 2I / 256 column
-  // tiles) and on the down GEMM below 256 (H / 256 column tiles), and costs
-  // time above.
+  // tiles share an expert's weights (M / E rows per expert on average) and the
+  // launch is large enough to contend for the caches (up to one round of 256
+  // tiles, counting a partial row tile per expert): they then give way to the
+  // activation rows, which every column tile of a row tile reads again.  Timed
+  // against plain loads on the DeepSeek-V2-, Mixtral- and DBRX-shaped
+  // routings: the hint pays on the gate/up GEMM up to 1024 rows per expert
+  // (four row tiles; its activation rows serve 2I / 256 column tiles) and on
+  // the down GEMM below 256 (H / 256 column tiles), and costs time above; on a
+  // single expert of 512 rows with 12 column tiles (24 tiles) it cost 40%.
   const int64_t per_expert = M / std::max(E, 1);
-  const bool wnt1 = per_expert <= 1024, wnt2 = per_expert < 256;
+  const int64_t row_tiles = ceil_div(M, kBigM) + E;
+  const bool big_launch1 = row_tiles * nt1 >= kComputeUnits, big_launch2 = row_tiles * nt2 >= kComputeUnits;
+  const bool wnt1 = per_expert <= 1024 && big_launch1, wnt2 = per_expert < 256 && big_launch2;
   return dt == MOE_BF16
              ? launch_ffn<true>(p1, k1 != kG256, grid1, m1, t1, p2, k2 != kG256, grid2, m2, t2, swiglu, wnt1, wnt2,
                                 ev, s)
