@@ -82,7 +82,7 @@ __device__ __forceinline__ f32x16 mma(float a, float b, const f32x16& c) {
 constexpr int kTileN = 256;      // weight rows per tile (gate/up: 128 + 128)
 constexpr int kRowBytes = 144;   // LDS row pitch: 128 data bytes + 16 pad
 constexpr int kGroupM = 8;       // row tiles per raster group
-constexpr int kStagedStoreMinBM = 128;  // bf16 forward tiles this tall store through LDS
+constexpr int kStagedStoreMinBM = 128;  // bf16 tiles this tall stage their SwiGLU or plain stores in LDS
 
 struct GemmArgs {
   const void* A;   // [M, K]; weight-gradient mode: [Mw, ld] (rows of transposed activations)
