@@ -695,7 +695,7 @@ def stats_bench(moe, synth, torch, np, reps=20):
             if it >= 3:
                 ts.append(a.elapsed_time(b) * 1e3)
         out.append({"workload": name, "T": T, "E": E, "k": k, "replica_budget": R,
-                    "cooccurrence_in": "lds (packed 16-bit)" if E * E <= 32768 else "global atomics",
+                    "cooccurrence_in": "lds (packed 16-bit)" if E * E <= 32768 else "lds (packed 8-bit)",
                     "us_median": round(float(np.median(ts)), 2)})
     return {"stats": out}
 

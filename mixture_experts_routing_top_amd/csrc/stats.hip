@@ -33,8 +33,13 @@ constexpr int kThreads = 256;
 constexpr int kTokPerBlock = 512;
 // One block's co-occurrence counts are at most 512 tokens x k^2 = 32768 per
 // cell, so while recording, two 16-bit counters share one LDS word: E*E up to
-// 32768 cells (E <= 181) stays in LDS; larger E adds into global memory.
+// 32768 cells (E <= 181) stays in LDS.  Up to 65536 cells (E <= 256) four
+// 8-bit counters share a word, in blocks of 255 tokens (stats_kernel<true>):
+// a token whose k experts are distinct, and whose previous layer's are too,
+// adds at most one to a cell; a token naming an expert twice adds into global
+// memory instead.
 constexpr int kLdsCooc = 128 * 128;  // LDS words for co-occurrence
+constexpr int kTokPerBlock8 = 255;
 constexpr int kSplitE = 64;          // above: the E*E work runs in pair_kernel
 
 struct Layout {
@@ -74,9 +79,10 @@ struct Args {
   int32_t* check;
 };
 
+template <bool k8>
 __global__ __launch_bounds__(kThreads) void stats_kernel(Args a) {
   __shared__ int32_t hist[moe::kMaxExperts];
-  __shared__ int32_t cooc[kLdsCooc];   // packed 16-bit counters of one block
+  __shared__ int32_t cooc[kLdsCooc];   // packed 16-bit (k8: 8-bit) counters of one block
   __shared__ int32_t nw[moe::kMaxExperts];
   __shared__ int32_t rowsum[moe::kMaxExperts];
   __shared__ float ps[moe::kMaxExperts];
@@ -86,7 +92,8 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(Args a) {
   const int E = a.E, k = a.k, tid = threadIdx.x;
   const int EE = E * E;
   const bool do_cooc = a.idx && a.layer > 0;
-  const bool lds_cooc = EE <= 2 * kLdsCooc;  // recording in LDS (packed)
+  const bool lds_cooc = !k8 && EE <= 2 * kLdsCooc;  // recording in LDS (packed 16-bit)
+  constexpr int kTPB = k8 ? kTokPerBlock8 : kTokPerBlock;
   int32_t* acc = a.state + a.lay.acc;
   int32_t* acc_cooc = a.state + a.lay.acc_cooc;
   unsigned* ticket = reinterpret_cast<unsigned*>(a.state + a.lay.ticket);
@@ -95,9 +102,11 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(Args a) {
     for (int e = tid; e < E; e += kThreads) hist[e] = 0;
     if (do_cooc && lds_cooc)
       for (int q = tid; q < (EE + 1) / 2; q += kThreads) cooc[q] = 0;
+    if (k8 && do_cooc)
+      for (int q = tid; q < (EE + 3) / 4; q += kThreads) cooc[q] = 0;
     __syncthreads();
-    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kTokPerBlock;
-    const int64_t t1 = min(a.T, t0 + kTokPerBlock);
+    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kTPB;
+    const int64_t t1 = min(a.T, t0 + kTPB);
     bool bad_index = false, bad_dup = false;
     for (int64_t t = t0 + tid; t < t1; t += kThreads) {
       int cur[moe::kMaxTopK];
@@ -116,7 +125,37 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(Args a) {
 #pragma unroll
           for (int j = 0; j < i; ++j) bad_dup |= i < k && cur[i] >= 0 && cur[i] == cur[j];
       }
-      if (do_cooc) {
+      if (k8 && do_cooc) {
+        int prv[moe::kMaxTopK];
+        bool dup = false;  // an expert named twice by this token or by its previous layer
+#pragma unroll
+        for (int i = 0; i < moe::kMaxTopK; ++i) {
+          prv[i] = -1;
+          if (i < k) {
+            const int p = a.prev[t * k + i];
+            if (p >= 0 && p < E) prv[i] = p;
+            else bad_index = true;
+          }
+        }
+#pragma unroll
+        for (int i = 1; i < moe::kMaxTopK; ++i)
+#pragma unroll
+          for (int j = 0; j < i; ++j)
+            dup |= i < k && ((cur[i] >= 0 && cur[i] == cur[j]) || (prv[i] >= 0 && prv[i] == prv[j]));
+#pragma unroll
+        for (int i = 0; i < moe::kMaxTopK; ++i) {
+          if (i >= k) break;
+          if (prv[i] < 0) continue;
+#pragma unroll
+          for (int j = 0; j < moe::kMaxTopK; ++j) {
+            if (j < k && cur[j] >= 0) {
+              const int q = prv[i] * E + cur[j];
+              if (!dup) atomicAdd(reinterpret_cast<unsigned*>(&cooc[q >> 2]), 1u << (8 * (q & 3)));
+              else atomicAdd(&acc_cooc[q], 1);
+            }
+          }
+        }
+      } else if (do_cooc) {
 #pragma unroll
         for (int i = 0; i < moe::kMaxTopK; ++i) {
           if (i >= k) break;
@@ -148,6 +187,13 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(Args a) {
         const unsigned v = static_cast<unsigned>(cooc[q]);
         if (v & 0xffffu) atomicAdd(&acc_cooc[2 * q], static_cast<int32_t>(v & 0xffffu));
         if (v >> 16) atomicAdd(&acc_cooc[2 * q + 1], static_cast<int32_t>(v >> 16));
+      }
+    if (k8 && do_cooc)
+      for (int q = tid; q < (EE + 3) / 4; q += kThreads) {
+        const unsigned v = static_cast<unsigned>(cooc[q]);
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          if ((v >> (8 * b)) & 0xffu) atomicAdd(&acc_cooc[4 * q + b], static_cast<int32_t>((v >> (8 * b)) & 0xffu));
       }
     __threadfence();
     __syncthreads();
@@ -511,8 +557,12 @@ extern "C" int moe_stats(void* state, size_t state_bytes, int L, int E, int wind
   a.pred = layer + 1 < L ? pred_next : nullptr;
   a.replicas = topk_idx ? replicas : nullptr;
   a.check = topk_idx ? check : nullptr;
-  const unsigned blocks = topk_idx ? static_cast<unsigned>(std::max<int64_t>(1, ceil_div(T, kTokPerBlock))) : 1u;
-  stats_kernel<<<blocks, kThreads, 0, as_stream(stream)>>>(a);
+  // E*E beyond the 16-bit LDS counters: 8-bit counters in blocks of fewer tokens
+  const bool k8 = topk_idx && layer > 0 && E * E > 2 * kLdsCooc && E * E <= 4 * kLdsCooc;
+  const int tpb = k8 ? kTokPerBlock8 : kTokPerBlock;
+  const unsigned blocks = topk_idx ? static_cast<unsigned>(std::max<int64_t>(1, ceil_div(T, tpb))) : 1u;
+  if (k8) stats_kernel<true><<<blocks, kThreads, 0, as_stream(stream)>>>(a);
+  else stats_kernel<false><<<blocks, kThreads, 0, as_stream(stream)>>>(a);
   if (E > kSplitE) {
     const int EE = E * E;
     const int n_ring = (topk_idx && layer > 0) ? static_cast<int>(ceil_div(EE, 8 * kThreads)) : 0;

@@ -122,15 +122,16 @@ def test_stats_dsv2_replicas_large_E():
 def test_stats_cooccurrence_large_E(E, k, T):
     """Co-occurrence of a 3-layer chain where E*E exceeds 128^2: up to E = 181 a
     block's counts are kept in LDS as packed 16-bit counters (the DeepSeek-V2
-    shape at full size: 512 tokens x 36 pairs per block), from E = 182 they go to
-    global atomics; bit-exact against the oracle either way."""
+    shape at full size: 512 tokens x 36 pairs per block), from E = 182 as packed
+    8-bit counters over blocks of 255 tokens; bit-exact against the oracle
+    either way."""
     cfg = synth.CONFIGS["dsv2"].scaled(T=T, E=E, k=k, L=3, R=0, window=3, gamma=1.5)
     _run_stats_chain(cfg, 4, check_every=False)
 
 
 def test_stats_maximum_E_and_k():
     """E = 256 experts, top-8, a 3-layer chain: the largest expert count and k the
-    library accepts (co-occurrence kept in global atomics rather than LDS)."""
+    library accepts (co-occurrence in packed 8-bit LDS counters)."""
     cfg = synth.CONFIGS["dsv2"].scaled(T=900, E=256, k=8, L=3, R=100, window=4)
     _run_stats_chain(cfg, 5)
 
