@@ -129,6 +129,43 @@ def test_stats_cooccurrence_large_E(E, k, T):
     _run_stats_chain(cfg, 4, check_every=False)
 
 
+def test_stats_8bit_cooccurrence_counts_duplicates():
+    """E = 200 records the co-occurrence in packed 8-bit LDS counters over blocks
+    of 255 tokens; tokens that name an expert twice (in this layer or in the
+    previous one) count with multiplicity, through global atomics.  Bit-exact
+    against the oracle over a 3-layer chain of 3 iterations with such tokens
+    in every block."""
+    L, E, k, win, T = 3, 200, 3, 2, 700
+    state = torch.empty(moe.moe_stats_state_bytes(L, E, win), dtype=torch.uint8, device="cuda")
+    moe.moe_stats_init(state, L, E, win)
+    ost = oracle.WindowStats(L, E, win)
+    outs = {n: torch.empty(sz, dtype=d, device="cuda") for n, sz, d in
+            [("counts", E, torch.int32), ("p_seq", E, torch.float32), ("cond", (E, E), torch.float32),
+             ("pred", E, torch.float32)]}
+    rng = np.random.default_rng(11)
+    for it in range(3):
+        prev_o, prev_g = None, None
+        for layer in range(L):
+            lg = (rng.standard_normal((T, E)) - np.log1p(rng.permutation(E))).astype(np.float32)
+            idx_o = oracle.route(lg, k)[0].copy()
+            for t in (5 + it, 260 + layer, 600):          # one per block of 255 tokens
+                idx_o[t, 1] = idx_o[t, 0]
+            idx_o[261 + it] = idx_o[261 + it, 2]           # an expert named three times
+            idx_g = to_dev(idx_o)
+            last = layer + 1 >= L
+            moe.moe_stats(state, L, E, win, layer, it, idx_g, prev_g, k, outs["counts"], outs["p_seq"],
+                          None if last else outs["cond"], None if last else outs["pred"], 0, None)
+            _sync()
+            cnt = ost.record(layer, it, idx_o, prev_o)
+            assert np.array_equal(from_dev(outs["counts"]), cnt), (it, layer)
+            p, P, ph = ost.outputs(layer)
+            assert np.max(np.abs(from_dev(outs["p_seq"]) - p)) <= 1e-7
+            if not last:
+                assert np.max(np.abs(from_dev(outs["cond"]) - P)) <= 1e-7, (it, layer)
+                assert np.max(np.abs(from_dev(outs["pred"]) - ph)) <= 1e-6, (it, layer)
+            prev_o, prev_g = idx_o, idx_g
+
+
 def test_stats_maximum_E_and_k():
     """E = 256 experts, top-8, a 3-layer chain: the largest expert count and k the
     library accepts (co-occurrence in packed 8-bit LDS counters)."""
