@@ -35,7 +35,7 @@ constexpr int kSmallM = 64;   // dense path: 64-row tiles
 
 struct WsLayout {
   size_t h, tab_slot[3], tab_row0[3], tab_rend[3], n_tiles, split_slot, split_row0, split_rend, split_counts,
-      mid_slot, mid_row0, mid_rend, alt_slot, alt_row0, alt_rend, bytes;
+      mid_slot, mid_row0, mid_rend, alt_slot, alt_row0, alt_rend, steal, bytes;
   int cap[3];     // tile capacity of each table
   int split_cap;  // entries of each GEMM's 64-row companion table
 };
@@ -81,6 +81,7 @@ WsLayout ws_layout(moe_dtype dt, int64_t M, int I, int max_slots) {
   w.alt_slot = take(sizeof(int32_t) * w.cap[kG256]);  // the gate/up GEMM's 256-row table without 128-row tails
   w.alt_row0 = take(sizeof(int32_t) * w.cap[kG256]);
   w.alt_rend = take(sizeof(int32_t) * w.cap[kG256]);
+  w.steal = take(9 * kStealStride * sizeof(int32_t));  // the gate/up launch's per-XCD counters
   w.bytes = at;
   return w;
 }
@@ -276,13 +277,16 @@ int ffn_impl(const void* x_perm, const int32_t* row_src, int64_t n_src, moe_dtyp
   // floor(M / 256) + (ranges x max(1, kRemTiles)) tiles, ranges <= max_slots
   // (a range's 128-row tile takes the place of its last 256-row tile), plus 3
   // more per re-listed trailing row tile (at most ceil(256 / nt) of those),
-  // plus the rounding of the 256- and 128-row parts to 8 blocks each.
+  // plus the rounding of the 256- and 128-row parts to 8 blocks each; a mixed
+  // launch that deals its tail at run time needs kStealExtra more blocks per
+  // XCD and a block per XCD for each of the three tables' uneven shares.
   auto grid = [&](Kind t, int nt) {
     int64_t blocks;
     if (t == kG256) {
       const int64_t both = exact[kG256] >= 0 ? exact[kG256] + exact_rem
                                              : M / kBigM + static_cast<int64_t>(max_slots) * std::max(1, kRemTiles);
       blocks = both * nt + 3 * ceil_div(kWaveBlocks, nt) * nt + 16;
+      if (blocks >= kStealMinTiles) blocks += 8 * (kStealExtra + 4);  // else the launch keeps the fixed schedule
     } else {
       blocks = (exact[t] >= 0 ? exact[t] : static_cast<int64_t>(w.cap[t])) * nt;
     }
@@ -322,6 +326,8 @@ int ffn_impl(const void* x_perm, const int32_t* row_src, int64_t n_src, moe_dtyp
   split.alt_slot = reinterpret_cast<int32_t*>(ws + w.alt_slot);
   split.alt_row0 = reinterpret_cast<int32_t*>(ws + w.alt_row0);
   split.alt_rend = reinterpret_cast<int32_t*>(ws + w.alt_rend);
+  int32_t* const steal = reinterpret_cast<int32_t*>(ws + w.steal);
+  split.steal = steal;
   auto build = [&](Kind t) {
     const int mode = t == kD64 ? kPadded : kCover;
     const int bm = t == kG256 ? kBigM : kSmallM;
@@ -357,6 +363,12 @@ int ffn_impl(const void* x_perm, const int32_t* row_src, int64_t n_src, moe_dtyp
   p2.K = I;
   p2.N = H;
   p2.n_col_tiles = nt2;
+  // The gate/up launch deals its tail at run time (its 256- and 128-row tiles
+  // are short enough to even out the XCDs' clocks: 1.4-3.5% faster on the
+  // Mixtral shape in same-box A/Bs); the down GEMM keeps the fixed schedule
+  // (its tiles last longer than the XCDs drift apart, and the counters cost
+  // it 0.6%).
+  p1.steal = k1 == kG256 ? steal : nullptr;
   auto on = [&](GemmArgs& g, Kind t, int which) {
     g.tile_slot = tab_slot(t);
     g.tile_row0 = tab_row0(t);

@@ -118,6 +118,11 @@ struct GemmArgs {
   // kGatherLimit so every offset stays in 31 bits.
   const int32_t* a_rows;
   int64_t a_n;
+  // Mixed launches only: eight per-XCD counters and an all-empty word
+  // (kStealStride apart, zero at launch) that deal the last tiles of each
+  // XCD's share at run time; null: every block's tile follows from its index
+  // alone.
+  int32_t* steal;
 };
 constexpr int64_t kGatherLimit = int64_t(0x7e000000);  // bytes of a gathered A
 constexpr int kGatherOut = 0x7f000000;                 // an A offset out of range: reads zero
@@ -1124,36 +1129,113 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 template <bool kBf16, int EPI>
 constexpr bool kHasMidTiles = kBf16 && (EPI == kEpiSwiGLU || EPI == kEpiStore);
 
-// A 256-row tile table, a 128-row one and a 64-row one in one launch: the
-// first round_up(n_big * nt, 8) blocks run the 256-row tiles, the next
-// round_up(n_mid * nt, 8) the 128-row tiles (ranges' last tiles of at most 128
-// rows), the blocks after them the 64-row tiles (short ranges and re-listed
+// A 256-row tile table, a 128-row one and a 64-row one in one launch.  Block b
+// runs on XCD b mod 8 (the hardware deals blocks to the XCDs in turn), and each
+// table gives XCD x a contiguous share of its tiles (gemm_tile's raster).
+//
+// Fixed schedule (big.steal null, or a launch of fewer than kStealMinTiles
+// tiles): the first round_up(n_big * nt, 8) blocks run the 256-row tiles, the
+// next round_up(n_mid * nt, 8) the 128-row tiles (ranges' last tiles of at most
+// 128 rows), the blocks after them the 64-row tiles (short ranges and re-listed
 // trailing tiles); the roundings keep every block's index congruent to its XCD
 // in each part.  The shorter tiles are dispatched last and so fill the CUs
 // that the last round of 256-row tiles leaves idle.  Blocks past all exit.
+//
+// Balanced tail (big.steal set): the XCDs run at different clocks under load
+// (per-block timestamps: up to 8% apart on one chip), so equal shares end at
+// different times and the launch waits for the slowest XCD.  Each XCD's own
+// blocks run the first share(256-row) - kStealBig of its 256-row tiles by
+// index; its remaining tiles (those kStealBig, then its 128-row and 64-row
+// shares, in that order) form its queue, dealt by an atomic counter to its next
+// blocks in turn.  Each XCD gets kStealExtra more blocks than it has tiles;
+// a block whose own queue is empty takes the next tile of the other XCDs'
+// queues, so a faster XCD takes over the tail of a slower one.  Every queue
+// entry is handed out once (the counter's old value); a block that finds all
+// eight queues empty sets a ninth word (the queues only ever drain) and exits,
+// and the blocks after it exit on reading that word.  No block waits for
+// another.
 // WNT: weights loaded non-temporally (bf16).
+constexpr int kStealStride = 32;        // ints between two XCDs' counters (a 128-byte line each)
+constexpr int kStealBig = 32;           // 256-row tiles per XCD in its queue
+constexpr int kStealExtra = 32;         // blocks per XCD beyond its own tiles
+constexpr int kStealMinTiles = 4 * 256; // smaller launches keep the fixed schedule
+
+__device__ __forceinline__ int xcd_share(int n, int x) { return (n >> 3) + (x < (n & 7) ? 1 : 0); }
+
+// The old value of *ctr after adding add (0: a plain read), by thread 0,
+// broadcast to the block through the first word of gemm_lds (no tile has
+// started using it).
+__device__ __forceinline__ int take_next(int32_t* ctr, int add = 1) {
+  int* const word = reinterpret_cast<int*>(gemm_lds);
+  __syncthreads();  // every lane has read the previous value
+  if (threadIdx.x == 0) *word = atomicAdd(ctr, add);
+  __syncthreads();
+  return __builtin_amdgcn_readfirstlane(*word);
+}
+
 template <bool kBf16, int NMAT, int EPI, bool WNT = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_mixed_kernel(GemmArgs big,
                                                                                                    GemmArgs mid,
                                                                                                    GemmArgs small) {
   static_assert(gemm_lds_bytes<kBf16, NMAT, EPI, 256, 2, false>() <= kGemmLdsBytes, "LDS");
   static_assert(gemm_lds_bytes<kBf16, NMAT, EPI, 64, 1, false>() <= kGemmLdsBytes, "LDS");
-  const int nb = (*big.n_tiles * big.n_col_tiles + 7) & ~7;
+  constexpr bool kMid = kHasMidTiles<kBf16, EPI>;
+  const int tb = *big.n_tiles * big.n_col_tiles;
+  const int tm = kMid ? *mid.n_tiles * mid.n_col_tiles : 0;
+  const int ts = *small.n_tiles * small.n_col_tiles;
   const int b = static_cast<int>(blockIdx.x);
-  if (b < nb) {
-    gemm_tile<kBf16, NMAT, EPI, 256, 2, false, 0, WNT>(big, b);
+  int table, bt;  // 0: 256-row, 1: 128-row, 2: 64-row table; the block index gemm_tile reads in it
+  if (big.steal && tb + tm + ts >= kStealMinTiles) {
+    const int x = b & 7, j = b >> 3;  // this block's XCD and its place in that XCD's order
+    const int D = min(kStealBig, tb >> 3);
+    const int fixed = xcd_share(tb, x) - D;
+    if (j < fixed) {
+      table = 0;
+      bt = b;
+    } else {
+      auto qlen = [&](int y) { return D + xcd_share(tm, y) + xcd_share(ts, y); };
+      if (j >= fixed + qlen(x) + kStealExtra) return;
+      int y = x, q = take_next(big.steal + x * kStealStride);  // own queue first
+      bool got = q < qlen(x);
+      if (!got && take_next(big.steal + 8 * kStealStride, 0) == 0) {  // then the others', unless all are empty
+        for (int t = 1; t < 8 && !got; ++t) {
+          y = (x + t) & 7;
+          q = take_next(big.steal + y * kStealStride);
+          got = q < qlen(y);
+        }
+        if (!got && threadIdx.x == 0) atomicExch(big.steal + 8 * kStealStride, 1);
+      }
+      __syncthreads();  // the broadcast word is read before the tile's stages overwrite it
+      if (!got) return;
+      // entry q of XCD y's queue, as the block index that maps to it in its table
+      if (q < D) {
+        table = 0;
+        bt = 8 * (xcd_share(tb, y) - D + q) + y;
+      } else if (q - D < xcd_share(tm, y)) {
+        table = 1;
+        bt = 8 * (q - D) + y;
+      } else {
+        table = 2;
+        bt = 8 * (q - D - xcd_share(tm, y)) + y;
+      }
+    }
+  } else {
+    const int nb = (tb + 7) & ~7, nm = (tm + 7) & ~7;
+    table = b < nb ? 0 : (kMid && b < nb + nm) ? 1 : 2;
+    bt = table == 0 ? b : table == 1 ? b - nb : b - nb - nm;
+  }
+  if (table == 0) {
+    gemm_tile<kBf16, NMAT, EPI, 256, 2, false, 0, WNT>(big, bt);
     return;
   }
-  int nm = 0;
-  if constexpr (kHasMidTiles<kBf16, EPI>) {
+  if constexpr (kMid) {
     static_assert(gemm_lds_bytes<kBf16, NMAT, EPI, 128, 1, false>() <= kGemmLdsBytes, "LDS");
-    nm = (*mid.n_tiles * mid.n_col_tiles + 7) & ~7;
-    if (b < nb + nm) {
-      gemm_tile<kBf16, NMAT, EPI, 128, 1, false, 0, WNT>(mid, b - nb);
+    if (table == 1) {
+      gemm_tile<kBf16, NMAT, EPI, 128, 1, false, 0, WNT>(mid, bt);
       return;
     }
   }
-  gemm_tile<kBf16, NMAT, EPI, 64, 1, false, 0, WNT>(small, b - nb - nm);
+  gemm_tile<kBf16, NMAT, EPI, 64, 1, false, 0, WNT>(small, bt);
 }
 
 // Lists the row tiles of the GEMMs.  With `merge`, consecutive slots of one
@@ -1203,6 +1285,9 @@ struct TileSplit {
   int32_t* alt_slot;
   int32_t* alt_row0;
   int32_t* alt_rend;
+  // a mixed launch's per-XCD counters and all-empty word (nine words,
+  // kStealStride apart), set to zero here before the launch; null: none
+  int32_t* steal;
 };
 constexpr int kWaveBlocks = 256;  // one block per CU
 
@@ -1233,6 +1318,7 @@ __global__ __launch_bounds__(256) void tiles_kernel(const int32_t* __restrict__ 
   const int rem_tiles = companion ? split.rem_tiles : 0;
   const int mid_rows = companion ? split.mid_rows : 0;
   const bool staged = n <= kLdsSlots;
+  if (companion && split.steal != nullptr && tid < 9) atomicExch(split.steal + tid * kStealStride, 0);
   if (staged) {
     for (int i = tid; i < n; i += 256) se_lds[i] = slot_expert[i];
     for (int i = tid; i <= n; i += 256) so_lds[i] = slot_off[i];
