@@ -92,6 +92,50 @@ def _run_stats_chain(cfg, iters, check_every=True):
     return state, ost
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 5, 6, 7, 8])
+def test_combine_every_k(dt, k):
+    """moe_combine on its own against the oracle's combine (an fp64 sum over the
+    k slots, rounded once) for every k: 700 tokens of a ragged row width (H =
+    200: 25 bf16 chunks or 50 fp32 chunks of 16 bytes, not a multiple of the
+    four chunks a thread takes), random gate weights and rows.  The kernel sums
+    in fp32 FMAs in slot order, so an element may differ from the oracle by the
+    fp32 chain's error, at most (k + 1) 2^-24 sum_i |w_i y_i| before the output
+    rounding (bf16: one unit in the last place of the output on top)."""
+    rng = np.random.default_rng(100 + k)
+    T, H, M = 700, 200, 1500
+    y32 = rng.standard_normal((M, H)).astype(np.float32)
+    y = synth.f32_to_bf16_bits(y32) if dt == "bf16" else y32
+    yv = f64(y)
+    inv = np.stack([rng.choice(M, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    w = rng.dirichlet(np.ones(k), size=T).astype(np.float32)
+    got = from_dev(moe.moe_combine(to_dev(y), to_dev(inv), to_dev(w)))
+    ref = oracle.combine(y, inv, w)
+    g, r = f64(got), f64(ref)
+    mag = np.einsum("tk,tkh->th", np.abs(w.astype(np.float64)), np.abs(yv[inv]))
+    bound = (k + 1) * 2.0 ** -24 * mag
+    if dt == "bf16":  # plus one bf16 unit of the larger magnitude
+        bound += 2.0 ** (np.floor(np.log2(np.maximum(np.maximum(np.abs(g), np.abs(r)), 1e-30))) - 7)
+    assert np.all(np.abs(g - r) <= bound), float(np.max(np.abs(g - r) - bound))
+
+
+@pytest.mark.parametrize("k", [2, 3, 8])
+def test_combine_skips_rows_outside_y(k):
+    """A slot whose row index lies outside [0, M) adds nothing: the output equals
+    the combine with that slot given weight 0 on a valid row, bit for bit."""
+    rng = np.random.default_rng(7 + k)
+    T, H, M = 300, 4096, 900
+    y = synth.f32_to_bf16_bits(rng.standard_normal((M, H)).astype(np.float32))
+    inv = np.stack([rng.choice(M, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    w = rng.dirichlet(np.ones(k), size=T).astype(np.float32)
+    drop = rng.random((T, k)) < 0.25
+    inv_bad = np.where(drop, np.where(rng.random((T, k)) < 0.5, -1, M + 5), inv).astype(np.int32)
+    w0 = np.where(drop, 0.0, w).astype(np.float32)
+    a = from_dev(moe.moe_combine(to_dev(y), to_dev(inv_bad), to_dev(w)))
+    b = from_dev(moe.moe_combine(to_dev(y), to_dev(inv), to_dev(w0)))
+    assert np.array_equal(a, b)
+
+
 def test_stats_tiny_chain_window():
     cfg = synth.CONFIGS["tiny"]
     state, ost = _run_stats_chain(cfg, 14)   # wraps the 10-slot ring
