@@ -328,7 +328,10 @@ int moe_dispatch_noalloc(const void* x, moe_dtype dt, int64_t T, int H, const in
  *              row copy (x_perm NULL there) feeds the FFN directly.  Entries
  *              outside [0, n_src) read as zero rows.  n_src * H * sizeof(dt)
  *              must stay below 0x7e000000 bytes (MOE_ERR_UNSUPPORTED).
- *   workspace  at least moe_expert_ffn_workspace_bytes(...) bytes.
+ *   workspace  at least moe_expert_ffn_workspace_bytes(...) bytes: h, the
+ *              tile tables and the counters that deal the gate/up launch's
+ *              last tiles, all rewritten by every call, so two calls in
+ *              flight at once (on different streams) need two workspaces.
  * Limits: dtype F32 or BF16; H and I multiples of 64; E <= max_slots;
  * M <= 2^31 - 1; rows referenced by slot_off lie in [0, M) (rows outside it
  * are clamped away).
