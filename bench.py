@@ -800,7 +800,7 @@ def vs_hipblaslt(moe, torch, np, reps=10):
 def main():
     a = parse()
     if a.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
+        print(json.dumps({"error": "the library runs on one GPU; --gpus must be 1 "
                                    "(the multi-GPU sharding is a design note, not built)"}))
         sys.exit(2)
 

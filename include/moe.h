@@ -58,7 +58,7 @@ extern "C" {
 typedef enum {
     MOE_OK = 0,
     MOE_ERR_INVALID_ARG = -1, /* null pointer, negative size, k > E, misalignment ... */
-    MOE_ERR_UNSUPPORTED = -2, /* valid but outside this build's limits (E > 256, H % 64 ...) */
+    MOE_ERR_UNSUPPORTED = -2, /* valid but outside the library's limits (E > 256, H % 64 ...) */
     MOE_ERR_WORKSPACE = -3,   /* workspace or state smaller than the *_bytes query says */
     MOE_ERR_HIP = -4,         /* a HIP runtime call failed; moe_last_error() has its text */
     MOE_ERR_DEVICE_CHECK = -5 /* moe_check_device_error: the kernels flagged invalid input */

@@ -20,7 +20,7 @@ inline int elem_bytes(moe_dtype dt) { return dt == MOE_BF16 ? 2 : 4; }
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-// Upper bounds of this build.
+// Upper bounds of the library.
 constexpr int kMaxExperts = 256;
 constexpr int kMaxTopK = 8;
 

@@ -29,7 +29,7 @@ extern "C" const char* moe_status_string(int status) {
   switch (status) {
     case MOE_OK: return "ok";
     case MOE_ERR_INVALID_ARG: return "invalid argument";
-    case MOE_ERR_UNSUPPORTED: return "unsupported by this build";
+    case MOE_ERR_UNSUPPORTED: return "unsupported by this library";
     case MOE_ERR_WORKSPACE: return "workspace or state too small";
     case MOE_ERR_HIP: return "HIP runtime error";
     case MOE_ERR_DEVICE_CHECK: return "the device check flagged invalid input";
