@@ -877,7 +877,6 @@ def main():
     def evict(i):
         torch.sum(flush, 0, out=flush_out)
 
-    spin = spin_cycles(torch, stream, 1.5)
 
     def make_layer(R_):
         state = torch.empty(moe.moe_stats_state_bytes(L, E, win), dtype=torch.uint8, device=dev)
@@ -889,6 +888,20 @@ def main():
                                          stats_dims=(L, E, win), layer=1, it=i, prev_topk_idx=prev_idx,
                                          path=a.path, bufs=bufs, stream=stream, ffn_events=ffn_events)
         return step, state, bufs
+
+    def host_issue_ms(step, first, n=5):
+        """Host time to issue one step, median of n; a GPU-side spin keeps the GPU
+        busy meanwhile, so no call of the step waits for it."""
+        busy = spin_cycles(torch, stream, 5.0)
+        ts = []
+        for i in range(n):
+            torch.cuda.synchronize()
+            torch.cuda._sleep(busy)
+            t = time.perf_counter()
+            step(first + i)
+            ts.append(time.perf_counter() - t)
+        torch.cuda.synchronize()
+        return float(np.median(ts)) * 1e3
 
     def timed_cold(step, K, first):
         """K steps, each on flushed caches: the 512 MiB flush, then a GPU-side spin
@@ -924,6 +937,15 @@ def main():
     for i in range(a.warmup):
         step(i)
     torch.cuda.synchronize()
+    # The spin before each cold step only has to outlast the host's issuing of
+    # that step: twice its measured issue time, at least 0.3 ms.  A longer idle
+    # spin is not neutral: the chip's power management raises the clock while
+    # it idles and pulls it back a few milliseconds into the step (a 1.5 ms
+    # spin made the cold step 3-4% slower, all of it in the down GEMM, which
+    # starts 3 ms into the step; back-to-back warm steps do not see it).
+    issue_ms = host_issue_ms(step, 10 ** 5)
+    spin_ms = max(0.3, 2.0 * issue_ms)
+    spin = spin_cycles(torch, stream, spin_ms)
     # Timed region: exactly K steps (the headline: cold caches before every step).
     ms_step, gateup_ms, down_ms, wall = timed_cold(step, a.steps, a.warmup)
     ms_warm = timed_warm(step, a.steps, a.warmup + a.steps)
@@ -943,7 +965,7 @@ def main():
     names = ["route", "stats", "dispatch", "expert_ffn", "combine"]
     samples = {n: [] for n in names}
     cold = {n: [] for n in names}
-    spin3 = spin_cycles(torch, stream, 3.0)
+    spin3 = spin
     for rep in range(10):
         phase_ev = [TimingEvent() for _ in range(6)]
         if rep >= 5:
@@ -993,7 +1015,8 @@ def main():
         "config": {"workload": "Mixtral-8x7B-shaped MoE layer", "T": T, "H": H, "I": I, "E": E, "k": k,
                    "act": "swiglu", "replica_budget": R, "slots_used": n_slots, "window": win,
                    "gemm_path": a.path, "stats_chain_layers": L,
-                   "timing": "cold: L2 and MALL flushed (512 MiB read) before every timed step"},
+                   "timing": "cold: L2 and MALL flushed (512 MiB read) before every timed step",
+                   "spin_ms": round(spin_ms, 3), "host_issue_ms": round(issue_ms, 3)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "kernel": "fused gate/up grouped GEMM (SwiGLU epilogue)",
