@@ -256,6 +256,9 @@ int moe_prediction_quality(const float* pred, const int32_t* counts, int E, cons
  * pair's rank among the block's pairs of its expert (wave ballots); one block
  * turning the block counts into offsets, the replica plan (replica_budget)
  * and the slot table; the row copy, which also writes perm_src and inv_pos.
+ * Small dispatches (T*k <= 1024 and E <= 64) take one launch instead, one
+ * block doing all three steps (plus the row copy when x_perm is given), and
+ * leave the workspace untouched; the results are the same.
  * check: MOE_CHECK_INDEX (an index outside [0, E): inv_pos = -1, no row),
  * MOE_CHECK_DUPLICATE, MOE_CHECK_COUNTS, MOE_CHECK_REPLICAS.
  * Limits: 1 <= E <= 256, 1 <= k <= min(E, 8), T*k < 2^31, E <= max_slots,
@@ -280,7 +283,8 @@ int moe_dispatch(const void* x, moe_dtype dt, int64_t T, int H, const int32_t* t
  * MOE_ERR_WORKSPACE.  Every call on one GPU shares the array: calls that
  * overlap on one GPU (different streams, or threads) race and must be
  * serialised by the caller.  Nothing in it needs clearing between calls (each
- * call writes every word it reads).  Same results as moe_dispatch.
+ * call writes every word it reads).  Same results as moe_dispatch; the small
+ * dispatches that moe_dispatch runs in one block do not touch the array.
  */
 int moe_dispatch_noalloc(const void* x, moe_dtype dt, int64_t T, int H, const int32_t* topk_idx, int k, int E,
                          const int32_t* counts, const int32_t* replicas, int replica_budget, int max_slots,

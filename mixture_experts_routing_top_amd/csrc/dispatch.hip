@@ -9,7 +9,9 @@
 //
 // The (token, slot) pairs are numbered f = t*k + i; inside an expert the rows
 // follow ascending f (ascending token index; a token naming one expert twice
-// gets two rows in slot order).  Three launches, no host sync:
+// gets two rows in slot order).  Small dispatches (up to 1024 pairs over up to
+// 64 experts) run in one launch (dispatch_small_kernel, plus the copy when
+// asked for); the others in three launches, no host sync:
 //   1. rank:    per block of kPairs pairs, its per-expert counts (into a
 //               [blocks, E] table) and each pair's rank among the block's
 //               pairs of the same expert: wave ballots over the distinct
@@ -126,6 +128,72 @@ __device__ void block_scan_inclusive(int64_t* v, int n) {
   }
 }
 
+// The expert totals `tot` (LDS) become the layer's offsets and slot table:
+// the replica plan from the totals when asked for (plan_budget), expert_off,
+// the slot table, and with a check word the totals against `counts` and the
+// replicas against the slot budget.  Leaves off[e] = inclusive prefix of the
+// totals (LDS) for the caller.  Every thread of the block takes part.
+__device__ void offsets_and_slots(const int32_t* tot, int64_t* off, int64_t* rep, int32_t* want_s, int E, int64_t P,
+                                  const int32_t* __restrict__ counts, const int32_t* __restrict__ replicas,
+                                  int plan_budget, int max_slots, int32_t* __restrict__ expert_off,
+                                  int32_t* __restrict__ slot_off, int32_t* __restrict__ slot_expert,
+                                  int32_t* __restrict__ n_slots, int32_t* __restrict__ check) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  if (tid < E) {
+    off[tid] = tot[tid];
+    want_s[tid] = replicas ? replicas[tid] : 0;
+  }
+  __syncthreads();
+  // this routing's replica plan (wave 0: 64 lanes x 4 experts; total = T*k)
+  if (plan_budget > 0 && tid < 64) {
+    int64_t n[4];
+    int r[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) n[j] = tid + 64 * j < E ? tot[tid + 64 * j] : 0;
+    moe::plan_replicas_wave(n, E, P, plan_budget, tid, r);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (tid + 64 * j < E) want_s[tid + 64 * j] = r[j];
+  }
+  __syncthreads();
+  if (tid < E) rep[tid] = max(want_s[tid], 0);
+  __syncthreads();
+  // exclusive prefixes: expert offsets and replica counts
+  block_scan_inclusive(off, E);
+  block_scan_inclusive(rep, E);
+  const int32_t M = E > 0 ? static_cast<int32_t>(off[E - 1]) : 0;
+  // expert offsets and the slot table
+  const int64_t budget = max_slots - E;
+  bool bad_counts = false, bad_reps = false;
+  for (int x = tid; x < E; x += nt) {
+    const int64_t excl = off[x] - tot[x];
+    expert_off[x] = static_cast<int32_t>(excl);
+    const int64_t want = max(want_s[x], 0);
+    const int64_t rp = rep[x] - want;  // copies of experts before x
+    const int64_t r = max<int64_t>(0, min<int64_t>(want, budget - rp));
+    const int64_t s0 = x + min<int64_t>(rp, budget);
+    const int64_t n = tot[x];
+    for (int64_t rho = 0; rho <= r; ++rho) {
+      slot_expert[s0 + rho] = x;
+      slot_off[s0 + rho] = static_cast<int32_t>(excl + (rho * n) / (r + 1));
+    }
+    bad_counts |= counts && counts[x] != tot[x];
+    bad_reps |= want_s[x] < 0 || r < want;
+  }
+  if (tid == 0) expert_off[E] = M;
+  const int64_t all = E > 0 ? rep[E - 1] : 0;
+  const int64_t used = E + min<int64_t>(all, budget);
+  for (int64_t q = used + tid; q <= max_slots; q += nt) {
+    slot_off[q] = M;
+    if (q < max_slots) slot_expert[q] = 0;
+  }
+  if (tid == 0) n_slots[0] = static_cast<int32_t>(used);
+  if (check) {
+    raise_check(check, bad_counts, MOE_CHECK_COUNTS);
+    raise_check(check, bad_reps, MOE_CHECK_REPLICAS);
+  }
+}
+
 template <int kScanThreads>
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(const int32_t* __restrict__ blk_cnt, int nblk, int E,
                                                         int64_t P, const int32_t* __restrict__ counts,
@@ -164,28 +232,10 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(const int32_t* __res
     int32_t t = 0;
     for (int q = 0; q < G; ++q) t += part[q * E + tid];
     tot[tid] = t;
-    off[tid] = t;
-    want_s[tid] = replicas ? replicas[tid] : 0;
   }
   __syncthreads();
-  // this routing's replica plan (wave 0: 64 lanes x 4 experts; total = T*k)
-  if (plan_budget > 0 && tid < 64) {
-    int64_t n[4];
-    int r[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) n[j] = tid + 64 * j < E ? tot[tid + 64 * j] : 0;
-    moe::plan_replicas_wave(n, E, P, plan_budget, tid, r);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (tid + 64 * j < E) want_s[tid + 64 * j] = r[j];
-  }
-  __syncthreads();
-  if (tid < E) rep[tid] = max(want_s[tid], 0);
-  __syncthreads();
-  // exclusive prefixes: expert offsets and replica counts
-  block_scan_inclusive(off, E);
-  block_scan_inclusive(rep, E);
-  const int32_t M = E > 0 ? static_cast<int32_t>(off[E - 1]) : 0;
+  offsets_and_slots(tot, off, rep, want_s, E, P, counts, replicas, plan_budget, max_slots, expert_off, slot_off,
+                    slot_expert, n_slots, check);
   // group prefix of each column, then this group's blocks
   if (g < G) {
     int32_t run = static_cast<int32_t>(off[e] - tot[e]);
@@ -201,35 +251,128 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(const int32_t* __res
       }
     }
   }
-  // expert offsets and the slot table
-  const int64_t budget = max_slots - E;
-  bool bad_counts = false, bad_reps = false;
-  for (int x = tid; x < E; x += kScanThreads) {
-    const int64_t excl = off[x] - tot[x];
-    expert_off[x] = static_cast<int32_t>(excl);
-    const int64_t want = max(want_s[x], 0);
-    const int64_t rp = rep[x] - want;  // copies of experts before x
-    const int64_t r = max<int64_t>(0, min<int64_t>(want, budget - rp));
-    const int64_t s0 = x + min<int64_t>(rp, budget);
-    const int64_t n = tot[x];
-    for (int64_t rho = 0; rho <= r; ++rho) {
-      slot_expert[s0 + rho] = x;
-      slot_off[s0 + rho] = static_cast<int32_t>(excl + (rho * n) / (r + 1));
+}
+
+// Small dispatches (at most kSmallPairs pairs, at most kSmallExperts experts)
+// in one launch of one block, where the three launches below would cost more
+// in launch latency than they do work.  Wave w takes a contiguous run of C
+// pairs (C a multiple of 64, 16 C >= P), so the pairs keep their ascending
+// order as (wave, round of 64, lane).  Each wave counts its run's experts with
+// one ballot per distinct expert of a round, lane v keeping expert v's count in
+// a register (E <= 64); the block turns the totals into offsets and slots
+// (offsets_and_slots); each expert's column of the [wave, expert] table of
+// counts becomes the first row of each wave's pairs of that expert; and each
+// wave ranks its run again with the same ballots, lane v holding and advancing
+// the wave's next row of expert v.  The rows are those of the three-launch
+// path, with no workspace.
+constexpr int kSmallThreads = 1024;
+constexpr int kSmallWaves = kSmallThreads / 64;
+// rounds of 64 pairs per wave: one.  A round costs each wave one ballot per
+// distinct expert of its 64 pairs, twice, and the block's 16 waves share one CU
+// where the three-launch path spreads its rank blocks over many: measured per
+// call, T*k = 512 and 1024 (E = 8) took 8.5 and 9.7 us against 12.3 and 13.1 us
+// in three launches, T*k = 4096 took 14.8 / 25.5 / 23.9 us (E = 8 / 32 / 64)
+// against 14.2 / 19.6 / 13.1 us.
+constexpr int kSmallRounds = 1;
+constexpr int64_t kSmallPairs = int64_t(kSmallThreads) * kSmallRounds;
+constexpr int kSmallExperts = 64;  // a round's ballots are at most min(E, 64)
+
+__global__ __launch_bounds__(kSmallThreads) void dispatch_small_kernel(
+    const int32_t* __restrict__ idx, int64_t P, int k, int E, const int32_t* __restrict__ counts,
+    const int32_t* __restrict__ replicas, int plan_budget, int max_slots, int32_t* __restrict__ expert_off,
+    int32_t* __restrict__ slot_off, int32_t* __restrict__ slot_expert, int32_t* __restrict__ n_slots,
+    int32_t* __restrict__ perm_src, int32_t* __restrict__ inv_pos, int32_t* __restrict__ check) {
+  __shared__ int64_t off[moe::kMaxExperts];
+  __shared__ int64_t rep[moe::kMaxExperts];
+  __shared__ int32_t tot[moe::kMaxExperts];
+  __shared__ int32_t want_s[moe::kMaxExperts];
+  __shared__ int32_t wtab[kSmallWaves][kSmallExperts];  // per wave: its counts, then its next rows
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  for (int q = tid; q < kSmallWaves * kSmallExperts; q += kSmallThreads) (&wtab[0][0])[q] = 0;
+  const int C = static_cast<int>((P + kSmallThreads - 1) / kSmallThreads) * 64;  // pairs per wave
+  const int rounds = C / 64;                                                      // <= kSmallRounds
+  int ev[kSmallRounds];
+  bool bad_index = false, bad_dup = false;
+#pragma unroll
+  for (int r = 0; r < kSmallRounds; ++r) {
+    const int64_t f = static_cast<int64_t>(w) * C + r * 64 + lane;
+    int e = -1;
+    if (r < rounds && f < P) {
+      e = idx[f];
+      if (e < 0 || e >= E) {
+        bad_index = true;
+        e = -1;
+      } else if (check) {
+        const int64_t t = f / k;
+        for (int64_t j = t * k; j < f; ++j) bad_dup |= idx[j] == e;
+      }
     }
-    bad_counts |= counts && counts[x] != tot[x];
-    bad_reps |= want_s[x] < 0 || r < want;
+    ev[r] = e;
   }
-  if (tid == 0) expert_off[E] = M;
-  const int64_t all = E > 0 ? rep[E - 1] : 0;
-  const int64_t used = E + min<int64_t>(all, budget);
-  for (int64_t q = used + tid; q <= max_slots; q += kScanThreads) {
-    slot_off[q] = M;
-    if (q < max_slots) slot_expert[q] = 0;
+  __syncthreads();
+  const uint64_t lt = (uint64_t(1) << lane) - 1;
+  // pass 1: this wave's counts, lane v counting expert v (E <= 64) in a register
+  int32_t cnt = 0;
+#pragma unroll
+  for (int r = 0; r < kSmallRounds; ++r) {
+    const int e = ev[r];
+    uint64_t todo = __ballot(e >= 0);
+    while (todo) {
+      const int leader = __ffsll(static_cast<unsigned long long>(todo)) - 1;
+      const int v = __builtin_amdgcn_readlane(e, leader);
+      const uint64_t m = __ballot(e == v);
+      if (lane == v) cnt += __popcll(m);
+      todo &= ~m;
+    }
   }
-  if (tid == 0) n_slots[0] = static_cast<int32_t>(used);
+  if (lane < E) wtab[w][lane] = cnt;
+  __syncthreads();
+  for (int x = tid; x < E; x += kSmallThreads) {
+    int32_t t = 0;
+#pragma unroll
+    for (int v = 0; v < kSmallWaves; ++v) t += wtab[v][x];
+    tot[x] = t;
+  }
+  __syncthreads();
+  offsets_and_slots(tot, off, rep, want_s, E, P, counts, replicas, plan_budget, max_slots, expert_off, slot_off,
+                    slot_expert, n_slots, check);
+  // each expert's column: the first row of every wave's pairs of that expert
+  for (int x = tid; x < E; x += kSmallThreads) {
+    int32_t row = static_cast<int32_t>(off[x] - tot[x]);
+#pragma unroll
+    for (int v = 0; v < kSmallWaves; ++v) {
+      const int32_t c = wtab[v][x];
+      wtab[v][x] = row;
+      row += c;
+    }
+  }
+  __syncthreads();
+  // pass 2: this wave's rows, in pair order; lane v holds the wave's next row
+  // of expert v
+  int32_t next = lane < E ? wtab[w][lane] : 0;
+#pragma unroll
+  for (int r = 0; r < kSmallRounds; ++r) {
+    const int64_t f = static_cast<int64_t>(w) * C + r * 64 + lane;
+    const int e = ev[r];
+    int32_t row = -1;
+    uint64_t todo = __ballot(e >= 0);
+    while (todo) {
+      const int leader = __ffsll(static_cast<unsigned long long>(todo)) - 1;
+      const int v = __builtin_amdgcn_readlane(e, leader);
+      const uint64_t m = __ballot(e == v);
+      const int32_t base = __builtin_amdgcn_readlane(next, v);
+      if (e == v) row = base + __popcll(m & lt);
+      if (lane == v) next += __popcll(m);
+      todo &= ~m;
+    }
+    if (r < rounds && f < P) {
+      inv_pos[f] = row;
+      if (row >= 0) perm_src[row] = static_cast<int32_t>(f / k);
+    }
+  }
   if (check) {
-    raise_check(check, bad_counts, MOE_CHECK_COUNTS);
-    raise_check(check, bad_reps, MOE_CHECK_REPLICAS);
+    raise_check(check, bad_index, MOE_CHECK_INDEX);
+    raise_check(check, bad_dup, MOE_CHECK_DUPLICATE);
   }
 }
 
@@ -240,6 +383,9 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(const int32_t* __res
 constexpr int kChunksPerThread = 4;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
+// kFromInv: the rows come from inv_pos, which dispatch_small_kernel has written
+// (as it has perm_src); blk_base and rank are not read.
+template <bool kFromInv>
 __global__ __launch_bounds__(256) void permute_kernel(const uint4* __restrict__ x, int64_t T, int chunks, int k, int E,
                                                       const int32_t* __restrict__ idx,
                                                       const int32_t* __restrict__ blk_base,
@@ -258,11 +404,16 @@ __global__ __launch_bounds__(256) void permute_kernel(const uint4* __restrict__ 
   }
   for (int i = 0; i < k; ++i) {
     const int64_t f = t * k + i;
-    const int e = idx[f];
-    const int32_t r = (e >= 0 && e < E) ? blk_base[(f / kPairs) * E + e] + rank[f] : -1;
-    if (c0 == 0) {
-      inv_pos[f] = r;
-      if (r >= 0) perm_src[r] = static_cast<int32_t>(t);
+    int32_t r;
+    if constexpr (kFromInv) {
+      r = inv_pos[f];
+    } else {
+      const int e = idx[f];
+      r = (e >= 0 && e < E) ? blk_base[(f / kPairs) * E + e] + rank[f] : -1;
+      if (c0 == 0) {
+        inv_pos[f] = r;
+        if (r >= 0) perm_src[r] = static_cast<int32_t>(t);
+      }
     }
     if (r < 0) continue;
     uint4* dst = x_perm + static_cast<int64_t>(r) * chunks;
@@ -355,6 +506,18 @@ extern "C" int moe_dispatch(const void* x, moe_dtype dt, int64_t T, int H, const
   int32_t* blk_base = reinterpret_cast<int32_t*>(ws + w.base);
   int32_t* rank = reinterpret_cast<int32_t*>(ws + w.rank);
   const int64_t P = T * k;
+  const int chunks = static_cast<int>(static_cast<int64_t>(H) * elem_bytes(dt) / 16);
+  const int64_t copy_threads = T * ceil_div(chunks, kChunksPerThread);
+  if (P <= kSmallPairs && E <= kSmallExperts) {
+    dispatch_small_kernel<<<1, kSmallThreads, 0, s>>>(topk_idx, P, k, E, counts, replicas, replica_budget, max_slots,
+                                                      expert_off, slot_off, slot_expert, n_slots, perm_src, inv_pos,
+                                                      check);
+    if (T > 0 && x_perm)
+      permute_kernel<true><<<static_cast<unsigned>(ceil_div(copy_threads, 256)), 256, 0, s>>>(
+          static_cast<const uint4*>(x), T, chunks, k, E, topk_idx, nullptr, nullptr, perm_src, inv_pos,
+          static_cast<uint4*>(x_perm));
+    return hip_status(hipGetLastError(), "moe_dispatch launch");
+  }
   const int nblk = static_cast<int>(ceil_div(P, kPairs));
   if (nblk > 0) rank_kernel<<<nblk, kThreads, 0, s>>>(topk_idx, P, k, E, blk_cnt, rank, check);
   if (static_cast<int64_t>(nblk) * E > kWideScan)
@@ -364,9 +527,7 @@ extern "C" int moe_dispatch(const void* x, moe_dtype dt, int64_t T, int H, const
     scan_kernel<256><<<1, 256, 0, s>>>(blk_cnt, nblk, E, P, counts, replicas, replica_budget, max_slots, blk_base,
                                        expert_off, slot_off, slot_expert, n_slots, check);
   if (T > 0 && x_perm) {
-    const int chunks = static_cast<int>(static_cast<int64_t>(H) * elem_bytes(dt) / 16);
-    const int64_t threads = T * ceil_div(chunks, kChunksPerThread);
-    permute_kernel<<<static_cast<unsigned>(ceil_div(threads, 256)), 256, 0, s>>>(
+    permute_kernel<false><<<static_cast<unsigned>(ceil_div(copy_threads, 256)), 256, 0, s>>>(
         static_cast<const uint4*>(x), T, chunks, k, E, topk_idx, blk_base, rank, perm_src, inv_pos,
         static_cast<uint4*>(x_perm));
   } else if (T > 0) {

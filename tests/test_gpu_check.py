@@ -88,13 +88,15 @@ def test_stats_flags_out_of_range_and_duplicate_indices():
     assert np.array_equal(from_dev(counts), np.bincount(valid, minlength=E))
 
 
-def test_dispatch_duplicate_indices_match_the_oracle():
+# T*k up to 1024 (at most 64 experts) runs the one-block dispatch, above it the three-launch path
+@pytest.mark.parametrize("T", [200, 4400])
+def test_dispatch_duplicate_indices_match_the_oracle(T):
     """A token naming one expert twice gets two rows in slot order (the stable
     order of the flattened pairs, as the oracle defines it), and is flagged."""
-    T, E, k, H = 513, 16, 4, 64
+    E, k, H = 16, 4, 64
     idx = oracle.route(_logits(T, E, 5), k)[0]
     idx[0] = [3, 3, 3, 1]
-    idx[200] = [7, 2, 7, 2]
+    idx[T // 2] = [7, 2, 7, 2]
     x = synth.f32_to_bf16_bits(np.random.default_rng(0).standard_normal((T, H)).astype(np.float32))
     word = _word()
     d = moe.moe_dispatch(to_dev(x), to_dev(idx), E, None, E, check=word)
@@ -105,17 +107,18 @@ def test_dispatch_duplicate_indices_match_the_oracle():
     assert np.array_equal(from_dev(d["x_perm"]), oracle.permute(x, ref["perm_src"]))
 
 
-def test_dispatch_skips_out_of_range_indices():
-    T, E, k, H = 700, 8, 2, 32
+@pytest.mark.parametrize("T", [300, 9000])
+def test_dispatch_skips_out_of_range_indices(T):
+    E, k, H = 8, 2, 32
     idx = oracle.route(_logits(T, E, 6), k)[0]
     idx[10, 1] = E
-    idx[600, 0] = -7
+    idx[T - 100, 0] = -7
     x = np.random.default_rng(1).standard_normal((T, H)).astype(np.float32)
     word = _word()
     d = moe.moe_dispatch(to_dev(x), to_dev(idx), E, None, E, check=word)
     assert _bits(word) == B["index"]
     inv = from_dev(d["inv_pos"])
-    assert inv[10, 1] == -1 and inv[600, 0] == -1
+    assert inv[10, 1] == -1 and inv[T - 100, 0] == -1
     # the valid pairs: stable order by expert, then pair index
     flat = idx.ravel()
     ok = np.flatnonzero((flat >= 0) & (flat < E))
@@ -127,8 +130,9 @@ def test_dispatch_skips_out_of_range_indices():
     assert np.array_equal(from_dev(d["x_perm"])[:n], x[order // k])
 
 
-def test_dispatch_flags_counts_and_replica_budget():
-    T, E, k = 256, 8, 2
+@pytest.mark.parametrize("T", [256, 8500])
+def test_dispatch_flags_counts_and_replica_budget(T):
+    E, k = 8, 2
     idx = oracle.route(_logits(T, E, 7), k)[0]
     n = np.bincount(idx.ravel(), minlength=E).astype(np.int32)
     x = to_dev(np.zeros((T, 8), np.float32))

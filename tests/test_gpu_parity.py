@@ -221,7 +221,13 @@ def test_stats_maximum_E_and_k():
 @pytest.mark.parametrize("T,E,k,H,dt,R", [(256, 8, 2, 64, "f32", 4), (1000, 160, 6, 96, "bf16", 0),
                                           (513, 16, 4, 64, "bf16", 16), (1, 8, 2, 8, "bf16", 3),
                                           (300, 32, 2, 40, "f32", 5), (4100, 8, 2, 128, "bf16", 8),
-                                          (777, 256, 8, 64, "bf16", 64)])
+                                          (777, 256, 8, 64, "bf16", 64),
+                                          # up to 1024 pairs over up to 64 experts one block does the whole
+                                          # dispatch, otherwise three launches: both sides of the boundary
+                                          (512, 8, 2, 32, "bf16", 8), (513, 8, 2, 32, "f32", 3),
+                                          (256, 64, 4, 16, "bf16", 12), (256, 65, 4, 16, "bf16", 12),
+                                          (1024, 16, 1, 16, "f32", 5), (128, 64, 8, 16, "bf16", 20),
+                                          (3000, 160, 6, 32, "bf16", 16)])
 @pytest.mark.parametrize("plan", [False, True])
 def test_dispatch_matches_oracle(T, E, k, H, dt, R, plan):
     """plan: the dispatch plans the replicas itself from the routing's counts

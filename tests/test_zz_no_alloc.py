@@ -38,8 +38,10 @@ def _outputs(T, k, H, E, max_slots, dtype):
 
 
 def test_noalloc_dispatch_matches_the_workspace_entry_point():
-    # two calls in a row, the second smaller (it reuses what the first left)
-    for T, E, k, H, R in ((8192, 8, 2, 4096, 8), (777, 160, 6, 128, 16)):
+    # two calls in a row on the scratch, the second smaller (it reuses what the
+    # first left); then one small enough for the one-block dispatch, which needs
+    # no scratch
+    for T, E, k, H, R in ((8192, 8, 2, 4096, 8), (777, 160, 6, 128, 16), (300, 8, 2, 128, 4)):
         x, idx, reps = _case(T, E, k, H, R, T)
         max_slots = E + R
         ref = moe.moe_dispatch(x, idx, E, reps, max_slots)
