@@ -939,10 +939,10 @@ def main():
     torch.cuda.synchronize()
     # The spin before each cold step only has to outlast the host's issuing of
     # that step: twice its measured issue time, at least 0.3 ms.  A longer idle
-    # spin is not neutral: the chip's power management raises the clock while
-    # it idles and pulls it back a few milliseconds into the step (a 1.5 ms
-    # spin made the cold step 3-4% slower, all of it in the down GEMM, which
-    # starts 3 ms into the step; back-to-back warm steps do not see it).
+    # spin is not neutral: a 1.5 ms spin made the cold step 3-4% slower, all of
+    # it in the down GEMM, which starts 3 ms into the step, while back-to-back
+    # warm steps do not see it (most likely the power management raising the
+    # clock while the chip idles and pulling it back inside the step).
     issue_ms = host_issue_ms(step, 10 ** 5)
     spin_ms = max(0.3, 2.0 * issue_ms)
     spin = spin_cycles(torch, stream, spin_ms)
