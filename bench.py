@@ -185,11 +185,18 @@ def memory_phase_summary(T, H, E, k, warm, cold):
     them from x) over their event-timed GPU phase times (which also hold the
     GPU's gaps between launches)."""
     b = memory_phase_bytes(T, H, E, k)
+    M = T * k
+    # the same bytes per phase (route; dispatch's index arrays; combine's rows)
+    per = {"route": T * E * 4 + T * k * 8, "dispatch": T * k * 4 + M * 8, "combine": M * H * 2 + T * H * 2 + M * 8}
+    assert sum(per.values()) == b
     out = {"bytes": b}
     for label, ph in (("warm", warm), ("cold", cold)):
         us = ph["route"] + ph["dispatch"] + ph["combine"]
         out[label] = {"us": round(us, 2), "GBps": round(b / (us * 1e-6) / 1e9, 1),
-                      "frac_of_hbm": round(b / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 3)}
+                      "frac_of_hbm": round(b / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 3),
+                      "per_phase": {n: {"bytes": per[n], "us": ph[n],
+                                        "frac_of_hbm": round(per[n] / (ph[n] * 1e-6) / 1e9 / PEAK_HBM_GBS, 3)}
+                                    for n in per}}
     return out
 
 
@@ -537,7 +544,7 @@ def pipeline_bench(moe, synth, torch, np, steps=10, warmup=3):
 PEAK_FP32_TFLOPS = 157.3         # MI355X dense fp32 MFMA
 
 
-def configs_bench(moe, synth, torch, np, steps=10, warmup=3):
+def configs_bench(moe, synth, torch, np, steps=20, warmup=20):
     """Every workload's layer forward on the GPU: routed tokens/s per layer and the
     fraction of its roofline, t_roof = max(flop / MFMA peak, active expert weights /
     HBM) + memory-phase bytes / HBM (routing, dispatch, combine; algorithmic)."""
