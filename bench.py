@@ -622,7 +622,7 @@ def configs_bench(moe, synth, torch, np, steps=20, warmup=20):
                                        "slots_used": int(bufs["disp"]["n_slots"].item())})
         del x, bufs
 
-    def chain(name, cfg, R):
+    def chain(name, cfg, R, graph=False):
         """All L layers of one iteration, statistics and prediction included; the
         time per layer is the chain time over L."""
         cache.clear()
@@ -644,23 +644,40 @@ def configs_bench(moe, synth, torch, np, steps=20, warmup=20):
         bufs = [dict() for _ in range(L)]
         it = [0]
 
-        def step():
+        def step(st=None):
             it[0] += 1
             xx, prev_idx = x0, None
             for l in range(L):
                 r = moe.moe_layer_forward(xx, lgs[l], k, *weights[l], cfg.act, R, stats_state=state,
                                           stats_dims=(L, E, win), layer=l, it=it[0], prev_topk_idx=prev_idx,
-                                          bufs=bufs[l], stream=stream)
+                                          bufs=bufs[l], stream=stream if st is None else st)
                 xx, prev_idx = r["out"], r["idx"]
         ms = timed(step) / L
         counts = np.mean([b["counts"].cpu().numpy() for b in bufs], axis=0)
-        report(name, cfg, ms, counts, {"layers": L, "replica_budget": R, "window": win,
-                                       "note": "time per layer of the full chain, statistics and prediction included"})
+        extra = {"layers": L, "replica_budget": R, "window": win,
+                 "note": "time per layer of the full chain, statistics and prediction included"}
+        if graph:
+            # the same chain (one iteration index) captured into a HIP graph and
+            # replayed: one host call issues every kernel of the chain
+            torch.cuda.synchronize()
+            side = torch.cuda.Stream()
+            side.wait_stream(stream)
+            with torch.cuda.stream(side):
+                step(side)
+            stream.wait_stream(side)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(torch.cuda.current_stream())
+            extra["graph_ms_per_layer"] = round(timed(g.replay) / L, 4)
+            extra["note"] += "; graph_ms_per_layer: the chain replayed from a HIP graph"
+            del g
+        report(name, cfg, ms, counts, extra)
         del weights, bufs
         torch.cuda.empty_cache()
 
     C = synth.CONFIGS
-    chain("tiny (2-layer chain)", C["tiny"], C["tiny"].R)
+    chain("tiny (2-layer chain)", C["tiny"], C["tiny"].R, graph=True)
     single_layer("Mixtral-shaped, R=0", C["mixtral"], 0)
     single_layer("Mixtral-shaped, R=8", C["mixtral"], 8)
     for T in synth.DSV2_T_SWEEP:
