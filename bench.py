@@ -901,7 +901,6 @@ def main():
     def evict(i):
         torch.sum(flush, 0, out=flush_out)
 
-
     def make_layer(R_):
         state = torch.empty(moe.moe_stats_state_bytes(L, E, win), dtype=torch.uint8, device=dev)
         moe.moe_stats_init(state, L, E, win)
